@@ -1,0 +1,26 @@
+"""CPU oracle of the BigVGAN decode path -- test infrastructure only.
+
+Only the test suite, the package's smoke check and the benchmark's CPU
+baseline may import this package; the product path never does.
+"""
+
+from .mh3a_oracle import (  # noqa: F401
+    DEFAULT_CONFIG,
+    activation1d,
+    amp_block,
+    bessel_i0,
+    conv1d,
+    conv_transpose1d,
+    decode,
+    decode_item,
+    decode_window,
+    downsample2,
+    fold_weight_norm,
+    kaiser_beta,
+    kaiser_sinc_filter,
+    kaiser_window,
+    receptive_radius_latents,
+    snake_beta,
+    stage_amp,
+    upsample2,
+)

@@ -1,0 +1,387 @@
+"""Plain CPU oracle for the MiniMax-H3 audio-VAE BigVGAN decoder.
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT. Only the test suite, the
+package's smoke check and the CPU-baseline leg of the benchmark may import
+this module. The GPU library never calls it and shares no code with it.
+
+What it computes is the decode path described on two pages:
+
+* diffusers docs, "AutoencoderKLMiniMaxH3Audio": the constructor defaults
+  (section "AutoencoderKLMiniMaxH3Audio", parameter list) and the decode
+  contract (section "decode": de-normalized latents (B, 32, N) in, waveform
+  (B, 1, 800 N) out, clamped to [-1, 1]).
+* FastVideo API docs, "minimax_h3_audio_vae": the module overview (BigVGAN
+  decoder, weight-normalized ConvTranspose1d upsampling, AMP residual blocks
+  with SnakeBeta behind alias-free Kaiser-window up/down sampling, final
+  SnakeBeta, conv and clamp), the source of ``MLXMiniMaxH3AudioVAE.decode``
+  (the order of the ops and their paddings) and ``kaiser_sinc_filter1d``
+  (the low-pass design).
+
+Numerics. The pages fix fp32 storage (``mlx_h3_audio_vae_from_dir`` refuses
+anything but fp32; "Waveforms are float32"), so every tensor between ops is
+float32. Inside each op the arithmetic is float64 and the op's output is
+rounded to float32 once. Nothing is blocked, fused or reordered beyond what
+each definition states; numpy's float64 matmul serves as the inner sum of a
+convolution tap.
+
+Readings of what the pages leave open (each is listed in the design doc):
+
+* R1 ``_conv1d`` / ``_conv_transpose1d`` bodies are not shown: the standard
+  PyTorch definitions (cross-correlation, zero padding, no output padding).
+* R2 ``_wn_weight(v, g)``: w = g * v / ||v||, the norm over every axis but
+  axis 0 of the stored weight (C_out for conv, C_in for transposed conv).
+* R3 AMP block internals are not shown: BigVGAN's AMPBlock1 -- for each
+  dilation d: x <- x + conv_{k,1}(act(conv_{k,d}(act(x)))), "same" zero
+  padding d(k-1)/2, six activations per block.
+* R4 the anti-aliased activation: BigVGAN's Activation1d -- 2x upsample
+  (replicate pad 5, zero-insert transposed conv with the 12-tap filter,
+  gain 2, crop 15/15), SnakeBeta at the 2x rate, 12-tap low-pass with
+  replicate pad 5 left / 6 right and stride 2. Filter: cutoff 0.25,
+  half-width 0.3, 12 taps.
+* R5 SnakeBeta: y = x + sin^2(alpha x) / beta, alpha and beta per channel,
+  used as stored (no log scale, no epsilon).
+* R6 de-normalization, optional: z * std_c + mean_c (the convention the
+  diffusers "AutoencoderKLMiniMaxH3" page states for its latents).
+* R7 ``decoder.conv_post.bias`` is read with ``w.get``: absent means zero.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+# Constructor defaults: diffusers "AutoencoderKLMiniMaxH3Audio", parameter
+# list; the same values as FastVideo's MiniMaxH3AudioVAEConfigView.
+DEFAULT_CONFIG = {
+    "latent_channels": 32,
+    "latent_dim": 2048,
+    "decoder_dim": 1024,
+    "decoder_rates": (5, 5, 2, 2, 2, 2, 2),
+    "decoder_kernel_sizes": (9, 9, 4, 4, 4, 4, 4),
+    "resblock_kernel_sizes": (3, 7, 11),
+    "resblock_dilation_sizes": ((1, 3, 5), (1, 3, 5), (1, 3, 5)),
+    "sampling_rate": 32000,
+    "hop_length": 800,
+    # Reading R4: BigVGAN's resampler, ratio 2.
+    "filter_taps": 12,
+    "filter_cutoff": 0.25,
+    "filter_half_width": 0.3,
+}
+
+
+def _f32(a):
+    return np.asarray(a, dtype=F64).astype(F32)
+
+
+# ---------------------------------------------------------------------------
+# Kaiser-windowed sinc low-pass: FastVideo "minimax_h3_audio_vae",
+# function kaiser_sinc_filter1d.
+# ---------------------------------------------------------------------------
+
+def bessel_i0(x):
+    """Modified Bessel function of the first kind, order 0, by its power
+    series sum_m ((x/2)^m / m!)^2, summed until the terms stop mattering."""
+    x = np.asarray(x, dtype=F64)
+    q = (x / 2.0) ** 2
+    term = np.ones_like(x)
+    total = np.ones_like(x)
+    for m in range(1, 200):
+        term = term * q / (m * m)
+        total = total + term
+        if np.all(term <= 1e-17 * total):
+            break
+    return total
+
+
+def kaiser_beta(cutoff, half_width, kernel_size):
+    """The page's Kaiser shape parameter: attenuation from the half size
+    (kernel_size // 2 minus one, as released) and 4 * half_width, then the
+    three-branch Kaiser formula."""
+    half_size = kernel_size // 2
+    attenuation = 2.285 * (half_size - 1) * math.pi * (4.0 * half_width) + 7.95
+    if attenuation > 50.0:
+        return 0.1102 * (attenuation - 8.7)
+    if attenuation >= 21.0:
+        return 0.5842 * (attenuation - 21.0) ** 0.4 + 0.07886 * (attenuation - 21.0)
+    return 0.0
+
+
+def kaiser_window(n, beta):
+    """Symmetric Kaiser window of n points: I0(beta sqrt(1 - (2k/(n-1) - 1)^2)) / I0(beta)."""
+    if n == 1:
+        return np.ones(1, dtype=F64)
+    k = np.arange(n, dtype=F64)
+    r = 2.0 * k / (n - 1) - 1.0
+    return bessel_i0(beta * np.sqrt(np.maximum(0.0, 1.0 - r * r))) / bessel_i0(np.asarray(beta))
+
+
+def kaiser_sinc_filter(cutoff, half_width, kernel_size):
+    """2 fc w[n] sinc(2 fc t_n), normalized to unit sum; t_n is the
+    half-integer grid n - K/2 + 1/2 for even K, the integer grid otherwise.
+    Evaluated in float64 and returned as float32."""
+    half_size = kernel_size // 2
+    beta = kaiser_beta(cutoff, half_width, kernel_size)
+    window = kaiser_window(kernel_size, beta)
+    if kernel_size % 2 == 0:
+        t = np.arange(kernel_size, dtype=F64) - half_size + 0.5
+    else:
+        t = np.arange(kernel_size, dtype=F64) - half_size
+    x = 2.0 * cutoff * t
+    sinc = np.where(x == 0.0, 1.0, np.sin(np.pi * x) / np.where(x == 0.0, 1.0, np.pi * x))
+    filt = 2.0 * cutoff * window * sinc
+    filt = filt / filt.sum()
+    return filt.astype(F32)
+
+
+# ---------------------------------------------------------------------------
+# Weight norm (reading R2).
+# ---------------------------------------------------------------------------
+
+def fold_weight_norm(v, g):
+    """w = g * v / ||v||, the norm taken over every axis of v except axis 0."""
+    v64 = np.asarray(v, dtype=F64)
+    g64 = np.asarray(g, dtype=F64).reshape((v64.shape[0],) + (1,) * (v64.ndim - 1))
+    norm = np.sqrt(np.sum(v64 * v64, axis=tuple(range(1, v64.ndim)), keepdims=True))
+    return _f32(g64 * v64 / norm)
+
+
+# ---------------------------------------------------------------------------
+# Convolutions (reading R1). x: (C_in, L) float32 for one batch item.
+# ---------------------------------------------------------------------------
+
+def conv1d(x, w, b=None, padding=0, dilation=1):
+    """y[o, t] = b[o] + sum_i sum_j w[o, i, j] x[i, t + j d - p], with x = 0
+    outside [0, L); output length L + 2p - d (k - 1)."""
+    x = np.asarray(x, dtype=F32)
+    w = np.asarray(w, dtype=F32)
+    c_out, c_in, k = w.shape
+    assert x.shape[0] == c_in, (x.shape, w.shape)
+    length = x.shape[1]
+    l_out = length + 2 * padding - dilation * (k - 1)
+    assert l_out >= 1
+    xp = np.zeros((c_in, length + 2 * padding), dtype=F64)
+    xp[:, padding:padding + length] = x
+    taps = np.ascontiguousarray(np.moveaxis(w.astype(F64), 2, 0))  # (k, C_out, C_in)
+    y = np.zeros((c_out, l_out), dtype=F64)
+    for j in range(k):
+        y += taps[j] @ xp[:, j * dilation:j * dilation + l_out]
+    if b is not None:
+        y += np.asarray(b, dtype=F64)[:, None]
+    return y.astype(F32)
+
+
+def conv_transpose1d(x, w, b, stride, padding):
+    """Transposed convolution: every input x[i, j] scatters w[i, o, q] x[i, j]
+    into position j r + q - p; positions outside [0, (L-1) r - 2p + k) are
+    dropped. w has shape (C_in, C_out, k)."""
+    x = np.asarray(x, dtype=F32)
+    w = np.asarray(w, dtype=F32)
+    c_in, c_out, k = w.shape
+    assert x.shape[0] == c_in
+    length = x.shape[1]
+    full_len = (length - 1) * stride + k
+    full = np.zeros((c_out, full_len), dtype=F64)
+    x64 = x.astype(F64)
+    taps = np.ascontiguousarray(np.transpose(w.astype(F64), (2, 1, 0)))  # (k, C_out, C_in)
+    for q in range(k):
+        full[:, q:q + (length - 1) * stride + 1:stride] += taps[q] @ x64
+    l_out = full_len - 2 * padding
+    y = full[:, padding:padding + l_out]
+    if b is not None:
+        y = y + np.asarray(b, dtype=F64)[:, None]
+    return y.astype(F32)
+
+
+# ---------------------------------------------------------------------------
+# Anti-aliased SnakeBeta (readings R4, R5). All arrays are (C, L), float64
+# inside.
+# ---------------------------------------------------------------------------
+
+def upsample2(x, f):
+    """Replicate-pad 5 on each side, transposed conv with stride 2 and the
+    12-tap filter (zero insertion followed by the FIR), gain 2, crop 15 on
+    each side: length L -> 2L."""
+    x = np.asarray(x, dtype=F64)
+    f = np.asarray(f, dtype=F64)
+    k = f.shape[0]
+    ratio = 2
+    pad = k // ratio - 1
+    crop_left = pad * ratio + (k - ratio) // 2
+    crop_right = pad * ratio + (k - ratio + 1) // 2
+    xp = np.pad(x, ((0, 0), (pad, pad)), mode="edge")
+    n = xp.shape[1]
+    full = np.zeros((x.shape[0], (n - 1) * ratio + k), dtype=F64)
+    for q in range(k):
+        full[:, q:q + (n - 1) * ratio + 1:ratio] += f[q] * xp
+    return ratio * full[:, crop_left:full.shape[1] - crop_right]
+
+
+def snake_beta(u, alpha, beta):
+    """u + sin^2(alpha u) / beta, per channel."""
+    a = np.asarray(alpha, dtype=F64).reshape(-1, 1)
+    b = np.asarray(beta, dtype=F64).reshape(-1, 1)
+    return u + np.sin(a * u) ** 2 / b
+
+
+def downsample2(s, f):
+    """Replicate-pad K/2 - 1 left and K/2 right, then the 12-tap FIR as a
+    cross-correlation with stride 2: length 2L -> L."""
+    s = np.asarray(s, dtype=F64)
+    f = np.asarray(f, dtype=F64)
+    k = f.shape[0]
+    pad_left = k // 2 - (1 if k % 2 == 0 else 0)
+    pad_right = k // 2
+    sp = np.pad(s, ((0, 0), (pad_left, pad_right)), mode="edge")
+    l_out = (sp.shape[1] - k) // 2 + 1
+    y = np.zeros((s.shape[0], l_out), dtype=F64)
+    for q in range(k):
+        y += f[q] * sp[:, q:q + 2 * (l_out - 1) + 1:2]
+    return y
+
+
+def activation1d(x, alpha, beta, f_up, f_down):
+    """Anti-aliased SnakeBeta: upsample2 -> SnakeBeta -> downsample2; the
+    three steps in float64, the result rounded to float32 once."""
+    u = upsample2(np.asarray(x, dtype=F32), f_up)
+    s = snake_beta(u, alpha, beta)
+    return downsample2(s, f_down).astype(F32)
+
+
+# ---------------------------------------------------------------------------
+# Parameter access.
+# ---------------------------------------------------------------------------
+
+def _conv_weight(params, prefix):
+    """A conv's weight: folded from weight_v / weight_g, or taken as given
+    when the parameter set holds an already-folded ``weight``."""
+    if prefix + ".weight_v" in params:
+        return fold_weight_norm(params[prefix + ".weight_v"], params[prefix + ".weight_g"])
+    return np.asarray(params[prefix + ".weight"], dtype=F32)
+
+
+def _act_params(params, prefix, default_filter):
+    alpha = params[prefix + ".act.alpha"]
+    beta = params[prefix + ".act.beta"]
+    f_up = params.get(prefix + ".upsample.filter", default_filter)
+    f_down = params.get(prefix + ".downsample.lowpass.filter", default_filter)
+    return (np.asarray(alpha, dtype=F32).reshape(-1), np.asarray(beta, dtype=F32).reshape(-1),
+            np.asarray(f_up, dtype=F32).reshape(-1), np.asarray(f_down, dtype=F32).reshape(-1))
+
+
+def amp_block(x, params, prefix, kernel, dilations, default_filter):
+    """Reading R3: for each dilation d, x <- x + conv2(act2(conv1(act1(x))))
+    with conv1 of dilation d and conv2 of dilation 1, both "same"-padded."""
+    for n, d in enumerate(dilations):
+        a1 = _act_params(params, f"{prefix}.activations.{2 * n}", default_filter)
+        a2 = _act_params(params, f"{prefix}.activations.{2 * n + 1}", default_filter)
+        t = activation1d(x, *a1)
+        t = conv1d(t, _conv_weight(params, f"{prefix}.convs1.{n}"), params[f"{prefix}.convs1.{n}.bias"],
+                   padding=d * (kernel - 1) // 2, dilation=d)
+        t = activation1d(t, *a2)
+        t = conv1d(t, _conv_weight(params, f"{prefix}.convs2.{n}"), params[f"{prefix}.convs2.{n}.bias"],
+                   padding=(kernel - 1) // 2, dilation=1)
+        x = _f32(x.astype(F64) + t.astype(F64))
+    return x
+
+
+def stage_amp(h, params, stage, config=None, filt=None):
+    """One stage's AMP set: the parallel blocks run from the same input and
+    their outputs are averaged (``decode``: residual_sum / num_resblocks)."""
+    cfg = dict(DEFAULT_CONFIG, **(config or {}))
+    if filt is None:
+        filt = kaiser_sinc_filter(cfg["filter_cutoff"], cfg["filter_half_width"], cfg["filter_taps"])
+    kernels = cfg["resblock_kernel_sizes"]
+    if len(kernels) == 0:
+        raise RuntimeError("decoder has no residual blocks")
+    acc = np.zeros(h.shape, dtype=F64)
+    for j, k in enumerate(kernels):
+        out = amp_block(h, params, f"decoder.resblocks.{stage * len(kernels) + j}", k,
+                        cfg["resblock_dilation_sizes"][j], filt)
+        acc += out.astype(F64)
+    return _f32(acc / len(kernels))
+
+
+def decode_item(params, z, config=None, denormalize=False, latents_mean=None, latents_std=None,
+                clamp=True, return_stages=False):
+    """One batch item: z (latent_channels, N) float32 -> (1, 800 N) float32.
+
+    Follows ``MLXMiniMaxH3AudioVAE.decode``: dec_in_proj (1x1), conv_pre
+    (pad 3), per upsampling stage a transposed conv with stride r and padding
+    (k - r) // 2 followed by the averaged AMP blocks, then activation_post,
+    conv_post (pad 3) and the clamp."""
+    cfg = dict(DEFAULT_CONFIG, **(config or {}))
+    filt = kaiser_sinc_filter(cfg["filter_cutoff"], cfg["filter_half_width"], cfg["filter_taps"])
+    stages = []
+    z = np.asarray(z, dtype=F32)
+    if denormalize:
+        mean = np.zeros(z.shape[0]) if latents_mean is None else np.asarray(latents_mean, dtype=F32)
+        std = np.ones(z.shape[0]) if latents_std is None else np.asarray(latents_std, dtype=F32)
+        z = _f32(z.astype(F64) * std.astype(F64)[:, None] + mean.astype(F64)[:, None])
+    h = conv1d(z, params["dec_in_proj.weight"], params["dec_in_proj.bias"])
+    stages.append(h)
+    h = conv1d(h, _conv_weight(params, "decoder.conv_pre"), params["decoder.conv_pre.bias"], padding=3)
+    stages.append(h)
+    for s, (rate, kernel) in enumerate(zip(cfg["decoder_rates"], cfg["decoder_kernel_sizes"])):
+        h = conv_transpose1d(h, _conv_weight(params, f"decoder.ups.{s}.0"), params[f"decoder.ups.{s}.0.bias"],
+                             stride=rate, padding=(kernel - rate) // 2)
+        stages.append(h)
+        h = stage_amp(h, params, s, cfg, filt)
+        stages.append(h)
+    h = activation1d(h, *_act_params(params, "decoder.activation_post", filt))
+    y = conv1d(h, _conv_weight(params, "decoder.conv_post"), params.get("decoder.conv_post.bias"), padding=3)
+    if clamp:
+        y = np.minimum(np.maximum(y, F32(-1.0)), F32(1.0))
+    if return_stages:
+        return y, stages
+    return y
+
+
+def decode(params, z, config=None, denormalize=False, latents_mean=None, latents_std=None, clamp=True):
+    """Latents (B, latent_channels, N) -> waveform (B, 1, 800 N). Batch items
+    (the stereo channels) decode independently and in order."""
+    z = np.asarray(z, dtype=F32)
+    assert z.ndim == 3
+    return np.stack([decode_item(params, z[b], config, denormalize, latents_mean, latents_std, clamp)
+                     for b in range(z.shape[0])])
+
+
+def receptive_radius_latents(config=None):
+    """Upper bound, in latents, on how far an output sample's dependence
+    reaches into the latent sequence: the sum of every layer's one-sided
+    reach converted to the latent rate (used to decode windows whose
+    interior equals the full decode)."""
+    cfg = dict(DEFAULT_CONFIG, **(config or {}))
+    act_reach = 5  # a[n] reads x[n-5 .. n+5] (R4)
+    reach = 0.0
+    reach += 3  # conv_pre, k = 7, latent rate
+    rate = 1
+    for r, k in zip(cfg["decoder_rates"], cfg["decoder_kernel_sizes"]):
+        reach += math.ceil(k / r) / rate  # transposed conv, input rate
+        rate *= r
+        block = 0
+        for kk, dils in zip(cfg["resblock_kernel_sizes"], cfg["resblock_dilation_sizes"]):
+            block = max(block, sum(d * (kk - 1) // 2 + (kk - 1) // 2 + 2 * act_reach for d in dils))
+        reach += block / rate
+    reach += (act_reach + 3) / rate  # activation_post + conv_post
+    return reach
+
+
+def decode_window(params, z, n0, n1, margin=None, config=None, denormalize=False, latents_mean=None,
+                  latents_std=None, clamp=True):
+    """Output samples [800 n0, 800 n1) of the full decode of z (B, C, N),
+    computed from the latent window [n0 - margin, n1 + margin) cut to the
+    sequence; the margin exceeds the receptive radius, so the cropped
+    result equals the full decode's samples."""
+    cfg = dict(DEFAULT_CONFIG, **(config or {}))
+    hop = int(np.prod(cfg["decoder_rates"]))
+    if margin is None:
+        margin = int(math.ceil(receptive_radius_latents(cfg))) + 4
+    n_total = z.shape[2]
+    a = max(0, n0 - margin)
+    b = min(n_total, n1 + margin)
+    y = decode(params, z[:, :, a:b], cfg, denormalize, latents_mean, latents_std, clamp)
+    return y[:, :, (n0 - a) * hop:(n1 - a) * hop]

@@ -1,0 +1,497 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself:
+library routines that implement the same textbook operation (scipy's Kaiser
+design, torch's convolutions and weight norm), closed forms derived by hand
+from the definitions, brute-force sums on tiny inputs, and invariants of the
+method (DC gain, impulse response, length laws, batch independence,
+linearity, shift equivariance)."""
+
+import math
+
+import numpy as np
+import pytest
+import scipy.signal as ss
+import scipy.special as sp
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+from neural_audio_vae_amd import synth
+from tests.conftest import SMALL_CONFIG
+
+F64 = torch.float64
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+# ---------------------------------------------------------------------------
+# Kaiser-windowed sinc low-pass (FastVideo "minimax_h3_audio_vae",
+# kaiser_sinc_filter1d)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("x", [0.0, 0.1, 1.0, 2.5, 4.6638, 10.0, 30.0])
+def test_bessel_i0_matches_scipy(x):
+    assert O.bessel_i0(x) == pytest.approx(sp.i0(x), rel=1e-14)
+
+
+@pytest.mark.parametrize("ksize,hw", [(12, 0.3), (6, 0.3), (4, 0.1), (16, 0.2), (11, 0.3)])
+def test_kaiser_beta_matches_scipy_design_rules(ksize, hw):
+    # The page's attenuation is scipy's kaiser_atten with (half_size - 1)
+    # in place of (numtaps - 1), i.e. numtaps = half_size, and width 4 hw;
+    # its three-branch beta is scipy's kaiser_beta.
+    atten = ss.kaiser_atten(ksize // 2, 4 * hw)
+    assert O.kaiser_beta(0.25, hw, ksize) == pytest.approx(ss.kaiser_beta(atten), rel=1e-13, abs=1e-15)
+
+
+def test_kaiser_beta_default_value():
+    # 2.285 * 5 * pi * 1.2 + 7.95 = 51.0212... > 50, beta = 0.1102 (A - 8.7)
+    atten = 2.285 * 5 * math.pi * 1.2 + 7.95
+    assert atten > 50
+    assert O.kaiser_beta(0.25, 0.3, 12) == pytest.approx(4.66380013, abs=1e-8)
+
+
+@pytest.mark.parametrize("n,beta", [(12, 4.6638), (11, 3.0), (2, 1.0), (31, 8.0)])
+def test_kaiser_window_matches_scipy(n, beta):
+    np.testing.assert_allclose(O.kaiser_window(n, beta), ss.windows.kaiser(n, beta, sym=True), rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("ksize,cutoff,hw", [(12, 0.25, 0.3), (11, 0.25, 0.3), (16, 0.2, 0.25), (12, 0.1, 0.3)])
+def test_filter_matches_scipy_firwin(ksize, cutoff, hw):
+    # firwin builds the same windowed sinc on the grid n - (K-1)/2 (half
+    # integers for even K, integers for odd K) with the cutoff as a fraction
+    # of Nyquist (2 fc), and scales it to unit DC gain.
+    beta = O.kaiser_beta(cutoff, hw, ksize)
+    ref = ss.firwin(ksize, 2 * cutoff, window=("kaiser", beta), scale=True)
+    got = O.kaiser_sinc_filter(cutoff, hw, ksize).astype(np.float64)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=2e-8)
+
+
+def test_filter_properties():
+    f = O.kaiser_sinc_filter(0.25, 0.3, 12).astype(np.float64)
+    assert f.dtype == np.float64 and f.shape == (12,)
+    assert abs(f.sum() - 1.0) < 1e-7
+    np.testing.assert_array_equal(f, f[::-1])
+    # Symmetry of a 12-tap filter maps even taps onto odd ones, so each
+    # polyphase branch sums to one half.
+    assert abs(f[0::2].sum() - 0.5) < 1e-7 and abs(f[1::2].sum() - 0.5) < 1e-7
+    # Centre taps dominate, outermost taps are small and positive.
+    assert f[5] > 0.4 and 0 < f[0] < 0.01
+
+
+# ---------------------------------------------------------------------------
+# Weight norm (reading: norm over all axes but axis 0)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(6, 4, 3), (4, 6, 9), (1, 8, 7)])
+def test_weight_norm_matches_torch(shape):
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal(shape).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, size=(shape[0], 1, 1)).astype(np.float32)
+    ref = torch._weight_norm(torch.tensor(v, dtype=F64), torch.tensor(g, dtype=F64), 0).numpy()
+    np.testing.assert_allclose(O.fold_weight_norm(v, g), ref, rtol=1e-6, atol=0)
+
+
+def test_weight_norm_invariants():
+    rng = np.random.default_rng(2)
+    v = rng.standard_normal((5, 3, 4)).astype(np.float32)
+    norm = np.sqrt((v.astype(np.float64) ** 2).sum(axis=(1, 2)))
+    np.testing.assert_allclose(O.fold_weight_norm(v, norm.reshape(5, 1, 1)), v, rtol=2e-7)
+    g = rng.uniform(0.5, 2, size=(5, 1, 1)).astype(np.float32)
+    np.testing.assert_allclose(O.fold_weight_norm(3.5 * v, g), O.fold_weight_norm(v, g), rtol=2e-7)
+    w = O.fold_weight_norm(v, -g).astype(np.float64)
+    np.testing.assert_allclose(np.sqrt((w ** 2).sum(axis=(1, 2))), g.reshape(-1), rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Convolutions: brute-force double sums on tiny shapes, and torch
+# ---------------------------------------------------------------------------
+
+def brute_conv1d(x, w, b, p, d):
+    """Scatter form: every input sample x[i, s] adds w[o, i, j] x[i, s] to
+    the output t with t + j d - p = s."""
+    c_out, c_in, k = w.shape
+    length = x.shape[1]
+    l_out = length + 2 * p - d * (k - 1)
+    y = [[float(b[o]) for _ in range(l_out)] for o in range(c_out)]
+    for o in range(c_out):
+        for i in range(c_in):
+            for j in range(k):
+                for s in range(length):
+                    t = s - j * d + p
+                    if 0 <= t < l_out:
+                        y[o][t] += float(w[o, i, j]) * float(x[i, s])
+    return np.array(y)
+
+
+def brute_conv_transpose1d(x, w, b, r, p):
+    """Gather form: y[o, t] = b[o] + sum over (i, j, q) with j r + q - p = t."""
+    c_in, c_out, k = w.shape
+    length = x.shape[1]
+    l_out = (length - 1) * r - 2 * p + k
+    y = np.zeros((c_out, l_out))
+    for o in range(c_out):
+        for t in range(l_out):
+            acc = float(b[o])
+            for i in range(c_in):
+                for j in range(length):
+                    q = t + p - j * r
+                    if 0 <= q < k:
+                        acc += float(w[i, o, q]) * float(x[i, j])
+            y[o, t] = acc
+    return y
+
+
+@pytest.mark.parametrize("k,d", [(1, 1), (3, 1), (3, 5), (7, 1), (7, 3), (11, 1), (11, 5), (4, 2)])
+def test_conv1d_matches_brute_force(k, d):
+    rng = np.random.default_rng(10 * k + d)
+    c_in, c_out, length = 3, 4, 9
+    p = d * (k - 1) // 2
+    if length + 2 * p - d * (k - 1) < 1:
+        pytest.skip("empty output")
+    x = rng.standard_normal((c_in, length)).astype(np.float32)
+    w = rng.standard_normal((c_out, c_in, k)).astype(np.float32)
+    b = rng.standard_normal(c_out).astype(np.float32)
+    got = O.conv1d(x, w, b, padding=p, dilation=d).astype(np.float64)
+    ref = brute_conv1d(x, w, b, p, d)
+    assert got.shape == ref.shape == (c_out, length + 2 * p - d * (k - 1))
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("k,d,p", [(3, 1, 1), (7, 3, 9), (11, 5, 25), (7, 1, 3), (1, 1, 0), (5, 2, 0)])
+def test_conv1d_matches_torch(k, d, p):
+    rng = np.random.default_rng(k * 100 + d)
+    x = rng.standard_normal((2, 6, 40)).astype(np.float32)
+    w = rng.standard_normal((5, 6, k)).astype(np.float32)
+    b = rng.standard_normal(5).astype(np.float32)
+    ref = F.conv1d(torch.tensor(x, dtype=F64), torch.tensor(w, dtype=F64), torch.tensor(b, dtype=F64),
+                   padding=p, dilation=d).numpy()
+    for bi in range(2):
+        np.testing.assert_allclose(O.conv1d(x[bi], w, b, padding=p, dilation=d), ref[bi], rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("r,k", [(5, 9), (2, 4), (3, 7), (4, 4)])
+def test_conv_transpose1d_matches_brute_force(r, k):
+    rng = np.random.default_rng(r * 31 + k)
+    c_in, c_out, length = 3, 2, 6
+    p = (k - r) // 2
+    x = rng.standard_normal((c_in, length)).astype(np.float32)
+    w = rng.standard_normal((c_in, c_out, k)).astype(np.float32)
+    b = rng.standard_normal(c_out).astype(np.float32)
+    got = O.conv_transpose1d(x, w, b, r, p).astype(np.float64)
+    ref = brute_conv_transpose1d(x, w, b, r, p)
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("r,k", [(5, 9), (2, 4)])
+def test_conv_transpose1d_matches_torch(r, k):
+    rng = np.random.default_rng(r + 7 * k)
+    x = rng.standard_normal((8, 33)).astype(np.float32)
+    w = rng.standard_normal((8, 5, k)).astype(np.float32)
+    b = rng.standard_normal(5).astype(np.float32)
+    p = (k - r) // 2
+    ref = F.conv_transpose1d(torch.tensor(x[None], dtype=F64), torch.tensor(w, dtype=F64),
+                             torch.tensor(b, dtype=F64), stride=r, padding=p).numpy()[0]
+    np.testing.assert_allclose(O.conv_transpose1d(x, w, b, r, p), ref, rtol=1e-6, atol=1e-6)
+
+
+def test_transposed_conv_length_law():
+    # (L - 1) r - 2p + k = r L with p = (k - r) // 2 for every stage.
+    x = np.ones((1, 7), dtype=np.float32)
+    for r, k in zip(O.DEFAULT_CONFIG["decoder_rates"], O.DEFAULT_CONFIG["decoder_kernel_sizes"]):
+        w = np.ones((1, 1, k), dtype=np.float32)
+        assert O.conv_transpose1d(x, w, None, r, (k - r) // 2).shape == (1, 7 * r)
+    assert int(np.prod(O.DEFAULT_CONFIG["decoder_rates"])) == O.DEFAULT_CONFIG["hop_length"] == 800
+
+
+# ---------------------------------------------------------------------------
+# Anti-aliased activation: up 2x -> SnakeBeta -> down 2x
+# ---------------------------------------------------------------------------
+
+FILT = O.kaiser_sinc_filter(0.25, 0.3, 12)
+
+
+def torch_upsample2(x, f):
+    """Replicate pad 5, grouped transposed conv (stride 2), gain 2, crop 15/15
+    -- the same operation composed from torch library routines."""
+    c = x.shape[0]
+    xt = F.pad(torch.tensor(x[None], dtype=F64), (5, 5), mode="replicate")
+    ft = torch.tensor(f, dtype=F64).view(1, 1, -1).expand(c, 1, 12).contiguous()
+    return (2 * F.conv_transpose1d(xt, ft, stride=2, groups=c))[0, :, 15:-15].numpy()
+
+
+def torch_downsample2(s, f):
+    c = s.shape[0]
+    st = F.pad(torch.tensor(s[None], dtype=F64), (5, 6), mode="replicate")
+    ft = torch.tensor(f, dtype=F64).view(1, 1, -1).expand(c, 1, 12).contiguous()
+    return F.conv1d(st, ft, stride=2, groups=c)[0].numpy()
+
+
+def brute_upsample2(x, f):
+    """Polyphase form derived by hand: with X the replicate-extended input,
+    u[2t] = 2 sum_{e=-2..3} X[t-e] f[5+2e] and
+    u[2t+1] = 2 sum_{e=-3..2} X[t-e] f[6+2e]."""
+    c, length = x.shape
+    u = np.zeros((c, 2 * length))
+    for ch in range(c):
+        X = lambda m: float(x[ch, min(max(m, 0), length - 1)])  # noqa: E731
+        for t in range(length):
+            u[ch, 2 * t] = 2 * sum(X(t - e) * float(f[5 + 2 * e]) for e in range(-2, 4))
+            u[ch, 2 * t + 1] = 2 * sum(X(t - e) * float(f[6 + 2 * e]) for e in range(-3, 3))
+    return u
+
+
+def brute_downsample2(s, f):
+    """a[n] = sum_q f[q] s[clamp(2n + q - 5)]."""
+    c, n2 = s.shape
+    out = np.zeros((c, n2 // 2))
+    for ch in range(c):
+        for n in range(n2 // 2):
+            out[ch, n] = sum(float(f[q]) * float(s[ch, min(max(2 * n + q - 5, 0), n2 - 1)]) for q in range(12))
+    return out
+
+
+@pytest.mark.parametrize("length", [1, 2, 5, 11, 40])
+def test_upsample_matches_torch_and_polyphase(length):
+    x = np.random.default_rng(length).standard_normal((3, length)).astype(np.float32)
+    got = O.upsample2(x, FILT)
+    assert got.shape == (3, 2 * length)
+    np.testing.assert_allclose(got, torch_upsample2(x, FILT), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got, brute_upsample2(x, FILT), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("length", [1, 2, 5, 11, 40])
+def test_downsample_matches_torch_and_brute(length):
+    s = np.random.default_rng(100 + length).standard_normal((3, 2 * length))
+    got = O.downsample2(s, FILT)
+    assert got.shape == (3, length)
+    np.testing.assert_allclose(got, torch_downsample2(s, FILT), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got, brute_downsample2(s, FILT), rtol=1e-12, atol=1e-12)
+
+
+def test_resampler_dc_gain():
+    # A constant passes the upsampler and the up->down cascade unchanged:
+    # each polyphase branch sums to 1/2 and the gain is 2.
+    c = np.full((2, 17), 0.7311, dtype=np.float32)
+    np.testing.assert_allclose(O.upsample2(c, FILT), 0.7311, rtol=1e-7)
+    np.testing.assert_allclose(O.downsample2(O.upsample2(c, FILT), FILT), 0.7311, rtol=1e-7)
+
+
+def test_resampler_impulse_response_is_even_autocorrelation():
+    # With an identity activation, up->down is LTI with impulse response
+    # h[m] = 2 (f * f)[2m] (f symmetric, so autocorrelation = convolution),
+    # centred on the impulse: zero delay, gain 2 on the even lags.
+    n0, length = 30, 61
+    x = np.zeros((1, length), dtype=np.float32)
+    x[0, n0] = 1.0
+    y = O.downsample2(O.upsample2(x, FILT), FILT)[0]
+    ac = np.correlate(FILT.astype(np.float64), FILT.astype(np.float64), mode="full")  # lags -11..11
+    h = 2 * ac[1::2]  # even lags -10..10 -> m = -5..5
+    expect = np.zeros(length)
+    expect[n0 - 5:n0 + 6] = h
+    np.testing.assert_allclose(y, expect, atol=1e-12)
+
+
+def test_resampler_passes_low_frequency_sine_without_delay():
+    n = np.arange(400)
+    x = np.sin(2 * np.pi * 0.02 * n)[None].astype(np.float32)
+    y = O.downsample2(O.upsample2(x, FILT), FILT)[0]
+    inner = slice(20, 380)
+    assert np.max(np.abs(y[inner] - x[0, inner])) < 5e-4
+
+
+def test_snake_beta_closed_forms():
+    u = np.array([[0.0, 0.3, -2.0, math.pi / 2]])
+    np.testing.assert_allclose(O.snake_beta(u, [1e-30], [0.7]), u, atol=1e-15)
+    # alpha u = pi/2 -> u + 1/beta
+    np.testing.assert_allclose(O.snake_beta(np.array([[math.pi / 2]]), [1.0], [0.8]), math.pi / 2 + 1.25)
+    # sin^2 is even in u
+    np.testing.assert_allclose(O.snake_beta(np.array([[1.3]]), [1.1], [0.6]) - 1.3,
+                               O.snake_beta(np.array([[-1.3]]), [1.1], [0.6]) + 1.3)
+
+
+def test_activation_alpha_to_zero_is_resampler_only():
+    x = np.random.default_rng(5).standard_normal((2, 50)).astype(np.float32)
+    got = O.activation1d(x, [0.0, 0.0], [1.0, 1.0], FILT, FILT)
+    ref = torch_downsample2(torch_upsample2(x, FILT), FILT)
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-6)
+
+
+def test_activation_of_constant():
+    c = 0.9
+    x = np.full((1, 23), c, dtype=np.float32)
+    got = O.activation1d(x, [1.3], [0.7], FILT, FILT)
+    c32 = float(np.float32(c))
+    np.testing.assert_allclose(got, c32 + math.sin(1.3 * c32) ** 2 / 0.7, rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Whole decoder: structure and invariants
+# ---------------------------------------------------------------------------
+
+def zero_alpha_bias(params):
+    p = dict(params)
+    for name in p:
+        if name.endswith(".alpha") or name.endswith(".bias"):
+            p[name] = np.zeros_like(p[name])
+    return p
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_decode_length_and_clamp(default_params, n):
+    z = synth.make_latents(1, n)
+    y = O.decode(default_params, z)
+    assert y.shape == (1, 1, 800 * n) and y.dtype == np.float32
+    assert np.all(y <= 1.0) and np.all(y >= -1.0)
+    assert np.all(np.isfinite(O.decode(default_params, z, clamp=False)))
+
+
+def test_decode_batch_items_independent_and_in_order(small_params):
+    z = synth.make_latents(2, 6, channels=4)
+    both = O.decode(small_params, z, SMALL_CONFIG, clamp=False)
+    np.testing.assert_array_equal(both[0], O.decode(small_params, z[:1], SMALL_CONFIG, clamp=False)[0])
+    np.testing.assert_array_equal(both[1], O.decode(small_params, z[1:], SMALL_CONFIG, clamp=False)[0])
+    assert not np.array_equal(both[0], both[1])
+
+
+def test_decode_linear_when_snake_and_biases_vanish(small_params):
+    p = zero_alpha_bias(small_params)
+    z1 = synth.make_latents(1, 5, seed=1, channels=4)
+    z2 = synth.make_latents(1, 5, seed=2, channels=4)
+    a, b = 0.75, -1.5
+    lhs = O.decode(p, a * z1 + b * z2, SMALL_CONFIG, clamp=False)
+    rhs = a * O.decode(p, z1, SMALL_CONFIG, clamp=False).astype(np.float64) + \
+        b * O.decode(p, z2, SMALL_CONFIG, clamp=False).astype(np.float64)
+    assert rel_l2(lhs, rhs) < 1e-5
+
+
+def test_decode_shift_equivariant_in_the_interior(small_params):
+    # Every layer is a finite stencil, so dropping s leading latents shifts
+    # the output by 800 s, away from both ends of the sequence.
+    n, s = 90, 3
+    z = synth.make_latents(1, n, seed=4, channels=4)
+    full = O.decode(small_params, z, SMALL_CONFIG, clamp=False)[0, 0]
+    cut = O.decode(small_params, z[:, :, s:], SMALL_CONFIG, clamp=False)[0, 0]
+    margin = int(math.ceil(O.receptive_radius_latents())) * 800
+    lo, hi = margin, (n - s) * 800 - margin
+    assert hi - lo > 800 * 20
+    np.testing.assert_allclose(cut[lo:hi], full[lo + 800 * s:hi + 800 * s], rtol=1e-6, atol=1e-6)
+    # ... while near the left end the replicate / zero padding makes them differ.
+    assert np.max(np.abs(cut[:800] - full[800 * s:800 * s + 800])) > 1e-3
+
+
+def test_receptive_radius_bounds_dependence(small_params):
+    # Perturbing a latent just outside the derived radius leaves a sample
+    # untouched; one well inside it changes the sample.
+    n = 80
+    radius = int(math.ceil(O.receptive_radius_latents()))
+    z = synth.make_latents(1, n, seed=6, channels=4)
+    base = O.decode(small_params, z, SMALL_CONFIG, clamp=False)[0, 0]
+    t = 10 * 800 + 400  # an output sample inside latent 10
+    far = z.copy()
+    far[0, :, 10 + radius + 1] += 3.0
+    near = z.copy()
+    near[0, :, 12] += 3.0
+    assert O.decode(small_params, far, SMALL_CONFIG, clamp=False)[0, 0, t] == base[t]
+    assert O.decode(small_params, near, SMALL_CONFIG, clamp=False)[0, 0, t] != base[t]
+
+
+def test_decode_window_equals_full_decode(small_params):
+    z = synth.make_latents(2, 100, seed=7, channels=4)
+    full = O.decode(small_params, z, SMALL_CONFIG, clamp=False)
+    for n0, n1 in [(0, 3), (48, 52), (96, 100)]:
+        win = O.decode_window(small_params, z, n0, n1, config=SMALL_CONFIG, clamp=False)
+        np.testing.assert_allclose(win, full[:, :, 800 * n0:800 * n1], rtol=1e-6, atol=1e-6)
+
+
+def test_decode_reduces_to_conv_chain_without_amp(small_params):
+    # With every AMP conv weight and bias zeroed each block returns its
+    # input, so a stage is its transposed conv; the decoder is then a chain
+    # of textbook layers, composed here from torch library routines.
+    p = dict(small_params)
+    for name in p:
+        if ".resblocks." in name and (".convs" in name) and (name.endswith(".bias") or name.endswith("_g")):
+            p[name] = np.zeros_like(p[name])
+    cfg = dict(O.DEFAULT_CONFIG, **SMALL_CONFIG)
+    z = synth.make_latents(1, 3, seed=8, channels=4)
+    got = O.decode(p, z, SMALL_CONFIG, clamp=False)[0]
+
+    def T(a):
+        return torch.tensor(np.asarray(a), dtype=F64)
+
+    def wn(pref):
+        return torch._weight_norm(T(p[pref + ".weight_v"]), T(p[pref + ".weight_g"]), 0)
+
+    h = F.conv1d(T(z), T(p["dec_in_proj.weight"]), T(p["dec_in_proj.bias"]))
+    h = F.conv1d(h, wn("decoder.conv_pre"), T(p["decoder.conv_pre.bias"]), padding=3)
+    for s, (r, k) in enumerate(zip(cfg["decoder_rates"], cfg["decoder_kernel_sizes"])):
+        h = F.conv_transpose1d(h, wn(f"decoder.ups.{s}.0"), T(p[f"decoder.ups.{s}.0.bias"]), stride=r,
+                               padding=(k - r) // 2)
+    c = h.shape[1]
+    f = T(FILT).view(1, 1, -1).expand(c, 1, 12).contiguous()
+    u = 2 * F.conv_transpose1d(F.pad(h, (5, 5), mode="replicate"), f, stride=2, groups=c)[..., 15:-15]
+    a = T(p["decoder.activation_post.act.alpha"]).view(1, -1, 1)
+    b = T(p["decoder.activation_post.act.beta"]).view(1, -1, 1)
+    u = u + torch.sin(a * u) ** 2 / b
+    h = F.conv1d(F.pad(u, (5, 6), mode="replicate"), f, stride=2, groups=c)
+    ref = F.conv1d(h, wn("decoder.conv_post"), T(p["decoder.conv_post.bias"]), padding=3)[0].numpy()
+    assert rel_l2(got, ref) < 1e-5
+
+
+def test_denormalization_is_per_channel_affine(small_params):
+    z = synth.make_latents(1, 4, seed=9, channels=4)
+    mean = np.array([0.1, -0.2, 0.05, 0.0], dtype=np.float32)
+    std = np.array([0.5, 2.0, 1.0, 1.5], dtype=np.float32)
+    a = O.decode(small_params, z, SMALL_CONFIG, denormalize=True, latents_mean=mean, latents_std=std, clamp=False)
+    zz = (z.astype(np.float64) * std[None, :, None] + mean[None, :, None]).astype(np.float32)
+    np.testing.assert_array_equal(a, O.decode(small_params, zz, SMALL_CONFIG, clamp=False))
+
+
+def test_zero_resblocks_rejected(small_params):
+    with pytest.raises(RuntimeError):
+        O.stage_amp(np.zeros((64, 5), dtype=np.float32), small_params, 0, dict(SMALL_CONFIG, resblock_kernel_sizes=()))
+
+
+def torch_act(x, alpha, beta):
+    c = x.shape[1]
+    f = torch.tensor(FILT, dtype=F64).view(1, 1, -1).expand(c, 1, 12).contiguous()
+    u = 2 * F.conv_transpose1d(F.pad(x, (5, 5), mode="replicate"), f, stride=2, groups=c)[..., 15:-15]
+    u = u + torch.sin(alpha.view(1, -1, 1) * u) ** 2 / beta.view(1, -1, 1)
+    return F.conv1d(F.pad(u, (5, 6), mode="replicate"), f, stride=2, groups=c)
+
+
+@pytest.mark.parametrize("block", [0, 1, 2])
+def test_amp_stage_matches_torch_composition(small_params, block):
+    # The AMP set of stage 3 (8 channels in the narrow decoder) against the
+    # same reading composed from torch's dilated conv1d and grouped
+    # resampling convs: per dilation d, x + conv_{k,1}(act(conv_{k,d}(act(x)))).
+    p = small_params
+    stage = 3
+    x = synth.make_signal((8, 37), seed=11)
+    kernels = (3, 7, 11)
+
+    def T(a):
+        return torch.tensor(np.asarray(a), dtype=F64)
+
+    outs = []
+    for j, k in enumerate(kernels):
+        pre = f"decoder.resblocks.{3 * stage + j}"
+        h = T(x[None])
+        for n, d in enumerate((1, 3, 5)):
+            w1 = torch._weight_norm(T(p[f"{pre}.convs1.{n}.weight_v"]), T(p[f"{pre}.convs1.{n}.weight_g"]), 0)
+            w2 = torch._weight_norm(T(p[f"{pre}.convs2.{n}.weight_v"]), T(p[f"{pre}.convs2.{n}.weight_g"]), 0)
+            t = torch_act(h, T(p[f"{pre}.activations.{2 * n}.act.alpha"]), T(p[f"{pre}.activations.{2 * n}.act.beta"]))
+            t = F.conv1d(t, w1, T(p[f"{pre}.convs1.{n}.bias"]), padding=d * (k - 1) // 2, dilation=d)
+            t = torch_act(t, T(p[f"{pre}.activations.{2 * n + 1}.act.alpha"]),
+                          T(p[f"{pre}.activations.{2 * n + 1}.act.beta"]))
+            t = F.conv1d(t, w2, T(p[f"{pre}.convs2.{n}.bias"]), padding=(k - 1) // 2)
+            h = h + t
+        outs.append(h[0].numpy())
+        if j == block:
+            got = O.amp_block(x, p, pre, k, (1, 3, 5), FILT)
+            assert rel_l2(got, outs[-1]) < 1e-6
+    if block == 2:
+        got = O.stage_amp(x, p, stage, SMALL_CONFIG)
+        assert rel_l2(got, sum(outs) / 3) < 1e-6
