@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Benchmark of the BigVGAN decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+A step is one full decode (dec_in_proj -> conv_pre -> 7 x (transposed conv
++ averaged AMP blocks) -> activation_post + conv_post + clamp) of one batch
+of seeded synthetic latents already resident in HBM. Prints one JSON line.
+
+The metric is decoded audio-seconds per second: B * N / 40 / seconds per
+step (40 latents per second of 32 kHz audio). The default workload is two
+30 s items (B=2, N=1200) with the default MiniMax-H3 decoder and seeded
+random weights. `roofline` covers the dominant kernel, the act-fused AMP
+convolution, whose kernel durations come from HIP events the library
+records on the decode stream around every launch during the timed steps.
+`cpu_baseline` times the CPU oracle on a bounded sample (the first 80
+latents of one item, decoded in full).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix, published
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+LATENTS_PER_SECOND = 40         # 32 kHz / hop 800
+
+WORKLOADS = {
+    # name: (batch, frames, flags, description)
+    "c1": (1, 4, 0, "B=1 x N=4 latents (0.1 s)"),
+    "c2": (2, 200, 1, "B=2 x N=200 latents (5 s/item), de-normalized latents"),
+    "c3": (2, 1200, 0, "B=2 x N=1200 latents (30 s/item)"),
+    "c5": (16, 401, 0, "B=16 x N=401 latents (10.025 s/item)"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--bf16", action="store_true", help="bf16-split matrix-core operands (MH3A_FLAG_BF16_MFMA)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-latents", type=int, default=80, help="latents in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(params, n_latents):
+    """The oracle, as it stands, on the first n latents of item 0 of the
+    workload (a full decode of that short clip)."""
+    import numpy as np
+    import oracle as O
+    from neural_audio_vae_amd import synth
+    try:
+        import threadpoolctl
+        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    z = synth.make_latents(2, 1200)[:1, :, :n_latents]
+    t0 = time.perf_counter()
+    y = O.decode(params, np.ascontiguousarray(z))
+    dt = time.perf_counter() - t0
+    assert y.shape == (1, 1, 800 * n_latents)
+    return {
+        "value": (n_latents / LATENTS_PER_SECOND) / dt,
+        "unit": "audio-s/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"full oracle decode of latents [0, {n_latents}) of item 0 "
+                  f"({n_latents / LATENTS_PER_SECOND:.1f} s of audio) in {dt:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the decode path runs on a single GPU).", file=sys.stderr)
+        return 2
+    import torch
+    from neural_audio_vae_amd import Decoder, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+    batch, frames, flags, desc = WORKLOADS[args.workload]
+    if args.bf16:
+        flags |= 0x2
+    params = synth.make_params()
+    mean, std = synth.make_denorm()
+    dec = Decoder(params, latents_mean=mean, latents_std=std)
+    z = torch.from_numpy(synth.make_latents(batch, frames)).cuda()
+    out = torch.empty((batch, 1, 800 * frames), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        dec.decode(z, flags=flags, out=out, stream=stream)
+    torch.cuda.synchronize()
+
+    dec.timing(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        dec.decode(z, flags=flags, out=out, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(stop)
+    kernels = dec.timing_read()
+    dec.timing(False)
+
+    ms_step = ms_total / args.steps
+    audio_s = batch * frames / LATENTS_PER_SECOND
+    value = audio_s / (ms_step / 1e3)
+    amp = kernels.get("amp_act_conv", {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+    achieved = amp["flops"] / (amp["ms"] / 1e3) / 1e12 if amp["ms"] > 0 else 0.0
+    per_step = {
+        name: {
+            "launches_per_step": k["launches"] / args.steps,
+            "ms_per_step": round(k["ms"] / args.steps, 4),
+            "tflops": round(k["flops"] / (k["ms"] / 1e3) / 1e12, 2) if k["ms"] > 0 else None,
+            "gbs_compulsory": round(k["bytes"] / (k["ms"] / 1e3) / 1e9, 1) if k["ms"] > 0 else None,
+        }
+        for name, k in kernels.items()
+    }
+    total_flops = sum(k["flops"] for k in kernels.values()) / args.steps
+    line = {
+        "metric": "decoded audio-sec/s (B=2, 30 s clips, fp32)" if args.workload == "c3" else
+                  f"decoded audio-sec/s ({args.workload})",
+        "value": round(value, 2),
+        "unit": "audio-s/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16x3" if args.bf16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"BigVGAN decode of the MiniMax-H3 audio VAE, {desc}, default decoder "
+                        "(32->2048 proj, conv_pre 2048->1024, 7 upsampling stages 1024->8 ch, AMP k 3/7/11 "
+                        "d 1/3/5), seeded random weights, 32 kHz mono output",
+            "batch": batch,
+            "frames": frames,
+            "samples_per_item": 800 * frames,
+            "flags": flags,
+        },
+        "algorithmic_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
+        "roofline": {
+            "kernel": "conv_kernel (AMP dilated conv with fused anti-aliased SnakeBeta)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": FP32_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "launches_per_step": amp["launches"] / args.steps,
+            "avg_launch_us": round(1e3 * amp["ms"] / max(1, amp["launches"]), 2),
+            "flops_per_launch": amp["flops"] / max(1, amp["launches"]),
+        },
+        "kernels": per_step,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(params, args.cpu_latents)
+    print(json.dumps(line), flush=True)
+    dec.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

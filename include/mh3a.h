@@ -1,0 +1,220 @@
+/*
+ * mh3a -- MiniMax-H3 audio-VAE BigVGAN decoder on AMD MI355X (gfx950).
+ *
+ * C ABI of the decode path: de-normalized latents (B, latent_channels, N)
+ * in, mono waveform (B, 1, hop * N) out, clamped to [-1, 1].
+ *
+ * Sources of what is computed (the decode contract and its layers):
+ *   diffusers docs "AutoencoderKLMiniMaxH3Audio", section "decode": latents
+ *     [batch, latent_channels, num_frames] -> waveform [batch, 1,
+ *     num_frames * 800] clamped to [-1, 1]; stereo is two batch items.
+ *   same page, class signature: the constructor defaults that
+ *     mh3a_config_default() reproduces.
+ *   FastVideo API docs "minimax_h3_audio_vae", MLXMiniMaxH3AudioVAE.decode:
+ *     dec_in_proj (1x1) -> weight-normalized conv_pre (pad 3) -> per stage a
+ *     weight-normalized ConvTranspose1d (stride r, padding (k - r) // 2) and
+ *     the average of the AMP residual blocks -> activation_post ->
+ *     weight-normalized conv_post (pad 3, optional bias) -> clip to [-1, 1].
+ *   same page, module overview: AMP blocks with SnakeBeta behind alias-free
+ *     Kaiser-window 2x up/down sampling; kaiser_sinc_filter1d designs the
+ *     low-pass (released filter buffers take precedence when present).
+ *   same page, mlx_h3_audio_vae_from_file: missing required tensors are an
+ *     error (dec_in_proj.weight, decoder.conv_pre.weight_v,
+ *     decoder.conv_post.weight_v).
+ *
+ * Conventions
+ *   - All tensors are float32, C-contiguous, time fastest: (B, C, L).
+ *   - Host pointers are read only during the call that receives them.
+ *   - Device pointers are borrowed: the library never frees them.
+ *   - Every entry point returns MH3A_OK (0) or a negative MH3A_E_* code and
+ *     then sets a thread-local message readable with mh3a_last_error().
+ *   - Argument, shape and configuration checks all run before the first
+ *     HIP call, so they behave the same on a machine without a GPU.
+ *   - mh3a_decode and the other device entry points only enqueue work on
+ *     the given stream (hipStream_t passed as void*, NULL = the null
+ *     stream); they never synchronize. A device fault surfaces at the
+ *     caller's next synchronization of that stream.
+ */
+#ifndef MH3A_H_
+#define MH3A_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define MH3A_OK 0
+#define MH3A_E_INVALID_ARG (-1)    /* null pointer, bad size, unknown flag     */
+#define MH3A_E_MISSING_TENSOR (-2) /* a required parameter is absent           */
+#define MH3A_E_SHAPE (-3)          /* a parameter has the wrong shape          */
+#define MH3A_E_CONFIG (-4)         /* inconsistent architecture configuration  */
+#define MH3A_E_WORKSPACE (-5)      /* workspace too small or misaligned        */
+#define MH3A_E_HIP (-6)            /* a HIP runtime call failed                */
+#define MH3A_E_NOMEM (-7)          /* host allocation failed                   */
+
+/* ---- decode flags ---- */
+/* Apply z * latents_std[c] + latents_mean[c] before dec_in_proj (the
+ * per-channel convention of the diffusers "AutoencoderKLMiniMaxH3" page).
+ * The affine map is folded into dec_in_proj at create time. */
+#define MH3A_FLAG_DENORMALIZE 0x1u
+/* Feed the AMP convs to the matrix cores as bfloat16 operands, each fp32
+ * operand split into a bf16 head and a bf16 tail, summing head*head +
+ * tail*head + head*tail with fp32 accumulation; storage stays fp32. */
+#define MH3A_FLAG_BF16_MFMA 0x2u
+/* Skip the final clamp (a test hook: most samples saturate under random
+ * weights, so the unclamped signal is the sharper comparison). */
+#define MH3A_FLAG_NO_CLAMP 0x4u
+#define MH3A_FLAG_ALL 0x7u
+
+/* ---- architecture limits ---- */
+#define MH3A_MAX_STAGES 8
+#define MH3A_MAX_RESBLOCKS 4
+#define MH3A_MAX_DILATIONS 4
+
+typedef struct mh3a_decoder mh3a_decoder; /* opaque, immutable after create */
+
+/* One named host parameter array (float32, C-contiguous). */
+typedef struct {
+    const char* name;
+    const float* data;
+    int ndim;
+    int64_t shape[3];
+} mh3a_tensor;
+
+/* Architecture constants. Defaults: diffusers "AutoencoderKLMiniMaxH3Audio"
+ * constructor (latent_channels 32, latent_dim 2048, decoder_dim 1024,
+ * decoder_rates (5,5,2,2,2,2,2), decoder_kernel_sizes (9,9,4,4,4,4,4),
+ * resblock_kernel_sizes (3,7,11), dilations (1,3,5) for each block, hop
+ * 800); the resampler filter is 12 taps, cutoff 0.25, half-width 0.3. */
+typedef struct {
+    int latent_channels;
+    int latent_dim;
+    int decoder_dim;
+    int hop_length;                 /* product of rates must equal it */
+    int num_ups;
+    int rates[MH3A_MAX_STAGES];
+    int kernels[MH3A_MAX_STAGES];
+    int num_resblocks;
+    int rb_kernels[MH3A_MAX_RESBLOCKS];
+    int num_dilations;
+    int rb_dilations[MH3A_MAX_RESBLOCKS][MH3A_MAX_DILATIONS];
+    int filter_taps;                /* only 12 is supported */
+    double filter_cutoff;
+    double filter_half_width;
+} mh3a_config;
+
+/* Fill *cfg with the defaults above. */
+void mh3a_config_default(mh3a_config* cfg);
+
+/*
+ * Build a decoder on GPU `device` from host parameters.
+ *
+ * params/n_params: named arrays. Required names (C_s = decoder_dim / 2^(s+1),
+ * n = 3 s + j for stage s and block j, d = dilation index, m = 0..5):
+ *   dec_in_proj.weight (latent_dim, latent_channels, 1), dec_in_proj.bias
+ *   decoder.conv_pre.{weight_v (decoder_dim, latent_dim, 7), weight_g
+ *     (decoder_dim, 1, 1), bias}
+ *   decoder.ups.{s}.0.{weight_v (2 C_s, C_s, k_s), weight_g (2 C_s, 1, 1), bias}
+ *   decoder.resblocks.{n}.convs1.{d}.{weight_v (C_s, C_s, k_j), weight_g, bias}
+ *   decoder.resblocks.{n}.convs2.{d}.{...same...}
+ *   decoder.resblocks.{n}.activations.{m}.act.{alpha, beta} (C_s)
+ *   decoder.activation_post.act.{alpha, beta} (C_6)
+ *   decoder.conv_post.{weight_v (1, C_6, 7), weight_g (1, 1, 1)} [, bias (1)]
+ * Every weight_v/weight_g pair may instead be given as an already folded
+ * `weight`. Optional filters: `<act>.upsample.filter` and
+ * `<act>.downsample.lowpass.filter` (12 taps) replace the designed
+ * Kaiser-sinc low-pass for that activation. conv_post.bias is optional
+ * (absent means zero). Names not listed are ignored.
+ *
+ * Weight norm is folded once here: w = g * v / ||v||, the norm over every
+ * axis but axis 0 (C_out for conv, C_in for the transposed conv).
+ *
+ * latents_mean / latents_std: host arrays of latent_channels floats used by
+ * MH3A_FLAG_DENORMALIZE; NULL means 0 / 1.
+ *
+ * On success *out owns device copies of everything; the caller may free
+ * its host arrays at once. Errors: MH3A_E_INVALID_ARG, MH3A_E_CONFIG,
+ * MH3A_E_MISSING_TENSOR, MH3A_E_SHAPE, MH3A_E_HIP, MH3A_E_NOMEM; *out is
+ * then NULL.
+ */
+int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n_params,
+                        const float* latents_mean, const float* latents_std, int device,
+                        mh3a_decoder** out);
+
+/* Release the decoder's device memory (waits for the device first). NULL is
+ * a no-op. */
+void mh3a_destroy(mh3a_decoder* dec);
+
+/* Device workspace (bytes) that mh3a_decode needs for B items of N latents.
+ * Errors: MH3A_E_INVALID_ARG (null, B < 1, N < 1, unknown flags). */
+int mh3a_decode_workspace_size(const mh3a_decoder* dec, int64_t batch, int64_t frames, uint32_t flags,
+                               size_t* bytes);
+
+/*
+ * Decode. latents: device (B, latent_channels, N); wave: device (B, 1, hop N).
+ * workspace: device buffer of at least mh3a_decode_workspace_size bytes,
+ * 256-byte aligned; it holds the intermediate activations and is clobbered.
+ * The call enqueues every kernel on `stream` and returns; concurrent calls
+ * on one decoder need distinct workspaces. Errors: MH3A_E_INVALID_ARG,
+ * MH3A_E_WORKSPACE, MH3A_E_HIP.
+ */
+int mh3a_decode(mh3a_decoder* dec, const float* latents, int64_t batch, int64_t frames, float* wave,
+                void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * The decode, stopped after layer `upto`, with that layer's output copied
+ * to `out` (device). Layer numbering follows the decode order: 0 =
+ * dec_in_proj (B, latent_dim, N), 1 = conv_pre (B, decoder_dim, N), then for
+ * stage s: 2 + 2 s = its transposed conv, 3 + 2 s = its averaged AMP blocks
+ * (both (B, C_s, N * r_0 ... r_s)). mh3a_decode_layer_shape reports the
+ * shape. Same workspace as mh3a_decode. Used for per-layer checks.
+ */
+int mh3a_decode_layer_shape(const mh3a_decoder* dec, int64_t frames, int upto, int64_t* channels,
+                            int64_t* length);
+int mh3a_decode_partial(mh3a_decoder* dec, const float* latents, int64_t batch, int64_t frames, int upto,
+                        float* out, void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * One stage's AMP set alone (FastVideo "minimax_h3_audio_vae", decode: the
+ * blocks of stage s run from the same input and are averaged): x device
+ * (B, C_s, L) -> y device (B, C_s, L). Flags: 0 or MH3A_FLAG_BF16_MFMA.
+ * Workspace from mh3a_amp_stage_workspace_size.
+ */
+int mh3a_amp_stage_workspace_size(const mh3a_decoder* dec, int stage, int64_t batch, int64_t length,
+                                  size_t* bytes);
+int mh3a_amp_stage(mh3a_decoder* dec, int stage, const float* x, int64_t batch, int64_t length, float* y,
+                   void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * Kernel timing (a measurement aid). While enabled, every launch a decode
+ * makes is bracketed by HIP events on the decode's stream and tagged with
+ * its kernel class and the algorithmic work it does: FLOPs of the dense
+ * convolution (2 * C_out * C_in * k per output position, the transposed
+ * conv counted at its k taps per input sample) and compulsory HBM bytes
+ * (input, output, residual / running-sum reads, weights). mh3a_timing_read
+ * waits for the recorded events, returns per-class totals in recording
+ * order of first use and clears them. Enabling or disabling also clears.
+ * Not thread-safe: one decode stream per decoder while enabled.
+ */
+typedef struct {
+    char name[32];
+    int64_t launches;
+    double ms;
+    double flops;
+    double bytes;
+} mh3a_kernel_stats;
+#define MH3A_MAX_KERNEL_KINDS 8
+int mh3a_timing_enable(mh3a_decoder* dec, int enable);
+int mh3a_timing_read(mh3a_decoder* dec, mh3a_kernel_stats* stats, int max_stats, int* n_stats);
+
+/* Message of the calling thread's last failure ("" if none). */
+const char* mh3a_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MH3A_H_ */

@@ -1,0 +1,267 @@
+"""ctypes binding of the mh3a C ABI (include/mh3a.h).
+
+Argument marshalling only: every function here has the name of the C entry
+point it calls and does no computation of its own. The library is the
+in-tree libmh3a.so; if it is missing, load() raises -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, byref, c_char_p, c_double, c_int, c_int64, c_size_t, c_uint32, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmh3a.so")
+
+MH3A_OK = 0
+MH3A_E_INVALID_ARG = -1
+MH3A_E_MISSING_TENSOR = -2
+MH3A_E_SHAPE = -3
+MH3A_E_CONFIG = -4
+MH3A_E_WORKSPACE = -5
+MH3A_E_HIP = -6
+MH3A_E_NOMEM = -7
+
+MH3A_FLAG_DENORMALIZE = 0x1
+MH3A_FLAG_BF16_MFMA = 0x2
+MH3A_FLAG_NO_CLAMP = 0x4
+
+MH3A_MAX_STAGES = 8
+MH3A_MAX_RESBLOCKS = 4
+MH3A_MAX_DILATIONS = 4
+
+EXPORTED = (
+    "mh3a_config_default",
+    "mh3a_decoder_create",
+    "mh3a_destroy",
+    "mh3a_decode_workspace_size",
+    "mh3a_decode",
+    "mh3a_decode_layer_shape",
+    "mh3a_decode_partial",
+    "mh3a_amp_stage_workspace_size",
+    "mh3a_amp_stage",
+    "mh3a_timing_enable",
+    "mh3a_timing_read",
+    "mh3a_last_error",
+)
+
+
+class mh3a_tensor(Structure):
+    _fields_ = [("name", c_char_p), ("data", c_void_p), ("ndim", c_int), ("shape", c_int64 * 3)]
+
+
+class mh3a_config(Structure):
+    _fields_ = [
+        ("latent_channels", c_int),
+        ("latent_dim", c_int),
+        ("decoder_dim", c_int),
+        ("hop_length", c_int),
+        ("num_ups", c_int),
+        ("rates", c_int * MH3A_MAX_STAGES),
+        ("kernels", c_int * MH3A_MAX_STAGES),
+        ("num_resblocks", c_int),
+        ("rb_kernels", c_int * MH3A_MAX_RESBLOCKS),
+        ("num_dilations", c_int),
+        ("rb_dilations", (c_int * MH3A_MAX_DILATIONS) * MH3A_MAX_RESBLOCKS),
+        ("filter_taps", c_int),
+        ("filter_cutoff", c_double),
+        ("filter_half_width", c_double),
+    ]
+
+
+class mh3a_kernel_stats(Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", c_int64), ("ms", c_double), ("flops", c_double),
+                ("bytes", c_double)]
+
+
+MH3A_MAX_KERNEL_KINDS = 8
+
+
+class MH3AError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"mh3a error {code}: {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def load():
+    """Load libmh3a.so (built by neural_audio_vae_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m neural_audio_vae_amd.build` "
+                           "(the decoder has no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.mh3a_config_default.argtypes = [POINTER(mh3a_config)]
+    lib.mh3a_config_default.restype = None
+    lib.mh3a_decoder_create.argtypes = [POINTER(mh3a_config), POINTER(mh3a_tensor), c_int, c_void_p, c_void_p, c_int,
+                                        POINTER(c_void_p)]
+    lib.mh3a_decoder_create.restype = c_int
+    lib.mh3a_destroy.argtypes = [c_void_p]
+    lib.mh3a_destroy.restype = None
+    lib.mh3a_decode_workspace_size.argtypes = [c_void_p, c_int64, c_int64, c_uint32, POINTER(c_size_t)]
+    lib.mh3a_decode_workspace_size.restype = c_int
+    lib.mh3a_decode.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_uint32, c_void_p]
+    lib.mh3a_decode.restype = c_int
+    lib.mh3a_decode_layer_shape.argtypes = [c_void_p, c_int64, c_int, POINTER(c_int64), POINTER(c_int64)]
+    lib.mh3a_decode_layer_shape.restype = c_int
+    lib.mh3a_decode_partial.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_int, c_void_p, c_void_p, c_size_t,
+                                        c_uint32, c_void_p]
+    lib.mh3a_decode_partial.restype = c_int
+    lib.mh3a_amp_stage_workspace_size.argtypes = [c_void_p, c_int, c_int64, c_int64, POINTER(c_size_t)]
+    lib.mh3a_amp_stage_workspace_size.restype = c_int
+    lib.mh3a_amp_stage.argtypes = [c_void_p, c_int, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_uint32,
+                                   c_void_p]
+    lib.mh3a_amp_stage.restype = c_int
+    lib.mh3a_timing_enable.argtypes = [c_void_p, c_int]
+    lib.mh3a_timing_enable.restype = c_int
+    lib.mh3a_timing_read.argtypes = [c_void_p, POINTER(mh3a_kernel_stats), c_int, POINTER(c_int)]
+    lib.mh3a_timing_read.restype = c_int
+    lib.mh3a_last_error.argtypes = []
+    lib.mh3a_last_error.restype = c_char_p
+    _lib = lib
+    return lib
+
+
+def mh3a_last_error():
+    return load().mh3a_last_error().decode()
+
+
+def _check(rc):
+    if rc != MH3A_OK:
+        raise MH3AError(rc, mh3a_last_error())
+    return rc
+
+
+def mh3a_config_default():
+    cfg = mh3a_config()
+    load().mh3a_config_default(byref(cfg))
+    return cfg
+
+
+def make_config(overrides=None):
+    """An mh3a_config from the defaults plus overrides given with the
+    constructor's keyword names (decoder_rates, resblock_kernel_sizes, ...)."""
+    cfg = mh3a_config_default()
+    o = dict(overrides or {})
+    for key in ("latent_channels", "latent_dim", "decoder_dim", "hop_length", "filter_taps"):
+        if key in o:
+            setattr(cfg, key, int(o[key]))
+    for key in ("filter_cutoff", "filter_half_width"):
+        if key in o:
+            setattr(cfg, key, float(o[key]))
+    if "decoder_rates" in o or "decoder_kernel_sizes" in o:
+        rates = list(o.get("decoder_rates", cfg.rates[:cfg.num_ups]))
+        kernels = list(o.get("decoder_kernel_sizes", cfg.kernels[:cfg.num_ups]))
+        if len(rates) != len(kernels) or len(rates) > MH3A_MAX_STAGES:
+            raise ValueError("decoder_rates and decoder_kernel_sizes must have equal length <= 8")
+        cfg.num_ups = len(rates)
+        for i in range(MH3A_MAX_STAGES):
+            cfg.rates[i] = rates[i] if i < len(rates) else 0
+            cfg.kernels[i] = kernels[i] if i < len(kernels) else 0
+        if "hop_length" not in o:
+            hop = 1
+            for r in rates:
+                hop *= int(r)
+            cfg.hop_length = hop
+    if "resblock_kernel_sizes" in o or "resblock_dilation_sizes" in o:
+        ks = list(o.get("resblock_kernel_sizes", cfg.rb_kernels[:cfg.num_resblocks]))
+        dils = o.get("resblock_dilation_sizes", [list(cfg.rb_dilations[j][:cfg.num_dilations]) for j in range(len(ks))])
+        if len(ks) > MH3A_MAX_RESBLOCKS:
+            raise ValueError("too many residual blocks")
+        cfg.num_resblocks = len(ks)
+        nd = len(dils[0]) if len(dils) else 0
+        if any(len(d) != nd for d in dils) or nd > MH3A_MAX_DILATIONS:
+            raise ValueError("every block needs the same number (<= 4) of dilations")
+        cfg.num_dilations = nd
+        for j in range(MH3A_MAX_RESBLOCKS):
+            cfg.rb_kernels[j] = ks[j] if j < len(ks) else 0
+            for n in range(MH3A_MAX_DILATIONS):
+                cfg.rb_dilations[j][n] = dils[j][n] if (j < len(dils) and n < nd) else 0
+    return cfg
+
+
+def mh3a_decoder_create(config, arrays, latents_mean=None, latents_std=None, device=0):
+    """config: mh3a_config; arrays: dict name -> C-contiguous float32 numpy
+    array (kept alive by the caller for the duration of the call)."""
+    import numpy as np
+
+    lib = load()
+    items = list(arrays.items())
+    table = (mh3a_tensor * max(1, len(items)))()
+    keep = []
+    for i, (name, arr) in enumerate(items):
+        a = np.ascontiguousarray(arr, dtype=np.float32)
+        keep.append(a)
+        if a.ndim < 1 or a.ndim > 3:
+            raise ValueError(f"{name}: ndim must be 1..3")
+        table[i].name = name.encode()
+        table[i].data = a.ctypes.data
+        table[i].ndim = a.ndim
+        for k in range(3):
+            table[i].shape[k] = a.shape[k] if k < a.ndim else 1
+    mean = std = None
+    if latents_mean is not None:
+        mean = np.ascontiguousarray(latents_mean, dtype=np.float32)
+        keep.append(mean)
+    if latents_std is not None:
+        std = np.ascontiguousarray(latents_std, dtype=np.float32)
+        keep.append(std)
+    handle = c_void_p()
+    _check(lib.mh3a_decoder_create(byref(config), table, len(items), mean.ctypes.data if mean is not None else None,
+                                   std.ctypes.data if std is not None else None, int(device), byref(handle)))
+    return handle.value
+
+
+def mh3a_destroy(handle):
+    load().mh3a_destroy(handle)
+
+
+def mh3a_decode_workspace_size(handle, batch, frames, flags=0):
+    n = c_size_t()
+    _check(load().mh3a_decode_workspace_size(handle, batch, frames, flags, byref(n)))
+    return n.value
+
+
+def mh3a_decode(handle, latents_ptr, batch, frames, wave_ptr, workspace_ptr, workspace_bytes, flags, stream):
+    return _check(load().mh3a_decode(handle, latents_ptr, batch, frames, wave_ptr, workspace_ptr, workspace_bytes,
+                                     flags, stream))
+
+
+def mh3a_decode_layer_shape(handle, frames, upto):
+    c, n = c_int64(), c_int64()
+    _check(load().mh3a_decode_layer_shape(handle, frames, upto, byref(c), byref(n)))
+    return c.value, n.value
+
+
+def mh3a_decode_partial(handle, latents_ptr, batch, frames, upto, out_ptr, workspace_ptr, workspace_bytes, flags,
+                        stream):
+    return _check(load().mh3a_decode_partial(handle, latents_ptr, batch, frames, upto, out_ptr, workspace_ptr,
+                                             workspace_bytes, flags, stream))
+
+
+def mh3a_amp_stage_workspace_size(handle, stage, batch, length):
+    n = c_size_t()
+    _check(load().mh3a_amp_stage_workspace_size(handle, stage, batch, length, byref(n)))
+    return n.value
+
+
+def mh3a_amp_stage(handle, stage, x_ptr, batch, length, y_ptr, workspace_ptr, workspace_bytes, flags, stream):
+    return _check(load().mh3a_amp_stage(handle, stage, x_ptr, batch, length, y_ptr, workspace_ptr, workspace_bytes,
+                                        flags, stream))
+
+
+def mh3a_timing_enable(handle, enable):
+    return _check(load().mh3a_timing_enable(handle, 1 if enable else 0))
+
+
+def mh3a_timing_read(handle):
+    """Per kernel class: dict name -> {launches, ms, flops, bytes}."""
+    arr = (mh3a_kernel_stats * MH3A_MAX_KERNEL_KINDS)()
+    n = c_int()
+    _check(load().mh3a_timing_read(handle, arr, MH3A_MAX_KERNEL_KINDS, byref(n)))
+    return {arr[i].name.decode(): {"launches": arr[i].launches, "ms": arr[i].ms, "flops": arr[i].flops,
+                                   "bytes": arr[i].bytes} for i in range(n.value)}

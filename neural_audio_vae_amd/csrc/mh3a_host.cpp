@@ -1,0 +1,977 @@
+// Host side of the mh3a C ABI: argument validation, parameter lookup,
+// weight-norm folding, Kaiser-sinc filter design, weight packing for the
+// matrix-core kernels, workspace layout and the decode launch sequence.
+//
+// The decode order follows FastVideo API docs "minimax_h3_audio_vae",
+// MLXMiniMaxH3AudioVAE.decode; the interface contract follows diffusers docs
+// "AutoencoderKLMiniMaxH3Audio", section "decode".
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "mh3a.h"
+#include "mh3a_internal.h"
+
+using namespace mh3a;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return MH3A_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Kaiser-windowed sinc low-pass (FastVideo "minimax_h3_audio_vae",
+// kaiser_sinc_filter1d): the attenuation uses (K/2 - 1) and 4 * half_width
+// as released; window = I0(beta sqrt(1 - r^2)) / I0(beta); taps
+// 2 fc w[n] sinc(2 fc t_n) on a half-integer grid for even K, normalized to
+// unit sum. Evaluated in double.
+// ---------------------------------------------------------------------------
+double bessel_i0(double x) {
+    const double q = 0.25 * x * x;
+    double term = 1.0, sum = 1.0;
+    for (int m = 1; m < 500; ++m) {
+        term *= q / ((double)m * m);
+        sum += term;
+        if (term < 1e-17 * sum) break;
+    }
+    return sum;
+}
+
+void design_lowpass(double cutoff, double half_width, int k, float* out) {
+    const int half = k / 2;
+    const double atten = 2.285 * (half - 1) * M_PI * (4.0 * half_width) + 7.95;
+    double beta;
+    if (atten > 50.0)
+        beta = 0.1102 * (atten - 8.7);
+    else if (atten >= 21.0)
+        beta = 0.5842 * std::pow(atten - 21.0, 0.4) + 0.07886 * (atten - 21.0);
+    else
+        beta = 0.0;
+    std::vector<double> f(k);
+    double sum = 0.0;
+    const double i0b = bessel_i0(beta);
+    for (int n = 0; n < k; ++n) {
+        const double r = (k > 1) ? 2.0 * n / (k - 1) - 1.0 : 0.0;
+        const double w = bessel_i0(beta * std::sqrt(std::fmax(0.0, 1.0 - r * r))) / i0b;
+        const double t = (k % 2 == 0) ? (n - half + 0.5) : (double)(n - half);
+        const double x = 2.0 * cutoff * t;
+        const double sinc = (x == 0.0) ? 1.0 : std::sin(M_PI * x) / (M_PI * x);
+        f[n] = 2.0 * cutoff * w * sinc;
+        sum += f[n];
+    }
+    for (int n = 0; n < k; ++n) out[n] = (float)(f[n] / sum);
+}
+
+// ---------------------------------------------------------------------------
+// Parameter table
+// ---------------------------------------------------------------------------
+struct Param {
+    const float* data;
+    int ndim;
+    int64_t shape[3];
+    int64_t numel() const {
+        int64_t n = 1;
+        for (int i = 0; i < ndim; ++i) n *= shape[i];
+        return n;
+    }
+};
+
+struct Table {
+    std::map<std::string, Param> m;
+    const Param* get(const std::string& name) const {
+        auto it = m.find(name);
+        return it == m.end() ? nullptr : &it->second;
+    }
+};
+
+// Shape check ignoring leading/trailing singleton differences of 1-D
+// vectors: a (C,) and a (C, 1, 1) view are both accepted for vectors.
+bool shape_is(const Param* p, int64_t a, int64_t b = -1, int64_t c = -1) {
+    int64_t want[3] = {a, b, c};
+    int wn = c >= 0 ? 3 : (b >= 0 ? 2 : 1);
+    if (p->ndim == wn) {
+        for (int i = 0; i < wn; ++i)
+            if (p->shape[i] != want[i]) return false;
+        return true;
+    }
+    return false;
+}
+
+bool vector_of(const Param* p, int64_t n) {
+    if (p->numel() != n) return false;
+    int non1 = 0;
+    for (int i = 0; i < p->ndim; ++i)
+        if (p->shape[i] != 1) ++non1;
+    return non1 <= 1;
+}
+
+// ---------------------------------------------------------------------------
+// Decoder object
+// ---------------------------------------------------------------------------
+struct ConvLayer {
+    int c_in = 0, c_out = 0, taps = 1, dil = 1, phases = 1, out_mul = 1;
+    int in_off[kMaxPhases] = {0};
+    int out_add[kMaxPhases] = {0};
+    int64_t w_off = -1;
+    int64_t w_phase_stride = 0;
+    int64_t b_off = -1;
+    int act = -1;       // index into acts, -1 = none
+    int alg_taps = 1;   // taps per input sample the layer's definition uses
+    int kind = 0;       // timing class
+};
+
+enum Kind { KIND_IN_PROJ = 0, KIND_CONV_PRE, KIND_UPSAMPLE, KIND_AMP, KIND_FINAL, KIND_COUNT };
+const char* const kKindNames[KIND_COUNT] = {"dec_in_proj", "conv_pre", "ups_transposed_conv", "amp_act_conv",
+                                            "act_post_conv_post"};
+
+struct TimingRec {
+    int kind;
+    double flops, bytes;
+    int ev;  // index of the start event; ev + 1 is the stop event
+};
+
+struct Timing {
+    bool on = false;
+    std::vector<hipEvent_t> evs;
+    int used = 0;
+    std::vector<TimingRec> recs;
+};
+
+struct ActLayer {
+    int64_t taps_off = -1;
+    int64_t ab_off = -1;
+};
+
+}  // namespace
+
+struct mh3a_decoder {
+    mh3a_config cfg;
+    int device = 0;
+    float* blob = nullptr;
+    int64_t blob_floats = 0;
+    ConvLayer in_proj, in_proj_dn, conv_pre;
+    std::vector<ConvLayer> ups;                 // [num_ups]
+    std::vector<std::vector<ConvLayer>> amp;    // [stage][(block * ndil + d) * 2 + {0,1}]
+    std::vector<ActLayer> acts;
+    int post_act = -1;
+    int64_t post_w_off = -1;
+    float post_bias = 0.0f;
+    std::vector<int> stage_c;   // output channels per stage
+    mutable Timing timing;
+};
+
+namespace {
+
+struct Blob {
+    std::vector<float> h;
+    int64_t add(const float* src, int64_t n) {
+        int64_t off = (int64_t)h.size();
+        h.resize(off + ((n + 63) / 64) * 64, 0.0f);
+        if (src) std::memcpy(h.data() + off, src, sizeof(float) * n);
+        return off;
+    }
+    int64_t reserve(int64_t n) { return add(nullptr, n); }
+};
+
+int check_config(const mh3a_config* c) {
+    if (c->latent_channels < 1 || c->latent_dim < 1 || c->decoder_dim < 1)
+        return fail(MH3A_E_CONFIG, "channel counts must be positive");
+    if (c->num_ups < 1 || c->num_ups > MH3A_MAX_STAGES)
+        return fail(MH3A_E_CONFIG, "num_ups must be in [1, %d]", MH3A_MAX_STAGES);
+    long long prod = 1;
+    for (int s = 0; s < c->num_ups; ++s) {
+        if (c->rates[s] < 1 || c->rates[s] > kMaxPhases)
+            return fail(MH3A_E_CONFIG, "rate %d of stage %d out of range [1, %d]", c->rates[s], s, kMaxPhases);
+        if (c->kernels[s] < c->rates[s])
+            return fail(MH3A_E_CONFIG, "stage %d: kernel %d smaller than rate %d", s, c->kernels[s], c->rates[s]);
+        prod *= c->rates[s];
+    }
+    if (prod != c->hop_length)
+        return fail(MH3A_E_CONFIG, "product of decoder rates (%lld) must equal hop_length (%d)", prod, c->hop_length);
+    if ((c->decoder_dim >> c->num_ups) < 1 || (c->decoder_dim % (1 << c->num_ups)) != 0)
+        return fail(MH3A_E_CONFIG, "decoder_dim %d cannot be halved %d times", c->decoder_dim, c->num_ups);
+    if (c->num_resblocks < 1) return fail(MH3A_E_CONFIG, "decoder has no residual blocks");
+    if (c->num_resblocks > MH3A_MAX_RESBLOCKS) return fail(MH3A_E_CONFIG, "too many residual blocks");
+    if (c->num_dilations < 1 || c->num_dilations > MH3A_MAX_DILATIONS)
+        return fail(MH3A_E_CONFIG, "num_dilations must be in [1, %d]", MH3A_MAX_DILATIONS);
+    for (int j = 0; j < c->num_resblocks; ++j) {
+        if (c->rb_kernels[j] < 1 || c->rb_kernels[j] % 2 == 0 || c->rb_kernels[j] > 15)
+            return fail(MH3A_E_CONFIG, "residual-block kernel %d must be odd and <= 15", c->rb_kernels[j]);
+        for (int d = 0; d < c->num_dilations; ++d)
+            if (c->rb_dilations[j][d] < 1 || c->rb_dilations[j][d] > 16)
+                return fail(MH3A_E_CONFIG, "dilation %d out of range [1, 16]", c->rb_dilations[j][d]);
+    }
+    if (c->filter_taps != kTaps) return fail(MH3A_E_CONFIG, "only %d-tap resampling filters are supported", kTaps);
+    if (!(c->filter_cutoff > 0.0 && c->filter_cutoff < 0.5 && c->filter_half_width > 0.0))
+        return fail(MH3A_E_CONFIG, "bad filter cutoff / half width");
+    return MH3A_OK;
+}
+
+// Fold weight norm: w = g v / ||v|| per axis-0 slice of v (n0 slices of
+// `inner` elements). Accepts an already folded "<prefix>.weight" instead.
+int fetch_weight(const Table& t, const std::string& prefix, int64_t d0, int64_t d1, int64_t d2,
+                 std::vector<float>& w) {
+    const Param* wt = t.get(prefix + ".weight");
+    const Param* v = t.get(prefix + ".weight_v");
+    const Param* g = t.get(prefix + ".weight_g");
+    w.assign((size_t)(d0 * d1 * d2), 0.0f);
+    if (v) {
+        if (!g) return fail(MH3A_E_MISSING_TENSOR, "missing %s.weight_g", prefix.c_str());
+        if (!shape_is(v, d0, d1, d2))
+            return fail(MH3A_E_SHAPE, "%s.weight_v must be (%lld, %lld, %lld)", prefix.c_str(), (long long)d0,
+                        (long long)d1, (long long)d2);
+        if (!vector_of(g, d0)) return fail(MH3A_E_SHAPE, "%s.weight_g must hold %lld values", prefix.c_str(), (long long)d0);
+        const int64_t inner = d1 * d2;
+        for (int64_t o = 0; o < d0; ++o) {
+            double ss = 0.0;
+            for (int64_t i = 0; i < inner; ++i) {
+                const double x = v->data[o * inner + i];
+                ss += x * x;
+            }
+            const double s = (double)g->data[o] / std::sqrt(ss);
+            for (int64_t i = 0; i < inner; ++i) w[o * inner + i] = (float)(s * (double)v->data[o * inner + i]);
+        }
+        return MH3A_OK;
+    }
+    if (wt) {
+        if (!shape_is(wt, d0, d1, d2))
+            return fail(MH3A_E_SHAPE, "%s.weight must be (%lld, %lld, %lld)", prefix.c_str(), (long long)d0,
+                        (long long)d1, (long long)d2);
+        std::memcpy(w.data(), wt->data, sizeof(float) * w.size());
+        return MH3A_OK;
+    }
+    return fail(MH3A_E_MISSING_TENSOR, "missing %s.weight_v (or %s.weight)", prefix.c_str(), prefix.c_str());
+}
+
+int fetch_vector(const Table& t, const std::string& name, int64_t n, const float** out) {
+    const Param* p = t.get(name);
+    if (!p) return fail(MH3A_E_MISSING_TENSOR, "missing %s", name.c_str());
+    if (!vector_of(p, n)) return fail(MH3A_E_SHAPE, "%s must hold %lld values", name.c_str(), (long long)n);
+    *out = p->data;
+    return MH3A_OK;
+}
+
+// Upload a conv layer (c_out, c_in, taps) with its bias.
+void add_conv(Blob& blob, ConvLayer& L, const std::vector<float>& w, const float* bias, int c_out, int c_in,
+              int taps) {
+    L.c_in = c_in;
+    L.c_out = c_out;
+    L.taps = taps;
+    const int64_t n = packed_weight_floats(c_out, c_in, taps);
+    L.w_off = blob.reserve(n);
+    pack_conv_weights(w.data(), c_out, c_in, taps, blob.h.data() + L.w_off);
+    L.b_off = bias ? blob.add(bias, c_out) : -1;
+}
+
+int add_act(Blob& blob, const Table& t, const std::string& prefix, int c, const float* designed,
+            std::vector<ActLayer>& acts) {
+    const float *alpha, *beta;
+    int rc;
+    if ((rc = fetch_vector(t, prefix + ".act.alpha", c, &alpha))) return rc;
+    if ((rc = fetch_vector(t, prefix + ".act.beta", c, &beta))) return rc;
+    const float* up = designed;
+    const float* dn = designed;
+    if (const Param* p = t.get(prefix + ".upsample.filter")) {
+        if (!vector_of(p, kTaps)) return fail(MH3A_E_SHAPE, "%s.upsample.filter must hold %d taps", prefix.c_str(), kTaps);
+        up = p->data;
+    }
+    if (const Param* p = t.get(prefix + ".downsample.lowpass.filter")) {
+        if (!vector_of(p, kTaps))
+            return fail(MH3A_E_SHAPE, "%s.downsample.lowpass.filter must hold %d taps", prefix.c_str(), kTaps);
+        dn = p->data;
+    }
+    float taps[24];
+    for (int e = 0; e < 6; ++e) {
+        taps[e] = 2.0f * up[1 + 2 * e];  // even outputs: gain 2
+        taps[6 + e] = 2.0f * up[2 * e];  // odd outputs
+    }
+    for (int q = 0; q < 12; ++q) taps[12 + q] = dn[q];
+    std::vector<float> ab(2 * (size_t)c);
+    for (int i = 0; i < c; ++i) {
+        if (!(beta[i] != 0.0f)) return fail(MH3A_E_SHAPE, "%s.act.beta[%d] is zero", prefix.c_str(), i);
+        ab[2 * i] = (float)((double)alpha[i] / M_PI);
+        ab[2 * i + 1] = (float)(0.5 / (double)beta[i]);
+    }
+    ActLayer a;
+    a.taps_off = blob.add(taps, 24);
+    a.ab_off = blob.add(ab.data(), 2 * c);
+    acts.push_back(a);
+    return MH3A_OK;
+}
+
+ActParams act_params(const mh3a_decoder* d, int idx) {
+    ActParams p{nullptr, nullptr};
+    if (idx >= 0) {
+        p.taps = d->blob + d->acts[idx].taps_off;
+        p.ab = reinterpret_cast<const float2*>(d->blob + d->acts[idx].ab_off);
+    }
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// Tile choice: a cycle model of the wave-specialized conv kernel, fitted to
+// measured stage times. Per K-chunk of 8 channels a consumer wave issues
+// taps * 4 * MBW * NBW fp32 MFMAs of 64 cycles; the producer waves stage
+// the window (act: ~12 cycles per window position, plain copy: ~2). Wave
+// tiles of at most 64 x 64 outputs leave room for two workgroups per CU,
+// which hide each other's stalls (measured ~65% of MFMA peak, ~58% with
+// one workgroup per CU). A launch takes ceil(workgroups / slots) rounds.
+// ---------------------------------------------------------------------------
+struct TileGeom {
+    int mbw, nbw, wm, wn;
+};
+
+TileGeom tile_geom(TileId t) {
+    switch (t) {
+#define MH3A_TILE(id, mbw, nbw, wm, wn) \
+    case id: return {mbw, nbw, wm, wn};
+        MH3A_TILE_LIST
+#undef MH3A_TILE
+        default: return {1, 1, 1, 4};
+    }
+}
+
+double tile_cost(const ConvLayer& L, TileId id, int positions, int groups, bool bf16) {
+    const TileShape s = tile_shape(id);
+    const TileGeom g = tile_geom(id);
+    const bool act = L.act >= 0;
+    const int nch = (L.c_in + kChunk - 1) / kChunk;
+    const int W = s.n + (L.taps - 1) * L.dil;
+    const double mt = (L.c_out + s.m - 1) / s.m;
+    const double nt = (positions + s.n - 1) / s.n;
+    const double wgs = mt * nt * groups;
+    const int occ = (g.mbw * g.nbw <= 4) ? 2 : 1;
+    const double rounds = std::ceil(wgs / (256.0 * occ));
+    const double eff = occ == 2 ? 0.65 : 0.58;
+    const double t_cons = (double)L.taps * 4 * g.mbw * g.nbw * 64 * (act && bf16 ? 3 : 1) / eff;
+    const double t_prod = (act ? 12.0 : 2.0) * W + 400;
+    const double t_chunk = std::max(t_cons, t_prod) + 200;
+    const double t_epi = 16.0 * g.mbw * g.nbw * 40 + 2000;
+    return rounds * occ * (nch * t_chunk + t_epi);
+}
+
+// MH3A_CONV_TILE=<index into MH3A_TILE_LIST> forces one tile shape for
+// every conv launch whose LDS it fits (a tuning aid, read once).
+int forced_tile() {
+    static const int v = [] {
+        const char* e = std::getenv("MH3A_CONV_TILE");
+        if (!e || !*e) return -1;
+        const int t = std::atoi(e);
+        return (t >= 0 && t < TILE_COUNT) ? t : -1;
+    }();
+    return v;
+}
+
+TileId choose_tile(const ConvLayer& L, int positions, int groups, bool bf16) {
+    if (forced_tile() >= 0) {
+        const TileShape s = tile_shape((TileId)forced_tile());
+        const int W = s.n + (L.taps - 1) * L.dil;
+        const int lds_floats = 2 * kChunk * W + (L.act >= 0 ? kChunk * (3 * W + 24) : 0);
+        if (lds_floats * 4 <= 160 * 1024) return (TileId)forced_tile();
+    }
+    double best = 1e300;
+    TileId pick = TILE_32x256;
+    const bool act = L.act >= 0;
+    const int mpad = ((L.c_out + 31) / 32) * 32;
+    // With at most 32 output channels the activation producers bound the
+    // kernel; the narrowest window measured fastest.
+    if (act && L.c_out <= 32) return TILE_32x256;
+    for (int id = 0; id < TILE_COUNT; ++id) {
+        const TileShape s = tile_shape((TileId)id);
+        if (s.m > mpad && s.m > 32) continue;  // consumer waves would idle
+        const int W = s.n + (L.taps - 1) * L.dil;
+        const int lds_floats = 2 * kChunk * W + (act ? kChunk * (3 * W + 24) : 0);
+        if (lds_floats * 4 > 160 * 1024) continue;
+        const double cost = tile_cost(L, (TileId)id, positions, groups, bf16);
+        if (cost < best) {
+            best = cost;
+            pick = (TileId)id;
+        }
+    }
+    return pick;
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers
+// ---------------------------------------------------------------------------
+struct Buf {
+    float* p;
+    int64_t bstride;
+};
+
+// Brackets a launch with timing events when timing is enabled.
+struct TimedLaunch {
+    const mh3a_decoder* d;
+    hipStream_t st;
+    int ev = -1;
+    TimedLaunch(const mh3a_decoder* d_, hipStream_t st_) : d(d_), st(st_) {
+        Timing& t = d->timing;
+        if (!t.on) return;
+        while ((int)t.evs.size() < t.used + 2) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) return;
+            t.evs.push_back(e);
+        }
+        ev = t.used;
+        t.used += 2;
+        hipEventRecord(t.evs[ev], st);
+    }
+    void done(int kind, double flops, double bytes) {
+        if (ev < 0) return;
+        Timing& t = d->timing;
+        hipEventRecord(t.evs[ev + 1], st);
+        t.recs.push_back({kind, flops, bytes, ev});
+    }
+};
+
+hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, int64_t x_bstride, int l_in,
+                    int positions, float* y, int64_t y_bstride, int batch, const float* res, const float* sum_in,
+                    float scale, bool bf16, hipStream_t st) {
+    ConvArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = x;
+    a.x_bstride = x_bstride;
+    a.c_in = L.c_in;
+    a.l_in = l_in;
+    a.w = d->blob + L.w_off;
+    a.w_phase_stride = L.w_phase_stride;
+    a.bias = L.b_off >= 0 ? d->blob + L.b_off : nullptr;
+    a.y = y;
+    a.y_bstride = y_bstride;
+    a.c_out = L.c_out;
+    a.positions = positions;
+    a.taps = L.taps;
+    a.dil = L.dil;
+    a.out_mul = L.out_mul;
+    a.phases = L.phases;
+    for (int i = 0; i < kMaxPhases; ++i) {
+        a.in_off[i] = L.in_off[i];
+        a.out_add[i] = L.out_add[i];
+    }
+    a.res = res;
+    a.sum_in = sum_in;
+    a.scale = scale;
+    a.act = act_params(d, L.act);
+    a.bf16 = bf16 ? 1 : 0;
+    TimedLaunch tl(d, st);
+    hipError_t e = launch_conv(a, batch, choose_tile(L, positions, batch * L.phases, bf16), st);
+    const double outs = (double)batch * L.c_out * L.out_mul * positions;
+    const double flops = 2.0 * L.c_out * (double)L.c_in * L.alg_taps * positions * batch;
+    const double bytes = 4.0 * ((double)batch * L.c_in * l_in + outs * (1 + (res ? 1 : 0) + (sum_in ? 1 : 0)) +
+                                (double)L.c_out * L.c_in * L.alg_taps + L.c_out);
+    tl.done(L.kind, flops, bytes);
+    return e;
+}
+
+#define HIP_TRY(expr)                                                                              \
+    do {                                                                                           \
+        hipError_t e_ = (expr);                                                                    \
+        if (e_ != hipSuccess) return fail(MH3A_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+int64_t max_cl(const mh3a_decoder* d, int64_t frames) {
+    const mh3a_config& c = d->cfg;
+    int64_t m = std::max<int64_t>((int64_t)c.latent_dim * frames, (int64_t)c.decoder_dim * frames);
+    int64_t len = frames;
+    for (int s = 0; s < c.num_ups; ++s) {
+        len *= c.rates[s];
+        m = std::max<int64_t>(m, (int64_t)d->stage_c[s] * len);
+    }
+    return m;
+}
+
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// AMP set of one stage: h (B, C, L) read-only; x_buf, t_buf scratch;
+// result in s_buf. Blocks run from the same h and are averaged in the
+// epilogue of each block's last conv.
+int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, float* t_buf, float* s_buf, int batch,
+            int64_t len, bool bf16, hipStream_t st) {
+    const mh3a_config& c = d->cfg;
+    const int C = d->stage_c[stage];
+    const int64_t bs = (int64_t)C * len;
+    const int nrb = c.num_resblocks, nd = c.num_dilations;
+    const int L = (int)len;
+    for (int j = 0; j < nrb; ++j) {
+        for (int n = 0; n < nd; ++n) {
+            const ConvLayer& c1 = d->amp[stage][(j * nd + n) * 2 + 0];
+            const ConvLayer& c2 = d->amp[stage][(j * nd + n) * 2 + 1];
+            const float* xin = (n == 0) ? h : x_buf;
+            HIP_TRY(run_conv(d, c1, xin, bs, L, L, t_buf, bs, batch, nullptr, nullptr, 1.0f, bf16, st));
+            const bool last = (n == nd - 1);
+            float* yout = last ? s_buf : x_buf;
+            const float* sum_in = (last && j > 0) ? s_buf : nullptr;
+            const float scale = (last && j == nrb - 1) ? 1.0f / (float)nrb : 1.0f;
+            HIP_TRY(run_conv(d, c2, t_buf, bs, L, L, yout, bs, batch, xin, sum_in, scale, bf16, st));
+        }
+    }
+    return MH3A_OK;
+}
+
+int check_decode_args(const mh3a_decoder* d, int64_t batch, int64_t frames, uint32_t flags) {
+    if (!d) return fail(MH3A_E_INVALID_ARG, "decoder is null");
+    if (batch < 1 || batch > 4096) return fail(MH3A_E_INVALID_ARG, "batch must be in [1, 4096]");
+    if (frames < 1) return fail(MH3A_E_INVALID_ARG, "frames must be >= 1");
+    if (flags & ~MH3A_FLAG_ALL) return fail(MH3A_E_INVALID_ARG, "unknown flags 0x%x", flags & ~MH3A_FLAG_ALL);
+    // every per-item length must fit the kernels' 32-bit positions
+    if ((int64_t)d->cfg.hop_length * frames > (int64_t)1 << 30)
+        return fail(MH3A_E_INVALID_ARG, "frames too large: %lld output samples per item", (long long)(d->cfg.hop_length * frames));
+    if (max_cl(d, frames) * batch > ((int64_t)1 << 40)) return fail(MH3A_E_INVALID_ARG, "problem too large");
+    return MH3A_OK;
+}
+
+size_t decode_ws_bytes(const mh3a_decoder* d, int64_t batch, int64_t frames) {
+    return (size_t)(4 * round_up(max_cl(d, frames) * batch, 64) * (int64_t)sizeof(float));
+}
+
+int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, float* wave, int upto,
+               float* out, void* ws, size_t ws_bytes, uint32_t flags, hipStream_t st) {
+    int rc = check_decode_args(d, batch, frames, flags);
+    if (rc) return rc;
+    if (!z || (!wave && !out)) return fail(MH3A_E_INVALID_ARG, "null latents or output pointer");
+    if (!ws) return fail(MH3A_E_WORKSPACE, "workspace is null");
+    if ((uintptr_t)ws % 256) return fail(MH3A_E_WORKSPACE, "workspace must be 256-byte aligned");
+    const size_t need = decode_ws_bytes(d, batch, frames);
+    if (ws_bytes < need) return fail(MH3A_E_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    const mh3a_config& c = d->cfg;
+    const int B = (int)batch;
+    const int N = (int)frames;
+    const int64_t slot = round_up(max_cl(d, frames) * batch, 64);
+    float* bufS = static_cast<float*>(ws);
+    float* bufH = bufS + slot;
+    float* bufX = bufH + slot;
+    float* bufT = bufX + slot;
+    const bool bf16 = (flags & MH3A_FLAG_BF16_MFMA) != 0;
+    HIP_TRY(hipSetDevice(d->device));
+
+    auto finish = [&](const float* src, int64_t count) -> int {
+        HIP_TRY(hipMemcpyAsync(out, src, sizeof(float) * count, hipMemcpyDeviceToDevice, st));
+        return ok();
+    };
+
+    const ConvLayer& inp = (flags & MH3A_FLAG_DENORMALIZE) ? d->in_proj_dn : d->in_proj;
+    const int64_t zb = (int64_t)c.latent_channels * N;
+    HIP_TRY(run_conv(d, inp, z, zb, N, N, bufX, (int64_t)c.latent_dim * N, B, nullptr, nullptr, 1.0f, false, st));
+    if (upto == 0) return finish(bufX, (int64_t)B * c.latent_dim * N);
+    HIP_TRY(run_conv(d, d->conv_pre, bufX, (int64_t)c.latent_dim * N, N, N, bufS, (int64_t)c.decoder_dim * N, B,
+                     nullptr, nullptr, 1.0f, false, st));
+    if (upto == 1) return finish(bufS, (int64_t)B * c.decoder_dim * N);
+    int64_t len = N;
+    int cin = c.decoder_dim;
+    for (int s = 0; s < c.num_ups; ++s) {
+        const int C = d->stage_c[s];
+        const int64_t lout = len * c.rates[s];
+        HIP_TRY(run_conv(d, d->ups[s], bufS, (int64_t)cin * len, (int)len, (int)len, bufH, (int64_t)C * lout, B,
+                         nullptr, nullptr, 1.0f, false, st));
+        if (upto == 2 + 2 * s) return finish(bufH, (int64_t)B * C * lout);
+        rc = run_amp(d, s, bufH, bufX, bufT, bufS, B, lout, bf16, st);
+        if (rc) return rc;
+        if (upto == 3 + 2 * s) return finish(bufS, (int64_t)B * C * lout);
+        len = lout;
+        cin = C;
+    }
+    FinalArgs fa;
+    fa.x = bufS;
+    fa.x_bstride = (int64_t)cin * len;
+    fa.c = cin;
+    fa.l = (int)len;
+    fa.act = act_params(d, d->post_act);
+    fa.w = d->blob + d->post_w_off;
+    fa.bias = d->post_bias;
+    fa.y = wave;
+    fa.clamp = (flags & MH3A_FLAG_NO_CLAMP) ? 0 : 1;
+    if (upto >= 0) return fail(MH3A_E_INVALID_ARG, "layer index %d out of range", upto);
+    TimedLaunch tl(d, st);
+    HIP_TRY(launch_final(fa, B, st));
+    tl.done(KIND_FINAL, 2.0 * 7 * cin * (double)len * B, 4.0 * ((double)B * cin * len + (double)B * len + 7 * cin));
+    return ok();
+}
+
+}  // namespace
+
+namespace mh3a {
+
+int64_t packed_weight_floats(int c_out, int c_in, int taps) {
+    const int64_t mb = (c_out + 31) / 32;
+    const int64_t g = (int64_t)((c_in + kChunk - 1) / kChunk) * taps;
+    return mb * g * 64 * 4;
+}
+
+// A-operand order of v_mfma_f32_32x32x2f32: for M-block mb, K-group g =
+// chunk * taps + tap (4 K-steps = the 4 channel pairs of the chunk), lane l
+// and step p, the value is W[mb*32 + l%32, chunk*8 + 2p + l/32, tap].
+void pack_conv_weights(const float* w, int c_out, int c_in, int taps, float* out) {
+    const int nmb = (c_out + 31) / 32;
+    const int nch = (c_in + kChunk - 1) / kChunk;
+    const int64_t G = (int64_t)nch * taps;
+    for (int mb = 0; mb < nmb; ++mb)
+        for (int ch = 0; ch < nch; ++ch)
+            for (int j = 0; j < taps; ++j) {
+                const int64_t g = (int64_t)ch * taps + j;
+                for (int l = 0; l < 64; ++l)
+                    for (int p = 0; p < 4; ++p) {
+                        const int o = mb * 32 + (l & 31);
+                        const int i = ch * kChunk + 2 * p + (l >> 5);
+                        float v = 0.0f;
+                        if (o < c_out && i < c_in) v = w[((int64_t)o * c_in + i) * taps + j];
+                        out[(((int64_t)mb * G + g) * 64 + l) * 4 + p] = v;
+                    }
+            }
+}
+
+}  // namespace mh3a
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+void mh3a_config_default(mh3a_config* c) {
+    if (!c) return;
+    std::memset(c, 0, sizeof *c);
+    c->latent_channels = 32;
+    c->latent_dim = 2048;
+    c->decoder_dim = 1024;
+    c->hop_length = 800;
+    c->num_ups = 7;
+    const int rates[7] = {5, 5, 2, 2, 2, 2, 2};
+    const int kernels[7] = {9, 9, 4, 4, 4, 4, 4};
+    for (int s = 0; s < 7; ++s) {
+        c->rates[s] = rates[s];
+        c->kernels[s] = kernels[s];
+    }
+    c->num_resblocks = 3;
+    c->rb_kernels[0] = 3;
+    c->rb_kernels[1] = 7;
+    c->rb_kernels[2] = 11;
+    c->num_dilations = 3;
+    for (int j = 0; j < 3; ++j) {
+        c->rb_dilations[j][0] = 1;
+        c->rb_dilations[j][1] = 3;
+        c->rb_dilations[j][2] = 5;
+    }
+    c->filter_taps = 12;
+    c->filter_cutoff = 0.25;
+    c->filter_half_width = 0.3;
+}
+
+const char* mh3a_last_error(void) { return g_err.c_str(); }
+
+int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n_params, const float* latents_mean,
+                        const float* latents_std, int device, mh3a_decoder** out) {
+    if (!out) return fail(MH3A_E_INVALID_ARG, "out is null");
+    *out = nullptr;
+    if (!cfg) return fail(MH3A_E_INVALID_ARG, "config is null");
+    if (n_params < 0 || (n_params > 0 && !params)) return fail(MH3A_E_INVALID_ARG, "bad parameter list");
+    if (device < 0) return fail(MH3A_E_INVALID_ARG, "device must be >= 0");
+    int rc = check_config(cfg);
+    if (rc) return rc;
+
+    Table t;
+    for (int i = 0; i < n_params; ++i) {
+        const mh3a_tensor& p = params[i];
+        if (!p.name || !p.data) return fail(MH3A_E_INVALID_ARG, "parameter %d has a null name or data", i);
+        if (p.ndim < 1 || p.ndim > 3) return fail(MH3A_E_SHAPE, "%s: ndim must be 1..3", p.name);
+        Param q;
+        q.data = p.data;
+        q.ndim = p.ndim;
+        for (int k = 0; k < 3; ++k) q.shape[k] = k < p.ndim ? p.shape[k] : 1;
+        for (int k = 0; k < p.ndim; ++k)
+            if (q.shape[k] < 1) return fail(MH3A_E_SHAPE, "%s: non-positive dimension", p.name);
+        t.m[p.name] = q;
+    }
+
+    mh3a_decoder* d = new (std::nothrow) mh3a_decoder();
+    if (!d) return fail(MH3A_E_NOMEM, "out of host memory");
+    std::unique_ptr<mh3a_decoder> guard(d);
+    d->cfg = *cfg;
+    d->device = device;
+    const mh3a_config& c = d->cfg;
+
+    float designed[kTaps];
+    design_lowpass(c.filter_cutoff, c.filter_half_width, c.filter_taps, designed);
+
+    Blob blob;
+    std::vector<float> w;
+    const float* bias;
+
+    // dec_in_proj (1x1, no weight norm); de-normalized copy folds
+    // z * std + mean: W' = W diag(std), b' = b + W mean.
+    {
+        const Param* wp = t.get("dec_in_proj.weight");
+        if (!wp) return fail(MH3A_E_MISSING_TENSOR, "missing dec_in_proj.weight");
+        if ((rc = fetch_weight(t, "dec_in_proj", c.latent_dim, c.latent_channels, 1, w))) return rc;
+        if ((rc = fetch_vector(t, "dec_in_proj.bias", c.latent_dim, &bias))) return rc;
+        add_conv(blob, d->in_proj, w, bias, c.latent_dim, c.latent_channels, 1);
+        d->in_proj.kind = KIND_IN_PROJ;
+        std::vector<float> w2(w.size()), b2(c.latent_dim);
+        for (int o = 0; o < c.latent_dim; ++o) {
+            double bb = bias[o];
+            for (int i = 0; i < c.latent_channels; ++i) {
+                const double wi = w[(size_t)o * c.latent_channels + i];
+                const double sd = latents_std ? latents_std[i] : 1.0;
+                const double mu = latents_mean ? latents_mean[i] : 0.0;
+                w2[(size_t)o * c.latent_channels + i] = (float)(wi * sd);
+                bb += wi * mu;
+            }
+            b2[o] = (float)bb;
+        }
+        add_conv(blob, d->in_proj_dn, w2, b2.data(), c.latent_dim, c.latent_channels, 1);
+        d->in_proj_dn.kind = KIND_IN_PROJ;
+    }
+    // conv_pre: k = 7, pad 3
+    if (!t.get("decoder.conv_pre.weight_v") && !t.get("decoder.conv_pre.weight"))
+        return fail(MH3A_E_MISSING_TENSOR, "missing decoder.conv_pre.weight_v");
+    if ((rc = fetch_weight(t, "decoder.conv_pre", c.decoder_dim, c.latent_dim, 7, w))) return rc;
+    if ((rc = fetch_vector(t, "decoder.conv_pre.bias", c.decoder_dim, &bias))) return rc;
+    add_conv(blob, d->conv_pre, w, bias, c.decoder_dim, c.latent_dim, 7);
+    d->conv_pre.in_off[0] = -3;
+    d->conv_pre.alg_taps = 7;
+    d->conv_pre.kind = KIND_CONV_PRE;
+
+    int cin = c.decoder_dim;
+    d->ups.resize(c.num_ups);
+    d->amp.resize(c.num_ups);
+    d->stage_c.resize(c.num_ups);
+    for (int s = 0; s < c.num_ups; ++s) {
+        const int C = cin / 2;
+        const int r = c.rates[s], k = c.kernels[s], pad = (k - r) / 2;
+        d->stage_c[s] = C;
+        // Transposed conv, polyphase: output t = r m + ph reads
+        // x[m + c_ph - u] with tap q = q0 + r u, q0 = (ph + pad) mod r,
+        // c_ph = (ph + pad) div r; as a conv over m with taps jj = ku-1-u.
+        const std::string pre = "decoder.ups." + std::to_string(s) + ".0";
+        if ((rc = fetch_weight(t, pre, cin, C, k, w))) return rc;
+        if ((rc = fetch_vector(t, pre + ".bias", C, &bias))) return rc;
+        ConvLayer& U = d->ups[s];
+        const int ku = (k + r - 1) / r;
+        U.c_in = cin;
+        U.c_out = C;
+        U.taps = ku;
+        U.phases = r;
+        U.out_mul = r;
+        U.alg_taps = k;
+        U.kind = KIND_UPSAMPLE;
+        const int64_t per = packed_weight_floats(C, cin, ku);
+        U.w_off = blob.reserve(per * r);
+        U.w_phase_stride = per;
+        std::vector<float> wph((size_t)C * cin * ku);
+        for (int ph = 0; ph < r; ++ph) {
+            const int q0 = (ph + pad) % r, cph = (ph + pad) / r;
+            U.in_off[ph] = cph - (ku - 1);
+            U.out_add[ph] = ph;
+            for (int o = 0; o < C; ++o)
+                for (int i = 0; i < cin; ++i)
+                    for (int jj = 0; jj < ku; ++jj) {
+                        const int q = q0 + r * (ku - 1 - jj);
+                        wph[((size_t)o * cin + i) * ku + jj] = q < k ? w[((size_t)i * C + o) * k + q] : 0.0f;
+                    }
+            pack_conv_weights(wph.data(), C, cin, ku, blob.h.data() + U.w_off + ph * per);
+        }
+        U.b_off = blob.add(bias, C);
+        // AMP blocks
+        for (int j = 0; j < c.num_resblocks; ++j) {
+            const int kk = c.rb_kernels[j];
+            const std::string rb = "decoder.resblocks." + std::to_string(s * c.num_resblocks + j);
+            for (int n = 0; n < c.num_dilations; ++n) {
+                const int dil = c.rb_dilations[j][n];
+                for (int which = 0; which < 2; ++which) {
+                    const std::string cp = rb + (which == 0 ? ".convs1." : ".convs2.") + std::to_string(n);
+                    if ((rc = fetch_weight(t, cp, C, C, kk, w))) return rc;
+                    if ((rc = fetch_vector(t, cp + ".bias", C, &bias))) return rc;
+                    ConvLayer L;
+                    add_conv(blob, L, w, bias, C, C, kk);
+                    L.dil = which == 0 ? dil : 1;
+                    L.alg_taps = kk;
+                    L.kind = KIND_AMP;
+                    L.in_off[0] = -(L.dil * (kk - 1) / 2);
+                    const std::string ap = rb + ".activations." + std::to_string(2 * n + which);
+                    if ((rc = add_act(blob, t, ap, C, designed, d->acts))) return rc;
+                    L.act = (int)d->acts.size() - 1;
+                    d->amp[s].push_back(L);
+                }
+            }
+        }
+        cin = C;
+    }
+    if ((rc = add_act(blob, t, "decoder.activation_post", cin, designed, d->acts))) return rc;
+    d->post_act = (int)d->acts.size() - 1;
+    if (!t.get("decoder.conv_post.weight_v") && !t.get("decoder.conv_post.weight"))
+        return fail(MH3A_E_MISSING_TENSOR, "missing decoder.conv_post.weight_v");
+    if ((rc = fetch_weight(t, "decoder.conv_post", 1, cin, 7, w))) return rc;
+    d->post_w_off = blob.add(w.data(), (int64_t)cin * 7);
+    if (const Param* pb = t.get("decoder.conv_post.bias")) {
+        if (!vector_of(pb, 1)) return fail(MH3A_E_SHAPE, "decoder.conv_post.bias must hold 1 value");
+        d->post_bias = pb->data[0];
+    }
+
+    // upload
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(MH3A_E_HIP, "no HIP device available");
+    if (device >= ndev) return fail(MH3A_E_INVALID_ARG, "device %d out of range (%d devices)", device, ndev);
+    HIP_TRY(hipSetDevice(device));
+    d->blob_floats = (int64_t)blob.h.size();
+    HIP_TRY(hipMalloc((void**)&d->blob, sizeof(float) * blob.h.size()));
+    HIP_TRY(hipMemcpy(d->blob, blob.h.data(), sizeof(float) * blob.h.size(), hipMemcpyHostToDevice));
+    *out = guard.release();
+    return ok();
+}
+
+void mh3a_destroy(mh3a_decoder* d) {
+    if (!d) return;
+    if (d->blob) {
+        hipSetDevice(d->device);
+        hipDeviceSynchronize();
+        hipFree(d->blob);
+        for (hipEvent_t e : d->timing.evs) hipEventDestroy(e);
+    }
+    delete d;
+}
+
+int mh3a_timing_enable(mh3a_decoder* d, int enable) {
+    if (!d) return fail(MH3A_E_INVALID_ARG, "decoder is null");
+    d->timing.on = enable != 0;
+    d->timing.used = 0;
+    d->timing.recs.clear();
+    return ok();
+}
+
+int mh3a_timing_read(mh3a_decoder* d, mh3a_kernel_stats* stats, int max_stats, int* n_stats) {
+    if (!d || !n_stats || (max_stats > 0 && !stats)) return fail(MH3A_E_INVALID_ARG, "null argument");
+    *n_stats = 0;
+    Timing& t = d->timing;
+    std::vector<int> order;
+    double ms[KIND_COUNT] = {0}, fl[KIND_COUNT] = {0}, by[KIND_COUNT] = {0};
+    int64_t cnt[KIND_COUNT] = {0};
+    HIP_TRY(hipSetDevice(d->device));
+    for (const TimingRec& r : t.recs) {
+        HIP_TRY(hipEventSynchronize(t.evs[r.ev + 1]));
+        float e = 0.0f;
+        HIP_TRY(hipEventElapsedTime(&e, t.evs[r.ev], t.evs[r.ev + 1]));
+        if (cnt[r.kind] == 0) order.push_back(r.kind);
+        ms[r.kind] += e;
+        fl[r.kind] += r.flops;
+        by[r.kind] += r.bytes;
+        cnt[r.kind] += 1;
+    }
+    t.recs.clear();
+    t.used = 0;
+    int n = 0;
+    for (int k : order) {
+        if (n >= max_stats) break;
+        mh3a_kernel_stats& o = stats[n++];
+        std::memset(&o, 0, sizeof o);
+        std::snprintf(o.name, sizeof o.name, "%s", kKindNames[k]);
+        o.launches = cnt[k];
+        o.ms = ms[k];
+        o.flops = fl[k];
+        o.bytes = by[k];
+    }
+    *n_stats = n;
+    return ok();
+}
+
+int mh3a_decode_workspace_size(const mh3a_decoder* d, int64_t batch, int64_t frames, uint32_t flags, size_t* bytes) {
+    if (!bytes) return fail(MH3A_E_INVALID_ARG, "bytes is null");
+    *bytes = 0;
+    int rc = check_decode_args(d, batch, frames, flags);
+    if (rc) return rc;
+    *bytes = decode_ws_bytes(d, batch, frames);
+    return ok();
+}
+
+int mh3a_decode(mh3a_decoder* d, const float* latents, int64_t batch, int64_t frames, float* wave, void* workspace,
+                size_t workspace_bytes, uint32_t flags, void* stream) {
+    if (!wave) return fail(MH3A_E_INVALID_ARG, "wave is null");
+    return run_decode(d, latents, batch, frames, wave, -1, nullptr, workspace, workspace_bytes, flags,
+                      static_cast<hipStream_t>(stream));
+}
+
+int mh3a_decode_layer_shape(const mh3a_decoder* d, int64_t frames, int upto, int64_t* channels, int64_t* length) {
+    if (!d || !channels || !length) return fail(MH3A_E_INVALID_ARG, "null argument");
+    if (frames < 1) return fail(MH3A_E_INVALID_ARG, "frames must be >= 1");
+    const mh3a_config& c = d->cfg;
+    if (upto < 0 || upto > 1 + 2 * c.num_ups) return fail(MH3A_E_INVALID_ARG, "layer index %d out of range", upto);
+    if (upto == 0) {
+        *channels = c.latent_dim;
+        *length = frames;
+        return ok();
+    }
+    if (upto == 1) {
+        *channels = c.decoder_dim;
+        *length = frames;
+        return ok();
+    }
+    const int s = (upto - 2) / 2;
+    int64_t len = frames;
+    for (int i = 0; i <= s; ++i) len *= c.rates[i];
+    *channels = d->stage_c[s];
+    *length = len;
+    return ok();
+}
+
+int mh3a_decode_partial(mh3a_decoder* d, const float* latents, int64_t batch, int64_t frames, int upto, float* out,
+                        void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+    if (!d) return fail(MH3A_E_INVALID_ARG, "decoder is null");
+    if (!out) return fail(MH3A_E_INVALID_ARG, "out is null");
+    if (upto < 0 || upto > 1 + 2 * d->cfg.num_ups) return fail(MH3A_E_INVALID_ARG, "layer index %d out of range", upto);
+    return run_decode(d, latents, batch, frames, nullptr, upto, out, workspace, workspace_bytes, flags,
+                      static_cast<hipStream_t>(stream));
+}
+
+int mh3a_amp_stage_workspace_size(const mh3a_decoder* d, int stage, int64_t batch, int64_t length, size_t* bytes) {
+    if (!bytes) return fail(MH3A_E_INVALID_ARG, "bytes is null");
+    *bytes = 0;
+    if (!d) return fail(MH3A_E_INVALID_ARG, "decoder is null");
+    if (stage < 0 || stage >= d->cfg.num_ups) return fail(MH3A_E_INVALID_ARG, "stage %d out of range", stage);
+    if (batch < 1 || batch > 4096 || length < 1 || length > ((int64_t)1 << 30))
+        return fail(MH3A_E_INVALID_ARG, "bad batch or length");
+    *bytes = (size_t)(2 * round_up(batch * d->stage_c[stage] * length, 64) * (int64_t)sizeof(float));
+    return ok();
+}
+
+int mh3a_amp_stage(mh3a_decoder* d, int stage, const float* x, int64_t batch, int64_t length, float* y,
+                   void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+    size_t need = 0;
+    int rc = mh3a_amp_stage_workspace_size(d, stage, batch, length, &need);
+    if (rc) return rc;
+    if (!x || !y) return fail(MH3A_E_INVALID_ARG, "null input or output");
+    if (flags & ~MH3A_FLAG_BF16_MFMA) return fail(MH3A_E_INVALID_ARG, "unsupported flags 0x%x", flags);
+    if (!workspace) return fail(MH3A_E_WORKSPACE, "workspace is null");
+    if ((uintptr_t)workspace % 256) return fail(MH3A_E_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need) return fail(MH3A_E_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    if (x == y) return fail(MH3A_E_INVALID_ARG, "x and y must not alias");
+    HIP_TRY(hipSetDevice(d->device));
+    float* xb = static_cast<float*>(workspace);
+    float* tb = xb + round_up(batch * d->stage_c[stage] * length, 64);
+    rc = run_amp(d, stage, x, xb, tb, y, (int)batch, length, (flags & MH3A_FLAG_BF16_MFMA) != 0,
+                 static_cast<hipStream_t>(stream));
+    if (rc) return rc;
+    return ok();
+}
+
+}  // extern "C"

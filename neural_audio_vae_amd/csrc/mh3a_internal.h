@@ -1,0 +1,102 @@
+// Internal interface between the host orchestration (mh3a_host.cpp) and the
+// gfx950 kernels (mh3a_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace mh3a {
+
+// Channels of one K-chunk of the implicit GEMM: each chunk stages CI input
+// channels of the (activated) input window in LDS.
+constexpr int kChunk = 8;
+// Resampler filter length (2x up / 2x down low-pass).
+constexpr int kTaps = 12;
+constexpr int kMaxPhases = 8;
+
+// Per-activation constants on the device: 12 up taps pre-multiplied by the
+// upsampler gain 2 and split by output parity, 12 down taps, then per
+// channel (alpha / pi, 0.5 / beta).
+struct ActParams {
+    const float* taps;  // [24]: even-parity up taps (6), odd-parity up taps (6), down taps (12)
+    const float2* ab;   // [C]: (alpha / pi, 0.5 / beta)
+};
+
+// One implicit-GEMM convolution launch:
+//   y[b, o, out_mul * pos + out_add[ph]] =
+//       scale * (bias[o] + sum_{i, j} W_ph[o, i, j] * A[b, i, pos + in_off[ph] + j * dil]
+//                + res[b, o, t] + sum_in[b, o, t])
+// for pos in [0, positions). A is x itself or, with act, the anti-aliased
+// SnakeBeta of x; A is zero outside [0, l_in) (zero padding).
+struct ConvArgs {
+    const float* x;
+    int64_t x_bstride;  // floats between batch items
+    int c_in;
+    int l_in;
+    const float* w;         // packed weights (see pack_conv_weights)
+    int64_t w_phase_stride; // floats between phases' packed weights
+    const float* bias;      // [c_out] or null
+    float* y;
+    int64_t y_bstride;
+    int c_out;
+    int positions;
+    int taps;
+    int dil;
+    int out_mul;
+    int phases;
+    int in_off[kMaxPhases];
+    int out_add[kMaxPhases];
+    const float* res;     // residual, y's layout, or null
+    const float* sum_in;  // running block sum, y's layout, or null
+    float scale;
+    ActParams act;        // act.taps == null: no activation
+    int bf16;             // round MFMA operands to bfloat16
+};
+
+// Tile shapes of the conv kernel: four consumer waves arranged WM x WN,
+// each computing MBW x NBW blocks of 32 x 32 outputs.
+//          id            MBW NBW WM WN     workgroup tile (M x N)
+#define MH3A_TILE_LIST                                              \
+    MH3A_TILE(TILE_512x64, 4, 2, 4, 1)   /* 512 x  64 */           \
+    MH3A_TILE(TILE_256x128, 2, 4, 4, 1)  /* 256 x 128 */           \
+    MH3A_TILE(TILE_256x96, 2, 3, 4, 1)   /* 256 x  96 */           \
+    MH3A_TILE(TILE_256x64, 2, 2, 4, 1)   /* 256 x  64 */           \
+    MH3A_TILE(TILE_128x256, 2, 4, 2, 2)  /* 128 x 256 */           \
+    MH3A_TILE(TILE_128x128, 2, 2, 2, 2)  /* 128 x 128 */           \
+    MH3A_TILE(TILE_64x512, 2, 4, 1, 4)   /*  64 x 512 */           \
+    MH3A_TILE(TILE_64x256, 2, 2, 1, 4)   /*  64 x 256 */           \
+    MH3A_TILE(TILE_32x512, 1, 4, 1, 4)   /*  32 x 512 */           \
+    MH3A_TILE(TILE_32x256, 1, 2, 1, 4)   /*  32 x 256 */
+enum TileId {
+#define MH3A_TILE(id, mbw, nbw, wm, wn) id,
+    MH3A_TILE_LIST
+#undef MH3A_TILE
+    TILE_COUNT
+};
+struct TileShape {
+    int m, n;
+};
+TileShape tile_shape(TileId t);
+
+// Number of packed floats for a conv weight of (c_out, c_in, taps).
+int64_t packed_weight_floats(int c_out, int c_in, int taps);
+// Pack w (c_out, c_in, taps), row-major, into the MFMA A-operand order.
+void pack_conv_weights(const float* w, int c_out, int c_in, int taps, float* out);
+
+hipError_t launch_conv(const ConvArgs& a, int batch, TileId tile, hipStream_t stream);
+
+// activation_post + conv_post (c -> 1, 7 taps, pad 3) + optional clamp.
+struct FinalArgs {
+    const float* x;
+    int64_t x_bstride;
+    int c;
+    int l;
+    ActParams act;
+    const float* w;  // [c * 7] folded conv_post weight
+    float bias;
+    float* y;        // (B, 1, l)
+    int clamp;
+};
+hipError_t launch_final(const FinalArgs& a, int batch, hipStream_t stream);
+
+}  // namespace mh3a

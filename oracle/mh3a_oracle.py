@@ -379,7 +379,7 @@ def decode_window(params, z, n0, n1, margin=None, config=None, denormalize=False
     cfg = dict(DEFAULT_CONFIG, **(config or {}))
     hop = int(np.prod(cfg["decoder_rates"]))
     if margin is None:
-        margin = int(math.ceil(receptive_radius_latents(cfg))) + 4
+        margin = int(math.ceil(receptive_radius_latents(cfg))) + 1
     n_total = z.shape[2]
     a = max(0, n0 - margin)
     b = min(n_total, n1 + margin)

@@ -1,0 +1,307 @@
+"""GPU path vs the CPU oracle, through the C ABI.
+
+Tolerances (fp32 path): relative L2 <= 1e-4 and max |diff| <= 1e-3 on both
+the clamped waveform and the unclamped signal (MH3A_FLAG_NO_CLAMP); most
+samples saturate under random weights, so the unclamped comparison is the
+sharp one. bf16 matrix-core operands: relative L2 <= 2e-2.
+
+Full-size workloads are checked on sampled output windows: the oracle
+decodes only the latents within the receptive radius of each window, whose
+interior equals the full decode (pinned in test_oracle_pins.py)."""
+
+import functools
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+from neural_audio_vae_amd import synth
+from tests.conftest import SMALL_CONFIG
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+REL_TOL, ABS_TOL, BF16_REL_TOL = 1e-4, 1e-3, 2e-2
+# The absolute bound is stated for the five workloads, whose signals stay
+# below ~10 in magnitude. The extra configurations (other widths, random
+# weight-norm gains, custom filters) produce larger signals; for them the
+# absolute bound scales with the signal: 1e-3 * max(1, max|ref| / 10).
+REF_SCALE = 10.0
+
+
+def scaled_abs(ref):
+    return ABS_TOL * max(1.0, float(np.max(np.abs(ref))) / REF_SCALE)
+
+
+NO_CLAMP, BF16, DENORM = 0x4, 0x2, 0x1
+
+
+def report(what, got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rl = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    ma = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    sat = float(np.mean(np.abs(ref) >= 1.0)) if ref.size else 0.0
+    mx = float(np.max(np.abs(ref))) if ref.size else 0.0
+    print(f"[parity] {what}: n={ref.size} rel_l2={rl:.3e} max_abs={ma:.3e} max|ref|={mx:.3g} |ref|>=1: {sat:.2%}",
+          flush=True)
+    return rl, ma
+
+
+def assert_close(what, got, ref, rel=REL_TOL, abs_=ABS_TOL):
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    rl, ma = report(what, got, ref)
+    assert rl <= rel and ma <= abs_, f"{what}: rel_l2={rl:.3e} max_abs={ma:.3e}"
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def default_decoder(default_params, dev):
+    from neural_audio_vae_amd import Decoder
+    mean, std = synth.make_denorm()
+    d = Decoder(default_params, latents_mean=mean, latents_std=std)
+    yield d
+    d.close()
+
+
+@pytest.fixture(scope="module")
+def small_decoder(small_params, dev):
+    from neural_audio_vae_amd import Decoder
+    d = Decoder(small_params, SMALL_CONFIG)
+    yield d
+    d.close()
+
+
+def gpu(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# Narrow decoder: full decodes, many lengths, both flags
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("batch,frames", [(1, 1), (1, 2), (2, 3), (1, 7), (3, 13)])
+def test_small_decoder_full_decode(small_decoder, small_params, dev, batch, frames):
+    z = synth.make_latents(batch, frames, seed=frames, channels=4)
+    ref = O.decode(small_params, z, SMALL_CONFIG, clamp=False)
+    got = host(small_decoder.decode(gpu(z, dev), flags=NO_CLAMP))
+    assert_close(f"small B={batch} N={frames} unclamped", got, ref, abs_=scaled_abs(ref))
+    got_c = host(small_decoder.decode(gpu(z, dev)))
+    assert_close(f"small B={batch} N={frames} clamped", got_c, np.clip(ref, -1, 1))
+    assert np.all(np.abs(got_c) <= 1.0)
+
+
+def test_small_decoder_fold_uses_axis0_of_each_weight(dev):
+    # g drawn away from ||v||: the fold changes every weight, per output
+    # channel for convs and per input channel for the transposed convs.
+    from neural_audio_vae_amd import Decoder
+    p = synth.make_params(SMALL_CONFIG, seed=5, g_mode="uniform")
+    d = Decoder(p, SMALL_CONFIG)
+    z = synth.make_latents(2, 5, seed=5, channels=4)
+    ref = O.decode(p, z, SMALL_CONFIG, clamp=False)
+    assert_close("small random-g", host(d.decode(gpu(z, dev), flags=NO_CLAMP)), ref, abs_=scaled_abs(ref))
+    d.close()
+
+
+def test_small_decoder_given_filters_and_folded_weights(dev):
+    # Filter buffers passed with the parameters replace the designed taps,
+    # and an already folded `.weight` replaces weight_v / weight_g.
+    from neural_audio_vae_amd import Decoder
+    p = dict(synth.make_params(SMALL_CONFIG, seed=6))
+    rng = np.random.default_rng(0)
+    for name in ("decoder.resblocks.2.activations.1", "decoder.resblocks.19.activations.4", "decoder.activation_post"):
+        f = rng.uniform(-0.2, 0.6, size=12).astype(np.float32)
+        p[name + ".upsample.filter"] = f
+        p[name + ".downsample.lowpass.filter"] = f[::-1].copy()
+    pre = "decoder.resblocks.7.convs2.1"
+    p[pre + ".weight"] = O.fold_weight_norm(p.pop(pre + ".weight_v"), p.pop(pre + ".weight_g"))
+    del p["decoder.conv_post.bias"]
+    d = Decoder(p, SMALL_CONFIG)
+    z = synth.make_latents(1, 6, seed=6, channels=4)
+    ref = O.decode(p, z, SMALL_CONFIG, clamp=False)
+    assert_close("small custom filters", host(d.decode(gpu(z, dev), flags=NO_CLAMP)), ref, abs_=scaled_abs(ref))
+    d.close()
+
+
+def test_small_decoder_other_shapes(dev):
+    # A different stage layout: two stages, one block, two dilations.
+    from neural_audio_vae_amd import Decoder
+    cfg = {"latent_channels": 3, "latent_dim": 20, "decoder_dim": 40, "decoder_rates": (4, 3),
+           "decoder_kernel_sizes": (8, 7), "resblock_kernel_sizes": (5,), "resblock_dilation_sizes": ((2, 7),),
+           "hop_length": 12}
+    p = synth.make_params(cfg, seed=8)
+    d = Decoder(p, cfg)
+    z = synth.make_latents(2, 9, seed=8, channels=3)
+    ref = O.decode(p, z, cfg, clamp=False)
+    assert_close("custom config", host(d.decode(gpu(z, dev), flags=NO_CLAMP)), ref, abs_=scaled_abs(ref))
+    d.close()
+
+
+# ---------------------------------------------------------------------------
+# Default decoder, c1: every layer, then the output
+# ---------------------------------------------------------------------------
+
+@functools.lru_cache(maxsize=None)
+def c1_oracle_stages():
+    p = synth.make_params()
+    z = synth.make_latents(1, 4)
+    y, stages = O.decode_item(p, z[0], clamp=False, return_stages=True)
+    return z, y, stages
+
+
+def test_c1_every_layer(default_decoder, dev):
+    z, _, stages = c1_oracle_stages()
+    zt = gpu(z, dev)
+    for upto, ref in enumerate(stages):
+        got = host(default_decoder.decode_partial(zt, upto))[0]
+        assert_close(f"c1 layer {upto}", got, ref)
+
+
+def test_c1_decode(default_decoder, dev):
+    z, y, _ = c1_oracle_stages()
+    got = host(default_decoder.decode(gpu(z, dev), flags=NO_CLAMP))
+    assert_close("c1 unclamped", got[0], y)
+    got_c = host(default_decoder.decode(gpu(z, dev)))
+    assert_close("c1 clamped", got_c[0], np.clip(y, -1, 1))
+
+
+def test_c1_bf16_variant(default_decoder, dev):
+    z, y, _ = c1_oracle_stages()
+    got = host(default_decoder.decode(gpu(z, dev), flags=NO_CLAMP | BF16))
+    assert_close("c1 bf16 unclamped", got[0], y, rel=BF16_REL_TOL, abs_=math.inf)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads on sampled windows
+# ---------------------------------------------------------------------------
+
+def oracle_windows(params, z, windows, denorm=None):
+    """[(item, n0, n1)] -> list of oracle outputs (1, 800 (n1 - n0))."""
+    out = []
+    for item, n0, n1 in windows:
+        kw = {}
+        if denorm is not None:
+            kw = dict(denormalize=True, latents_mean=denorm[0], latents_std=denorm[1])
+        out.append(O.decode_window(params, z[item:item + 1], n0, n1, clamp=False, **kw)[0, 0])
+    return out
+
+
+def check_windows(tag, got, refs, windows, rel=REL_TOL, abs_=ABS_TOL):
+    for (item, n0, n1), ref in zip(windows, refs):
+        g = got[item, 0, 800 * n0:800 * n1]
+        assert_close(f"{tag} item {item} latents [{n0},{n1}) unclamped", g, ref, rel, abs_)
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c3", "c5"])
+def test_full_size_sampled_windows(default_decoder, default_params, dev, cfg):
+    if cfg == "c2":
+        batch, frames, flags = 2, 200, DENORM
+        denorm = synth.make_denorm()
+        windows = [(0, 0, 3), (1, 100, 103), (1, 197, 200)]
+    elif cfg == "c3":
+        batch, frames, flags, denorm = 2, 1200, 0, None
+        windows = [(0, 0, 2), (0, 600, 603), (1, 1198, 1200)]
+    else:
+        batch, frames, flags, denorm = 16, 401, 0, None
+        windows = [(0, 0, 2), (7, 200, 203), (15, 399, 401)]
+    z = synth.make_latents(batch, frames)
+    print(f"[case] {cfg} B={batch} N={frames} flags={flags}", flush=True)
+    out = default_decoder.decode(gpu(z, dev), flags=flags | NO_CLAMP)
+    got = host(out)
+    assert got.shape == (batch, 1, 800 * frames)
+    assert np.all(np.isfinite(got))
+    refs = oracle_windows(default_params, z, windows, denorm)
+    check_windows(cfg, got, refs, windows)
+    clamped = host(default_decoder.decode(gpu(z, dev), flags=flags))
+    np.testing.assert_array_equal(clamped, np.clip(got, -1, 1))
+
+
+def test_c3_bf16_variant_sampled(default_decoder, default_params, dev):
+    z = synth.make_latents(2, 1200)
+    windows = [(0, 600, 602), (1, 0, 2)]
+    got = host(default_decoder.decode(gpu(z, dev), flags=NO_CLAMP | BF16))
+    refs = oracle_windows(default_params, z, windows)
+    check_windows("c3 bf16", got, refs, windows, rel=BF16_REL_TOL, abs_=math.inf)
+
+
+def test_c4_amp_stage_microbench(default_decoder, default_params, dev):
+    # Stage-1 AMP set alone on (2, 256, 30000) ~ N(0, 1); checked on
+    # windows whose margin (120 samples) exceeds the set's radius (90).
+    x = synth.make_signal((2, 256, 30000), seed=0)
+    got = host(default_decoder.amp_stage(1, gpu(x, dev)))
+    assert got.shape == x.shape
+    margin = 120
+    for item, a, b in [(0, 0, 64), (1, 15000, 15064), (1, 29936, 30000), (0, 29990, 30000)]:
+        lo, hi = max(0, a - margin), min(30000, b + margin)
+        ref = O.stage_amp(x[item][:, lo:hi], default_params, 1)[:, a - lo:b - lo]
+        assert_close(f"c4 item {item} [{a},{b})", got[item][:, a:b], ref)
+
+
+def test_amp_stage_rejects_bad_arguments(default_decoder, dev):
+    from neural_audio_vae_amd import MH3AError
+    x = torch.zeros((1, 256, 50), device=dev)
+    with pytest.raises(MH3AError):
+        default_decoder.amp_stage(7, x)
+    with pytest.raises(MH3AError):
+        default_decoder.amp_stage(1, x, flags=0x1)
+
+
+# ---------------------------------------------------------------------------
+# Batch semantics and determinism
+# ---------------------------------------------------------------------------
+
+def test_batch_items_decode_independently_bitwise(default_decoder, dev):
+    z = synth.make_latents(3, 37, seed=2)
+    both = host(default_decoder.decode(gpu(z, dev), flags=NO_CLAMP))
+    for i in range(3):
+        one = host(default_decoder.decode(gpu(z[i:i + 1], dev), flags=NO_CLAMP))
+        np.testing.assert_array_equal(both[i], one[0])
+
+
+def test_decode_is_deterministic(default_decoder, dev):
+    z = gpu(synth.make_latents(2, 33, seed=3), dev)
+    a = host(default_decoder.decode(z, flags=NO_CLAMP))
+    b = host(default_decoder.decode(z, flags=NO_CLAMP))
+    np.testing.assert_array_equal(a, b)
+
+
+def test_decode_argument_errors(default_decoder, dev):
+    from neural_audio_vae_amd import _lib
+    z = gpu(synth.make_latents(1, 4), dev)
+    out = torch.empty((1, 1, 3200), device=dev)
+    need = default_decoder.workspace_size(1, 4)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    h = default_decoder._h
+    st = torch.cuda.current_stream().cuda_stream
+    with pytest.raises(_lib.MH3AError) as e:
+        _lib.mh3a_decode(h, z.data_ptr(), 1, 4, out.data_ptr(), ws.data_ptr(), need - 1, 0, st)
+    assert e.value.code == _lib.MH3A_E_WORKSPACE
+    with pytest.raises(_lib.MH3AError) as e:
+        _lib.mh3a_decode(h, z.data_ptr(), 1, 4, out.data_ptr(), ws.data_ptr() + 4, need, 0, st)
+    assert e.value.code == _lib.MH3A_E_WORKSPACE
+    with pytest.raises(_lib.MH3AError) as e:
+        _lib.mh3a_decode(h, z.data_ptr(), 0, 4, out.data_ptr(), ws.data_ptr(), need, 0, st)
+    assert e.value.code == _lib.MH3A_E_INVALID_ARG
+    with pytest.raises(_lib.MH3AError) as e:
+        _lib.mh3a_decode(h, z.data_ptr(), 1, 4, out.data_ptr(), ws.data_ptr(), need, 0x80, st)
+    assert e.value.code == _lib.MH3A_E_INVALID_ARG
+    with pytest.raises(_lib.MH3AError):
+        default_decoder.decode_partial(z, 16)
+    # the good call still works afterwards
+    _lib.mh3a_decode(h, z.data_ptr(), 1, 4, out.data_ptr(), ws.data_ptr(), need, 0, st)
+    torch.cuda.synchronize()
+    print("[case] argument errors ok", file=sys.stderr)
