@@ -51,7 +51,39 @@ def parse():
     ap.add_argument("--bf16", action="store_true", help="bf16-split matrix-core operands (MH3A_FLAG_BF16_MFMA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-latents", type=int, default=80, help="latents in the oracle's timed sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_probe(nbytes):
+    """One plain device copy of nbytes: the reference the HBM read/write
+    counters of the decode kernels are scaled by."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4}), flush=True)
+    return 0
+
+
+def measured_traffic(workload, flags):
+    """HBM bytes per AMP-conv launch from the committed rocprofv3 counter
+    runs (profiles/amp_conv_c3_traffic.json), or None when the kernel
+    sources changed since the counters were taken or the workload differs."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "amp_conv_c3_traffic.json")
+    if workload != "c3" or flags & 0x2 or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
 
 
 def cpu_baseline(params, n_latents):
@@ -82,6 +114,8 @@ def cpu_baseline(params, n_latents):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               "(the decode path runs on a single GPU).", file=sys.stderr)
@@ -165,7 +199,7 @@ def main():
             "peak": FP32_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload, flags),
             "launches_per_step": amp["launches"] / args.steps,
             "avg_launch_us": round(1e3 * amp["ms"] / max(1, amp["launches"]), 2),
             "flops_per_launch": amp["flops"] / max(1, amp["launches"]),
