@@ -390,7 +390,7 @@ TileId choose_tile(const ConvLayer& L, int positions, int groups, bool bf16) {
     if (forced_tile() >= 0) {
         const TileShape s = tile_shape((TileId)forced_tile());
         const int W = s.n + (L.taps - 1) * L.dil;
-        const int lds_floats = 2 * kChunk * W + (L.act >= 0 ? kChunk * (3 * W + 24) : 0);
+        const int lds_floats = 2 * kChunk * W + (L.act >= 0 ? kChunk * (3 * W + 32) : 0);
         if (lds_floats * 4 <= 160 * 1024) return (TileId)forced_tile();
     }
     double best = 1e300;
@@ -398,13 +398,13 @@ TileId choose_tile(const ConvLayer& L, int positions, int groups, bool bf16) {
     const bool act = L.act >= 0;
     const int mpad = ((L.c_out + 31) / 32) * 32;
     // With at most 32 output channels the activation producers bound the
-    // kernel; the narrowest window measured fastest.
+    // kernel; the narrow window measured fastest (more resident workgroups).
     if (act && L.c_out <= 32) return TILE_32x256;
     for (int id = 0; id < TILE_COUNT; ++id) {
         const TileShape s = tile_shape((TileId)id);
         if (s.m > mpad && s.m > 32) continue;  // consumer waves would idle
         const int W = s.n + (L.taps - 1) * L.dil;
-        const int lds_floats = 2 * kChunk * W + (act ? kChunk * (3 * W + 24) : 0);
+        const int lds_floats = 2 * kChunk * W + (act ? kChunk * (3 * W + 32) : 0);
         if (lds_floats * 4 > 160 * 1024) continue;
         const double cost = tile_cost(L, (TileId)id, positions, groups, bf16);
         if (cost < best) {
@@ -468,6 +468,7 @@ hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, i
     a.dil = L.dil;
     a.out_mul = L.out_mul;
     a.phases = L.phases;
+    a.groups = batch * L.phases;
     for (int i = 0; i < kMaxPhases; ++i) {
         a.in_off[i] = L.in_off[i];
         a.out_add[i] = L.out_add[i];
@@ -478,7 +479,7 @@ hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, i
     a.act = act_params(d, L.act);
     a.bf16 = bf16 ? 1 : 0;
     TimedLaunch tl(d, st);
-    hipError_t e = launch_conv(a, batch, choose_tile(L, positions, batch * L.phases, bf16), st);
+    hipError_t e = launch_conv(a, choose_tile(L, positions, batch * L.phases, bf16), st);
     const double outs = (double)batch * L.c_out * L.out_mul * positions;
     const double flops = 2.0 * L.c_out * (double)L.c_in * L.alg_taps * positions * batch;
     const double bytes = 4.0 * ((double)batch * L.c_in * l_in + outs * (1 + (res ? 1 : 0) + (sum_in ? 1 : 0)) +

@@ -44,6 +44,7 @@ struct ConvArgs {
     int dil;
     int out_mul;
     int phases;
+    int groups;           // batch * phases
     int in_off[kMaxPhases];
     int out_add[kMaxPhases];
     const float* res;     // residual, y's layout, or null
@@ -83,7 +84,7 @@ int64_t packed_weight_floats(int c_out, int c_in, int taps);
 // Pack w (c_out, c_in, taps), row-major, into the MFMA A-operand order.
 void pack_conv_weights(const float* w, int c_out, int c_in, int taps, float* out);
 
-hipError_t launch_conv(const ConvArgs& a, int batch, TileId tile, hipStream_t stream);
+hipError_t launch_conv(const ConvArgs& a, TileId tile, hipStream_t stream);
 
 // activation_post + conv_post (c -> 1, 7 taps, pad 3) + optional clamp.
 struct FinalArgs {

@@ -20,6 +20,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "mh3a_internal.h"
 
 namespace mh3a {
@@ -47,6 +49,13 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// LDS row lengths of the activation staging for window width W: the x row
+// holds X[n_lo - 6 ...] with room for the two-pair reads, the s row holds the
+// 2x-rate slots shifted by one (slot m at index m + 1) so that the pair
+// stores and the down-filter reads are 16-byte aligned.
+__host__ __device__ constexpr int act_xs_len(int W) { return (W + 14 + 3) & ~3; }
+__host__ __device__ constexpr int act_ss_len(int W) { return (2 * W + 14 + 3) & ~3; }
+
 // Stage CI channels [ch0, ch0 + CI) of act(x) over input positions
 // [n_lo, n_lo + W) into as[CI][W] (zero outside [0, l_in): the conv's zero
 // padding). act is the anti-aliased SnakeBeta:
@@ -57,31 +66,81 @@ __device__ __forceinline__ void wave_lds_sync() {
 //   a[n] = sum_{q=0..11} f[q] s[clamp(2n + q - 5, 0, 2L-1)]   (pad 5 / 6, stride 2)
 // `lane32` in [0, 32) and `ci` identify the calling thread: 32 threads of
 // one wave own one channel, so the steps synchronize only within the wave.
-// LDS: xs[CI][W + 12] holds X[n_lo - 6 ...], ss[CI][2W + 12] holds
-// s[clamp(2 n_lo - 5 + mm)], as[CI][W] the result.
+// LDS: xs[CI][act_xs_len(W)] holds X[n_lo - 6 ...]; ss[CI][act_ss_len(W)]
+// holds slot mm = s[clamp(2 n_lo - 5 + mm)] at index mm + 1; as[CI][W] is
+// the result (W even).
+//
+// Tiles whose window lies inside the sequence (no clamping, no zeroing)
+// take the fast path: each thread computes two adjacent pairs from eight X
+// values and stores their four s values at once, then two adjacent outputs
+// from sixteen s values. Edge tiles take the general path.
 template <int CI>
-__device__ __forceinline__ void stage_act(float* __restrict__ as, float* __restrict__ xs, float* __restrict__ ss,
-                                          const float* __restrict__ xb, int ch0, int c_in, int l_in, int n_lo,
-                                          int W, const ActParams& ap, int ci, int lane32) {
+__device__ __forceinline__ void act_from_xs(float* __restrict__ as, float* __restrict__ xs, float* __restrict__ ss,
+                                            int ch0, int c_in, int l_in, int n_lo, int W, const ActParams& ap,
+                                            int ci, int lane32) {
     const int ch = ch0 + ci;
     const bool live = ch < c_in;
-    const int XS = W + 12, SS = 2 * W + 12;
+    const int XS = act_xs_len(W), SS = act_ss_len(W);
     float* xrow = xs + ci * XS;
     float* srow = ss + ci * SS;
     float* arow = as + ci * W;
-    const float* xc = xb + (int64_t)(live ? ch : 0) * l_in;
-    for (int w = lane32; w < XS; w += 32) {
-        xrow[w] = live ? xc[clampi(n_lo - 6 + w, 0, l_in - 1)] : 0.0f;
-    }
-    wave_lds_sync();
     const float* tp = ap.taps;
-    float fe[6], fo[6];
+    float fe[6], fo[6], fd[12];
 #pragma unroll
     for (int e = 0; e < 6; ++e) {
         fe[e] = tp[e];
         fo[e] = tp[6 + e];
     }
-    float2 ab = live ? ap.ab[ch] : make_float2(0.0f, 0.0f);
+#pragma unroll
+    for (int q = 0; q < 12; ++q) fd[q] = tp[12 + q];
+    const float2 ab = live ? ap.ab[ch] : make_float2(0.0f, 0.0f);
+    const bool interior = n_lo - 6 >= 0 && n_lo + W + 8 <= l_in && ch0 + CI <= c_in;
+
+    (void)XS;
+    if (interior) {
+        // pairs idx, idx + 1 (t' = n_lo - 3 + idx): X[t' - 3 ...] = xrow[idx ...]
+        for (int idx = 2 * lane32; idx < W + 6; idx += 64) {
+            const float2 x01 = *reinterpret_cast<const float2*>(xrow + idx);
+            const float2 x23 = *reinterpret_cast<const float2*>(xrow + idx + 2);
+            const float2 x45 = *reinterpret_cast<const float2*>(xrow + idx + 4);
+            const float2 x67 = *reinterpret_cast<const float2*>(xrow + idx + 6);
+            const float X[8] = {x01.x, x01.y, x23.x, x23.y, x45.x, x45.y, x67.x, x67.y};
+            float ue0 = 0.f, uo0 = 0.f, ue1 = 0.f, uo1 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 6; ++e) {
+                ue0 = fmaf(fe[e], X[5 - e], ue0);
+                uo0 = fmaf(fo[e], X[6 - e], uo0);
+                ue1 = fmaf(fe[e], X[6 - e], ue1);
+                uo1 = fmaf(fo[e], X[7 - e], uo1);
+            }
+            // slots 2 idx - 1 .. 2 idx + 2 at srow[2 idx .. 2 idx + 3]
+            *reinterpret_cast<float4*>(srow + 2 * idx) =
+                make_float4(snake_beta(ue0, ab.x, ab.y), snake_beta(uo0, ab.x, ab.y), snake_beta(ue1, ab.x, ab.y),
+                            snake_beta(uo1, ab.x, ab.y));
+        }
+        wave_lds_sync();
+        // outputs w, w + 1: a[w] = sum_q f[q] slot[2w + q] = sum_q f[q] srow[2w + q + 1]
+        for (int w = 2 * lane32; w < W; w += 64) {
+            float S[16];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float4 t4 = *reinterpret_cast<const float4*>(srow + 2 * w + 4 * v);
+                S[4 * v] = t4.x;
+                S[4 * v + 1] = t4.y;
+                S[4 * v + 2] = t4.z;
+                S[4 * v + 3] = t4.w;
+            }
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int q = 0; q < 12; ++q) {
+                a0 = fmaf(fd[q], S[q + 1], a0);
+                a1 = fmaf(fd[q], S[q + 3], a1);
+            }
+            *reinterpret_cast<float2*>(arow + w) = make_float2(a0, a1);
+        }
+        return;
+    }
+
     // pairs t' = n_lo - 3 + idx, idx in [0, W + 6): slot 2 idx - 1 <- s[2t'], slot 2 idx <- s[2t' + 1]
     for (int idx = lane32; idx < W + 6; idx += 32) {
         const int tq = n_lo - 3 + idx;
@@ -97,18 +156,15 @@ __device__ __forceinline__ void stage_act(float* __restrict__ as, float* __restr
         float so = snake_beta(uo, ab.x, ab.y);
         if (tq < 0) so = se;
         if (tq >= l_in) se = so;
-        if (idx > 0) srow[2 * idx - 1] = se;
-        srow[2 * idx] = so;
+        srow[2 * idx] = se;
+        srow[2 * idx + 1] = so;
     }
     wave_lds_sync();
-    float fd[12];
-#pragma unroll
-    for (int q = 0; q < 12; ++q) fd[q] = tp[12 + q];
     for (int w = lane32; w < W; w += 32) {
         const int n = n_lo + w;
         float v = 0.0f;
         if (live && n >= 0 && n < l_in) {
-            const float* sv = srow + 2 * w;
+            const float* sv = srow + 2 * w + 1;
 #pragma unroll
             for (int q = 0; q < 12; ++q) v = fmaf(fd[q], sv[q], v);
         }
@@ -116,17 +172,19 @@ __device__ __forceinline__ void stage_act(float* __restrict__ as, float* __restr
     }
 }
 
-// Plain staging: as[ci][w] = x[ch0 + ci, n_lo + w], zero outside.
-__device__ __forceinline__ void stage_plain(float* __restrict__ as, const float* __restrict__ xb, int ch0, int c_in,
-                                            int l_in, int n_lo, int W, int ci, int lane32) {
+// Load X[n_lo - 6 ...] (replicate-clamped) for channel ch0 + ci into xs and
+// run act_from_xs (the single-buffer path of the final kernel).
+template <int CI>
+__device__ __forceinline__ void stage_act(float* __restrict__ as, float* __restrict__ xs, float* __restrict__ ss,
+                                          const float* __restrict__ xb, int ch0, int c_in, int l_in, int n_lo,
+                                          int W, const ActParams& ap, int ci, int lane32) {
     const int ch = ch0 + ci;
     const bool live = ch < c_in;
     const float* xc = xb + (int64_t)(live ? ch : 0) * l_in;
-    float* arow = as + ci * W;
-    for (int w = lane32; w < W; w += 32) {
-        const int n = n_lo + w;
-        arow[w] = (live && n >= 0 && n < l_in) ? xc[n] : 0.0f;
-    }
+    float* xrow = xs + ci * act_xs_len(W);
+    for (int w = lane32; w < act_xs_len(W); w += 32) xrow[w] = live ? xc[clampi(n_lo - 6 + w, 0, l_in - 1)] : 0.0f;
+    wave_lds_sync();
+    act_from_xs<CI>(as, xs, ss, ch0, c_in, l_in, n_lo, W, ap, ci, lane32);
 }
 
 __device__ __forceinline__ float round_bf16(float v) {
@@ -138,15 +196,18 @@ __device__ __forceinline__ float round_bf16(float v) {
 
 // LDS floats of the conv kernel for window width W.
 __host__ __device__ constexpr int conv_lds_floats(int W, bool act) {
-    return 2 * kChunk * W + (act ? kChunk * (W + 12) + kChunk * (2 * W + 12) : 0);
+    return 2 * kChunk * W + (act ? kChunk * act_xs_len(W) + kChunk * act_ss_len(W) : 0);
 }
 
-// Wave-specialized implicit-GEMM conv. 512 threads: waves 0-3 are the
-// consumers (matrix-core loop, WM x WN of them, each MBW x NBW blocks of
-// 32 x 32 outputs); waves 4-7 are the producers, which stage the next
-// K-chunk's (activated) input window into the other half of a
-// double-buffered LDS tile while the consumers work on the current one.
-// One workgroup barrier per chunk hands the buffers over.
+// Wave-specialized, persistent implicit-GEMM conv. 512 threads: waves 0-3
+// are the consumers (matrix-core loop, WM x WN of them, each MBW x NBW
+// blocks of 32 x 32 outputs); waves 4-7 are the producers. A workgroup owns
+// a contiguous range of output tiles and walks the (tile, K-chunk) items of
+// that range as one pipeline: while the consumers multiply item i, the
+// producers stage item i + 1 (the next chunk, or the first chunk of the next
+// tile) into the other half of a double-buffered LDS window, so the
+// epilogue of one tile overlaps the staging of the next. One workgroup
+// barrier per item hands the buffers over.
 template <int MBW, int NBW, int WM, int WN, bool ACT, bool BF16>
 __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     static_assert(WM * WN == 4, "four consumer waves");
@@ -157,127 +218,252 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const bool producer = wave >= 4;
-    const int ph = blockIdx.z % a.phases;
-    const int b = blockIdx.z / a.phases;
-    const int p0 = blockIdx.x * NWG;
-    const int m0 = blockIdx.y * MWG;
     const int W = NWG + (a.taps - 1) * a.dil;
-    const int n_lo = p0 + a.in_off[ph];
     float* abuf = lds;                       // [2][CI][W]
-    float* xs = lds + 2 * CI * W;            // [CI][W + 12]   (act only)
-    float* ss = xs + CI * (W + 12);          // [CI][2W + 12]  (act only)
-    const float* xb = a.x + (int64_t)b * a.x_bstride;
+    float* xs = lds + 2 * CI * W;            // [CI][act_xs_len(W)]   (act only)
+    float* ss = xs + CI * act_xs_len(W);     // [CI][act_ss_len(W)]   (act only)
     const int nch = (a.c_in + CI - 1) / CI;
     const int G = nch * a.taps;
+    const int n_nt = (a.positions + NWG - 1) / NWG;
+    const int n_mt = (a.c_out + MWG - 1) / MWG;
+    const int total = n_nt * n_mt * a.groups;
+    const int t_begin = (int)((int64_t)total * blockIdx.x / gridDim.x);
+    const int t_end = (int)((int64_t)total * (blockIdx.x + 1) / gridDim.x);
+    const int n_items = (t_end - t_begin) * nch;
+    if (n_items == 0) return;
+
+    // tile id -> (batch item, phase, M tile, N tile); N tiles vary fastest
+    struct Tile {
+        int b, ph, mt, p0;
+    };
+    auto tile_at = [&](int id) {
+        const int nt = id % n_nt;
+        const int rest = id / n_nt;
+        const int mt = rest % n_mt;
+        const int g = rest / n_mt;
+        return Tile{g / a.phases, g % a.phases, mt, nt * NWG};
+    };
 
     // producer identity: 256 threads, 32 per channel
     const int ptid = tid - 256;
     const int pci = ptid >> 5, plane = ptid & 31;
+    // An item's input row for this thread's channel: with the activation
+    // X[n_lo - 6 ...] over act_xs_len(W) (replicate-clamped), without it
+    // x[n_lo ...] over W (zero outside). Rows of up to 32 * XR values are
+    // prefetched into registers one item ahead; longer rows load directly.
+    constexpr int XR = (NWG + 64 + 16 + 31) / 32;
+    const int row_len = ACT ? act_xs_len(W) : W;
+    const bool prefetchable = row_len <= 32 * XR;
+    float xr[XR];
+    auto row_value = [&](const Tile& t, int c, int w) {
+        const int ch = c * CI + pci;
+        if (ch >= a.c_in) return 0.0f;
+        const float* xc = a.x + (int64_t)t.b * a.x_bstride + (int64_t)ch * a.l_in;
+        const int n_lo = t.p0 + a.in_off[t.ph];
+        if constexpr (ACT) {
+            return xc[clampi(n_lo - 6 + w, 0, a.l_in - 1)];
+        } else {
+            const int n = n_lo + w;
+            return (n >= 0 && n < a.l_in) ? xc[n] : 0.0f;
+        }
+    };
+    auto prefetch = [&](const Tile& t, int c) {
+#pragma unroll
+        for (int r = 0; r < XR; ++r) {
+            const int w = plane + 32 * r;
+            xr[r] = w < row_len ? row_value(t, c, w) : 0.0f;
+        }
+    };
+    // write item (t, c)'s row to LDS (from the prefetch registers when it
+    // fits) and, with the activation, compute it into dst
+    auto stage = [&](const Tile& t, int c, float* dst) {
+        float* row = ACT ? xs + pci * act_xs_len(W) : dst + pci * W;
+        if (prefetchable) {
+#pragma unroll
+            for (int r = 0; r < XR; ++r) {
+                const int w = plane + 32 * r;
+                if (w < row_len) row[w] = xr[r];
+            }
+        } else {
+            for (int w = plane; w < row_len; w += 32) row[w] = row_value(t, c, w);
+        }
+    };
+    auto compute = [&](const Tile& t, int c, float* dst) {
+        if constexpr (ACT) {
+            wave_lds_sync();
+            act_from_xs<CI>(dst, xs, ss, c * CI, a.c_in, a.l_in, t.p0 + a.in_off[t.ph], W, a.act, pci, plane);
+        }
+    };
 
     // consumer identity
     const int wm = wave % WM, wn = wave / WM;
     const int mb_tot = (a.c_out + 31) >> 5;
-    const int mb_base = (m0 >> 5) + wm * MBW;
-    const bool wave_live = !producer && mb_base < mb_tot;
     const int hi = lane >> 5, lo = lane & 31;
     const int colbase = wn * NBW * 32 + lo;
-    const float4* wp = reinterpret_cast<const float4*>(a.w + (int64_t)ph * a.w_phase_stride);
-
-    auto stage = [&](int c, float* dst) {
-        if constexpr (ACT) {
-            stage_act<CI>(dst, xs, ss, xb, c * CI, a.c_in, a.l_in, n_lo, W, a.act, pci, plane);
-        } else {
-            stage_plain(dst, xb, c * CI, a.c_in, a.l_in, n_lo, W, pci, plane);
-        }
-    };
 
     v16f acc[MBW][NBW];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < MBW; ++i)
+        for (int i = 0; i < MBW; ++i)
 #pragma unroll
-        for (int j = 0; j < NBW; ++j)
+            for (int j = 0; j < NBW; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    float4 An[MBW];
-    auto load_a = [&](int g) {
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    };
+    // A operand of K-group g for the M blocks starting at mb_base, phase ph
+    auto load_a = [&](float4 (&dst)[MBW], int mb_base, int ph, int g) {
+        const float4* wp = reinterpret_cast<const float4*>(a.w + (int64_t)ph * a.w_phase_stride) +
+                           ((int64_t)mb_base * G + g) * 64 + lane;
+        if (mb_base + MBW <= mb_tot) {
 #pragma unroll
-        for (int mb = 0; mb < MBW; ++mb) {
-            const int mbg = mb_base + mb;
-            An[mb] = (mbg < mb_tot && g < G) ? wp[((int64_t)mbg * G + g) * 64 + lane]
-                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int mb = 0; mb < MBW; ++mb) dst[mb] = wp[(int64_t)mb * G * 64];
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb)
+                dst[mb] = mb_base + mb < mb_tot ? wp[(int64_t)mb * G * 64] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
+    // B operand of one tap: the 4 channel pairs x NBW blocks of 32 positions
+    auto load_b = [&](float (&dst)[4][NBW], const float* buf, int j) {
+        const float* brow = buf + hi * W + colbase + j * a.dil;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) dst[p][nb] = brow[2 * p * W + nb * 32];
+    };
+    auto mfma_tap = [&](const float4 (&A)[MBW], const float (&Bv)[4][NBW]) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb) {
+                const float av = p == 0 ? A[mb].x : (p == 1 ? A[mb].y : (p == 2 ? A[mb].z : A[mb].w));
+                if constexpr (BF16) {
+                    // three-term bfloat16 split: ah*bh + al*bh + ah*bl
+                    const float ah = round_bf16(av), al = round_bf16(av - ah);
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb) {
+                        const float bh = round_bf16(Bv[p][nb]), bl = round_bf16(Bv[p][nb] - bh);
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(ah, bh, acc[mb][nb], 0, 0, 0);
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(al, bh, acc[mb][nb], 0, 0, 0);
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(ah, bl, acc[mb][nb], 0, 0, 0);
+                    }
+                } else {
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, Bv[p][nb], acc[mb][nb], 0, 0, 0);
+                }
+            }
+        }
+    };
+    float4 An[MBW];
 
-    if (producer) stage(0, abuf);
-    if (wave_live) load_a(0);
+    // The pipeline walks items (tile, chunk) with chunk fastest. Producers
+    // and consumers run separate loops with one barrier per item each, so
+    // the compiler allocates registers for the larger role only.
+    if (producer) {
+        Tile cur = tile_at(t_begin);
+        int cur_c = 0;
+        if (prefetchable) prefetch(cur, 0);
+        // look-ahead item (the one after `cur`)
+        Tile la = cur;
+        int la_c = 0;
+        auto advance = [&](Tile& t, int& c, int item) {
+            if (++c == nch) {
+                c = 0;
+                t = tile_at(t_begin + item / nch);
+            }
+        };
+        stage(cur, 0, abuf);
+        if (n_items > 1) {
+            advance(la, la_c, 1);
+            if (prefetchable) prefetch(la, la_c);
+        }
+        compute(cur, 0, abuf);
+        __syncthreads();
+        for (int it = 0; it < n_items; ++it) {
+            if (it + 1 < n_items) {
+                // la is item it + 1: commit its row, start fetching it + 2, compute it + 1
+                float* dst = abuf + ((it + 1) & 1) * CI * W;
+                const Tile t1 = la;
+                const int c1 = la_c;
+                stage(t1, c1, dst);
+                if (it + 2 < n_items) {
+                    advance(la, la_c, it + 2);
+                    if (prefetchable) prefetch(la, la_c);
+                }
+                compute(t1, c1, dst);
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    Tile cur = tile_at(t_begin);
+    int cur_c = 0;
+    zero_acc();
+    load_a(An, __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW), cur.ph, 0);
     __syncthreads();
-
-    for (int c = 0; c < nch; ++c) {
-        if (producer) {
-            if (c + 1 < nch) stage(c + 1, abuf + ((c + 1) & 1) * CI * W);
-        } else if (wave_live) {
-            const float* cur = abuf + (c & 1) * CI * W;
-            for (int j = 0; j < a.taps; ++j) {
-                const int g = c * a.taps + j;
-                float4 Ac[MBW];
+    for (int it = 0; it < n_items; ++it) {
+        // the item after this one
+        const bool has_next = it + 1 < n_items;
+        Tile nxt = cur;
+        int nxt_c = cur_c + 1;
+        if (nxt_c == nch) {
+            nxt_c = 0;
+            if (has_next) nxt = tile_at(t_begin + (it + 1) / nch);
+        }
+        // wave-uniform M-block base (the compiler cannot see it is uniform)
+        const int mb_base = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
+        const bool live = mb_base < mb_tot;
+        const float* cur_buf = abuf + (it & 1) * CI * W;
+        const int g0 = cur_c * a.taps;
+        // The weights of tap j + 1 load while tap j multiplies; the LDS
+        // operands are read per tap and the second resident workgroup
+        // covers their latency (a deeper software pipeline measured slower:
+        // its registers cost the second workgroup).
+        for (int j = 0; j < a.taps; ++j) {
+            float4 Ac[MBW];
 #pragma unroll
-                for (int mb = 0; mb < MBW; ++mb) Ac[mb] = An[mb];
-                load_a(g + 1);
-                const float* brow = cur + hi * W + colbase + j * a.dil;
-                float Bv[4][NBW];
+            for (int mb = 0; mb < MBW; ++mb) Ac[mb] = An[mb];
+            if (j + 1 < a.taps) {
+                load_a(An, mb_base, cur.ph, g0 + j + 1);
+            } else if (has_next) {
+                load_a(An, __builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW), nxt.ph, nxt_c * a.taps);
+            }
+            if (!live) continue;
+            float Bv[4][NBW];
+            load_b(Bv, cur_buf, j);
+            mfma_tap(Ac, Bv);
+        }
+        if (cur_c == nch - 1) {
+            if (live) {
+                const int64_t ostride = (int64_t)a.out_mul * a.positions;
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
+                for (int mb = 0; mb < MBW; ++mb) {
 #pragma unroll
-                    for (int nb = 0; nb < NBW; ++nb) Bv[p][nb] = brow[2 * p * W + nb * 32];
+                    for (int nb = 0; nb < NBW; ++nb) {
+                        const int pos = cur.p0 + wn * NBW * 32 + nb * 32 + lo;
+                        if (pos >= a.positions) continue;
+                        const int tt = a.out_mul * pos + a.out_add[cur.ph];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-#pragma unroll
-                    for (int mb = 0; mb < MBW; ++mb) {
-                        const float av = p == 0 ? Ac[mb].x : (p == 1 ? Ac[mb].y : (p == 2 ? Ac[mb].z : Ac[mb].w));
-                        if constexpr (BF16) {
-                            // three-term bfloat16 split: ah*bh + al*bh + ah*bl
-                            const float ah = round_bf16(av), al = round_bf16(av - ah);
-#pragma unroll
-                            for (int nb = 0; nb < NBW; ++nb) {
-                                const float bh = round_bf16(Bv[p][nb]), bl = round_bf16(Bv[p][nb] - bh);
-                                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(ah, bh, acc[mb][nb], 0, 0, 0);
-                                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(al, bh, acc[mb][nb], 0, 0, 0);
-                                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(ah, bl, acc[mb][nb], 0, 0, 0);
-                            }
-                        } else {
-#pragma unroll
-                            for (int nb = 0; nb < NBW; ++nb)
-                                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, Bv[p][nb], acc[mb][nb], 0, 0, 0);
+                        for (int r = 0; r < 16; ++r) {
+                            const int o = (mb_base + mb) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                            if (o >= a.c_out) continue;
+                            const int64_t idx = (int64_t)cur.b * a.y_bstride + (int64_t)o * ostride + tt;
+                            float v = acc[mb][nb][r];
+                            if (a.bias) v += a.bias[o];
+                            if (a.res) v += a.res[idx];
+                            if (a.sum_in) v += a.sum_in[idx];
+                            a.y[idx] = v * a.scale;
                         }
                     }
                 }
             }
+            zero_acc();
         }
+        cur = nxt;
+        cur_c = nxt_c;
         __syncthreads();
-    }
-
-    if (!wave_live) return;
-    const int64_t ostride = (int64_t)a.out_mul * a.positions;
-#pragma unroll
-    for (int mb = 0; mb < MBW; ++mb) {
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-            const int pos = p0 + wn * NBW * 32 + nb * 32 + lo;
-            if (pos >= a.positions) continue;
-            const int t = a.out_mul * pos + a.out_add[ph];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int o = (mb_base + mb) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                if (o >= a.c_out) continue;
-                const int64_t idx = (int64_t)b * a.y_bstride + (int64_t)o * ostride + t;
-                float v = acc[mb][nb][r];
-                if (a.bias) v += a.bias[o];
-                if (a.res) v += a.res[idx];
-                if (a.sum_in) v += a.sum_in[idx];
-                a.y[idx] = v * a.scale;
-            }
-        }
     }
 }
 
@@ -291,35 +477,54 @@ TileShape tile_shape(TileId t) {
     }
 }
 
-template <int MBW, int NBW, int WM, int WN>
-static hipError_t launch_tile(const ConvArgs& a, int batch, hipStream_t stream) {
-    constexpr int NWG = WN * NBW * 32;
-    constexpr int MWG = WM * MBW * 32;
-    const int W = NWG + (a.taps - 1) * a.dil;
-    dim3 grid((a.positions + NWG - 1) / NWG, (a.c_out + MWG - 1) / MWG, batch * a.phases);
-    const bool act = a.act.taps != nullptr;
-    const size_t lds = sizeof(float) * (size_t)conv_lds_floats(W, act);
-    if (lds > 160 * 1024) return hipErrorInvalidValue;
-    if (act && a.bf16) {
-        auto k = conv_kernel<MBW, NBW, WM, WN, true, true>;
-        if (lds > 64 * 1024) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL(k, grid, dim3(512), lds, stream, a);
-    } else if (act) {
-        auto k = conv_kernel<MBW, NBW, WM, WN, true, false>;
-        if (lds > 64 * 1024) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL(k, grid, dim3(512), lds, stream, a);
-    } else {
-        auto k = conv_kernel<MBW, NBW, WM, WN, false, false>;
-        if (lds > 64 * 1024) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL(k, grid, dim3(512), lds, stream, a);
+template <typename K>
+static hipError_t launch_persistent(K kernel, const ConvArgs& a, int64_t tiles, size_t lds, hipStream_t stream) {
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
     }
+    // One slot per resident workgroup; cached per (kernel, LDS size).
+    static thread_local const void* last_k = nullptr;
+    static thread_local size_t last_lds = 0;
+    static thread_local int last_slots = 0;
+    int slots;
+    if (last_k == (const void*)kernel && last_lds == lds) {
+        slots = last_slots;
+    } else {
+        int per_cu = 0, dev = 0, cus = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 512, lds);
+        if (e != hipSuccess) return e;
+        if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        slots = std::max(1, per_cu) * std::max(1, cus);
+        last_k = (const void*)kernel;
+        last_lds = lds;
+        last_slots = slots;
+    }
+    const int64_t grid = std::min<int64_t>(tiles, slots);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(512), lds, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_conv(const ConvArgs& a, int batch, TileId tile, hipStream_t stream) {
+template <int MBW, int NBW, int WM, int WN>
+static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
+    constexpr int NWG = WN * NBW * 32;
+    constexpr int MWG = WM * MBW * 32;
+    const int W = NWG + (a.taps - 1) * a.dil;
+    const int64_t tiles =
+        (int64_t)((a.positions + NWG - 1) / NWG) * ((a.c_out + MWG - 1) / MWG) * a.groups;
+    const bool act = a.act.taps != nullptr;
+    const size_t lds = sizeof(float) * (size_t)conv_lds_floats(W, act);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    if (act && a.bf16) return launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, true>, a, tiles, lds, stream);
+    if (act) return launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, false>, a, tiles, lds, stream);
+    return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, false>, a, tiles, lds, stream);
+}
+
+hipError_t launch_conv(const ConvArgs& a, TileId tile, hipStream_t stream) {
     switch (tile) {
 #define MH3A_TILE(id, mbw, nbw, wm, wn) \
-    case id: return launch_tile<mbw, nbw, wm, wn>(a, batch, stream);
+    case id: return launch_tile<mbw, nbw, wm, wn>(a, stream);
         MH3A_TILE_LIST
 #undef MH3A_TILE
         default: return hipErrorInvalidValue;
@@ -335,9 +540,9 @@ constexpr int kFinalT = 256;
 __global__ void __launch_bounds__(256) final_kernel(FinalArgs a) {
     constexpr int CI = kChunk;
     constexpr int W = kFinalT + 6;
-    __shared__ float as[CI * W];
-    __shared__ float xs[CI * (W + 12)];
-    __shared__ float ss[CI * (2 * W + 12)];
+    __shared__ __attribute__((aligned(16))) float as[CI * W];
+    __shared__ __attribute__((aligned(16))) float xs[CI * act_xs_len(W)];
+    __shared__ __attribute__((aligned(16))) float ss[CI * act_ss_len(W)];
     const int b = blockIdx.y;
     const int t0 = blockIdx.x * kFinalT;
     const float* xb = a.x + (int64_t)b * a.x_bstride;
