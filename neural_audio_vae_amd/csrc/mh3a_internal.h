@@ -74,6 +74,12 @@ enum TileId {
 #undef MH3A_TILE
     TILE_COUNT
 };
+// Tiles with act-fused instances specialized for 3, 7 and 11 taps (the
+// shapes the tile model picks for the AMP convs); other shapes run those
+// convs with a runtime tap count.
+constexpr bool tile_has_act_taps(int t) {
+    return t == TILE_256x96 || t == TILE_256x64 || t == TILE_128x128 || t == TILE_64x256 || t == TILE_32x256;
+}
 struct TileShape {
     int m, n;
 };

@@ -208,7 +208,7 @@ __host__ __device__ constexpr int conv_lds_floats(int W, bool act) {
 // tile) into the other half of a double-buffered LDS window, so the
 // epilogue of one tile overlaps the staging of the next. One workgroup
 // barrier per item hands the buffers over.
-template <int MBW, int NBW, int WM, int WN, bool ACT, bool BF16>
+template <int MBW, int NBW, int WM, int WN, bool ACT, bool BF16, int TAPS>
 __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     static_assert(WM * WN == 4, "four consumer waves");
     constexpr int CI = kChunk;
@@ -323,6 +323,14 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
                 dst[mb] = mb_base + mb < mb_tot ? wp[(int64_t)mb * G * 64] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
+    // Branch-free variant: blocks past c_out read the last valid block (their
+    // rows are discarded in the epilogue), so no exec-mask branch breaks the
+    // counter waits of the unrolled tap loop.
+    auto load_a_nb = [&](float4 (&dst)[MBW], int mb_base, int ph, int g) {
+        const float4* wp = reinterpret_cast<const float4*>(a.w + (int64_t)ph * a.w_phase_stride) + g * 64 + lane;
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) dst[mb] = wp[(int64_t)min(mb_base + mb, mb_tot - 1) * G * 64];
+    };
     // B operand of one tap: the 4 channel pairs x NBW blocks of 32 positions
     auto load_b = [&](float (&dst)[4][NBW], const float* buf, int j) {
         const float* brow = buf + hi * W + colbase + j * a.dil;
@@ -401,7 +409,15 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     Tile cur = tile_at(t_begin);
     int cur_c = 0;
     zero_acc();
-    load_a(An, __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW), cur.ph, 0);
+    float4 Ar0[MBW], Ar1[MBW], Ar2[MBW];
+    if constexpr (TAPS > 0) {
+        const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
+        load_a_nb(Ar0, mb0, cur.ph, 0);
+        load_a_nb(Ar1, mb0, cur.ph, 1);
+    } else {
+        load_a(An, __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW), cur.ph, 0);
+    }
+    (void)Ar2;
     __syncthreads();
     for (int it = 0; it < n_items; ++it) {
         // the item after this one
@@ -417,23 +433,68 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
         const bool live = mb_base < mb_tot;
         const float* cur_buf = abuf + (it & 1) * CI * W;
         const int g0 = cur_c * a.taps;
-        // The weights of tap j + 1 load while tap j multiplies; the LDS
-        // operands are read per tap and the second resident workgroup
-        // covers their latency (a deeper software pipeline measured slower:
-        // its registers cost the second workgroup).
-        for (int j = 0; j < a.taps; ++j) {
-            float4 Ac[MBW];
+        if constexpr (TAPS > 0) {
+            // Compile-time tap count: the tap loop is fully unrolled and
+            // branch-free. The weights ride a three-slot register ring loaded
+            // two taps ahead (one tap of MFMAs does not cover the L2
+            // latency); the last two taps prefetch the next item's first two.
+            // Slots 0 and 1 hold taps 0 and 1 of the current item on entry.
+            const int nmb_base = __builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW);
+            const int nph = has_next ? nxt.ph : cur.ph;
+            const int ng0 = has_next ? nxt_c * TAPS : g0;
+            const int nmb = has_next ? nmb_base : mb_base;
 #pragma unroll
-            for (int mb = 0; mb < MBW; ++mb) Ac[mb] = An[mb];
-            if (j + 1 < a.taps) {
-                load_a(An, mb_base, cur.ph, g0 + j + 1);
-            } else if (has_next) {
-                load_a(An, __builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW), nxt.ph, nxt_c * a.taps);
+            for (int j = 0; j < TAPS; ++j) {
+                float4(&use)[MBW] = (j % 3 == 0) ? Ar0 : ((j % 3 == 1) ? Ar1 : Ar2);
+                float4(&fill)[MBW] = ((j + 2) % 3 == 0) ? Ar0 : (((j + 2) % 3 == 1) ? Ar1 : Ar2);
+                if (j + 2 < TAPS) {
+                    load_a_nb(fill, mb_base, cur.ph, g0 + j + 2);
+                } else {
+                    load_a_nb(fill, nmb, nph, ng0 + (j + 2 - TAPS));
+                }
+                // keep the prefetch at the top of the tap: the scheduler would
+                // otherwise sink it next to its use two taps later
+                __builtin_amdgcn_sched_barrier(0);
+                float Bv[4][NBW];
+                load_b(Bv, cur_buf, j);
+                // issue all of the tap's LDS reads before its MFMAs
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_tap(use, Bv);
             }
-            if (!live) continue;
-            float Bv[4][NBW];
-            load_b(Bv, cur_buf, j);
-            mfma_tap(Ac, Bv);
+            // the next item's taps 0 and 1 sit in slots TAPS % 3, (TAPS + 1) % 3
+            if constexpr (TAPS % 3 == 1) {
+#pragma unroll
+                for (int mb = 0; mb < MBW; ++mb) {
+                    Ar0[mb] = Ar1[mb];
+                    Ar1[mb] = Ar2[mb];
+                }
+            } else if constexpr (TAPS % 3 == 2) {
+#pragma unroll
+                for (int mb = 0; mb < MBW; ++mb) {
+                    const float4 t0 = Ar2[mb];
+                    Ar1[mb] = Ar0[mb];
+                    Ar0[mb] = t0;
+                }
+            }
+        } else {
+            // Runtime tap count: the weights of tap j + 1 load while tap j
+            // multiplies; the LDS operands are read per tap and the second
+            // resident workgroup covers their latency.
+            for (int j = 0; j < a.taps; ++j) {
+                float4 Ac[MBW];
+#pragma unroll
+                for (int mb = 0; mb < MBW; ++mb) Ac[mb] = An[mb];
+                if (j + 1 < a.taps) {
+                    load_a(An, mb_base, cur.ph, g0 + j + 1);
+                } else if (has_next) {
+                    load_a(An, __builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW), nxt.ph,
+                           nxt_c * a.taps);
+                }
+                if (!live) continue;
+                float Bv[4][NBW];
+                load_b(Bv, cur_buf, j);
+                mfma_tap(Ac, Bv);
+            }
         }
         if (cur_c == nch - 1) {
             if (live) {
@@ -506,7 +567,7 @@ static hipError_t launch_persistent(K kernel, const ConvArgs& a, int64_t tiles, 
     return hipGetLastError();
 }
 
-template <int MBW, int NBW, int WM, int WN>
+template <int MBW, int NBW, int WM, int WN, bool ACT_TILE>
 static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
     constexpr int NWG = WN * NBW * 32;
     constexpr int MWG = WM * MBW * 32;
@@ -516,15 +577,27 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
     const bool act = a.act.taps != nullptr;
     const size_t lds = sizeof(float) * (size_t)conv_lds_floats(W, act);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
-    if (act && a.bf16) return launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, true>, a, tiles, lds, stream);
-    if (act) return launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, false>, a, tiles, lds, stream);
-    return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, false>, a, tiles, lds, stream);
+    if (act) {
+        if constexpr (ACT_TILE) {
+#define MH3A_ACT_TAPS(T)                                                                                            \
+    if (a.taps == T)                                                                                               \
+        return a.bf16 ? launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, true, T>, a, tiles, lds, stream)     \
+                      : launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, false, T>, a, tiles, lds, stream);
+            MH3A_ACT_TAPS(3)
+            MH3A_ACT_TAPS(7)
+            MH3A_ACT_TAPS(11)
+#undef MH3A_ACT_TAPS
+        }
+        return a.bf16 ? launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, true, 0>, a, tiles, lds, stream)
+                      : launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, false, 0>, a, tiles, lds, stream);
+    }
+    return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, false, 0>, a, tiles, lds, stream);
 }
 
 hipError_t launch_conv(const ConvArgs& a, TileId tile, hipStream_t stream) {
     switch (tile) {
 #define MH3A_TILE(id, mbw, nbw, wm, wn) \
-    case id: return launch_tile<mbw, nbw, wm, wn>(a, stream);
+    case id: return launch_tile<mbw, nbw, wm, wn, tile_has_act_taps(id)>(a, stream);
         MH3A_TILE_LIST
 #undef MH3A_TILE
         default: return hipErrorInvalidValue;
