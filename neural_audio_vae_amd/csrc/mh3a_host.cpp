@@ -284,7 +284,11 @@ void add_conv(Blob& blob, ConvLayer& L, const std::vector<float>& w, const float
     const int64_t n = packed_weight_floats(c_out, c_in, taps);
     L.w_off = blob.reserve(n);
     pack_conv_weights(w.data(), c_out, c_in, taps, blob.h.data() + L.w_off);
-    L.b_off = bias ? blob.add(bias, c_out) : -1;
+    if (bias) {
+        L.b_off = blob.add(bias, c_out);
+    } else {
+        L.b_off = blob.reserve(c_out);  // zeros: the kernels always add a bias
+    }
 }
 
 int add_act(Blob& blob, const Table& t, const std::string& prefix, int c, const float* designed,
@@ -397,9 +401,16 @@ TileId choose_tile(const ConvLayer& L, int positions, int groups, bool bf16) {
     TileId pick = TILE_32x256;
     const bool act = L.act >= 0;
     const int mpad = ((L.c_out + 31) / 32) * 32;
-    // With at most 32 output channels the activation producers bound the
-    // kernel; the narrow window measured fastest (more resident workgroups).
-    if (act && L.c_out <= 32) return TILE_32x256;
+    // The act-fused AMP convs use the shapes measured fastest per width in a
+    // tile sweep of every stage (one-workgroup-per-CU shapes only pay off at
+    // 512 channels, where they fill the 256 CUs in one round).
+    if (act) {
+        if (L.c_out >= 512) return TILE_256x96;
+        if (L.c_out >= 256) return TILE_256x64;
+        if (L.c_out >= 128) return TILE_128x128;
+        if (L.c_out >= 64) return TILE_64x256;
+        return TILE_32x256;
+    }
     for (int id = 0; id < TILE_COUNT; ++id) {
         const TileShape s = tile_shape((TileId)id);
         if (s.m > mpad && s.m > 32) continue;  // consumer waves would idle
@@ -541,7 +552,8 @@ int check_decode_args(const mh3a_decoder* d, int64_t batch, int64_t frames, uint
     // every per-item length must fit the kernels' 32-bit positions
     if ((int64_t)d->cfg.hop_length * frames > (int64_t)1 << 30)
         return fail(MH3A_E_INVALID_ARG, "frames too large: %lld output samples per item", (long long)(d->cfg.hop_length * frames));
-    if (max_cl(d, frames) * batch > ((int64_t)1 << 40)) return fail(MH3A_E_INVALID_ARG, "problem too large");
+    // the kernels address one batch item's tensor with 32-bit byte offsets
+    if (max_cl(d, frames) >= ((int64_t)1 << 29)) return fail(MH3A_E_INVALID_ARG, "frames too large for one item");
     return MH3A_OK;
 }
 
@@ -949,7 +961,8 @@ int mh3a_amp_stage_workspace_size(const mh3a_decoder* d, int stage, int64_t batc
     *bytes = 0;
     if (!d) return fail(MH3A_E_INVALID_ARG, "decoder is null");
     if (stage < 0 || stage >= d->cfg.num_ups) return fail(MH3A_E_INVALID_ARG, "stage %d out of range", stage);
-    if (batch < 1 || batch > 4096 || length < 1 || length > ((int64_t)1 << 30))
+    if (batch < 1 || batch > 4096 || length < 1 || length > ((int64_t)1 << 30) ||
+        (int64_t)d->stage_c[stage] * length >= ((int64_t)1 << 29))
         return fail(MH3A_E_INVALID_ARG, "bad batch or length");
     *bytes = (size_t)(2 * round_up(batch * d->stage_c[stage] * length, 64) * (int64_t)sizeof(float));
     return ok();

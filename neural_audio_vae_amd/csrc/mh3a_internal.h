@@ -62,6 +62,7 @@ struct ConvArgs {
     MH3A_TILE(TILE_256x128, 2, 4, 4, 1)  /* 256 x 128 */           \
     MH3A_TILE(TILE_256x96, 2, 3, 4, 1)   /* 256 x  96 */           \
     MH3A_TILE(TILE_256x64, 2, 2, 4, 1)   /* 256 x  64 */           \
+    MH3A_TILE(TILE_128x96, 1, 3, 4, 1)   /* 128 x  96 */           \
     MH3A_TILE(TILE_128x256, 2, 4, 2, 2)  /* 128 x 256 */           \
     MH3A_TILE(TILE_128x128, 2, 2, 2, 2)  /* 128 x 128 */           \
     MH3A_TILE(TILE_64x512, 2, 4, 1, 4)   /*  64 x 512 */           \
@@ -78,7 +79,7 @@ enum TileId {
 // shapes the tile model picks for the AMP convs); other shapes run those
 // convs with a runtime tap count.
 constexpr bool tile_has_act_taps(int t) {
-    return t == TILE_256x96 || t == TILE_256x64 || t == TILE_128x128 || t == TILE_64x256 || t == TILE_32x256;
+    return t == TILE_256x96 || t == TILE_256x64 || t == TILE_128x96 || t == TILE_128x128 || t == TILE_64x256 || t == TILE_32x256;
 }
 struct TileShape {
     int m, n;

@@ -28,6 +28,7 @@ namespace mh3a {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // SnakeBeta at the 2x rate: u + sin^2(alpha u) / beta, written as
@@ -302,13 +303,23 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     const int colbase = wn * NBW * 32 + lo;
 
     v16f acc[MBW][NBW];
-    auto zero_acc = [&]() {
+    // Accumulators start at the bias: one MFMA of the bias column (lanes
+    // 0-31 hold bias[row], K index 0) against a ones row (K index 0).
+    float bias_frag[MBW];
+    auto load_bias = [&](int mb_base) {
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb)
+            bias_frag[mb] = hi == 0 ? a.bias[min((mb_base + mb) * 32 + lo, a.c_out - 1)] : 0.0f;
+    };
+    auto init_acc = [&]() {
+        const float ones = hi == 0 ? 1.0f : 0.0f;
+        v16f z;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z[r] = 0.0f;
 #pragma unroll
         for (int i = 0; i < MBW; ++i)
 #pragma unroll
-            for (int j = 0; j < NBW; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int j = 0; j < NBW; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bias_frag[i], ones, z, 0, 0, 0);
     };
     // A operand of K-group g for the M blocks starting at mb_base, phase ph
     auto load_a = [&](float4 (&dst)[MBW], int mb_base, int ph, int g) {
@@ -408,7 +419,8 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
 
     Tile cur = tile_at(t_begin);
     int cur_c = 0;
-    zero_acc();
+    load_bias(__builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW));
+    init_acc();
     float4 Ar0[MBW], Ar1[MBW], Ar2[MBW];
     if constexpr (TAPS > 0) {
         const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
@@ -430,6 +442,8 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
         }
         // wave-uniform M-block base (the compiler cannot see it is uniform)
         const int mb_base = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
+        // the next tile's bias, in flight during this item
+        if (nxt_c == 0 && has_next) load_bias(__builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW));
         const bool live = mb_base < mb_tot;
         const float* cur_buf = abuf + (it & 1) * CI * W;
         const int g0 = cur_c * a.taps;
@@ -497,6 +511,8 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
             }
         }
         if (cur_c == nch - 1) {
+            // Per-element epilogue (a batched variant measured no faster: its
+            // registers cost resident workgroups).
             if (live) {
                 const int64_t ostride = (int64_t)a.out_mul * a.positions;
 #pragma unroll
@@ -512,7 +528,6 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
                             if (o >= a.c_out) continue;
                             const int64_t idx = (int64_t)cur.b * a.y_bstride + (int64_t)o * ostride + tt;
                             float v = acc[mb][nb][r];
-                            if (a.bias) v += a.bias[o];
                             if (a.res) v += a.res[idx];
                             if (a.sum_in) v += a.sum_in[idx];
                             a.y[idx] = v * a.scale;
@@ -520,7 +535,7 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
                     }
                 }
             }
-            zero_acc();
+            init_acc();
         }
         cur = nxt;
         cur_c = nxt_c;
