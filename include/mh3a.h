@@ -67,7 +67,15 @@ extern "C" {
 /* Skip the final clamp (a test hook: most samples saturate under random
  * weights, so the unclamped signal is the sharper comparison). */
 #define MH3A_FLAG_NO_CLAMP 0x4u
-#define MH3A_FLAG_ALL 0x7u
+/* Plan every convolution from one batch item's shape alone, so that the
+ * order in which each output's terms are summed, and hence every bit of an
+ * item's result, is the same whatever batch the item is decoded in. By
+ * default launches with few output tiles split the contraction into ranges
+ * summed by a second pass, with the number of ranges chosen for the whole
+ * batch (fastest, deterministic for a given batch, but a different batch
+ * size may round differently). */
+#define MH3A_FLAG_BATCH_INVARIANT 0x8u
+#define MH3A_FLAG_ALL 0xFu
 
 /* ---- architecture limits ---- */
 #define MH3A_MAX_STAGES 8
@@ -180,7 +188,8 @@ int mh3a_decode_partial(mh3a_decoder* dec, const float* latents, int64_t batch, 
 /*
  * One stage's AMP set alone (FastVideo "minimax_h3_audio_vae", decode: the
  * blocks of stage s run from the same input and are averaged): x device
- * (B, C_s, L) -> y device (B, C_s, L). Flags: 0 or MH3A_FLAG_BF16_MFMA.
+ * (B, C_s, L) -> y device (B, C_s, L). Flags: MH3A_FLAG_BF16_MFMA and / or
+ * MH3A_FLAG_BATCH_INVARIANT.
  * Workspace from mh3a_amp_stage_workspace_size.
  */
 int mh3a_amp_stage_workspace_size(const mh3a_decoder* dec, int stage, int64_t batch, int64_t length,

@@ -9,5 +9,6 @@ Importing the package does not load the library; constructing a Decoder
 does, and fails if libmh3a.so has not been built.
 """
 
-from ._lib import MH3A_FLAG_BF16_MFMA, MH3A_FLAG_DENORMALIZE, MH3A_FLAG_NO_CLAMP, MH3AError  # noqa: F401
+from ._lib import (MH3A_FLAG_BATCH_INVARIANT, MH3A_FLAG_BF16_MFMA, MH3A_FLAG_DENORMALIZE,  # noqa: F401
+                   MH3A_FLAG_NO_CLAMP, MH3AError)  # noqa: F401
 from .decoder import Decoder  # noqa: F401

@@ -16,7 +16,9 @@
 #include <cstring>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "mh3a.h"
@@ -168,6 +170,9 @@ struct ActLayer {
 
 }  // namespace
 
+// Launch shape of one conv: (layer, positions, batch, bf16 operands | batch-invariant plan << 1).
+using PlanKey = std::tuple<const void*, int, int, int>;
+
 struct mh3a_decoder {
     mh3a_config cfg;
     int device = 0;
@@ -181,7 +186,10 @@ struct mh3a_decoder {
     int64_t post_w_off = -1;
     float post_bias = 0.0f;
     std::vector<int> stage_c;   // output channels per stage
+    int num_cus = 256;          // compute units of `device`
     mutable Timing timing;
+    mutable std::mutex plan_mu;                          // guards plans
+    mutable std::map<PlanKey, std::pair<int, int>> plans;  // (tile, ksplit) per launch shape
 };
 
 namespace {
@@ -359,7 +367,9 @@ TileGeom tile_geom(TileId t) {
     }
 }
 
-double tile_cost(const ConvLayer& L, TileId id, int positions, int groups, bool bf16) {
+// With a K split of S ranges the launch has S times the workgroups, each
+// walking nch / S chunks, plus a reduce pass over the S partial tiles.
+double tile_cost(const ConvLayer& L, TileId id, int positions, int groups, bool bf16, int ksplit, int num_cus) {
     const TileShape s = tile_shape(id);
     const TileGeom g = tile_geom(id);
     const bool act = L.act >= 0;
@@ -367,15 +377,22 @@ double tile_cost(const ConvLayer& L, TileId id, int positions, int groups, bool 
     const int W = s.n + (L.taps - 1) * L.dil;
     const double mt = (L.c_out + s.m - 1) / s.m;
     const double nt = (positions + s.n - 1) / s.n;
-    const double wgs = mt * nt * groups;
+    const double wgs = mt * nt * groups * ksplit;
     const int occ = (g.mbw * g.nbw <= 4) ? 2 : 1;
-    const double rounds = std::ceil(wgs / (256.0 * occ));
+    const double rounds = std::ceil(wgs / ((double)num_cus * occ));
+    const double shared = std::min<double>(occ, std::ceil(wgs / num_cus));  // workgroups sharing a CU
     const double eff = occ == 2 ? 0.65 : 0.58;
     const double t_cons = (double)L.taps * 4 * g.mbw * g.nbw * 64 * (act && bf16 ? 3 : 1) / eff;
     const double t_prod = (act ? 12.0 : 2.0) * W + 400;
     const double t_chunk = std::max(t_cons, t_prod) + 200;
     const double t_epi = 16.0 * g.mbw * g.nbw * 40 + 2000;
-    return rounds * occ * (nch * t_chunk + t_epi);
+    double cost = rounds * shared * ((double)(nch / ksplit) * t_chunk + t_epi);
+    if (ksplit > 1) {
+        // one more launch (~3 us) streaming S partials in and the output out
+        const double outs = mt * s.m * nt * s.n * groups;
+        cost += 8000.0 + (ksplit + 2.0) * outs * 4.0 / 1700.0;
+    }
+    return cost;
 }
 
 // MH3A_CONV_TILE=<index into MH3A_TILE_LIST> forces one tile shape for
@@ -390,7 +407,14 @@ int forced_tile() {
     return v;
 }
 
-TileId choose_tile(const ConvLayer& L, int positions, int groups, bool bf16) {
+bool tile_fits(const ConvLayer& L, TileId id) {
+    const TileShape s = tile_shape(id);
+    const int W = s.n + (L.taps - 1) * L.dil;
+    const int lds_floats = 2 * kChunk * W + (L.act >= 0 ? kChunk * (3 * W + 32) : 0);
+    return lds_floats * 4 <= 160 * 1024;
+}
+
+TileId choose_tile(const ConvLayer& L, int positions, int groups, bool bf16, int ksplit, int num_cus) {
     if (forced_tile() >= 0) {
         const TileShape s = tile_shape((TileId)forced_tile());
         const int W = s.n + (L.taps - 1) * L.dil;
@@ -417,13 +441,74 @@ TileId choose_tile(const ConvLayer& L, int positions, int groups, bool bf16) {
         const int W = s.n + (L.taps - 1) * L.dil;
         const int lds_floats = 2 * kChunk * W + (act ? kChunk * (3 * W + 32) : 0);
         if (lds_floats * 4 > 160 * 1024) continue;
-        const double cost = tile_cost(L, (TileId)id, positions, groups, bf16);
+        const double cost = tile_cost(L, (TileId)id, positions, groups, bf16, ksplit, num_cus);
         if (cost < best) {
             best = cost;
             pick = (TileId)id;
         }
     }
     return pick;
+}
+
+// Launch plan of one conv: tile shape and K split. Splits are powers of two
+// dividing the chunk count, picked by the cost model for the batch's
+// geometry, or with `invariant` for one item's (groups = phases), so that
+// the order in which an output's terms are summed does not depend on the
+// batch size. The tile shape never changes that order. The bound on the
+// partial sums keeps the workspace modest.
+struct ConvPlan {
+    TileId tile;
+    int ksplit;
+};
+constexpr int64_t kMaxPartialFloats = (int64_t)32 << 20;
+
+int64_t plan_partial_floats(const ConvLayer& L, int positions, int groups, const ConvPlan& p) {
+    if (p.ksplit <= 1) return 0;
+    const TileShape s = tile_shape(p.tile);
+    return (int64_t)p.ksplit * ((L.c_out + s.m - 1) / s.m) * ((positions + s.n - 1) / s.n) * groups * s.m * s.n;
+}
+
+ConvPlan plan_conv_uncached(const mh3a_decoder* d, const ConvLayer& L, int positions, int batch, bool bf16,
+                            bool invariant) {
+    const int nch = (L.c_in + kChunk - 1) / kChunk;
+    const int item_groups = invariant ? L.phases : batch * L.phases;
+    int best_s = 1;
+    double best = 1e300;
+    for (int S = 1; S <= 64 && S <= nch; S *= 2) {
+        if (nch % S) continue;
+        const TileId t = choose_tile(L, positions, item_groups, bf16, S, d->num_cus);
+        // the batch's own tile must keep the partials bounded too
+        const TileId tb = choose_tile(L, positions, batch * L.phases, bf16, S, d->num_cus);
+        if (S > 1 && plan_partial_floats(L, positions, batch * L.phases, {tb, S}) > kMaxPartialFloats) break;
+        const double c = tile_cost(L, t, positions, item_groups, bf16, S, d->num_cus);
+        if (c < 0.97 * best) {
+            best = c;
+            best_s = S;
+        }
+    }
+    return {choose_tile(L, positions, batch * L.phases, bf16, best_s, d->num_cus), best_s};
+}
+
+ConvPlan plan_conv(const mh3a_decoder* d, const ConvLayer& L, int positions, int batch, bool bf16, bool invariant) {
+    const PlanKey key{&L, positions, batch, (bf16 ? 1 : 0) | (invariant ? 2 : 0)};
+    std::lock_guard<std::mutex> lock(d->plan_mu);
+    auto it = d->plans.find(key);
+    if (it != d->plans.end()) return {(TileId)it->second.first, it->second.second};
+    const ConvPlan p = plan_conv_uncached(d, L, positions, batch, bf16, invariant);
+    // MH3A_PLAN_LOG=1 prints each new plan to stderr (a tuning aid)
+    static const bool log = [] {
+        const char* e = std::getenv("MH3A_PLAN_LOG");
+        return e && *e == '1';
+    }();
+    if (log) {
+        const TileShape ts = tile_shape(p.tile);
+        std::fprintf(stderr, "mh3a plan: %s c_in %d c_out %d taps %d dil %d positions %d batch %d%s -> tile %dx%d ksplit %d\n",
+                     kKindNames[L.kind], L.c_in, L.c_out, L.taps, L.dil, positions, batch, invariant ? " (invariant)" : "",
+                     ts.m, ts.n, p.ksplit);
+    }
+    if (d->plans.size() > 4096) d->plans.clear();
+    d->plans.emplace(key, std::make_pair((int)p.tile, p.ksplit));
+    return p;
 }
 
 // ---------------------------------------------------------------------------
@@ -459,9 +544,10 @@ struct TimedLaunch {
     }
 };
 
+// `partial` holds at least the plan's partial sums (plan_partial_floats).
 hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, int64_t x_bstride, int l_in,
                     int positions, float* y, int64_t y_bstride, int batch, const float* res, const float* sum_in,
-                    float scale, bool bf16, hipStream_t st) {
+                    float scale, bool bf16, bool invariant, float* partial, hipStream_t st) {
     ConvArgs a;
     std::memset(&a, 0, sizeof a);
     a.x = x;
@@ -489,8 +575,12 @@ hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, i
     a.scale = scale;
     a.act = act_params(d, L.act);
     a.bf16 = bf16 ? 1 : 0;
+    const ConvPlan plan = plan_conv(d, L, positions, batch, bf16, invariant);
+    a.ksplit = plan.ksplit;
+    a.partial = partial;
+    if (plan.ksplit > 1 && !partial) return hipErrorInvalidValue;
     TimedLaunch tl(d, st);
-    hipError_t e = launch_conv(a, choose_tile(L, positions, batch * L.phases, bf16), st);
+    hipError_t e = launch_conv(a, plan.tile, st);
     const double outs = (double)batch * L.c_out * L.out_mul * positions;
     const double flops = 2.0 * L.c_out * (double)L.c_in * L.alg_taps * positions * batch;
     const double bytes = 4.0 * ((double)batch * L.c_in * l_in + outs * (1 + (res ? 1 : 0) + (sum_in ? 1 : 0)) +
@@ -522,7 +612,7 @@ int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 // result in s_buf. Blocks run from the same h and are averaged in the
 // epilogue of each block's last conv.
 int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, float* t_buf, float* s_buf, int batch,
-            int64_t len, bool bf16, hipStream_t st) {
+            int64_t len, bool bf16, bool invariant, float* partial, hipStream_t st) {
     const mh3a_config& c = d->cfg;
     const int C = d->stage_c[stage];
     const int64_t bs = (int64_t)C * len;
@@ -533,12 +623,12 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, floa
             const ConvLayer& c1 = d->amp[stage][(j * nd + n) * 2 + 0];
             const ConvLayer& c2 = d->amp[stage][(j * nd + n) * 2 + 1];
             const float* xin = (n == 0) ? h : x_buf;
-            HIP_TRY(run_conv(d, c1, xin, bs, L, L, t_buf, bs, batch, nullptr, nullptr, 1.0f, bf16, st));
+            HIP_TRY(run_conv(d, c1, xin, bs, L, L, t_buf, bs, batch, nullptr, nullptr, 1.0f, bf16, invariant, partial, st));
             const bool last = (n == nd - 1);
             float* yout = last ? s_buf : x_buf;
             const float* sum_in = (last && j > 0) ? s_buf : nullptr;
             const float scale = (last && j == nrb - 1) ? 1.0f / (float)nrb : 1.0f;
-            HIP_TRY(run_conv(d, c2, t_buf, bs, L, L, yout, bs, batch, xin, sum_in, scale, bf16, st));
+            HIP_TRY(run_conv(d, c2, t_buf, bs, L, L, yout, bs, batch, xin, sum_in, scale, bf16, invariant, partial, st));
         }
     }
     return MH3A_OK;
@@ -557,8 +647,36 @@ int check_decode_args(const mh3a_decoder* d, int64_t batch, int64_t frames, uint
     return MH3A_OK;
 }
 
-size_t decode_ws_bytes(const mh3a_decoder* d, int64_t batch, int64_t frames) {
-    return (size_t)(4 * round_up(max_cl(d, frames) * batch, 64) * (int64_t)sizeof(float));
+// Largest partial-sum region any conv of one AMP stage needs.
+int64_t amp_partial_floats(const mh3a_decoder* d, int stage, int batch, int len, bool bf16, bool inv) {
+    int64_t m = 0;
+    for (const ConvLayer& L : d->amp[stage])
+        m = std::max(m, plan_partial_floats(L, len, batch * L.phases, plan_conv(d, L, len, batch, bf16, inv)));
+    return m;
+}
+
+// Largest partial-sum region any conv of a decode needs.
+// (in_proj, conv_pre and the upsamplers always run full fp32 operands.)
+int64_t decode_partial_floats(const mh3a_decoder* d, int batch, int frames, bool bf16, bool inv) {
+    const mh3a_config& c = d->cfg;
+    int64_t m = 0;
+    for (const ConvLayer* L : {&d->in_proj, &d->in_proj_dn, &d->conv_pre})
+        m = std::max(m, plan_partial_floats(*L, frames, batch * L->phases, plan_conv(d, *L, frames, batch, false, inv)));
+    int64_t len = frames;
+    for (int s = 0; s < c.num_ups; ++s) {
+        const ConvLayer& U = d->ups[s];
+        m = std::max(m, plan_partial_floats(U, (int)len, batch * U.phases, plan_conv(d, U, (int)len, batch, false, inv)));
+        len *= c.rates[s];
+        m = std::max(m, amp_partial_floats(d, s, batch, (int)len, bf16, inv));
+    }
+    return m;
+}
+
+size_t decode_ws_bytes(const mh3a_decoder* d, int64_t batch, int64_t frames, uint32_t flags) {
+    const int64_t slots = 4 * round_up(max_cl(d, frames) * batch, 64);
+    const bool bf16 = (flags & MH3A_FLAG_BF16_MFMA) != 0;
+    const bool inv = (flags & MH3A_FLAG_BATCH_INVARIANT) != 0;
+    return (size_t)((slots + decode_partial_floats(d, (int)batch, (int)frames, bf16, inv)) * (int64_t)sizeof(float));
 }
 
 int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, float* wave, int upto,
@@ -568,7 +686,7 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
     if (!z || (!wave && !out)) return fail(MH3A_E_INVALID_ARG, "null latents or output pointer");
     if (!ws) return fail(MH3A_E_WORKSPACE, "workspace is null");
     if ((uintptr_t)ws % 256) return fail(MH3A_E_WORKSPACE, "workspace must be 256-byte aligned");
-    const size_t need = decode_ws_bytes(d, batch, frames);
+    const size_t need = decode_ws_bytes(d, batch, frames, flags);
     if (ws_bytes < need) return fail(MH3A_E_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     const mh3a_config& c = d->cfg;
     const int B = (int)batch;
@@ -578,7 +696,9 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
     float* bufH = bufS + slot;
     float* bufX = bufH + slot;
     float* bufT = bufX + slot;
+    float* partial = bufT + slot;
     const bool bf16 = (flags & MH3A_FLAG_BF16_MFMA) != 0;
+    const bool invariant = (flags & MH3A_FLAG_BATCH_INVARIANT) != 0;
     HIP_TRY(hipSetDevice(d->device));
 
     auto finish = [&](const float* src, int64_t count) -> int {
@@ -588,10 +708,11 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
 
     const ConvLayer& inp = (flags & MH3A_FLAG_DENORMALIZE) ? d->in_proj_dn : d->in_proj;
     const int64_t zb = (int64_t)c.latent_channels * N;
-    HIP_TRY(run_conv(d, inp, z, zb, N, N, bufX, (int64_t)c.latent_dim * N, B, nullptr, nullptr, 1.0f, false, st));
+    HIP_TRY(run_conv(d, inp, z, zb, N, N, bufX, (int64_t)c.latent_dim * N, B, nullptr, nullptr, 1.0f, false, invariant,
+                     partial, st));
     if (upto == 0) return finish(bufX, (int64_t)B * c.latent_dim * N);
     HIP_TRY(run_conv(d, d->conv_pre, bufX, (int64_t)c.latent_dim * N, N, N, bufS, (int64_t)c.decoder_dim * N, B,
-                     nullptr, nullptr, 1.0f, false, st));
+                     nullptr, nullptr, 1.0f, false, invariant, partial, st));
     if (upto == 1) return finish(bufS, (int64_t)B * c.decoder_dim * N);
     int64_t len = N;
     int cin = c.decoder_dim;
@@ -599,9 +720,9 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
         const int C = d->stage_c[s];
         const int64_t lout = len * c.rates[s];
         HIP_TRY(run_conv(d, d->ups[s], bufS, (int64_t)cin * len, (int)len, (int)len, bufH, (int64_t)C * lout, B,
-                         nullptr, nullptr, 1.0f, false, st));
+                         nullptr, nullptr, 1.0f, false, invariant, partial, st));
         if (upto == 2 + 2 * s) return finish(bufH, (int64_t)B * C * lout);
-        rc = run_amp(d, s, bufH, bufX, bufT, bufS, B, lout, bf16, st);
+        rc = run_amp(d, s, bufH, bufX, bufT, bufS, B, lout, bf16, invariant, partial, st);
         if (rc) return rc;
         if (upto == 3 + 2 * s) return finish(bufS, (int64_t)B * C * lout);
         len = lout;
@@ -847,6 +968,8 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(MH3A_E_HIP, "no HIP device available");
     if (device >= ndev) return fail(MH3A_E_INVALID_ARG, "device %d out of range (%d devices)", device, ndev);
     HIP_TRY(hipSetDevice(device));
+    HIP_TRY(hipDeviceGetAttribute(&d->num_cus, hipDeviceAttributeMultiprocessorCount, device));
+    d->num_cus = std::max(1, d->num_cus);
     d->blob_floats = (int64_t)blob.h.size();
     HIP_TRY(hipMalloc((void**)&d->blob, sizeof(float) * blob.h.size()));
     HIP_TRY(hipMemcpy(d->blob, blob.h.data(), sizeof(float) * blob.h.size(), hipMemcpyHostToDevice));
@@ -913,7 +1036,7 @@ int mh3a_decode_workspace_size(const mh3a_decoder* d, int64_t batch, int64_t fra
     *bytes = 0;
     int rc = check_decode_args(d, batch, frames, flags);
     if (rc) return rc;
-    *bytes = decode_ws_bytes(d, batch, frames);
+    *bytes = decode_ws_bytes(d, batch, frames, flags);
     return ok();
 }
 
@@ -964,7 +1087,11 @@ int mh3a_amp_stage_workspace_size(const mh3a_decoder* d, int stage, int64_t batc
     if (batch < 1 || batch > 4096 || length < 1 || length > ((int64_t)1 << 30) ||
         (int64_t)d->stage_c[stage] * length >= ((int64_t)1 << 29))
         return fail(MH3A_E_INVALID_ARG, "bad batch or length");
-    *bytes = (size_t)(2 * round_up(batch * d->stage_c[stage] * length, 64) * (int64_t)sizeof(float));
+    // the partial region covers every flag combination (the flags come later)
+    int64_t part = 0;
+    for (int f = 0; f < 4; ++f)
+        part = std::max(part, amp_partial_floats(d, stage, (int)batch, (int)length, f & 1, f & 2));
+    *bytes = (size_t)((2 * round_up(batch * d->stage_c[stage] * length, 64) + part) * (int64_t)sizeof(float));
     return ok();
 }
 
@@ -974,7 +1101,8 @@ int mh3a_amp_stage(mh3a_decoder* d, int stage, const float* x, int64_t batch, in
     int rc = mh3a_amp_stage_workspace_size(d, stage, batch, length, &need);
     if (rc) return rc;
     if (!x || !y) return fail(MH3A_E_INVALID_ARG, "null input or output");
-    if (flags & ~MH3A_FLAG_BF16_MFMA) return fail(MH3A_E_INVALID_ARG, "unsupported flags 0x%x", flags);
+    if (flags & ~(MH3A_FLAG_BF16_MFMA | MH3A_FLAG_BATCH_INVARIANT))
+        return fail(MH3A_E_INVALID_ARG, "unsupported flags 0x%x", flags);
     if (!workspace) return fail(MH3A_E_WORKSPACE, "workspace is null");
     if ((uintptr_t)workspace % 256) return fail(MH3A_E_WORKSPACE, "workspace must be 256-byte aligned");
     if (workspace_bytes < need) return fail(MH3A_E_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
@@ -982,8 +1110,9 @@ int mh3a_amp_stage(mh3a_decoder* d, int stage, const float* x, int64_t batch, in
     HIP_TRY(hipSetDevice(d->device));
     float* xb = static_cast<float*>(workspace);
     float* tb = xb + round_up(batch * d->stage_c[stage] * length, 64);
+    float* part = tb + round_up(batch * d->stage_c[stage] * length, 64);
     rc = run_amp(d, stage, x, xb, tb, y, (int)batch, length, (flags & MH3A_FLAG_BF16_MFMA) != 0,
-                 static_cast<hipStream_t>(stream));
+                 (flags & MH3A_FLAG_BATCH_INVARIANT) != 0, part, static_cast<hipStream_t>(stream));
     if (rc) return rc;
     return ok();
 }

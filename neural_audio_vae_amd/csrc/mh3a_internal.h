@@ -51,7 +51,9 @@ struct ConvArgs {
     const float* sum_in;  // running block sum, y's layout, or null
     float scale;
     ActParams act;        // act.taps == null: no activation
-    int bf16;             // round MFMA operands to bfloat16
+    int bf16;             // three-term bfloat16 split of the MFMA operands
+    int ksplit;           // K ranges (divides the chunk count); > 1 uses `partial`
+    float* partial;       // ksplit * tiles * tile_m * tile_n floats of raw sums
 };
 
 // Tile shapes of the conv kernel: four consumer waves arranged WM x WN,

@@ -225,24 +225,31 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     float* ss = xs + CI * act_xs_len(W);     // [CI][act_ss_len(W)]   (act only)
     const int nch = (a.c_in + CI - 1) / CI;
     const int G = nch * a.taps;
+    // With a K split the chunks are cut into ksplit equal ranges; each
+    // (range, tile) pair is a virtual tile whose raw sums go to `partial`.
+    const int nchs = nch / a.ksplit;
     const int n_nt = (a.positions + NWG - 1) / NWG;
     const int n_mt = (a.c_out + MWG - 1) / MWG;
-    const int total = n_nt * n_mt * a.groups;
+    const int base_tiles = n_nt * n_mt * a.groups;
+    const int total = base_tiles * a.ksplit;
     const int t_begin = (int)((int64_t)total * blockIdx.x / gridDim.x);
     const int t_end = (int)((int64_t)total * (blockIdx.x + 1) / gridDim.x);
-    const int n_items = (t_end - t_begin) * nch;
+    const int n_items = (t_end - t_begin) * nchs;
     if (n_items == 0) return;
 
-    // tile id -> (batch item, phase, M tile, N tile); N tiles vary fastest
+    // virtual tile id -> (K range, batch item, phase, M tile, N tile); N tiles
+    // vary fastest, K ranges slowest
     struct Tile {
-        int b, ph, mt, p0;
+        int b, ph, mt, p0, c0, vid;
     };
     auto tile_at = [&](int id) {
-        const int nt = id % n_nt;
-        const int rest = id / n_nt;
+        const int split = a.ksplit > 1 ? id / base_tiles : 0;
+        const int bid = id - split * base_tiles;
+        const int nt = bid % n_nt;
+        const int rest = bid / n_nt;
         const int mt = rest % n_mt;
         const int g = rest / n_mt;
-        return Tile{g / a.phases, g % a.phases, mt, nt * NWG};
+        return Tile{g / a.phases, g % a.phases, mt, nt * NWG, split * nchs, id};
     };
 
     // producer identity: 256 threads, 32 per channel
@@ -257,7 +264,7 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     const bool prefetchable = row_len <= 32 * XR;
     float xr[XR];
     auto row_value = [&](const Tile& t, int c, int w) {
-        const int ch = c * CI + pci;
+        const int ch = (t.c0 + c) * CI + pci;
         if (ch >= a.c_in) return 0.0f;
         const float* xc = a.x + (int64_t)t.b * a.x_bstride + (int64_t)ch * a.l_in;
         const int n_lo = t.p0 + a.in_off[t.ph];
@@ -292,7 +299,8 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     auto compute = [&](const Tile& t, int c, float* dst) {
         if constexpr (ACT) {
             wave_lds_sync();
-            act_from_xs<CI>(dst, xs, ss, c * CI, a.c_in, a.l_in, t.p0 + a.in_off[t.ph], W, a.act, pci, plane);
+            act_from_xs<CI>(dst, xs, ss, (t.c0 + c) * CI, a.c_in, a.l_in, t.p0 + a.in_off[t.ph], W, a.act, pci,
+                            plane);
         }
     };
 
@@ -306,10 +314,10 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     // Accumulators start at the bias: one MFMA of the bias column (lanes
     // 0-31 hold bias[row], K index 0) against a ones row (K index 0).
     float bias_frag[MBW];
-    auto load_bias = [&](int mb_base) {
+    auto load_bias = [&](int mb_base, int c0) {
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb)
-            bias_frag[mb] = hi == 0 ? a.bias[min((mb_base + mb) * 32 + lo, a.c_out - 1)] : 0.0f;
+            bias_frag[mb] = (hi == 0 && c0 == 0) ? a.bias[min((mb_base + mb) * 32 + lo, a.c_out - 1)] : 0.0f;
     };
     auto init_acc = [&]() {
         const float ones = hi == 0 ? 1.0f : 0.0f;
@@ -387,9 +395,9 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
         Tile la = cur;
         int la_c = 0;
         auto advance = [&](Tile& t, int& c, int item) {
-            if (++c == nch) {
+            if (++c == nchs) {
                 c = 0;
-                t = tile_at(t_begin + item / nch);
+                t = tile_at(t_begin + item / nchs);
             }
         };
         stage(cur, 0, abuf);
@@ -419,15 +427,15 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
 
     Tile cur = tile_at(t_begin);
     int cur_c = 0;
-    load_bias(__builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW));
+    load_bias(__builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW), cur.c0);
     init_acc();
     float4 Ar0[MBW], Ar1[MBW], Ar2[MBW];
     if constexpr (TAPS > 0) {
         const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
-        load_a_nb(Ar0, mb0, cur.ph, 0);
-        load_a_nb(Ar1, mb0, cur.ph, 1);
+        load_a_nb(Ar0, mb0, cur.ph, cur.c0 * a.taps);
+        load_a_nb(Ar1, mb0, cur.ph, cur.c0 * a.taps + 1);
     } else {
-        load_a(An, __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW), cur.ph, 0);
+        load_a(An, __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW), cur.ph, cur.c0 * a.taps);
     }
     (void)Ar2;
     __syncthreads();
@@ -436,17 +444,18 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
         const bool has_next = it + 1 < n_items;
         Tile nxt = cur;
         int nxt_c = cur_c + 1;
-        if (nxt_c == nch) {
+        if (nxt_c == nchs) {
             nxt_c = 0;
-            if (has_next) nxt = tile_at(t_begin + (it + 1) / nch);
+            if (has_next) nxt = tile_at(t_begin + (it + 1) / nchs);
         }
         // wave-uniform M-block base (the compiler cannot see it is uniform)
         const int mb_base = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
         // the next tile's bias, in flight during this item
-        if (nxt_c == 0 && has_next) load_bias(__builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW));
+        if (nxt_c == 0 && has_next)
+            load_bias(__builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW), nxt.c0);
         const bool live = mb_base < mb_tot;
         const float* cur_buf = abuf + (it & 1) * CI * W;
-        const int g0 = cur_c * a.taps;
+        const int g0 = (cur.c0 + cur_c) * a.taps;
         if constexpr (TAPS > 0) {
             // Compile-time tap count: the tap loop is fully unrolled and
             // branch-free. The weights ride a three-slot register ring loaded
@@ -455,7 +464,7 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
             // Slots 0 and 1 hold taps 0 and 1 of the current item on entry.
             const int nmb_base = __builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW);
             const int nph = has_next ? nxt.ph : cur.ph;
-            const int ng0 = has_next ? nxt_c * TAPS : g0;
+            const int ng0 = has_next ? (nxt.c0 + nxt_c) * TAPS : g0;
             const int nmb = has_next ? nmb_base : mb_base;
 #pragma unroll
             for (int j = 0; j < TAPS; ++j) {
@@ -502,7 +511,7 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
                     load_a(An, mb_base, cur.ph, g0 + j + 1);
                 } else if (has_next) {
                     load_a(An, __builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW), nxt.ph,
-                           nxt_c * a.taps);
+                           (nxt.c0 + nxt_c) * a.taps);
                 }
                 if (!live) continue;
                 float Bv[4][NBW];
@@ -510,10 +519,21 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
                 mfma_tap(Ac, Bv);
             }
         }
-        if (cur_c == nch - 1) {
-            // Per-element epilogue (a batched variant measured no faster: its
-            // registers cost resident workgroups).
-            if (live) {
+        if (cur_c == nchs - 1) {
+            if (a.ksplit > 1) {
+                // raw partial sums of this K range in MFMA fragment order:
+                // [wave][mb][nb][r][lane], so each register is one 256-byte
+                // row of the wave and the 16 of a block share one address
+                float* pt = a.partial + (int64_t)cur.vid * (MWG * NWG) + wave * (MBW * NBW * 1024) + lane;
+#pragma unroll
+                for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) pt[(mb * NBW + nb) * 1024 + r * 64] = acc[mb][nb][r];
+            } else if (live) {
+                // Per-element epilogue (a batched variant measured no faster:
+                // its registers cost resident workgroups).
                 const int64_t ostride = (int64_t)a.out_mul * a.positions;
 #pragma unroll
                 for (int mb = 0; mb < MBW; ++mb) {
@@ -541,6 +561,44 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
         cur_c = nxt_c;
         __syncthreads();
     }
+}
+
+// Sum the ksplit partial tiles of a split conv in a fixed order and apply
+// residual, running sum and scale (the bias is in the first range's sums).
+// One thread per (base tile, row, column); the partial tiles are in the
+// conv kernel's fragment order for consumer waves arranged wm + WM * wn.
+struct SplitGeom {
+    int mbw, nbw, wm, wn;
+};
+__global__ void __launch_bounds__(256) split_reduce_kernel(ConvArgs a, SplitGeom g) {
+    const int tile_m = g.wm * g.mbw * 32, tile_n = g.wn * g.nbw * 32;
+    const int n_nt = (a.positions + tile_n - 1) / tile_n;
+    const int n_mt = (a.c_out + tile_m - 1) / tile_m;
+    const int64_t base_tiles = (int64_t)n_nt * n_mt * a.groups;
+    const int64_t per_tile = (int64_t)tile_m * tile_n;
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= base_tiles * per_tile) return;
+    const int64_t id = e / per_tile;
+    const int local = (int)(e - id * per_tile);
+    const int row = local / tile_n, col = local - row * tile_n;
+    const int nt = (int)(id % n_nt);
+    const int64_t rest = id / n_nt;
+    const int mt = (int)(rest % n_mt);
+    const int grp = (int)(rest / n_mt);
+    const int b = grp / a.phases, ph = grp % a.phases;
+    const int o = mt * tile_m + row, pos = nt * tile_n + col;
+    if (o >= a.c_out || pos >= a.positions) return;
+    // (row, col) -> fragment slot
+    const int wm = row / (g.mbw * 32), mb = (row / 32) % g.mbw, rr = row % 32;
+    const int wn = col / (g.nbw * 32), nb = (col / 32) % g.nbw, lo = col % 32;
+    const int r = 4 * (rr / 8) + rr % 4, hi = (rr / 4) % 2;
+    const int slot = ((((wn * g.wm + wm) * g.mbw + mb) * g.nbw + nb) * 16 + r) * 64 + hi * 32 + lo;
+    float v = 0.0f;
+    for (int sp = 0; sp < a.ksplit; ++sp) v += a.partial[(sp * base_tiles + id) * per_tile + slot];
+    const int64_t idx = (int64_t)b * a.y_bstride + (int64_t)o * a.out_mul * a.positions + a.out_mul * pos + a.out_add[ph];
+    if (a.res) v += a.res[idx];
+    if (a.sum_in) v += a.sum_in[idx];
+    a.y[idx] = v * a.scale;
 }
 
 TileShape tile_shape(TileId t) {
@@ -588,7 +646,7 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
     constexpr int MWG = WM * MBW * 32;
     const int W = NWG + (a.taps - 1) * a.dil;
     const int64_t tiles =
-        (int64_t)((a.positions + NWG - 1) / NWG) * ((a.c_out + MWG - 1) / MWG) * a.groups;
+        (int64_t)((a.positions + NWG - 1) / NWG) * ((a.c_out + MWG - 1) / MWG) * a.groups * a.ksplit;
     const bool act = a.act.taps != nullptr;
     const size_t lds = sizeof(float) * (size_t)conv_lds_floats(W, act);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
@@ -610,13 +668,30 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_conv(const ConvArgs& a, TileId tile, hipStream_t stream) {
+    // the kernel cuts the chunks into ksplit equal ranges
+    const int nch = (a.c_in + kChunk - 1) / kChunk;
+    if (a.ksplit < 1 || nch % a.ksplit != 0 || (a.ksplit > 1 && !a.partial)) return hipErrorInvalidValue;
+    hipError_t e = hipSuccess;
     switch (tile) {
 #define MH3A_TILE(id, mbw, nbw, wm, wn) \
-    case id: return launch_tile<mbw, nbw, wm, wn, tile_has_act_taps(id)>(a, stream);
+    case id: e = launch_tile<mbw, nbw, wm, wn, tile_has_act_taps(id)>(a, stream); break;
         MH3A_TILE_LIST
 #undef MH3A_TILE
         default: return hipErrorInvalidValue;
     }
+    if (e != hipSuccess || a.ksplit <= 1) return e;
+    SplitGeom g{};
+    switch (tile) {
+#define MH3A_TILE(id, mbw, nbw, wm, wn) \
+    case id: g = {mbw, nbw, wm, wn}; break;
+        MH3A_TILE_LIST
+#undef MH3A_TILE
+        default: return hipErrorInvalidValue;
+    }
+    const int tm = g.wm * g.mbw * 32, tn = g.wn * g.nbw * 32;
+    const int64_t n = (int64_t)((a.positions + tn - 1) / tn) * ((a.c_out + tm - 1) / tm) * a.groups * tm * tn;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a, g);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

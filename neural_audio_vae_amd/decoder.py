@@ -9,7 +9,8 @@ from __future__ import annotations
 import numpy as np
 
 from . import _lib
-from ._lib import MH3A_FLAG_BF16_MFMA, MH3A_FLAG_DENORMALIZE, MH3A_FLAG_NO_CLAMP, MH3AError  # noqa: F401
+from ._lib import (MH3A_FLAG_BATCH_INVARIANT, MH3A_FLAG_BF16_MFMA, MH3A_FLAG_DENORMALIZE,  # noqa: F401
+                   MH3A_FLAG_NO_CLAMP, MH3AError)  # noqa: F401
 
 
 def _torch():

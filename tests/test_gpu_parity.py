@@ -36,7 +36,7 @@ def scaled_abs(ref):
     return ABS_TOL * max(1.0, float(np.max(np.abs(ref))) / REF_SCALE)
 
 
-NO_CLAMP, BF16, DENORM = 0x4, 0x2, 0x1
+NO_CLAMP, BF16, DENORM, INVARIANT = 0x4, 0x2, 0x1, 0x8
 
 
 def report(what, got, ref):
@@ -264,12 +264,36 @@ def test_amp_stage_rejects_bad_arguments(default_decoder, dev):
 # Batch semantics and determinism
 # ---------------------------------------------------------------------------
 
-def test_batch_items_decode_independently_bitwise(default_decoder, dev):
+def test_batch_invariant_flag_items_decode_bitwise_alike(default_decoder, default_params, dev):
+    # With MH3A_FLAG_BATCH_INVARIANT every launch is planned from one item's
+    # shape, so an item's output does not depend on the batch it rides in.
+    z = synth.make_latents(3, 37, seed=2)
+    both = host(default_decoder.decode(gpu(z, dev), flags=NO_CLAMP | INVARIANT))
+    for i in range(3):
+        one = host(default_decoder.decode(gpu(z[i:i + 1], dev), flags=NO_CLAMP | INVARIANT))
+        np.testing.assert_array_equal(both[i], one[0])
+    windows = [(1, 17, 20)]
+    check_windows("batch-invariant B=3 N=37", both, oracle_windows(default_params, z, windows), windows)
+
+
+def test_default_plans_agree_across_batch_sizes(default_decoder, dev):
+    # Default plans split the contraction by the batch's size; items then
+    # agree across batch sizes to rounding, not bitwise.
     z = synth.make_latents(3, 37, seed=2)
     both = host(default_decoder.decode(gpu(z, dev), flags=NO_CLAMP))
     for i in range(3):
         one = host(default_decoder.decode(gpu(z[i:i + 1], dev), flags=NO_CLAMP))
-        np.testing.assert_array_equal(both[i], one[0])
+        assert_close(f"B=3 item {i} vs B=1", both[i], one[0])
+
+
+@pytest.mark.parametrize("flags", [0, INVARIANT])
+def test_amp_stage_short_signal_split_contraction(default_decoder, default_params, dev, flags):
+    # Stage 0 on a short signal: few output tiles, so the contraction over
+    # 512 channels is split into ranges and summed by the reduce pass.
+    x = synth.make_signal((1, 512, 150), seed=4)
+    got = host(default_decoder.amp_stage(0, gpu(x, dev), flags=flags))
+    ref = O.stage_amp(x[0], default_params, 0)
+    assert_close(f"stage 0 (1, 512, 150) flags {flags}", got[0], ref)
 
 
 def test_decode_is_deterministic(default_decoder, dev):
