@@ -16,7 +16,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmh3a.so")
-SOURCES = [os.path.join(PKG, "csrc", "mh3a_host.cpp"), os.path.join(PKG, "csrc", "mh3a_kernels.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mh3a_host.cpp", "mh3a_plan.cpp", "mh3a_kernels.hip")]
 ARCH = "gfx950"
 
 

@@ -95,6 +95,24 @@ void pack_conv_weights(const float* w, int c_out, int c_in, int taps, float* out
 
 hipError_t launch_conv(const ConvArgs& a, TileId tile, hipStream_t stream);
 
+// What the planner needs of a conv layer.
+struct ConvShape {
+    int c_in, c_out, taps, dil, phases;
+    bool act;  // act-fused (AMP) conv
+};
+// Tile shape and K split of one launch.
+struct ConvPlan {
+    TileId tile;
+    int ksplit;
+};
+// Bound on a plan's partial sums (floats), which live in the workspace.
+constexpr int64_t kMaxPartialFloats = (int64_t)32 << 20;
+// Plan one conv launch of `batch` items over `positions` output positions
+// per phase on a device with num_cus compute units.
+ConvPlan plan_conv(const ConvShape& s, int positions, int batch, bool bf16, bool invariant, int num_cus);
+// Floats of partial sums the plan needs (0 without a K split).
+int64_t plan_partial_floats(const ConvShape& s, int positions, int groups, const ConvPlan& p);
+
 // activation_post + conv_post (c -> 1, 7 taps, pad 3) + optional clamp.
 struct FinalArgs {
     const float* x;
