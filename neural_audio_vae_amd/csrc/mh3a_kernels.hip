@@ -57,6 +57,25 @@ __device__ __forceinline__ void wave_lds_sync() {
 __host__ __device__ constexpr int act_xs_len(int W) { return (W + 14 + 3) & ~3; }
 __host__ __device__ constexpr int act_ss_len(int W) { return (2 * W + 14 + 3) & ~3; }
 
+// The resampler taps in registers: even / odd parity up taps (gain folded)
+// and the down taps. Loaded once per kernel: they are the same for every
+// channel, and loading them next to the input rows would make the first
+// use wait for those rows too (vector memory counters retire in order).
+struct ActTaps {
+    float fe[6], fo[6], fd[12];
+};
+__device__ __forceinline__ ActTaps load_act_taps(const float* tp) {
+    ActTaps t;
+#pragma unroll
+    for (int e = 0; e < 6; ++e) {
+        t.fe[e] = tp[e];
+        t.fo[e] = tp[6 + e];
+    }
+#pragma unroll
+    for (int q = 0; q < 12; ++q) t.fd[q] = tp[12 + q];
+    return t;
+}
+
 // Stage CI channels [ch0, ch0 + CI) of act(x) over input positions
 // [n_lo, n_lo + W) into as[CI][W] (zero outside [0, l_in): the conv's zero
 // padding). act is the anti-aliased SnakeBeta:
@@ -67,6 +86,7 @@ __host__ __device__ constexpr int act_ss_len(int W) { return (2 * W + 14 + 3) & 
 //   a[n] = sum_{q=0..11} f[q] s[clamp(2n + q - 5, 0, 2L-1)]   (pad 5 / 6, stride 2)
 // `lane32` in [0, 32) and `ci` identify the calling thread: 32 threads of
 // one wave own one channel, so the steps synchronize only within the wave.
+// `ab` is this thread's channel's (alpha / pi, 0.5 / beta).
 // LDS: xs[CI][act_xs_len(W)] holds X[n_lo - 6 ...]; ss[CI][act_ss_len(W)]
 // holds slot mm = s[clamp(2 n_lo - 5 + mm)] at index mm + 1; as[CI][W] is
 // the result (W even).
@@ -77,24 +97,17 @@ __host__ __device__ constexpr int act_ss_len(int W) { return (2 * W + 14 + 3) & 
 // from sixteen s values. Edge tiles take the general path.
 template <int CI>
 __device__ __forceinline__ void act_from_xs(float* __restrict__ as, float* __restrict__ xs, float* __restrict__ ss,
-                                            int ch0, int c_in, int l_in, int n_lo, int W, const ActParams& ap,
-                                            int ci, int lane32) {
+                                            int ch0, int c_in, int l_in, int n_lo, int W, const ActTaps& f,
+                                            float2 ab, int ci, int lane32) {
     const int ch = ch0 + ci;
     const bool live = ch < c_in;
     const int XS = act_xs_len(W), SS = act_ss_len(W);
     float* xrow = xs + ci * XS;
     float* srow = ss + ci * SS;
     float* arow = as + ci * W;
-    const float* tp = ap.taps;
-    float fe[6], fo[6], fd[12];
-#pragma unroll
-    for (int e = 0; e < 6; ++e) {
-        fe[e] = tp[e];
-        fo[e] = tp[6 + e];
-    }
-#pragma unroll
-    for (int q = 0; q < 12; ++q) fd[q] = tp[12 + q];
-    const float2 ab = live ? ap.ab[ch] : make_float2(0.0f, 0.0f);
+    const float(&fe)[6] = f.fe;
+    const float(&fo)[6] = f.fo;
+    const float(&fd)[12] = f.fd;
     const bool interior = n_lo - 6 >= 0 && n_lo + W + 8 <= l_in && ch0 + CI <= c_in;
 
     (void)XS;
@@ -178,14 +191,15 @@ __device__ __forceinline__ void act_from_xs(float* __restrict__ as, float* __res
 template <int CI>
 __device__ __forceinline__ void stage_act(float* __restrict__ as, float* __restrict__ xs, float* __restrict__ ss,
                                           const float* __restrict__ xb, int ch0, int c_in, int l_in, int n_lo,
-                                          int W, const ActParams& ap, int ci, int lane32) {
+                                          int W, const ActTaps& f, const float2* abp, int ci, int lane32) {
     const int ch = ch0 + ci;
     const bool live = ch < c_in;
     const float* xc = xb + (int64_t)(live ? ch : 0) * l_in;
+    const float2 ab = live ? abp[ch] : make_float2(0.0f, 0.0f);
     float* xrow = xs + ci * act_xs_len(W);
     for (int w = lane32; w < act_xs_len(W); w += 32) xrow[w] = live ? xc[clampi(n_lo - 6 + w, 0, l_in - 1)] : 0.0f;
     wave_lds_sync();
-    act_from_xs<CI>(as, xs, ss, ch0, c_in, l_in, n_lo, W, ap, ci, lane32);
+    act_from_xs<CI>(as, xs, ss, ch0, c_in, l_in, n_lo, W, f, ab, ci, lane32);
 }
 
 __device__ __forceinline__ float round_bf16(float v) {
@@ -240,7 +254,7 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     // virtual tile id -> (K range, batch item, phase, M tile, N tile); N tiles
     // vary fastest, K ranges slowest
     struct Tile {
-        int b, ph, mt, p0, c0, vid;
+        int b, ph, mt, p0, c0, vid, n_lo;  // n_lo: first input position of the window
     };
     auto tile_at = [&](int id) {
         const int split = a.ksplit > 1 ? id / base_tiles : 0;
@@ -249,7 +263,8 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
         const int rest = bid / n_nt;
         const int mt = rest % n_mt;
         const int g = rest / n_mt;
-        return Tile{g / a.phases, g % a.phases, mt, nt * NWG, split * nchs, id};
+        const int ph = g % a.phases;
+        return Tile{g / a.phases, ph, mt, nt * NWG, split * nchs, id, nt * NWG + a.in_off[ph]};
     };
 
     // producer identity: 256 threads, 32 per channel
@@ -263,23 +278,41 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     const int row_len = ACT ? act_xs_len(W) : W;
     const bool prefetchable = row_len <= 32 * XR;
     float xr[XR];
+    float2 ab_pf = make_float2(0.0f, 0.0f);  // prefetched (alpha / pi, 0.5 / beta) of the row's channel
+    float2 ab_st = ab_pf;                    // that of the staged row
     auto row_value = [&](const Tile& t, int c, int w) {
         const int ch = (t.c0 + c) * CI + pci;
         if (ch >= a.c_in) return 0.0f;
         const float* xc = a.x + (int64_t)t.b * a.x_bstride + (int64_t)ch * a.l_in;
-        const int n_lo = t.p0 + a.in_off[t.ph];
         if constexpr (ACT) {
-            return xc[clampi(n_lo - 6 + w, 0, a.l_in - 1)];
+            return xc[clampi(t.n_lo - 6 + w, 0, a.l_in - 1)];
         } else {
-            const int n = n_lo + w;
+            const int n = t.n_lo + w;
             return (n >= 0 && n < a.l_in) ? xc[n] : 0.0f;
         }
     };
+    // Branch-free row prefetch: every load is issued, from a clamped (in
+    // bounds) address, and masked after it lands.
     auto prefetch = [&](const Tile& t, int c) {
+        const int ch = (t.c0 + c) * CI + pci;
+        const bool live = ch < a.c_in;
+        const int chc = min(ch, a.c_in - 1);
+        const float* xc = a.x + (int64_t)t.b * a.x_bstride + (int64_t)chc * a.l_in;
 #pragma unroll
         for (int r = 0; r < XR; ++r) {
             const int w = plane + 32 * r;
-            xr[r] = w < row_len ? row_value(t, c, w) : 0.0f;
+            if constexpr (ACT) {
+                const float v = xc[clampi(t.n_lo - 6 + w, 0, a.l_in - 1)];
+                xr[r] = live ? v : 0.0f;
+            } else {
+                const int n = t.n_lo + w;
+                const float v = xc[clampi(n, 0, a.l_in - 1)];
+                xr[r] = (live && n >= 0 && n < a.l_in) ? v : 0.0f;
+            }
+        }
+        if constexpr (ACT) {
+            const float2 v = a.act.ab[chc];
+            ab_pf = live ? v : make_float2(0.0f, 0.0f);
         }
     };
     // write item (t, c)'s row to LDS (from the prefetch registers when it
@@ -292,15 +325,23 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
                 const int w = plane + 32 * r;
                 if (w < row_len) row[w] = xr[r];
             }
+            ab_st = ab_pf;
         } else {
             for (int w = plane; w < row_len; w += 32) row[w] = row_value(t, c, w);
+            if constexpr (ACT) {
+                const int ch = (t.c0 + c) * CI + pci;
+                ab_st = ch < a.c_in ? a.act.ab[ch] : make_float2(0.0f, 0.0f);
+            }
         }
     };
+    ActTaps ftaps;
+    if constexpr (ACT) {
+        if (producer) ftaps = load_act_taps(a.act.taps);
+    }
     auto compute = [&](const Tile& t, int c, float* dst) {
         if constexpr (ACT) {
             wave_lds_sync();
-            act_from_xs<CI>(dst, xs, ss, (t.c0 + c) * CI, a.c_in, a.l_in, t.p0 + a.in_off[t.ph], W, a.act, pci,
-                            plane);
+            act_from_xs<CI>(dst, xs, ss, (t.c0 + c) * CI, a.c_in, a.l_in, t.n_lo, W, ftaps, ab_st, pci, plane);
         }
     };
 
@@ -711,9 +752,10 @@ __global__ void __launch_bounds__(256) final_kernel(FinalArgs a) {
     const float* xb = a.x + (int64_t)b * a.x_bstride;
     const int t = t0 + threadIdx.x;
     float acc = 0.0f;
+    const ActTaps f = load_act_taps(a.act.taps);
     for (int c0 = 0; c0 < a.c; c0 += CI) {
         __syncthreads();
-        stage_act<CI>(as, xs, ss, xb, c0, a.c, a.l, t0 - 3, W, a.act, threadIdx.x >> 5, threadIdx.x & 31);
+        stage_act<CI>(as, xs, ss, xb, c0, a.c, a.l, t0 - 3, W, f, a.act.ab, threadIdx.x >> 5, threadIdx.x & 31);
         __syncthreads();
         for (int ci = 0; ci < CI && c0 + ci < a.c; ++ci) {
             const float* wr = a.w + (c0 + ci) * 7;
