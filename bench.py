@@ -156,7 +156,7 @@ def main():
     ms_step = ms_total / args.steps
     audio_s = batch * frames / LATENTS_PER_SECOND
     value = audio_s / (ms_step / 1e3)
-    amp = kernels.get("amp_act_conv", {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+    amp = kernels.get("amp_conv", {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
     achieved = amp["flops"] / (amp["ms"] / 1e3) / 1e12 if amp["ms"] > 0 else 0.0
     per_step = {
         name: {

@@ -146,8 +146,8 @@ struct ConvLayer {
     int kind = 0;       // timing class
 };
 
-enum Kind { KIND_IN_PROJ = 0, KIND_CONV_PRE, KIND_UPSAMPLE, KIND_AMP, KIND_FINAL, KIND_COUNT };
-const char* const kKindNames[KIND_COUNT] = {"dec_in_proj", "conv_pre", "ups_transposed_conv", "amp_act_conv",
+enum Kind { KIND_IN_PROJ = 0, KIND_CONV_PRE, KIND_UPSAMPLE, KIND_AMP, KIND_AMP_ACT, KIND_FINAL, KIND_COUNT };
+const char* const kKindNames[KIND_COUNT] = {"dec_in_proj", "conv_pre", "ups_transposed_conv", "amp_conv", "amp_act",
                                             "act_post_conv_post"};
 
 struct TimingRec {
@@ -187,6 +187,7 @@ struct mh3a_decoder {
     float post_bias = 0.0f;
     std::vector<int> stage_c;   // output channels per stage
     int num_cus = 256;          // compute units of `device`
+    bool pk_ok = false;         // every AMP conv can read a packed activated input
     mutable Timing timing;
     mutable std::mutex plan_mu;                          // guards plans
     mutable std::map<PlanKey, std::pair<int, int>> plans;  // (tile, ksplit) per launch shape
@@ -344,19 +345,47 @@ ActParams act_params(const mh3a_decoder* d, int idx) {
     return p;
 }
 
-ConvShape shape_of(const ConvLayer& L) { return {L.c_in, L.c_out, L.taps, L.dil, L.phases, L.act >= 0}; }
+// fused: the layer's activation runs in the conv's operand staging (else the
+// conv reads an already activated input)
+ConvShape shape_of(const ConvLayer& L, bool fused) {
+    return {L.c_in, L.c_out, L.taps, L.dil, L.phases, fused && L.act >= 0, L.kind == KIND_AMP};
+}
 
-int64_t plan_partial_floats(const ConvLayer& L, int positions, int groups, const ConvPlan& p) {
-    return mh3a::plan_partial_floats(shape_of(L), positions, groups, p);
+int64_t plan_partial_floats(const ConvLayer& L, int positions, int groups, const ConvPlan& p, bool fused) {
+    return mh3a::plan_partial_floats(shape_of(L, fused), positions, groups, p);
+}
+
+// Whether an AMP conv of a (batch, C, L) activation fuses its activation.
+// Fused, the producer waves compute it per tile on the SIMDs whose matrix
+// cores the consumer waves keep busy, and their vector work barely advances
+// while the MFMAs stream (measured: ~3.5x slower than alone), so the tile
+// waits on it; at 256+ channels it is also repeated per M tile. Separate,
+// a standalone pass writes the packed input and the conv's producers only
+// copy it to LDS. Measured per stage (B=2 x 1200 latents): separate wins at
+// 512 channels, ties at 256, loses below (the pass costs more than the
+// contention there). Small launches stay fused (one launch, less latency).
+// MH3A_AMP_ACT=fused|separate overrides (a tuning aid).
+bool amp_act_fused(const mh3a_decoder* d, int64_t batch, int64_t c, int64_t len) {
+    if (!d->pk_ok) return true;
+    static const int mode = [] {
+        const char* e = std::getenv("MH3A_AMP_ACT");
+        if (!e) return 0;
+        if (!std::strcmp(e, "fused")) return 1;
+        if (!std::strcmp(e, "separate")) return 2;
+        return 0;
+    }();
+    if (mode) return mode == 1;
+    return c < 256 || batch * c * len < kSeparateActMin;
 }
 
 // Plans are cached per launch shape.
-ConvPlan plan_conv(const mh3a_decoder* d, const ConvLayer& L, int positions, int batch, bool bf16, bool invariant) {
-    const PlanKey key{&L, positions, batch, (bf16 ? 1 : 0) | (invariant ? 2 : 0)};
+ConvPlan plan_conv(const mh3a_decoder* d, const ConvLayer& L, int positions, int batch, bool bf16, bool invariant,
+                   bool fused) {
+    const PlanKey key{&L, positions, batch, (bf16 ? 1 : 0) | (invariant ? 2 : 0) | (fused ? 4 : 0)};
     std::lock_guard<std::mutex> lock(d->plan_mu);
     auto it = d->plans.find(key);
     if (it != d->plans.end()) return {(TileId)it->second.first, it->second.second};
-    const ConvPlan p = mh3a::plan_conv(shape_of(L), positions, batch, bf16, invariant, d->num_cus);
+    const ConvPlan p = mh3a::plan_conv(shape_of(L, fused), positions, batch, bf16, invariant, d->num_cus);
     // MH3A_PLAN_LOG=1 prints each new plan to stderr (a tuning aid)
     static const bool log = [] {
         const char* e = std::getenv("MH3A_PLAN_LOG");
@@ -364,9 +393,9 @@ ConvPlan plan_conv(const mh3a_decoder* d, const ConvLayer& L, int positions, int
     }();
     if (log) {
         const TileShape ts = tile_shape(p.tile);
-        std::fprintf(stderr, "mh3a plan: %s c_in %d c_out %d taps %d dil %d positions %d batch %d%s -> tile %dx%d ksplit %d\n",
+        std::fprintf(stderr, "mh3a plan: %s c_in %d c_out %d taps %d dil %d positions %d batch %d%s%s -> tile %dx%d ksplit %d\n",
                      kKindNames[L.kind], L.c_in, L.c_out, L.taps, L.dil, positions, batch, invariant ? " (invariant)" : "",
-                     ts.m, ts.n, p.ksplit);
+                     (L.act >= 0 && !fused) ? " (act separate)" : "", ts.m, ts.n, p.ksplit);
     }
     if (d->plans.size() > 4096) d->plans.clear();
     d->plans.emplace(key, std::make_pair((int)p.tile, p.ksplit));
@@ -410,9 +439,11 @@ struct TimedLaunch {
 // `partial` holds at least the plan's partial sums (plan_partial_floats).
 hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, int64_t x_bstride, int l_in,
                     int positions, float* y, int64_t y_bstride, int batch, const float* res, const float* sum_in,
-                    float scale, bool bf16, bool invariant, float* partial, hipStream_t st) {
+                    float scale, bool bf16, bool invariant, bool fused, float* partial, hipStream_t st,
+                    int pk_lp = 0) {
     ConvArgs a;
     std::memset(&a, 0, sizeof a);
+    a.pk_lp = pk_lp;
     a.x = x;
     a.x_bstride = x_bstride;
     a.c_in = L.c_in;
@@ -436,9 +467,9 @@ hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, i
     a.res = res;
     a.sum_in = sum_in;
     a.scale = scale;
-    a.act = act_params(d, L.act);
+    a.act = fused ? act_params(d, L.act) : ActParams{nullptr, nullptr};
     a.bf16 = bf16 ? 1 : 0;
-    const ConvPlan plan = plan_conv(d, L, positions, batch, bf16, invariant);
+    const ConvPlan plan = plan_conv(d, L, positions, batch, bf16, invariant, fused);
     a.ksplit = plan.ksplit;
     a.partial = partial;
     if (plan.ksplit > 1 && !partial) return hipErrorInvalidValue;
@@ -471,27 +502,69 @@ int64_t max_cl(const mh3a_decoder* d, int64_t frames) {
 
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-// AMP set of one stage: h (B, C, L) read-only; x_buf, t_buf scratch;
+// Packed activated input of one (C, L) item (see kPkPadL): row length and
+// floats per item.
+int64_t pk_lp(int64_t len) { return len + kPkPadL + kPkPadR; }
+int64_t pk_item_floats(int c, int64_t len) { return (int64_t)((c + kChunk - 1) / kChunk) * kChunk * pk_lp(len); }
+
+// The standalone activation of AMP layer `act_idx`: y = act(x), x (B, C, L)
+// rows, y packed.
+hipError_t run_act(const mh3a_decoder* d, int act_idx, const float* x, float* y, int batch, int c, int64_t len,
+                   hipStream_t st) {
+    ActArgs a;
+    a.x = x;
+    a.x_bstride = (int64_t)c * len;
+    a.y = y;
+    a.y_bstride = pk_item_floats(c, len);
+    a.c = c;
+    a.l = (int)len;
+    a.lp = (int)pk_lp(len);
+    a.act = act_params(d, act_idx);
+    TimedLaunch tl(d, st);
+    hipError_t e = launch_act(a, batch, st);
+    const double n = (double)batch * c * len;
+    // 12 up + 12 down multiply-adds and the SnakeBeta per sample; in and out
+    tl.done(KIND_AMP_ACT, 48.0 * n, 8.0 * n);
+    return e;
+}
+
+// AMP set of one stage: h (B, C, L) read-only; x_buf, t_buf, a_buf scratch;
 // result in s_buf. Blocks run from the same h and are averaged in the
-// epilogue of each block's last conv.
-int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, float* t_buf, float* s_buf, int batch,
-            int64_t len, bool bf16, bool invariant, float* partial, hipStream_t st) {
+// epilogue of each block's last conv. Each conv's activation is fused into
+// its operand staging, or (large tensors) runs as its own pass into a_buf.
+int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, float* t_buf, float* s_buf, float* a_buf,
+            int batch, int64_t len, bool bf16, bool invariant, float* partial, hipStream_t st) {
     const mh3a_config& c = d->cfg;
     const int C = d->stage_c[stage];
     const int64_t bs = (int64_t)C * len;
     const int nrb = c.num_resblocks, nd = c.num_dilations;
     const int L = (int)len;
+    const bool fused = amp_act_fused(d, batch, C, len);
+    const int64_t pbs = pk_item_floats(C, len);  // packed batch stride
+    const int plp = fused ? 0 : (int)pk_lp(len);
     for (int j = 0; j < nrb; ++j) {
         for (int n = 0; n < nd; ++n) {
             const ConvLayer& c1 = d->amp[stage][(j * nd + n) * 2 + 0];
             const ConvLayer& c2 = d->amp[stage][(j * nd + n) * 2 + 1];
             const float* xin = (n == 0) ? h : x_buf;
-            HIP_TRY(run_conv(d, c1, xin, bs, L, L, t_buf, bs, batch, nullptr, nullptr, 1.0f, bf16, invariant, partial, st));
+            const float* in1 = xin;
+            if (!fused) {
+                HIP_TRY(run_act(d, c1.act, xin, a_buf, batch, C, len, st));
+                in1 = a_buf;
+            }
+            HIP_TRY(run_conv(d, c1, in1, fused ? bs : pbs, L, L, t_buf, bs, batch, nullptr, nullptr, 1.0f, bf16,
+                             invariant, fused, partial, st, plp));
+            const float* in2 = t_buf;
+            if (!fused) {
+                HIP_TRY(run_act(d, c2.act, t_buf, a_buf, batch, C, len, st));
+                in2 = a_buf;
+            }
             const bool last = (n == nd - 1);
             float* yout = last ? s_buf : x_buf;
             const float* sum_in = (last && j > 0) ? s_buf : nullptr;
             const float scale = (last && j == nrb - 1) ? 1.0f / (float)nrb : 1.0f;
-            HIP_TRY(run_conv(d, c2, t_buf, bs, L, L, yout, bs, batch, xin, sum_in, scale, bf16, invariant, partial, st));
+            HIP_TRY(run_conv(d, c2, in2, fused ? bs : pbs, L, L, yout, bs, batch, xin, sum_in, scale, bf16, invariant,
+                             fused, partial, st, plp));
         }
     }
     return MH3A_OK;
@@ -513,8 +586,10 @@ int check_decode_args(const mh3a_decoder* d, int64_t batch, int64_t frames, uint
 // Largest partial-sum region any conv of one AMP stage needs.
 int64_t amp_partial_floats(const mh3a_decoder* d, int stage, int batch, int len, bool bf16, bool inv) {
     int64_t m = 0;
+    const bool fused = amp_act_fused(d, batch, d->stage_c[stage], len);
     for (const ConvLayer& L : d->amp[stage])
-        m = std::max(m, plan_partial_floats(L, len, batch * L.phases, plan_conv(d, L, len, batch, bf16, inv)));
+        m = std::max(m, plan_partial_floats(L, len, batch * L.phases, plan_conv(d, L, len, batch, bf16, inv, fused),
+                                            fused));
     return m;
 }
 
@@ -524,22 +599,44 @@ int64_t decode_partial_floats(const mh3a_decoder* d, int batch, int frames, bool
     const mh3a_config& c = d->cfg;
     int64_t m = 0;
     for (const ConvLayer* L : {&d->in_proj, &d->in_proj_dn, &d->conv_pre})
-        m = std::max(m, plan_partial_floats(*L, frames, batch * L->phases, plan_conv(d, *L, frames, batch, false, inv)));
+        m = std::max(m, plan_partial_floats(*L, frames, batch * L->phases, plan_conv(d, *L, frames, batch, false, inv, true),
+                                            true));
     int64_t len = frames;
     for (int s = 0; s < c.num_ups; ++s) {
         const ConvLayer& U = d->ups[s];
-        m = std::max(m, plan_partial_floats(U, (int)len, batch * U.phases, plan_conv(d, U, (int)len, batch, false, inv)));
+        m = std::max(m, plan_partial_floats(U, (int)len, batch * U.phases, plan_conv(d, U, (int)len, batch, false, inv, true),
+                                            true));
         len *= c.rates[s];
         m = std::max(m, amp_partial_floats(d, s, batch, (int)len, bf16, inv));
     }
     return m;
 }
 
+// Floats of the packed activated input of stage s (0 when its convs fuse the
+// activation).
+int64_t stage_pk_floats(const mh3a_decoder* d, int stage, int64_t batch, int64_t len) {
+    if (amp_act_fused(d, batch, d->stage_c[stage], len)) return 0;
+    return round_up(batch * pk_item_floats(d->stage_c[stage], len), 64);
+}
+
+int64_t decode_pk_floats(const mh3a_decoder* d, int64_t batch, int64_t frames) {
+    int64_t m = 0, len = frames;
+    for (int s = 0; s < d->cfg.num_ups; ++s) {
+        len *= d->cfg.rates[s];
+        m = std::max(m, stage_pk_floats(d, s, batch, len));
+    }
+    return m;
+}
+
+// Workspace: slots S, H, X, T, then the packed activated input, then the
+// partial sums of split launches.
 size_t decode_ws_bytes(const mh3a_decoder* d, int64_t batch, int64_t frames, uint32_t flags) {
     const int64_t slots = 4 * round_up(max_cl(d, frames) * batch, 64);
     const bool bf16 = (flags & MH3A_FLAG_BF16_MFMA) != 0;
     const bool inv = (flags & MH3A_FLAG_BATCH_INVARIANT) != 0;
-    return (size_t)((slots + decode_partial_floats(d, (int)batch, (int)frames, bf16, inv)) * (int64_t)sizeof(float));
+    return (size_t)((slots + decode_pk_floats(d, batch, frames) +
+                     decode_partial_floats(d, (int)batch, (int)frames, bf16, inv)) *
+                    (int64_t)sizeof(float));
 }
 
 int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, float* wave, int upto,
@@ -559,7 +656,8 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
     float* bufH = bufS + slot;
     float* bufX = bufH + slot;
     float* bufT = bufX + slot;
-    float* partial = bufT + slot;
+    float* bufA = bufT + slot;
+    float* partial = bufA + decode_pk_floats(d, batch, frames);
     const bool bf16 = (flags & MH3A_FLAG_BF16_MFMA) != 0;
     const bool invariant = (flags & MH3A_FLAG_BATCH_INVARIANT) != 0;
     HIP_TRY(hipSetDevice(d->device));
@@ -572,10 +670,10 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
     const ConvLayer& inp = (flags & MH3A_FLAG_DENORMALIZE) ? d->in_proj_dn : d->in_proj;
     const int64_t zb = (int64_t)c.latent_channels * N;
     HIP_TRY(run_conv(d, inp, z, zb, N, N, bufX, (int64_t)c.latent_dim * N, B, nullptr, nullptr, 1.0f, false, invariant,
-                     partial, st));
+                     true, partial, st));
     if (upto == 0) return finish(bufX, (int64_t)B * c.latent_dim * N);
     HIP_TRY(run_conv(d, d->conv_pre, bufX, (int64_t)c.latent_dim * N, N, N, bufS, (int64_t)c.decoder_dim * N, B,
-                     nullptr, nullptr, 1.0f, false, invariant, partial, st));
+                     nullptr, nullptr, 1.0f, false, invariant, true, partial, st));
     if (upto == 1) return finish(bufS, (int64_t)B * c.decoder_dim * N);
     int64_t len = N;
     int cin = c.decoder_dim;
@@ -583,9 +681,9 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
         const int C = d->stage_c[s];
         const int64_t lout = len * c.rates[s];
         HIP_TRY(run_conv(d, d->ups[s], bufS, (int64_t)cin * len, (int)len, (int)len, bufH, (int64_t)C * lout, B,
-                         nullptr, nullptr, 1.0f, false, invariant, partial, st));
+                         nullptr, nullptr, 1.0f, false, invariant, true, partial, st));
         if (upto == 2 + 2 * s) return finish(bufH, (int64_t)B * C * lout);
-        rc = run_amp(d, s, bufH, bufX, bufT, bufS, B, lout, bf16, invariant, partial, st);
+        rc = run_amp(d, s, bufH, bufX, bufT, bufS, bufA, B, lout, bf16, invariant, partial, st);
         if (rc) return rc;
         if (upto == 3 + 2 * s) return finish(bufS, (int64_t)B * C * lout);
         len = lout;
@@ -826,6 +924,17 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
         d->post_bias = pb->data[0];
     }
 
+    // every AMP conv can read a packed activated input (compile-time taps and
+    // pads that cover its halo with output tiles of up to 256 positions)
+    d->pk_ok = true;
+    for (const auto& stage_layers : d->amp)
+        for (const ConvLayer& L : stage_layers) {
+            const int pad = -L.in_off[0];
+            const bool taps_ok = L.taps == 3 || L.taps == 7 || L.taps == 11;
+            if (!taps_ok || L.phases != 1 || pad > kPkPadL || 255 + (L.taps - 1) * L.dil - pad > kPkPadR)
+                d->pk_ok = false;
+        }
+
     // upload
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(MH3A_E_HIP, "no HIP device available");
@@ -954,7 +1063,9 @@ int mh3a_amp_stage_workspace_size(const mh3a_decoder* d, int stage, int64_t batc
     int64_t part = 0;
     for (int f = 0; f < 4; ++f)
         part = std::max(part, amp_partial_floats(d, stage, (int)batch, (int)length, f & 1, f & 2));
-    *bytes = (size_t)((2 * round_up(batch * d->stage_c[stage] * length, 64) + part) * (int64_t)sizeof(float));
+    *bytes = (size_t)((2 * round_up(batch * d->stage_c[stage] * length, 64) + stage_pk_floats(d, stage, batch, length) +
+                       part) *
+                      (int64_t)sizeof(float));
     return ok();
 }
 
@@ -973,8 +1084,9 @@ int mh3a_amp_stage(mh3a_decoder* d, int stage, const float* x, int64_t batch, in
     HIP_TRY(hipSetDevice(d->device));
     float* xb = static_cast<float*>(workspace);
     float* tb = xb + round_up(batch * d->stage_c[stage] * length, 64);
-    float* part = tb + round_up(batch * d->stage_c[stage] * length, 64);
-    rc = run_amp(d, stage, x, xb, tb, y, (int)batch, length, (flags & MH3A_FLAG_BF16_MFMA) != 0,
+    float* ab = tb + round_up(batch * d->stage_c[stage] * length, 64);
+    float* part = ab + stage_pk_floats(d, stage, batch, length);
+    rc = run_amp(d, stage, x, xb, tb, y, ab, (int)batch, length, (flags & MH3A_FLAG_BF16_MFMA) != 0,
                  (flags & MH3A_FLAG_BATCH_INVARIANT) != 0, part, static_cast<hipStream_t>(stream));
     if (rc) return rc;
     return ok();

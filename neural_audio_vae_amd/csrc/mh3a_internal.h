@@ -54,7 +54,19 @@ struct ConvArgs {
     int bf16;             // three-term bfloat16 split of the MFMA operands
     int ksplit;           // K ranges (divides the chunk count); > 1 uses `partial`
     float* partial;       // ksplit * tiles * tile_m * tile_n floats of raw sums
+    int pk_lp;            // packed input (see below): padded row length; 0 = plain rows
 };
+
+// Packed activated input of an AMP conv, written by the standalone
+// activation and read by the conv without any arithmetic on the way to LDS:
+// per batch item [chunk of 8 channels][hi = channel & 1][lp][p = (channel & 7) >> 1]
+// with lp = l + kPkPadL + kPkPadR positions, position n at index
+// kPkPadL + n, zeros in the pads and in channels past c. One chunk's window
+// is then two contiguous runs of 16-byte groups, already in the matrix-core
+// operand order. The pads cover the conv's zero padding and the overhang of
+// the last output tile: pad <= kPkPadL and tile_n - 1 + (k - 1) d - pad <= kPkPadR.
+constexpr int kPkPadL = 32;
+constexpr int kPkPadR = 288;
 
 // Tile shapes of the conv kernel: four consumer waves arranged WM x WN,
 // each computing MBW x NBW blocks of 32 x 32 outputs.
@@ -77,8 +89,8 @@ enum TileId {
 #undef MH3A_TILE
     TILE_COUNT
 };
-// Tiles with act-fused instances specialized for 3, 7 and 11 taps (the
-// shapes the tile model picks for the AMP convs); other shapes run those
+// Tiles with instances specialized for 3, 7 and 11 taps (the shapes the AMP
+// convs use, with or without the fused activation); other shapes run those
 // convs with a runtime tap count.
 constexpr bool tile_has_act_taps(int t) {
     return t == TILE_256x96 || t == TILE_256x64 || t == TILE_128x96 || t == TILE_128x128 || t == TILE_64x256 || t == TILE_32x256;
@@ -98,8 +110,12 @@ hipError_t launch_conv(const ConvArgs& a, TileId tile, hipStream_t stream);
 // What the planner needs of a conv layer.
 struct ConvShape {
     int c_in, c_out, taps, dil, phases;
-    bool act;  // act-fused (AMP) conv
+    bool act;  // activation fused into the operand staging
+    bool amp;  // an AMP conv (tile table measured for them)
 };
+// AMP activations of at least this many (batch x channel x position)
+// elements run as their own pass (see amp_act_fused in mh3a_host.cpp).
+constexpr int64_t kSeparateActMin = (int64_t)1 << 20;
 // Tile shape and K split of one launch.
 struct ConvPlan {
     TileId tile;
@@ -112,6 +128,20 @@ constexpr int64_t kMaxPartialFloats = (int64_t)32 << 20;
 ConvPlan plan_conv(const ConvShape& s, int positions, int batch, bool bf16, bool invariant, int num_cus);
 // Floats of partial sums the plan needs (0 without a K split).
 int64_t plan_partial_floats(const ConvShape& s, int positions, int groups, const ConvPlan& p);
+
+// The anti-aliased SnakeBeta alone: y = act(x), x (B, c, l) rows, y packed
+// (lp = l + kPkPadL + kPkPadR, pads written as zeros).
+struct ActArgs {
+    const float* x;
+    int64_t x_bstride;
+    float* y;
+    int64_t y_bstride;  // ceil(c / 8) * 8 * lp
+    int c;
+    int l;
+    int lp;
+    ActParams act;
+};
+hipError_t launch_act(const ActArgs& a, int batch, hipStream_t stream);
 
 // activation_post + conv_post (c -> 1, 7 taps, pad 3) + optional clamp.
 struct FinalArgs {

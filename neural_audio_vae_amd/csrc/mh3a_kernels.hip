@@ -13,6 +13,10 @@
 //   The same kernel runs the transposed convolutions as polyphase convs
 //   (one weight set per output phase, output stride = rate).
 //
+// act_kernel: the anti-aliased SnakeBeta alone, (B, C, L) rows -> the packed
+//   operand layout, for AMP convs that take their activated input from
+//   memory (their producer waves then copy it to LDS with no arithmetic).
+//
 // final_kernel: activation_post + conv_post (C -> 1, k = 7, pad 3) + clamp.
 //
 // Method: FastVideo API docs "minimax_h3_audio_vae" (MLXMiniMaxH3AudioVAE.decode,
@@ -95,16 +99,23 @@ __device__ __forceinline__ ActTaps load_act_taps(const float* tp) {
 // take the fast path: each thread computes two adjacent pairs from eight X
 // values and stores their four s values at once, then two adjacent outputs
 // from sixteen s values. Edge tiles take the general path.
-template <int CI>
-__device__ __forceinline__ void act_from_xs(float* __restrict__ as, float* __restrict__ xs, float* __restrict__ ss,
-                                            int ch0, int c_in, int l_in, int n_lo, int W, const ActTaps& f,
-                                            float2 ab, int ci, int lane32) {
+//
+// PAIRED writes the result in the conv kernel's operand layout instead of
+// rows: as[hi][w][p] holds channel 2p + hi, so that one 16-byte LDS read
+// gives a matrix-core lane its four K-steps (channels hi, 2 + hi, 4 + hi,
+// 6 + hi) at one position.
+template <int CI, bool PAIRED = false>
+__device__ __forceinline__ void act_from_xs(float* as, float* xs, float* __restrict__ ss, int ch0, int c_in, int l_in,
+                                            int n_lo, int W, const ActTaps& f, float2 ab, int ci, int lane32,
+                                            int as_stride) {
     const int ch = ch0 + ci;
     const bool live = ch < c_in;
     const int XS = act_xs_len(W), SS = act_ss_len(W);
     float* xrow = xs + ci * XS;
     float* srow = ss + ci * SS;
-    float* arow = as + ci * W;
+    static_assert(!PAIRED || CI == 8, "paired layout holds 8 channels");
+    constexpr int OS = PAIRED ? 4 : 1;  // float stride between positions
+    float* arow = PAIRED ? as + (ci & 1) * W * 4 + (ci >> 1) : as + ci * as_stride;
     const float(&fe)[6] = f.fe;
     const float(&fo)[6] = f.fo;
     const float(&fd)[12] = f.fd;
@@ -150,7 +161,12 @@ __device__ __forceinline__ void act_from_xs(float* __restrict__ as, float* __res
                 a0 = fmaf(fd[q], S[q + 1], a0);
                 a1 = fmaf(fd[q], S[q + 3], a1);
             }
-            *reinterpret_cast<float2*>(arow + w) = make_float2(a0, a1);
+            if constexpr (PAIRED) {
+                arow[w * OS] = a0;
+                arow[(w + 1) * OS] = a1;
+            } else {
+                *reinterpret_cast<float2*>(arow + w) = make_float2(a0, a1);
+            }
         }
         return;
     }
@@ -182,16 +198,18 @@ __device__ __forceinline__ void act_from_xs(float* __restrict__ as, float* __res
 #pragma unroll
             for (int q = 0; q < 12; ++q) v = fmaf(fd[q], sv[q], v);
         }
-        arow[w] = v;
+        arow[w * OS] = v;
     }
 }
 
 // Load X[n_lo - 6 ...] (replicate-clamped) for channel ch0 + ci into xs and
-// run act_from_xs (the single-buffer path of the final kernel).
+// run act_from_xs into rows of `as` (stride as_stride; `as` may be xs itself
+// with stride act_xs_len(W): a channel's x row is dead once its up pass is
+// done, and each channel's rows belong to one wave).
 template <int CI>
-__device__ __forceinline__ void stage_act(float* __restrict__ as, float* __restrict__ xs, float* __restrict__ ss,
-                                          const float* __restrict__ xb, int ch0, int c_in, int l_in, int n_lo,
-                                          int W, const ActTaps& f, const float2* abp, int ci, int lane32) {
+__device__ __forceinline__ void stage_act(float* as, float* xs, float* __restrict__ ss, const float* __restrict__ xb,
+                                          int ch0, int c_in, int l_in, int n_lo, int W, const ActTaps& f,
+                                          const float2* abp, int ci, int lane32, int as_stride) {
     const int ch = ch0 + ci;
     const bool live = ch < c_in;
     const float* xc = xb + (int64_t)(live ? ch : 0) * l_in;
@@ -199,7 +217,7 @@ __device__ __forceinline__ void stage_act(float* __restrict__ as, float* __restr
     float* xrow = xs + ci * act_xs_len(W);
     for (int w = lane32; w < act_xs_len(W); w += 32) xrow[w] = live ? xc[clampi(n_lo - 6 + w, 0, l_in - 1)] : 0.0f;
     wave_lds_sync();
-    act_from_xs<CI>(as, xs, ss, ch0, c_in, l_in, n_lo, W, f, ab, ci, lane32);
+    act_from_xs<CI>(as, xs, ss, ch0, c_in, l_in, n_lo, W, f, ab, ci, lane32, as_stride);
 }
 
 __device__ __forceinline__ float round_bf16(float v) {
@@ -224,9 +242,14 @@ __host__ __device__ constexpr int conv_lds_floats(int W, bool act) {
 // epilogue of one tile overlaps the staging of the next. One workgroup
 // barrier per item hands the buffers over.
 template <int MBW, int NBW, int WM, int WN, bool ACT, bool BF16, int TAPS>
-__global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
+// (tiles of at most 2 x 2 blocks per wave keep two workgroups per CU: <= 128 VGPRs)
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MBW * NBW <= 4 ? 4 : 1)))
+conv_kernel(ConvArgs a) {
     static_assert(WM * WN == 4, "four consumer waves");
     constexpr int CI = kChunk;
+    // AMP convs without the fused activation (compile-time taps) read the
+    // packed activated input; other plain convs read rows.
+    constexpr bool PK = !ACT && TAPS > 0;
     constexpr int NWG = WN * NBW * 32;
     constexpr int MWG = WM * MBW * 32;
     extern __shared__ float lds[];
@@ -318,16 +341,19 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     // write item (t, c)'s row to LDS (from the prefetch registers when it
     // fits) and, with the activation, compute it into dst
     auto stage = [&](const Tile& t, int c, float* dst) {
-        float* row = ACT ? xs + pci * act_xs_len(W) : dst + pci * W;
+        // with the activation the x row goes to its staging row; without, the
+        // values go straight to the operand layout (position stride 4)
+        constexpr int RS = ACT ? 1 : 4;
+        float* row = ACT ? xs + pci * act_xs_len(W) : dst + (pci & 1) * W * 4 + (pci >> 1);
         if (prefetchable) {
 #pragma unroll
             for (int r = 0; r < XR; ++r) {
                 const int w = plane + 32 * r;
-                if (w < row_len) row[w] = xr[r];
+                if (w < row_len) row[w * RS] = xr[r];
             }
             ab_st = ab_pf;
         } else {
-            for (int w = plane; w < row_len; w += 32) row[w] = row_value(t, c, w);
+            for (int w = plane; w < row_len; w += 32) row[w * RS] = row_value(t, c, w);
             if constexpr (ACT) {
                 const int ch = (t.c0 + c) * CI + pci;
                 ab_st = ch < a.c_in ? a.act.ab[ch] : make_float2(0.0f, 0.0f);
@@ -341,7 +367,8 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     auto compute = [&](const Tile& t, int c, float* dst) {
         if constexpr (ACT) {
             wave_lds_sync();
-            act_from_xs<CI>(dst, xs, ss, (t.c0 + c) * CI, a.c_in, a.l_in, t.n_lo, W, ftaps, ab_st, pci, plane);
+            act_from_xs<CI, true>(dst, xs, ss, (t.c0 + c) * CI, a.c_in, a.l_in, t.n_lo, W, ftaps, ab_st, pci, plane,
+                                  0);
         }
     };
 
@@ -392,12 +419,17 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
         for (int mb = 0; mb < MBW; ++mb) dst[mb] = wp[(int64_t)min(mb_base + mb, mb_tot - 1) * G * 64];
     };
     // B operand of one tap: the 4 channel pairs x NBW blocks of 32 positions
+    // (operand layout [hi][position][p]: one 16-byte read per block)
     auto load_b = [&](float (&dst)[4][NBW], const float* buf, int j) {
-        const float* brow = buf + hi * W + colbase + j * a.dil;
+        const float* bp = buf + (hi * W + colbase + j * a.dil) * 4;
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) dst[p][nb] = brow[2 * p * W + nb * 32];
+        for (int nb = 0; nb < NBW; ++nb) {
+            const float4 v = *reinterpret_cast<const float4*>(bp + nb * 128);
+            dst[0][nb] = v.x;
+            dst[1][nb] = v.y;
+            dst[2][nb] = v.z;
+            dst[3][nb] = v.w;
+        }
     };
     auto mfma_tap = [&](const float4 (&A)[MBW], const float (&Bv)[4][NBW]) {
 #pragma unroll
@@ -429,6 +461,45 @@ __global__ void __launch_bounds__(512) conv_kernel(ConvArgs a) {
     // and consumers run separate loops with one barrier per item each, so
     // the compiler allocates registers for the larger role only.
     if (producer) {
+        if constexpr (PK) {
+            // Packed input: the window of each channel parity is a contiguous
+            // run of W 16-byte groups, already in the operand layout; the
+            // memory unit copies it to LDS 1 KB per wave instruction, so the
+            // producers issue no vector ALU work next to the matrix cores.
+            const int pw = wave - 4;
+            const int segs = (W + 63) >> 6;  // 64-position segments per parity
+            auto dma = [&](const Tile& t, int c, float* dst) {
+                const float* src =
+                    a.x + (int64_t)t.b * a.x_bstride + ((int64_t)(t.c0 + c) * 2 * a.pk_lp + kPkPadL + t.n_lo) * 4;
+                for (int q = pw; q < 2 * segs; q += 4) {
+                    const int hp = q >= segs ? 1 : 0;
+                    const int pos0 = (q - hp * segs) * 64;
+                    const int pos = pos0 + lane;
+                    auto* ldst = (__attribute__((address_space(3))) void*)(dst + (hp * W + pos0) * 4);
+                    if (pos < W)
+                        __builtin_amdgcn_global_load_lds((const void*)(src + ((int64_t)hp * a.pk_lp + pos) * 4), ldst, 16,
+                                                         0, 0);
+                }
+            };
+            Tile nt = tile_at(t_begin);
+            int nc = 0;
+            dma(nt, 0, abuf);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            for (int it = 0; it < n_items; ++it) {
+                if (it + 1 < n_items) {
+                    if (++nc == nchs) {
+                        nc = 0;
+                        nt = tile_at(t_begin + (it + 1) / nchs);
+                    }
+                    dma(nt, nc, abuf + ((it + 1) & 1) * CI * W);
+                }
+                // the copies land in LDS before the buffer is handed over
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
+            return;
+        }
         Tile cur = tile_at(t_begin);
         int cur_c = 0;
         if (prefetchable) prefetch(cur, 0);
@@ -681,7 +752,7 @@ static hipError_t launch_persistent(K kernel, const ConvArgs& a, int64_t tiles, 
     return hipGetLastError();
 }
 
-template <int MBW, int NBW, int WM, int WN, bool ACT_TILE>
+template <int MBW, int NBW, int WM, int WN, bool TAPS_TILE>
 static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
     constexpr int NWG = WN * NBW * 32;
     constexpr int MWG = WM * MBW * 32;
@@ -691,21 +762,34 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
     const bool act = a.act.taps != nullptr;
     const size_t lds = sizeof(float) * (size_t)conv_lds_floats(W, act);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
-    if (act) {
-        if constexpr (ACT_TILE) {
-#define MH3A_ACT_TAPS(T)                                                                                            \
+    // instances with the AMP tap counts compiled in (3, 7, 11)
+#define MH3A_TAPS(ACTV, T)                                                                                          \
     if (a.taps == T)                                                                                               \
-        return a.bf16 ? launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, true, T>, a, tiles, lds, stream)     \
-                      : launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, false, T>, a, tiles, lds, stream);
-            MH3A_ACT_TAPS(3)
-            MH3A_ACT_TAPS(7)
-            MH3A_ACT_TAPS(11)
-#undef MH3A_ACT_TAPS
+        return a.bf16 ? launch_persistent(conv_kernel<MBW, NBW, WM, WN, ACTV, true, T>, a, tiles, lds, stream)     \
+                      : launch_persistent(conv_kernel<MBW, NBW, WM, WN, ACTV, false, T>, a, tiles, lds, stream);
+    if (act) {
+        if constexpr (TAPS_TILE) {
+            MH3A_TAPS(true, 3)
+            MH3A_TAPS(true, 7)
+            MH3A_TAPS(true, 11)
         }
         return a.bf16 ? launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, true, 0>, a, tiles, lds, stream)
                       : launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, false, 0>, a, tiles, lds, stream);
     }
-    return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, false, 0>, a, tiles, lds, stream);
+    if (a.pk_lp > 0) {
+        // packed input: compile-time taps only
+        if constexpr (TAPS_TILE) {
+            if (NWG > 256) return hipErrorInvalidValue;
+            MH3A_TAPS(false, 3)
+            MH3A_TAPS(false, 7)
+            MH3A_TAPS(false, 11)
+        }
+        return hipErrorInvalidValue;
+    }
+#undef MH3A_TAPS
+    // (in_proj, conv_pre and the upsamplers: fp32 operands, runtime taps)
+    return a.bf16 ? hipErrorInvalidValue
+                  : launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, false, 0>, a, tiles, lds, stream);
 }
 
 hipError_t launch_conv(const ConvArgs& a, TileId tile, hipStream_t stream) {
@@ -755,7 +839,7 @@ __global__ void __launch_bounds__(256) final_kernel(FinalArgs a) {
     const ActTaps f = load_act_taps(a.act.taps);
     for (int c0 = 0; c0 < a.c; c0 += CI) {
         __syncthreads();
-        stage_act<CI>(as, xs, ss, xb, c0, a.c, a.l, t0 - 3, W, f, a.act.ab, threadIdx.x >> 5, threadIdx.x & 31);
+        stage_act<CI>(as, xs, ss, xb, c0, a.c, a.l, t0 - 3, W, f, a.act.ab, threadIdx.x >> 5, threadIdx.x & 31, W);
         __syncthreads();
         for (int ci = 0; ci < CI && c0 + ci < a.c; ++ci) {
             const float* wr = a.w + (c0 + ci) * 7;
@@ -769,6 +853,57 @@ __global__ void __launch_bounds__(256) final_kernel(FinalArgs a) {
         if (a.clamp) v = fminf(fmaxf(v, -1.0f), 1.0f);
         a.y[(int64_t)b * a.l + t] = v;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Standalone activation: a workgroup owns kActT padded positions of kChunk
+// channels (32 threads per channel, as in the conv producers), computes them
+// into LDS rows and stores them packed: each thread writes the 16-byte group
+// of one (hi, position), so every wave stores 1 KB contiguous.
+// ---------------------------------------------------------------------------
+constexpr int kActT = 256;
+
+template <int W>
+__global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
+    constexpr int CI = kChunk;
+    // each channel's result row reuses its x row (dead after the up pass)
+    static_assert(act_xs_len(W) >= W, "result rows alias the x rows");
+    __shared__ __attribute__((aligned(16))) float xs[CI * act_xs_len(W)];
+    __shared__ __attribute__((aligned(16))) float ss[CI * act_ss_len(W)];
+    float* as = xs;
+    const int t0 = blockIdx.x * W - kPkPadL;  // first position (pads included)
+    const int chunk = blockIdx.y;
+    const int b = blockIdx.z;
+    const int ci = threadIdx.x >> 5, lane32 = threadIdx.x & 31;
+    float* yc = a.y + (int64_t)b * a.y_bstride + (int64_t)chunk * 2 * a.lp * 4;
+    if (t0 >= a.l || t0 + W <= 0) {
+        // all padding
+        for (int idx = threadIdx.x; idx < 2 * W; idx += 256) {
+            const int hi = idx / W, w = idx - hi * W;
+            const int q = t0 + kPkPadL + w;
+            if (q < a.lp) *reinterpret_cast<float4*>(yc + ((int64_t)hi * a.lp + q) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        return;
+    }
+    const ActTaps f = load_act_taps(a.act.taps);
+    constexpr int XS = act_xs_len(W);
+    stage_act<CI>(as, xs, ss, a.x + (int64_t)b * a.x_bstride, chunk * CI, a.c, a.l, t0, W, f, a.act.ab, ci, lane32, XS);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 2 * W; idx += 256) {
+        const int hi = idx / W, w = idx - hi * W;
+        const int q = t0 + kPkPadL + w;  // index in the padded row
+        if (q >= a.lp) continue;
+        const float4 v =
+            make_float4(as[hi * XS + w], as[(2 + hi) * XS + w], as[(4 + hi) * XS + w], as[(6 + hi) * XS + w]);
+        *reinterpret_cast<float4*>(yc + ((int64_t)hi * a.lp + q) * 4) = v;
+    }
+}
+
+hipError_t launch_act(const ActArgs& a, int batch, hipStream_t stream) {
+    if (a.c < 1 || a.l < 1 || batch < 1 || !a.act.taps || a.lp != a.l + kPkPadL + kPkPadR) return hipErrorInvalidValue;
+    dim3 grid((a.lp + kActT - 1) / kActT, (a.c + kChunk - 1) / kChunk, batch);
+    hipLaunchKernelGGL(act_kernel<kActT>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_final(const FinalArgs& a, int batch, hipStream_t stream) {

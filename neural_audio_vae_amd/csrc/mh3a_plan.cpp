@@ -91,7 +91,7 @@ TileId choose_tile(const ConvShape& L, int positions, int groups, bool bf16, int
     // The act-fused AMP convs use the shapes measured fastest per width in a
     // tile sweep of every stage (one-workgroup-per-CU shapes only pay off at
     // 512 channels, where they fill the 256 CUs in one round).
-    if (act) {
+    if (L.amp) {
         if (L.c_out >= 512) return TILE_256x96;
         if (L.c_out >= 256) return TILE_256x64;
         if (L.c_out >= 128) return TILE_128x128;

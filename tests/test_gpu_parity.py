@@ -251,6 +251,19 @@ def test_c4_amp_stage_microbench(default_decoder, default_params, dev):
         assert_close(f"c4 item {item} [{a},{b})", got[item][:, a:b], ref)
 
 
+def test_stage0_packed_activation_path(default_decoder, default_params, dev):
+    # Stage 0 (512 channels) on (1, 512, 3000): large enough that each conv
+    # takes its activated input from the standalone pass (packed, zero
+    # padded), including the tiles that overhang both ends.
+    x = synth.make_signal((1, 512, 3000), seed=5)
+    got = host(default_decoder.amp_stage(0, gpu(x, dev)))
+    margin = 120
+    for a, b in [(0, 48), (1500, 1548), (2952, 3000)]:
+        lo, hi = max(0, a - margin), min(3000, b + margin)
+        ref = O.stage_amp(x[0][:, lo:hi], default_params, 0)[:, a - lo:b - lo]
+        assert_close(f"stage 0 packed [{a},{b})", got[0][:, a:b], ref)
+
+
 def test_amp_stage_rejects_bad_arguments(default_decoder, dev):
     from neural_audio_vae_amd import MH3AError
     x = torch.zeros((1, 256, 50), device=dev)
