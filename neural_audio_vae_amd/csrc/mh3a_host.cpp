@@ -362,8 +362,9 @@ int64_t plan_partial_floats(const ConvLayer& L, int positions, int groups, const
 // waits on it; at 256+ channels it is also repeated per M tile. Separate,
 // a standalone pass writes the packed input and the conv's producers only
 // copy it to LDS. Measured per stage (B=2 x 1200 latents): separate wins at
-// 512 channels, ties at 256, loses below (the pass costs more than the
-// contention there). Small launches stay fused (one launch, less latency).
+// 128 to 512 channels, ties at 64 and loses below, where the pass (~30 us
+// per 15 M samples) costs more than the contention saves. Small launches
+// stay fused (one launch, less latency).
 // MH3A_AMP_ACT=fused|separate overrides (a tuning aid).
 bool amp_act_fused(const mh3a_decoder* d, int64_t batch, int64_t c, int64_t len) {
     if (!d->pk_ok) return true;
@@ -375,7 +376,7 @@ bool amp_act_fused(const mh3a_decoder* d, int64_t batch, int64_t c, int64_t len)
         return 0;
     }();
     if (mode) return mode == 1;
-    return c < 256 || batch * c * len < kSeparateActMin;
+    return c < 128 || batch * c * len < kSeparateActMin;
 }
 
 // Plans are cached per launch shape.

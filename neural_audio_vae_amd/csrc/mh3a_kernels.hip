@@ -54,12 +54,15 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// LDS row lengths of the activation staging for window width W: the x row
-// holds X[n_lo - 6 ...] with room for the two-pair reads, the s row holds the
-// 2x-rate slots shifted by one (slot m at index m + 1) so that the pair
-// stores and the down-filter reads are 16-byte aligned.
+// LDS row lengths of the activation staging for window width W. The x row
+// holds X[n_lo - 6 ...] with room for the two-pair reads. The 2x-rate
+// signal is kept as two planes of act_ss_half(W): even slots and odd slots
+// (the latter shifted by one), so that both the up pass's pair stores and
+// the down pass's tap reads are 8-byte accesses at an 8-byte lane stride
+// (no LDS bank conflicts).
 __host__ __device__ constexpr int act_xs_len(int W) { return (W + 14 + 3) & ~3; }
-__host__ __device__ constexpr int act_ss_len(int W) { return (2 * W + 14 + 3) & ~3; }
+__host__ __device__ constexpr int act_ss_half(int W) { return (W + 8 + 3) & ~3; }
+__host__ __device__ constexpr int act_ss_len(int W) { return 2 * act_ss_half(W); }
 
 // The resampler taps in registers: even / odd parity up taps (gain folded)
 // and the down taps. Loaded once per kernel: they are the same for every
@@ -110,9 +113,12 @@ __device__ __forceinline__ void act_from_xs(float* as, float* xs, float* __restr
                                             int as_stride) {
     const int ch = ch0 + ci;
     const bool live = ch < c_in;
-    const int XS = act_xs_len(W), SS = act_ss_len(W);
+    const int XS = act_xs_len(W), SH = act_ss_half(W);
     float* xrow = xs + ci * XS;
-    float* srow = ss + ci * SS;
+    // slot m of the 2x-rate signal, s[2 n_lo - 5 + m]: even m = 2k at ev[k],
+    // odd m = 2k + 1 at od[k + 1]
+    float* ev = ss + ci * 2 * SH;
+    float* od = ev + SH;
     static_assert(!PAIRED || CI == 8, "paired layout holds 8 channels");
     constexpr int OS = PAIRED ? 4 : 1;  // float stride between positions
     float* arow = PAIRED ? as + (ci & 1) * W * 4 + (ci >> 1) : as + ci * as_stride;
@@ -138,28 +144,35 @@ __device__ __forceinline__ void act_from_xs(float* as, float* xs, float* __restr
                 ue1 = fmaf(fe[e], X[6 - e], ue1);
                 uo1 = fmaf(fo[e], X[7 - e], uo1);
             }
-            // slots 2 idx - 1 .. 2 idx + 2 at srow[2 idx .. 2 idx + 3]
-            *reinterpret_cast<float4*>(srow + 2 * idx) =
-                make_float4(snake_beta(ue0, ab.x, ab.y), snake_beta(uo0, ab.x, ab.y), snake_beta(ue1, ab.x, ab.y),
-                            snake_beta(uo1, ab.x, ab.y));
+            // s[2t'] is slot 2 idx - 1 (od[idx]), s[2t' + 1] slot 2 idx (ev[idx])
+            *reinterpret_cast<float2*>(od + idx) = make_float2(snake_beta(ue0, ab.x, ab.y), snake_beta(ue1, ab.x, ab.y));
+            *reinterpret_cast<float2*>(ev + idx) = make_float2(snake_beta(uo0, ab.x, ab.y), snake_beta(uo1, ab.x, ab.y));
         }
         wave_lds_sync();
-        // outputs w, w + 1: a[w] = sum_q f[q] slot[2w + q] = sum_q f[q] srow[2w + q + 1]
+        // outputs w, w + 1: a[w] = sum_q f[q] slot[2w + q], i.e. f[2j] ev[w + j]
+        // and f[2j + 1] od[w + j + 1]; w even, so the reads are 8-byte aligned
+        const float2* ev2 = reinterpret_cast<const float2*>(__builtin_assume_aligned(ev, 8));
+        const float2* od2 = reinterpret_cast<const float2*>(__builtin_assume_aligned(od, 8));
         for (int w = 2 * lane32; w < W; w += 64) {
-            float S[16];
+            float E[8], O[8];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const float4 t4 = *reinterpret_cast<const float4*>(srow + 2 * w + 4 * v);
-                S[4 * v] = t4.x;
-                S[4 * v + 1] = t4.y;
-                S[4 * v + 2] = t4.z;
-                S[4 * v + 3] = t4.w;
+                const float2 e2 = ev2[w / 2 + v], o2 = od2[w / 2 + v];
+                E[2 * v] = e2.x;
+                E[2 * v + 1] = e2.y;
+                O[2 * v] = o2.x;
+                O[2 * v + 1] = o2.y;
             }
             float a0 = 0.f, a1 = 0.f;
 #pragma unroll
             for (int q = 0; q < 12; ++q) {
-                a0 = fmaf(fd[q], S[q + 1], a0);
-                a1 = fmaf(fd[q], S[q + 3], a1);
+                if (q % 2 == 0) {
+                    a0 = fmaf(fd[q], E[q / 2], a0);
+                    a1 = fmaf(fd[q], E[q / 2 + 1], a1);
+                } else {
+                    a0 = fmaf(fd[q], O[(q + 1) / 2], a0);
+                    a1 = fmaf(fd[q], O[(q + 1) / 2 + 1], a1);
+                }
             }
             if constexpr (PAIRED) {
                 arow[w * OS] = a0;
@@ -171,7 +184,8 @@ __device__ __forceinline__ void act_from_xs(float* as, float* xs, float* __restr
         return;
     }
 
-    // pairs t' = n_lo - 3 + idx, idx in [0, W + 6): slot 2 idx - 1 <- s[2t'], slot 2 idx <- s[2t' + 1]
+    // pairs t' = n_lo - 3 + idx, idx in [0, W + 6): slot 2 idx - 1 (od[idx]) <- s[2t'],
+    // slot 2 idx (ev[idx]) <- s[2t' + 1]
     for (int idx = lane32; idx < W + 6; idx += 32) {
         const int tq = n_lo - 3 + idx;
         const int tc = clampi(tq, 0, l_in - 1);
@@ -186,17 +200,16 @@ __device__ __forceinline__ void act_from_xs(float* as, float* xs, float* __restr
         float so = snake_beta(uo, ab.x, ab.y);
         if (tq < 0) so = se;
         if (tq >= l_in) se = so;
-        srow[2 * idx] = se;
-        srow[2 * idx + 1] = so;
+        od[idx] = se;
+        ev[idx] = so;
     }
     wave_lds_sync();
     for (int w = lane32; w < W; w += 32) {
         const int n = n_lo + w;
         float v = 0.0f;
         if (live && n >= 0 && n < l_in) {
-            const float* sv = srow + 2 * w + 1;
 #pragma unroll
-            for (int q = 0; q < 12; ++q) v = fmaf(fd[q], sv[q], v);
+            for (int q = 0; q < 12; ++q) v = fmaf(fd[q], (q % 2 == 0) ? ev[w + q / 2] : od[w + (q + 1) / 2], v);
         }
         arow[w * OS] = v;
     }
@@ -206,16 +219,27 @@ __device__ __forceinline__ void act_from_xs(float* as, float* xs, float* __restr
 // run act_from_xs into rows of `as` (stride as_stride; `as` may be xs itself
 // with stride act_xs_len(W): a channel's x row is dead once its up pass is
 // done, and each channel's rows belong to one wave).
-template <int CI>
+// The row is loaded into registers with every load in flight at once (a
+// loop of load-then-store would wait one memory latency per element).
+template <int CI, int W>
 __device__ __forceinline__ void stage_act(float* as, float* xs, float* __restrict__ ss, const float* __restrict__ xb,
-                                          int ch0, int c_in, int l_in, int n_lo, int W, const ActTaps& f,
+                                          int ch0, int c_in, int l_in, int n_lo, const ActTaps& f,
                                           const float2* abp, int ci, int lane32, int as_stride) {
+    constexpr int XL = act_xs_len(W);
+    constexpr int NR = (XL + 31) / 32;
     const int ch = ch0 + ci;
     const bool live = ch < c_in;
     const float* xc = xb + (int64_t)(live ? ch : 0) * l_in;
     const float2 ab = live ? abp[ch] : make_float2(0.0f, 0.0f);
-    float* xrow = xs + ci * act_xs_len(W);
-    for (int w = lane32; w < act_xs_len(W); w += 32) xrow[w] = live ? xc[clampi(n_lo - 6 + w, 0, l_in - 1)] : 0.0f;
+    float* xrow = xs + ci * XL;
+    float v[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) v[r] = xc[clampi(n_lo - 6 + lane32 + 32 * r, 0, l_in - 1)];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int w = lane32 + 32 * r;
+        if (w < XL) xrow[w] = live ? v[r] : 0.0f;
+    }
     wave_lds_sync();
     act_from_xs<CI>(as, xs, ss, ch0, c_in, l_in, n_lo, W, f, ab, ci, lane32, as_stride);
 }
@@ -839,7 +863,7 @@ __global__ void __launch_bounds__(256) final_kernel(FinalArgs a) {
     const ActTaps f = load_act_taps(a.act.taps);
     for (int c0 = 0; c0 < a.c; c0 += CI) {
         __syncthreads();
-        stage_act<CI>(as, xs, ss, xb, c0, a.c, a.l, t0 - 3, W, f, a.act.ab, threadIdx.x >> 5, threadIdx.x & 31, W);
+        stage_act<CI, W>(as, xs, ss, xb, c0, a.c, a.l, t0 - 3, f, a.act.ab, threadIdx.x >> 5, threadIdx.x & 31, W);
         __syncthreads();
         for (int ci = 0; ci < CI && c0 + ci < a.c; ++ci) {
             const float* wr = a.w + (c0 + ci) * 7;
@@ -887,7 +911,7 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
     }
     const ActTaps f = load_act_taps(a.act.taps);
     constexpr int XS = act_xs_len(W);
-    stage_act<CI>(as, xs, ss, a.x + (int64_t)b * a.x_bstride, chunk * CI, a.c, a.l, t0, W, f, a.act.ab, ci, lane32, XS);
+    stage_act<CI, W>(as, xs, ss, a.x + (int64_t)b * a.x_bstride, chunk * CI, a.c, a.l, t0, f, a.act.ab, ci, lane32, XS);
     __syncthreads();
     for (int idx = threadIdx.x; idx < 2 * W; idx += 256) {
         const int hi = idx / W, w = idx - hi * W;
