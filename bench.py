@@ -12,7 +12,9 @@ step (40 latents per second of 32 kHz audio). The default workload is two
 30 s items (B=2, N=1200) with the default MiniMax-H3 decoder and seeded
 random weights. `roofline` covers the dominant kernel, the act-fused AMP
 convolution, whose kernel durations come from HIP events the library
-records on the decode stream around every launch during the timed steps.
+records on the decode stream around every AMP conv launch of the last timed
+step (other launches are not bracketed there; a second, untimed pass with
+every launch bracketed gives the per-class breakdown).
 `cpu_baseline` times the CPU oracle on a bounded sample (the first 80
 latents of one item, decoded in full).
 """
@@ -121,7 +123,7 @@ def main():
               "(the decode path runs on a single GPU).", file=sys.stderr)
         return 2
     import torch
-    from neural_audio_vae_amd import Decoder, synth
+    from neural_audio_vae_amd import Decoder, _lib, synth
 
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
@@ -139,24 +141,35 @@ def main():
         dec.decode(z, flags=flags, out=out, stream=stream)
     torch.cuda.synchronize()
 
-    dec.timing(True)
+    # Timed region: K decodes. In the last one the library brackets each AMP
+    # conv launch (the roofline kernel) with HIP events on the decode stream
+    # (events on every step would add their own cost, ~2%, to every step).
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        if i == args.steps - 1:
+            dec.timing(_lib.MH3A_TIMING_AMP_CONV)
         dec.decode(z, flags=flags, out=out, stream=stream)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(stop)
+    amp_only = dec.timing_read()
+    # Per-class breakdown from a second, untimed pass with every launch
+    # bracketed (the events add ~2% when on every launch).
+    dec.timing(_lib.MH3A_TIMING_ALL)
+    for _ in range(args.steps):
+        dec.decode(z, flags=flags, out=out, stream=stream)
+    torch.cuda.synchronize()
     kernels = dec.timing_read()
-    dec.timing(False)
+    dec.timing(_lib.MH3A_TIMING_OFF)
 
     ms_step = ms_total / args.steps
     audio_s = batch * frames / LATENTS_PER_SECOND
     value = audio_s / (ms_step / 1e3)
-    amp = kernels.get("amp_conv", {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+    amp = amp_only.get("amp_conv", {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
     achieved = amp["flops"] / (amp["ms"] / 1e3) / 1e12 if amp["ms"] > 0 else 0.0
     per_step = {
         name: {
@@ -193,14 +206,14 @@ def main():
         },
         "algorithmic_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
         "roofline": {
-            "kernel": "conv_kernel (AMP dilated conv with fused anti-aliased SnakeBeta)",
+            "kernel": "conv_kernel (AMP dilated conv; activation fused or from the packed pass)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": FP32_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4),
             "traffic": measured_traffic(args.workload, flags),
-            "launches_per_step": amp["launches"] / args.steps,
+            "launches_timed": amp["launches"],
             "avg_launch_us": round(1e3 * amp["ms"] / max(1, amp["launches"]), 2),
             "flops_per_launch": amp["flops"] / max(1, amp["launches"]),
         },

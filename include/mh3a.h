@@ -198,8 +198,10 @@ int mh3a_amp_stage(mh3a_decoder* dec, int stage, const float* x, int64_t batch, 
                    void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
- * Kernel timing (a measurement aid). While enabled, every launch a decode
- * makes is bracketed by HIP events on the decode's stream and tagged with
+ * Kernel timing (a measurement aid). While enabled (MH3A_TIMING_ALL), every
+ * launch a decode makes is bracketed by HIP events on the decode's stream
+ * (MH3A_TIMING_AMP_CONV: only the AMP conv launches, which keeps the events'
+ * own cost off the other launches) and tagged with
  * its kernel class and the algorithmic work it does: FLOPs of the dense
  * convolution (2 * C_out * C_in * k per output position, the transposed
  * conv counted at its k taps per input sample) and compulsory HBM bytes
@@ -216,6 +218,10 @@ typedef struct {
     double bytes;
 } mh3a_kernel_stats;
 #define MH3A_MAX_KERNEL_KINDS 8
+#define MH3A_TIMING_OFF 0
+#define MH3A_TIMING_ALL 1
+#define MH3A_TIMING_AMP_CONV 2
+/* enable: one of MH3A_TIMING_*; other values are MH3A_E_INVALID_ARG. */
 int mh3a_timing_enable(mh3a_decoder* dec, int enable);
 int mh3a_timing_read(mh3a_decoder* dec, mh3a_kernel_stats* stats, int max_stats, int* n_stats);
 

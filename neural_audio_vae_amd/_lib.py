@@ -26,6 +26,7 @@ MH3A_FLAG_DENORMALIZE = 0x1
 MH3A_FLAG_BF16_MFMA = 0x2
 MH3A_FLAG_NO_CLAMP = 0x4
 MH3A_FLAG_BATCH_INVARIANT = 0x8
+MH3A_TIMING_OFF, MH3A_TIMING_ALL, MH3A_TIMING_AMP_CONV = 0, 1, 2
 
 MH3A_MAX_STAGES = 8
 MH3A_MAX_RESBLOCKS = 4

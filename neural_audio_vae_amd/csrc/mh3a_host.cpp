@@ -158,6 +158,7 @@ struct TimingRec {
 
 struct Timing {
     bool on = false;
+    bool amp_only = false;  // only the AMP conv launches
     std::vector<hipEvent_t> evs;
     int used = 0;
     std::vector<TimingRec> recs;
@@ -416,9 +417,9 @@ struct TimedLaunch {
     const mh3a_decoder* d;
     hipStream_t st;
     int ev = -1;
-    TimedLaunch(const mh3a_decoder* d_, hipStream_t st_) : d(d_), st(st_) {
+    TimedLaunch(const mh3a_decoder* d_, hipStream_t st_, int kind) : d(d_), st(st_) {
         Timing& t = d->timing;
-        if (!t.on) return;
+        if (!t.on || (t.amp_only && kind != KIND_AMP)) return;
         while ((int)t.evs.size() < t.used + 2) {
             hipEvent_t e;
             // timing-only events: no system-scope fence (no cache writeback between launches)
@@ -474,7 +475,7 @@ hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, i
     a.ksplit = plan.ksplit;
     a.partial = partial;
     if (plan.ksplit > 1 && !partial) return hipErrorInvalidValue;
-    TimedLaunch tl(d, st);
+    TimedLaunch tl(d, st, L.kind);
     hipError_t e = launch_conv(a, plan.tile, st);
     const double outs = (double)batch * L.c_out * L.out_mul * positions;
     const double flops = 2.0 * L.c_out * (double)L.c_in * L.alg_taps * positions * batch;
@@ -521,7 +522,7 @@ hipError_t run_act(const mh3a_decoder* d, int act_idx, const float* x, float* y,
     a.l = (int)len;
     a.lp = (int)pk_lp(len);
     a.act = act_params(d, act_idx);
-    TimedLaunch tl(d, st);
+    TimedLaunch tl(d, st, KIND_AMP_ACT);
     hipError_t e = launch_act(a, batch, st);
     const double n = (double)batch * c * len;
     // 12 up + 12 down multiply-adds and the SnakeBeta per sample; in and out
@@ -701,7 +702,7 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
     fa.y = wave;
     fa.clamp = (flags & MH3A_FLAG_NO_CLAMP) ? 0 : 1;
     if (upto >= 0) return fail(MH3A_E_INVALID_ARG, "layer index %d out of range", upto);
-    TimedLaunch tl(d, st);
+    TimedLaunch tl(d, st, KIND_FINAL);
     HIP_TRY(launch_final(fa, B, st));
     tl.done(KIND_FINAL, 2.0 * 7 * cin * (double)len * B, 4.0 * ((double)B * cin * len + (double)B * len + 7 * cin));
     return ok();
@@ -963,7 +964,9 @@ void mh3a_destroy(mh3a_decoder* d) {
 
 int mh3a_timing_enable(mh3a_decoder* d, int enable) {
     if (!d) return fail(MH3A_E_INVALID_ARG, "decoder is null");
+    if (enable < 0 || enable > MH3A_TIMING_AMP_CONV) return fail(MH3A_E_INVALID_ARG, "bad timing mode %d", enable);
     d->timing.on = enable != 0;
+    d->timing.amp_only = enable == MH3A_TIMING_AMP_CONV;
     d->timing.used = 0;
     d->timing.recs.clear();
     return ok();
