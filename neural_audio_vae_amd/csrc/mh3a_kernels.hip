@@ -602,6 +602,13 @@ conv_kernel(ConvArgs a) {
             const int nph = has_next ? nxt.ph : cur.ph;
             const int ng0 = has_next ? (nxt.c0 + nxt_c) * TAPS : g0;
             const int nmb = has_next ? nmb_base : mb_base;
+            // Large wave tiles (more than 2 x 2 blocks) double-buffer the LDS
+            // operands across taps: tap j + 1's reads go out before tap j's
+            // MFMAs, so only tap 0 waits on LDS latency. (Smaller tiles would
+            // pay for the registers with resident workgroups.)
+            constexpr bool BDB = MBW * NBW > 4;
+            float Bb[BDB ? 2 : 1][4][NBW];
+            if constexpr (BDB) load_b(Bb[0], cur_buf, 0);
 #pragma unroll
             for (int j = 0; j < TAPS; ++j) {
                 float4(&use)[MBW] = (j % 3 == 0) ? Ar0 : ((j % 3 == 1) ? Ar1 : Ar2);
@@ -614,11 +621,14 @@ conv_kernel(ConvArgs a) {
                 // keep the prefetch at the top of the tap: the scheduler would
                 // otherwise sink it next to its use two taps later
                 __builtin_amdgcn_sched_barrier(0);
-                float Bv[4][NBW];
-                load_b(Bv, cur_buf, j);
-                // issue all of the tap's LDS reads before its MFMAs
+                if constexpr (BDB) {
+                    if (j + 1 < TAPS) load_b(Bb[(j + 1) & 1], cur_buf, j + 1);
+                } else {
+                    load_b(Bb[0], cur_buf, j);
+                }
+                // issue the LDS reads before the tap's MFMAs
                 __builtin_amdgcn_sched_barrier(0);
-                mfma_tap(use, Bv);
+                mfma_tap(use, Bb[BDB ? (j & 1) : 0]);
             }
             // the next item's taps 0 and 1 sit in slots TAPS % 3, (TAPS + 1) % 3
             if constexpr (TAPS % 3 == 1) {
