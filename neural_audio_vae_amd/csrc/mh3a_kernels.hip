@@ -251,9 +251,12 @@ __device__ __forceinline__ float round_bf16(float v) {
     return __uint_as_float(u);
 }
 
-// LDS floats of the conv kernel for window width W.
+// LDS floats of the conv kernel for window width W: the double-buffered
+// operand window, the activation staging (act only) and 64 floats per
+// producer wave that the epilogue line touches write into (never read).
+constexpr int kTouchFloats = 4 * 64;
 __host__ __device__ constexpr int conv_lds_floats(int W, bool act) {
-    return 2 * kChunk * W + (act ? kChunk * act_xs_len(W) + kChunk * act_ss_len(W) : 0);
+    return 2 * kChunk * W + (act ? kChunk * act_xs_len(W) + kChunk * act_ss_len(W) : 0) + kTouchFloats;
 }
 
 // Wave-specialized, persistent implicit-GEMM conv. 512 threads: waves 0-3
@@ -284,6 +287,7 @@ conv_kernel(ConvArgs a) {
     float* abuf = lds;                       // [2][CI][W]
     float* xs = lds + 2 * CI * W;            // [CI][act_xs_len(W)]   (act only)
     float* ss = xs + CI * act_xs_len(W);     // [CI][act_ss_len(W)]   (act only)
+    float* touch = lds + conv_lds_floats(W, ACT) - kTouchFloats;  // [4][64], write-only
     const int nch = (a.c_in + CI - 1) / CI;
     const int G = nch * a.taps;
     // With a K split the chunks are cut into ksplit equal ranges; each
@@ -484,6 +488,28 @@ conv_kernel(ConvArgs a) {
     // The pipeline walks items (tile, chunk) with chunk fastest. Producers
     // and consumers run separate loops with one barrier per item each, so
     // the compiler allocates registers for the larger role only.
+    // Epilogue line touches: when the producers stage the last K-chunk of a
+    // tile, one lane per 128-byte line of the tile's residual and running-sum
+    // rows loads it (into a write-only LDS scratch), so that the consumers'
+    // epilogue reads, one item later, hit L2 instead of waiting on HBM.
+    auto touch_epilogue = [&](const Tile& t) {
+        if (a.ksplit > 1 || a.out_mul != 1 || (!a.res && !a.sum_in)) return;
+        const int row0 = t.mt * MWG;
+        const int nrows = min(MWG, a.c_out - row0);
+        const int npos = min(NWG, a.positions - t.p0);
+        if (nrows <= 0 || npos <= 0) return;
+        const int lpr = ((npos + 31) >> 5) + 1;  // lines per row segment (+1: unaligned start)
+        const int64_t base = (int64_t)t.b * a.y_bstride + (int64_t)row0 * a.positions + t.p0 + a.out_add[t.ph];
+        auto* tl = (__attribute__((address_space(3))) void*)(touch + (wave - 4) * 64);
+        for (int i = tid - 256; i < nrows * lpr; i += 256) {
+            const int row = i / lpr;
+            const int off = min((i - row * lpr) * 32, npos - 1);
+            const int64_t idx = base + (int64_t)row * a.positions + off;
+            if (a.res) __builtin_amdgcn_global_load_lds((const void*)(a.res + idx), tl, 4, 0, 0);
+            if (a.sum_in) __builtin_amdgcn_global_load_lds((const void*)(a.sum_in + idx), tl, 4, 0, 0);
+        }
+    };
+
     if (producer) {
         if constexpr (PK) {
             // Packed input: the window of each channel parity is a contiguous
@@ -508,6 +534,7 @@ conv_kernel(ConvArgs a) {
             Tile nt = tile_at(t_begin);
             int nc = 0;
             dma(nt, 0, abuf);
+            if (nchs == 1) touch_epilogue(nt);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             for (int it = 0; it < n_items; ++it) {
@@ -517,6 +544,7 @@ conv_kernel(ConvArgs a) {
                         nt = tile_at(t_begin + (it + 1) / nchs);
                     }
                     dma(nt, nc, abuf + ((it + 1) & 1) * CI * W);
+                    if (nc == nchs - 1) touch_epilogue(nt);
                 }
                 // the copies land in LDS before the buffer is handed over
                 __builtin_amdgcn_s_waitcnt(0);
@@ -537,6 +565,7 @@ conv_kernel(ConvArgs a) {
             }
         };
         stage(cur, 0, abuf);
+        if (nchs == 1) touch_epilogue(cur);
         if (n_items > 1) {
             advance(la, la_c, 1);
             if (prefetchable) prefetch(la, la_c);
@@ -550,6 +579,7 @@ conv_kernel(ConvArgs a) {
                 const Tile t1 = la;
                 const int c1 = la_c;
                 stage(t1, c1, dst);
+                if (c1 == nchs - 1) touch_epilogue(t1);
                 if (it + 2 < n_items) {
                     advance(la, la_c, it + 2);
                     if (prefetchable) prefetch(la, la_c);
