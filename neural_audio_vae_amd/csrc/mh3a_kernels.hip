@@ -708,25 +708,68 @@ conv_kernel(ConvArgs a) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) pt[(mb * NBW + nb) * 1024 + r * 64] = acc[mb][nb][r];
             } else if (live) {
-                // Per-element epilogue (a batched variant measured no faster:
-                // its registers cost resident workgroups).
                 const int64_t ostride = (int64_t)a.out_mul * a.positions;
+                if constexpr (MBW * NBW > 4) {
+                    // Large tiles (one workgroup per CU, registers to spare):
+                    // by row group of 4 outputs per lane, the group's residual
+                    // and running-sum loads all go out before its adds and
+                    // stores. y may alias both (in-place updates), so the
+                    // compiler keeps every load behind the stores before it;
+                    // grouping is still exact, since no output is read after
+                    // another output has been written. Groups past c_out are
+                    // skipped.
+                    const int64_t ybase = (int64_t)cur.b * a.y_bstride;
 #pragma unroll
-                for (int mb = 0; mb < MBW; ++mb) {
+                    for (int mb = 0; mb < MBW; ++mb) {
+                        const int row0 = (mb_base + mb) * 32;
 #pragma unroll
-                    for (int nb = 0; nb < NBW; ++nb) {
-                        const int pos = cur.p0 + wn * NBW * 32 + nb * 32 + lo;
-                        if (pos >= a.positions) continue;
-                        const int tt = a.out_mul * pos + a.out_add[cur.ph];
+                        for (int nb = 0; nb < NBW; ++nb) {
+                            const int pos = cur.p0 + wn * NBW * 32 + nb * 32 + lo;
+                            const bool pos_ok = pos < a.positions;
+                            const int tt = a.out_mul * pos + a.out_add[cur.ph];
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int o = (mb_base + mb) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                            if (o >= a.c_out) continue;
-                            const int64_t idx = (int64_t)cur.b * a.y_bstride + (int64_t)o * ostride + tt;
-                            float v = acc[mb][nb][r];
-                            if (a.res) v += a.res[idx];
-                            if (a.sum_in) v += a.sum_in[idx];
-                            a.y[idx] = v * a.scale;
+                            for (int g = 0; g < 4; ++g) {
+                                if (row0 + 8 * g >= a.c_out) break;
+                                const int o0 = row0 + 8 * g + 4 * hi;
+                                float rv[4], sv[4];
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const bool ok = pos_ok && o0 + i < a.c_out;
+                                    const int64_t idx = ok ? ybase + (int64_t)(o0 + i) * ostride + tt : 0;
+                                    rv[i] = a.res ? a.res[idx] : 0.0f;
+                                    sv[i] = a.sum_in ? a.sum_in[idx] : 0.0f;
+                                }
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    if (!(pos_ok && o0 + i < a.c_out)) continue;
+                                    float v = acc[mb][nb][4 * g + i];
+                                    if (a.res) v += rv[i];
+                                    if (a.sum_in) v += sv[i];
+                                    a.y[ybase + (int64_t)(o0 + i) * ostride + tt] = v * a.scale;
+                                }
+                            }
+                        }
+                    }
+                } else {
+                    // Per element (smaller tiles: batching costs a resident
+                    // workgroup per CU, measured slower).
+#pragma unroll
+                    for (int mb = 0; mb < MBW; ++mb) {
+#pragma unroll
+                        for (int nb = 0; nb < NBW; ++nb) {
+                            const int pos = cur.p0 + wn * NBW * 32 + nb * 32 + lo;
+                            if (pos >= a.positions) continue;
+                            const int tt = a.out_mul * pos + a.out_add[cur.ph];
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int o = (mb_base + mb) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                                if (o >= a.c_out) continue;
+                                const int64_t idx = (int64_t)cur.b * a.y_bstride + (int64_t)o * ostride + tt;
+                                float v = acc[mb][nb][r];
+                                if (a.res) v += a.res[idx];
+                                if (a.sum_in) v += a.sum_in[idx];
+                                a.y[idx] = v * a.scale;
+                            }
                         }
                     }
                 }
