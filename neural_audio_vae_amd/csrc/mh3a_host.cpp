@@ -139,6 +139,7 @@ struct ConvLayer {
     int in_off[kMaxPhases] = {0};
     int out_add[kMaxPhases] = {0};
     int64_t w_off = -1;
+    int64_t w16_off = -1;  // 16-row tile packing (AMP convs of <= 16 output channels), or -1
     int64_t w_phase_stride = 0;
     int64_t b_off = -1;
     int act = -1;       // index into acts, -1 = none
@@ -349,7 +350,7 @@ ActParams act_params(const mh3a_decoder* d, int idx) {
 // fused: the layer's activation runs in the conv's operand staging (else the
 // conv reads an already activated input)
 ConvShape shape_of(const ConvLayer& L, bool fused) {
-    return {L.c_in, L.c_out, L.taps, L.dil, L.phases, fused && L.act >= 0, L.kind == KIND_AMP};
+    return {L.c_in, L.c_out, L.taps, L.dil, L.phases, fused && L.act >= 0, L.kind == KIND_AMP, L.w16_off >= 0};
 }
 
 int64_t plan_partial_floats(const ConvLayer& L, int positions, int groups, const ConvPlan& p, bool fused) {
@@ -451,6 +452,7 @@ hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, i
     a.c_in = L.c_in;
     a.l_in = l_in;
     a.w = d->blob + L.w_off;
+    a.w16 = L.w16_off >= 0 ? d->blob + L.w16_off : nullptr;
     a.w_phase_stride = L.w_phase_stride;
     a.bias = L.b_off >= 0 ? d->blob + L.b_off : nullptr;
     a.y = y;
@@ -740,6 +742,34 @@ void pack_conv_weights(const float* w, int c_out, int c_in, int taps, float* out
             }
 }
 
+int64_t packed_weight_floats16(int c_out, int c_in, int taps) {
+    const int64_t mb = (c_out + 15) / 16;
+    const int64_t g = (int64_t)((c_in + kChunk - 1) / kChunk) * taps;
+    return mb * g * 64 * 2;
+}
+
+// A-operand order of v_mfma_f32_16x16x4f32: for 16-row block mb, K-group
+// g = chunk * taps + tap, lane l and half s, the value is
+// W[mb*16 + l%16, chunk*8 + 4s + l/16, tap].
+void pack_conv_weights16(const float* w, int c_out, int c_in, int taps, float* out) {
+    const int nmb = (c_out + 15) / 16;
+    const int nch = (c_in + kChunk - 1) / kChunk;
+    const int64_t G = (int64_t)nch * taps;
+    for (int mb = 0; mb < nmb; ++mb)
+        for (int ch = 0; ch < nch; ++ch)
+            for (int j = 0; j < taps; ++j) {
+                const int64_t g = (int64_t)ch * taps + j;
+                for (int l = 0; l < 64; ++l)
+                    for (int h = 0; h < 2; ++h) {
+                        const int o = mb * 16 + (l & 15);
+                        const int i = ch * kChunk + 4 * h + (l >> 4);
+                        float v = 0.0f;
+                        if (o < c_out && i < c_in) v = w[((int64_t)o * c_in + i) * taps + j];
+                        out[(((int64_t)mb * G + g) * 64 + l) * 2 + h] = v;
+                    }
+            }
+}
+
 }  // namespace mh3a
 
 // ===========================================================================
@@ -902,6 +932,10 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
                     if ((rc = fetch_vector(t, cp + ".bias", C, &bias))) return rc;
                     ConvLayer L;
                     add_conv(blob, L, w, bias, C, C, kk);
+                    if (C <= 16 && (kk == 3 || kk == 7 || kk == 11)) {
+                        L.w16_off = blob.reserve(packed_weight_floats16(C, C, kk));
+                        pack_conv_weights16(w.data(), C, C, kk, blob.h.data() + L.w16_off);
+                    }
                     L.dil = which == 0 ? dil : 1;
                     L.alg_taps = kk;
                     L.kind = KIND_AMP;

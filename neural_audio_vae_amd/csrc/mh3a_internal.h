@@ -34,6 +34,7 @@ struct ConvArgs {
     int c_in;
     int l_in;
     const float* w;         // packed weights (see pack_conv_weights)
+    const float* w16;       // the same for 16-row tiles (see pack_conv_weights16), or null
     int64_t w_phase_stride; // floats between phases' packed weights
     const float* bias;      // [c_out] or null
     float* y;
@@ -87,7 +88,11 @@ enum TileId {
 #define MH3A_TILE(id, mbw, nbw, wm, wn) id,
     MH3A_TILE_LIST
 #undef MH3A_TILE
-    TILE_COUNT
+    TILE_COUNT,
+    // 16 x 256 on v_mfma_f32_16x16x4f32 (four waves of 16 x 64): AMP convs
+    // of at most 16 output channels, fp32, compile-time taps, no K split.
+    // Not part of the tile model's search.
+    TILE_16x256 = TILE_COUNT
 };
 // Tiles with instances specialized for 3, 7 and 11 taps (the shapes the AMP
 // convs use, with or without the fused activation); other shapes run those
@@ -104,6 +109,9 @@ TileShape tile_shape(TileId t);
 int64_t packed_weight_floats(int c_out, int c_in, int taps);
 // Pack w (c_out, c_in, taps), row-major, into the MFMA A-operand order.
 void pack_conv_weights(const float* w, int c_out, int c_in, int taps, float* out);
+// The same for 16-row tiles (v_mfma_f32_16x16x4f32 A-operand order).
+int64_t packed_weight_floats16(int c_out, int c_in, int taps);
+void pack_conv_weights16(const float* w, int c_out, int c_in, int taps, float* out);
 
 hipError_t launch_conv(const ConvArgs& a, TileId tile, hipStream_t stream);
 
@@ -112,6 +120,7 @@ struct ConvShape {
     int c_in, c_out, taps, dil, phases;
     bool act;  // activation fused into the operand staging
     bool amp;  // an AMP conv (tile table measured for them)
+    bool m16;  // weights packed for 16-row tiles too
 };
 // AMP activations of at least this many (batch x channel x position)
 // elements run as their own pass (see amp_act_fused in mh3a_host.cpp).

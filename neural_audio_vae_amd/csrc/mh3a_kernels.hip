@@ -268,17 +268,22 @@ __host__ __device__ constexpr int conv_lds_floats(int W, bool act) {
 // tile) into the other half of a double-buffered LDS window, so the
 // epilogue of one tile overlaps the staging of the next. One workgroup
 // barrier per item hands the buffers over.
-template <int MBW, int NBW, int WM, int WN, bool ACT, bool BF16, int TAPS>
+//
+// RB = 16 selects 16 x 16 blocks on v_mfma_f32_16x16x4f32 (MBW = WM = 1):
+// for AMP convs of at most 16 output channels a 32-row block would be half
+// or three quarters padding.
+template <int MBW, int NBW, int WM, int WN, bool ACT, bool BF16, int TAPS, int RB = 32>
 // (tiles of at most 2 x 2 blocks per wave keep two workgroups per CU: <= 128 VGPRs)
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MBW * NBW <= 4 ? 4 : 1)))
 conv_kernel(ConvArgs a) {
     static_assert(WM * WN == 4, "four consumer waves");
+    static_assert(RB == 32 || (RB == 16 && MBW == 1 && WM == 1 && TAPS > 0 && !BF16), "16-row tiles");
     constexpr int CI = kChunk;
     // AMP convs without the fused activation (compile-time taps) read the
     // packed activated input; other plain convs read rows.
     constexpr bool PK = !ACT && TAPS > 0;
-    constexpr int NWG = WN * NBW * 32;
-    constexpr int MWG = WM * MBW * 32;
+    constexpr int NWG = WN * NBW * RB;
+    constexpr int MWG = WM * MBW * RB;
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -591,6 +596,101 @@ conv_kernel(ConvArgs a) {
         return;
     }
 
+    if constexpr (RB == 16) {
+        // 16 x 16 x 4 roles: lane l is row / column l % 16 and K-step l / 16.
+        // K-step k of half s is channel 4s + k of the chunk, in LDS at
+        // [hi = k & 1][position][p = 2s + (k >> 1)]: one 16-byte read gives
+        // a lane both halves.
+        typedef float v4f __attribute__((ext_vector_type(4)));
+        const int l16 = lane & 15, k4 = lane >> 4;
+        const int kp = k4 >> 1, khi = k4 & 1;
+        const int colbase16 = wave * NBW * 16 + l16;  // (WM == 1: consumer wave = column)
+        const float2* w16 = reinterpret_cast<const float2*>(a.w16);
+        auto ld16 = [&](int mt, int g) { return w16[((int64_t)mt * G + g) * 64 + lane]; };
+        v4f acc16[NBW];
+        // accumulators start at the bias: bias column (K-step 0) x ones row
+        auto init16 = [&](int mt) {
+            const int m = mt * 16 + l16;
+            const float bz = (k4 == 0 && m < a.c_out) ? a.bias[m] : 0.0f;
+            const float one = k4 == 0 ? 1.0f : 0.0f;
+            const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) acc16[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bz, one, z, 0, 0, 0);
+        };
+        Tile cur = tile_at(t_begin);
+        int cur_c = 0;
+        init16(cur.mt);
+        // weights of taps j, j + 1, j + 2 in a three-slot ring (as the 32-row path)
+        float2 R0 = ld16(cur.mt, cur.c0 * TAPS), R1 = ld16(cur.mt, cur.c0 * TAPS + 1), R2;
+        __syncthreads();
+        for (int it = 0; it < n_items; ++it) {
+            const bool has_next = it + 1 < n_items;
+            Tile nxt = cur;
+            int nxt_c = cur_c + 1;
+            if (nxt_c == nchs) {
+                nxt_c = 0;
+                if (has_next) nxt = tile_at(t_begin + (it + 1) / nchs);
+            }
+            const float* cur_buf = abuf + (it & 1) * CI * W;
+            const int g0 = (cur.c0 + cur_c) * TAPS;
+            const int ng0 = has_next ? (nxt.c0 + nxt_c) * TAPS : g0;
+            const int nmt = has_next ? nxt.mt : cur.mt;
+#pragma unroll
+            for (int j = 0; j < TAPS; ++j) {
+                float2& use = (j % 3 == 0) ? R0 : ((j % 3 == 1) ? R1 : R2);
+                float2& fill = ((j + 2) % 3 == 0) ? R0 : (((j + 2) % 3 == 1) ? R1 : R2);
+                fill = (j + 2 < TAPS) ? ld16(cur.mt, g0 + j + 2) : ld16(nmt, ng0 + (j + 2 - TAPS));
+                __builtin_amdgcn_sched_barrier(0);
+                float4 bv[NBW];
+                const float* bp = cur_buf + (khi * W + colbase16 + j * a.dil) * 4;
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) bv[nb] = *reinterpret_cast<const float4*>(bp + nb * 64);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) {
+                    const float b0 = kp ? bv[nb].y : bv[nb].x;
+                    const float b1 = kp ? bv[nb].w : bv[nb].z;
+                    acc16[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(use.x, b0, acc16[nb], 0, 0, 0);
+                    acc16[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(use.y, b1, acc16[nb], 0, 0, 0);
+                }
+            }
+            // the next item's taps 0 and 1 sit in slots TAPS % 3, (TAPS + 1) % 3
+            if constexpr (TAPS % 3 == 1) {
+                R0 = R1;
+                R1 = R2;
+            } else if constexpr (TAPS % 3 == 2) {
+                const float2 t0 = R2;
+                R1 = R0;
+                R0 = t0;
+            }
+            if (cur_c == nchs - 1) {
+                // row 4 (l / 16) + i, column l % 16 of each 16 x 16 block
+                const int64_t ostride = (int64_t)a.out_mul * a.positions;
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) {
+                    const int pos = cur.p0 + colbase16 + nb * 16;
+                    if (pos >= a.positions) continue;
+                    const int tt = a.out_mul * pos + a.out_add[cur.ph];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int o = cur.mt * 16 + 4 * k4 + i;
+                        if (o >= a.c_out) continue;
+                        const int64_t idx = (int64_t)cur.b * a.y_bstride + (int64_t)o * ostride + tt;
+                        float v = acc16[nb][i];
+                        if (a.res) v += a.res[idx];
+                        if (a.sum_in) v += a.sum_in[idx];
+                        a.y[idx] = v * a.scale;
+                    }
+                }
+                init16(nmt);
+            }
+            cur = nxt;
+            cur_c = nxt_c;
+            __syncthreads();
+        }
+        return;
+    }
+
     Tile cur = tile_at(t_begin);
     int cur_c = 0;
     load_bias(__builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW), cur.c0);
@@ -821,6 +921,7 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(ConvArgs a, SplitGeom
 }
 
 TileShape tile_shape(TileId t) {
+    if (t == TILE_16x256) return {16, 256};
     switch (t) {
 #define MH3A_TILE(id, mbw, nbw, wm, wn) \
     case id: return {wm * mbw * 32, wn * nbw * 32};
@@ -899,10 +1000,33 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
                   : launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, false, 0>, a, tiles, lds, stream);
 }
 
+// 16 x 256 tiles: AMP convs (compile-time taps, fp32), fused activation or
+// packed input, no K split.
+static hipError_t launch_tile16(const ConvArgs& a, hipStream_t stream) {
+    constexpr int NWG = 256;
+    if (!a.w16 || a.bf16 || a.ksplit != 1 || a.phases != 1) return hipErrorInvalidValue;
+    const int W = NWG + (a.taps - 1) * a.dil;
+    const int64_t tiles = (int64_t)((a.positions + NWG - 1) / NWG) * ((a.c_out + 15) / 16) * a.groups;
+    const bool act = a.act.taps != nullptr;
+    if (!act && a.pk_lp <= 0) return hipErrorInvalidValue;
+    const size_t lds = sizeof(float) * (size_t)conv_lds_floats(W, act);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+#define MH3A_TAPS16(T)                                                                                            \
+    if (a.taps == T)                                                                                             \
+        return act ? launch_persistent(conv_kernel<1, 4, 1, 4, true, false, T, 16>, a, tiles, lds, stream)        \
+                   : launch_persistent(conv_kernel<1, 4, 1, 4, false, false, T, 16>, a, tiles, lds, stream);
+    MH3A_TAPS16(3)
+    MH3A_TAPS16(7)
+    MH3A_TAPS16(11)
+#undef MH3A_TAPS16
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_conv(const ConvArgs& a, TileId tile, hipStream_t stream) {
     // the kernel cuts the chunks into ksplit equal ranges
     const int nch = (a.c_in + kChunk - 1) / kChunk;
     if (a.ksplit < 1 || nch % a.ksplit != 0 || (a.ksplit > 1 && !a.partial)) return hipErrorInvalidValue;
+    if (tile == TILE_16x256) return launch_tile16(a, stream);
     hipError_t e = hipSuccess;
     switch (tile) {
 #define MH3A_TILE(id, mbw, nbw, wm, wn) \

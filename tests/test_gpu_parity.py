@@ -264,6 +264,19 @@ def test_stage0_packed_activation_path(default_decoder, default_params, dev):
         assert_close(f"stage 0 packed [{a},{b})", got[0][:, a:b], ref)
 
 
+@pytest.mark.parametrize("stage,channels", [(4, 32), (5, 16), (6, 8)])
+def test_narrow_stage_windows(default_decoder, default_params, dev, stage, channels):
+    # Stages of <= 16 channels run on 16-row tiles (v_mfma_f32_16x16x4f32),
+    # 32 channels on 32-row tiles; (2, C, 3000) with windows at both ends.
+    x = synth.make_signal((2, channels, 3000), seed=10 + stage)
+    got = host(default_decoder.amp_stage(stage, gpu(x, dev)))
+    margin = 120
+    for item, a, b in [(0, 0, 64), (1, 1400, 1464), (1, 2936, 3000)]:
+        lo, hi = max(0, a - margin), min(3000, b + margin)
+        ref = O.stage_amp(x[item][:, lo:hi], default_params, stage)[:, a - lo:b - lo]
+        assert_close(f"stage {stage} item {item} [{a},{b})", got[item][:, a:b], ref)
+
+
 def test_amp_stage_rejects_bad_arguments(default_decoder, dev):
     from neural_audio_vae_amd import MH3AError
     x = torch.zeros((1, 256, 50), device=dev)
