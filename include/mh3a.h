@@ -186,6 +186,38 @@ int mh3a_decode_partial(mh3a_decoder* dec, const float* latents, int64_t batch, 
                         float* out, void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
+ * Time-chunked decode with bounded memory. No page prints this schedule; it
+ * follows from the decoder being a stack of convolutions along time
+ * (diffusers "AutoencoderKLMiniMaxH3Audio" overview; FastVideo
+ * "minimax_h3_audio_vae" module overview: 1x1 projection, BigVGAN
+ * upsamplers and AMP blocks, final conv), so an output sample depends only
+ * on latents within a finite radius of it.
+ *
+ * mh3a_decode_margin reports that radius as a whole number of latents M
+ * (an upper bound summed over every layer's one-sided reach, plus one).
+ * mh3a_decode_chunked splits the N latents into chunks of chunk_frames
+ * (the last may be shorter); chunk [n0, n1) is decoded from the window
+ * [n0 - M, n1 + M) cut to [0, N) and samples [hop (n0 - w0), hop (n1 - w0))
+ * of the window's waveform are written to wave[:, :, hop n0 : hop n1].
+ * The result equals mh3a_decode's up to fp32 rounding order (each window
+ * plans its own launches); chunk_frames >= N is mh3a_decode itself.
+ *
+ * latents: device (B, latent_channels, N); wave: device (B, 1, hop N).
+ * workspace: device, 256-byte aligned, at least
+ * mh3a_decode_chunked_workspace_size bytes; that size grows with B and
+ * chunk_frames + 2 M, not with N (beyond N < chunk_frames + 2 M).
+ * Chunks run one after another on `stream`. Errors: MH3A_E_INVALID_ARG
+ * (null, chunk_frames < 1, batch or frames out of range, unknown flags),
+ * MH3A_E_WORKSPACE, MH3A_E_HIP.
+ */
+int mh3a_decode_margin(const mh3a_decoder* dec, int64_t* margin);
+int mh3a_decode_chunked_workspace_size(const mh3a_decoder* dec, int64_t batch, int64_t frames,
+                                       int64_t chunk_frames, uint32_t flags, size_t* bytes);
+int mh3a_decode_chunked(mh3a_decoder* dec, const float* latents, int64_t batch, int64_t frames,
+                        int64_t chunk_frames, float* wave, void* workspace, size_t workspace_bytes,
+                        uint32_t flags, void* stream);
+
+/*
  * One stage's AMP set alone (FastVideo "minimax_h3_audio_vae", decode: the
  * blocks of stage s run from the same input and are averaged): x device
  * (B, C_s, L) -> y device (B, C_s, L). Flags: MH3A_FLAG_BF16_MFMA and / or

@@ -40,6 +40,9 @@ EXPORTED = (
     "mh3a_decode",
     "mh3a_decode_layer_shape",
     "mh3a_decode_partial",
+    "mh3a_decode_margin",
+    "mh3a_decode_chunked_workspace_size",
+    "mh3a_decode_chunked",
     "mh3a_amp_stage_workspace_size",
     "mh3a_amp_stage",
     "mh3a_timing_enable",
@@ -113,6 +116,13 @@ def load():
     lib.mh3a_decode_partial.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_int, c_void_p, c_void_p, c_size_t,
                                         c_uint32, c_void_p]
     lib.mh3a_decode_partial.restype = c_int
+    lib.mh3a_decode_margin.argtypes = [c_void_p, POINTER(c_int64)]
+    lib.mh3a_decode_margin.restype = c_int
+    lib.mh3a_decode_chunked_workspace_size.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_uint32, POINTER(c_size_t)]
+    lib.mh3a_decode_chunked_workspace_size.restype = c_int
+    lib.mh3a_decode_chunked.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_size_t,
+                                        c_uint32, c_void_p]
+    lib.mh3a_decode_chunked.restype = c_int
     lib.mh3a_amp_stage_workspace_size.argtypes = [c_void_p, c_int, c_int64, c_int64, POINTER(c_size_t)]
     lib.mh3a_amp_stage_workspace_size.restype = c_int
     lib.mh3a_amp_stage.argtypes = [c_void_p, c_int, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_uint32,
@@ -245,6 +255,24 @@ def mh3a_decode_partial(handle, latents_ptr, batch, frames, upto, out_ptr, works
                                              workspace_bytes, flags, stream))
 
 
+def mh3a_decode_margin(handle):
+    m = c_int64()
+    _check(load().mh3a_decode_margin(handle, byref(m)))
+    return m.value
+
+
+def mh3a_decode_chunked_workspace_size(handle, batch, frames, chunk_frames, flags=0):
+    n = c_size_t()
+    _check(load().mh3a_decode_chunked_workspace_size(handle, batch, frames, chunk_frames, flags, byref(n)))
+    return n.value
+
+
+def mh3a_decode_chunked(handle, latents_ptr, batch, frames, chunk_frames, wave_ptr, workspace_ptr, workspace_bytes,
+                        flags, stream):
+    return _check(load().mh3a_decode_chunked(handle, latents_ptr, batch, frames, chunk_frames, wave_ptr,
+                                             workspace_ptr, workspace_bytes, flags, stream))
+
+
 def mh3a_amp_stage_workspace_size(handle, stage, batch, length):
     n = c_size_t()
     _check(load().mh3a_amp_stage_workspace_size(handle, stage, batch, length, byref(n)))
@@ -256,8 +284,9 @@ def mh3a_amp_stage(handle, stage, x_ptr, batch, length, y_ptr, workspace_ptr, wo
                                         flags, stream))
 
 
-def mh3a_timing_enable(handle, enable):
-    return _check(load().mh3a_timing_enable(handle, 1 if enable else 0))
+def mh3a_timing_enable(handle, mode):
+    # mode: MH3A_TIMING_* (True / False map to ALL / OFF)
+    return _check(load().mh3a_timing_enable(handle, int(mode)))
 
 
 def mh3a_timing_read(handle):

@@ -17,6 +17,7 @@
 #include <map>
 #include <memory>
 #include <mutex>
+#include <set>
 #include <string>
 #include <tuple>
 #include <vector>
@@ -710,6 +711,99 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
     return ok();
 }
 
+// Latents of context a decoded window needs on each side so that its
+// interior equals the full decode: an upper bound on how far one output
+// sample's dependence reaches, summed over the layers at the latent rate.
+// conv_pre (k = 7) reaches 3; a transposed conv of kernel k and stride r
+// reaches ceil(k / r) inputs; a "same" conv of kernel k and dilation d
+// reaches d (k - 1) / 2; an anti-aliased activation (2x up, SnakeBeta,
+// 2x down, both low-pass filters `filter_taps` long) reaches at most
+// filter_taps / 2 samples; the AMP blocks of a stage run side by side, so
+// the widest counts; act_post + conv_post (k = 7) close the chain.
+int64_t decode_margin(const mh3a_decoder* d) {
+    const mh3a_config& c = d->cfg;
+    const double act = c.filter_taps / 2;
+    double reach = 3.0, rate = 1.0;
+    for (int s = 0; s < c.num_ups; ++s) {
+        reach += (double)((c.kernels[s] + c.rates[s] - 1) / c.rates[s]) / rate;
+        rate *= c.rates[s];
+        double block = 0.0;
+        for (int j = 0; j < c.num_resblocks; ++j) {
+            const int k = c.rb_kernels[j];
+            double b = 0.0;
+            for (int i = 0; i < c.num_dilations; ++i)
+                b += c.rb_dilations[j][i] * (k - 1) / 2 + (k - 1) / 2 + 2 * act;
+            block = std::max(block, b);
+        }
+        reach += block / rate;
+    }
+    reach += (act + 3.0) / rate;
+    return (int64_t)std::ceil(reach) + 1;
+}
+
+// Chunk k of a chunked decode: output latents [n0, n1) decoded from the
+// window [w0, w1) = [n0 - margin, n1 + margin) cut to the sequence.
+struct Chunk {
+    int64_t n0, n1, w0, w1;
+};
+Chunk chunk_at(int64_t k, int64_t frames, int64_t cf, int64_t margin) {
+    Chunk ch;
+    ch.n0 = k * cf;
+    ch.n1 = std::min(frames, ch.n0 + cf);
+    ch.w0 = std::max<int64_t>(0, ch.n0 - margin);
+    ch.w1 = std::min(frames, ch.n1 + margin);
+    return ch;
+}
+
+// Distinct window lengths of a chunked decode. Chunks at least
+// edge = ceil(margin / cf) + 1 away from both ends have windows of exactly
+// cf + 2 margin latents, so one of them stands for all.
+std::set<int64_t> chunk_window_lengths(int64_t frames, int64_t cf, int64_t margin) {
+    std::set<int64_t> lens;
+    const int64_t K = (frames + cf - 1) / cf;
+    const int64_t edge = (margin + cf - 1) / cf + 1;
+    for (int64_t k = 0; k < K; ++k) {
+        const Chunk ch = chunk_at(k, frames, cf, margin);
+        lens.insert(ch.w1 - ch.w0);
+        if (k == edge && K - 1 - edge > k + 1) k = K - 2 - edge;
+    }
+    return lens;
+}
+
+int check_chunk_args(const mh3a_decoder* d, int64_t batch, int64_t frames, int64_t cf, uint32_t flags) {
+    if (!d) return fail(MH3A_E_INVALID_ARG, "decoder is null");
+    if (cf < 1) return fail(MH3A_E_INVALID_ARG, "chunk_frames must be >= 1");
+    if (batch < 1 || batch > 4096) return fail(MH3A_E_INVALID_ARG, "batch must be in [1, 4096]");
+    if (frames < 1 || frames > ((int64_t)1 << 40) / d->cfg.hop_length / batch)
+        return fail(MH3A_E_INVALID_ARG, "frames out of range");
+    if (flags & ~MH3A_FLAG_ALL) return fail(MH3A_E_INVALID_ARG, "unknown flags 0x%x", flags & ~MH3A_FLAG_ALL);
+    return MH3A_OK;
+}
+
+// Workspace of a chunked decode: the window decode's own workspace (largest
+// over the window lengths used), then the latent window and the wave
+// window. One chunk covering the sequence decodes in place: no windows.
+int chunked_ws_bytes(const mh3a_decoder* d, int64_t batch, int64_t frames, int64_t cf, uint32_t flags, size_t* bytes,
+                     size_t* dec_bytes, int64_t* wmax) {
+    *bytes = *dec_bytes = 0;
+    *wmax = 0;
+    int rc = check_chunk_args(d, batch, frames, cf, flags);
+    if (rc) return rc;
+    const int64_t margin = decode_margin(d);
+    for (int64_t wl : chunk_window_lengths(frames, cf, margin)) {
+        rc = check_decode_args(d, batch, wl, flags);
+        if (rc) return rc;
+        *dec_bytes = std::max(*dec_bytes, (size_t)round_up((int64_t)decode_ws_bytes(d, batch, wl, flags), 256));
+        *wmax = std::max(*wmax, wl);
+    }
+    *bytes = *dec_bytes;
+    if (cf < frames)
+        *bytes += (size_t)(round_up(batch * d->cfg.latent_channels * *wmax, 64) +
+                           round_up(batch * d->cfg.hop_length * *wmax, 64)) *
+                  sizeof(float);
+    return MH3A_OK;
+}
+
 }  // namespace
 
 namespace mh3a {
@@ -1087,6 +1181,57 @@ int mh3a_decode_partial(mh3a_decoder* d, const float* latents, int64_t batch, in
     if (upto < 0 || upto > 1 + 2 * d->cfg.num_ups) return fail(MH3A_E_INVALID_ARG, "layer index %d out of range", upto);
     return run_decode(d, latents, batch, frames, nullptr, upto, out, workspace, workspace_bytes, flags,
                       static_cast<hipStream_t>(stream));
+}
+
+int mh3a_decode_margin(const mh3a_decoder* d, int64_t* margin) {
+    if (!d || !margin) return fail(MH3A_E_INVALID_ARG, "null argument");
+    *margin = decode_margin(d);
+    return ok();
+}
+
+int mh3a_decode_chunked_workspace_size(const mh3a_decoder* d, int64_t batch, int64_t frames, int64_t chunk_frames,
+                                       uint32_t flags, size_t* bytes) {
+    if (!bytes) return fail(MH3A_E_INVALID_ARG, "bytes is null");
+    size_t dec_bytes = 0;
+    int64_t wmax = 0;
+    int rc = chunked_ws_bytes(d, batch, frames, chunk_frames, flags, bytes, &dec_bytes, &wmax);
+    if (rc) return rc;
+    return ok();
+}
+
+int mh3a_decode_chunked(mh3a_decoder* d, const float* latents, int64_t batch, int64_t frames, int64_t chunk_frames,
+                        float* wave, void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+    size_t need = 0, dec_bytes = 0;
+    int64_t wmax = 0;
+    int rc = chunked_ws_bytes(d, batch, frames, chunk_frames, flags, &need, &dec_bytes, &wmax);
+    if (rc) return rc;
+    if (!latents || !wave) return fail(MH3A_E_INVALID_ARG, "null latents or wave");
+    if (!workspace) return fail(MH3A_E_WORKSPACE, "workspace is null");
+    if ((uintptr_t)workspace % 256) return fail(MH3A_E_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need) return fail(MH3A_E_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (chunk_frames >= frames)
+        return run_decode(d, latents, batch, frames, wave, -1, nullptr, workspace, dec_bytes, flags, st);
+    HIP_TRY(hipSetDevice(d->device));
+    const int64_t lc = d->cfg.latent_channels, hop = d->cfg.hop_length;
+    const int64_t margin = decode_margin(d);
+    float* zwin = reinterpret_cast<float*>(static_cast<char*>(workspace) + dec_bytes);
+    float* ywin = zwin + round_up(batch * lc * wmax, 64);
+    const int64_t K = (frames + chunk_frames - 1) / chunk_frames;
+    for (int64_t k = 0; k < K; ++k) {
+        const Chunk ch = chunk_at(k, frames, chunk_frames, margin);
+        const int64_t wl = ch.w1 - ch.w0;
+        // latent window: rows of (batch * lc) channels, wl latents from w0
+        HIP_TRY(hipMemcpy2DAsync(zwin, wl * sizeof(float), latents + ch.w0, frames * sizeof(float), wl * sizeof(float),
+                                 batch * lc, hipMemcpyDeviceToDevice, st));
+        rc = run_decode(d, zwin, batch, wl, ywin, -1, nullptr, workspace, dec_bytes, flags, st);
+        if (rc) return rc;
+        // keep the samples of latents [n0, n1)
+        HIP_TRY(hipMemcpy2DAsync(wave + hop * ch.n0, hop * frames * sizeof(float), ywin + hop * (ch.n0 - ch.w0),
+                                 hop * wl * sizeof(float), hop * (ch.n1 - ch.n0) * sizeof(float), batch,
+                                 hipMemcpyDeviceToDevice, st));
+    }
+    return ok();
 }
 
 int mh3a_amp_stage_workspace_size(const mh3a_decoder* d, int stage, int64_t batch, int64_t length, size_t* bytes) {

@@ -97,6 +97,28 @@ class Decoder:
                                  st)
         return out
 
+    def margin(self):
+        """Latents of context each chunk of decode_chunked takes on either side."""
+        return _lib.mh3a_decode_margin(self._h)
+
+    def decode_chunked(self, latents, chunk_frames, flags=0, out=None, stream=None):
+        """decode() in time chunks of chunk_frames latents, each decoded from
+        a window widened by margin() latents per side and cropped; the
+        workspace depends on chunk_frames, not on the sequence length."""
+        torch = _torch()
+        z = self._check_input(latents, 3, "latents")
+        b, c, n = z.shape
+        if c != self.latent_channels:
+            raise ValueError(f"latents must have {self.latent_channels} channels")
+        if out is None:
+            out = torch.empty((b, 1, self.hop * n), dtype=torch.float32, device=z.device)
+        nbytes = _lib.mh3a_decode_chunked_workspace_size(self._h, b, n, chunk_frames, flags)
+        ws = self._workspace(nbytes)
+        st = (stream or torch.cuda.current_stream(z.device)).cuda_stream
+        _lib.mh3a_decode_chunked(self._h, z.data_ptr(), b, n, chunk_frames, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                 flags, st)
+        return out
+
     def amp_stage(self, stage, x, flags=0, out=None, stream=None):
         torch = _torch()
         x = self._check_input(x, 3, "x")

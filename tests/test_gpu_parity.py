@@ -355,3 +355,76 @@ def test_decode_argument_errors(default_decoder, dev):
     _lib.mh3a_decode(h, z.data_ptr(), 1, 4, out.data_ptr(), ws.data_ptr(), need, 0, st)
     torch.cuda.synchronize()
     print("[case] argument errors ok", file=sys.stderr)
+
+
+# ---------------------------------------------------------------------------
+# Time-chunked decode (bounded memory, overlap-and-crop)
+# ---------------------------------------------------------------------------
+
+def test_small_decoder_chunked_matches_oracle(small_decoder, small_params, dev):
+    # Every chunking of N = 90 latents, including one-latent chunks (each a
+    # window cut at both ends), a chunk that does not divide N and chunks
+    # at least N long, reproduces the oracle's full decode.
+    z = synth.make_latents(2, 90, seed=11, channels=4)
+    ref = O.decode(small_params, z, SMALL_CONFIG, clamp=False)
+    m = small_decoder.margin()
+    assert m >= math.ceil(O.receptive_radius_latents(SMALL_CONFIG)) + 1
+    for cf in (1, 7, 25, 89, 90, 200):
+        print(f"[case] small chunked N=90 chunk={cf} margin={m}", flush=True)
+        got = host(small_decoder.decode_chunked(gpu(z, dev), cf, flags=NO_CLAMP))
+        assert_close(f"small chunked chunk={cf}", got, ref, abs_=scaled_abs(ref))
+
+
+def test_chunked_decode_full_size(default_decoder, default_params, dev):
+    # (2, 32, 300) in chunks of 64 (last chunk 44 latents), dequantised
+    # latents: against the whole-sequence decode everywhere, and against the
+    # oracle on windows that straddle chunk boundaries.
+    z = synth.make_latents(2, 300, seed=4)
+    denorm = synth.make_denorm()
+    flags = DENORM | NO_CLAMP
+    print("[case] chunked full-size B=2 N=300 chunk=64", flush=True)
+    full = host(default_decoder.decode(gpu(z, dev), flags=flags))
+    got = host(default_decoder.decode_chunked(gpu(z, dev), 64, flags=flags))
+    assert_close("chunked vs whole decode", got, full)
+    windows = [(0, 62, 66), (1, 254, 258), (1, 296, 300)]
+    refs = oracle_windows(default_params, z, windows, denorm)
+    check_windows("chunked", got, refs, windows)
+    # chunks covering the sequence are the whole decode itself
+    one = host(default_decoder.decode_chunked(gpu(z, dev), 300, flags=flags))
+    np.testing.assert_array_equal(one, full)
+    clamped = host(default_decoder.decode_chunked(gpu(z, dev), 64, flags=DENORM))
+    assert np.all(np.abs(clamped) <= 1.0)
+
+
+def test_chunked_workspace_is_bounded(default_decoder, dev):
+    from neural_audio_vae_amd import _lib
+    h = default_decoder._h
+    m = default_decoder.margin()
+    a = _lib.mh3a_decode_chunked_workspace_size(h, 2, 1000, 64, 0)
+    b = _lib.mh3a_decode_chunked_workspace_size(h, 2, 100000, 64, 0)
+    assert a == b
+    assert a < _lib.mh3a_decode_workspace_size(h, 2, 1000, 0)
+    # a window never exceeds chunk + 2 margin latents
+    assert a >= _lib.mh3a_decode_workspace_size(h, 2, 64 + 2 * m, 0)
+
+
+def test_chunked_decode_argument_errors(default_decoder, dev):
+    from neural_audio_vae_amd import _lib
+    h = default_decoder._h
+    z = gpu(synth.make_latents(1, 100), dev)
+    out = torch.empty((1, 1, 80000), device=dev)
+    need = _lib.mh3a_decode_chunked_workspace_size(h, 1, 100, 16, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    with pytest.raises(_lib.MH3AError) as e:
+        _lib.mh3a_decode_chunked(h, z.data_ptr(), 1, 100, 0, out.data_ptr(), ws.data_ptr(), need, 0, st)
+    assert e.value.code == _lib.MH3A_E_INVALID_ARG
+    with pytest.raises(_lib.MH3AError) as e:
+        _lib.mh3a_decode_chunked(h, z.data_ptr(), 1, 100, 16, out.data_ptr(), ws.data_ptr(), need - 1, 0, st)
+    assert e.value.code == _lib.MH3A_E_WORKSPACE
+    with pytest.raises(_lib.MH3AError) as e:
+        _lib.mh3a_decode_chunked(h, z.data_ptr(), 1, 100, 16, out.data_ptr(), ws.data_ptr(), need, 0x80, st)
+    assert e.value.code == _lib.MH3A_E_INVALID_ARG
+    _lib.mh3a_decode_chunked(h, z.data_ptr(), 1, 100, 16, out.data_ptr(), ws.data_ptr(), need, 0, st)
+    torch.cuda.synchronize()
+    print("[case] chunked argument errors ok", file=sys.stderr)
