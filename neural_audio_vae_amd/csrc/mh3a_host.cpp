@@ -140,7 +140,7 @@ struct ConvLayer {
     int in_off[kMaxPhases] = {0};
     int out_add[kMaxPhases] = {0};
     int64_t w_off = -1;
-    int64_t w16_off = -1;  // 16-row tile packing (AMP convs of <= 16 output channels), or -1
+    int64_t w16_off = -1;  // 16-row MFMA packing (AMP convs of <= 32 channels), or -1
     int64_t w_phase_stride = 0;
     int64_t b_off = -1;
     int act = -1;       // index into acts, -1 = none
@@ -148,9 +148,9 @@ struct ConvLayer {
     int kind = 0;       // timing class
 };
 
-enum Kind { KIND_IN_PROJ = 0, KIND_CONV_PRE, KIND_UPSAMPLE, KIND_AMP, KIND_AMP_ACT, KIND_FINAL, KIND_COUNT };
+enum Kind { KIND_IN_PROJ = 0, KIND_CONV_PRE, KIND_UPSAMPLE, KIND_AMP, KIND_AMP_ACT, KIND_FINAL, KIND_AMP_UNIT, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"dec_in_proj", "conv_pre", "ups_transposed_conv", "amp_conv", "amp_act",
-                                            "act_post_conv_post"};
+                                            "act_post_conv_post", "amp_unit"};
 
 struct TimingRec {
     int kind;
@@ -351,7 +351,8 @@ ActParams act_params(const mh3a_decoder* d, int idx) {
 // fused: the layer's activation runs in the conv's operand staging (else the
 // conv reads an already activated input)
 ConvShape shape_of(const ConvLayer& L, bool fused) {
-    return {L.c_in, L.c_out, L.taps, L.dil, L.phases, fused && L.act >= 0, L.kind == KIND_AMP, L.w16_off >= 0};
+    return {L.c_in, L.c_out, L.taps, L.dil, L.phases, fused && L.act >= 0, L.kind == KIND_AMP,
+            L.w16_off >= 0 && L.c_out <= 16};
 }
 
 int64_t plan_partial_floats(const ConvLayer& L, int positions, int groups, const ConvPlan& p, bool fused) {
@@ -537,6 +538,64 @@ hipError_t run_act(const mh3a_decoder* d, int act_idx, const float* x, float* y,
 // result in s_buf. Blocks run from the same h and are averaged in the
 // epilogue of each block's last conv. Each conv's activation is fused into
 // its operand staging, or (large tensors) runs as its own pass into a_buf.
+// Whether stage s runs each residual unit as one launch (unit_kernel): fp32
+// operands, a channel count and every conv's taps and dilation that the
+// kernel has instances for. MH3A_AMP_UNIT=0 turns it off (a tuning aid).
+bool amp_unit_path(const mh3a_decoder* d, int stage, bool bf16) {
+    static const bool off = [] {
+        const char* e = std::getenv("MH3A_AMP_UNIT");
+        return e && !std::strcmp(e, "0");
+    }();
+    if (off || bf16) return false;
+    for (const ConvLayer& L : d->amp[stage])
+        if (L.w16_off < 0 || L.b_off < 0 || L.act < 0 || !unit_supported(L.c_out, L.taps, L.dil)) return false;
+    return true;
+}
+
+// The residual units of one AMP stage as unit_kernel launches. Unit n of a
+// block reads the block input h (n = 0) or the previous unit's output, and
+// writes x_buf / t_buf alternately (a unit reads its input around its own
+// outputs, so it cannot update in place); the block's last unit adds into
+// the running sum s_buf, scaled by 1 / blocks at the last block.
+int run_amp_units(const mh3a_decoder* d, int stage, const float* h, float* x_buf, float* t_buf, float* s_buf,
+                  int batch, int64_t len, hipStream_t st) {
+    const mh3a_config& c = d->cfg;
+    const int C = d->stage_c[stage];
+    const int nrb = c.num_resblocks, nd = c.num_dilations;
+    for (int j = 0; j < nrb; ++j) {
+        const float* xin = h;
+        for (int n = 0; n < nd; ++n) {
+            const ConvLayer& c1 = d->amp[stage][(j * nd + n) * 2 + 0];
+            const ConvLayer& c2 = d->amp[stage][(j * nd + n) * 2 + 1];
+            const bool last = (n == nd - 1);
+            UnitArgs u;
+            u.x = xin;
+            u.y = last ? s_buf : ((n & 1) ? t_buf : x_buf);
+            u.sum_in = (last && j > 0) ? s_buf : nullptr;
+            u.scale = (last && j == nrb - 1) ? 1.0f / (float)nrb : 1.0f;
+            u.bstride = (int64_t)C * len;
+            u.c = C;
+            u.l = (int)len;
+            u.taps = c1.taps;
+            u.dil = c1.dil;
+            u.w1 = d->blob + c1.w16_off;
+            u.b1 = d->blob + c1.b_off;
+            u.act1 = act_params(d, c1.act);
+            u.w2 = d->blob + c2.w16_off;
+            u.b2 = d->blob + c2.b_off;
+            u.act2 = act_params(d, c2.act);
+            if (c2.taps != c1.taps || c2.dil != 1) return fail(MH3A_E_INVALID_ARG, "unit convs disagree");
+            TimedLaunch tl(d, st, KIND_AMP_UNIT);
+            HIP_TRY(launch_unit(u, batch, st));
+            const double n_out = (double)batch * C * len;
+            tl.done(KIND_AMP_UNIT, 2.0 * 2.0 * C * (double)C * c1.alg_taps * n_out,
+                    4.0 * (n_out * (2 + (u.sum_in ? 1 : 0)) + 2.0 * C * C * c1.alg_taps + 2.0 * C));
+            xin = u.y;
+        }
+    }
+    return MH3A_OK;
+}
+
 int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, float* t_buf, float* s_buf, float* a_buf,
             int batch, int64_t len, bool bf16, bool invariant, float* partial, hipStream_t st) {
     const mh3a_config& c = d->cfg;
@@ -544,6 +603,7 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, floa
     const int64_t bs = (int64_t)C * len;
     const int nrb = c.num_resblocks, nd = c.num_dilations;
     const int L = (int)len;
+    if (amp_unit_path(d, stage, bf16)) return run_amp_units(d, stage, h, x_buf, t_buf, s_buf, batch, len, st);
     const bool fused = amp_act_fused(d, batch, C, len);
     const int64_t pbs = pk_item_floats(C, len);  // packed batch stride
     const int plp = fused ? 0 : (int)pk_lp(len);
@@ -591,6 +651,7 @@ int check_decode_args(const mh3a_decoder* d, int64_t batch, int64_t frames, uint
 // Largest partial-sum region any conv of one AMP stage needs.
 int64_t amp_partial_floats(const mh3a_decoder* d, int stage, int batch, int len, bool bf16, bool inv) {
     int64_t m = 0;
+    if (amp_unit_path(d, stage, bf16)) return 0;  // the unit kernel splits no contraction
     const bool fused = amp_act_fused(d, batch, d->stage_c[stage], len);
     for (const ConvLayer& L : d->amp[stage])
         m = std::max(m, plan_partial_floats(L, len, batch * L.phases, plan_conv(d, L, len, batch, bf16, inv, fused),
@@ -1026,7 +1087,7 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
                     if ((rc = fetch_vector(t, cp + ".bias", C, &bias))) return rc;
                     ConvLayer L;
                     add_conv(blob, L, w, bias, C, C, kk);
-                    if (C <= 16 && (kk == 3 || kk == 7 || kk == 11)) {
+                    if (C <= 32 && (kk == 3 || kk == 7 || kk == 11)) {
                         L.w16_off = blob.reserve(packed_weight_floats16(C, C, kk));
                         pack_conv_weights16(w.data(), C, C, kk, blob.h.data() + L.w16_off);
                     }

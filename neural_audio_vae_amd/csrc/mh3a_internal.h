@@ -152,6 +152,32 @@ struct ActArgs {
 };
 hipError_t launch_act(const ActArgs& a, int batch, hipStream_t stream);
 
+// One AMP residual unit in one launch, for narrow stages:
+//   y = scale * (x + conv2(act2(conv1(act1(x)))) + sum_in)
+// conv1 has k taps at dilation dil, conv2 k taps at dilation 1, both "same"
+// padded with bias; x, y and sum_in are (B, c, l) rows; y must not alias x
+// (workgroups read x around their own outputs); sum_in may alias y.
+// Weights in the 16-row MFMA order (pack_conv_weights16).
+struct UnitArgs {
+    const float* x;
+    float* y;
+    const float* sum_in;  // or null
+    float scale;
+    int64_t bstride;      // floats between batch items (c * l)
+    int c, l, taps, dil;
+    const float* w1;
+    const float* b1;
+    ActParams act1;
+    const float* w2;
+    const float* b2;
+    ActParams act2;
+};
+// Shapes the unit kernel has instances for: c in {8, 16, 32}, taps in
+// {3, 7, 11}, 1 <= dil <= kUnitMaxDil.
+constexpr int kUnitMaxDil = 5;
+bool unit_supported(int c, int taps, int dil);
+hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream);
+
 // activation_post + conv_post (c -> 1, 7 taps, pad 3) + optional clamp.
 struct FinalArgs {
     const float* x;

@@ -1137,6 +1137,260 @@ hipError_t launch_act(const ActArgs& a, int batch, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// One AMP residual unit per launch, for narrow stages (8 to 32 channels):
+//   y = scale * (x + conv2(act2(conv1(act1(x)))) + sum_in)
+// A workgroup of four waves owns T output positions [p0, p0 + T) of one
+// batch item and every channel, and keeps the unit's intermediates in LDS:
+//   x rows  over [x_lo, x_lo + act_xs_len(W1))   replicate-clamped loads
+//   act1 -> A1 over [a1_lo, a1_lo + W1)          zero outside [0, l): conv1's padding
+//   conv1 -> Y1 over [y1_lo, y1_lo + XS2)        into the x region; positions outside
+//                                                [0, l) then take the edge values
+//                                                (act2's replicate padding)
+//   act2 -> A2 over [a2_lo, a2_lo + W2)          into the A1 region
+//   conv2 + bias + x (+ sum_in), * scale -> y over [p0, p0 + T)
+// where a2_lo = p0 - R2 (R2 = (K - 1) / 2, conv2's reach), y1_lo = a2_lo - 6
+// (the origin act_from_xs expects of its input row), a1_lo = y1_lo - dil R2
+// (conv1's reach) and x_lo = a1_lo - 6. HBM sees x once (plus the residual
+// re-read, an L2 hit), y once and sum_in once, against three tensor reads
+// and two writes per conv when the convs run apart.
+//
+// Both convs run on v_mfma_f32_16x16x4f32: M = output channels in 16-row
+// blocks, N = positions in 16-column blocks, K = (input channel, tap) in the
+// order of pack_conv_weights16. Each wave keeps its row block's whole weight
+// set in registers and streams the operand from LDS rows: one 4-byte read
+// per lane gives 16 consecutive positions of 4 channels, with a row stride
+// of 16 mod 64 floats, so the 64 lanes hit 64 distinct banks.
+// ---------------------------------------------------------------------------
+template <int C, int K, int T>
+struct UnitGeom {
+    static constexpr int R2 = (K - 1) / 2;
+    static constexpr int W2 = T + 2 * R2;                      // act2 outputs (conv2 operand)
+    static constexpr int XS2 = act_xs_len(W2);                 // Y1 row = act2 input row
+    static constexpr int NY1 = (XS2 + 15) / 16 * 16;           // conv1 outputs computed
+    static constexpr int W1MAX = NY1 + 2 * kUnitMaxDil * R2;   // act1 outputs at the widest dilation
+    static constexpr int XS1MAX = act_xs_len(W1MAX);
+    static constexpr int SA = (W1MAX + 47) / 64 * 64 + 16;     // A row stride: >= W1MAX, 16 mod 64
+    static constexpr int XR = XS1MAX > XS2 ? XS1MAX : XS2;
+    static constexpr int LDS_X = C * XR;
+    static constexpr int LDS_A = C * SA;
+    static constexpr int LDS_S = kChunk * act_ss_len(W1MAX);
+    static constexpr int LDS_FLOATS = LDS_X + LDS_A + LDS_S;
+    static_assert(C % kChunk == 0 && C <= 32, "8, 16 or 32 channels");
+    static_assert(T % 16 == 0, "whole 16-column blocks");
+};
+
+// Work split of one unit conv over the four waves: MB row blocks, WPM waves
+// per row block, each wave taking every WPM-th column block in NBAT batches
+// of NBB blocks (accumulators in flight).
+template <int C, int NOUT>
+struct UnitConvSplit {
+    static constexpr int MB = (C + 15) / 16;
+    static constexpr int WPM = 4 / MB;
+    static constexpr int NBLK = NOUT / 16;
+    static constexpr int MYN = (NBLK + WPM - 1) / WPM;
+    static constexpr int NBAT = (MYN + 5) / 6;
+    static constexpr int NBB = (MYN + NBAT - 1) / NBAT;
+};
+
+// out[co][n] = bias[co] + sum_{ci, j} W[co][ci][j] A[ci][n + j dil] for n in
+// [0, NOUT); A rows at stride SA. pre(q, mb, nb) runs before a batch's
+// matrix-core work (for loads whose latency that work hides), epi(q, acc,
+// mb, nb) after it, for each real block of the batch.
+template <int C, int K, int SA, int NOUT, typename Pre, typename Epi>
+__device__ __forceinline__ void unit_conv(const float* __restrict__ A, const float* __restrict__ wp,
+                                          const float* __restrict__ bias, int dil, Pre pre, Epi epi) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    using S = UnitConvSplit<C, NOUT>;
+    constexpr int G = (C / kChunk) * K;  // float2 weight groups: (chunk of 8 channels, tap)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int mb = wave / S::WPM, ws = wave % S::WPM;
+    float2 wr[G];
+    const float2* wp2 = reinterpret_cast<const float2*>(wp) + (int64_t)mb * G * 64 + lane;
+#pragma unroll
+    for (int g = 0; g < G; ++g) wr[g] = wp2[g * 64];
+    float bv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int co = mb * 16 + 4 * (lane >> 4) + r;
+        bv[r] = co < C ? bias[co] : 0.0f;
+    }
+    const float* al = A + (lane >> 4) * SA + (lane & 15);
+    for (int bt = 0; bt < S::NBAT; ++bt) {
+        int nbq[S::NBB];
+        v4f acc[S::NBB];
+#pragma unroll
+        for (int q = 0; q < S::NBB; ++q) {
+            const int nb = ws + S::WPM * (bt * S::NBB + q);
+            nbq[q] = nb < S::NBLK ? nb : S::NBLK - 1;  // spare slots repeat the last block
+            if (nb < S::NBLK) pre(q, mb, nb);
+            acc[q] = v4f{bv[0], bv[1], bv[2], bv[3]};
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+#pragma unroll
+            for (int ch = 0; ch < C / kChunk; ++ch) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float wv = h ? wr[ch * K + j].y : wr[ch * K + j].x;
+#pragma unroll
+                    for (int q = 0; q < S::NBB; ++q) {
+                        const float b = al[(ch * kChunk + 4 * h) * SA + nbq[q] * 16 + j * dil];
+                        acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv, b, acc[q], 0, 0, 0);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < S::NBB; ++q) {
+            const int nb = ws + S::WPM * (bt * S::NBB + q);
+            if (nb < S::NBLK) epi(q, acc[q], mb, nb);
+        }
+    }
+}
+
+template <int C, int K, int T>
+__global__ void __launch_bounds__(256, 2) unit_kernel(UnitArgs a) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    using G = UnitGeom<C, K, T>;
+    using S2 = UnitConvSplit<C, T>;
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    float* xr = lds;               // x rows (stride act_xs_len(W1)), then Y1 rows (stride XS2)
+    float* ar = lds + G::LDS_X;    // A1 rows, then A2 rows (stride SA)
+    float* ss = ar + G::LDS_A;     // 2x-rate rows of the activation, one per channel in flight
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int ci = tid >> 5, lane32 = tid & 31;
+    const int b = blockIdx.y;
+    const int p0 = blockIdx.x * T;
+    const int L = a.l, dil = a.dil;
+    const float* xb = a.x + (int64_t)b * a.bstride;
+    const int a2_lo = p0 - G::R2, y1_lo = a2_lo - 6;
+    const int W1 = G::NY1 + 2 * dil * G::R2;
+    const int a1_lo = y1_lo - dil * G::R2, x_lo = a1_lo - 6;
+    const int XS1 = act_xs_len(W1);
+
+    const ActTaps f1 = load_act_taps(a.act1.taps);
+    // x rows, replicate-clamped; each batch of 8 rows has all its loads in
+    // flight before the stores
+    {
+        constexpr int NW = (G::XS1MAX + 255) / 256;
+#pragma unroll
+        for (int c0 = 0; c0 < C; c0 += 8) {
+            float v[8][NW];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int u = 0; u < NW; ++u)
+                    v[r][u] = xb[(c0 + r) * L + clampi(x_lo + tid + 256 * u, 0, L - 1)];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int u = 0; u < NW; ++u)
+                    if (tid + 256 * u < XS1) xr[(c0 + r) * XS1 + tid + 256 * u] = v[r][u];
+        }
+    }
+    __syncthreads();
+    // act1, 8 channels at a time (32 lanes per channel)
+#pragma unroll
+    for (int c0 = 0; c0 < C; c0 += kChunk) {
+        act_from_xs<kChunk>(ar + c0 * G::SA, xr + c0 * XS1, ss, c0, C, L, a1_lo, W1, f1, a.act1.ab[c0 + ci], ci,
+                            lane32, G::SA);
+        wave_lds_sync();  // this wave's 2x-rate rows are reused by its next channels
+    }
+    __syncthreads();
+    // conv1 -> Y1 rows
+    unit_conv<C, K, G::SA, G::NY1>(
+        ar, a.w1, a.b1, dil, [](int, int, int) {},
+        [&](int, v4f acc, int mb, int nb) {
+            const int n = nb * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = mb * 16 + 4 * (lane >> 4) + r;
+                if (co < C && n < G::XS2) xr[co * G::XS2 + n] = acc[r];
+            }
+        });
+    __syncthreads();
+    // Y1 past the sequence ends repeats its edge values
+    if (y1_lo < 0 || y1_lo + G::XS2 > L) {
+        const int i0 = -y1_lo, i1 = L - 1 - y1_lo;  // row indices of positions 0 and L - 1
+        for (int idx = tid; idx < C * G::XS2; idx += 256) {
+            const int co = idx / G::XS2, w = idx - co * G::XS2;
+            const int src = w < i0 ? i0 : (w > i1 ? i1 : -1);
+            if (src >= 0) xr[co * G::XS2 + w] = xr[co * G::XS2 + src];
+        }
+        __syncthreads();
+    }
+    // act2 -> A2 rows (A1 is dead)
+    {
+        const ActTaps f2 = load_act_taps(a.act2.taps);
+#pragma unroll
+        for (int c0 = 0; c0 < C; c0 += kChunk) {
+            act_from_xs<kChunk>(ar + c0 * G::SA, xr + c0 * G::XS2, ss, c0, C, L, a2_lo, G::W2, f2, a.act2.ab[c0 + ci],
+                                ci, lane32, G::SA);
+            wave_lds_sync();
+        }
+    }
+    __syncthreads();
+    // conv2 + residual (+ running sum), scaled, -> y; the residual and sum
+    // loads are issued before each batch's matrix-core work
+    float rs[S2::NBB][4];
+    const float* sb = a.sum_in ? a.sum_in + (int64_t)b * a.bstride : nullptr;
+    float* yb = a.y + (int64_t)b * a.bstride;
+    unit_conv<C, K, G::SA, T>(
+        ar, a.w2, a.b2, 1,
+        [&](int q, int mb, int nb) {
+            const int n = min(p0 + nb * 16 + (lane & 15), L - 1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = min(mb * 16 + 4 * (lane >> 4) + r, C - 1);
+                rs[q][r] = xb[co * L + n] + (sb ? sb[co * L + n] : 0.0f);
+            }
+        },
+        [&](int q, v4f acc, int mb, int nb) {
+            const int n = p0 + nb * 16 + (lane & 15);
+            if (n >= L) return;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = mb * 16 + 4 * (lane >> 4) + r;
+                if (co < C) yb[co * L + n] = (acc[r] + rs[q][r]) * a.scale;
+            }
+        });
+}
+
+bool unit_supported(int c, int taps, int dil) {
+    return (c == 8 || c == 16 || c == 32) && (taps == 3 || taps == 7 || taps == 11) && dil >= 1 &&
+           dil <= kUnitMaxDil;
+}
+
+template <int C, int K, int T>
+static hipError_t launch_unit_t(const UnitArgs& a, int batch, hipStream_t stream) {
+    constexpr size_t lds = sizeof(float) * UnitGeom<C, K, T>::LDS_FLOATS;
+    static_assert(2 * lds <= 160 * 1024, "two workgroups per compute unit");
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)unit_kernel<C, K, T>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    dim3 grid((a.l + T - 1) / T, batch);
+    hipLaunchKernelGGL((unit_kernel<C, K, T>), grid, dim3(256), lds, stream, a);
+    return hipGetLastError();
+}
+
+// Tile widths: 128 positions at 32 channels, 256 at 16, 512 at 8 (about
+// 60-80 KB of LDS each, two workgroups per compute unit).
+hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream) {
+    if (!unit_supported(a.c, a.taps, a.dil) || a.l < 1 || batch < 1 || batch > 65535 || !a.x || !a.y ||
+        a.x == a.y || !a.w1 || !a.w2 || !a.b1 || !a.b2 || !a.act1.taps || !a.act2.taps)
+        return hipErrorInvalidValue;
+#define MH3A_UNIT(C_, K_, T_) \
+    if (a.c == C_ && a.taps == K_) return launch_unit_t<C_, K_, T_>(a, batch, stream);
+    MH3A_UNIT(32, 3, 128) MH3A_UNIT(32, 7, 128) MH3A_UNIT(32, 11, 128)
+    MH3A_UNIT(16, 3, 256) MH3A_UNIT(16, 7, 256) MH3A_UNIT(16, 11, 256)
+    MH3A_UNIT(8, 3, 512) MH3A_UNIT(8, 7, 512) MH3A_UNIT(8, 11, 512)
+#undef MH3A_UNIT
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_final(const FinalArgs& a, int batch, hipStream_t stream) {
     dim3 grid((a.l + kFinalT - 1) / kFinalT, batch);
     hipLaunchKernelGGL(final_kernel, grid, dim3(256), 0, stream, a);
