@@ -141,6 +141,7 @@ struct ConvLayer {
     int out_add[kMaxPhases] = {0};
     int64_t w_off = -1;
     int64_t w16_off = -1;  // 16-row MFMA packing (AMP convs of <= 32 channels), or -1
+    int64_t w6_off = -1;   // bf16 pieces for split products (AMP convs), or -1
     int64_t w_phase_stride = 0;
     int64_t b_off = -1;
     int act = -1;       // index into acts, -1 = none
@@ -191,6 +192,7 @@ struct mh3a_decoder {
     std::vector<int> stage_c;   // output channels per stage
     int num_cus = 256;          // compute units of `device`
     bool pk_ok = false;         // every AMP conv can read a packed activated input
+    bool bx6_ok = false;        // ... and has split-product weights (see kPieces)
     mutable Timing timing;
     mutable std::mutex plan_mu;                          // guards plans
     mutable std::map<PlanKey, std::pair<int, int>> plans;  // (tile, ksplit) per launch shape
@@ -445,10 +447,12 @@ struct TimedLaunch {
 hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, int64_t x_bstride, int l_in,
                     int positions, float* y, int64_t y_bstride, int batch, const float* res, const float* sum_in,
                     float scale, bool bf16, bool invariant, bool fused, float* partial, hipStream_t st,
-                    int pk_lp = 0) {
+                    int pk_lp = 0, bool bx6 = false) {
     ConvArgs a;
     std::memset(&a, 0, sizeof a);
     a.pk_lp = pk_lp;
+    a.bx6 = bx6 ? 1 : 0;
+    a.w6 = L.w6_off >= 0 ? d->blob + L.w6_off : nullptr;
     a.x = x;
     a.x_bstride = x_bstride;
     a.c_in = L.c_in;
@@ -511,20 +515,37 @@ int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 // Packed activated input of one (C, L) item (see kPkPadL): row length and
 // floats per item.
 int64_t pk_lp(int64_t len) { return len + kPkPadL + kPkPadR; }
-int64_t pk_item_floats(int c, int64_t len) { return (int64_t)((c + kChunk - 1) / kChunk) * kChunk * pk_lp(len); }
+
+// Whether packed AMP inputs take the split-product form (bf16 pieces and
+// six-way products on bf16 matrix cores, fp32-level accuracy; see kPieces).
+// MH3A_BX6=0 selects the fp32 matrix-core form (a tuning aid).
+bool use_bx6(const mh3a_decoder* d) {
+    static const bool off = [] {
+        const char* e = std::getenv("MH3A_BX6");
+        return e && !std::strcmp(e, "0");
+    }();
+    return d->bx6_ok && !off;
+}
+// Floats per item of a packed input: per chunk of 8 channels, two fp32
+// planes or kPieces bf16 planes of lp 16-byte groups.
+int64_t pk_item_floats(const mh3a_decoder* d, int c, int64_t len) {
+    const int planes = use_bx6(d) ? kPieces : 2;
+    return (int64_t)((c + kChunk - 1) / kChunk) * planes * 4 * pk_lp(len);
+}
 
 // The standalone activation of AMP layer `act_idx`: y = act(x), x (B, C, L)
 // rows, y packed.
 hipError_t run_act(const mh3a_decoder* d, int act_idx, const float* x, float* y, int batch, int c, int64_t len,
-                   hipStream_t st) {
+                   bool pieces, hipStream_t st) {
     ActArgs a;
     a.x = x;
     a.x_bstride = (int64_t)c * len;
     a.y = y;
-    a.y_bstride = pk_item_floats(c, len);
+    a.y_bstride = pk_item_floats(d, c, len);
     a.c = c;
     a.l = (int)len;
     a.lp = (int)pk_lp(len);
+    a.pieces = pieces ? kPieces : 0;
     a.act = act_params(d, act_idx);
     TimedLaunch tl(d, st, KIND_AMP_ACT);
     hipError_t e = launch_act(a, batch, st);
@@ -605,8 +626,9 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, floa
     const int L = (int)len;
     if (amp_unit_path(d, stage, bf16)) return run_amp_units(d, stage, h, x_buf, t_buf, s_buf, batch, len, st);
     const bool fused = amp_act_fused(d, batch, C, len);
-    const int64_t pbs = pk_item_floats(C, len);  // packed batch stride
+    const int64_t pbs = pk_item_floats(d, C, len);  // packed batch stride
     const int plp = fused ? 0 : (int)pk_lp(len);
+    const bool px = !fused && !bf16 && use_bx6(d);  // packed inputs in the split-product form
     for (int j = 0; j < nrb; ++j) {
         for (int n = 0; n < nd; ++n) {
             const ConvLayer& c1 = d->amp[stage][(j * nd + n) * 2 + 0];
@@ -614,14 +636,14 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, floa
             const float* xin = (n == 0) ? h : x_buf;
             const float* in1 = xin;
             if (!fused) {
-                HIP_TRY(run_act(d, c1.act, xin, a_buf, batch, C, len, st));
+                HIP_TRY(run_act(d, c1.act, xin, a_buf, batch, C, len, px, st));
                 in1 = a_buf;
             }
             HIP_TRY(run_conv(d, c1, in1, fused ? bs : pbs, L, L, t_buf, bs, batch, nullptr, nullptr, 1.0f, bf16,
-                             invariant, fused, partial, st, plp));
+                             invariant, fused, partial, st, plp, px));
             const float* in2 = t_buf;
             if (!fused) {
-                HIP_TRY(run_act(d, c2.act, t_buf, a_buf, batch, C, len, st));
+                HIP_TRY(run_act(d, c2.act, t_buf, a_buf, batch, C, len, px, st));
                 in2 = a_buf;
             }
             const bool last = (n == nd - 1);
@@ -629,7 +651,7 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, floa
             const float* sum_in = (last && j > 0) ? s_buf : nullptr;
             const float scale = (last && j == nrb - 1) ? 1.0f / (float)nrb : 1.0f;
             HIP_TRY(run_conv(d, c2, in2, fused ? bs : pbs, L, L, yout, bs, batch, xin, sum_in, scale, bf16, invariant,
-                             fused, partial, st, plp));
+                             fused, partial, st, plp, px));
         }
     }
     return MH3A_OK;
@@ -682,7 +704,7 @@ int64_t decode_partial_floats(const mh3a_decoder* d, int batch, int frames, bool
 // activation).
 int64_t stage_pk_floats(const mh3a_decoder* d, int stage, int64_t batch, int64_t len) {
     if (amp_act_fused(d, batch, d->stage_c[stage], len)) return 0;
-    return round_up(batch * pk_item_floats(d->stage_c[stage], len), 64);
+    return round_up(batch * pk_item_floats(d, d->stage_c[stage], len), 64);
 }
 
 int64_t decode_pk_floats(const mh3a_decoder* d, int64_t batch, int64_t frames) {
@@ -925,6 +947,55 @@ void pack_conv_weights16(const float* w, int c_out, int c_in, int taps, float* o
             }
 }
 
+// Split-product weights for v_mfma_f32_32x32x16_bf16: for 32-row block mb,
+// chunk ch, tap pair q, piece p and lane l, the 8 bf16 values
+// piece_p(W[mb*32 + l%32, ch*8 + i, 2q + l/32]), i = 0..7 (zero past c_out,
+// c_in or the last tap), at 16-byte group ((mb * nch + ch) * npairs + q) *
+// kPieces + p) * 64 + l. Pieces: v0 = bf16(v), v1 = bf16(v - v0),
+// v2 = bf16(v - v0 - v1), rounded to nearest even.
+int64_t packed_weight_floats6(int c_out, int c_in, int taps) {
+    const int64_t nmb = (c_out + 31) / 32, nch = (c_in + kChunk - 1) / kChunk, np = (taps + 1) / 2;
+    return nmb * nch * np * kPieces * 64 * 4;
+}
+
+static uint32_t bf16_rne_bits(float v) {
+    uint32_t u;
+    std::memcpy(&u, &v, 4);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+static float bf16_bits_value(uint32_t b) {
+    const uint32_t u = b << 16;
+    float v;
+    std::memcpy(&v, &u, 4);
+    return v;
+}
+
+void pack_conv_weights6(const float* w, int c_out, int c_in, int taps, float* out) {
+    const int nmb = (c_out + 31) / 32, nch = (c_in + kChunk - 1) / kChunk, np = (taps + 1) / 2;
+    uint32_t* o = reinterpret_cast<uint32_t*>(out);
+    for (int mb = 0; mb < nmb; ++mb)
+        for (int ch = 0; ch < nch; ++ch)
+            for (int q = 0; q < np; ++q)
+                for (int l = 0; l < 64; ++l) {
+                    uint16_t pc[kPieces][kChunk];
+                    for (int i = 0; i < kChunk; ++i) {
+                        const int m = mb * 32 + (l & 31), c = ch * kChunk + i, j = 2 * q + (l >> 5);
+                        const float v = (m < c_out && c < c_in && j < taps) ? w[((int64_t)m * c_in + c) * taps + j] : 0.0f;
+                        const uint32_t p0 = bf16_rne_bits(v);
+                        const float r1 = v - bf16_bits_value(p0);
+                        const uint32_t p1 = bf16_rne_bits(r1);
+                        const uint32_t p2 = bf16_rne_bits(r1 - bf16_bits_value(p1));
+                        pc[0][i] = (uint16_t)p0;
+                        pc[1][i] = (uint16_t)p1;
+                        pc[2][i] = (uint16_t)p2;
+                    }
+                    for (int p = 0; p < kPieces; ++p) {
+                        uint32_t* g = o + ((((int64_t)mb * nch + ch) * np + q) * kPieces + p) * 256 + l * 4;
+                        for (int k = 0; k < 4; ++k) g[k] = (uint32_t)pc[p][2 * k] | ((uint32_t)pc[p][2 * k + 1] << 16);
+                    }
+                }
+}
+
 }  // namespace mh3a
 
 // ===========================================================================
@@ -1087,6 +1158,10 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
                     if ((rc = fetch_vector(t, cp + ".bias", C, &bias))) return rc;
                     ConvLayer L;
                     add_conv(blob, L, w, bias, C, C, kk);
+                    if (kk == 3 || kk == 7 || kk == 11) {
+                        L.w6_off = blob.reserve(packed_weight_floats6(C, C, kk));
+                        pack_conv_weights6(w.data(), C, C, kk, blob.h.data() + L.w6_off);
+                    }
                     if (C <= 32 && (kk == 3 || kk == 7 || kk == 11)) {
                         L.w16_off = blob.reserve(packed_weight_floats16(C, C, kk));
                         pack_conv_weights16(w.data(), C, C, kk, blob.h.data() + L.w16_off);
@@ -1125,6 +1200,10 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
             if (!taps_ok || L.phases != 1 || pad > kPkPadL || 255 + (L.taps - 1) * L.dil - pad > kPkPadR)
                 d->pk_ok = false;
         }
+    d->bx6_ok = d->pk_ok;
+    for (const auto& stage_layers : d->amp)
+        for (const ConvLayer& L : stage_layers)
+            if (L.w6_off < 0 || L.dil > kBx6MaxDil) d->bx6_ok = false;
 
     // upload
     int ndev = 0;

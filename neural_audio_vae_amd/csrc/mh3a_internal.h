@@ -35,6 +35,7 @@ struct ConvArgs {
     int l_in;
     const float* w;         // packed weights (see pack_conv_weights)
     const float* w16;       // the same for 16-row tiles (see pack_conv_weights16), or null
+    const float* w6;        // bf16 pieces for split products (see pack_conv_weights6), or null
     int64_t w_phase_stride; // floats between phases' packed weights
     const float* bias;      // [c_out] or null
     float* y;
@@ -56,6 +57,7 @@ struct ConvArgs {
     int ksplit;           // K ranges (divides the chunk count); > 1 uses `partial`
     float* partial;       // ksplit * tiles * tile_m * tile_n floats of raw sums
     int pk_lp;            // packed input (see below): padded row length; 0 = plain rows
+    int bx6;              // packed input holds bf16 pieces; products split six ways (see below)
 };
 
 // Packed activated input of an AMP conv, written by the standalone
@@ -68,6 +70,18 @@ struct ConvArgs {
 // the last output tile: pad <= kPkPadL and tile_n - 1 + (k - 1) d - pad <= kPkPadR.
 constexpr int kPkPadL = 32;
 constexpr int kPkPadR = 288;
+
+// Split-product ("bx6") form of the packed input: every value v is split
+// into bf16 pieces v0 = bf16(v), v1 = bf16(v - v0), v2 = bf16(v - v0 - v1)
+// (round to nearest even), so v0 + v1 + v2 equals v to about 2^-27 relative.
+// Per batch item: [chunk][piece][lp][8 bf16 of the chunk's channels], the
+// same padding as above. A conv then sums the six piece products of order
+// <= 2 (w0 x0, w0 x1, w1 x0, w0 x2, w1 x1, w2 x0) on bf16 matrix cores with
+// fp32 accumulation, which keeps fp32-level accuracy (the dropped products
+// are about 2^-27 of w x).
+constexpr int kPieces = 3;
+// Largest dilation the split-product conv has LDS planes for.
+constexpr int kBx6MaxDil = 5;
 
 // Tile shapes of the conv kernel: four consumer waves arranged WM x WN,
 // each computing MBW x NBW blocks of 32 x 32 outputs.
@@ -112,6 +126,9 @@ void pack_conv_weights(const float* w, int c_out, int c_in, int taps, float* out
 // The same for 16-row tiles (v_mfma_f32_16x16x4f32 A-operand order).
 int64_t packed_weight_floats16(int c_out, int c_in, int taps);
 void pack_conv_weights16(const float* w, int c_out, int c_in, int taps, float* out);
+// The same as bf16 pieces for v_mfma_f32_32x32x16_bf16 (see pack_conv_weights6).
+int64_t packed_weight_floats6(int c_out, int c_in, int taps);
+void pack_conv_weights6(const float* w, int c_out, int c_in, int taps, float* out);
 
 hipError_t launch_conv(const ConvArgs& a, TileId tile, hipStream_t stream);
 
@@ -148,6 +165,7 @@ struct ActArgs {
     int c;
     int l;
     int lp;
+    int pieces;         // 0: fp32 packed layout; kPieces: bf16 pieces (split-product form)
     ActParams act;
 };
 hipError_t launch_act(const ActArgs& a, int batch, hipStream_t stream);

@@ -251,12 +251,34 @@ __device__ __forceinline__ float round_bf16(float v) {
     return __uint_as_float(u);
 }
 
+// Upper 16 bits of v rounded to nearest even: bf16(v) as raw bits.
+__device__ __forceinline__ unsigned bf16_bits(float v) {
+    const unsigned u = __float_as_uint(v);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+// The three bf16 pieces of v (raw bits): v0 = bf16(v), v1 = bf16(v - v0),
+// v2 = bf16(v - v0 - v1); both differences are exact in fp32.
+__device__ __forceinline__ void split3_bf16(float v, unsigned& p0, unsigned& p1, unsigned& p2) {
+    p0 = bf16_bits(v);
+    const float r1 = v - __uint_as_float(p0 << 16);
+    p1 = bf16_bits(r1);
+    const float r2 = r1 - __uint_as_float(p1 << 16);
+    p2 = bf16_bits(r2);
+}
+
 // LDS floats of the conv kernel for window width W: the double-buffered
 // operand window, the activation staging (act only) and 64 floats per
 // producer wave that the epilogue line touches write into (never read).
 constexpr int kTouchFloats = 4 * 64;
 __host__ __device__ constexpr int conv_lds_floats(int W, bool act) {
     return 2 * kChunk * W + (act ? kChunk * act_xs_len(W) + kChunk * act_ss_len(W) : 0) + kTouchFloats;
+}
+// Split-product convs: per item kPieces planes of PS positions (16 bytes
+// each), PS sized for the largest dilation so that plane offsets are
+// compile-time constants.
+__host__ __device__ constexpr int bx6_plane(int nwg, int taps) { return nwg + (taps - 1) * kBx6MaxDil; }
+__host__ __device__ constexpr int conv_lds_floats6(int nwg, int taps) {
+    return 2 * kPieces * bx6_plane(nwg, taps) * 4 + kTouchFloats;
 }
 
 // Wave-specialized, persistent implicit-GEMM conv. 512 threads: waves 0-3
@@ -272,27 +294,37 @@ __host__ __device__ constexpr int conv_lds_floats(int W, bool act) {
 // RB = 16 selects 16 x 16 blocks on v_mfma_f32_16x16x4f32 (MBW = WM = 1):
 // for AMP convs of at most 16 output channels a 32-row block would be half
 // or three quarters padding.
-template <int MBW, int NBW, int WM, int WN, bool ACT, bool BF16, int TAPS, int RB = 32>
-// (tiles of at most 2 x 2 blocks per wave keep two workgroups per CU: <= 128 VGPRs)
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MBW * NBW <= 4 ? 4 : 1)))
+//
+// PREC selects the products: 0 fp32 matrix cores; 1 the bf16 operand
+// variant (three-term split on fp32 matrix cores); 2 split products on bf16
+// matrix cores (packed input in the split-product form, see kPieces).
+template <int MBW, int NBW, int WM, int WN, bool ACT, int PREC, int TAPS, int RB = 32>
+// (fp32 tiles of at most 2 x 2 blocks per wave keep two workgroups per CU: <= 128 VGPRs)
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((MBW * NBW <= 4 && PREC != 2) ? 4 : 1)))
 conv_kernel(ConvArgs a) {
+    constexpr bool BF16 = PREC == 1;
+    constexpr bool BX6 = PREC == 2;
     static_assert(WM * WN == 4, "four consumer waves");
     static_assert(RB == 32 || (RB == 16 && MBW == 1 && WM == 1 && TAPS > 0 && !BF16), "16-row tiles");
     constexpr int CI = kChunk;
     // AMP convs without the fused activation (compile-time taps) read the
     // packed activated input; other plain convs read rows.
     constexpr bool PK = !ACT && TAPS > 0;
+    static_assert(!BX6 || (PK && RB == 32), "split products read the packed input");
     constexpr int NWG = WN * NBW * RB;
     constexpr int MWG = WM * MBW * RB;
+    constexpr int PS6 = bx6_plane(NWG, TAPS > 0 ? TAPS : 1);  // split-product plane stride (positions)
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const bool producer = wave >= 4;
     const int W = NWG + (a.taps - 1) * a.dil;
-    float* abuf = lds;                       // [2][CI][W]
+    // one item's operand window: [CI][W] floats, or kPieces planes of PS6 16-byte groups
+    const int ABUF = BX6 ? kPieces * PS6 * 4 : CI * W;
+    float* abuf = lds;                       // [2][ABUF]
     float* xs = lds + 2 * CI * W;            // [CI][act_xs_len(W)]   (act only)
     float* ss = xs + CI * act_xs_len(W);     // [CI][act_ss_len(W)]   (act only)
-    float* touch = lds + conv_lds_floats(W, ACT) - kTouchFloats;  // [4][64], write-only
+    float* touch = lds + (BX6 ? 2 * ABUF : conv_lds_floats(W, ACT) - kTouchFloats);  // [4][64], write-only
     const int nch = (a.c_in + CI - 1) / CI;
     const int G = nch * a.taps;
     // With a K split the chunks are cut into ksplit equal ranges; each
@@ -490,6 +522,41 @@ conv_kernel(ConvArgs a) {
     };
     float4 An[MBW];
 
+    // Split products (PREC 2): v_mfma_f32_32x32x16_bf16 with K = 16 = two
+    // taps x the chunk's 8 channels. Lane l holds, for piece p, the A values
+    // W[m = l % 32][chunk channel i][tap 2q + l / 32] and the B values of the
+    // chunk's 8 channels at position n + (2q + l / 32) dil: one 16-byte read
+    // per piece and block. An odd tap count pads the last pair with zero
+    // weights (its upper half reads tap 2q again, so no read leaves the
+    // window). Weights ride a two-slot ring one pair ahead.
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+    constexpr int NP6 = (TAPS + 1) / 2;
+    static_assert(!BX6 || NP6 % 2 == 0, "the ring's slot 0 holds each item's first pair");
+    const int G6 = nch * NP6;
+    v4u A6a[BX6 ? kPieces : 1][MBW], A6b[BX6 ? kPieces : 1][MBW];
+    auto load_a6 = [&](v4u (&dst)[BX6 ? kPieces : 1][MBW], int mb_base, int g) {
+        const v4u* wp = reinterpret_cast<const v4u*>(a.w6) + (int64_t)g * kPieces * 64 + lane;
+#pragma unroll
+        for (int p = 0; p < (BX6 ? kPieces : 1); ++p)
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb)
+                dst[p][mb] = wp[((int64_t)min(mb_base + mb, mb_tot - 1) * G6 * kPieces + p) * 64];
+    };
+    // the six products of order <= 2: (A piece, B piece)
+    auto mfma6 = [&](const v4u (&A)[BX6 ? kPieces : 1][MBW], const v4u (&B)[BX6 ? kPieces : 1][NBW]) {
+        constexpr int TA[6] = {0, 0, 1, 0, 1, 2}, TB[6] = {0, 1, 0, 2, 1, 0};
+#pragma unroll
+        for (int t = 0; t < 6; ++t)
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(v8bf, A[BX6 ? TA[t] : 0][mb]), __builtin_bit_cast(v8bf, B[BX6 ? TB[t] : 0][nb]),
+                        acc[mb][nb], 0, 0, 0);
+    };
+
     // The pipeline walks items (tile, chunk) with chunk fastest. Producers
     // and consumers run separate loops with one barrier per item each, so
     // the compiler allocates registers for the larger role only.
@@ -521,16 +588,19 @@ conv_kernel(ConvArgs a) {
             // run of W 16-byte groups, already in the operand layout; the
             // memory unit copies it to LDS 1 KB per wave instruction, so the
             // producers issue no vector ALU work next to the matrix cores.
+            // (split products: kPieces planes per chunk instead of two parities)
+            constexpr int NPL = BX6 ? kPieces : 2;
+            const int DS = BX6 ? PS6 : W;    // LDS plane stride (positions)
             const int pw = wave - 4;
-            const int segs = (W + 63) >> 6;  // 64-position segments per parity
+            const int segs = (W + 63) >> 6;  // 64-position segments per plane
             auto dma = [&](const Tile& t, int c, float* dst) {
                 const float* src =
-                    a.x + (int64_t)t.b * a.x_bstride + ((int64_t)(t.c0 + c) * 2 * a.pk_lp + kPkPadL + t.n_lo) * 4;
-                for (int q = pw; q < 2 * segs; q += 4) {
-                    const int hp = q >= segs ? 1 : 0;
+                    a.x + (int64_t)t.b * a.x_bstride + ((int64_t)(t.c0 + c) * NPL * a.pk_lp + kPkPadL + t.n_lo) * 4;
+                for (int q = pw; q < NPL * segs; q += 4) {
+                    const int hp = q / segs;
                     const int pos0 = (q - hp * segs) * 64;
                     const int pos = pos0 + lane;
-                    auto* ldst = (__attribute__((address_space(3))) void*)(dst + (hp * W + pos0) * 4);
+                    auto* ldst = (__attribute__((address_space(3))) void*)(dst + (hp * DS + pos0) * 4);
                     if (pos < W)
                         __builtin_amdgcn_global_load_lds((const void*)(src + ((int64_t)hp * a.pk_lp + pos) * 4), ldst, 16,
                                                          0, 0);
@@ -548,7 +618,7 @@ conv_kernel(ConvArgs a) {
                         nc = 0;
                         nt = tile_at(t_begin + (it + 1) / nchs);
                     }
-                    dma(nt, nc, abuf + ((it + 1) & 1) * CI * W);
+                    dma(nt, nc, abuf + ((it + 1) & 1) * ABUF);
                     if (nc == nchs - 1) touch_epilogue(nt);
                 }
                 // the copies land in LDS before the buffer is handed over
@@ -580,7 +650,7 @@ conv_kernel(ConvArgs a) {
         for (int it = 0; it < n_items; ++it) {
             if (it + 1 < n_items) {
                 // la is item it + 1: commit its row, start fetching it + 2, compute it + 1
-                float* dst = abuf + ((it + 1) & 1) * CI * W;
+                float* dst = abuf + ((it + 1) & 1) * ABUF;
                 const Tile t1 = la;
                 const int c1 = la_c;
                 stage(t1, c1, dst);
@@ -631,7 +701,7 @@ conv_kernel(ConvArgs a) {
                 nxt_c = 0;
                 if (has_next) nxt = tile_at(t_begin + (it + 1) / nchs);
             }
-            const float* cur_buf = abuf + (it & 1) * CI * W;
+            const float* cur_buf = abuf + (it & 1) * ABUF;
             const int g0 = (cur.c0 + cur_c) * TAPS;
             const int ng0 = has_next ? (nxt.c0 + nxt_c) * TAPS : g0;
             const int nmt = has_next ? nxt.mt : cur.mt;
@@ -696,7 +766,9 @@ conv_kernel(ConvArgs a) {
     load_bias(__builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW), cur.c0);
     init_acc();
     float4 Ar0[MBW], Ar1[MBW], Ar2[MBW];
-    if constexpr (TAPS > 0) {
+    if constexpr (BX6) {
+        load_a6(A6a, __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW), cur.c0 * NP6);
+    } else if constexpr (TAPS > 0) {
         const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
         load_a_nb(Ar0, mb0, cur.ph, cur.c0 * a.taps);
         load_a_nb(Ar1, mb0, cur.ph, cur.c0 * a.taps + 1);
@@ -720,9 +792,37 @@ conv_kernel(ConvArgs a) {
         if (nxt_c == 0 && has_next)
             load_bias(__builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW), nxt.c0);
         const bool live = mb_base < mb_tot;
-        const float* cur_buf = abuf + (it & 1) * CI * W;
+        const float* cur_buf = abuf + (it & 1) * ABUF;
         const int g0 = (cur.c0 + cur_c) * a.taps;
-        if constexpr (TAPS > 0) {
+        if constexpr (BX6) {
+            const int nmb_base = __builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW);
+            const int q0 = (cur.c0 + cur_c) * NP6;
+            const int nq0 = has_next ? (nxt.c0 + nxt_c) * NP6 : q0;
+            const int nmb = has_next ? nmb_base : mb_base;
+            const float* bb_h = cur_buf + (colbase + hi * a.dil) * 4;  // this lane's tap of each pair
+            const float* bb_0 = cur_buf + colbase * 4;                 // the pair's first tap
+#pragma unroll
+            for (int q = 0; q < NP6; ++q) {
+                v4u(&use)[kPieces][MBW] = (q & 1) ? A6b : A6a;
+                v4u(&fill)[kPieces][MBW] = (q & 1) ? A6a : A6b;
+                if (q + 1 < NP6) {
+                    load_a6(fill, mb_base, q0 + q + 1);
+                } else {
+                    load_a6(fill, nmb, nq0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const bool pad = (TAPS & 1) && q == NP6 - 1;
+                const float* bq = (pad ? bb_0 : bb_h) + 2 * q * a.dil * 4;
+                v4u Bv[kPieces][NBW];
+#pragma unroll
+                for (int p = 0; p < kPieces; ++p)
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb)
+                        Bv[p][nb] = *reinterpret_cast<const v4u*>(bq + (p * PS6 + nb * 32) * 4);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma6(use, Bv);
+            }
+        } else if constexpr (TAPS > 0) {
             // Compile-time tap count: the tap loop is fully unrolled and
             // branch-free. The weights ride a three-slot register ring loaded
             // two taps ahead (one tap of MFMAs does not cover the L2
@@ -968,26 +1068,40 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
     const int64_t tiles =
         (int64_t)((a.positions + NWG - 1) / NWG) * ((a.c_out + MWG - 1) / MWG) * a.groups * a.ksplit;
     const bool act = a.act.taps != nullptr;
+    if (a.bx6 && (act || a.pk_lp <= 0)) return hipErrorInvalidValue;
     const size_t lds = sizeof(float) * (size_t)conv_lds_floats(W, act);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     // instances with the AMP tap counts compiled in (3, 7, 11)
 #define MH3A_TAPS(ACTV, T)                                                                                          \
     if (a.taps == T)                                                                                               \
-        return a.bf16 ? launch_persistent(conv_kernel<MBW, NBW, WM, WN, ACTV, true, T>, a, tiles, lds, stream)     \
-                      : launch_persistent(conv_kernel<MBW, NBW, WM, WN, ACTV, false, T>, a, tiles, lds, stream);
+        return a.bf16 ? launch_persistent(conv_kernel<MBW, NBW, WM, WN, ACTV, 1, T>, a, tiles, lds, stream)        \
+                      : launch_persistent(conv_kernel<MBW, NBW, WM, WN, ACTV, 0, T>, a, tiles, lds, stream);
     if (act) {
         if constexpr (TAPS_TILE) {
             MH3A_TAPS(true, 3)
             MH3A_TAPS(true, 7)
             MH3A_TAPS(true, 11)
         }
-        return a.bf16 ? launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, true, 0>, a, tiles, lds, stream)
-                      : launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, false, 0>, a, tiles, lds, stream);
+        return a.bf16 ? launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, 1, 0>, a, tiles, lds, stream)
+                      : launch_persistent(conv_kernel<MBW, NBW, WM, WN, true, 0, 0>, a, tiles, lds, stream);
     }
     if (a.pk_lp > 0) {
         // packed input: compile-time taps only
         if constexpr (TAPS_TILE) {
             if (NWG > 256) return hipErrorInvalidValue;
+            if (a.bx6) {
+                // split products: bf16 pieces, one phase, planes sized for kBx6MaxDil
+                if (a.bf16 || !a.w6 || a.phases != 1 || a.dil > kBx6MaxDil) return hipErrorInvalidValue;
+#define MH3A_TAPS6(T)                                                                                           \
+    if (a.taps == T)                                                                                           \
+        return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 2, T>, a, tiles,                         \
+                                 sizeof(float) * (size_t)conv_lds_floats6(NWG, T), stream);
+                MH3A_TAPS6(3)
+                MH3A_TAPS6(7)
+                MH3A_TAPS6(11)
+#undef MH3A_TAPS6
+                return hipErrorInvalidValue;
+            }
             MH3A_TAPS(false, 3)
             MH3A_TAPS(false, 7)
             MH3A_TAPS(false, 11)
@@ -996,15 +1110,15 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
     }
 #undef MH3A_TAPS
     // (in_proj, conv_pre and the upsamplers: fp32 operands, runtime taps)
-    return a.bf16 ? hipErrorInvalidValue
-                  : launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, false, 0>, a, tiles, lds, stream);
+    return (a.bf16 || a.bx6) ? hipErrorInvalidValue
+                             : launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 0, 0>, a, tiles, lds, stream);
 }
 
 // 16 x 256 tiles: AMP convs (compile-time taps, fp32), fused activation or
 // packed input, no K split.
 static hipError_t launch_tile16(const ConvArgs& a, hipStream_t stream) {
     constexpr int NWG = 256;
-    if (!a.w16 || a.bf16 || a.ksplit != 1 || a.phases != 1) return hipErrorInvalidValue;
+    if (!a.w16 || a.bf16 || a.bx6 || a.ksplit != 1 || a.phases != 1) return hipErrorInvalidValue;
     const int W = NWG + (a.taps - 1) * a.dil;
     const int64_t tiles = (int64_t)((a.positions + NWG - 1) / NWG) * ((a.c_out + 15) / 16) * a.groups;
     const bool act = a.act.taps != nullptr;
@@ -1013,8 +1127,8 @@ static hipError_t launch_tile16(const ConvArgs& a, hipStream_t stream) {
     if (lds > 160 * 1024) return hipErrorInvalidValue;
 #define MH3A_TAPS16(T)                                                                                            \
     if (a.taps == T)                                                                                             \
-        return act ? launch_persistent(conv_kernel<1, 4, 1, 4, true, false, T, 16>, a, tiles, lds, stream)        \
-                   : launch_persistent(conv_kernel<1, 4, 1, 4, false, false, T, 16>, a, tiles, lds, stream);
+        return act ? launch_persistent(conv_kernel<1, 4, 1, 4, true, 0, T, 16>, a, tiles, lds, stream)            \
+                   : launch_persistent(conv_kernel<1, 4, 1, 4, false, 0, T, 16>, a, tiles, lds, stream);
     MH3A_TAPS16(3)
     MH3A_TAPS16(7)
     MH3A_TAPS16(11)
@@ -1094,7 +1208,7 @@ __global__ void __launch_bounds__(256) final_kernel(FinalArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kActT = 256;
 
-template <int W>
+template <int W, bool PIECES>
 __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
     constexpr int CI = kChunk;
     // each channel's result row reuses its x row (dead after the up pass)
@@ -1106,10 +1220,11 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
     const int chunk = blockIdx.y;
     const int b = blockIdx.z;
     const int ci = threadIdx.x >> 5, lane32 = threadIdx.x & 31;
-    float* yc = a.y + (int64_t)b * a.y_bstride + (int64_t)chunk * 2 * a.lp * 4;
+    constexpr int NPL = PIECES ? kPieces : 2;  // planes per chunk: pieces, or channel parities
+    float* yc = a.y + (int64_t)b * a.y_bstride + (int64_t)chunk * NPL * a.lp * 4;
     if (t0 >= a.l || t0 + W <= 0) {
         // all padding
-        for (int idx = threadIdx.x; idx < 2 * W; idx += 256) {
+        for (int idx = threadIdx.x; idx < NPL * W; idx += 256) {
             const int hi = idx / W, w = idx - hi * W;
             const int q = t0 + kPkPadL + w;
             if (q < a.lp) *reinterpret_cast<float4*>(yc + ((int64_t)hi * a.lp + q) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1120,6 +1235,26 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
     constexpr int XS = act_xs_len(W);
     stage_act<CI, W>(as, xs, ss, a.x + (int64_t)b * a.x_bstride, chunk * CI, a.c, a.l, t0, f, a.act.ab, ci, lane32, XS);
     __syncthreads();
+    if constexpr (PIECES) {
+        // one position per thread: the 8 channels' pieces, 16 bytes per plane
+        for (int w = threadIdx.x; w < W; w += 256) {
+            const int q = t0 + kPkPadL + w;
+            if (q >= a.lp) continue;
+            unsigned pc[kPieces][CI];
+#pragma unroll
+            for (int c = 0; c < CI; ++c) split3_bf16(as[c * XS + w], pc[0][c], pc[1][c], pc[2][c]);
+#pragma unroll
+            for (int p = 0; p < kPieces; ++p) {
+                uint4 v;
+                v.x = pc[p][0] | (pc[p][1] << 16);
+                v.y = pc[p][2] | (pc[p][3] << 16);
+                v.z = pc[p][4] | (pc[p][5] << 16);
+                v.w = pc[p][6] | (pc[p][7] << 16);
+                *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = v;
+            }
+        }
+        return;
+    }
     for (int idx = threadIdx.x; idx < 2 * W; idx += 256) {
         const int hi = idx / W, w = idx - hi * W;
         const int q = t0 + kPkPadL + w;  // index in the padded row
@@ -1133,7 +1268,11 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
 hipError_t launch_act(const ActArgs& a, int batch, hipStream_t stream) {
     if (a.c < 1 || a.l < 1 || batch < 1 || !a.act.taps || a.lp != a.l + kPkPadL + kPkPadR) return hipErrorInvalidValue;
     dim3 grid((a.lp + kActT - 1) / kActT, (a.c + kChunk - 1) / kChunk, batch);
-    hipLaunchKernelGGL(act_kernel<kActT>, grid, dim3(256), 0, stream, a);
+    if (a.pieces != 0 && a.pieces != kPieces) return hipErrorInvalidValue;
+    if (a.pieces)
+        hipLaunchKernelGGL((act_kernel<kActT, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((act_kernel<kActT, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
