@@ -528,13 +528,12 @@ conv_kernel(ConvArgs a) {
     // chunk's 8 channels at position n + (2q + l / 32) dil: one 16-byte read
     // per piece and block. An odd tap count pads the last pair with zero
     // weights (its upper half reads tap 2q again, so no read leaves the
-    // window). Weights ride a two-slot ring one pair ahead.
+    // window). Weights ride a three-slot ring two pairs ahead.
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
     constexpr int NP6 = (TAPS + 1) / 2;
-    static_assert(!BX6 || NP6 % 2 == 0, "the ring's slot 0 holds each item's first pair");
     const int G6 = nch * NP6;
-    v4u A6a[BX6 ? kPieces : 1][MBW], A6b[BX6 ? kPieces : 1][MBW];
+    v4u A6a[BX6 ? kPieces : 1][MBW], A6b[BX6 ? kPieces : 1][MBW], A6c[BX6 ? kPieces : 1][MBW];
     auto load_a6 = [&](v4u (&dst)[BX6 ? kPieces : 1][MBW], int mb_base, int g) {
         const v4u* wp = reinterpret_cast<const v4u*>(a.w6) + (int64_t)g * kPieces * 64 + lane;
 #pragma unroll
@@ -767,7 +766,9 @@ conv_kernel(ConvArgs a) {
     init_acc();
     float4 Ar0[MBW], Ar1[MBW], Ar2[MBW];
     if constexpr (BX6) {
-        load_a6(A6a, __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW), cur.c0 * NP6);
+        const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
+        load_a6(A6a, mb0, cur.c0 * NP6);
+        load_a6(A6b, mb0, cur.c0 * NP6 + 1);
     } else if constexpr (TAPS > 0) {
         const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
         load_a_nb(Ar0, mb0, cur.ph, cur.c0 * a.taps);
@@ -801,14 +802,16 @@ conv_kernel(ConvArgs a) {
             const int nmb = has_next ? nmb_base : mb_base;
             const float* bb_h = cur_buf + (colbase + hi * a.dil) * 4;  // this lane's tap of each pair
             const float* bb_0 = cur_buf + colbase * 4;                 // the pair's first tap
+            // slots 0 and 1 hold pairs 0 and 1 on entry; pair q + 2 (or the next
+            // item's pair q + 2 - NP6) loads while pair q multiplies
 #pragma unroll
             for (int q = 0; q < NP6; ++q) {
-                v4u(&use)[kPieces][MBW] = (q & 1) ? A6b : A6a;
-                v4u(&fill)[kPieces][MBW] = (q & 1) ? A6a : A6b;
-                if (q + 1 < NP6) {
-                    load_a6(fill, mb_base, q0 + q + 1);
+                v4u(&use)[kPieces][MBW] = (q % 3 == 0) ? A6a : ((q % 3 == 1) ? A6b : A6c);
+                v4u(&fill)[kPieces][MBW] = ((q + 2) % 3 == 0) ? A6a : (((q + 2) % 3 == 1) ? A6b : A6c);
+                if (q + 2 < NP6) {
+                    load_a6(fill, mb_base, q0 + q + 2);
                 } else {
-                    load_a6(fill, nmb, nq0);
+                    load_a6(fill, nmb, nq0 + (q + 2 - NP6));
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 const bool pad = (TAPS & 1) && q == NP6 - 1;
@@ -821,6 +824,25 @@ conv_kernel(ConvArgs a) {
                         Bv[p][nb] = *reinterpret_cast<const v4u*>(bq + (p * PS6 + nb * 32) * 4);
                 __builtin_amdgcn_sched_barrier(0);
                 mfma6(use, Bv);
+            }
+            // the next item's pairs 0 and 1 sit in slots NP6 % 3, (NP6 + 1) % 3
+            if constexpr (NP6 % 3 == 1) {
+#pragma unroll
+                for (int p = 0; p < kPieces; ++p)
+#pragma unroll
+                    for (int mb = 0; mb < MBW; ++mb) {
+                        A6a[p][mb] = A6b[p][mb];
+                        A6b[p][mb] = A6c[p][mb];
+                    }
+            } else if constexpr (NP6 % 3 == 2) {
+#pragma unroll
+                for (int p = 0; p < kPieces; ++p)
+#pragma unroll
+                    for (int mb = 0; mb < MBW; ++mb) {
+                        const v4u t0 = A6c[p][mb];
+                        A6b[p][mb] = A6a[p][mb];
+                        A6a[p][mb] = t0;
+                    }
             }
         } else if constexpr (TAPS > 0) {
             // Compile-time tap count: the tap loop is fully unrolled and
