@@ -352,13 +352,24 @@ ActParams act_params(const mh3a_decoder* d, int idx) {
 
 // fused: the layer's activation runs in the conv's operand staging (else the
 // conv reads an already activated input)
-ConvShape shape_of(const ConvLayer& L, bool fused) {
+ConvShape shape_of(const ConvLayer& L, bool fused, bool bx6 = false) {
     return {L.c_in, L.c_out, L.taps, L.dil, L.phases, fused && L.act >= 0, L.kind == KIND_AMP,
-            L.w16_off >= 0 && L.c_out <= 16};
+            L.w16_off >= 0 && L.c_out <= 16, bx6};
 }
 
 int64_t plan_partial_floats(const ConvLayer& L, int positions, int groups, const ConvPlan& p, bool fused) {
     return mh3a::plan_partial_floats(shape_of(L, fused), positions, groups, p);
+}
+
+// Whether packed AMP inputs take the split-product form (bf16 pieces and
+// six-way products on bf16 matrix cores, fp32-level accuracy; see kPieces).
+// MH3A_BX6=0 selects the fp32 matrix-core form (a tuning aid).
+bool use_bx6(const mh3a_decoder* d) {
+    static const bool off = [] {
+        const char* e = std::getenv("MH3A_BX6");
+        return e && !std::strcmp(e, "0");
+    }();
+    return d->bx6_ok && !off;
 }
 
 // Whether an AMP conv of a (batch, C, L) activation fuses its activation.
@@ -382,17 +393,21 @@ bool amp_act_fused(const mh3a_decoder* d, int64_t batch, int64_t c, int64_t len)
         return 0;
     }();
     if (mode) return mode == 1;
-    return c < 128 || batch * c * len < kSeparateActMin;
+    // split-product convs gain enough from matrix-core speed to pay for the
+    // separate pass from 64 channels on
+    return c < (use_bx6(d) ? 64 : 128) || batch * c * len < kSeparateActMin;
 }
 
 // Plans are cached per launch shape.
 ConvPlan plan_conv(const mh3a_decoder* d, const ConvLayer& L, int positions, int batch, bool bf16, bool invariant,
                    bool fused) {
-    const PlanKey key{&L, positions, batch, (bf16 ? 1 : 0) | (invariant ? 2 : 0) | (fused ? 4 : 0)};
+    // packed AMP inputs in the split-product form (see run_amp)
+    const bool bx6 = !fused && !bf16 && L.kind == KIND_AMP && L.act >= 0 && use_bx6(d);
+    const PlanKey key{&L, positions, batch, (bf16 ? 1 : 0) | (invariant ? 2 : 0) | (fused ? 4 : 0) | (bx6 ? 8 : 0)};
     std::lock_guard<std::mutex> lock(d->plan_mu);
     auto it = d->plans.find(key);
     if (it != d->plans.end()) return {(TileId)it->second.first, it->second.second};
-    const ConvPlan p = mh3a::plan_conv(shape_of(L, fused), positions, batch, bf16, invariant, d->num_cus);
+    const ConvPlan p = mh3a::plan_conv(shape_of(L, fused, bx6), positions, batch, bf16, invariant, d->num_cus);
     // MH3A_PLAN_LOG=1 prints each new plan to stderr (a tuning aid)
     static const bool log = [] {
         const char* e = std::getenv("MH3A_PLAN_LOG");
@@ -516,16 +531,6 @@ int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 // floats per item.
 int64_t pk_lp(int64_t len) { return len + kPkPadL + kPkPadR; }
 
-// Whether packed AMP inputs take the split-product form (bf16 pieces and
-// six-way products on bf16 matrix cores, fp32-level accuracy; see kPieces).
-// MH3A_BX6=0 selects the fp32 matrix-core form (a tuning aid).
-bool use_bx6(const mh3a_decoder* d) {
-    static const bool off = [] {
-        const char* e = std::getenv("MH3A_BX6");
-        return e && !std::strcmp(e, "0");
-    }();
-    return d->bx6_ok && !off;
-}
 // Floats per item of a packed input: per chunk of 8 channels, two fp32
 // planes or kPieces bf16 planes of lp 16-byte groups.
 int64_t pk_item_floats(const mh3a_decoder* d, int c, int64_t len) {

@@ -97,7 +97,11 @@ constexpr int kBx6MaxDil = 5;
     MH3A_TILE(TILE_64x512, 2, 4, 1, 4)   /*  64 x 512 */           \
     MH3A_TILE(TILE_64x256, 2, 2, 1, 4)   /*  64 x 256 */           \
     MH3A_TILE(TILE_32x512, 1, 4, 1, 4)   /*  32 x 512 */           \
-    MH3A_TILE(TILE_32x256, 1, 2, 1, 4)   /*  32 x 256 */
+    MH3A_TILE(TILE_32x256, 1, 2, 1, 4)   /*  32 x 256 */           \
+    MH3A_TILE(TILE_128x128R, 1, 4, 4, 1) /* 128 x 128, waves of 32 x 128 */ \
+    MH3A_TILE(TILE_64x256R, 1, 4, 2, 2)  /*  64 x 256, waves of 32 x 128 */
+// (the tiles from TILE_128x128R on serve AMP convs only: the general
+// search of the planner skips them)
 enum TileId {
 #define MH3A_TILE(id, mbw, nbw, wm, wn) id,
     MH3A_TILE_LIST
@@ -112,7 +116,8 @@ enum TileId {
 // convs use, with or without the fused activation); other shapes run those
 // convs with a runtime tap count.
 constexpr bool tile_has_act_taps(int t) {
-    return t == TILE_256x96 || t == TILE_256x64 || t == TILE_128x96 || t == TILE_128x128 || t == TILE_64x256 || t == TILE_32x256;
+    return t == TILE_256x96 || t == TILE_256x64 || t == TILE_128x96 || t == TILE_128x128 || t == TILE_64x256 ||
+           t == TILE_32x256 || t == TILE_128x128R || t == TILE_64x256R;
 }
 struct TileShape {
     int m, n;
@@ -138,6 +143,7 @@ struct ConvShape {
     bool act;  // activation fused into the operand staging
     bool amp;  // an AMP conv (tile table measured for them)
     bool m16;  // weights packed for 16-row tiles too
+    bool bx6;  // packed input in the split-product form
 };
 // AMP activations of at least this many (batch x channel x position)
 // elements run as their own pass (see amp_act_fused in mh3a_host.cpp).

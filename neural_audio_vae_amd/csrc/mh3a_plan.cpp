@@ -92,13 +92,16 @@ TileId choose_tile(const ConvShape& L, int positions, int groups, bool bf16, int
     // tile sweep of every stage (one-workgroup-per-CU shapes only pay off at
     // 512 channels, where they fill the 256 CUs in one round).
     if (L.amp) {
+        // split products at 128 to 256 channels: waves of 32 x 128 (half the
+        // weight fetches per product of 64 x 64 waves; measured 2-3% faster)
+        if (L.bx6 && L.c_out >= 128 && L.c_out < 512) return TILE_128x128R;
         if (L.c_out >= 512) return TILE_256x96;
         if (L.c_out >= 256) return TILE_256x64;
         if (L.c_out >= 128) return TILE_128x128;
         if (L.c_out >= 64) return TILE_64x256;
         return TILE_32x256;
     }
-    for (int id = 0; id < TILE_COUNT; ++id) {
+    for (int id = 0; id < TILE_128x128R; ++id) {
         const TileShape s = tile_shape((TileId)id);
         if (s.m > mpad && s.m > 32) continue;  // consumer waves would idle
         const int W = s.n + (L.taps - 1) * L.dil;
