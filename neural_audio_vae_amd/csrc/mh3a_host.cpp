@@ -402,7 +402,7 @@ bool amp_act_fused(const mh3a_decoder* d, int64_t batch, int64_t c, int64_t len)
 ConvPlan plan_conv(const mh3a_decoder* d, const ConvLayer& L, int positions, int batch, bool bf16, bool invariant,
                    bool fused) {
     // packed AMP inputs in the split-product form (see run_amp)
-    const bool bx6 = !fused && !bf16 && L.kind == KIND_AMP && L.act >= 0 && use_bx6(d);
+    const bool bx6 = !fused && !bf16 && L.kind == KIND_AMP && L.act >= 0 && use_bx6(d) && L.c_in % 16 == 0;
     const PlanKey key{&L, positions, batch, (bf16 ? 1 : 0) | (invariant ? 2 : 0) | (fused ? 4 : 0) | (bx6 ? 8 : 0)};
     std::lock_guard<std::mutex> lock(d->plan_mu);
     auto it = d->plans.find(key);
@@ -633,7 +633,7 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, floa
     const bool fused = amp_act_fused(d, batch, C, len);
     const int64_t pbs = pk_item_floats(d, C, len);  // packed batch stride
     const int plp = fused ? 0 : (int)pk_lp(len);
-    const bool px = !fused && !bf16 && use_bx6(d);  // packed inputs in the split-product form
+    const bool px = !fused && !bf16 && use_bx6(d) && C % 16 == 0;  // packed inputs in the split-product form
     for (int j = 0; j < nrb; ++j) {
         for (int n = 0; n < nd; ++n) {
             const ConvLayer& c1 = d->amp[stage][(j * nd + n) * 2 + 0];

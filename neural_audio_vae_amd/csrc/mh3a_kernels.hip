@@ -278,7 +278,7 @@ __host__ __device__ constexpr int conv_lds_floats(int W, bool act) {
 // compile-time constants.
 __host__ __device__ constexpr int bx6_plane(int nwg, int taps) { return nwg + (taps - 1) * kBx6MaxDil; }
 __host__ __device__ constexpr int conv_lds_floats6(int nwg, int taps) {
-    return 2 * kPieces * bx6_plane(nwg, taps) * 4 + kTouchFloats;
+    return 2 * 2 * kPieces * bx6_plane(nwg, taps) * 4 + kTouchFloats;  // two buffers of two-chunk items
 }
 
 // Wave-specialized, persistent implicit-GEMM conv. 512 threads: waves 0-3
@@ -314,13 +314,16 @@ conv_kernel(ConvArgs a) {
     constexpr int NWG = WN * NBW * RB;
     constexpr int MWG = WM * MBW * RB;
     constexpr int PS6 = bx6_plane(NWG, TAPS > 0 ? TAPS : 1);  // split-product plane stride (positions)
+    // an item is CPI chunks (split products: two, so that each barrier hands
+    // over as much matrix-core work as an fp32 item)
+    constexpr int CPI = BX6 ? 2 : 1;
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const bool producer = wave >= 4;
     const int W = NWG + (a.taps - 1) * a.dil;
     // one item's operand window: [CI][W] floats, or kPieces planes of PS6 16-byte groups
-    const int ABUF = BX6 ? kPieces * PS6 * 4 : CI * W;
+    const int ABUF = BX6 ? CPI * kPieces * PS6 * 4 : CI * W;
     float* abuf = lds;                       // [2][ABUF]
     float* xs = lds + 2 * CI * W;            // [CI][act_xs_len(W)]   (act only)
     float* ss = xs + CI * act_xs_len(W);     // [CI][act_ss_len(W)]   (act only)
@@ -330,13 +333,14 @@ conv_kernel(ConvArgs a) {
     // With a K split the chunks are cut into ksplit equal ranges; each
     // (range, tile) pair is a virtual tile whose raw sums go to `partial`.
     const int nchs = nch / a.ksplit;
+    const int ipt = nchs / CPI;  // items per tile
     const int n_nt = (a.positions + NWG - 1) / NWG;
     const int n_mt = (a.c_out + MWG - 1) / MWG;
     const int base_tiles = n_nt * n_mt * a.groups;
     const int total = base_tiles * a.ksplit;
     const int t_begin = (int)((int64_t)total * blockIdx.x / gridDim.x);
     const int t_end = (int)((int64_t)total * (blockIdx.x + 1) / gridDim.x);
-    const int n_items = (t_end - t_begin) * nchs;
+    const int n_items = (t_end - t_begin) * ipt;
     if (n_items == 0) return;
 
     // virtual tile id -> (K range, batch item, phase, M tile, N tile); N tiles
@@ -592,11 +596,12 @@ conv_kernel(ConvArgs a) {
             const int DS = BX6 ? PS6 : W;    // LDS plane stride (positions)
             const int pw = wave - 4;
             const int segs = (W + 63) >> 6;  // 64-position segments per plane
+            // item c of tile t: chunks t.c0 + CPI c + cc, planes one after another
             auto dma = [&](const Tile& t, int c, float* dst) {
-                const float* src =
-                    a.x + (int64_t)t.b * a.x_bstride + ((int64_t)(t.c0 + c) * NPL * a.pk_lp + kPkPadL + t.n_lo) * 4;
-                for (int q = pw; q < NPL * segs; q += 4) {
-                    const int hp = q / segs;
+                const float* src = a.x + (int64_t)t.b * a.x_bstride +
+                                   ((int64_t)(t.c0 + CPI * c) * NPL * a.pk_lp + kPkPadL + t.n_lo) * 4;
+                for (int q = pw; q < CPI * NPL * segs; q += 4) {
+                    const int hp = q / segs;  // plane within the item (chunk cc = hp / NPL)
                     const int pos0 = (q - hp * segs) * 64;
                     const int pos = pos0 + lane;
                     auto* ldst = (__attribute__((address_space(3))) void*)(dst + (hp * DS + pos0) * 4);
@@ -608,17 +613,17 @@ conv_kernel(ConvArgs a) {
             Tile nt = tile_at(t_begin);
             int nc = 0;
             dma(nt, 0, abuf);
-            if (nchs == 1) touch_epilogue(nt);
+            if (ipt == 1) touch_epilogue(nt);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             for (int it = 0; it < n_items; ++it) {
                 if (it + 1 < n_items) {
-                    if (++nc == nchs) {
+                    if (++nc == ipt) {
                         nc = 0;
-                        nt = tile_at(t_begin + (it + 1) / nchs);
+                        nt = tile_at(t_begin + (it + 1) / ipt);
                     }
                     dma(nt, nc, abuf + ((it + 1) & 1) * ABUF);
-                    if (nc == nchs - 1) touch_epilogue(nt);
+                    if (nc == ipt - 1) touch_epilogue(nt);
                 }
                 // the copies land in LDS before the buffer is handed over
                 __builtin_amdgcn_s_waitcnt(0);
@@ -633,13 +638,13 @@ conv_kernel(ConvArgs a) {
         Tile la = cur;
         int la_c = 0;
         auto advance = [&](Tile& t, int& c, int item) {
-            if (++c == nchs) {
+            if (++c == ipt) {
                 c = 0;
-                t = tile_at(t_begin + item / nchs);
+                t = tile_at(t_begin + item / ipt);
             }
         };
         stage(cur, 0, abuf);
-        if (nchs == 1) touch_epilogue(cur);
+        if (ipt == 1) touch_epilogue(cur);
         if (n_items > 1) {
             advance(la, la_c, 1);
             if (prefetchable) prefetch(la, la_c);
@@ -653,7 +658,7 @@ conv_kernel(ConvArgs a) {
                 const Tile t1 = la;
                 const int c1 = la_c;
                 stage(t1, c1, dst);
-                if (c1 == nchs - 1) touch_epilogue(t1);
+                if (c1 == ipt - 1) touch_epilogue(t1);
                 if (it + 2 < n_items) {
                     advance(la, la_c, it + 2);
                     if (prefetchable) prefetch(la, la_c);
@@ -696,9 +701,9 @@ conv_kernel(ConvArgs a) {
             const bool has_next = it + 1 < n_items;
             Tile nxt = cur;
             int nxt_c = cur_c + 1;
-            if (nxt_c == nchs) {
+            if (nxt_c == ipt) {
                 nxt_c = 0;
-                if (has_next) nxt = tile_at(t_begin + (it + 1) / nchs);
+                if (has_next) nxt = tile_at(t_begin + (it + 1) / ipt);
             }
             const float* cur_buf = abuf + (it & 1) * ABUF;
             const int g0 = (cur.c0 + cur_c) * TAPS;
@@ -732,7 +737,7 @@ conv_kernel(ConvArgs a) {
                 R1 = R0;
                 R0 = t0;
             }
-            if (cur_c == nchs - 1) {
+            if (cur_c == ipt - 1) {
                 // row 4 (l / 16) + i, column l % 16 of each 16 x 16 block
                 const int64_t ostride = (int64_t)a.out_mul * a.positions;
 #pragma unroll
@@ -783,9 +788,9 @@ conv_kernel(ConvArgs a) {
         const bool has_next = it + 1 < n_items;
         Tile nxt = cur;
         int nxt_c = cur_c + 1;
-        if (nxt_c == nchs) {
+        if (nxt_c == ipt) {
             nxt_c = 0;
-            if (has_next) nxt = tile_at(t_begin + (it + 1) / nchs);
+            if (has_next) nxt = tile_at(t_begin + (it + 1) / ipt);
         }
         // wave-uniform M-block base (the compiler cannot see it is uniform)
         const int mb_base = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
@@ -797,25 +802,28 @@ conv_kernel(ConvArgs a) {
         const int g0 = (cur.c0 + cur_c) * a.taps;
         if constexpr (BX6) {
             const int nmb_base = __builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW);
-            const int q0 = (cur.c0 + cur_c) * NP6;
-            const int nq0 = has_next ? (nxt.c0 + nxt_c) * NP6 : q0;
+            // the item's CPI chunks: pair u = cc NP6 + q is weight group q0 + u
+            constexpr int NPI = CPI * NP6;
+            const int q0 = (cur.c0 + CPI * cur_c) * NP6;
+            const int nq0 = has_next ? (nxt.c0 + CPI * nxt_c) * NP6 : q0;
             const int nmb = has_next ? nmb_base : mb_base;
             const float* bb_h = cur_buf + (colbase + hi * a.dil) * 4;  // this lane's tap of each pair
             const float* bb_0 = cur_buf + colbase * 4;                 // the pair's first tap
-            // slots 0 and 1 hold pairs 0 and 1 on entry; pair q + 2 (or the next
-            // item's pair q + 2 - NP6) loads while pair q multiplies
+            // slots 0 and 1 hold pairs 0 and 1 on entry; pair u + 2 (or the next
+            // item's pair u + 2 - NPI) loads while pair u multiplies
 #pragma unroll
-            for (int q = 0; q < NP6; ++q) {
-                v4u(&use)[kPieces][MBW] = (q % 3 == 0) ? A6a : ((q % 3 == 1) ? A6b : A6c);
-                v4u(&fill)[kPieces][MBW] = ((q + 2) % 3 == 0) ? A6a : (((q + 2) % 3 == 1) ? A6b : A6c);
-                if (q + 2 < NP6) {
-                    load_a6(fill, mb_base, q0 + q + 2);
+            for (int u = 0; u < NPI; ++u) {
+                const int q = u % NP6, cc = u / NP6;
+                v4u(&use)[kPieces][MBW] = (u % 3 == 0) ? A6a : ((u % 3 == 1) ? A6b : A6c);
+                v4u(&fill)[kPieces][MBW] = ((u + 2) % 3 == 0) ? A6a : (((u + 2) % 3 == 1) ? A6b : A6c);
+                if (u + 2 < NPI) {
+                    load_a6(fill, mb_base, q0 + u + 2);
                 } else {
-                    load_a6(fill, nmb, nq0 + (q + 2 - NP6));
+                    load_a6(fill, nmb, nq0 + (u + 2 - NPI));
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 const bool pad = (TAPS & 1) && q == NP6 - 1;
-                const float* bq = (pad ? bb_0 : bb_h) + 2 * q * a.dil * 4;
+                const float* bq = (pad ? bb_0 : bb_h) + (cc * kPieces * PS6 + 2 * q * a.dil) * 4;
                 v4u Bv[kPieces][NBW];
 #pragma unroll
                 for (int p = 0; p < kPieces; ++p)
@@ -825,8 +833,8 @@ conv_kernel(ConvArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
                 mfma6(use, Bv);
             }
-            // the next item's pairs 0 and 1 sit in slots NP6 % 3, (NP6 + 1) % 3
-            if constexpr (NP6 % 3 == 1) {
+            // the next item's pairs 0 and 1 sit in slots NPI % 3, (NPI + 1) % 3
+            if constexpr (NPI % 3 == 1) {
 #pragma unroll
                 for (int p = 0; p < kPieces; ++p)
 #pragma unroll
@@ -834,7 +842,7 @@ conv_kernel(ConvArgs a) {
                         A6a[p][mb] = A6b[p][mb];
                         A6b[p][mb] = A6c[p][mb];
                     }
-            } else if constexpr (NP6 % 3 == 2) {
+            } else if constexpr (NPI % 3 == 2) {
 #pragma unroll
                 for (int p = 0; p < kPieces; ++p)
 #pragma unroll
@@ -917,7 +925,7 @@ conv_kernel(ConvArgs a) {
                 mfma_tap(Ac, Bv);
             }
         }
-        if (cur_c == nchs - 1) {
+        if (cur_c == ipt - 1) {
             if (a.ksplit > 1) {
                 // raw partial sums of this K range in MFMA fragment order:
                 // [wave][mb][nb][r][lane], so each register is one 256-byte
@@ -1114,6 +1122,7 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
             if (a.bx6) {
                 // split products: bf16 pieces, one phase, planes sized for kBx6MaxDil
                 if (a.bf16 || !a.w6 || a.phases != 1 || a.dil > kBx6MaxDil) return hipErrorInvalidValue;
+                if ((((a.c_in + kChunk - 1) / kChunk) / a.ksplit) % 2) return hipErrorInvalidValue;  // two-chunk items
 #define MH3A_TAPS6(T)                                                                                           \
     if (a.taps == T)                                                                                           \
         return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 2, T>, a, tiles,                         \
