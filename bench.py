@@ -10,11 +10,16 @@ of seeded synthetic latents already resident in HBM. Prints one JSON line.
 The metric is decoded audio-seconds per second: B * N / 40 / seconds per
 step (40 latents per second of 32 kHz audio). The default workload is two
 30 s items (B=2, N=1200) with the default MiniMax-H3 decoder and seeded
-random weights. `roofline` covers the dominant kernel, the act-fused AMP
-convolution, whose kernel durations come from HIP events the library
-records on the decode stream around every AMP conv launch of the last timed
-step (other launches are not bracketed there; a second, untimed pass with
-every launch bracketed gives the per-class breakdown).
+random weights. `roofline` covers the dominant kernel, the AMP dilated
+convolution of the wide stages (conv_kernel on the packed activated input;
+its products run as six bf16 piece products on the bf16 matrix cores with
+fp32 accumulation, fp32-accurate), whose kernel durations come from HIP
+events the library records on the decode stream around every AMP conv
+launch of the last timed step (other launches are not bracketed there; a
+second, untimed pass with every launch bracketed gives the per-class
+breakdown). Its peak is the fp32-equivalent rate of that scheme: the dense
+bf16 matrix peak over six products; with MH3A_BX6=0 (fp32 matrix cores) it
+is the fp32 matrix peak.
 `cpu_baseline` times the CPU oracle on a bounded sample (the first 80
 latents of one item, decoded in full).
 """
@@ -32,6 +37,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+SPLIT_PRODUCTS = 6              # bf16 piece products per fp32 product
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 LATENTS_PER_SECOND = 40         # 32 kHz / hop 800
 
@@ -171,6 +178,8 @@ def main():
     value = audio_s / (ms_step / 1e3)
     amp = amp_only.get("amp_conv", {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
     achieved = amp["flops"] / (amp["ms"] / 1e3) / 1e12 if amp["ms"] > 0 else 0.0
+    split = os.environ.get("MH3A_BX6") != "0" and not args.bf16
+    peak = BF16_MFMA_PEAK_TFLOPS / SPLIT_PRODUCTS if split else FP32_MFMA_PEAK_TFLOPS
     per_step = {
         name: {
             "launches_per_step": k["launches"] / args.steps,
@@ -206,12 +215,16 @@ def main():
         },
         "algorithmic_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
         "roofline": {
-            "kernel": "conv_kernel (AMP dilated conv; activation fused or from the packed pass)",
+            "kernel": "conv_kernel, AMP dilated convs of the 64-512 channel stages (packed activated input; "
+                      + ("six bf16 piece products per fp32 product on v_mfma_f32_32x32x16_bf16, fp32 accumulation)"
+                         if split else "fp32 matrix cores)"),
             "bound": "mfma",
             "achieved": round(achieved, 2),
-            "peak": FP32_MFMA_PEAK_TFLOPS,
+            "peak": round(peak, 2),
+            "peak_basis": ("dense bf16 matrix peak 2500 TFLOP/s / 6 piece products (fp32-equivalent)" if split
+                           else "dense fp32 matrix peak"),
             "unit": "TFLOP/s",
-            "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4),
+            "frac": round(achieved / peak, 4),
             "traffic": measured_traffic(args.workload, flags),
             "launches_timed": amp["launches"],
             "avg_launch_us": round(1e3 * amp["ms"] / max(1, amp["launches"]), 2),
