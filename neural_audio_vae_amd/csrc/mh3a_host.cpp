@@ -141,7 +141,8 @@ struct ConvLayer {
     int out_add[kMaxPhases] = {0};
     int64_t w_off = -1;
     int64_t w16_off = -1;  // 16-row MFMA packing (AMP convs of <= 32 channels), or -1
-    int64_t w6_off = -1;   // bf16 pieces for split products (AMP convs), or -1
+    int64_t w6_off = -1;   // bf16 pieces for split products, or -1
+    int64_t w6_phase_stride = 0;
     int64_t w_phase_stride = 0;
     int64_t b_off = -1;
     int act = -1;       // index into acts, -1 = none
@@ -149,9 +150,19 @@ struct ConvLayer {
     int kind = 0;       // timing class
 };
 
-enum Kind { KIND_IN_PROJ = 0, KIND_CONV_PRE, KIND_UPSAMPLE, KIND_AMP, KIND_AMP_ACT, KIND_FINAL, KIND_AMP_UNIT, KIND_COUNT };
+enum Kind {
+    KIND_IN_PROJ = 0,
+    KIND_CONV_PRE,
+    KIND_UPSAMPLE,
+    KIND_AMP,
+    KIND_AMP_ACT,
+    KIND_FINAL,
+    KIND_AMP_UNIT,
+    KIND_SPLIT,
+    KIND_COUNT
+};
 const char* const kKindNames[KIND_COUNT] = {"dec_in_proj", "conv_pre", "ups_transposed_conv", "amp_conv", "amp_act",
-                                            "act_post_conv_post", "amp_unit"};
+                                            "act_post_conv_post", "amp_unit", "input_split"};
 
 struct TimingRec {
     int kind;
@@ -305,6 +316,18 @@ void add_conv(Blob& blob, ConvLayer& L, const std::vector<float>& w, const float
     }
 }
 
+// A conv (all phases) can read its input in the packed split-product form:
+// a compile-time tap count the kernel has instances for, whole two-chunk
+// items, and windows (output tiles up to 256 positions plus the dilated
+// span) inside the packed row's pads.
+bool split_input_ok(const ConvLayer& L) {
+    if (!(L.taps == 2 || L.taps == 3 || L.taps == 7 || L.taps == 11)) return false;
+    if (L.c_in % 16 || L.c_out < 32 || L.dil < 1 || L.dil > kBx6MaxDil) return false;
+    for (int ph = 0; ph < L.phases; ++ph)
+        if (-L.in_off[ph] > kPkPadL || 255 + (L.taps - 1) * L.dil + L.in_off[ph] > kPkPadR) return false;
+    return true;
+}
+
 int add_act(Blob& blob, const Table& t, const std::string& prefix, int c, const float* designed,
             std::vector<ActLayer>& acts) {
     const float *alpha, *beta;
@@ -398,11 +421,19 @@ bool amp_act_fused(const mh3a_decoder* d, int64_t batch, int64_t c, int64_t len)
     return c < (use_bx6(d) ? 64 : 128) || batch * c * len < kSeparateActMin;
 }
 
+// Whether the AMP convs of a (batch, C, L) stage read the packed input in the
+// split-product form.
+bool stage_px(const mh3a_decoder* d, int64_t batch, int c, int64_t len, bool bf16) {
+    return !amp_act_fused(d, batch, c, len) && !bf16 && use_bx6(d) && c % 16 == 0;
+}
+
+// Whether conv_pre / a transposed conv reads its input in the split-product
+// form (a split pass, then the packed path): layers packed for it at create.
+bool pre_bx6(const mh3a_decoder* d, const ConvLayer& L) { return use_bx6(d) && L.w6_off >= 0; }
+
 // Plans are cached per launch shape.
 ConvPlan plan_conv(const mh3a_decoder* d, const ConvLayer& L, int positions, int batch, bool bf16, bool invariant,
-                   bool fused) {
-    // packed AMP inputs in the split-product form (see run_amp)
-    const bool bx6 = !fused && !bf16 && L.kind == KIND_AMP && L.act >= 0 && use_bx6(d) && L.c_in % 16 == 0;
+                   bool fused, bool bx6 = false) {
     const PlanKey key{&L, positions, batch, (bf16 ? 1 : 0) | (invariant ? 2 : 0) | (fused ? 4 : 0) | (bx6 ? 8 : 0)};
     std::lock_guard<std::mutex> lock(d->plan_mu);
     auto it = d->plans.find(key);
@@ -468,6 +499,7 @@ hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, i
     a.pk_lp = pk_lp;
     a.bx6 = bx6 ? 1 : 0;
     a.w6 = L.w6_off >= 0 ? d->blob + L.w6_off : nullptr;
+    a.w6_phase_stride = L.w6_phase_stride;
     a.x = x;
     a.x_bstride = x_bstride;
     a.c_in = L.c_in;
@@ -494,7 +526,7 @@ hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, i
     a.scale = scale;
     a.act = fused ? act_params(d, L.act) : ActParams{nullptr, nullptr};
     a.bf16 = bf16 ? 1 : 0;
-    const ConvPlan plan = plan_conv(d, L, positions, batch, bf16, invariant, fused);
+    const ConvPlan plan = plan_conv(d, L, positions, batch, bf16, invariant, fused, bx6);
     a.ksplit = plan.ksplit;
     a.partial = partial;
     if (plan.ksplit > 1 && !partial) return hipErrorInvalidValue;
@@ -557,6 +589,26 @@ hipError_t run_act(const mh3a_decoder* d, int act_idx, const float* x, float* y,
     const double n = (double)batch * c * len;
     // 12 up + 12 down multiply-adds and the SnakeBeta per sample; in and out
     tl.done(KIND_AMP_ACT, 48.0 * n, 8.0 * n);
+    return e;
+}
+
+// The split pass of a conv input: x (B, c, len) rows -> y in the packed
+// split-product form.
+hipError_t run_split(const mh3a_decoder* d, const float* x, float* y, int batch, int c, int64_t len, hipStream_t st) {
+    ActArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = x;
+    a.x_bstride = (int64_t)c * len;
+    a.y = y;
+    a.y_bstride = pk_item_floats(d, c, len);
+    a.c = c;
+    a.l = (int)len;
+    a.lp = (int)pk_lp(len);
+    a.pieces = kPieces;
+    TimedLaunch tl(d, st, KIND_SPLIT);
+    hipError_t e = launch_split(a, batch, st);
+    const double n = (double)batch * c * len;
+    tl.done(KIND_SPLIT, 0.0, 10.0 * n);  // 4 bytes in, 6 out
     return e;
 }
 
@@ -633,7 +685,7 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, floa
     const bool fused = amp_act_fused(d, batch, C, len);
     const int64_t pbs = pk_item_floats(d, C, len);  // packed batch stride
     const int plp = fused ? 0 : (int)pk_lp(len);
-    const bool px = !fused && !bf16 && use_bx6(d) && C % 16 == 0;  // packed inputs in the split-product form
+    const bool px = stage_px(d, batch, C, len, bf16);  // packed inputs in the split-product form
     for (int j = 0; j < nrb; ++j) {
         for (int n = 0; n < nd; ++n) {
             const ConvLayer& c1 = d->amp[stage][(j * nd + n) * 2 + 0];
@@ -680,8 +732,9 @@ int64_t amp_partial_floats(const mh3a_decoder* d, int stage, int batch, int len,
     int64_t m = 0;
     if (amp_unit_path(d, stage, bf16)) return 0;  // the unit kernel splits no contraction
     const bool fused = amp_act_fused(d, batch, d->stage_c[stage], len);
+    const bool px = stage_px(d, batch, d->stage_c[stage], len, bf16);
     for (const ConvLayer& L : d->amp[stage])
-        m = std::max(m, plan_partial_floats(L, len, batch * L.phases, plan_conv(d, L, len, batch, bf16, inv, fused),
+        m = std::max(m, plan_partial_floats(L, len, batch * L.phases, plan_conv(d, L, len, batch, bf16, inv, fused, px),
                                             fused));
     return m;
 }
@@ -692,13 +745,13 @@ int64_t decode_partial_floats(const mh3a_decoder* d, int batch, int frames, bool
     const mh3a_config& c = d->cfg;
     int64_t m = 0;
     for (const ConvLayer* L : {&d->in_proj, &d->in_proj_dn, &d->conv_pre})
-        m = std::max(m, plan_partial_floats(*L, frames, batch * L->phases, plan_conv(d, *L, frames, batch, false, inv, true),
-                                            true));
+        m = std::max(m, plan_partial_floats(*L, frames, batch * L->phases,
+                                            plan_conv(d, *L, frames, batch, false, inv, true, pre_bx6(d, *L)), true));
     int64_t len = frames;
     for (int s = 0; s < c.num_ups; ++s) {
         const ConvLayer& U = d->ups[s];
-        m = std::max(m, plan_partial_floats(U, (int)len, batch * U.phases, plan_conv(d, U, (int)len, batch, false, inv, true),
-                                            true));
+        m = std::max(m, plan_partial_floats(U, (int)len, batch * U.phases,
+                                            plan_conv(d, U, (int)len, batch, false, inv, true, pre_bx6(d, U)), true));
         len *= c.rates[s];
         m = std::max(m, amp_partial_floats(d, s, batch, (int)len, bf16, inv));
     }
@@ -714,7 +767,9 @@ int64_t stage_pk_floats(const mh3a_decoder* d, int stage, int64_t batch, int64_t
 
 int64_t decode_pk_floats(const mh3a_decoder* d, int64_t batch, int64_t frames) {
     int64_t m = 0, len = frames;
+    if (pre_bx6(d, d->conv_pre)) m = round_up(batch * pk_item_floats(d, d->conv_pre.c_in, frames), 64);
     for (int s = 0; s < d->cfg.num_ups; ++s) {
+        if (pre_bx6(d, d->ups[s])) m = std::max(m, round_up(batch * pk_item_floats(d, d->ups[s].c_in, len), 64));
         len *= d->cfg.rates[s];
         m = std::max(m, stage_pk_floats(d, s, batch, len));
     }
@@ -765,16 +820,30 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
     HIP_TRY(run_conv(d, inp, z, zb, N, N, bufX, (int64_t)c.latent_dim * N, B, nullptr, nullptr, 1.0f, false, invariant,
                      true, partial, st));
     if (upto == 0) return finish(bufX, (int64_t)B * c.latent_dim * N);
-    HIP_TRY(run_conv(d, d->conv_pre, bufX, (int64_t)c.latent_dim * N, N, N, bufS, (int64_t)c.decoder_dim * N, B,
-                     nullptr, nullptr, 1.0f, false, invariant, true, partial, st));
+    if (pre_bx6(d, d->conv_pre)) {
+        HIP_TRY(run_split(d, bufX, bufA, B, c.latent_dim, N, st));
+        HIP_TRY(run_conv(d, d->conv_pre, bufA, pk_item_floats(d, c.latent_dim, N), N, N, bufS,
+                         (int64_t)c.decoder_dim * N, B, nullptr, nullptr, 1.0f, false, invariant, true, partial, st,
+                         (int)pk_lp(N), true));
+    } else {
+        HIP_TRY(run_conv(d, d->conv_pre, bufX, (int64_t)c.latent_dim * N, N, N, bufS, (int64_t)c.decoder_dim * N, B,
+                         nullptr, nullptr, 1.0f, false, invariant, true, partial, st));
+    }
     if (upto == 1) return finish(bufS, (int64_t)B * c.decoder_dim * N);
     int64_t len = N;
     int cin = c.decoder_dim;
     for (int s = 0; s < c.num_ups; ++s) {
         const int C = d->stage_c[s];
         const int64_t lout = len * c.rates[s];
-        HIP_TRY(run_conv(d, d->ups[s], bufS, (int64_t)cin * len, (int)len, (int)len, bufH, (int64_t)C * lout, B,
-                         nullptr, nullptr, 1.0f, false, invariant, true, partial, st));
+        if (pre_bx6(d, d->ups[s])) {
+            HIP_TRY(run_split(d, bufS, bufA, B, cin, len, st));
+            HIP_TRY(run_conv(d, d->ups[s], bufA, pk_item_floats(d, cin, len), (int)len, (int)len, bufH,
+                             (int64_t)C * lout, B, nullptr, nullptr, 1.0f, false, invariant, true, partial, st,
+                             (int)pk_lp(len), true));
+        } else {
+            HIP_TRY(run_conv(d, d->ups[s], bufS, (int64_t)cin * len, (int)len, (int)len, bufH, (int64_t)C * lout, B,
+                             nullptr, nullptr, 1.0f, false, invariant, true, partial, st));
+        }
         if (upto == 2 + 2 * s) return finish(bufH, (int64_t)B * C * lout);
         rc = run_amp(d, s, bufH, bufX, bufT, bufS, bufA, B, lout, bf16, invariant, partial, st);
         if (rc) return rc;
@@ -1110,6 +1179,11 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
     d->conv_pre.in_off[0] = -3;
     d->conv_pre.alg_taps = 7;
     d->conv_pre.kind = KIND_CONV_PRE;
+    d->conv_pre.dil = 1;
+    if (split_input_ok(d->conv_pre)) {
+        d->conv_pre.w6_off = blob.reserve(packed_weight_floats6(c.decoder_dim, c.latent_dim, 7));
+        pack_conv_weights6(w.data(), c.decoder_dim, c.latent_dim, 7, blob.h.data() + d->conv_pre.w6_off);
+    }
 
     int cin = c.decoder_dim;
     d->ups.resize(c.num_ups);
@@ -1137,11 +1211,19 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
         const int64_t per = packed_weight_floats(C, cin, ku);
         U.w_off = blob.reserve(per * r);
         U.w_phase_stride = per;
+        for (int ph = 0; ph < r; ++ph) {
+            U.in_off[ph] = (ph + pad) / r - (ku - 1);
+            U.out_add[ph] = ph;
+        }
+        const bool split6 = split_input_ok(U);
+        const int64_t per6 = split6 ? packed_weight_floats6(C, cin, ku) : 0;
+        if (split6) {
+            U.w6_off = blob.reserve(per6 * r);
+            U.w6_phase_stride = per6;
+        }
         std::vector<float> wph((size_t)C * cin * ku);
         for (int ph = 0; ph < r; ++ph) {
-            const int q0 = (ph + pad) % r, cph = (ph + pad) / r;
-            U.in_off[ph] = cph - (ku - 1);
-            U.out_add[ph] = ph;
+            const int q0 = (ph + pad) % r;
             for (int o = 0; o < C; ++o)
                 for (int i = 0; i < cin; ++i)
                     for (int jj = 0; jj < ku; ++jj) {
@@ -1149,6 +1231,7 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
                         wph[((size_t)o * cin + i) * ku + jj] = q < k ? w[((size_t)i * C + o) * k + q] : 0.0f;
                     }
             pack_conv_weights(wph.data(), C, cin, ku, blob.h.data() + U.w_off + ph * per);
+            if (split6) pack_conv_weights6(wph.data(), C, cin, ku, blob.h.data() + U.w6_off + ph * per6);
         }
         U.b_off = blob.add(bias, C);
         // AMP blocks

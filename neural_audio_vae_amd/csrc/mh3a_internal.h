@@ -36,6 +36,7 @@ struct ConvArgs {
     const float* w;         // packed weights (see pack_conv_weights)
     const float* w16;       // the same for 16-row tiles (see pack_conv_weights16), or null
     const float* w6;        // bf16 pieces for split products (see pack_conv_weights6), or null
+    int64_t w6_phase_stride; // floats between phases' split-product weights
     int64_t w_phase_stride; // floats between phases' packed weights
     const float* bias;      // [c_out] or null
     float* y;
@@ -175,6 +176,9 @@ struct ActArgs {
     ActParams act;
 };
 hipError_t launch_act(const ActArgs& a, int batch, hipStream_t stream);
+// The same layout without the activation: y = x in the split-product form
+// (a.act unused, a.pieces must be kPieces).
+hipError_t launch_split(const ActArgs& a, int batch, hipStream_t stream);
 
 // One AMP residual unit in one launch, for narrow stages:
 //   y = scale * (x + conv2(act2(conv1(act1(x)))) + sum_in)

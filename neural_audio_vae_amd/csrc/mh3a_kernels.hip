@@ -538,8 +538,8 @@ conv_kernel(ConvArgs a) {
     constexpr int NP6 = (TAPS + 1) / 2;
     const int G6 = nch * NP6;
     v4u A6a[BX6 ? kPieces : 1][MBW], A6b[BX6 ? kPieces : 1][MBW], A6c[BX6 ? kPieces : 1][MBW];
-    auto load_a6 = [&](v4u (&dst)[BX6 ? kPieces : 1][MBW], int mb_base, int g) {
-        const v4u* wp = reinterpret_cast<const v4u*>(a.w6) + (int64_t)g * kPieces * 64 + lane;
+    auto load_a6 = [&](v4u (&dst)[BX6 ? kPieces : 1][MBW], int mb_base, int ph, int g) {
+        const v4u* wp = reinterpret_cast<const v4u*>(a.w6 + (int64_t)ph * a.w6_phase_stride) + (int64_t)g * kPieces * 64 + lane;
 #pragma unroll
         for (int p = 0; p < (BX6 ? kPieces : 1); ++p)
 #pragma unroll
@@ -772,8 +772,8 @@ conv_kernel(ConvArgs a) {
     float4 Ar0[MBW], Ar1[MBW], Ar2[MBW];
     if constexpr (BX6) {
         const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
-        load_a6(A6a, mb0, cur.c0 * NP6);
-        load_a6(A6b, mb0, cur.c0 * NP6 + 1);
+        load_a6(A6a, mb0, cur.ph, cur.c0 * NP6);
+        load_a6(A6b, mb0, cur.ph, cur.c0 * NP6 + 1);
     } else if constexpr (TAPS > 0) {
         const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
         load_a_nb(Ar0, mb0, cur.ph, cur.c0 * a.taps);
@@ -807,6 +807,7 @@ conv_kernel(ConvArgs a) {
             const int q0 = (cur.c0 + CPI * cur_c) * NP6;
             const int nq0 = has_next ? (nxt.c0 + CPI * nxt_c) * NP6 : q0;
             const int nmb = has_next ? nmb_base : mb_base;
+            const int nph6 = has_next ? nxt.ph : cur.ph;
             const float* bb_h = cur_buf + (colbase + hi * a.dil) * 4;  // this lane's tap of each pair
             const float* bb_0 = cur_buf + colbase * 4;                 // the pair's first tap
             // slots 0 and 1 hold pairs 0 and 1 on entry; pair u + 2 (or the next
@@ -817,9 +818,9 @@ conv_kernel(ConvArgs a) {
                 v4u(&use)[kPieces][MBW] = (u % 3 == 0) ? A6a : ((u % 3 == 1) ? A6b : A6c);
                 v4u(&fill)[kPieces][MBW] = ((u + 2) % 3 == 0) ? A6a : (((u + 2) % 3 == 1) ? A6b : A6c);
                 if (u + 2 < NPI) {
-                    load_a6(fill, mb_base, q0 + u + 2);
+                    load_a6(fill, mb_base, cur.ph, q0 + u + 2);
                 } else {
-                    load_a6(fill, nmb, nq0 + (u + 2 - NPI));
+                    load_a6(fill, nmb, nph6, nq0 + (u + 2 - NPI));
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 const bool pad = (TAPS & 1) && q == NP6 - 1;
@@ -1121,12 +1122,13 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
             if (NWG > 256) return hipErrorInvalidValue;
             if (a.bx6) {
                 // split products: bf16 pieces, one phase, planes sized for kBx6MaxDil
-                if (a.bf16 || !a.w6 || a.phases != 1 || a.dil > kBx6MaxDil) return hipErrorInvalidValue;
+                if (a.bf16 || !a.w6 || a.dil > kBx6MaxDil) return hipErrorInvalidValue;
                 if ((((a.c_in + kChunk - 1) / kChunk) / a.ksplit) % 2) return hipErrorInvalidValue;  // two-chunk items
 #define MH3A_TAPS6(T)                                                                                           \
     if (a.taps == T)                                                                                           \
         return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 2, T>, a, tiles,                         \
                                  sizeof(float) * (size_t)conv_lds_floats6(NWG, T), stream);
+                MH3A_TAPS6(2)
                 MH3A_TAPS6(3)
                 MH3A_TAPS6(7)
                 MH3A_TAPS6(11)
@@ -1559,6 +1561,43 @@ hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream) {
     MH3A_UNIT(8, 3, 512) MH3A_UNIT(8, 7, 512) MH3A_UNIT(8, 11, 512)
 #undef MH3A_UNIT
     return hipErrorInvalidValue;
+}
+
+// x (B, c, l) rows -> the split-product packed layout (kPieces planes per
+// chunk of 8 channels, zero pads): one padded position per thread, the 8
+// channels' pieces written as three 16-byte groups.
+__global__ void __launch_bounds__(256) split_kernel(ActArgs a) {
+    const int q = blockIdx.x * 256 + threadIdx.x;  // index in the padded row
+    const int chunk = blockIdx.y, b = blockIdx.z;
+    if (q >= a.lp) return;
+    const int n = q - kPkPadL;
+    const bool in = n >= 0 && n < a.l;
+    const float* xb = a.x + (int64_t)b * a.x_bstride;
+    unsigned pc[kPieces][kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        const int ch = chunk * kChunk + i;
+        const float v = (in && ch < a.c) ? xb[(int64_t)ch * a.l + n] : 0.0f;
+        split3_bf16(v, pc[0][i], pc[1][i], pc[2][i]);
+    }
+    float* yc = a.y + (int64_t)b * a.y_bstride + (int64_t)chunk * kPieces * a.lp * 4;
+#pragma unroll
+    for (int p = 0; p < kPieces; ++p) {
+        uint4 v;
+        v.x = pc[p][0] | (pc[p][1] << 16);
+        v.y = pc[p][2] | (pc[p][3] << 16);
+        v.z = pc[p][4] | (pc[p][5] << 16);
+        v.w = pc[p][6] | (pc[p][7] << 16);
+        *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = v;
+    }
+}
+
+hipError_t launch_split(const ActArgs& a, int batch, hipStream_t stream) {
+    if (a.c < 1 || a.l < 1 || batch < 1 || batch > 65535 || a.pieces != kPieces || a.lp != a.l + kPkPadL + kPkPadR)
+        return hipErrorInvalidValue;
+    dim3 grid((a.lp + 255) / 256, (a.c + kChunk - 1) / kChunk, batch);
+    hipLaunchKernelGGL(split_kernel, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_final(const FinalArgs& a, int batch, hipStream_t stream) {

@@ -78,6 +78,10 @@ int forced_tile() {
 }
 
 TileId choose_tile(const ConvShape& L, int positions, int groups, bool bf16, int ksplit, int num_cus) {
+    // split products on a packed input (conv_pre, transposed convs): the
+    // compile-time-tap shapes, by output width
+    if (L.bx6 && !L.amp && forced_tile() < 0)
+        return L.c_out >= 128 ? TILE_128x128R : (L.c_out >= 64 ? TILE_64x256 : TILE_32x256);
     if (forced_tile() >= 0) {
         const TileShape s = tile_shape((TileId)forced_tile());
         const int W = s.n + (L.taps - 1) * L.dil;
