@@ -100,7 +100,8 @@ constexpr int kBx6MaxDil = 5;
     MH3A_TILE(TILE_32x512, 1, 4, 1, 4)   /*  32 x 512 */           \
     MH3A_TILE(TILE_32x256, 1, 2, 1, 4)   /*  32 x 256 */           \
     MH3A_TILE(TILE_128x128R, 1, 4, 4, 1) /* 128 x 128, waves of 32 x 128 */ \
-    MH3A_TILE(TILE_64x256R, 1, 4, 2, 2)  /*  64 x 256, waves of 32 x 128 */
+    MH3A_TILE(TILE_64x256R, 1, 4, 2, 2)  /*  64 x 256, waves of 32 x 128 */ \
+    MH3A_TILE(TILE_128x160R, 1, 5, 4, 1) /* 128 x 160, waves of 32 x 160 */
 // (the tiles from TILE_128x128R on serve AMP convs only: the general
 // search of the planner skips them)
 enum TileId {
@@ -118,7 +119,7 @@ enum TileId {
 // convs with a runtime tap count.
 constexpr bool tile_has_act_taps(int t) {
     return t == TILE_256x96 || t == TILE_256x64 || t == TILE_128x96 || t == TILE_128x128 || t == TILE_64x256 ||
-           t == TILE_32x256 || t == TILE_128x128R || t == TILE_64x256R;
+           t == TILE_32x256 || t == TILE_128x128R || t == TILE_64x256R || t == TILE_128x160R;
 }
 struct TileShape {
     int m, n;
