@@ -142,6 +142,7 @@ struct ConvLayer {
     int64_t w_off = -1;
     int64_t w16_off = -1;  // 16-row MFMA packing (AMP convs of <= 32 channels), or -1
     int64_t w6_off = -1;   // bf16 pieces for split products, or -1
+    int64_t w6u_off = -1;  // bf16 pieces for the split-product unit kernel (<= 32 channels), or -1
     int64_t w6_phase_stride = 0;
     int64_t w_phase_stride = 0;
     int64_t b_off = -1;
@@ -630,6 +631,14 @@ bool amp_unit_path(const mh3a_decoder* d, int stage, bool bf16) {
     return true;
 }
 
+// ... with split products (bf16 matrix cores) when every layer has the weights for it
+bool amp_unit_split(const mh3a_decoder* d, int stage) {
+    if (!use_bx6(d)) return false;
+    for (const ConvLayer& L : d->amp[stage])
+        if (L.w6u_off < 0) return false;
+    return true;
+}
+
 // The residual units of one AMP stage as unit_kernel launches. Unit n of a
 // block reads the block input h (n = 0) or the previous unit's output, and
 // writes x_buf / t_buf alternately (a unit reads its input around its own
@@ -640,6 +649,7 @@ int run_amp_units(const mh3a_decoder* d, int stage, const float* h, float* x_buf
     const mh3a_config& c = d->cfg;
     const int C = d->stage_c[stage];
     const int nrb = c.num_resblocks, nd = c.num_dilations;
+    const bool split = amp_unit_split(d, stage);
     for (int j = 0; j < nrb; ++j) {
         const float* xin = h;
         for (int n = 0; n < nd; ++n) {
@@ -656,10 +666,11 @@ int run_amp_units(const mh3a_decoder* d, int stage, const float* h, float* x_buf
             u.l = (int)len;
             u.taps = c1.taps;
             u.dil = c1.dil;
-            u.w1 = d->blob + c1.w16_off;
+            u.split = split ? 1 : 0;
+            u.w1 = d->blob + (split ? c1.w6u_off : c1.w16_off);
             u.b1 = d->blob + c1.b_off;
             u.act1 = act_params(d, c1.act);
-            u.w2 = d->blob + c2.w16_off;
+            u.w2 = d->blob + (split ? c2.w6u_off : c2.w16_off);
             u.b2 = d->blob + c2.b_off;
             u.act2 = act_params(d, c2.act);
             if (c2.taps != c1.taps || c2.dil != 1) return fail(MH3A_E_INVALID_ARG, "unit convs disagree");
@@ -1070,6 +1081,43 @@ void pack_conv_weights6(const float* w, int c_out, int c_in, int taps, float* ou
                 }
 }
 
+// Split-product weights of the unit kernel (v_mfma_f32_16x16x32_bf16): for
+// 16-row block mb, K-step ks, piece p and lane l, the 8 bf16 values
+// piece_p(W[mb*16 + l%16, cb*8 + i, ks*TG + tsub]), i = 0..7, where the
+// lane's K-group l/16 is (cb = (l/16) % CB, tsub = (l/16) / CB), CB = c/8
+// channel blocks, TG = 4/CB taps per step; zero past c or the last tap.
+// 16-byte group ((mb * KS + ks) * kPieces + p) * 64 + l.
+int64_t unit_weight_floats6(int c, int taps) {
+    const int cb = c / 8, tg = 4 / cb, ks = (taps + tg - 1) / tg, nmb = (c + 15) / 16;
+    return (int64_t)nmb * ks * kPieces * 64 * 4;
+}
+
+void pack_unit_weights6(const float* w, int c, int taps, float* out) {
+    const int CB = c / 8, TG = 4 / CB, KS = (taps + TG - 1) / TG, nmb = (c + 15) / 16;
+    uint32_t* o = reinterpret_cast<uint32_t*>(out);
+    for (int mb = 0; mb < nmb; ++mb)
+        for (int ks = 0; ks < KS; ++ks)
+            for (int l = 0; l < 64; ++l) {
+                const int g4 = l >> 4, cb = g4 % CB, tsub = g4 / CB, m = mb * 16 + (l & 15), j = ks * TG + tsub;
+                uint16_t pc[kPieces][8];
+                for (int i = 0; i < 8; ++i) {
+                    const int ci = cb * 8 + i;
+                    const float v = (m < c && ci < c && j < taps) ? w[((int64_t)m * c + ci) * taps + j] : 0.0f;
+                    const uint32_t p0 = bf16_rne_bits(v);
+                    const float r1 = v - bf16_bits_value(p0);
+                    const uint32_t p1 = bf16_rne_bits(r1);
+                    const uint32_t p2 = bf16_rne_bits(r1 - bf16_bits_value(p1));
+                    pc[0][i] = (uint16_t)p0;
+                    pc[1][i] = (uint16_t)p1;
+                    pc[2][i] = (uint16_t)p2;
+                }
+                for (int p = 0; p < kPieces; ++p) {
+                    uint32_t* g = o + ((((int64_t)mb * KS + ks) * kPieces + p) * 64 + l) * 4;
+                    for (int k = 0; k < 4; ++k) g[k] = (uint32_t)pc[p][2 * k] | ((uint32_t)pc[p][2 * k + 1] << 16);
+                }
+            }
+}
+
 }  // namespace mh3a
 
 // ===========================================================================
@@ -1249,6 +1297,10 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
                     if (kk == 3 || kk == 7 || kk == 11) {
                         L.w6_off = blob.reserve(packed_weight_floats6(C, C, kk));
                         pack_conv_weights6(w.data(), C, C, kk, blob.h.data() + L.w6_off);
+                    }
+                    if (C <= 32 && C % 8 == 0 && (kk == 3 || kk == 7 || kk == 11)) {
+                        L.w6u_off = blob.reserve(unit_weight_floats6(C, kk));
+                        pack_unit_weights6(w.data(), C, kk, blob.h.data() + L.w6u_off);
                     }
                     if (C <= 32 && (kk == 3 || kk == 7 || kk == 11)) {
                         L.w16_off = blob.reserve(packed_weight_floats16(C, C, kk));

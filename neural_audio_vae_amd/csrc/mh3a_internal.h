@@ -200,12 +200,16 @@ struct UnitArgs {
     const float* w2;
     const float* b2;
     ActParams act2;
+    int split;            // w1, w2 in the split-product unit order (pack_unit_weights6): bf16 matrix cores
 };
 // Shapes the unit kernel has instances for: c in {8, 16, 32}, taps in
 // {3, 7, 11}, 1 <= dil <= kUnitMaxDil.
 constexpr int kUnitMaxDil = 5;
 bool unit_supported(int c, int taps, int dil);
 hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream);
+// Unit-kernel weights as bf16 pieces for v_mfma_f32_16x16x32_bf16.
+int64_t unit_weight_floats6(int c, int taps);
+void pack_unit_weights6(const float* w, int c, int taps, float* out);
 
 // activation_post + conv_post (c -> 1, 7 taps, pad 3) + optional clamp.
 struct FinalArgs {

@@ -1529,6 +1529,228 @@ __global__ void __launch_bounds__(256, 2) unit_kernel(UnitArgs a) {
         });
 }
 
+// Split-product form of the unit kernel: the same unit, with both convs on
+// v_mfma_f32_16x16x32_bf16 over three bf16 pieces of the activations and of
+// the weights (the six products of order <= 2, fp32 accumulation; see
+// kPieces). K = 32 per instruction: lane l holds 8 consecutive channels of
+// channel block cb at tap ks * TG + tsub, where (cb, tsub) enumerate the
+// lane's K-group l / 16 (CB = C / 8 channel blocks, TG = 4 / CB taps per
+// instruction; padded taps carry zero weights and re-read the last tap).
+// LDS: the fp32 rows (x, then the activation in place, then Y1, then the
+// second activation in place) and one region that is first the
+// activation's 2x-rate scratch, then the pieces of A1, of A2:
+// [piece][position][C bf16], one 16-byte group per (position, channel block).
+template <int C, int K, int T>
+struct Unit6Geom {
+    using G = UnitGeom<C, K, T>;
+    static constexpr int CB = C / 8, TG = 4 / CB, KS = (K + TG - 1) / TG;
+    static constexpr int WP = G::W1MAX;                          // positions per piece plane
+    static constexpr int PC = kPieces * WP * CB * 4;             // floats of the three planes
+    static constexpr int SS = kChunk * act_ss_len(G::W1MAX);     // floats of the 2x-rate scratch
+    static constexpr int LDS_P = PC > SS ? PC : SS;
+    static constexpr int LDS_FLOATS = G::LDS_X + LDS_P;
+    static_assert(C == 8 || C == 16 || C == 32, "8, 16 or 32 channels");
+};
+
+// fp32 rows (stride rs) of n positions -> pieces (16-byte group per
+// position and channel block, planes of WP positions)
+template <int C, int WP>
+__device__ __forceinline__ void unit_pack6(const float* rows, int rs, int n, uint4* pc) {
+    constexpr int CB = C / 8;
+    for (int idx = threadIdx.x; idx < n * CB; idx += 256) {
+        const int w = idx / CB, cb = idx - w * CB;
+        unsigned pw[kPieces][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) split3_bf16(rows[(cb * 8 + i) * rs + w], pw[0][i], pw[1][i], pw[2][i]);
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p)
+            pc[p * WP * CB + idx] = make_uint4(pw[p][0] | (pw[p][1] << 16), pw[p][2] | (pw[p][3] << 16),
+                                               pw[p][4] | (pw[p][5] << 16), pw[p][6] | (pw[p][7] << 16));
+    }
+}
+
+// out[co][n] = bias[co] + sum W[co][ci][j] A[ci][n + j dil], A as pieces
+template <int C, int K, int WP, int NOUT, typename Pre, typename Epi>
+__device__ __forceinline__ void unit_conv6(const uint4* __restrict__ pc, const float* __restrict__ wp,
+                                           const float* __restrict__ bias, int dil, Pre pre, Epi epi) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+    using S = UnitConvSplit<C, NOUT>;
+    constexpr int CB = C / 8, TG = 4 / CB, KS = (K + TG - 1) / TG;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int mb = wave / S::WPM, ws = wave % S::WPM;
+    const int g4 = lane >> 4, cb = g4 % CB, tsub = g4 / CB, col = lane & 15;
+    v4u wr[KS][kPieces];
+    const v4u* w6 = reinterpret_cast<const v4u*>(wp) + (int64_t)mb * KS * kPieces * 64 + lane;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) wr[ks][p] = w6[(ks * kPieces + p) * 64];
+    float bv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int co = mb * 16 + 4 * g4 + r;
+        bv[r] = co < C ? bias[co] : 0.0f;
+    }
+    const v4u* pcv = reinterpret_cast<const v4u*>(pc);
+    constexpr int TA[6] = {0, 0, 1, 0, 1, 2}, TB[6] = {0, 1, 0, 2, 1, 0};
+    for (int bt = 0; bt < S::NBAT; ++bt) {
+        int nbq[S::NBB];
+        v4f acc[S::NBB];
+#pragma unroll
+        for (int q = 0; q < S::NBB; ++q) {
+            const int nb = ws + S::WPM * (bt * S::NBB + q);
+            nbq[q] = nb < S::NBLK ? nb : S::NBLK - 1;
+            if (nb < S::NBLK) pre(q, mb, nb);
+            acc[q] = v4f{bv[0], bv[1], bv[2], bv[3]};
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int tap = min(ks * TG + tsub, K - 1);  // padded taps re-read the last one (zero weights)
+            const int off = (col + tap * dil) * CB + cb;
+            v4u b[S::NBB][kPieces];
+#pragma unroll
+            for (int q = 0; q < S::NBB; ++q)
+#pragma unroll
+                for (int p = 0; p < kPieces; ++p) b[q][p] = pcv[p * WP * CB + nbq[q] * 16 * CB + off];
+#pragma unroll
+            for (int t = 0; t < 6; ++t)
+#pragma unroll
+                for (int q = 0; q < S::NBB; ++q)
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, wr[ks][TA[t]]),
+                                                                     __builtin_bit_cast(v8bf, b[q][TB[t]]), acc[q], 0,
+                                                                     0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < S::NBB; ++q) {
+            const int nb = ws + S::WPM * (bt * S::NBB + q);
+            if (nb < S::NBLK) epi(q, acc[q], mb, nb);
+        }
+    }
+}
+
+template <int C, int K, int T>
+__global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    using G = UnitGeom<C, K, T>;
+    using G6 = Unit6Geom<C, K, T>;
+    using S2 = UnitConvSplit<C, T>;
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    float* xr = lds;                                             // fp32 rows
+    uint4* pc = reinterpret_cast<uint4*>(lds + G::LDS_X);      // pieces (or the 2x-rate scratch)
+    float* ss = lds + G::LDS_X;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int ci = tid >> 5, lane32 = tid & 31;
+    const int b = blockIdx.y;
+    const int p0 = blockIdx.x * T;
+    const int L = a.l, dil = a.dil;
+    const float* xb = a.x + (int64_t)b * a.bstride;
+    const int a2_lo = p0 - G::R2, y1_lo = a2_lo - 6;
+    const int W1 = G::NY1 + 2 * dil * G::R2;
+    const int a1_lo = y1_lo - dil * G::R2, x_lo = a1_lo - 6;
+    const int XS1 = act_xs_len(W1);
+
+    const ActTaps f1 = load_act_taps(a.act1.taps);
+    {
+        constexpr int NW = (G::XS1MAX + 255) / 256;
+#pragma unroll
+        for (int c0 = 0; c0 < C; c0 += 8) {
+            float v[8][NW];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int u = 0; u < NW; ++u)
+                    v[r][u] = xb[(c0 + r) * L + clampi(x_lo + tid + 256 * u, 0, L - 1)];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int u = 0; u < NW; ++u)
+                    if (tid + 256 * u < XS1) xr[(c0 + r) * XS1 + tid + 256 * u] = v[r][u];
+        }
+    }
+    __syncthreads();
+    // act1 in place over the x rows (a channel's x row is dead after its up pass)
+#pragma unroll
+    for (int c0 = 0; c0 < C; c0 += kChunk) {
+        act_from_xs<kChunk>(xr + c0 * XS1, xr + c0 * XS1, ss, c0, C, L, a1_lo, W1, f1, a.act1.ab[c0 + ci], ci, lane32,
+                            XS1);
+        wave_lds_sync();
+    }
+    __syncthreads();
+    unit_pack6<C, G6::WP>(xr, XS1, W1, pc);
+    __syncthreads();
+    // conv1 -> Y1 rows
+    unit_conv6<C, K, G6::WP, G::NY1>(
+        pc, a.w1, a.b1, dil, [](int, int, int) {},
+        [&](int, v4f acc, int mb, int nb) {
+            const int n = nb * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = mb * 16 + 4 * (lane >> 4) + r;
+                if (co < C && n < G::XS2) xr[co * G::XS2 + n] = acc[r];
+            }
+        });
+    __syncthreads();
+    if (y1_lo < 0 || y1_lo + G::XS2 > L) {
+        const int i0 = -y1_lo, i1 = L - 1 - y1_lo;
+        for (int idx = tid; idx < C * G::XS2; idx += 256) {
+            const int co = idx / G::XS2, w = idx - co * G::XS2;
+            const int src = w < i0 ? i0 : (w > i1 ? i1 : -1);
+            if (src >= 0) xr[co * G::XS2 + w] = xr[co * G::XS2 + src];
+        }
+        __syncthreads();
+    }
+    {
+        const ActTaps f2 = load_act_taps(a.act2.taps);
+#pragma unroll
+        for (int c0 = 0; c0 < C; c0 += kChunk) {
+            act_from_xs<kChunk>(xr + c0 * G::XS2, xr + c0 * G::XS2, ss, c0, C, L, a2_lo, G::W2, f2,
+                                a.act2.ab[c0 + ci], ci, lane32, G::XS2);
+            wave_lds_sync();
+        }
+    }
+    __syncthreads();
+    unit_pack6<C, G6::WP>(xr, G::XS2, G::W2, pc);
+    __syncthreads();
+    float rs[S2::NBB][4];
+    const float* sb = a.sum_in ? a.sum_in + (int64_t)b * a.bstride : nullptr;
+    float* yb = a.y + (int64_t)b * a.bstride;
+    unit_conv6<C, K, G6::WP, T>(
+        pc, a.w2, a.b2, 1,
+        [&](int q, int mb, int nb) {
+            const int n = min(p0 + nb * 16 + (lane & 15), L - 1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = min(mb * 16 + 4 * (lane >> 4) + r, C - 1);
+                rs[q][r] = xb[co * L + n] + (sb ? sb[co * L + n] : 0.0f);
+            }
+        },
+        [&](int q, v4f acc, int mb, int nb) {
+            const int n = p0 + nb * 16 + (lane & 15);
+            if (n >= L) return;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = mb * 16 + 4 * (lane >> 4) + r;
+                if (co < C) yb[co * L + n] = (acc[r] + rs[q][r]) * a.scale;
+            }
+        });
+}
+
+template <int C, int K, int T>
+static hipError_t launch_unit6_t(const UnitArgs& a, int batch, hipStream_t stream) {
+    constexpr size_t lds = sizeof(float) * Unit6Geom<C, K, T>::LDS_FLOATS;
+    static_assert(2 * lds <= 160 * 1024, "two workgroups per compute unit");
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)unit6_kernel<C, K, T>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    dim3 grid((a.l + T - 1) / T, batch);
+    hipLaunchKernelGGL((unit6_kernel<C, K, T>), grid, dim3(256), lds, stream, a);
+    return hipGetLastError();
+}
+
 bool unit_supported(int c, int taps, int dil) {
     return (c == 8 || c == 16 || c == 32) && (taps == 3 || taps == 7 || taps == 11) && dil >= 1 &&
            dil <= kUnitMaxDil;
@@ -1554,8 +1776,9 @@ hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream) {
     if (!unit_supported(a.c, a.taps, a.dil) || a.l < 1 || batch < 1 || batch > 65535 || !a.x || !a.y ||
         a.x == a.y || !a.w1 || !a.w2 || !a.b1 || !a.b2 || !a.act1.taps || !a.act2.taps)
         return hipErrorInvalidValue;
-#define MH3A_UNIT(C_, K_, T_) \
-    if (a.c == C_ && a.taps == K_) return launch_unit_t<C_, K_, T_>(a, batch, stream);
+#define MH3A_UNIT(C_, K_, T_)                                                  \
+    if (a.c == C_ && a.taps == K_)                                             \
+        return a.split ? launch_unit6_t<C_, K_, T_>(a, batch, stream) : launch_unit_t<C_, K_, T_>(a, batch, stream);
     MH3A_UNIT(32, 3, 128) MH3A_UNIT(32, 7, 128) MH3A_UNIT(32, 11, 128)
     MH3A_UNIT(16, 3, 256) MH3A_UNIT(16, 7, 256) MH3A_UNIT(16, 11, 256)
     MH3A_UNIT(8, 3, 512) MH3A_UNIT(8, 7, 512) MH3A_UNIT(8, 11, 512)

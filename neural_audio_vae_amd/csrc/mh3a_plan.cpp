@@ -133,7 +133,7 @@ TileId choose_tile(const ConvShape& L, int positions, int groups, bool bf16, int
 ConvPlan plan_conv(const ConvShape& L, int positions, int batch, bool bf16, bool invariant, int num_cus) {
     // AMP convs of <= 16 output channels: 16-row tiles (a 32-row block would
     // be half or three quarters padding); they never split (1-2 chunks).
-    if (L.amp && L.m16 && !bf16 && forced_tile() < 0) return {TILE_16x256, 1};
+    if (L.amp && L.m16 && !bf16 && !L.bx6 && forced_tile() < 0) return {TILE_16x256, 1};
     const int nch = (L.c_in + kChunk - 1) / kChunk;
     const int item_groups = invariant ? L.phases : batch * L.phases;
     int best_s = 1;
