@@ -428,3 +428,52 @@ def test_chunked_decode_argument_errors(default_decoder, dev):
     _lib.mh3a_decode_chunked(h, z.data_ptr(), 1, 100, 16, out.data_ptr(), ws.data_ptr(), need, 0, st)
     torch.cuda.synchronize()
     print("[case] chunked argument errors ok", file=sys.stderr)
+
+
+# ---------------------------------------------------------------------------
+# fp32 matrix-core forms (MH3A_BX6=0, read once per process)
+# ---------------------------------------------------------------------------
+
+_FP32_FORMS_CHECK = r"""
+import sys
+import numpy as np
+import torch
+sys.path.insert(0, sys.argv[1])
+import oracle as O
+from neural_audio_vae_amd import Decoder, synth
+
+def check(what, got, ref, rel=1e-4, abs_=1e-3):
+    got = np.asarray(got, np.float64); ref = np.asarray(ref, np.float64)
+    rl = float(np.linalg.norm(got - ref) / np.linalg.norm(ref)); ma = float(np.max(np.abs(got - ref)))
+    print(f"[parity] fp32 forms {what}: rel_l2={rl:.3e} max_abs={ma:.3e}", flush=True)
+    assert rl <= rel and ma <= abs_, what
+
+p = synth.make_params()
+d = Decoder(p)
+z = synth.make_latents(1, 4)
+y = O.decode_item(p, z[0], clamp=False)
+got = d.decode(torch.from_numpy(z).cuda(), flags=0x4).cpu().numpy()[0]
+check("c1 decode", got, y)
+for stage, c in ((0, 512), (1, 256), (4, 32)):
+    x = synth.make_signal((1, c, 3000), seed=stage)
+    out = d.amp_stage(stage, torch.from_numpy(x).cuda()).cpu().numpy()
+    ref = O.stage_amp(x[0][:, 1380:1684], p, stage)[:, 120:184]  # 120 samples of margin each side
+    check(f"stage {stage} [1500,1564)", out[0][:, 1500:1564], ref)
+print("ok", flush=True)
+"""
+
+
+def test_fp32_matrix_core_forms(dev):
+    # The fp32 forms (packed fp32 input at 512 channels, fused activation at
+    # 256 on this short signal, fp32 unit kernel, plain-row conv_pre and
+    # transposed convs) stay selectable with
+    # MH3A_BX6=0; a fresh process checks them against the oracle.
+    import os
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, MH3A_BX6="0")
+    print("[case] fp32 forms in a subprocess (MH3A_BX6=0)", flush=True)
+    r = subprocess.run([sys.executable, "-c", _FP32_FORMS_CHECK, root], env=env, capture_output=True, text=True,
+                       timeout=240)
+    print(r.stdout, flush=True)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr[-2000:]
