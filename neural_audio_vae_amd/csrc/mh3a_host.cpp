@@ -424,8 +424,10 @@ bool amp_act_fused(const mh3a_decoder* d, int64_t batch, int64_t c, int64_t len)
 
 // Whether the AMP convs of a (batch, C, L) stage read the packed input in the
 // split-product form.
+// (with the bf16 operand flag the convs take the three-product variant)
 bool stage_px(const mh3a_decoder* d, int64_t batch, int c, int64_t len, bool bf16) {
-    return !amp_act_fused(d, batch, c, len) && !bf16 && use_bx6(d) && c % 16 == 0;
+    (void)bf16;
+    return !amp_act_fused(d, batch, c, len) && use_bx6(d) && c % 16 == 0;
 }
 
 // Whether conv_pre / a transposed conv reads its input in the split-product
@@ -617,6 +619,14 @@ hipError_t run_split(const mh3a_decoder* d, const float* x, float* y, int batch,
 // result in s_buf. Blocks run from the same h and are averaged in the
 // epilogue of each block's last conv. Each conv's activation is fused into
 // its operand staging, or (large tensors) runs as its own pass into a_buf.
+// Whether stage s's unit kernels can use split products (every layer has the weights)
+bool amp_unit_split(const mh3a_decoder* d, int stage) {
+    if (!use_bx6(d)) return false;
+    for (const ConvLayer& L : d->amp[stage])
+        if (L.w6u_off < 0) return false;
+    return true;
+}
+
 // Whether stage s runs each residual unit as one launch (unit_kernel): fp32
 // operands, a channel count and every conv's taps and dilation that the
 // kernel has instances for. MH3A_AMP_UNIT=0 turns it off (a tuning aid).
@@ -625,19 +635,13 @@ bool amp_unit_path(const mh3a_decoder* d, int stage, bool bf16) {
         const char* e = std::getenv("MH3A_AMP_UNIT");
         return e && !std::strcmp(e, "0");
     }();
-    if (off || bf16) return false;
+    if (off) return false;
     for (const ConvLayer& L : d->amp[stage])
         if (L.w16_off < 0 || L.b_off < 0 || L.act < 0 || !unit_supported(L.c_out, L.taps, L.dil)) return false;
-    return true;
+    // the bf16 operand flag needs the split-product unit kernel (three products)
+    return !bf16 || amp_unit_split(d, stage);
 }
 
-// ... with split products (bf16 matrix cores) when every layer has the weights for it
-bool amp_unit_split(const mh3a_decoder* d, int stage) {
-    if (!use_bx6(d)) return false;
-    for (const ConvLayer& L : d->amp[stage])
-        if (L.w6u_off < 0) return false;
-    return true;
-}
 
 // The residual units of one AMP stage as unit_kernel launches. Unit n of a
 // block reads the block input h (n = 0) or the previous unit's output, and
@@ -645,7 +649,7 @@ bool amp_unit_split(const mh3a_decoder* d, int stage) {
 // outputs, so it cannot update in place); the block's last unit adds into
 // the running sum s_buf, scaled by 1 / blocks at the last block.
 int run_amp_units(const mh3a_decoder* d, int stage, const float* h, float* x_buf, float* t_buf, float* s_buf,
-                  int batch, int64_t len, hipStream_t st) {
+                  int batch, int64_t len, bool bf16, hipStream_t st) {
     const mh3a_config& c = d->cfg;
     const int C = d->stage_c[stage];
     const int nrb = c.num_resblocks, nd = c.num_dilations;
@@ -666,7 +670,7 @@ int run_amp_units(const mh3a_decoder* d, int stage, const float* h, float* x_buf
             u.l = (int)len;
             u.taps = c1.taps;
             u.dil = c1.dil;
-            u.split = split ? 1 : 0;
+            u.split = split ? (bf16 ? 3 : 6) : 0;
             u.w1 = d->blob + (split ? c1.w6u_off : c1.w16_off);
             u.b1 = d->blob + c1.b_off;
             u.act1 = act_params(d, c1.act);
@@ -692,7 +696,7 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, floa
     const int64_t bs = (int64_t)C * len;
     const int nrb = c.num_resblocks, nd = c.num_dilations;
     const int L = (int)len;
-    if (amp_unit_path(d, stage, bf16)) return run_amp_units(d, stage, h, x_buf, t_buf, s_buf, batch, len, st);
+    if (amp_unit_path(d, stage, bf16)) return run_amp_units(d, stage, h, x_buf, t_buf, s_buf, batch, len, bf16, st);
     const bool fused = amp_act_fused(d, batch, C, len);
     const int64_t pbs = pk_item_floats(d, C, len);  // packed batch stride
     const int plp = fused ? 0 : (int)pk_lp(len);

@@ -200,7 +200,8 @@ struct UnitArgs {
     const float* w2;
     const float* b2;
     ActParams act2;
-    int split;            // w1, w2 in the split-product unit order (pack_unit_weights6): bf16 matrix cores
+    int split;            // 0: fp32 matrix cores; 6 / 3: w1, w2 in the split-product unit order
+                          // (pack_unit_weights6), six / three piece products on bf16 matrix cores
 };
 // Shapes the unit kernel has instances for: c in {8, 16, 32}, taps in
 // {3, 7, 11}, 1 <= dil <= kUnitMaxDil.

@@ -297,13 +297,17 @@ __host__ __device__ constexpr int conv_lds_floats6(int nwg, int taps) {
 //
 // PREC selects the products: 0 fp32 matrix cores; 1 the bf16 operand
 // variant (three-term split on fp32 matrix cores); 2 split products on bf16
-// matrix cores (packed input in the split-product form, see kPieces).
+// matrix cores (packed input in the split-product form, see kPieces); 3 the
+// bf16 operand variant on bf16 matrix cores (pieces 0 and 1 only, the three
+// products w0 x0, w0 x1, w1 x0: the numerics of PREC 1).
 template <int MBW, int NBW, int WM, int WN, bool ACT, int PREC, int TAPS, int RB = 32>
 // (fp32 tiles of at most 2 x 2 blocks per wave keep two workgroups per CU: <= 128 VGPRs)
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((MBW * NBW <= 4 && PREC != 2) ? 4 : 1)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((MBW * NBW <= 4 && PREC < 2) ? 4 : 1)))
 conv_kernel(ConvArgs a) {
     constexpr bool BF16 = PREC == 1;
-    constexpr bool BX6 = PREC == 2;
+    constexpr bool BX6 = PREC >= 2;            // bf16 matrix cores on the pieces
+    constexpr int NPROD = PREC == 3 ? 3 : 6;   // piece products per pair
+    constexpr int NPA = PREC == 3 ? 2 : kPieces;  // weight / activation pieces used
     static_assert(WM * WN == 4, "four consumer waves");
     static_assert(RB == 32 || (RB == 16 && MBW == 1 && WM == 1 && TAPS > 0 && !BF16), "16-row tiles");
     constexpr int CI = kChunk;
@@ -541,16 +545,16 @@ conv_kernel(ConvArgs a) {
     auto load_a6 = [&](v4u (&dst)[BX6 ? kPieces : 1][MBW], int mb_base, int ph, int g) {
         const v4u* wp = reinterpret_cast<const v4u*>(a.w6 + (int64_t)ph * a.w6_phase_stride) + (int64_t)g * kPieces * 64 + lane;
 #pragma unroll
-        for (int p = 0; p < (BX6 ? kPieces : 1); ++p)
+        for (int p = 0; p < (BX6 ? NPA : 1); ++p)
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb)
                 dst[p][mb] = wp[((int64_t)min(mb_base + mb, mb_tot - 1) * G6 * kPieces + p) * 64];
     };
-    // the six products of order <= 2: (A piece, B piece)
+    // the six products of order <= 2 (the first three for PREC 3): (A piece, B piece)
     auto mfma6 = [&](const v4u (&A)[BX6 ? kPieces : 1][MBW], const v4u (&B)[BX6 ? kPieces : 1][NBW]) {
         constexpr int TA[6] = {0, 0, 1, 0, 1, 2}, TB[6] = {0, 1, 0, 2, 1, 0};
 #pragma unroll
-        for (int t = 0; t < 6; ++t)
+        for (int t = 0; t < NPROD; ++t)
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
@@ -827,7 +831,7 @@ conv_kernel(ConvArgs a) {
                 const float* bq = (pad ? bb_0 : bb_h) + (cc * kPieces * PS6 + 2 * q * a.dil) * 4;
                 v4u Bv[kPieces][NBW];
 #pragma unroll
-                for (int p = 0; p < kPieces; ++p)
+                for (int p = 0; p < NPA; ++p)
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb)
                         Bv[p][nb] = *reinterpret_cast<const v4u*>(bq + (p * PS6 + nb * 32) * 4);
@@ -1152,12 +1156,14 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
             if (NWG > 256) return hipErrorInvalidValue;
             if (a.bx6) {
                 // split products: bf16 pieces, one phase, planes sized for kBx6MaxDil
-                if (a.bf16 || !a.w6 || a.dil > kBx6MaxDil) return hipErrorInvalidValue;
+                if (!a.w6 || a.dil > kBx6MaxDil) return hipErrorInvalidValue;
                 if ((((a.c_in + kChunk - 1) / kChunk) / a.ksplit) % 2) return hipErrorInvalidValue;  // two-chunk items
 #define MH3A_TAPS6(T)                                                                                           \
     if (a.taps == T)                                                                                           \
-        return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 2, T>, a, tiles,                         \
-                                 sizeof(float) * (size_t)conv_lds_floats6(NWG, T), stream);
+        return a.bf16 ? launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 3, T>, a, tiles,                \
+                                          sizeof(float) * (size_t)conv_lds_floats6(NWG, T), stream)            \
+                      : launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 2, T>, a, tiles,                \
+                                          sizeof(float) * (size_t)conv_lds_floats6(NWG, T), stream);
                 MH3A_TAPS6(2)
                 MH3A_TAPS6(3)
                 MH3A_TAPS6(7)
@@ -1600,7 +1606,7 @@ __device__ __forceinline__ void unit_pack6(const float* rows, int rs, int n, uin
 }
 
 // out[co][n] = bias[co] + sum W[co][ci][j] A[ci][n + j dil], A as pieces
-template <int C, int K, int WP, int NOUT, typename Pre, typename Epi>
+template <int C, int K, int WP, int NOUT, int NPROD, typename Pre, typename Epi>
 __device__ __forceinline__ void unit_conv6(const uint4* __restrict__ pc, const float* __restrict__ wp,
                                            const float* __restrict__ bias, int dil, Pre pre, Epi epi) {
     typedef float v4f __attribute__((ext_vector_type(4)));
@@ -1608,6 +1614,7 @@ __device__ __forceinline__ void unit_conv6(const uint4* __restrict__ pc, const f
     typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
     using S = UnitConvSplit<C, NOUT>;
     constexpr int CB = C / 8, TG = 4 / CB, KS = (K + TG - 1) / TG;
+    constexpr int NPU = NPROD == 3 ? 2 : kPieces;  // pieces used
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int mb = wave / S::WPM, ws = wave % S::WPM;
     const int g4 = lane >> 4, cb = g4 % CB, tsub = g4 / CB, col = lane & 15;
@@ -1616,7 +1623,7 @@ __device__ __forceinline__ void unit_conv6(const uint4* __restrict__ pc, const f
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int p = 0; p < kPieces; ++p) wr[ks][p] = w6[(ks * kPieces + p) * 64];
+        for (int p = 0; p < NPU; ++p) wr[ks][p] = w6[(ks * kPieces + p) * 64];
     float bv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1643,9 +1650,9 @@ __device__ __forceinline__ void unit_conv6(const uint4* __restrict__ pc, const f
 #pragma unroll
             for (int q = 0; q < S::NBB; ++q)
 #pragma unroll
-                for (int p = 0; p < kPieces; ++p) b[q][p] = pcv[p * WP * CB + nbq[q] * 16 * CB + off];
+                for (int p = 0; p < NPU; ++p) b[q][p] = pcv[p * WP * CB + nbq[q] * 16 * CB + off];
 #pragma unroll
-            for (int t = 0; t < 6; ++t)
+            for (int t = 0; t < NPROD; ++t)
 #pragma unroll
                 for (int q = 0; q < S::NBB; ++q)
                     acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, wr[ks][TA[t]]),
@@ -1660,7 +1667,7 @@ __device__ __forceinline__ void unit_conv6(const uint4* __restrict__ pc, const f
     }
 }
 
-template <int C, int K, int T>
+template <int C, int K, int T, int NPROD>
 __global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
     typedef float v4f __attribute__((ext_vector_type(4)));
     using G = UnitGeom<C, K, T>;
@@ -1711,7 +1718,7 @@ __global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
     unit_pack6<C, G6::WP>(xr, XS1, W1, pc);
     __syncthreads();
     // conv1 -> Y1 rows
-    unit_conv6<C, K, G6::WP, G::NY1>(
+    unit_conv6<C, K, G6::WP, G::NY1, NPROD>(
         pc, a.w1, a.b1, dil, [](int, int, int) {},
         [&](int, v4f acc, int mb, int nb) {
             const int n = nb * 16 + (lane & 15);
@@ -1746,7 +1753,7 @@ __global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
     float rs[S2::NBB][4];
     const float* sb = a.sum_in ? a.sum_in + (int64_t)b * a.bstride : nullptr;
     float* yb = a.y + (int64_t)b * a.bstride;
-    unit_conv6<C, K, G6::WP, T>(
+    unit_conv6<C, K, G6::WP, T, NPROD>(
         pc, a.w2, a.b2, 1,
         [&](int q, int mb, int nb) {
             const int n = min(p0 + nb * 16 + (lane & 15), L - 1);
@@ -1767,17 +1774,17 @@ __global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
         });
 }
 
-template <int C, int K, int T>
+template <int C, int K, int T, int NPROD>
 static hipError_t launch_unit6_t(const UnitArgs& a, int batch, hipStream_t stream) {
     constexpr size_t lds = sizeof(float) * Unit6Geom<C, K, T>::LDS_FLOATS;
     static_assert(2 * lds <= 160 * 1024, "two workgroups per compute unit");
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void*)unit6_kernel<C, K, T>,
+        hipError_t e = hipFuncSetAttribute((const void*)unit6_kernel<C, K, T, NPROD>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     dim3 grid((a.l + T - 1) / T, batch);
-    hipLaunchKernelGGL((unit6_kernel<C, K, T>), grid, dim3(256), lds, stream, a);
+    hipLaunchKernelGGL((unit6_kernel<C, K, T, NPROD>), grid, dim3(256), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -1803,12 +1810,15 @@ static hipError_t launch_unit_t(const UnitArgs& a, int batch, hipStream_t stream
 // Tile widths: 128 positions at 32 channels, 256 at 16, 512 at 8 (about
 // 60-80 KB of LDS each, two workgroups per compute unit).
 hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream) {
-    if (!unit_supported(a.c, a.taps, a.dil) || a.l < 1 || batch < 1 || batch > 65535 || !a.x || !a.y ||
+    if (!unit_supported(a.c, a.taps, a.dil) || (a.split != 0 && a.split != 3 && a.split != 6) || a.l < 1 || batch < 1 ||
+        batch > 65535 || !a.x || !a.y ||
         a.x == a.y || !a.w1 || !a.w2 || !a.b1 || !a.b2 || !a.act1.taps || !a.act2.taps)
         return hipErrorInvalidValue;
 #define MH3A_UNIT(C_, K_, T_)                                                  \
     if (a.c == C_ && a.taps == K_)                                             \
-        return a.split ? launch_unit6_t<C_, K_, T_>(a, batch, stream) : launch_unit_t<C_, K_, T_>(a, batch, stream);
+        return a.split == 6   ? launch_unit6_t<C_, K_, T_, 6>(a, batch, stream)                             \
+               : a.split == 3 ? launch_unit6_t<C_, K_, T_, 3>(a, batch, stream)                             \
+                              : launch_unit_t<C_, K_, T_>(a, batch, stream);
     MH3A_UNIT(32, 3, 128) MH3A_UNIT(32, 7, 128) MH3A_UNIT(32, 11, 128)
     MH3A_UNIT(16, 3, 256) MH3A_UNIT(16, 7, 256) MH3A_UNIT(16, 11, 256)
     MH3A_UNIT(8, 3, 512) MH3A_UNIT(8, 7, 512) MH3A_UNIT(8, 11, 512)
