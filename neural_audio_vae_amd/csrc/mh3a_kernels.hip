@@ -550,9 +550,12 @@ conv_kernel(ConvArgs a) {
             for (int mb = 0; mb < MBW; ++mb)
                 dst[p][mb] = wp[((int64_t)min(mb_base + mb, mb_tot - 1) * G6 * kPieces + p) * 64];
     };
-    // the six products of order <= 2 (the first three for PREC 3): (A piece, B piece)
+    // the six products of order <= 2 (the first three for PREC 3): (A piece, B piece),
+    // measured 1-2% faster in this order
     auto mfma6 = [&](const v4u (&A)[BX6 ? kPieces : 1][MBW], const v4u (&B)[BX6 ? kPieces : 1][NBW]) {
-        constexpr int TA[6] = {0, 0, 1, 0, 1, 2}, TB[6] = {0, 1, 0, 2, 1, 0};
+        // by activation piece, so that only piece 0's LDS reads gate the first
+        // products (PREC 3: the first three entries are its products too)
+        constexpr int TA[6] = {0, 1, 0, 2, 1, 0}, TB[6] = {0, 0, 1, 0, 1, 2};
 #pragma unroll
         for (int t = 0; t < NPROD; ++t)
 #pragma unroll
