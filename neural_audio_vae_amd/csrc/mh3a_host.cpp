@@ -681,7 +681,8 @@ int run_amp_units(const mh3a_decoder* d, int stage, const float* h, float* x_buf
             TimedLaunch tl(d, st, KIND_AMP_UNIT);
             HIP_TRY(launch_unit(u, batch, st));
             const double n_out = (double)batch * C * len;
-            tl.done(KIND_AMP_UNIT, 2.0 * 2.0 * C * (double)C * c1.alg_taps * n_out,
+            // two convs of 2 C k multiply-adds per output
+            tl.done(KIND_AMP_UNIT, 2.0 * 2.0 * C * (double)c1.alg_taps * n_out,
                     4.0 * (n_out * (2 + (u.sum_in ? 1 : 0)) + 2.0 * C * C * c1.alg_taps + 2.0 * C));
             xin = u.y;
         }
