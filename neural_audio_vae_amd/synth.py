@@ -18,7 +18,9 @@ Distributions (there are no released weights to load):
   ``mean_c ~ N(0, 0.1)``.
 
 Every stream is a numpy PCG64 generator keyed by ``(seed, stream, ...)``:
-stream 0 parameters, 1 latents, 2 mean/std, 3 free-standing stage inputs.
+stream 0 parameters, 1 latents, 2 mean/std, 3 free-standing stage inputs,
+4 encoder parameters (plain Snake ``alpha ~ U[0.5, 1.5]``), 5 waveforms
+(``N(0, 0.25)``, clipped to [-1, 1]).
 The parameters therefore do not depend on the batch or sequence length.
 """
 
@@ -128,3 +130,65 @@ def make_signal(shape, seed=0, scale=1.0):
     layer tests)."""
     rng = np.random.default_rng([seed, 3] + [int(s) for s in shape])
     return (scale * rng.standard_normal(shape)).astype(np.float32)
+
+
+ENC_DEFAULTS = {"encoder_dim": 64, "encoder_rates": (2, 4, 4, 5, 5), "latent_dim": 2048}
+
+
+def encoder_param_specs(config=None):
+    """(name, shape, kind) for every parameter of the encoder's convolution
+    stack (the names ``MLXMiniMaxH3AudioVAE.encode`` reads)."""
+    c = dict(ENC_DEFAULTS)
+    if config:
+        c.update({k: v for k, v in config.items() if k in ENC_DEFAULTS})
+    specs = []
+
+    def conv(prefix, c_out, c_in, k):
+        specs.append((f"{prefix}.weight_v", (c_out, c_in, k), "v"))
+        specs.append((f"{prefix}.weight_g", (c_out, 1, 1), "g"))
+        specs.append((f"{prefix}.bias", (c_out,), "bias"))
+
+    dim = c["encoder_dim"]
+    conv("encoder.block.0", dim, 1, 7)
+    for index, stride in enumerate(c["encoder_rates"], start=1):
+        p = f"encoder.block.{index}"
+        for unit in range(3):
+            u = f"{p}.block.{unit}"
+            specs.append((f"{u}.block.0.alpha", (dim,), "alpha"))
+            conv(f"{u}.block.1", dim, dim, 7)
+            specs.append((f"{u}.block.2.alpha", (dim,), "alpha"))
+            conv(f"{u}.block.3", dim, dim, 1)
+        specs.append((f"{p}.block.3.alpha", (dim,), "alpha"))
+        conv(f"{p}.block.4", 2 * dim, dim, 2 * stride)
+        dim *= 2
+    n = len(c["encoder_rates"])
+    specs.append((f"encoder.block.{n + 1}.alpha", (dim,), "alpha"))
+    conv(f"encoder.block.{n + 2}", c["latent_dim"], dim, 3)
+    return specs
+
+
+def make_encoder_params(config=None, seed=0):
+    """Encoder convolution-stack parameters, name -> float32 array (weights
+    v ~ N(0, 1) / sqrt(fan_in k) with g = ||v|| per output channel, biases
+    N(0, 0.01), alpha ~ U[0.5, 1.5])."""
+    rng = np.random.default_rng([seed, 4])
+    out = {}
+    last_v = None
+    for name, shape, kind in encoder_param_specs(config):
+        if kind == "v":
+            arr = rng.standard_normal(shape) / np.sqrt(shape[1] * shape[2])
+            last_v = arr
+        elif kind == "g":
+            arr = np.sqrt(np.sum(last_v * last_v, axis=(1, 2))).reshape(shape)
+        elif kind == "bias":
+            arr = rng.normal(0.0, 0.01, size=shape)
+        else:
+            arr = rng.uniform(0.5, 1.5, size=shape)
+        out[name] = np.ascontiguousarray(arr, dtype=np.float32)
+    return out
+
+
+def make_waveform(batch, samples, seed=0):
+    """Waveforms (batch, 1, samples) ~ N(0, 0.25) clipped to [-1, 1], float32."""
+    rng = np.random.default_rng([seed, 5, batch, samples])
+    return np.clip(0.5 * rng.standard_normal((batch, 1, samples)), -1.0, 1.0).astype(np.float32)

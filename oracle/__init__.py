@@ -15,11 +15,14 @@ from .mh3a_oracle import (  # noqa: F401
     decode_item,
     decode_window,
     downsample2,
+    encode_hidden,
+    encode_hidden_item,
     fold_weight_norm,
     kaiser_beta,
     kaiser_sinc_filter,
     kaiser_window,
     receptive_radius_latents,
+    snake,
     snake_beta,
     stage_amp,
     upsample2,

@@ -43,6 +43,20 @@ Readings of what the pages leave open (each is listed in the design doc):
 * R6 de-normalization, optional: z * std_c + mean_c (the convention the
   diffusers "AutoencoderKLMiniMaxH3" page states for its latents).
 * R7 ``decoder.conv_post.bias`` is read with ``w.get``: absent means zero.
+
+The encoder's convolution stack (``encode_hidden``: everything of
+``MLXMiniMaxH3AudioVAE.encode`` before the attention projection) follows
+the source of ``encode`` on the FastVideo page, with these readings:
+
+* E1 ``_snake(x, alpha)`` is not shown: the plain Snake
+  y = x + sin^2(alpha x) / (alpha + 1e-9), alpha per channel (the module
+  overview calls the encoder's residual units plain-Snake).
+* E2 the strided convolution's kernel is 2 x stride (not shown; the page
+  gives its stride and padding ceil(stride / 2)); the residual units'
+  second convolution has kernel 1 (no padding given); the final
+  convolution has kernel 3 (padding 1) and latent_dim output channels.
+* E3 the crop ``x[..., pad:-pad]`` never fires: every unit keeps the
+  length ("same" padding), so pad = 0.
 """
 
 from __future__ import annotations
@@ -66,6 +80,8 @@ DEFAULT_CONFIG = {
     "resblock_dilation_sizes": ((1, 3, 5), (1, 3, 5), (1, 3, 5)),
     "sampling_rate": 32000,
     "hop_length": 800,
+    "encoder_dim": 64,
+    "encoder_rates": (2, 4, 4, 5, 5),
     # Reading R4: BigVGAN's resampler, ratio 2.
     "filter_taps": 12,
     "filter_cutoff": 0.25,
@@ -153,22 +169,22 @@ def fold_weight_norm(v, g):
 # Convolutions (reading R1). x: (C_in, L) float32 for one batch item.
 # ---------------------------------------------------------------------------
 
-def conv1d(x, w, b=None, padding=0, dilation=1):
-    """y[o, t] = b[o] + sum_i sum_j w[o, i, j] x[i, t + j d - p], with x = 0
-    outside [0, L); output length L + 2p - d (k - 1)."""
+def conv1d(x, w, b=None, padding=0, dilation=1, stride=1):
+    """y[o, t] = b[o] + sum_i sum_j w[o, i, j] x[i, t s + j d - p], with x = 0
+    outside [0, L); output length floor((L + 2p - d (k - 1) - 1) / s) + 1."""
     x = np.asarray(x, dtype=F32)
     w = np.asarray(w, dtype=F32)
     c_out, c_in, k = w.shape
     assert x.shape[0] == c_in, (x.shape, w.shape)
     length = x.shape[1]
-    l_out = length + 2 * padding - dilation * (k - 1)
+    l_out = (length + 2 * padding - dilation * (k - 1) - 1) // stride + 1
     assert l_out >= 1
     xp = np.zeros((c_in, length + 2 * padding), dtype=F64)
     xp[:, padding:padding + length] = x
     taps = np.ascontiguousarray(np.moveaxis(w.astype(F64), 2, 0))  # (k, C_out, C_in)
     y = np.zeros((c_out, l_out), dtype=F64)
     for j in range(k):
-        y += taps[j] @ xp[:, j * dilation:j * dilation + l_out]
+        y += taps[j] @ xp[:, j * dilation:j * dilation + stride * (l_out - 1) + 1:stride]
     if b is not None:
         y += np.asarray(b, dtype=F64)[:, None]
     return y.astype(F32)
@@ -385,3 +401,66 @@ def decode_window(params, z, n0, n1, margin=None, config=None, denormalize=False
     b = min(n_total, n1 + margin)
     y = decode(params, z[:, :, a:b], cfg, denormalize, latents_mean, latents_std, clamp)
     return y[:, :, (n0 - a) * hop:(n1 - a) * hop]
+
+
+# ---------------------------------------------------------------------------
+# Encoder convolution stack (FastVideo "minimax_h3_audio_vae", source of
+# ``MLXMiniMaxH3AudioVAE.encode`` up to ``hidden``; readings E1-E3)
+# ---------------------------------------------------------------------------
+
+def snake(x, alpha):
+    """Plain Snake (reading E1): x + sin^2(alpha x) / (alpha + 1e-9), alpha
+    per channel of x (C, L)."""
+    x64 = np.asarray(x, dtype=F64)
+    a = np.asarray(alpha, dtype=F64).reshape(-1)[:, None]
+    return _f32(x64 + np.sin(a * x64) ** 2 / (a + 1e-9))
+
+
+def _enc_conv(params, prefix):
+    w = fold_weight_norm(params[prefix + ".weight_v"], params[prefix + ".weight_g"])
+    return w, params[prefix + ".bias"]
+
+
+def encode_hidden_item(params, wave, config=None):
+    """One waveform (S,) -> hidden (latent_dim, ceil(S / hop)): right zero
+    pad to a whole number of hops, k7 conv, then per stride s a block of
+    three plain-Snake residual units (dilations 1, 3, 9: snake, k7 dilated
+    conv, snake, k1 conv, add) followed by snake and a conv of kernel 2s,
+    stride s, padding ceil(s / 2) that doubles the width; last a snake and
+    a k3 conv."""
+    cfg = dict(DEFAULT_CONFIG, **(config or {}))
+    hop = int(np.prod(cfg["encoder_rates"]))
+    x = np.asarray(wave, dtype=F32).reshape(1, -1)
+    samples = x.shape[1]
+    right_pad = -(-samples // hop) * hop - samples
+    if right_pad:
+        x = np.concatenate([x, np.zeros((1, right_pad), dtype=F32)], axis=1)
+    w, b = _enc_conv(params, "encoder.block.0")
+    x = conv1d(x, w, b, padding=3)
+    for index, stride in enumerate(cfg["encoder_rates"], start=1):
+        prefix = f"encoder.block.{index}"
+        for unit, dilation in enumerate((1, 3, 9)):
+            p = f"{prefix}.block.{unit}"
+            r = snake(x, params[p + ".block.0.alpha"])
+            w, b = _enc_conv(params, p + ".block.1")
+            r = conv1d(r, w, b, padding=(7 - 1) * dilation // 2, dilation=dilation)
+            r = snake(r, params[p + ".block.2.alpha"])
+            w, b = _enc_conv(params, p + ".block.3")
+            r = conv1d(r, w, b)
+            assert r.shape == x.shape  # reading E3: no crop
+            x = _f32(x.astype(F64) + r.astype(F64))
+        x = snake(x, params[prefix + ".block.3.alpha"])
+        w, b = _enc_conv(params, prefix + ".block.4")
+        length = x.shape[1]
+        x = conv1d(x, w, b, stride=stride, padding=-(-stride // 2))
+        assert x.shape[1] * stride == length
+    n = len(cfg["encoder_rates"])
+    x = snake(x, params[f"encoder.block.{n + 1}.alpha"])
+    w, b = _enc_conv(params, f"encoder.block.{n + 2}")
+    return conv1d(x, w, b, padding=1)
+
+
+def encode_hidden(params, wave, config=None):
+    """Waveforms (B, 1, S) -> hidden (B, latent_dim, ceil(S / hop))."""
+    wave = np.asarray(wave, dtype=F32)
+    return np.stack([encode_hidden_item(params, wave[i].reshape(-1), config) for i in range(wave.shape[0])])

@@ -495,3 +495,120 @@ def test_amp_stage_matches_torch_composition(small_params, block):
     if block == 2:
         got = O.stage_amp(x, p, stage, SMALL_CONFIG)
         assert rel_l2(got, sum(outs) / 3) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Encoder convolution stack (FastVideo "minimax_h3_audio_vae", source of
+# MLXMiniMaxH3AudioVAE.encode up to `hidden`; readings E1-E3)
+# ---------------------------------------------------------------------------
+
+ENC_SMALL = {"encoder_dim": 4, "latent_dim": 16}
+
+
+@pytest.mark.parametrize("k,s,p,d", [(4, 2, 1, 1), (8, 4, 2, 1), (10, 5, 3, 1), (7, 1, 9, 3), (3, 2, 0, 2)])
+def test_conv1d_stride_matches_brute_force_and_torch(k, s, p, d):
+    rng = np.random.default_rng(k * 10 + s)
+    x = rng.standard_normal((3, 23)).astype(np.float32)
+    w = rng.standard_normal((2, 3, k)).astype(np.float32)
+    b = rng.standard_normal(2).astype(np.float32)
+    got = O.conv1d(x, w, b, padding=p, dilation=d, stride=s)
+    l_out = (23 + 2 * p - d * (k - 1) - 1) // s + 1
+    ref = np.zeros((2, l_out))
+    for o in range(2):
+        for t in range(l_out):
+            acc = float(b[o])
+            for i in range(3):
+                for j in range(k):
+                    n = t * s + j * d - p
+                    if 0 <= n < 23:
+                        acc += float(w[o, i, j]) * float(x[i, n])
+            ref[o, t] = acc
+    assert got.shape == ref.shape
+    np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
+    tref = F.conv1d(torch.from_numpy(x).double()[None], torch.from_numpy(w).double(), torch.from_numpy(b).double(),
+                    stride=s, padding=p, dilation=d)[0].numpy()
+    np.testing.assert_allclose(got, tref, rtol=1e-5, atol=1e-5)
+
+
+def test_snake_closed_forms():
+    alpha = np.array([1.0, 2.0, 0.5], dtype=np.float32)
+    x = np.array([[math.pi / 2], [math.pi / 4], [math.pi]], dtype=np.float32)   # sin(alpha x) = 1
+    np.testing.assert_allclose(O.snake(x, alpha)[:, 0], x[:, 0] + 1.0 / alpha, rtol=1e-6)
+    z = np.array([[math.pi], [math.pi / 2], [2 * math.pi]], dtype=np.float32)   # sin(alpha x) = 0
+    np.testing.assert_allclose(O.snake(z, alpha)[:, 0], z[:, 0], atol=1e-6)
+    np.testing.assert_array_equal(O.snake(np.zeros((3, 4), np.float32), alpha), np.zeros((3, 4), np.float32))
+
+
+def _torch_encode(params, wave, cfg):
+    """The encoder's steps composed from torch CPU float64 ops (conv1d with
+    stride / dilation / padding, torch's weight norm, Snake written out)."""
+    p = {k: torch.from_numpy(np.asarray(v)).double() for k, v in params.items()}
+
+    def wn(prefix):
+        return torch._weight_norm(p[prefix + ".weight_v"], p[prefix + ".weight_g"], 0)
+
+    def snake(x, a):
+        a = a.reshape(1, -1, 1)
+        return x + torch.sin(a * x) ** 2 / (a + 1e-9)
+
+    x = torch.from_numpy(wave).double()
+    hop = int(np.prod(cfg["encoder_rates"]))
+    pad = -(-x.shape[-1] // hop) * hop - x.shape[-1]
+    x = F.pad(x, (0, pad))
+    x = F.conv1d(x, wn("encoder.block.0"), p["encoder.block.0.bias"], padding=3)
+    for i, s in enumerate(cfg["encoder_rates"], start=1):
+        for u, d in enumerate((1, 3, 9)):
+            q = f"encoder.block.{i}.block.{u}"
+            r = snake(x, p[q + ".block.0.alpha"])
+            r = F.conv1d(r, wn(q + ".block.1"), p[q + ".block.1.bias"], padding=3 * d, dilation=d)
+            r = snake(r, p[q + ".block.2.alpha"])
+            r = F.conv1d(r, wn(q + ".block.3"), p[q + ".block.3.bias"])
+            x = x + r
+        x = snake(x, p[f"encoder.block.{i}.block.3.alpha"])
+        x = F.conv1d(x, wn(f"encoder.block.{i}.block.4"), p[f"encoder.block.{i}.block.4.bias"], stride=s,
+                     padding=math.ceil(s / 2))
+    n = len(cfg["encoder_rates"])
+    x = snake(x, p[f"encoder.block.{n + 1}.alpha"])
+    return F.conv1d(x, wn(f"encoder.block.{n + 2}"), p[f"encoder.block.{n + 2}.bias"], padding=1).numpy()
+
+
+def test_encode_hidden_matches_torch_composition():
+    cfg = dict(O.DEFAULT_CONFIG, **ENC_SMALL)
+    params = synth.make_encoder_params(ENC_SMALL, seed=3)
+    wave = synth.make_waveform(2, 2 * 800 + 37, seed=3)
+    got = O.encode_hidden(params, wave, ENC_SMALL)
+    ref = _torch_encode(params, wave, cfg)
+    assert got.shape == (2, 16, 3)
+    # the oracle rounds every layer's output to fp32 (about 40 of them)
+    assert rel_l2(got, ref) < 3e-5
+
+
+def test_encode_hidden_length_law_and_right_pad():
+    params = synth.make_encoder_params(ENC_SMALL, seed=1)
+    wave = synth.make_waveform(1, 1601, seed=1)
+    h = O.encode_hidden(params, wave, ENC_SMALL)
+    assert h.shape == (1, 16, 3)
+    padded = np.concatenate([wave, np.zeros((1, 1, 799), np.float32)], axis=2)
+    np.testing.assert_array_equal(O.encode_hidden(params, padded, ENC_SMALL), h)
+    assert O.encode_hidden(params, wave[:, :, :1600], ENC_SMALL).shape == (1, 16, 2)
+
+
+def test_encode_hidden_depends_on_a_finite_window():
+    # Latent 0 reaches at most ~8.7 k samples past its own 800: perturbing
+    # the last 2400 of 16 latents' samples leaves it unchanged, latent 15 not.
+    params = synth.make_encoder_params(ENC_SMALL, seed=2)
+    wave = synth.make_waveform(1, 16 * 800, seed=2)
+    h = O.encode_hidden(params, wave, ENC_SMALL)
+    w2 = wave.copy()
+    w2[:, :, -2400:] += 0.25
+    h2 = O.encode_hidden(params, w2, ENC_SMALL)
+    np.testing.assert_array_equal(h2[:, :, 0], h[:, :, 0])
+    assert np.max(np.abs(h2[:, :, 15] - h[:, :, 15])) > 1e-3
+
+
+def test_encode_hidden_batch_items_independent():
+    params = synth.make_encoder_params(ENC_SMALL, seed=4)
+    wave = synth.make_waveform(3, 1600, seed=4)
+    h = O.encode_hidden(params, wave, ENC_SMALL)
+    for i in range(3):
+        np.testing.assert_array_equal(h[i], O.encode_hidden_item(params, wave[i, 0], ENC_SMALL))
