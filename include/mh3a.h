@@ -249,13 +249,73 @@ typedef struct {
     double flops;
     double bytes;
 } mh3a_kernel_stats;
-#define MH3A_MAX_KERNEL_KINDS 8
+#define MH3A_MAX_KERNEL_KINDS 16
 #define MH3A_TIMING_OFF 0
 #define MH3A_TIMING_ALL 1
 #define MH3A_TIMING_AMP_CONV 2
 /* enable: one of MH3A_TIMING_*; other values are MH3A_E_INVALID_ARG. */
 int mh3a_timing_enable(mh3a_decoder* dec, int enable);
 int mh3a_timing_read(mh3a_decoder* dec, mh3a_kernel_stats* stats, int max_stats, int* n_stats);
+
+/*
+ * Encoder convolution stack: waveform (B, 1, S) -> hidden (B, latent_dim,
+ * F), F = ceil(S / hop), hop = product of the rates. Source: FastVideo API
+ * docs "minimax_h3_audio_vae", the source of MLXMiniMaxH3AudioVAE.encode up
+ * to the hidden state that feeds its attention projection (module overview:
+ * a DAC-style encoder with plain-Snake residual units):
+ *   right zero pad to F * hop samples; weight-normalized conv 1 -> dim, k7,
+ *   pad 3; per rate s: three residual units (dilation 1, 3, 9) of
+ *   x + conv_k1(snake(conv_k7_dil(snake(x)))) (k7 padded 3 * dilation),
+ *   then snake and a conv dim -> 2 dim of kernel 2 s, stride s, padding
+ *   ceil(s / 2); then snake and a conv -> latent_dim of kernel 3, pad 1.
+ *   snake(x) = x + sin^2(alpha x) / (alpha + 1e-9), alpha per channel.
+ * The page leaves the Snake form, the strided kernel (2 s), the unit's
+ * second kernel (1) and the final kernel (3) implicit; those are the
+ * readings taken here.
+ *
+ * Parameters (i = 1 .. num_blocks, u = 0 .. 2, dim_i = encoder_dim 2^(i-1)):
+ *   encoder.block.0.{weight_v (dim, 1, 7), weight_g, bias}
+ *   encoder.block.{i}.block.{u}.block.{0,2}.alpha (dim_i)
+ *   encoder.block.{i}.block.{u}.block.1.{weight_v (dim_i, dim_i, 7), weight_g, bias}
+ *   encoder.block.{i}.block.{u}.block.3.{weight_v (dim_i, dim_i, 1), weight_g, bias}
+ *   encoder.block.{i}.block.3.alpha (dim_i)
+ *   encoder.block.{i}.block.4.{weight_v (2 dim_i, dim_i, 2 s_i), weight_g, bias}
+ *   encoder.block.{n+1}.alpha (encoder_dim 2^n), encoder.block.{n+2}.{weight_v
+ *     (latent_dim, encoder_dim 2^n, 3), weight_g, bias}
+ * (a folded `weight` may replace each weight_v / weight_g pair).
+ *
+ * Conventions as for the decoder: fp32 C-contiguous tensors, device
+ * pointers borrowed, work only enqueued on `stream`, a 256-byte aligned
+ * device workspace of at least mh3a_encode_workspace_size bytes (clobbered;
+ * concurrent calls need distinct workspaces). Flags: 0 or
+ * MH3A_FLAG_BATCH_INVARIANT. Errors: MH3A_E_INVALID_ARG (null, sizes,
+ * flags), MH3A_E_CONFIG, MH3A_E_MISSING_TENSOR, MH3A_E_SHAPE,
+ * MH3A_E_WORKSPACE, MH3A_E_HIP, MH3A_E_NOMEM.
+ */
+#define MH3A_MAX_ENC_BLOCKS 8
+typedef struct mh3a_encoder mh3a_encoder; /* opaque, immutable after create */
+typedef struct {
+    int encoder_dim;                  /* channels after the first conv (64) */
+    int num_blocks;                   /* strided blocks (5) */
+    int rates[MH3A_MAX_ENC_BLOCKS];   /* their strides (2, 4, 4, 5, 5) */
+    int latent_dim;                   /* hidden channels (2048) */
+} mh3a_encoder_config;
+void mh3a_encoder_config_default(mh3a_encoder_config* cfg);
+int mh3a_encoder_create(const mh3a_encoder_config* cfg, const mh3a_tensor* params, int n_params, int device,
+                        mh3a_encoder** out);
+/* NULL is a no-op; waits for the device first. */
+void mh3a_encoder_destroy(mh3a_encoder* enc);
+/* F = ceil(samples / hop). */
+int mh3a_encode_frames(const mh3a_encoder* enc, int64_t samples, int64_t* frames);
+int mh3a_encode_workspace_size(const mh3a_encoder* enc, int64_t batch, int64_t samples, uint32_t flags,
+                               size_t* bytes);
+/* wave: device (B, 1, samples); hidden: device (B, latent_dim, F). */
+int mh3a_encode_hidden(mh3a_encoder* enc, const float* wave, int64_t batch, int64_t samples, float* hidden,
+                       void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+/* Kernel timing as mh3a_timing_enable / mh3a_timing_read (MH3A_TIMING_AMP_CONV
+ * selects the residual units' k7 convs). */
+int mh3a_encoder_timing_enable(mh3a_encoder* enc, int enable);
+int mh3a_encoder_timing_read(mh3a_encoder* enc, mh3a_kernel_stats* stats, int max_stats, int* n_stats);
 
 /* Message of the calling thread's last failure ("" if none). */
 const char* mh3a_last_error(void);

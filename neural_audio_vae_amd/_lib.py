@@ -48,6 +48,14 @@ EXPORTED = (
     "mh3a_timing_enable",
     "mh3a_timing_read",
     "mh3a_last_error",
+    "mh3a_encoder_config_default",
+    "mh3a_encoder_create",
+    "mh3a_encoder_destroy",
+    "mh3a_encode_frames",
+    "mh3a_encode_workspace_size",
+    "mh3a_encode_hidden",
+    "mh3a_encoder_timing_enable",
+    "mh3a_encoder_timing_read",
 )
 
 
@@ -74,12 +82,20 @@ class mh3a_config(Structure):
     ]
 
 
+MH3A_MAX_ENC_BLOCKS = 8
+
+
+class mh3a_encoder_config(Structure):
+    _fields_ = [("encoder_dim", c_int), ("num_blocks", c_int), ("rates", c_int * MH3A_MAX_ENC_BLOCKS),
+                ("latent_dim", c_int)]
+
+
 class mh3a_kernel_stats(Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("launches", c_int64), ("ms", c_double), ("flops", c_double),
                 ("bytes", c_double)]
 
 
-MH3A_MAX_KERNEL_KINDS = 8
+MH3A_MAX_KERNEL_KINDS = 16
 
 
 class MH3AError(RuntimeError):
@@ -134,6 +150,24 @@ def load():
     lib.mh3a_timing_read.restype = c_int
     lib.mh3a_last_error.argtypes = []
     lib.mh3a_last_error.restype = c_char_p
+    lib.mh3a_encoder_config_default.argtypes = [POINTER(mh3a_encoder_config)]
+    lib.mh3a_encoder_config_default.restype = None
+    lib.mh3a_encoder_create.argtypes = [POINTER(mh3a_encoder_config), POINTER(mh3a_tensor), c_int, c_int,
+                                        POINTER(c_void_p)]
+    lib.mh3a_encoder_create.restype = c_int
+    lib.mh3a_encoder_destroy.argtypes = [c_void_p]
+    lib.mh3a_encoder_destroy.restype = None
+    lib.mh3a_encode_frames.argtypes = [c_void_p, c_int64, POINTER(c_int64)]
+    lib.mh3a_encode_frames.restype = c_int
+    lib.mh3a_encode_workspace_size.argtypes = [c_void_p, c_int64, c_int64, c_uint32, POINTER(c_size_t)]
+    lib.mh3a_encode_workspace_size.restype = c_int
+    lib.mh3a_encode_hidden.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_uint32,
+                                       c_void_p]
+    lib.mh3a_encode_hidden.restype = c_int
+    lib.mh3a_encoder_timing_enable.argtypes = [c_void_p, c_int]
+    lib.mh3a_encoder_timing_enable.restype = c_int
+    lib.mh3a_encoder_timing_read.argtypes = [c_void_p, POINTER(mh3a_kernel_stats), c_int, POINTER(c_int)]
+    lib.mh3a_encoder_timing_read.restype = c_int
     _lib = lib
     return lib
 
@@ -196,12 +230,10 @@ def make_config(overrides=None):
     return cfg
 
 
-def mh3a_decoder_create(config, arrays, latents_mean=None, latents_std=None, device=0):
-    """config: mh3a_config; arrays: dict name -> C-contiguous float32 numpy
-    array (kept alive by the caller for the duration of the call)."""
+def _tensor_table(arrays):
+    """(mh3a_tensor array, count, numpy arrays to keep alive) for a dict of arrays."""
     import numpy as np
 
-    lib = load()
     items = list(arrays.items())
     table = (mh3a_tensor * max(1, len(items)))()
     keep = []
@@ -215,6 +247,16 @@ def mh3a_decoder_create(config, arrays, latents_mean=None, latents_std=None, dev
         table[i].ndim = a.ndim
         for k in range(3):
             table[i].shape[k] = a.shape[k] if k < a.ndim else 1
+    return table, len(items), keep
+
+
+def mh3a_decoder_create(config, arrays, latents_mean=None, latents_std=None, device=0):
+    """config: mh3a_config; arrays: dict name -> C-contiguous float32 numpy
+    array (kept alive by the caller for the duration of the call)."""
+    import numpy as np
+
+    lib = load()
+    table, n_items, keep = _tensor_table(arrays)
     mean = std = None
     if latents_mean is not None:
         mean = np.ascontiguousarray(latents_mean, dtype=np.float32)
@@ -223,7 +265,7 @@ def mh3a_decoder_create(config, arrays, latents_mean=None, latents_std=None, dev
         std = np.ascontiguousarray(latents_std, dtype=np.float32)
         keep.append(std)
     handle = c_void_p()
-    _check(lib.mh3a_decoder_create(byref(config), table, len(items), mean.ctypes.data if mean is not None else None,
+    _check(lib.mh3a_decoder_create(byref(config), table, n_items, mean.ctypes.data if mean is not None else None,
                                    std.ctypes.data if std is not None else None, int(device), byref(handle)))
     return handle.value
 
@@ -294,5 +336,70 @@ def mh3a_timing_read(handle):
     arr = (mh3a_kernel_stats * MH3A_MAX_KERNEL_KINDS)()
     n = c_int()
     _check(load().mh3a_timing_read(handle, arr, MH3A_MAX_KERNEL_KINDS, byref(n)))
+    return {arr[i].name.decode(): {"launches": arr[i].launches, "ms": arr[i].ms, "flops": arr[i].flops,
+                                   "bytes": arr[i].bytes} for i in range(n.value)}
+
+
+def mh3a_encoder_config_default():
+    cfg = mh3a_encoder_config()
+    load().mh3a_encoder_config_default(byref(cfg))
+    return cfg
+
+
+def make_encoder_config(overrides=None):
+    """An mh3a_encoder_config from the defaults plus encoder_dim,
+    encoder_rates and latent_dim overrides."""
+    cfg = mh3a_encoder_config_default()
+    o = dict(overrides or {})
+    for key in ("encoder_dim", "latent_dim"):
+        if key in o:
+            setattr(cfg, key, int(o[key]))
+    if "encoder_rates" in o:
+        rates = [int(r) for r in o["encoder_rates"]]
+        if len(rates) > MH3A_MAX_ENC_BLOCKS:
+            raise ValueError("at most 8 encoder rates")
+        cfg.num_blocks = len(rates)
+        for i in range(MH3A_MAX_ENC_BLOCKS):
+            cfg.rates[i] = rates[i] if i < len(rates) else 0
+    return cfg
+
+
+def mh3a_encoder_create(config, arrays, device=0):
+    table, n, keep = _tensor_table(arrays)
+    handle = c_void_p()
+    _check(load().mh3a_encoder_create(byref(config), table, n, int(device), byref(handle)))
+    del keep
+    return handle.value
+
+
+def mh3a_encoder_destroy(handle):
+    load().mh3a_encoder_destroy(handle)
+
+
+def mh3a_encode_frames(handle, samples):
+    f = c_int64()
+    _check(load().mh3a_encode_frames(handle, samples, byref(f)))
+    return f.value
+
+
+def mh3a_encode_workspace_size(handle, batch, samples, flags=0):
+    n = c_size_t()
+    _check(load().mh3a_encode_workspace_size(handle, batch, samples, flags, byref(n)))
+    return n.value
+
+
+def mh3a_encode_hidden(handle, wave_ptr, batch, samples, hidden_ptr, workspace_ptr, workspace_bytes, flags, stream):
+    return _check(load().mh3a_encode_hidden(handle, wave_ptr, batch, samples, hidden_ptr, workspace_ptr,
+                                            workspace_bytes, flags, stream))
+
+
+def mh3a_encoder_timing_enable(handle, mode):
+    return _check(load().mh3a_encoder_timing_enable(handle, int(mode)))
+
+
+def mh3a_encoder_timing_read(handle):
+    arr = (mh3a_kernel_stats * MH3A_MAX_KERNEL_KINDS)()
+    n = c_int()
+    _check(load().mh3a_encoder_timing_read(handle, arr, MH3A_MAX_KERNEL_KINDS, byref(n)))
     return {arr[i].name.decode(): {"launches": arr[i].launches, "ms": arr[i].ms, "flops": arr[i].flops,
                                    "bytes": arr[i].bytes} for i in range(n.value)}

@@ -160,10 +160,15 @@ enum Kind {
     KIND_FINAL,
     KIND_AMP_UNIT,
     KIND_SPLIT,
+    KIND_ENC_UNIT_CONV,  // encoder: the residual units' dilated k7 convs
+    KIND_ENC_CONV,       // encoder: pointwise, strided, first and last convs
+    KIND_ENC_SNAKE,      // encoder: Snake (and space-to-depth) passes
     KIND_COUNT
 };
-const char* const kKindNames[KIND_COUNT] = {"dec_in_proj", "conv_pre", "ups_transposed_conv", "amp_conv", "amp_act",
-                                            "act_post_conv_post", "amp_unit", "input_split"};
+const char* const kKindNames[KIND_COUNT] = {"dec_in_proj", "conv_pre",   "ups_transposed_conv", "amp_conv",
+                                            "amp_act",     "act_post_conv_post", "amp_unit", "input_split",
+                                            "enc_unit_conv", "enc_conv", "enc_snake"};
+static_assert(KIND_COUNT <= MH3A_MAX_KERNEL_KINDS, "timing classes fit mh3a_timing_read's table");
 
 struct TimingRec {
     int kind;
@@ -189,25 +194,30 @@ struct ActLayer {
 // Launch shape of one conv: (layer, positions, batch, bf16 operands | batch-invariant plan << 1).
 using PlanKey = std::tuple<const void*, int, int, int>;
 
-struct mh3a_decoder {
-    mh3a_config cfg;
+// What the launch helpers need of a decoder or an encoder: the device, the
+// parameter blob, activation constants, timing state and the plan cache.
+struct mh3a_net {
     int device = 0;
     float* blob = nullptr;
     int64_t blob_floats = 0;
+    std::vector<ActLayer> acts;
+    int num_cus = 256;          // compute units of `device`
+    mutable Timing timing;
+    mutable std::mutex plan_mu;                          // guards plans
+    mutable std::map<PlanKey, std::pair<int, int>> plans;  // (tile, ksplit) per launch shape
+};
+
+struct mh3a_decoder : mh3a_net {
+    mh3a_config cfg;
     ConvLayer in_proj, in_proj_dn, conv_pre;
     std::vector<ConvLayer> ups;                 // [num_ups]
     std::vector<std::vector<ConvLayer>> amp;    // [stage][(block * ndil + d) * 2 + {0,1}]
-    std::vector<ActLayer> acts;
     int post_act = -1;
     int64_t post_w_off = -1;
     float post_bias = 0.0f;
     std::vector<int> stage_c;   // output channels per stage
-    int num_cus = 256;          // compute units of `device`
     bool pk_ok = false;         // every AMP conv can read a packed activated input
     bool bx6_ok = false;        // ... and has split-product weights (see kPieces)
-    mutable Timing timing;
-    mutable std::mutex plan_mu;                          // guards plans
-    mutable std::map<PlanKey, std::pair<int, int>> plans;  // (tile, ksplit) per launch shape
 };
 
 namespace {
@@ -365,7 +375,7 @@ int add_act(Blob& blob, const Table& t, const std::string& prefix, int c, const 
     return MH3A_OK;
 }
 
-ActParams act_params(const mh3a_decoder* d, int idx) {
+ActParams act_params(const mh3a_net* d, int idx) {
     ActParams p{nullptr, nullptr};
     if (idx >= 0) {
         p.taps = d->blob + d->acts[idx].taps_off;
@@ -388,13 +398,14 @@ int64_t plan_partial_floats(const ConvLayer& L, int positions, int groups, const
 // Whether packed AMP inputs take the split-product form (bf16 pieces and
 // six-way products on bf16 matrix cores, fp32-level accuracy; see kPieces).
 // MH3A_BX6=0 selects the fp32 matrix-core form (a tuning aid).
-bool use_bx6(const mh3a_decoder* d) {
+bool bx6_disabled() {
     static const bool off = [] {
         const char* e = std::getenv("MH3A_BX6");
         return e && !std::strcmp(e, "0");
     }();
-    return d->bx6_ok && !off;
+    return off;
 }
+bool use_bx6(const mh3a_decoder* d) { return d->bx6_ok && !bx6_disabled(); }
 
 // Whether an AMP conv of a (batch, C, L) activation fuses its activation.
 // Fused, the producer waves compute it per tile on the SIMDs whose matrix
@@ -435,7 +446,7 @@ bool stage_px(const mh3a_decoder* d, int64_t batch, int c, int64_t len, bool bf1
 bool pre_bx6(const mh3a_decoder* d, const ConvLayer& L) { return use_bx6(d) && L.w6_off >= 0; }
 
 // Plans are cached per launch shape.
-ConvPlan plan_conv(const mh3a_decoder* d, const ConvLayer& L, int positions, int batch, bool bf16, bool invariant,
+ConvPlan plan_conv(const mh3a_net* d, const ConvLayer& L, int positions, int batch, bool bf16, bool invariant,
                    bool fused, bool bx6 = false) {
     const PlanKey key{&L, positions, batch, (bf16 ? 1 : 0) | (invariant ? 2 : 0) | (fused ? 4 : 0) | (bx6 ? 8 : 0)};
     std::lock_guard<std::mutex> lock(d->plan_mu);
@@ -468,12 +479,12 @@ struct Buf {
 
 // Brackets a launch with timing events when timing is enabled.
 struct TimedLaunch {
-    const mh3a_decoder* d;
+    const mh3a_net* d;
     hipStream_t st;
     int ev = -1;
-    TimedLaunch(const mh3a_decoder* d_, hipStream_t st_, int kind) : d(d_), st(st_) {
+    TimedLaunch(const mh3a_net* d_, hipStream_t st_, int kind) : d(d_), st(st_) {
         Timing& t = d->timing;
-        if (!t.on || (t.amp_only && kind != KIND_AMP)) return;
+        if (!t.on || (t.amp_only && kind != KIND_AMP && kind != KIND_ENC_UNIT_CONV)) return;
         while ((int)t.evs.size() < t.used + 2) {
             hipEvent_t e;
             // timing-only events: no system-scope fence (no cache writeback between launches)
@@ -493,7 +504,7 @@ struct TimedLaunch {
 };
 
 // `partial` holds at least the plan's partial sums (plan_partial_floats).
-hipError_t run_conv(const mh3a_decoder* d, const ConvLayer& L, const float* x, int64_t x_bstride, int l_in,
+hipError_t run_conv(const mh3a_net* d, const ConvLayer& L, const float* x, int64_t x_bstride, int l_in,
                     int positions, float* y, int64_t y_bstride, int batch, const float* res, const float* sum_in,
                     float scale, bool bf16, bool invariant, bool fused, float* partial, hipStream_t st,
                     int pk_lp = 0, bool bx6 = false) {
@@ -977,6 +988,52 @@ int chunked_ws_bytes(const mh3a_decoder* d, int64_t batch, int64_t frames, int64
     return MH3A_OK;
 }
 
+// Timing state of a decoder or an encoder (mh3a_timing_enable / _read).
+int timing_enable(mh3a_net* d, int enable) {
+    if (!d) return fail(MH3A_E_INVALID_ARG, "handle is null");
+    if (enable < 0 || enable > MH3A_TIMING_AMP_CONV) return fail(MH3A_E_INVALID_ARG, "bad timing mode %d", enable);
+    d->timing.on = enable != 0;
+    d->timing.amp_only = enable == MH3A_TIMING_AMP_CONV;
+    d->timing.used = 0;
+    d->timing.recs.clear();
+    return ok();
+}
+
+int timing_read(mh3a_net* d, mh3a_kernel_stats* stats, int max_stats, int* n_stats) {
+    if (!d || !n_stats || (max_stats > 0 && !stats)) return fail(MH3A_E_INVALID_ARG, "null argument");
+    *n_stats = 0;
+    Timing& t = d->timing;
+    std::vector<int> order;
+    double ms[KIND_COUNT] = {0}, fl[KIND_COUNT] = {0}, by[KIND_COUNT] = {0};
+    int64_t cnt[KIND_COUNT] = {0};
+    HIP_TRY(hipSetDevice(d->device));
+    for (const TimingRec& r : t.recs) {
+        HIP_TRY(hipEventSynchronize(t.evs[r.ev + 1]));
+        float e = 0.0f;
+        HIP_TRY(hipEventElapsedTime(&e, t.evs[r.ev], t.evs[r.ev + 1]));
+        if (cnt[r.kind] == 0) order.push_back(r.kind);
+        ms[r.kind] += e;
+        fl[r.kind] += r.flops;
+        by[r.kind] += r.bytes;
+        cnt[r.kind] += 1;
+    }
+    t.recs.clear();
+    t.used = 0;
+    int n = 0;
+    for (int k : order) {
+        if (n >= max_stats) break;
+        mh3a_kernel_stats& o = stats[n++];
+        std::memset(&o, 0, sizeof o);
+        std::snprintf(o.name, sizeof o.name, "%s", kKindNames[k]);
+        o.launches = cnt[k];
+        o.ms = ms[k];
+        o.flops = fl[k];
+        o.bytes = by[k];
+    }
+    *n_stats = n;
+    return ok();
+}
+
 }  // namespace
 
 namespace mh3a {
@@ -1375,49 +1432,9 @@ void mh3a_destroy(mh3a_decoder* d) {
     delete d;
 }
 
-int mh3a_timing_enable(mh3a_decoder* d, int enable) {
-    if (!d) return fail(MH3A_E_INVALID_ARG, "decoder is null");
-    if (enable < 0 || enable > MH3A_TIMING_AMP_CONV) return fail(MH3A_E_INVALID_ARG, "bad timing mode %d", enable);
-    d->timing.on = enable != 0;
-    d->timing.amp_only = enable == MH3A_TIMING_AMP_CONV;
-    d->timing.used = 0;
-    d->timing.recs.clear();
-    return ok();
-}
-
+int mh3a_timing_enable(mh3a_decoder* d, int enable) { return timing_enable(d, enable); }
 int mh3a_timing_read(mh3a_decoder* d, mh3a_kernel_stats* stats, int max_stats, int* n_stats) {
-    if (!d || !n_stats || (max_stats > 0 && !stats)) return fail(MH3A_E_INVALID_ARG, "null argument");
-    *n_stats = 0;
-    Timing& t = d->timing;
-    std::vector<int> order;
-    double ms[KIND_COUNT] = {0}, fl[KIND_COUNT] = {0}, by[KIND_COUNT] = {0};
-    int64_t cnt[KIND_COUNT] = {0};
-    HIP_TRY(hipSetDevice(d->device));
-    for (const TimingRec& r : t.recs) {
-        HIP_TRY(hipEventSynchronize(t.evs[r.ev + 1]));
-        float e = 0.0f;
-        HIP_TRY(hipEventElapsedTime(&e, t.evs[r.ev], t.evs[r.ev + 1]));
-        if (cnt[r.kind] == 0) order.push_back(r.kind);
-        ms[r.kind] += e;
-        fl[r.kind] += r.flops;
-        by[r.kind] += r.bytes;
-        cnt[r.kind] += 1;
-    }
-    t.recs.clear();
-    t.used = 0;
-    int n = 0;
-    for (int k : order) {
-        if (n >= max_stats) break;
-        mh3a_kernel_stats& o = stats[n++];
-        std::memset(&o, 0, sizeof o);
-        std::snprintf(o.name, sizeof o.name, "%s", kKindNames[k]);
-        o.launches = cnt[k];
-        o.ms = ms[k];
-        o.flops = fl[k];
-        o.bytes = by[k];
-    }
-    *n_stats = n;
-    return ok();
+    return timing_read(d, stats, max_stats, n_stats);
 }
 
 int mh3a_decode_workspace_size(const mh3a_decoder* d, int64_t batch, int64_t frames, uint32_t flags, size_t* bytes) {
@@ -1558,6 +1575,393 @@ int mh3a_amp_stage(mh3a_decoder* d, int stage, const float* x, int64_t batch, in
                  (flags & MH3A_FLAG_BATCH_INVARIANT) != 0, part, static_cast<hipStream_t>(stream));
     if (rc) return rc;
     return ok();
+}
+
+}  // extern "C"
+
+// ===========================================================================
+// Encoder convolution stack (FastVideo "minimax_h3_audio_vae", source of
+// MLXMiniMaxH3AudioVAE.encode up to the hidden state; module overview: the
+// DAC-style encoder of plain-Snake residual units): waveform (B, 1, S) ->
+// hidden (B, latent_dim, ceil(S / hop)).
+//
+// Each strided conv (kernel 2s, stride s, padding p = ceil(s / 2)) runs as a
+// 2-tap, stride-1 conv over a space-to-depth regrouping of its Snake input:
+// channel c s + r at position t holds snake(x)[c, t s + r - p], so output t
+// reads positions t and t + 1 with the weight w[o, c, j s + r] at tap j.
+// ===========================================================================
+
+struct SnakeLayer {
+    int c = 0;
+    int64_t alpha_off = -1, inv_off = -1;
+};
+
+struct mh3a_encoder : mh3a_net {
+    mh3a_encoder_config cfg;
+    ConvLayer conv_in;                 // 1 -> dim, k7, pad 3
+    std::vector<ConvLayer> unit_conv;  // [block][unit][k7 dilated, k1]: (block * 3 + unit) * 2 + {0, 1}
+    std::vector<ConvLayer> down;       // [block]: the strided conv as a 2-tap conv over C s channels
+    ConvLayer conv_out;                // final k3, pad 1
+    std::vector<SnakeLayer> snakes;    // [block][unit][0, 1], then [block] before `down`, then the final one
+    std::vector<int> block_c;          // input channels of each block
+    int hop = 1;
+};
+
+namespace {
+
+constexpr int kEncDils[3] = {1, 3, 9};
+
+int enc_check_config(const mh3a_encoder_config* c) {
+    if (c->encoder_dim < 1 || c->latent_dim < 1) return fail(MH3A_E_CONFIG, "channel counts must be positive");
+    if (c->num_blocks < 1 || c->num_blocks > MH3A_MAX_ENC_BLOCKS)
+        return fail(MH3A_E_CONFIG, "num_blocks must be in [1, %d]", MH3A_MAX_ENC_BLOCKS);
+    int64_t hop = 1, dim = c->encoder_dim;
+    for (int i = 0; i < c->num_blocks; ++i) {
+        if (c->rates[i] < 1 || c->rates[i] > 16) return fail(MH3A_E_CONFIG, "rate %d of block %d out of [1, 16]", c->rates[i], i);
+        hop *= c->rates[i];
+        dim *= 2;
+    }
+    if (hop > 65536 || dim > 65536) return fail(MH3A_E_CONFIG, "encoder hop or width too large");
+    return MH3A_OK;
+}
+
+int build_table(const mh3a_tensor* params, int n_params, Table& t) {
+    for (int i = 0; i < n_params; ++i) {
+        const mh3a_tensor& p = params[i];
+        if (!p.name || !p.data) return fail(MH3A_E_INVALID_ARG, "parameter %d has a null name or data", i);
+        if (p.ndim < 1 || p.ndim > 3) return fail(MH3A_E_SHAPE, "%s: ndim must be 1..3", p.name);
+        Param q;
+        q.data = p.data;
+        q.ndim = p.ndim;
+        for (int k = 0; k < 3; ++k) q.shape[k] = k < p.ndim ? p.shape[k] : 1;
+        for (int k = 0; k < p.ndim; ++k)
+            if (q.shape[k] < 1) return fail(MH3A_E_SHAPE, "%s: non-positive dimension", p.name);
+        t.m[p.name] = q;
+    }
+    return MH3A_OK;
+}
+
+// Whether a conv of the encoder can take the split-product packed input.
+bool enc_split_ok(const ConvLayer& L) {
+    const bool taps_ok = L.taps == 1 || L.taps == 2 || L.taps == 3 || (L.taps == 7 && L.dil <= kBx6WideDil) ||
+                         (L.taps == 11 && L.dil <= kBx6MaxDil);
+    if (!taps_ok || L.c_in % 16 || L.c_out < 32 || L.dil < 1) return false;
+    return -L.in_off[0] <= kPkPadL && 255 + (L.taps - 1) * L.dil + L.in_off[0] <= kPkPadR;
+}
+
+// A weight-normalized conv of the encoder: fp32 packing always, split-product
+// pieces where the packed path serves it.
+int enc_conv(Blob& blob, const Table& t, const std::string& prefix, ConvLayer& L, int c_out, int c_in, int k, int dil,
+             int pad, int kind) {
+    std::vector<float> w;
+    const float* bias = nullptr;
+    int rc = fetch_weight(t, prefix, c_out, c_in, k, w);
+    if (rc) return rc;
+    if ((rc = fetch_vector(t, prefix + ".bias", c_out, &bias))) return rc;
+    add_conv(blob, L, w, bias, c_out, c_in, k);
+    L.dil = dil;
+    L.in_off[0] = -pad;
+    L.alg_taps = k;
+    L.kind = kind;
+    if (enc_split_ok(L)) {
+        L.w6_off = blob.reserve(packed_weight_floats6(c_out, c_in, k));
+        pack_conv_weights6(w.data(), c_out, c_in, k, blob.h.data() + L.w6_off);
+    }
+    return MH3A_OK;
+}
+
+int enc_snake_layer(Blob& blob, const Table& t, const std::string& name, int c, std::vector<SnakeLayer>& out) {
+    const float* alpha = nullptr;
+    int rc = fetch_vector(t, name, c, &alpha);
+    if (rc) return rc;
+    std::vector<float> inv(c);
+    for (int i = 0; i < c; ++i) inv[i] = (float)(1.0 / ((double)alpha[i] + 1e-9));
+    SnakeLayer S;
+    S.c = c;
+    S.alpha_off = blob.add(alpha, c);
+    S.inv_off = blob.add(inv.data(), c);
+    out.push_back(S);
+    return MH3A_OK;
+}
+
+bool enc_bx6(const ConvLayer& L) { return L.w6_off >= 0 && !bx6_disabled(); }
+
+// Per-item lengths: S' = frames * hop samples after the right pad; block i
+// runs at L_i = S' / (r_0 ... r_{i-1}) positions.
+int64_t enc_frames(const mh3a_encoder* e, int64_t samples) { return (samples + e->hop - 1) / e->hop; }
+
+// Floats of one Snake output (per item) feeding conv L over l_out positions.
+int64_t enc_snake_item_floats(const ConvLayer& L, int64_t l_out) {
+    if (enc_bx6(L)) return (int64_t)((L.c_in + kChunk - 1) / kChunk) * kPieces * 4 * pk_lp(l_out);
+    return (int64_t)L.c_in * l_out;
+}
+
+struct EncWs {
+    int64_t x, r, p, partial;  // floats of each region (all items)
+};
+
+EncWs enc_ws_floats(const mh3a_encoder* e, int64_t batch, int64_t frames, bool inv) {
+    EncWs w{0, 0, 0, 0};
+    int64_t len = frames * e->hop;
+    auto part = [&](const ConvLayer& L, int64_t positions) {
+        const bool bx6 = enc_bx6(L);
+        const ConvPlan pl = plan_conv(e, L, (int)positions, (int)batch, false, inv, true, bx6);
+        w.partial = std::max(w.partial, plan_partial_floats(L, (int)positions, (int)batch, pl, true));
+    };
+    w.x = (int64_t)e->cfg.encoder_dim * len;
+    part(e->conv_in, len);
+    for (int i = 0; i < e->cfg.num_blocks; ++i) {
+        const int C = e->block_c[i], s = e->cfg.rates[i];
+        w.x = std::max(w.x, (int64_t)C * len);
+        for (int u = 0; u < 3; ++u) {
+            const ConvLayer& k7 = e->unit_conv[(i * 3 + u) * 2];
+            const ConvLayer& k1 = e->unit_conv[(i * 3 + u) * 2 + 1];
+            w.p = std::max({w.p, enc_snake_item_floats(k7, len), enc_snake_item_floats(k1, len)});
+            part(k7, len);
+            part(k1, len);
+        }
+        w.p = std::max(w.p, enc_snake_item_floats(e->down[i], len / s + 1));
+        part(e->down[i], len / s);
+        len /= s;
+        w.x = std::max(w.x, (int64_t)2 * C * len);
+    }
+    w.p = std::max(w.p, enc_snake_item_floats(e->conv_out, len));
+    part(e->conv_out, len);
+    w.r = w.x;
+    w.x = round_up(w.x * batch, 64);
+    w.r = round_up(w.r * batch, 64);
+    w.p = round_up(w.p * batch, 64);
+    w.partial = round_up(w.partial, 64);
+    return w;
+}
+
+int enc_check_args(const mh3a_encoder* e, int64_t batch, int64_t samples, uint32_t flags) {
+    if (!e) return fail(MH3A_E_INVALID_ARG, "encoder is null");
+    if (batch < 1 || batch > 4096) return fail(MH3A_E_INVALID_ARG, "batch must be in [1, 4096]");
+    if (samples < 1) return fail(MH3A_E_INVALID_ARG, "samples must be >= 1");
+    if (flags & ~MH3A_FLAG_BATCH_INVARIANT)
+        return fail(MH3A_E_INVALID_ARG, "unsupported encode flags 0x%x", flags & ~MH3A_FLAG_BATCH_INVARIANT);
+    const int64_t len = enc_frames(e, samples) * e->hop;
+    // per-item tensors are addressed with 32-bit offsets in the kernels
+    if (len > ((int64_t)1 << 30) || (int64_t)e->cfg.encoder_dim * 3 * (len + 2 * kPkPadR) >= ((int64_t)1 << 29))
+        return fail(MH3A_E_INVALID_ARG, "samples too large for one item: %lld", (long long)samples);
+    return MH3A_OK;
+}
+
+size_t enc_ws_bytes(const mh3a_encoder* e, int64_t batch, int64_t samples, uint32_t flags) {
+    const EncWs w = enc_ws_floats(e, batch, enc_frames(e, samples), (flags & MH3A_FLAG_BATCH_INVARIANT) != 0);
+    return (size_t)(w.x + w.r + w.p + w.partial) * sizeof(float);
+}
+
+// Snake of x (batch, c, l) rows into the input form of conv L (space-to-depth
+// by s with shift p; l_out output positions).
+hipError_t enc_run_snake(const mh3a_encoder* e, const SnakeLayer& S, const ConvLayer& L, const float* x, int l,
+                         int s, int shift, int l_out, float* y, int batch, hipStream_t st) {
+    SnakeArgs a;
+    a.x = x;
+    a.x_bstride = (int64_t)S.c * l;
+    a.c = S.c;
+    a.l = l;
+    a.alpha = e->blob + S.alpha_off;
+    a.inv = e->blob + S.inv_off;
+    a.s = s;
+    a.shift = shift;
+    a.l_out = l_out;
+    a.y = y;
+    a.y_bstride = enc_snake_item_floats(L, l_out);
+    a.lp = enc_bx6(L) ? (int)pk_lp(l_out) : 0;
+    TimedLaunch tl(e, st, KIND_ENC_SNAKE);
+    hipError_t err = launch_snake(a, batch, st);
+    const double n_in = (double)batch * S.c * l, n_out = (double)batch * S.c * s * l_out;
+    tl.done(KIND_ENC_SNAKE, 4.0 * n_in, 4.0 * n_in + (a.lp ? 6.0 : 4.0) * n_out);
+    return err;
+}
+
+// conv L over its Snake input y (as enc_run_snake wrote it, l_in positions)
+hipError_t enc_run_conv(const mh3a_encoder* e, const ConvLayer& L, const float* p, int l_in, int positions,
+                        float* out, int batch, const float* res, bool inv, float* partial, hipStream_t st) {
+    const bool bx6 = enc_bx6(L);
+    return run_conv(e, L, p, enc_snake_item_floats(L, l_in), l_in, positions, out, (int64_t)L.c_out * positions,
+                    batch, res, nullptr, 1.0f, false, inv, true, partial, st, bx6 ? (int)pk_lp(l_in) : 0, bx6);
+}
+
+int run_encode(mh3a_encoder* e, const float* wave, int64_t batch, int64_t samples, float* hidden, void* ws,
+               size_t ws_bytes, uint32_t flags, hipStream_t st) {
+    int rc = enc_check_args(e, batch, samples, flags);
+    if (rc) return rc;
+    if (!wave || !hidden) return fail(MH3A_E_INVALID_ARG, "null wave or hidden pointer");
+    if (!ws) return fail(MH3A_E_WORKSPACE, "workspace is null");
+    if ((uintptr_t)ws % 256) return fail(MH3A_E_WORKSPACE, "workspace must be 256-byte aligned");
+    const bool inv = (flags & MH3A_FLAG_BATCH_INVARIANT) != 0;
+    const size_t need = enc_ws_bytes(e, batch, samples, flags);
+    if (ws_bytes < need) return fail(MH3A_E_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    const int64_t frames = enc_frames(e, samples);
+    const EncWs w = enc_ws_floats(e, batch, frames, inv);
+    float* bufX = static_cast<float*>(ws);
+    float* bufR = bufX + w.x;
+    float* bufP = bufR + w.r;
+    float* partial = bufP + w.p;
+    const int B = (int)batch;
+    HIP_TRY(hipSetDevice(e->device));
+
+    int len = (int)(frames * e->hop);
+    // first conv straight from the waveform: samples past S read as zeros,
+    // which is the right pad to a whole number of hops
+    HIP_TRY(run_conv(e, e->conv_in, wave, samples, (int)samples, len, bufX, (int64_t)e->cfg.encoder_dim * len, B,
+                     nullptr, nullptr, 1.0f, false, inv, true, partial, st));
+    size_t si = 0;
+    for (int i = 0; i < e->cfg.num_blocks; ++i) {
+        const int C = e->block_c[i], s = e->cfg.rates[i];
+        for (int u = 0; u < 3; ++u) {
+            const ConvLayer& k7 = e->unit_conv[(i * 3 + u) * 2];
+            const ConvLayer& k1 = e->unit_conv[(i * 3 + u) * 2 + 1];
+            HIP_TRY(enc_run_snake(e, e->snakes[si++], k7, bufX, len, 1, 0, len, bufP, B, st));
+            HIP_TRY(enc_run_conv(e, k7, bufP, len, len, bufR, B, nullptr, inv, partial, st));
+            HIP_TRY(enc_run_snake(e, e->snakes[si++], k1, bufR, len, 1, 0, len, bufP, B, st));
+            // residual add in place: each output element is read and written by one thread
+            HIP_TRY(enc_run_conv(e, k1, bufP, len, len, bufX, B, bufX, inv, partial, st));
+        }
+        const int lout = len / s;
+        HIP_TRY(enc_run_snake(e, e->snakes[si++], e->down[i], bufX, len, s, (s + 1) / 2, lout + 1, bufP, B, st));
+        (void)C;
+        HIP_TRY(enc_run_conv(e, e->down[i], bufP, lout + 1, lout, bufX, B, nullptr, inv, partial, st));
+        len = lout;
+    }
+    HIP_TRY(enc_run_snake(e, e->snakes[si++], e->conv_out, bufX, len, 1, 0, len, bufP, B, st));
+    HIP_TRY(enc_run_conv(e, e->conv_out, bufP, len, len, hidden, B, nullptr, inv, partial, st));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+void mh3a_encoder_config_default(mh3a_encoder_config* c) {
+    if (!c) return;
+    std::memset(c, 0, sizeof *c);
+    c->encoder_dim = 64;
+    c->num_blocks = 5;
+    const int rates[5] = {2, 4, 4, 5, 5};
+    for (int i = 0; i < 5; ++i) c->rates[i] = rates[i];
+    c->latent_dim = 2048;
+}
+
+int mh3a_encoder_create(const mh3a_encoder_config* cfg, const mh3a_tensor* params, int n_params, int device,
+                        mh3a_encoder** out) {
+    if (!out) return fail(MH3A_E_INVALID_ARG, "out is null");
+    *out = nullptr;
+    if (!cfg) return fail(MH3A_E_INVALID_ARG, "config is null");
+    if (n_params < 0 || (n_params > 0 && !params)) return fail(MH3A_E_INVALID_ARG, "bad parameter list");
+    if (device < 0) return fail(MH3A_E_INVALID_ARG, "device must be >= 0");
+    int rc = enc_check_config(cfg);
+    if (rc) return rc;
+    Table t;
+    if ((rc = build_table(params, n_params, t))) return rc;
+
+    mh3a_encoder* e = new (std::nothrow) mh3a_encoder();
+    if (!e) return fail(MH3A_E_NOMEM, "out of host memory");
+    std::unique_ptr<mh3a_encoder> guard(e);
+    e->cfg = *cfg;
+    e->device = device;
+    Blob blob;
+    int dim = cfg->encoder_dim;
+    if ((rc = enc_conv(blob, t, "encoder.block.0", e->conv_in, dim, 1, 7, 1, 3, KIND_ENC_CONV))) return rc;
+    e->hop = 1;
+    for (int i = 0; i < cfg->num_blocks; ++i) {
+        const std::string pre = "encoder.block." + std::to_string(i + 1);
+        const int s = cfg->rates[i];
+        e->block_c.push_back(dim);
+        e->hop *= s;
+        for (int u = 0; u < 3; ++u) {
+            const std::string q = pre + ".block." + std::to_string(u);
+            ConvLayer k7, k1;
+            const int d = kEncDils[u];
+            if ((rc = enc_snake_layer(blob, t, q + ".block.0.alpha", dim, e->snakes))) return rc;
+            if ((rc = enc_conv(blob, t, q + ".block.1", k7, dim, dim, 7, d, 3 * d, KIND_ENC_UNIT_CONV))) return rc;
+            if ((rc = enc_snake_layer(blob, t, q + ".block.2.alpha", dim, e->snakes))) return rc;
+            if ((rc = enc_conv(blob, t, q + ".block.3", k1, dim, dim, 1, 1, 0, KIND_ENC_CONV))) return rc;
+            e->unit_conv.push_back(k7);
+            e->unit_conv.push_back(k1);
+        }
+        if ((rc = enc_snake_layer(blob, t, pre + ".block.3.alpha", dim, e->snakes))) return rc;
+        // strided conv (2 dim, dim, 2 s) regrouped as (2 dim, dim s, 2): [o][c s + r][j] = w[o][c][j s + r]
+        std::vector<float> w;
+        const float* bias = nullptr;
+        const std::string dp = pre + ".block.4";
+        if ((rc = fetch_weight(t, dp, 2 * dim, dim, 2 * s, w))) return rc;
+        if ((rc = fetch_vector(t, dp + ".bias", 2 * dim, &bias))) return rc;
+        std::vector<float> w2((size_t)2 * dim * dim * s * 2);
+        for (int o = 0; o < 2 * dim; ++o)
+            for (int c = 0; c < dim; ++c)
+                for (int r = 0; r < s; ++r)
+                    for (int j = 0; j < 2; ++j)
+                        w2[(((size_t)o * dim + c) * s + r) * 2 + j] = w[((size_t)o * dim + c) * 2 * s + j * s + r];
+        ConvLayer D;
+        add_conv(blob, D, w2, bias, 2 * dim, dim * s, 2);
+        D.alg_taps = 2;
+        D.kind = KIND_ENC_CONV;
+        if (enc_split_ok(D)) {
+            D.w6_off = blob.reserve(packed_weight_floats6(2 * dim, dim * s, 2));
+            pack_conv_weights6(w2.data(), 2 * dim, dim * s, 2, blob.h.data() + D.w6_off);
+        }
+        e->down.push_back(D);
+        dim *= 2;
+    }
+    const std::string fin = "encoder.block." + std::to_string(cfg->num_blocks + 1);
+    if ((rc = enc_snake_layer(blob, t, fin + ".alpha", dim, e->snakes))) return rc;
+    if ((rc = enc_conv(blob, t, "encoder.block." + std::to_string(cfg->num_blocks + 2), e->conv_out, cfg->latent_dim,
+                       dim, 3, 1, 1, KIND_ENC_CONV)))
+        return rc;
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(MH3A_E_HIP, "no HIP device available");
+    if (device >= ndev) return fail(MH3A_E_INVALID_ARG, "device %d out of range (%d devices)", device, ndev);
+    HIP_TRY(hipSetDevice(device));
+    HIP_TRY(hipDeviceGetAttribute(&e->num_cus, hipDeviceAttributeMultiprocessorCount, device));
+    e->num_cus = std::max(1, e->num_cus);
+    e->blob_floats = (int64_t)blob.h.size();
+    HIP_TRY(hipMalloc((void**)&e->blob, sizeof(float) * blob.h.size()));
+    HIP_TRY(hipMemcpy(e->blob, blob.h.data(), sizeof(float) * blob.h.size(), hipMemcpyHostToDevice));
+    *out = guard.release();
+    return ok();
+}
+
+void mh3a_encoder_destroy(mh3a_encoder* e) {
+    if (!e) return;
+    if (e->blob) {
+        hipSetDevice(e->device);
+        hipDeviceSynchronize();
+        hipFree(e->blob);
+        for (hipEvent_t ev : e->timing.evs) hipEventDestroy(ev);
+    }
+    delete e;
+}
+
+int mh3a_encode_frames(const mh3a_encoder* e, int64_t samples, int64_t* frames) {
+    if (!e || !frames) return fail(MH3A_E_INVALID_ARG, "null argument");
+    if (samples < 1) return fail(MH3A_E_INVALID_ARG, "samples must be >= 1");
+    *frames = enc_frames(e, samples);
+    return ok();
+}
+
+int mh3a_encode_workspace_size(const mh3a_encoder* e, int64_t batch, int64_t samples, uint32_t flags, size_t* bytes) {
+    if (!bytes) return fail(MH3A_E_INVALID_ARG, "bytes is null");
+    *bytes = 0;
+    int rc = enc_check_args(e, batch, samples, flags);
+    if (rc) return rc;
+    *bytes = enc_ws_bytes(e, batch, samples, flags);
+    return ok();
+}
+
+int mh3a_encode_hidden(mh3a_encoder* e, const float* wave, int64_t batch, int64_t samples, float* hidden,
+                       void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+    return run_encode(e, wave, batch, samples, hidden, workspace, workspace_bytes, flags,
+                      static_cast<hipStream_t>(stream));
+}
+
+int mh3a_encoder_timing_enable(mh3a_encoder* e, int enable) { return timing_enable(e, enable); }
+int mh3a_encoder_timing_read(mh3a_encoder* e, mh3a_kernel_stats* stats, int max_stats, int* n_stats) {
+    return timing_read(e, stats, max_stats, n_stats);
 }
 
 }  // extern "C"

@@ -83,6 +83,8 @@ constexpr int kPkPadR = 288;
 constexpr int kPieces = 3;
 // Largest dilation the split-product conv has LDS planes for.
 constexpr int kBx6MaxDil = 5;
+// Dilation bound of the wider-plane instances (7 taps; the encoder's units).
+constexpr int kBx6WideDil = 9;
 
 // Tile shapes of the conv kernel: four consumer waves arranged WM x WN,
 // each computing MBW x NBW blocks of 32 x 32 outputs.
@@ -211,6 +213,23 @@ hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream);
 // Unit-kernel weights as bf16 pieces for v_mfma_f32_16x16x32_bf16.
 int64_t unit_weight_floats6(int c, int taps);
 void pack_unit_weights6(const float* w, int c, int taps, float* out);
+
+// Encoder Snake: y = snake(x) regrouped space-to-depth by s (s = 1: plain):
+// output channel c * s + r at position t is snake(x[c, t * s + r - shift]),
+// zero outside [0, l); t in [0, l_out). lp = 0: plain (B, c * s, l_out)
+// rows; lp = l_out + kPkPadL + kPkPadR: the split-product packed form.
+struct SnakeArgs {
+    const float* x;
+    int64_t x_bstride;
+    int c, l;
+    const float* alpha;  // [c]
+    const float* inv;    // [c] 1 / (alpha + 1e-9)
+    int s, shift, l_out;
+    float* y;
+    int64_t y_bstride;
+    int lp;
+};
+hipError_t launch_snake(const SnakeArgs& a, int batch, hipStream_t stream);
 
 // activation_post + conv_post (c -> 1, 7 taps, pad 3) + optional clamp.
 struct FinalArgs {

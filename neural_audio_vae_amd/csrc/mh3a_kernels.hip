@@ -276,9 +276,9 @@ __host__ __device__ constexpr int conv_lds_floats(int W, bool act) {
 // Split-product convs: per item kPieces planes of PS positions (16 bytes
 // each), PS sized for the largest dilation so that plane offsets are
 // compile-time constants.
-__host__ __device__ constexpr int bx6_plane(int nwg, int taps) { return nwg + (taps - 1) * kBx6MaxDil; }
-__host__ __device__ constexpr int conv_lds_floats6(int nwg, int taps) {
-    return 2 * 2 * kPieces * bx6_plane(nwg, taps) * 4 + kTouchFloats;  // two buffers of two-chunk items
+__host__ __device__ constexpr int bx6_plane(int nwg, int taps, int dmax = kBx6MaxDil) { return nwg + (taps - 1) * dmax; }
+__host__ __device__ constexpr int conv_lds_floats6(int nwg, int taps, int dmax = kBx6MaxDil) {
+    return 2 * 2 * kPieces * bx6_plane(nwg, taps, dmax) * 4 + kTouchFloats;  // two buffers of two-chunk items
 }
 
 // Wave-specialized, persistent implicit-GEMM conv. 512 threads: waves 0-3
@@ -300,7 +300,10 @@ __host__ __device__ constexpr int conv_lds_floats6(int nwg, int taps) {
 // matrix cores (packed input in the split-product form, see kPieces); 3 the
 // bf16 operand variant on bf16 matrix cores (pieces 0 and 1 only, the three
 // products w0 x0, w0 x1, w1 x0: the numerics of PREC 1).
-template <int MBW, int NBW, int WM, int WN, bool ACT, int PREC, int TAPS, int RB = 32>
+//
+// DMAX bounds the dilation of a split-product conv (its LDS planes hold
+// NWG + (TAPS - 1) DMAX positions).
+template <int MBW, int NBW, int WM, int WN, bool ACT, int PREC, int TAPS, int RB = 32, int DMAX = kBx6MaxDil>
 // (fp32 tiles of at most 2 x 2 blocks per wave keep two workgroups per CU: <= 128 VGPRs)
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((MBW * NBW <= 4 && PREC < 2) ? 4 : 1)))
 conv_kernel(ConvArgs a) {
@@ -317,7 +320,7 @@ conv_kernel(ConvArgs a) {
     static_assert(!BX6 || (PK && RB == 32), "split products read the packed input");
     constexpr int NWG = WN * NBW * RB;
     constexpr int MWG = WM * MBW * RB;
-    constexpr int PS6 = bx6_plane(NWG, TAPS > 0 ? TAPS : 1);  // split-product plane stride (positions)
+    constexpr int PS6 = bx6_plane(NWG, TAPS > 0 ? TAPS : 1, DMAX);  // split-product plane stride (positions)
     // an item is CPI chunks (split products: two, so that each barrier hands
     // over as much matrix-core work as an fp32 item)
     constexpr int CPI = BX6 ? 2 : 1;
@@ -1159,8 +1162,17 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
             if (NWG > 256) return hipErrorInvalidValue;
             if (a.bx6) {
                 // split products: bf16 pieces, one phase, planes sized for kBx6MaxDil
-                if (!a.w6 || a.dil > kBx6MaxDil) return hipErrorInvalidValue;
+                if (!a.w6 || a.dil < 1) return hipErrorInvalidValue;
                 if ((((a.c_in + kChunk - 1) / kChunk) / a.ksplit) % 2) return hipErrorInvalidValue;  // two-chunk items
+                if (a.dil > kBx6MaxDil) {
+                    // wider planes: 7 taps up to dilation kBx6WideDil (encoder units), fp32-level products only
+                    if (a.taps != 7 || a.dil > kBx6WideDil || a.bf16) return hipErrorInvalidValue;
+                    return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 2, 7, 32, kBx6WideDil>, a, tiles,
+                                             sizeof(float) * (size_t)conv_lds_floats6(NWG, 7, kBx6WideDil), stream);
+                }
+                if (a.taps == 1 && !a.bf16)  // pointwise convs (encoder units): one zero-padded tap pair
+                    return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 2, 1>, a, tiles,
+                                             sizeof(float) * (size_t)conv_lds_floats6(NWG, 1), stream);
 #define MH3A_TAPS6(T)                                                                                           \
     if (a.taps == T)                                                                                           \
         return a.bf16 ? launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 3, T>, a, tiles,                \
@@ -1863,6 +1875,64 @@ hipError_t launch_split(const ActArgs& a, int batch, hipStream_t stream) {
         return hipErrorInvalidValue;
     dim3 grid((a.lp + 255) / 256, (a.c + kChunk - 1) / kChunk, batch);
     hipLaunchKernelGGL(split_kernel, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Plain Snake with an optional space-to-depth regrouping (encoder):
+// output channel c s + r at position t holds snake(x[c, t s + r - shift]),
+// snake(v) = v + sin^2(alpha v) / (alpha + 1e-9), zero outside [0, l) (the
+// Snake of a zero is zero, so padding before or after it is the same).
+// Packed output: one padded position of one 8-channel chunk per thread, as
+// split_kernel. Plain output: one (channel, position) per thread.
+__device__ __forceinline__ float snake_at(const SnakeArgs& a, const float* xb, int oc, int t) {
+    const int c = oc / a.s, r = oc - c * a.s;
+    const int64_t n = (int64_t)t * a.s + r - a.shift;
+    if (c >= a.c || t < 0 || t >= a.l_out || n < 0 || n >= a.l) return 0.0f;
+    const float v = xb[(int64_t)c * a.l + n];
+    const float sn = sinf(a.alpha[c] * v);
+    return fmaf(sn * sn, a.inv[c], v);
+}
+
+__global__ void __launch_bounds__(256) snake_packed_kernel(SnakeArgs a) {
+    const int q = blockIdx.x * 256 + threadIdx.x;
+    const int chunk = blockIdx.y, b = blockIdx.z;
+    if (q >= a.lp) return;
+    const float* xb = a.x + (int64_t)b * a.x_bstride;
+    unsigned pc[kPieces][kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) split3_bf16(snake_at(a, xb, chunk * kChunk + i, q - kPkPadL), pc[0][i], pc[1][i], pc[2][i]);
+    float* yc = a.y + (int64_t)b * a.y_bstride + (int64_t)chunk * kPieces * a.lp * 4;
+#pragma unroll
+    for (int p = 0; p < kPieces; ++p) {
+        uint4 v;
+        v.x = pc[p][0] | (pc[p][1] << 16);
+        v.y = pc[p][2] | (pc[p][3] << 16);
+        v.z = pc[p][4] | (pc[p][5] << 16);
+        v.w = pc[p][6] | (pc[p][7] << 16);
+        *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = v;
+    }
+}
+
+__global__ void __launch_bounds__(256) snake_rows_kernel(SnakeArgs a) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    const int oc = blockIdx.y, b = blockIdx.z;
+    if (t >= a.l_out) return;
+    a.y[(int64_t)b * a.y_bstride + (int64_t)oc * a.l_out + t] = snake_at(a, a.x + (int64_t)b * a.x_bstride, oc, t);
+}
+
+hipError_t launch_snake(const SnakeArgs& a, int batch, hipStream_t stream) {
+    const int64_t oc = (int64_t)a.c * a.s;
+    if (a.c < 1 || a.l < 1 || a.s < 1 || a.l_out < 1 || batch < 1 || batch > 65535 || oc > 65535 * (int64_t)kChunk)
+        return hipErrorInvalidValue;
+    if (a.lp > 0) {
+        if (a.lp != a.l_out + kPkPadL + kPkPadR) return hipErrorInvalidValue;
+        dim3 grid((a.lp + 255) / 256, (unsigned)((oc + kChunk - 1) / kChunk), batch);
+        hipLaunchKernelGGL(snake_packed_kernel, grid, dim3(256), 0, stream, a);
+    } else {
+        if (oc > 65535) return hipErrorInvalidValue;
+        dim3 grid((a.l_out + 255) / 256, (unsigned)oc, batch);
+        hipLaunchKernelGGL(snake_rows_kernel, grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

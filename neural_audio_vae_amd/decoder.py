@@ -135,3 +135,55 @@ class Decoder:
 
 def to_numpy_params(params):
     return {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in params.items()}
+
+
+class Encoder:
+    """The encoder's convolution stack (waveform -> hidden), built once from
+    host parameters (weight norm folded at construction)."""
+
+    def __init__(self, params, config=None, device=0):
+        self.config = dict(config or {})
+        self.device = int(device)
+        cfg = _lib.make_encoder_config(self.config)
+        self.latent_dim = cfg.latent_dim
+        self._h = _lib.mh3a_encoder_create(cfg, params, self.device)
+        self._ws = None
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.mh3a_encoder_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def frames(self, samples):
+        return _lib.mh3a_encode_frames(self._h, samples)
+
+    def workspace_size(self, batch, samples, flags=0):
+        return _lib.mh3a_encode_workspace_size(self._h, batch, samples, flags)
+
+    def encode_hidden(self, wave, flags=0, out=None, stream=None):
+        torch = _torch()
+        x = Decoder._check_input(wave, 3, "wave")
+        b, c, s = x.shape
+        if c != 1:
+            raise ValueError("wave must be (B, 1, samples)")
+        if out is None:
+            out = torch.empty((b, self.latent_dim, self.frames(s)), dtype=torch.float32, device=x.device)
+        nbytes = self.workspace_size(b, s, flags)
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=f"cuda:{self.device}")
+        st = (stream or torch.cuda.current_stream(x.device)).cuda_stream
+        _lib.mh3a_encode_hidden(self._h, x.data_ptr(), b, s, out.data_ptr(), self._ws.data_ptr(), self._ws.numel(),
+                                flags, st)
+        return out
+
+    def timing(self, mode):
+        _lib.mh3a_encoder_timing_enable(self._h, mode)
+
+    def timing_read(self):
+        return _lib.mh3a_encoder_timing_read(self._h)

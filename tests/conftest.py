@@ -32,3 +32,21 @@ SMALL_CONFIG = {
 def small_params():
     from neural_audio_vae_amd import synth
     return synth.make_params(SMALL_CONFIG, seed=3)
+
+
+def encoder_margin_frames(rates):
+    """Frames of context on either side that make an encoder window's
+    interior equal to the full encode: the stack's one-sided reach in samples
+    (k7 first conv: 3; per block at sample spacing P: units of dilation 1, 3,
+    9 reach 3 (1 + 3 + 9) = 39 positions, the strided conv p = ceil(s / 2)
+    back and 2 s - 1 - p forward; final k3: one frame), plus one frame."""
+    hop, P, left, right = 1, 1, 3, 3
+    for s in rates:
+        p = (s + 1) // 2
+        left += (39 + p) * P
+        right += (39 + 2 * s - 1 - p) * P
+        P *= s
+    hop = P
+    left += hop
+    right += hop
+    return -(-max(left, right) // hop) + 1

@@ -149,3 +149,53 @@ def test_valid_create_reaches_the_device_step(small):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     expect_error(_lib.MH3A_E_HIP, create, _lib.make_config(SMALL_CONFIG), small)
+
+
+# ---- encoder convolution stack ----
+
+ENC_SMALL = {"encoder_dim": 4, "latent_dim": 16}
+
+
+def test_encoder_config_default():
+    # the FastVideo encoder's defaults: encoder_dim 64, rates (2, 4, 4, 5, 5), latent_dim 2048
+    c = _lib.mh3a_encoder_config_default()
+    assert (c.encoder_dim, c.num_blocks, c.latent_dim) == (64, 5, 2048)
+    assert list(c.rates[:5]) == [2, 4, 4, 5, 5]
+    c = _lib.make_encoder_config({"encoder_dim": 8, "encoder_rates": (2, 2)})
+    assert (c.encoder_dim, c.num_blocks, list(c.rates[:2])) == (8, 2, [2, 2])
+
+
+@pytest.fixture(scope="module")
+def enc_small():
+    return synth.make_encoder_params(ENC_SMALL, seed=1)
+
+
+def test_encoder_create_errors(enc_small):
+    cfg = _lib.make_encoder_config(ENC_SMALL)
+    for name in ("encoder.block.0.weight_v", "encoder.block.3.block.1.block.2.alpha", "encoder.block.7.bias"):
+        p = dict(enc_small)
+        del p[name]
+        expect_error(_lib.MH3A_E_MISSING_TENSOR, _lib.mh3a_encoder_create, cfg, p, match=re.escape(name))
+    p = dict(enc_small)
+    p["encoder.block.2.block.4.weight_v"] = np.zeros((16, 8, 7), dtype=np.float32)
+    expect_error(_lib.MH3A_E_SHAPE, _lib.mh3a_encoder_create, cfg, p, match="block.2.block.4.weight_v")
+    p = dict(enc_small)
+    p["encoder.block.1.block.0.block.0.alpha"] = np.ones(5, dtype=np.float32)
+    expect_error(_lib.MH3A_E_SHAPE, _lib.mh3a_encoder_create, cfg, p)
+    bad = _lib.make_encoder_config(ENC_SMALL)
+    bad.num_blocks = 0
+    expect_error(_lib.MH3A_E_CONFIG, _lib.mh3a_encoder_create, bad, enc_small)
+    bad = _lib.make_encoder_config(ENC_SMALL)
+    bad.rates[1] = 0
+    expect_error(_lib.MH3A_E_CONFIG, _lib.mh3a_encoder_create, bad, enc_small)
+
+
+def test_encoder_null_handle_errors():
+    lib = _lib.load()
+    from ctypes import byref, c_int64, c_size_t
+    n = c_size_t()
+    assert lib.mh3a_encode_workspace_size(None, 1, 800, 0, byref(n)) == _lib.MH3A_E_INVALID_ARG
+    f = c_int64()
+    assert lib.mh3a_encode_frames(None, 800, byref(f)) == _lib.MH3A_E_INVALID_ARG
+    assert lib.mh3a_encode_hidden(None, None, 1, 800, None, None, 0, 0, None) == _lib.MH3A_E_INVALID_ARG
+    lib.mh3a_encoder_destroy(None)

@@ -612,3 +612,22 @@ def test_encode_hidden_batch_items_independent():
     h = O.encode_hidden(params, wave, ENC_SMALL)
     for i in range(3):
         np.testing.assert_array_equal(h[i], O.encode_hidden_item(params, wave[i, 0], ENC_SMALL))
+
+
+def test_encoder_window_interior_equals_full_encode():
+    # a window widened by encoder_margin_frames per side reproduces the full
+    # encode on its interior (what the GPU test's sampled windows rely on)
+    from tests.conftest import encoder_margin_frames
+    rates = O.DEFAULT_CONFIG["encoder_rates"]
+    m = encoder_margin_frames(rates)
+    assert m == 14
+    params = synth.make_encoder_params(ENC_SMALL, seed=5)
+    n = 2 * m + 3
+    wave = synth.make_waveform(1, n * 800 - 321, seed=5)
+    full = O.encode_hidden(params, wave, ENC_SMALL)
+    f0, f1 = m, m + 2
+    win = O.encode_hidden(params, wave[:, :, (f0 - m) * 800:(f1 + m) * 800], ENC_SMALL)
+    np.testing.assert_array_equal(win[:, :, m:m + 2], full[:, :, f0:f1])
+    # the right edge: the window ends at the ragged end of the waveform
+    win = O.encode_hidden(params, wave[:, :, (n - 1 - m) * 800:], ENC_SMALL)
+    np.testing.assert_array_equal(win[:, :, m:], full[:, :, n - 1:])
