@@ -2,6 +2,7 @@
 """Benchmark of the BigVGAN decode path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+    python bench.py --path encode [--workload e3]
 
 A step is one full decode (dec_in_proj -> conv_pre -> 7 x (transposed conv
 + averaged AMP blocks) -> activation_post + conv_post + clamp) of one batch
@@ -41,6 +42,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 SPLIT_PRODUCTS = 6              # bf16 piece products per fp32 product
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 LATENTS_PER_SECOND = 40         # 32 kHz / hop 800
+SAMPLE_RATE = 32000
 
 WORKLOADS = {
     # name: (batch, frames, flags, description)
@@ -49,6 +51,10 @@ WORKLOADS = {
     "c3": (2, 1200, 0, "B=2 x N=1200 latents (30 s/item)"),
     "c5": (16, 401, 0, "B=16 x N=401 latents (10.025 s/item)"),
 }
+# encoder workloads (--path encode): name: (batch, samples, description)
+ENC_WORKLOADS = {
+    "e3": (2, 960000, "B=2 x 960000 samples (30 s/item at 32 kHz)"),
+}
 
 
 def parse():
@@ -56,10 +62,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--path", default="decode", choices=("decode", "encode"),
+                    help="decode: the BigVGAN decoder (default); encode: the encoder's convolution stack")
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + sorted(ENC_WORKLOADS))
     ap.add_argument("--bf16", action="store_true", help="bf16-split matrix-core operands (MH3A_FLAG_BF16_MFMA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-latents", type=int, default=80, help="latents in the oracle's timed sample")
+    ap.add_argument("--cpu-samples", type=int, default=16000, help="samples in the oracle's timed encode sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -134,6 +143,12 @@ def main():
 
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+    if args.path == "encode":
+        return main_encode(args)
+    args.workload = args.workload or "c3"
+    if args.workload not in WORKLOADS:
+        print(f"--workload {args.workload} is an encoder workload (use --path encode)", file=sys.stderr)
         return 2
     batch, frames, flags, desc = WORKLOADS[args.workload]
     if args.bf16:
@@ -237,6 +252,134 @@ def main():
         line["cpu_baseline"] = cpu_baseline(params, args.cpu_latents)
     print(json.dumps(line), flush=True)
     dec.close()
+    return 0
+
+
+def cpu_baseline_encode(params, n_samples):
+    """The oracle's encoder stack, as it stands, on the first n samples of
+    item 0 of the workload."""
+    import numpy as np
+    import oracle as O
+    from neural_audio_vae_amd import synth
+    try:
+        import threadpoolctl
+        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    wave = synth.make_waveform(1, n_samples, seed=0)
+    t0 = time.perf_counter()
+    h = O.encode_hidden(params, wave)
+    dt = time.perf_counter() - t0
+    assert h.shape[-1] == -(-n_samples // 800)
+    return {
+        "value": (n_samples / SAMPLE_RATE) / dt,
+        "unit": "audio-s/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"oracle encode of a {n_samples}-sample waveform ({n_samples / SAMPLE_RATE:.2f} s of audio) "
+                  f"in {dt:.1f} s",
+    }
+
+
+def main_encode(args):
+    """A step is one pass of the encoder's convolution stack (k7 conv, five
+    strided blocks of Snake residual units, final Snake + k3 conv) over a
+    batch of seeded synthetic waveforms resident in HBM."""
+    import torch
+    from neural_audio_vae_amd import Encoder, _lib, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+    args.workload = args.workload or "e3"
+    if args.workload not in ENC_WORKLOADS:
+        print(f"--workload {args.workload} is a decoder workload (use --path decode)", file=sys.stderr)
+        return 2
+    batch, samples, desc = ENC_WORKLOADS[args.workload]
+    params = synth.make_encoder_params(seed=0)
+    enc = Encoder(params)
+    x = torch.from_numpy(synth.make_waveform(batch, samples, seed=0)).cuda()
+    out = torch.empty((batch, enc.latent_dim, enc.frames(samples)), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        enc.encode_hidden(x, out=out, stream=stream)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        if i == args.steps - 1:
+            enc.timing(_lib.MH3A_TIMING_AMP_CONV)  # the residual units' k7 convs only
+        enc.encode_hidden(x, out=out, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(stop)
+    unit_only = enc.timing_read()
+    enc.timing(_lib.MH3A_TIMING_ALL)
+    for _ in range(args.steps):
+        enc.encode_hidden(x, out=out, stream=stream)
+    torch.cuda.synchronize()
+    kernels = enc.timing_read()
+    enc.timing(_lib.MH3A_TIMING_OFF)
+    ms_step = ms_total / args.steps
+    value = batch * samples / SAMPLE_RATE / (ms_step / 1e3)
+    k7 = unit_only.get("enc_unit_conv", {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+    achieved = k7["flops"] / (k7["ms"] / 1e3) / 1e12 if k7["ms"] > 0 else 0.0
+    split = os.environ.get("MH3A_BX6") != "0"
+    peak = BF16_MFMA_PEAK_TFLOPS / SPLIT_PRODUCTS if split else FP32_MFMA_PEAK_TFLOPS
+    total_flops = sum(k["flops"] for k in kernels.values()) / args.steps
+    line = {
+        "metric": f"encoded audio-sec/s ({args.workload}, fp32)",
+        "value": round(value, 2),
+        "unit": "audio-s/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"encoder convolution stack of the MiniMax-H3 audio VAE, {desc}, encoder_dim 64, "
+                        "rates (2, 4, 4, 5, 5), hidden 2048, seeded random weights",
+            "batch": batch,
+            "samples_per_item": samples,
+        },
+        "algorithmic_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
+        "roofline": {
+            "kernel": "conv_kernel, the residual units' k7 dilated convs (split-product packed input; "
+                      + ("six bf16 piece products per fp32 product on v_mfma_f32_32x32x16_bf16)" if split
+                         else "fp32 matrix cores)"),
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(peak, 2),
+            "peak_basis": ("dense bf16 matrix peak 2500 TFLOP/s / 6 piece products (fp32-equivalent)" if split
+                           else "dense fp32 matrix peak"),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "launches_timed": k7["launches"],
+            "avg_launch_us": round(1e3 * k7["ms"] / max(1, k7["launches"]), 2),
+            "flops_per_launch": k7["flops"] / max(1, k7["launches"]),
+        },
+        "kernels": {
+            name: {
+                "launches_per_step": k["launches"] / args.steps,
+                "ms_per_step": round(k["ms"] / args.steps, 4),
+                "tflops": round(k["flops"] / (k["ms"] / 1e3) / 1e12, 2) if k["ms"] > 0 else None,
+                "gbs_compulsory": round(k["bytes"] / (k["ms"] / 1e3) / 1e9, 1) if k["ms"] > 0 else None,
+            }
+            for name, k in kernels.items()
+        },
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_encode(params, args.cpu_samples)
+    print(json.dumps(line), flush=True)
+    enc.close()
     return 0
 
 

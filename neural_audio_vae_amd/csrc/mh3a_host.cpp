@@ -334,6 +334,7 @@ void add_conv(Blob& blob, ConvLayer& L, const std::vector<float>& w, const float
 bool split_input_ok(const ConvLayer& L) {
     if (!(L.taps == 2 || L.taps == 3 || L.taps == 7 || L.taps == 11)) return false;
     if (L.c_in % 16 || L.c_out < 32 || L.dil < 1 || L.dil > kBx6MaxDil) return false;
+    if (L.taps <= 2 && (L.c_in / kChunk) % bx6_cpi(128, L.taps)) return false;  // whole items of 8 chunks
     for (int ph = 0; ph < L.phases; ++ph)
         if (-L.in_off[ph] > kPkPadL || 255 + (L.taps - 1) * L.dil + L.in_off[ph] > kPkPadR) return false;
     return true;
@@ -1646,6 +1647,7 @@ bool enc_split_ok(const ConvLayer& L) {
     const bool taps_ok = L.taps == 1 || L.taps == 2 || L.taps == 3 || (L.taps == 7 && L.dil <= kBx6WideDil) ||
                          (L.taps == 11 && L.dil <= kBx6MaxDil);
     if (!taps_ok || L.c_in % 16 || L.c_out < 32 || L.dil < 1) return false;
+    if (L.taps <= 2 && (L.c_in / kChunk) % bx6_cpi(128, L.taps)) return false;  // whole items of 8 chunks
     return -L.in_off[0] <= kPkPadL && 255 + (L.taps - 1) * L.dil + L.in_off[0] <= kPkPadR;
 }
 
@@ -1664,8 +1666,21 @@ int enc_conv(Blob& blob, const Table& t, const std::string& prefix, ConvLayer& L
     L.alg_taps = k;
     L.kind = kind;
     if (enc_split_ok(L)) {
-        L.w6_off = blob.reserve(packed_weight_floats6(c_out, c_in, k));
-        pack_conv_weights6(w.data(), c_out, c_in, k, blob.h.data() + L.w6_off);
+        if (k == 1) {
+            // pointwise: packed as a 2-tap conv over c_in / 2 channels (chunk pairs, see bx6_cpi)
+            std::vector<float> w2((size_t)c_out * c_in);
+            for (int o = 0; o < c_out; ++o)
+                for (int kc = 0; kc < c_in / (2 * kChunk); ++kc)
+                    for (int i = 0; i < kChunk; ++i)
+                        for (int j = 0; j < 2; ++j)
+                            w2[((size_t)o * (c_in / 2) + kc * kChunk + i) * 2 + j] =
+                                w[(size_t)o * c_in + (2 * kc + j) * kChunk + i];
+            L.w6_off = blob.reserve(packed_weight_floats6(c_out, c_in / 2, 2));
+            pack_conv_weights6(w2.data(), c_out, c_in / 2, 2, blob.h.data() + L.w6_off);
+        } else {
+            L.w6_off = blob.reserve(packed_weight_floats6(c_out, c_in, k));
+            pack_conv_weights6(w.data(), c_out, c_in, k, blob.h.data() + L.w6_off);
+        }
     }
     return MH3A_OK;
 }

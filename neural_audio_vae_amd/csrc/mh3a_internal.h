@@ -85,6 +85,14 @@ constexpr int kPieces = 3;
 constexpr int kBx6MaxDil = 5;
 // Dilation bound of the wider-plane instances (7 taps; the encoder's units).
 constexpr int kBx6WideDil = 9;
+// Chunks per pipeline item of a split-product conv with output tiles nwg
+// wide: two for 3+ taps; for 1 or 2 taps (one tap pair per chunk) eight, or
+// four on 256-wide tiles (LDS), so each item still carries eight pairs of
+// matrix-core work. The chunks of a K range must be a multiple of it.
+constexpr int bx6_cpi(int nwg, int taps) { return taps <= 2 ? (nwg <= 128 ? 8 : 4) : 2; }
+// Pointwise (1-tap) split-product convs pair two chunks per matrix-core
+// instruction instead of two taps: their weights are packed as a 2-tap conv
+// over c_in / 2 channels, w2[o][8 k + i][j] = w[o][8 (2 k + j) + i].
 
 // Tile shapes of the conv kernel: four consumer waves arranged WM x WN,
 // each computing MBW x NBW blocks of 32 x 32 outputs.

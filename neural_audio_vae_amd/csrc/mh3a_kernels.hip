@@ -278,7 +278,7 @@ __host__ __device__ constexpr int conv_lds_floats(int W, bool act) {
 // compile-time constants.
 __host__ __device__ constexpr int bx6_plane(int nwg, int taps, int dmax = kBx6MaxDil) { return nwg + (taps - 1) * dmax; }
 __host__ __device__ constexpr int conv_lds_floats6(int nwg, int taps, int dmax = kBx6MaxDil) {
-    return 2 * 2 * kPieces * bx6_plane(nwg, taps, dmax) * 4 + kTouchFloats;  // two buffers of two-chunk items
+    return 2 * bx6_cpi(nwg, taps) * kPieces * bx6_plane(nwg, taps, dmax) * 4 + kTouchFloats;  // two item buffers
 }
 
 // Wave-specialized, persistent implicit-GEMM conv. 512 threads: waves 0-3
@@ -323,7 +323,9 @@ conv_kernel(ConvArgs a) {
     constexpr int PS6 = bx6_plane(NWG, TAPS > 0 ? TAPS : 1, DMAX);  // split-product plane stride (positions)
     // an item is CPI chunks (split products: two, so that each barrier hands
     // over as much matrix-core work as an fp32 item)
-    constexpr int CPI = BX6 ? 2 : 1;
+    constexpr int CPI = BX6 ? bx6_cpi(NWG, TAPS) : 1;
+    // pointwise split products: a pair spans two chunks (see bx6_cpi)
+    constexpr bool CP1 = BX6 && TAPS == 1;
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -543,7 +545,7 @@ conv_kernel(ConvArgs a) {
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
     constexpr int NP6 = (TAPS + 1) / 2;
-    const int G6 = nch * NP6;
+    const int G6 = CP1 ? nch / 2 : nch * NP6;  // weight groups per 32-row block
     v4u A6a[BX6 ? kPieces : 1][MBW], A6b[BX6 ? kPieces : 1][MBW], A6c[BX6 ? kPieces : 1][MBW];
     auto load_a6 = [&](v4u (&dst)[BX6 ? kPieces : 1][MBW], int mb_base, int ph, int g) {
         const v4u* wp = reinterpret_cast<const v4u*>(a.w6 + (int64_t)ph * a.w6_phase_stride) + (int64_t)g * kPieces * 64 + lane;
@@ -782,8 +784,9 @@ conv_kernel(ConvArgs a) {
     float4 Ar0[MBW], Ar1[MBW], Ar2[MBW];
     if constexpr (BX6) {
         const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
-        load_a6(A6a, mb0, cur.ph, cur.c0 * NP6);
-        load_a6(A6b, mb0, cur.ph, cur.c0 * NP6 + 1);
+        const int g0 = CP1 ? cur.c0 / 2 : cur.c0 * NP6;
+        load_a6(A6a, mb0, cur.ph, g0);
+        load_a6(A6b, mb0, cur.ph, g0 + 1);
     } else if constexpr (TAPS > 0) {
         const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
         load_a_nb(Ar0, mb0, cur.ph, cur.c0 * a.taps);
@@ -813,9 +816,11 @@ conv_kernel(ConvArgs a) {
         if constexpr (BX6) {
             const int nmb_base = __builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW);
             // the item's CPI chunks: pair u = cc NP6 + q is weight group q0 + u
-            constexpr int NPI = CPI * NP6;
-            const int q0 = (cur.c0 + CPI * cur_c) * NP6;
-            const int nq0 = has_next ? (nxt.c0 + CPI * nxt_c) * NP6 : q0;
+            // (pointwise: pair u = chunks 2u, 2u + 1 is weight group q0 + u)
+            constexpr int NPI = CP1 ? CPI / 2 : CPI * NP6;
+            static_assert(NPI >= 2, "the weight ring holds two pairs ahead");
+            const int q0 = CP1 ? (cur.c0 + CPI * cur_c) / 2 : (cur.c0 + CPI * cur_c) * NP6;
+            const int nq0 = has_next ? (CP1 ? (nxt.c0 + CPI * nxt_c) / 2 : (nxt.c0 + CPI * nxt_c) * NP6) : q0;
             const int nmb = has_next ? nmb_base : mb_base;
             const int nph6 = has_next ? nxt.ph : cur.ph;
             const float* bb_h = cur_buf + (colbase + hi * a.dil) * 4;  // this lane's tap of each pair
@@ -834,7 +839,9 @@ conv_kernel(ConvArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 const bool pad = (TAPS & 1) && q == NP6 - 1;
-                const float* bq = (pad ? bb_0 : bb_h) + (cc * kPieces * PS6 + 2 * q * a.dil) * 4;
+                // pointwise: lanes of half hi read chunk 2u + hi at the lane's position
+                const float* bq = CP1 ? bb_0 + (2 * u + hi) * kPieces * PS6 * 4
+                                      : (pad ? bb_0 : bb_h) + (cc * kPieces * PS6 + 2 * q * a.dil) * 4;
                 v4u Bv[kPieces][NBW];
 #pragma unroll
                 for (int p = 0; p < NPA; ++p)
@@ -1163,7 +1170,8 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
             if (a.bx6) {
                 // split products: bf16 pieces, one phase, planes sized for kBx6MaxDil
                 if (!a.w6 || a.dil < 1) return hipErrorInvalidValue;
-                if ((((a.c_in + kChunk - 1) / kChunk) / a.ksplit) % 2) return hipErrorInvalidValue;  // two-chunk items
+                // whole items per K range
+                if ((((a.c_in + kChunk - 1) / kChunk) / a.ksplit) % bx6_cpi(NWG, a.taps)) return hipErrorInvalidValue;
                 if (a.dil > kBx6MaxDil) {
                     // wider planes: 7 taps up to dilation kBx6WideDil (encoder units), fp32-level products only
                     if (a.taps != 7 || a.dil > kBx6WideDil || a.bf16) return hipErrorInvalidValue;
