@@ -1594,7 +1594,7 @@ int mh3a_amp_stage(mh3a_decoder* d, int stage, const float* x, int64_t batch, in
 
 struct SnakeLayer {
     int c = 0;
-    int64_t alpha_off = -1, inv_off = -1;
+    int64_t ab_off = -1;  // [c] float2 (alpha / pi, 0.5 / (alpha + 1e-9))
 };
 
 struct mh3a_encoder : mh3a_net {
@@ -1689,12 +1689,14 @@ int enc_snake_layer(Blob& blob, const Table& t, const std::string& name, int c, 
     const float* alpha = nullptr;
     int rc = fetch_vector(t, name, c, &alpha);
     if (rc) return rc;
-    std::vector<float> inv(c);
-    for (int i = 0; i < c; ++i) inv[i] = (float)(1.0 / ((double)alpha[i] + 1e-9));
+    std::vector<float> ab(2 * (size_t)c);
+    for (int i = 0; i < c; ++i) {
+        ab[2 * i] = (float)((double)alpha[i] / M_PI);
+        ab[2 * i + 1] = (float)(0.5 / ((double)alpha[i] + 1e-9));
+    }
     SnakeLayer S;
     S.c = c;
-    S.alpha_off = blob.add(alpha, c);
-    S.inv_off = blob.add(inv.data(), c);
+    S.ab_off = blob.add(ab.data(), 2 * (int64_t)c);
     out.push_back(S);
     return MH3A_OK;
 }
@@ -1777,8 +1779,7 @@ hipError_t enc_run_snake(const mh3a_encoder* e, const SnakeLayer& S, const ConvL
     a.x_bstride = (int64_t)S.c * l;
     a.c = S.c;
     a.l = l;
-    a.alpha = e->blob + S.alpha_off;
-    a.inv = e->blob + S.inv_off;
+    a.ab = reinterpret_cast<const float2*>(e->blob + S.ab_off);
     a.s = s;
     a.shift = shift;
     a.l_out = l_out;

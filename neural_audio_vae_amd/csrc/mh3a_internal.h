@@ -230,8 +230,7 @@ struct SnakeArgs {
     const float* x;
     int64_t x_bstride;
     int c, l;
-    const float* alpha;  // [c]
-    const float* inv;    // [c] 1 / (alpha + 1e-9)
+    const float2* ab;    // [c]: (alpha / pi, 0.5 / (alpha + 1e-9))
     int s, shift, l_out;
     float* y;
     int64_t y_bstride;

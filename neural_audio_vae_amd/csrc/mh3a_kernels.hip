@@ -1888,7 +1888,9 @@ hipError_t launch_split(const ActArgs& a, int batch, hipStream_t stream) {
 
 // Plain Snake with an optional space-to-depth regrouping (encoder):
 // output channel c s + r at position t holds snake(x[c, t s + r - shift]),
-// snake(v) = v + sin^2(alpha v) / (alpha + 1e-9), zero outside [0, l) (the
+// snake(v) = v + sin^2(alpha v) / (alpha + 1e-9) = v + hb (1 - cos(2 alpha v))
+// with hb = 0.5 / (alpha + 1e-9), the cosine on the hardware unit as in
+// snake_beta; zero outside [0, l) (the
 // Snake of a zero is zero, so padding before or after it is the same).
 // Packed output: one padded position of one 8-channel chunk per thread, as
 // split_kernel. Plain output: one (channel, position) per thread.
@@ -1896,9 +1898,8 @@ __device__ __forceinline__ float snake_at(const SnakeArgs& a, const float* xb, i
     const int c = oc / a.s, r = oc - c * a.s;
     const int64_t n = (int64_t)t * a.s + r - a.shift;
     if (c >= a.c || t < 0 || t >= a.l_out || n < 0 || n >= a.l) return 0.0f;
-    const float v = xb[(int64_t)c * a.l + n];
-    const float sn = sinf(a.alpha[c] * v);
-    return fmaf(sn * sn, a.inv[c], v);
+    const float2 ab = a.ab[c];
+    return snake_beta(xb[(int64_t)c * a.l + n], ab.x, ab.y);
 }
 
 __global__ void __launch_bounds__(256) snake_packed_kernel(SnakeArgs a) {
