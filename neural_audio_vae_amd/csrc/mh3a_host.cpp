@@ -1095,15 +1095,17 @@ void pack_conv_weights16(const float* w, int c_out, int c_in, int taps, float* o
             }
 }
 
-// Split-product weights for v_mfma_f32_32x32x16_bf16: for 32-row block mb,
-// chunk ch, tap pair q, piece p and lane l, the 8 bf16 values
-// piece_p(W[mb*32 + l%32, ch*8 + i, 2q + l/32]), i = 0..7 (zero past c_out,
-// c_in or the last tap), at 16-byte group ((mb * nch + ch) * npairs + q) *
-// kPieces + p) * 64 + l. Pieces: v0 = bf16(v), v1 = bf16(v - v0),
-// v2 = bf16(v - v0 - v1), rounded to nearest even.
+// Split-product weights for v_mfma_f32_32x32x16_bf16. The (chunk, tap)
+// slots of a 32-row block run chunk-major, s = chunk * taps + tap, and pair
+// P holds slots 2P (lanes 0-31) and 2P + 1 (lanes 32-63): for piece p and
+// lane l the 8 bf16 values piece_p(W[mb*32 + l%32, ch*8 + i, j]), i = 0..7,
+// with (ch, j) = divmod(2P + l/32, taps) (zero past c_out, c_in or the last
+// slot), at 16-byte group ((mb * npairs + P) * kPieces + p) * 64 + l.
+// Pieces: v0 = bf16(v), v1 = bf16(v - v0), v2 = bf16(v - v0 - v1), rounded to
+// nearest even.
 int64_t packed_weight_floats6(int c_out, int c_in, int taps) {
-    const int64_t nmb = (c_out + 31) / 32, nch = (c_in + kChunk - 1) / kChunk, np = (taps + 1) / 2;
-    return nmb * nch * np * kPieces * 64 * 4;
+    const int64_t nmb = (c_out + 31) / 32, nch = (c_in + kChunk - 1) / kChunk, np = (nch * taps + 1) / 2;
+    return nmb * np * kPieces * 64 * 4;
 }
 
 static uint32_t bf16_rne_bits(float v) {
@@ -1119,29 +1121,29 @@ static float bf16_bits_value(uint32_t b) {
 }
 
 void pack_conv_weights6(const float* w, int c_out, int c_in, int taps, float* out) {
-    const int nmb = (c_out + 31) / 32, nch = (c_in + kChunk - 1) / kChunk, np = (taps + 1) / 2;
+    const int nmb = (c_out + 31) / 32, nch = (c_in + kChunk - 1) / kChunk, np = (nch * taps + 1) / 2;
     uint32_t* o = reinterpret_cast<uint32_t*>(out);
     for (int mb = 0; mb < nmb; ++mb)
-        for (int ch = 0; ch < nch; ++ch)
-            for (int q = 0; q < np; ++q)
-                for (int l = 0; l < 64; ++l) {
-                    uint16_t pc[kPieces][kChunk];
-                    for (int i = 0; i < kChunk; ++i) {
-                        const int m = mb * 32 + (l & 31), c = ch * kChunk + i, j = 2 * q + (l >> 5);
-                        const float v = (m < c_out && c < c_in && j < taps) ? w[((int64_t)m * c_in + c) * taps + j] : 0.0f;
-                        const uint32_t p0 = bf16_rne_bits(v);
-                        const float r1 = v - bf16_bits_value(p0);
-                        const uint32_t p1 = bf16_rne_bits(r1);
-                        const uint32_t p2 = bf16_rne_bits(r1 - bf16_bits_value(p1));
-                        pc[0][i] = (uint16_t)p0;
-                        pc[1][i] = (uint16_t)p1;
-                        pc[2][i] = (uint16_t)p2;
-                    }
-                    for (int p = 0; p < kPieces; ++p) {
-                        uint32_t* g = o + ((((int64_t)mb * nch + ch) * np + q) * kPieces + p) * 256 + l * 4;
-                        for (int k = 0; k < 4; ++k) g[k] = (uint32_t)pc[p][2 * k] | ((uint32_t)pc[p][2 * k + 1] << 16);
-                    }
+        for (int q = 0; q < np; ++q)
+            for (int l = 0; l < 64; ++l) {
+                const int slot = 2 * q + (l >> 5), ch = slot / taps, j = slot % taps;
+                uint16_t pc[kPieces][kChunk];
+                for (int i = 0; i < kChunk; ++i) {
+                    const int m = mb * 32 + (l & 31), c = ch * kChunk + i;
+                    const float v = (m < c_out && ch < nch && c < c_in) ? w[((int64_t)m * c_in + c) * taps + j] : 0.0f;
+                    const uint32_t p0 = bf16_rne_bits(v);
+                    const float r1 = v - bf16_bits_value(p0);
+                    const uint32_t p1 = bf16_rne_bits(r1);
+                    const uint32_t p2 = bf16_rne_bits(r1 - bf16_bits_value(p1));
+                    pc[0][i] = (uint16_t)p0;
+                    pc[1][i] = (uint16_t)p1;
+                    pc[2][i] = (uint16_t)p2;
                 }
+                for (int p = 0; p < kPieces; ++p) {
+                    uint32_t* g = o + ((((int64_t)mb * np + q) * kPieces + p) * 64 + l) * 4;
+                    for (int k = 0; k < 4; ++k) g[k] = (uint32_t)pc[p][2 * k] | ((uint32_t)pc[p][2 * k + 1] << 16);
+                }
+            }
 }
 
 // Split-product weights of the unit kernel (v_mfma_f32_16x16x32_bf16): for
@@ -1666,21 +1668,8 @@ int enc_conv(Blob& blob, const Table& t, const std::string& prefix, ConvLayer& L
     L.alg_taps = k;
     L.kind = kind;
     if (enc_split_ok(L)) {
-        if (k == 1) {
-            // pointwise: packed as a 2-tap conv over c_in / 2 channels (chunk pairs, see bx6_cpi)
-            std::vector<float> w2((size_t)c_out * c_in);
-            for (int o = 0; o < c_out; ++o)
-                for (int kc = 0; kc < c_in / (2 * kChunk); ++kc)
-                    for (int i = 0; i < kChunk; ++i)
-                        for (int j = 0; j < 2; ++j)
-                            w2[((size_t)o * (c_in / 2) + kc * kChunk + i) * 2 + j] =
-                                w[(size_t)o * c_in + (2 * kc + j) * kChunk + i];
-            L.w6_off = blob.reserve(packed_weight_floats6(c_out, c_in / 2, 2));
-            pack_conv_weights6(w2.data(), c_out, c_in / 2, 2, blob.h.data() + L.w6_off);
-        } else {
-            L.w6_off = blob.reserve(packed_weight_floats6(c_out, c_in, k));
-            pack_conv_weights6(w.data(), c_out, c_in, k, blob.h.data() + L.w6_off);
-        }
+        L.w6_off = blob.reserve(packed_weight_floats6(c_out, c_in, k));
+        pack_conv_weights6(w.data(), c_out, c_in, k, blob.h.data() + L.w6_off);
     }
     return MH3A_OK;
 }

@@ -90,9 +90,9 @@ constexpr int kBx6WideDil = 9;
 // four on 256-wide tiles (LDS), so each item still carries eight pairs of
 // matrix-core work. The chunks of a K range must be a multiple of it.
 constexpr int bx6_cpi(int nwg, int taps) { return taps <= 2 ? (nwg <= 128 ? 8 : 4) : 2; }
-// Pointwise (1-tap) split-product convs pair two chunks per matrix-core
-// instruction instead of two taps: their weights are packed as a 2-tap conv
-// over c_in / 2 channels, w2[o][8 k + i][j] = w[o][8 (2 k + j) + i].
+// (A matrix-core instruction of a split-product conv takes two consecutive
+// (chunk, tap) slots, which for odd tap counts may lie in two chunks; see
+// pack_conv_weights6.)
 
 // Tile shapes of the conv kernel: four consumer waves arranged WM x WN,
 // each computing MBW x NBW blocks of 32 x 32 outputs.

@@ -324,8 +324,6 @@ conv_kernel(ConvArgs a) {
     // an item is CPI chunks (split products: two, so that each barrier hands
     // over as much matrix-core work as an fp32 item)
     constexpr int CPI = BX6 ? bx6_cpi(NWG, TAPS) : 1;
-    // pointwise split products: a pair spans two chunks (see bx6_cpi)
-    constexpr bool CP1 = BX6 && TAPS == 1;
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -536,16 +534,16 @@ conv_kernel(ConvArgs a) {
     float4 An[MBW];
 
     // Split products (PREC 2): v_mfma_f32_32x32x16_bf16 with K = 16 = two
-    // taps x the chunk's 8 channels. Lane l holds, for piece p, the A values
-    // W[m = l % 32][chunk channel i][tap 2q + l / 32] and the B values of the
-    // chunk's 8 channels at position n + (2q + l / 32) dil: one 16-byte read
-    // per piece and block. An odd tap count pads the last pair with zero
-    // weights (its upper half reads tap 2q again, so no read leaves the
-    // window). Weights ride a three-slot ring two pairs ahead.
+    // (chunk, tap) slots x 8 channels. The slots of a K range run chunk-major,
+    // s = chunk * TAPS + tap, and instruction u of an item takes slots 2u and
+    // 2u + 1: lane l holds, for piece p, the A values W[m = l % 32][channel i
+    // of the chunk of slot 2u + l / 32][its tap] and the B values of that
+    // chunk's 8 channels at position n + tap dil: one 16-byte read per piece
+    // and block. With an odd tap count a pair may span two chunks, so no slot
+    // is padding. Weights ride a three-slot ring two pairs ahead.
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-    constexpr int NP6 = (TAPS + 1) / 2;
-    const int G6 = CP1 ? nch / 2 : nch * NP6;  // weight groups per 32-row block
+    const int G6 = nch * (TAPS > 0 ? TAPS : 1) / 2;  // weight groups (slot pairs) per 32-row block
     v4u A6a[BX6 ? kPieces : 1][MBW], A6b[BX6 ? kPieces : 1][MBW], A6c[BX6 ? kPieces : 1][MBW];
     auto load_a6 = [&](v4u (&dst)[BX6 ? kPieces : 1][MBW], int mb_base, int ph, int g) {
         const v4u* wp = reinterpret_cast<const v4u*>(a.w6 + (int64_t)ph * a.w6_phase_stride) + (int64_t)g * kPieces * 64 + lane;
@@ -784,7 +782,7 @@ conv_kernel(ConvArgs a) {
     float4 Ar0[MBW], Ar1[MBW], Ar2[MBW];
     if constexpr (BX6) {
         const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
-        const int g0 = CP1 ? cur.c0 / 2 : cur.c0 * NP6;
+        const int g0 = cur.c0 * TAPS / 2;
         load_a6(A6a, mb0, cur.ph, g0);
         load_a6(A6b, mb0, cur.ph, g0 + 1);
     } else if constexpr (TAPS > 0) {
@@ -815,21 +813,18 @@ conv_kernel(ConvArgs a) {
         const int g0 = (cur.c0 + cur_c) * a.taps;
         if constexpr (BX6) {
             const int nmb_base = __builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW);
-            // the item's CPI chunks: pair u = cc NP6 + q is weight group q0 + u
-            // (pointwise: pair u = chunks 2u, 2u + 1 is weight group q0 + u)
-            constexpr int NPI = CP1 ? CPI / 2 : CPI * NP6;
-            static_assert(NPI >= 2, "the weight ring holds two pairs ahead");
-            const int q0 = CP1 ? (cur.c0 + CPI * cur_c) / 2 : (cur.c0 + CPI * cur_c) * NP6;
-            const int nq0 = has_next ? (CP1 ? (nxt.c0 + CPI * nxt_c) / 2 : (nxt.c0 + CPI * nxt_c) * NP6) : q0;
+            // the item's CPI chunks hold CPI * TAPS slots: pair u is weight group q0 + u
+            constexpr int NPI = CPI * TAPS / 2;
+            static_assert((CPI * TAPS) % 2 == 0 && NPI >= 2, "whole slot pairs; the ring holds two ahead");
+            const int q0 = (cur.c0 + CPI * cur_c) * TAPS / 2;
+            const int nq0 = has_next ? (nxt.c0 + CPI * nxt_c) * TAPS / 2 : q0;
             const int nmb = has_next ? nmb_base : mb_base;
             const int nph6 = has_next ? nxt.ph : cur.ph;
-            const float* bb_h = cur_buf + (colbase + hi * a.dil) * 4;  // this lane's tap of each pair
-            const float* bb_0 = cur_buf + colbase * 4;                 // the pair's first tap
+            const float* bb_0 = cur_buf + colbase * 4;
             // slots 0 and 1 hold pairs 0 and 1 on entry; pair u + 2 (or the next
             // item's pair u + 2 - NPI) loads while pair u multiplies
 #pragma unroll
             for (int u = 0; u < NPI; ++u) {
-                const int q = u % NP6, cc = u / NP6;
                 v4u(&use)[kPieces][MBW] = (u % 3 == 0) ? A6a : ((u % 3 == 1) ? A6b : A6c);
                 v4u(&fill)[kPieces][MBW] = ((u + 2) % 3 == 0) ? A6a : (((u + 2) % 3 == 1) ? A6b : A6c);
                 if (u + 2 < NPI) {
@@ -838,10 +833,10 @@ conv_kernel(ConvArgs a) {
                     load_a6(fill, nmb, nph6, nq0 + (u + 2 - NPI));
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                const bool pad = (TAPS & 1) && q == NP6 - 1;
-                // pointwise: lanes of half hi read chunk 2u + hi at the lane's position
-                const float* bq = CP1 ? bb_0 + (2 * u + hi) * kPieces * PS6 * 4
-                                      : (pad ? bb_0 : bb_h) + (cc * kPieces * PS6 + 2 * q * a.dil) * 4;
+                const int s0 = 2 * u, s1 = 2 * u + 1;
+                const int off0 = (s0 / TAPS) * kPieces * PS6 + (s0 % TAPS) * a.dil;
+                const int off1 = (s1 / TAPS) * kPieces * PS6 + (s1 % TAPS) * a.dil;
+                const float* bq = bb_0 + (hi ? off1 : off0) * 4;
                 v4u Bv[kPieces][NBW];
 #pragma unroll
                 for (int p = 0; p < NPA; ++p)
