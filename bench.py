@@ -21,7 +21,7 @@ second, untimed pass with every launch bracketed gives the per-class
 breakdown). Its peak is the fp32-equivalent rate of that scheme: the dense
 bf16 matrix peak over six products; with MH3A_BX6=0 (fp32 matrix cores) it
 is the fp32 matrix peak.
-`cpu_baseline` times the CPU oracle on a bounded sample (the first 80
+`cpu_baseline` times the CPU oracle on a bounded sample (the first 320
 latents of one item, decoded in full).
 """
 
@@ -67,8 +67,8 @@ def parse():
     ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + sorted(ENC_WORKLOADS))
     ap.add_argument("--bf16", action="store_true", help="bf16-split matrix-core operands (MH3A_FLAG_BF16_MFMA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-latents", type=int, default=80, help="latents in the oracle's timed sample")
-    ap.add_argument("--cpu-samples", type=int, default=16000, help="samples in the oracle's timed encode sample")
+    ap.add_argument("--cpu-latents", type=int, default=320, help="latents in the oracle's timed sample")
+    ap.add_argument("--cpu-samples", type=int, default=128000, help="samples in the oracle's timed encode sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -89,12 +89,17 @@ def copy_probe(nbytes):
 
 
 def measured_traffic(workload, flags):
-    """HBM bytes per AMP-conv launch from the committed rocprofv3 counter
-    runs (profiles/amp_conv_c3_traffic.json), or None when the kernel
-    sources changed since the counters were taken or the workload differs."""
+    """HBM bytes per launch of the roofline kernel from the committed
+    rocprofv3 counter runs (profiles/amp_conv_c3_traffic.json for the
+    decode's AMP convs, profiles/enc_unit_conv_e3_traffic.json for the
+    encoder's k7 convs), or None when the kernel sources changed since the
+    counters were taken or the workload differs."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "amp_conv_c3_traffic.json")
-    if workload != "c3" or flags & 0x2 or not os.path.exists(path):
+    files = {"c3": "amp_conv_c3_traffic.json", "e3": "enc_unit_conv_e3_traffic.json"}
+    if workload not in files or flags & 0x2 or os.environ.get("MH3A_BX6") == "0":
+        return None
+    path = os.path.join(ROOT, "profiles", files[workload])
+    if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     h = hashlib.sha256()
@@ -360,7 +365,7 @@ def main_encode(args):
                            else "dense fp32 matrix peak"),
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload, 0),
             "launches_timed": k7["launches"],
             "avg_launch_us": round(1e3 * k7["ms"] / max(1, k7["launches"]), 2),
             "flops_per_launch": k7["flops"] / max(1, k7["launches"]),
