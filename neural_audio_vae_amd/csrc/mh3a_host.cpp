@@ -334,7 +334,7 @@ void add_conv(Blob& blob, ConvLayer& L, const std::vector<float>& w, const float
 bool split_input_ok(const ConvLayer& L) {
     if (!(L.taps == 2 || L.taps == 3 || L.taps == 7 || L.taps == 11)) return false;
     if (L.c_in % 16 || L.c_out < 32 || L.dil < 1 || L.dil > kBx6MaxDil) return false;
-    if (L.taps <= 2 && (L.c_in / kChunk) % bx6_cpi(128, L.taps)) return false;  // whole items of 8 chunks
+    if ((L.c_in / kChunk) % bx6_cpi(128, L.taps)) return false;  // whole pipeline items
     for (int ph = 0; ph < L.phases; ++ph)
         if (-L.in_off[ph] > kPkPadL || 255 + (L.taps - 1) * L.dil + L.in_off[ph] > kPkPadR) return false;
     return true;
@@ -439,7 +439,7 @@ bool amp_act_fused(const mh3a_decoder* d, int64_t batch, int64_t c, int64_t len)
 // (with the bf16 operand flag the convs take the three-product variant)
 bool stage_px(const mh3a_decoder* d, int64_t batch, int c, int64_t len, bool bf16) {
     (void)bf16;
-    return !amp_act_fused(d, batch, c, len) && use_bx6(d) && c % 16 == 0;
+    return !amp_act_fused(d, batch, c, len) && use_bx6(d) && c % 64 == 0;  // whole items of up to 8 chunks
 }
 
 // Whether conv_pre / a transposed conv reads its input in the split-product
@@ -1649,7 +1649,7 @@ bool enc_split_ok(const ConvLayer& L) {
     const bool taps_ok = L.taps == 1 || L.taps == 2 || L.taps == 3 || (L.taps == 7 && L.dil <= kBx6WideDil) ||
                          (L.taps == 11 && L.dil <= kBx6MaxDil);
     if (!taps_ok || L.c_in % 16 || L.c_out < 32 || L.dil < 1) return false;
-    if (L.taps <= 2 && (L.c_in / kChunk) % bx6_cpi(128, L.taps)) return false;  // whole items of 8 chunks
+    if ((L.c_in / kChunk) % bx6_cpi(128, L.taps)) return false;  // whole pipeline items
     return -L.in_off[0] <= kPkPadL && 255 + (L.taps - 1) * L.dil + L.in_off[0] <= kPkPadR;
 }
 

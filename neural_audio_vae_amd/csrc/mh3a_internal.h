@@ -86,10 +86,11 @@ constexpr int kBx6MaxDil = 5;
 // Dilation bound of the wider-plane instances (7 taps; the encoder's units).
 constexpr int kBx6WideDil = 9;
 // Chunks per pipeline item of a split-product conv with output tiles nwg
-// wide: two for 3+ taps; for 1 or 2 taps (one tap pair per chunk) eight, or
-// four on 256-wide tiles (LDS), so each item still carries eight pairs of
-// matrix-core work. The chunks of a K range must be a multiple of it.
-constexpr int bx6_cpi(int nwg, int taps) { return taps <= 2 ? (nwg <= 128 ? 8 : 4) : 2; }
+// wide, so that one barrier hands over at least six instruction pairs: 1 or
+// 2 taps eight chunks (four on 256-wide tiles, for LDS), 3 and 7 taps four
+// (measured ~1% faster than two), 11 taps two. The chunks of a K range must
+// be a multiple of it.
+constexpr int bx6_cpi(int nwg, int taps) { return taps <= 2 ? (nwg <= 128 ? 8 : 4) : (taps <= 7 ? 4 : 2); }
 // (A matrix-core instruction of a split-product conv takes two consecutive
 // (chunk, tap) slots, which for odd tap counts may lie in two chunks; see
 // pack_conv_weights6.)
