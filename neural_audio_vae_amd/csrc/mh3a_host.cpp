@@ -334,7 +334,7 @@ void add_conv(Blob& blob, ConvLayer& L, const std::vector<float>& w, const float
 bool split_input_ok(const ConvLayer& L) {
     if (!(L.taps == 2 || L.taps == 3 || L.taps == 7 || L.taps == 11)) return false;
     if (L.c_in % 16 || L.c_out < 32 || L.dil < 1 || L.dil > kBx6MaxDil) return false;
-    if ((L.c_in / kChunk) % bx6_cpi(128, L.taps)) return false;  // whole pipeline items
+    if ((L.c_in / kChunk) % bx6_cpi_max(L.taps)) return false;  // whole pipeline items
     for (int ph = 0; ph < L.phases; ++ph)
         if (-L.in_off[ph] > kPkPadL || 255 + (L.taps - 1) * L.dil + L.in_off[ph] > kPkPadR) return false;
     return true;
@@ -1649,7 +1649,7 @@ bool enc_split_ok(const ConvLayer& L) {
     const bool taps_ok = L.taps == 1 || L.taps == 2 || L.taps == 3 || (L.taps == 7 && L.dil <= kBx6WideDil) ||
                          (L.taps == 11 && L.dil <= kBx6MaxDil);
     if (!taps_ok || L.c_in % 16 || L.c_out < 32 || L.dil < 1) return false;
-    if ((L.c_in / kChunk) % bx6_cpi(128, L.taps)) return false;  // whole pipeline items
+    if ((L.c_in / kChunk) % bx6_cpi_max(L.taps)) return false;  // whole pipeline items
     return -L.in_off[0] <= kPkPadL && 255 + (L.taps - 1) * L.dil + L.in_off[0] <= kPkPadR;
 }
 

@@ -86,11 +86,17 @@ constexpr int kBx6MaxDil = 5;
 // Dilation bound of the wider-plane instances (7 taps; the encoder's units).
 constexpr int kBx6WideDil = 9;
 // Chunks per pipeline item of a split-product conv with output tiles nwg
-// wide, so that one barrier hands over at least six instruction pairs: 1 or
-// 2 taps eight chunks (four on 256-wide tiles, for LDS), 3 and 7 taps four
-// (measured ~1% faster than two), 11 taps two. The chunks of a K range must
-// be a multiple of it.
-constexpr int bx6_cpi(int nwg, int taps) { return taps <= 2 ? (nwg <= 128 ? 8 : 4) : (taps <= 7 ? 4 : 2); }
+// wide: eight for up to 7 taps and four for more (2 to 28 instruction pairs
+// per barrier), halved until the two item buffers fit 156 KB of LDS
+// (256-wide tiles). Measured against two chunks per item for
+// 3+ taps: about 1% faster. The chunks of a K range must be a multiple of it.
+constexpr int bx6_cpi(int nwg, int taps, int dmax = kBx6MaxDil) {
+    int c = taps <= 7 ? 8 : 4;
+    while (c > 2 && 2 * c * kPieces * (nwg + (taps - 1) * dmax) * 16 > 156 * 1024) c /= 2;
+    return c;
+}
+// The largest item any tile uses for a tap count (eligibility: whole items).
+constexpr int bx6_cpi_max(int taps) { return bx6_cpi(32, taps, 1); }
 // (A matrix-core instruction of a split-product conv takes two consecutive
 // (chunk, tap) slots, which for odd tap counts may lie in two chunks; see
 // pack_conv_weights6.)

@@ -278,7 +278,7 @@ __host__ __device__ constexpr int conv_lds_floats(int W, bool act) {
 // compile-time constants.
 __host__ __device__ constexpr int bx6_plane(int nwg, int taps, int dmax = kBx6MaxDil) { return nwg + (taps - 1) * dmax; }
 __host__ __device__ constexpr int conv_lds_floats6(int nwg, int taps, int dmax = kBx6MaxDil) {
-    return 2 * bx6_cpi(nwg, taps) * kPieces * bx6_plane(nwg, taps, dmax) * 4 + kTouchFloats;  // two item buffers
+    return 2 * bx6_cpi(nwg, taps, dmax) * kPieces * bx6_plane(nwg, taps, dmax) * 4 + kTouchFloats;  // two item buffers
 }
 
 // Wave-specialized, persistent implicit-GEMM conv. 512 threads: waves 0-3
@@ -323,7 +323,7 @@ conv_kernel(ConvArgs a) {
     constexpr int PS6 = bx6_plane(NWG, TAPS > 0 ? TAPS : 1, DMAX);  // split-product plane stride (positions)
     // an item is CPI chunks (split products: two, so that each barrier hands
     // over as much matrix-core work as an fp32 item)
-    constexpr int CPI = BX6 ? bx6_cpi(NWG, TAPS) : 1;
+    constexpr int CPI = BX6 ? bx6_cpi(NWG, TAPS, DMAX) : 1;
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;

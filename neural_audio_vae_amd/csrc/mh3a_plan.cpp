@@ -144,7 +144,7 @@ ConvPlan plan_conv(const ConvShape& L, int positions, int batch, bool bf16, bool
     double best = 1e300;
     for (int S = 1; S <= 64 && S <= nch; S *= 2) {
         if (nch % S) continue;
-        if (L.bx6 && (nch / S) % bx6_cpi(128, L.taps)) continue;  // whole split-product items (<= 8 chunks)
+        if (L.bx6 && (nch / S) % bx6_cpi_max(L.taps)) continue;  // whole split-product items (<= 8 chunks)
         const TileId t = choose_tile(L, positions, item_groups, bf16, S, num_cus);
         // the batch's own tile must keep the partials bounded too
         const TileId tb = choose_tile(L, positions, batch * L.phases, bf16, S, num_cus);
