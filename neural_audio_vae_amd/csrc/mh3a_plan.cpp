@@ -84,7 +84,10 @@ TileId choose_tile(const ConvShape& L, int positions, int groups, bool bf16, int
         // pointwise convs of 64-127 outputs: one row block per wave (its
         // batched epilogue; measured 18% faster on the HBM-bound 64-channel case)
         if (L.taps == 1 && L.c_out >= 64 && L.c_out < 128) return TILE_64x256R;
-        return L.c_out >= 128 ? TILE_128x128R : (L.c_out >= 64 ? TILE_64x256 : TILE_32x256);
+        // (128 x 160 tiles from 128 outputs: measured 1.3% faster on the
+        // encoder than 128 x 128, even on the decoder's conv_pre and
+        // transposed convs)
+        return L.c_out >= 128 ? TILE_128x160R : (L.c_out >= 64 ? TILE_64x256 : TILE_32x256);
     }
     if (forced_tile() >= 0) {
         const TileShape s = tile_shape((TileId)forced_tile());
