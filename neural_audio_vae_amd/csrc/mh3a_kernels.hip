@@ -959,6 +959,45 @@ conv_kernel(ConvArgs a) {
                     // in-place updates: no output is read after another one
                     // has been written; per-workgroup time measured 4% lower).
                     const int64_t ybase = (int64_t)cur.b * a.y_bstride;
+                    if (!a.sum_in) {
+                        // no running sum (the encoder's convs, conv_pre, the
+                        // transposed convs): the residual loads of three
+                        // blocks at a time go out together (all NBW would
+                        // spill registers), so a tile pays ceil(NBW / 3)
+                        // memory round trips
+                        constexpr int EG = 3;
+#pragma unroll
+                        for (int g0 = 0; g0 < NBW; g0 += EG) {
+                            float rv[EG][16];
+#pragma unroll
+                            for (int k = 0; k < EG; ++k) {
+                                if (g0 + k >= NBW) break;
+                                const int pos = cur.p0 + wn * NBW * 32 + (g0 + k) * 32 + lo;
+                                const bool pos_ok = pos < a.positions;
+                                const int tt = a.out_mul * pos + a.out_add[cur.ph];
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const int o = mb_base * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                                    const int64_t idx =
+                                        (pos_ok && o < a.c_out) ? ybase + (int64_t)o * ostride + tt : ybase;
+                                    rv[k][r] = a.res ? a.res[idx] : 0.0f;
+                                }
+                            }
+#pragma unroll
+                            for (int k = 0; k < EG; ++k) {
+                                if (g0 + k >= NBW) break;
+                                const int pos = cur.p0 + wn * NBW * 32 + (g0 + k) * 32 + lo;
+                                const bool pos_ok = pos < a.positions;
+                                const int tt = a.out_mul * pos + a.out_add[cur.ph];
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const int o = mb_base * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                                    if (!(pos_ok && o < a.c_out)) continue;
+                                    a.y[ybase + (int64_t)o * ostride + tt] = (acc[0][g0 + k][r] + rv[k][r]) * a.scale;
+                                }
+                            }
+                        }
+                    } else
 #pragma unroll
                     for (int mb = 0; mb < MBW; ++mb) {
 #pragma unroll
