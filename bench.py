@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + sorted(ENC_WORKLOADS))
     ap.add_argument("--bf16", action="store_true", help="bf16-split matrix-core operands (MH3A_FLAG_BF16_MFMA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time K replays of one decode captured in a HIP graph (graph_ms_per_step)")
     ap.add_argument("--cpu-latents", type=int, default=320, help="latents in the oracle's timed sample")
     ap.add_argument("--cpu-samples", type=int, default=128000, help="samples in the oracle's timed encode sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -253,6 +255,27 @@ def main():
         "kernels": per_step,
         "wall_s_timed": round(wall, 4),
     }
+    if args.graph:
+        # one decode captured on a side stream (after a warm-up call there),
+        # then K replays between synchronizations: the launch overhead of the
+        # ~130 kernels goes away, which matters for the small workloads
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            dec.decode(z, flags=flags, out=out, stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            dec.decode(z, flags=flags, out=out, stream=s)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        line["graph_ms_per_step"] = round((time.perf_counter() - t0) / args.steps * 1e3, 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(params, args.cpu_latents)
     print(json.dumps(line), flush=True)

@@ -23,7 +23,12 @@ def _torch():
 
 class Decoder:
     """A decoder built once from host parameters (weight norm folded and
-    filters designed at construction)."""
+    filters designed at construction).
+
+    The decode only enqueues kernels on the given stream (no allocation,
+    memset or synchronization inside), so a call can be captured into a HIP
+    graph (torch.cuda.graph) once a first call of the same shape has sized
+    the workspace; workspaces are kept until close()."""
 
     def __init__(self, params, config=None, latents_mean=None, latents_std=None, device=0):
         self.config = dict(config or {})
@@ -34,11 +39,13 @@ class Decoder:
         self.num_ups = cfg.num_ups
         self._h = _lib.mh3a_decoder_create(cfg, params, latents_mean, latents_std, self.device)
         self._ws = None
+        self._old_ws = []
 
     def close(self):
         if getattr(self, "_h", None):
             _lib.mh3a_destroy(self._h)
             self._h = None
+        self._ws, self._old_ws = None, []
 
     def __del__(self):
         try:
@@ -49,6 +56,10 @@ class Decoder:
     def _workspace(self, nbytes):
         torch = _torch()
         if self._ws is None or self._ws.numel() < nbytes:
+            # a captured HIP graph may still use the previous buffer: keep it
+            # until close()
+            if self._ws is not None:
+                self._old_ws.append(self._ws)
             self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=f"cuda:{self.device}")
         return self._ws
 
@@ -148,11 +159,13 @@ class Encoder:
         self.latent_dim = cfg.latent_dim
         self._h = _lib.mh3a_encoder_create(cfg, params, self.device)
         self._ws = None
+        self._old_ws = []
 
     def close(self):
         if getattr(self, "_h", None):
             _lib.mh3a_encoder_destroy(self._h)
             self._h = None
+        self._ws, self._old_ws = None, []
 
     def __del__(self):
         try:
@@ -176,6 +189,8 @@ class Encoder:
             out = torch.empty((b, self.latent_dim, self.frames(s)), dtype=torch.float32, device=x.device)
         nbytes = self.workspace_size(b, s, flags)
         if self._ws is None or self._ws.numel() < nbytes:
+            if self._ws is not None:
+                self._old_ws.append(self._ws)  # a captured graph may still use it
             self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=f"cuda:{self.device}")
         st = (stream or torch.cuda.current_stream(x.device)).cuda_stream
         _lib.mh3a_encode_hidden(self._h, x.data_ptr(), b, s, out.data_ptr(), self._ws.data_ptr(), self._ws.numel(),
