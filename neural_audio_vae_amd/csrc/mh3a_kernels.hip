@@ -251,10 +251,10 @@ __device__ __forceinline__ float round_bf16(float v) {
     return __uint_as_float(u);
 }
 
-// Upper 16 bits of v rounded to nearest even: bf16(v) as raw bits.
+// bf16(v) rounded to nearest even, as raw bits: one v_cvt_pk_bf16_f32 on
+// gfx950 (the same bits as (u + 0x7fff + ((u >> 16) & 1)) >> 16 for finite v).
 __device__ __forceinline__ unsigned bf16_bits(float v) {
-    const unsigned u = __float_as_uint(v);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return __builtin_bit_cast(unsigned short, (__bf16)v);
 }
 // The three bf16 pieces of v (raw bits): v0 = bf16(v), v1 = bf16(v - v0),
 // v2 = bf16(v - v0 - v1); both differences are exact in fp32.
