@@ -256,6 +256,34 @@ __device__ __forceinline__ float round_bf16(float v) {
 __device__ __forceinline__ unsigned bf16_bits(float v) {
     return __builtin_bit_cast(unsigned short, (__bf16)v);
 }
+// bf16(a) | bf16(b) << 16, both rounded to nearest even: one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ unsigned bf16x2_bits(float a, float b) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 v = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf2));
+}
+// The three bf16 pieces of 8 values (see split3_bf16) as three 16-byte
+// groups, g[p] = piece p of v[0..7]; channel pairs share each conversion.
+__device__ __forceinline__ void split3_pack8(const float (&v)[8], uint4 (&g)[3]) {
+    unsigned w[3][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float a = v[2 * k], b = v[2 * k + 1];
+        unsigned p = bf16x2_bits(a, b);
+        w[0][k] = p;
+        a -= __uint_as_float(p << 16);
+        b -= __uint_as_float(p & 0xffff0000u);
+        p = bf16x2_bits(a, b);
+        w[1][k] = p;
+        a -= __uint_as_float(p << 16);
+        b -= __uint_as_float(p & 0xffff0000u);
+        w[2][k] = bf16x2_bits(a, b);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) g[p] = make_uint4(w[p][0], w[p][1], w[p][2], w[p][3]);
+}
 // The three bf16 pieces of v (raw bits): v0 = bf16(v), v1 = bf16(v - v0),
 // v2 = bf16(v - v0 - v1); both differences are exact in fp32.
 __device__ __forceinline__ void split3_bf16(float v, unsigned& p0, unsigned& p1, unsigned& p2) {
@@ -1366,18 +1394,14 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
         for (int w = threadIdx.x; w < W; w += 256) {
             const int q = t0 + kPkPadL + w;
             if (q >= a.lp) continue;
-            unsigned pc[kPieces][CI];
+            static_assert(CI == 8, "one 16-byte group per piece");
+            float v8[8];
 #pragma unroll
-            for (int c = 0; c < CI; ++c) split3_bf16(as[c * XS + w], pc[0][c], pc[1][c], pc[2][c]);
+            for (int c = 0; c < CI; ++c) v8[c] = as[c * XS + w];
+            uint4 g[kPieces];
+            split3_pack8(v8, g);
 #pragma unroll
-            for (int p = 0; p < kPieces; ++p) {
-                uint4 v;
-                v.x = pc[p][0] | (pc[p][1] << 16);
-                v.y = pc[p][2] | (pc[p][3] << 16);
-                v.z = pc[p][4] | (pc[p][5] << 16);
-                v.w = pc[p][6] | (pc[p][7] << 16);
-                *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = v;
-            }
+            for (int p = 0; p < kPieces; ++p) *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = g[p];
         }
         return;
     }
@@ -1652,13 +1676,13 @@ __device__ __forceinline__ void unit_pack6(const float* rows, int rs, int n, uin
     constexpr int CB = C / 8;
     for (int idx = threadIdx.x; idx < n * CB; idx += 256) {
         const int w = idx / CB, cb = idx - w * CB;
-        unsigned pw[kPieces][8];
+        float v8[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) split3_bf16(rows[(cb * 8 + i) * rs + w], pw[0][i], pw[1][i], pw[2][i]);
+        for (int i = 0; i < 8; ++i) v8[i] = rows[(cb * 8 + i) * rs + w];
+        uint4 g[kPieces];
+        split3_pack8(v8, g);
 #pragma unroll
-        for (int p = 0; p < kPieces; ++p)
-            pc[p * WP * CB + idx] = make_uint4(pw[p][0] | (pw[p][1] << 16), pw[p][2] | (pw[p][3] << 16),
-                                               pw[p][4] | (pw[p][5] << 16), pw[p][6] | (pw[p][7] << 16));
+        for (int p = 0; p < kPieces; ++p) pc[p * WP * CB + idx] = g[p];
     }
 }
 
@@ -1893,23 +1917,17 @@ __global__ void __launch_bounds__(256) split_kernel(ActArgs a) {
     const int n = q - kPkPadL;
     const bool in = n >= 0 && n < a.l;
     const float* xb = a.x + (int64_t)b * a.x_bstride;
-    unsigned pc[kPieces][kChunk];
+    float v8[kChunk];
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
         const int ch = chunk * kChunk + i;
-        const float v = (in && ch < a.c) ? xb[(int64_t)ch * a.l + n] : 0.0f;
-        split3_bf16(v, pc[0][i], pc[1][i], pc[2][i]);
+        v8[i] = (in && ch < a.c) ? xb[(int64_t)ch * a.l + n] : 0.0f;
     }
+    uint4 g[kPieces];
+    split3_pack8(v8, g);
     float* yc = a.y + (int64_t)b * a.y_bstride + (int64_t)chunk * kPieces * a.lp * 4;
 #pragma unroll
-    for (int p = 0; p < kPieces; ++p) {
-        uint4 v;
-        v.x = pc[p][0] | (pc[p][1] << 16);
-        v.y = pc[p][2] | (pc[p][3] << 16);
-        v.z = pc[p][4] | (pc[p][5] << 16);
-        v.w = pc[p][6] | (pc[p][7] << 16);
-        *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = v;
-    }
+    for (int p = 0; p < kPieces; ++p) *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = g[p];
 }
 
 hipError_t launch_split(const ActArgs& a, int batch, hipStream_t stream) {
@@ -1941,19 +1959,14 @@ __global__ void __launch_bounds__(256) snake_packed_kernel(SnakeArgs a) {
     const int chunk = blockIdx.y, b = blockIdx.z;
     if (q >= a.lp) return;
     const float* xb = a.x + (int64_t)b * a.x_bstride;
-    unsigned pc[kPieces][kChunk];
+    float v8[kChunk];
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) split3_bf16(snake_at(a, xb, chunk * kChunk + i, q - kPkPadL), pc[0][i], pc[1][i], pc[2][i]);
+    for (int i = 0; i < kChunk; ++i) v8[i] = snake_at(a, xb, chunk * kChunk + i, q - kPkPadL);
+    uint4 g[kPieces];
+    split3_pack8(v8, g);
     float* yc = a.y + (int64_t)b * a.y_bstride + (int64_t)chunk * kPieces * a.lp * 4;
 #pragma unroll
-    for (int p = 0; p < kPieces; ++p) {
-        uint4 v;
-        v.x = pc[p][0] | (pc[p][1] << 16);
-        v.y = pc[p][2] | (pc[p][3] << 16);
-        v.z = pc[p][4] | (pc[p][5] << 16);
-        v.w = pc[p][6] | (pc[p][7] << 16);
-        *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = v;
-    }
+    for (int p = 0; p < kPieces; ++p) *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = g[p];
 }
 
 __global__ void __launch_bounds__(256) snake_rows_kernel(SnakeArgs a) {
