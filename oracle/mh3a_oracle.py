@@ -18,13 +18,13 @@ What it computes is the decode path described on two pages:
   (the low-pass design).
 
 Numerics. The pages fix fp32 storage (``mlx_h3_audio_vae_from_dir`` refuses
-anything but fp32; "Waveforms are float32"), so every tensor between ops is
-float32. Inside each op the arithmetic is float64 and the op's output is
+anything but fp32, and the module overview gives waveforms as float32), so
+every tensor between ops is float32. Inside each op the arithmetic is float64 and the op's output is
 rounded to float32 once. Nothing is blocked, fused or reordered beyond what
 each definition states; numpy's float64 matmul serves as the inner sum of a
 convolution tap.
 
-Readings of what the pages leave open (each is listed in the design doc):
+Readings of what the pages leave open:
 
 * R1 ``_conv1d`` / ``_conv_transpose1d`` bodies are not shown: the standard
   PyTorch definitions (cross-correlation, zero padding, no output padding).
