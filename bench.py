@@ -142,8 +142,8 @@ def main():
     if args.copy_probe:
         return copy_probe(args.copy_probe)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the decode path runs on a single GPU).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the decode and encode paths run on a single GPU; see the sharding notes).", file=sys.stderr)
         return 2
     import torch
     from neural_audio_vae_amd import Decoder, _lib, synth
