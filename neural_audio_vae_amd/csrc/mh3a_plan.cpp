@@ -80,6 +80,9 @@ int forced_tile() {
 TileId choose_tile(const ConvShape& L, int positions, int groups, bool bf16, int ksplit, int num_cus) {
     // split products on a packed input (conv_pre, transposed convs): the
     // compile-time-tap shapes, by output width
+    // fp32 transposed convs of at most 16 outputs (the two narrowest stages):
+    // 32 x 256 tiles (measured 7% faster than the model's pick, 32 x 512)
+    if (!L.bx6 && !L.amp && L.phases > 1 && L.c_out <= 16 && forced_tile() < 0) return TILE_32x256;
     if (L.bx6 && !L.amp && forced_tile() < 0) {
         // pointwise convs of 64-127 outputs: one row block per wave (its
         // batched epilogue; measured 18% faster on the HBM-bound 64-channel case)
