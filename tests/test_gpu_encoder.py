@@ -126,6 +126,12 @@ def test_encoder_argument_errors(default_encoder):
         assert e.value.code == _lib.MH3A_E_INVALID_ARG
     with pytest.raises(_lib.MH3AError):
         _lib.mh3a_encode_hidden(enc._h, x.data_ptr(), 0, HOP, y.data_ptr(), ws.data_ptr(), need, 0, None)
+    # empty and oversized waveforms are refused before any launch
+    for samples in (0, -5, 1 << 31):
+        with pytest.raises(_lib.MH3AError) as e:
+            _lib.mh3a_encode_workspace_size(enc._h, 1, samples, 0)
+        assert e.value.code == _lib.MH3A_E_INVALID_ARG
+    assert _lib.mh3a_encode_frames(enc._h, 1) == 1 and _lib.mh3a_encode_frames(enc._h, 801) == 2
     torch.cuda.synchronize()
 
 
