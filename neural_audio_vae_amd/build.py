@@ -2,12 +2,16 @@
 
     python -m neural_audio_vae_amd.build
 
-compiles csrc/*.hip and csrc/*.cpp with hipcc into
-neural_audio_vae_amd/libmh3a.so (always recompiles).
+compiles csrc/*.hip and csrc/*.cpp with hipcc, one process per source (the
+conv kernel's tile shapes sit in translation units of their own so that
+they compile in parallel), and links neural_audio_vae_amd/libmh3a.so.
+Always recompiles.
 """
 
 from __future__ import annotations
 
+import concurrent.futures as cf
+import glob
 import os
 import shutil
 import subprocess
@@ -15,9 +19,14 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmh3a.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mh3a_host.cpp", "mh3a_plan.cpp", "mh3a_kernels.hip")]
+OBJ = os.path.join(PKG, "_build")
 ARCH = "gfx950"
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def hipcc():
@@ -27,24 +36,53 @@ def hipcc():
     raise RuntimeError("hipcc not found; the mh3a library needs the ROCm toolchain")
 
 
-def build(verbose=False):
-    tmp = LIB + ".tmp"
-    cmd = [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # keep the compiler from emitting packed fp32 VALU ops
+def compile_flags():
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        # keep the compiler from emitting packed fp32 VALU ops (the host
+        # pass warns that it does not know the feature; only the device
+        # pass acts on it)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-        "-o", tmp,
-    ] + SOURCES
+        "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    ]
+
+
+def _compile(src, verbose):
+    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + compile_flags() + ["-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    return src, obj, res
+
+
+def build(verbose=False, jobs=None):
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(16, os.cpu_count() or 1)
+    objs, failed = [], []
+    # the largest translation units first
+    order = sorted(srcs, key=lambda s: -os.path.getsize(s))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        for src, obj, res in ex.map(lambda s: _compile(s, verbose), order):
+            if res.returncode != 0:
+                failed.append((src, res))
+            objs.append(obj)
+    if failed:
+        for src, res in failed:
+            sys.stderr.write(f"--- {os.path.basename(src)}\n" + res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libmh3a.so")
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + sorted(objs)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libmh3a.so")
+        raise RuntimeError("linking libmh3a.so failed")
     os.replace(tmp, LIB)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,8 @@
+// Conv kernel instances of the 128x96 tile shape (see mh3a_conv.h).
+#include "mh3a_conv.h"
+
+namespace mh3a {
+
+MH3A_DEFINE_TILE_LAUNCHER(TILE_128x96, 1, 3, 4, 1)
+
+}  // namespace mh3a
