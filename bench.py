@@ -11,18 +11,23 @@ of seeded synthetic latents already resident in HBM. Prints one JSON line.
 The metric is decoded audio-seconds per second: B * N / 40 / seconds per
 step (40 latents per second of 32 kHz audio). The default workload is two
 30 s items (B=2, N=1200) with the default MiniMax-H3 decoder and seeded
-random weights. `roofline` covers the dominant kernel, the AMP dilated
-convolution of the wide stages (conv_kernel on the packed activated input;
-its products run as six bf16 piece products on the bf16 matrix cores with
-fp32 accumulation, fp32-accurate), whose kernel durations come from HIP
-events the library records on the decode stream around every AMP conv
-launch of the last timed step (other launches are not bracketed there; a
-second, untimed pass with every launch bracketed gives the per-class
-breakdown). Its peak is the fp32-equivalent rate of that scheme: the dense
-bf16 matrix peak over six products; with MH3A_BX6=0 (fp32 matrix cores) it
-is the fp32 matrix peak.
-`cpu_baseline` times the CPU oracle on a bounded sample (the first 320
-latents of one item, decoded in full).
+random weights. `--workload c4` times the stage-1 AMP set alone on
+(2, 256, 30000).
+
+`roofline` covers the dominant kernel, the AMP dilated convolution of the
+wide stages (conv_kernel on the packed activated input; its products run as
+six bf16 piece products on the bf16 matrix cores with fp32 accumulation,
+fp32-accurate), whose kernel durations come from HIP events the library
+records on the decode stream around every AMP conv launch of the last timed
+step (other launches are not bracketed there; a second, untimed pass with
+every launch bracketed gives the per-class breakdown). `achieved` counts
+the method's FLOPs (2 C_out C_in k per output); `peak` is the dense peak of
+the matrix instruction the kernel issues (bf16, 2500 TFLOP/s; fp32 with
+--fp32-matrix), so `frac` is at most 1 / products. The named extras give
+the matrix pipe's occupancy counting every piece product, and the ratio to
+the fp32 matrix peak.
+`cpu_baseline` times the CPU oracle (numpy, fp64 inside each op) on a
+bounded sample: the first 320 latents of item 0, decoded in full.
 """
 
 from __future__ import annotations
@@ -45,10 +50,11 @@ LATENTS_PER_SECOND = 40         # 32 kHz / hop 800
 SAMPLE_RATE = 32000
 
 WORKLOADS = {
-    # name: (batch, frames, flags, description)
+    # name: (batch, frames, flags, description); c4 is (batch, channels, length) of the AMP stage-1 set
     "c1": (1, 4, 0, "B=1 x N=4 latents (0.1 s)"),
     "c2": (2, 200, 1, "B=2 x N=200 latents (5 s/item), de-normalized latents"),
     "c3": (2, 1200, 0, "B=2 x N=1200 latents (30 s/item)"),
+    "c4": (2, 256, 30000, "stage-1 AMP set alone on (2, 256, 30000): three blocks k 3/7/11, d 1/3/5, averaged"),
     "c5": (16, 401, 0, "B=16 x N=401 latents (10.025 s/item)"),
 }
 # encoder workloads (--path encode): name: (batch, samples, description)
@@ -66,6 +72,8 @@ def parse():
                     help="decode: the BigVGAN decoder (default); encode: the encoder's convolution stack")
     ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + sorted(ENC_WORKLOADS))
     ap.add_argument("--bf16", action="store_true", help="bf16-split matrix-core operands (MH3A_FLAG_BF16_MFMA)")
+    ap.add_argument("--fp32-matrix", action="store_true",
+                    help="build the decoder with matrix_form = MH3A_MATRIX_FP32 (fp32 matrix cores throughout)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time K replays of one decode captured in a HIP graph (graph_ms_per_step)")
@@ -90,7 +98,7 @@ def copy_probe(nbytes):
     return 0
 
 
-def measured_traffic(workload, flags):
+def measured_traffic(workload, flags, fp32_matrix=False):
     """HBM bytes per launch of the roofline kernel from the committed
     rocprofv3 counter runs (profiles/amp_conv_c3_traffic.json for the
     decode's AMP convs, profiles/enc_unit_conv_e3_traffic.json for the
@@ -98,7 +106,7 @@ def measured_traffic(workload, flags):
     counters were taken or the workload differs."""
     import hashlib
     files = {"c3": "amp_conv_c3_traffic.json", "e3": "enc_unit_conv_e3_traffic.json"}
-    if workload not in files or flags & 0x2 or os.environ.get("MH3A_BX6") == "0":
+    if workload not in files or flags & 0x2 or fp32_matrix:
         return None
     path = os.path.join(ROOT, "profiles", files[workload])
     if not os.path.exists(path):
@@ -111,17 +119,21 @@ def measured_traffic(workload, flags):
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
 
 
+def _blas_threads():
+    try:
+        import threadpoolctl
+        return max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(params, n_latents):
     """The oracle, as it stands, on the first n latents of item 0 of the
     workload (a full decode of that short clip)."""
     import numpy as np
     import oracle as O
     from neural_audio_vae_amd import synth
-    try:
-        import threadpoolctl
-        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = _blas_threads()
     z = synth.make_latents(2, 1200)[:1, :, :n_latents]
     t0 = time.perf_counter()
     y = O.decode(params, np.ascontiguousarray(z))
@@ -132,8 +144,48 @@ def cpu_baseline(params, n_latents):
         "unit": "audio-s/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"full oracle decode of latents [0, {n_latents}) of item 0 "
-                  f"({n_latents / LATENTS_PER_SECOND:.1f} s of audio) in {dt:.1f} s",
+        "sample": f"numpy oracle (fp64 inside each op; its per-tap matmuls on {threads} BLAS threads, the "
+                  f"resampling and SnakeBeta steps on one thread): full decode of latents [0, {n_latents}) of "
+                  f"item 0 of the workload ({n_latents / LATENTS_PER_SECOND:.1f} s of audio, a bounded sample) "
+                  f"in {dt:.1f} s",
+    }
+
+
+def roofline_entry(kernel, stats, form):
+    """The roofline record of the matrix-core kernel from its HIP-event
+    stats: `form` is "split" (six bf16 piece products), "bf16x3" (three) or
+    "fp32" (fp32 matrix cores)."""
+    products = {"split": SPLIT_PRODUCTS, "bf16x3": 3, "fp32": 1}[form]
+    peak = FP32_MFMA_PEAK_TFLOPS if form == "fp32" else BF16_MFMA_PEAK_TFLOPS
+    achieved = stats["flops"] / (stats["ms"] / 1e3) / 1e12 if stats["ms"] > 0 else 0.0
+    return {
+        "kernel": kernel,
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "peak_basis": ("dense fp32 matrix peak (v_mfma_f32_32x32x2f32)" if form == "fp32" else
+                       "dense bf16 matrix peak (v_mfma_f32_32x32x16_bf16, the instruction issued)"),
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "achieved_counts": "the method's FLOPs, 2 C_out C_in k per output",
+        "products_per_fp32_product": products,
+        "matrix_pipe_occupancy": round(achieved * products / peak, 4),
+        "vs_fp32_matrix_peak": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4),
+        "launches_timed": stats["launches"],
+        "avg_launch_us": round(1e3 * stats["ms"] / max(1, stats["launches"]), 2),
+        "flops_per_launch": stats["flops"] / max(1, stats["launches"]),
+    }
+
+
+def _per_step(kernels, steps):
+    return {
+        name: {
+            "launches_per_step": k["launches"] / steps,
+            "ms_per_step": round(k["ms"] / steps, 4),
+            "tflops": round(k["flops"] / (k["ms"] / 1e3) / 1e12, 2) if k["ms"] > 0 else None,
+            "gbs_compulsory": round(k["bytes"] / (k["ms"] / 1e3) / 1e9, 1) if k["ms"] > 0 else None,
+        }
+        for name, k in kernels.items()
     }
 
 
@@ -157,20 +209,37 @@ def main():
     if args.workload not in WORKLOADS:
         print(f"--workload {args.workload} is an encoder workload (use --path encode)", file=sys.stderr)
         return 2
-    batch, frames, flags, desc = WORKLOADS[args.workload]
+    stage_bench = args.workload == "c4"
+    if stage_bench:
+        batch, channels, length, desc = WORKLOADS["c4"]
+        flags = 0
+    else:
+        batch, frames, flags, desc = WORKLOADS[args.workload]
     if args.bf16:
         flags |= 0x2
+    form = "fp32" if args.fp32_matrix else ("bf16x3" if args.bf16 else "split")
     params = synth.make_params()
     mean, std = synth.make_denorm()
-    dec = Decoder(params, latents_mean=mean, latents_std=std)
-    z = torch.from_numpy(synth.make_latents(batch, frames)).cuda()
-    out = torch.empty((batch, 1, 800 * frames), dtype=torch.float32, device="cuda")
+    cfg = {"matrix_form": _lib.MH3A_MATRIX_FP32} if args.fp32_matrix else None
+    dec = Decoder(params, cfg, latents_mean=mean, latents_std=std)
     stream = torch.cuda.current_stream()
+    if stage_bench:
+        x = torch.from_numpy(synth.make_signal((batch, channels, length), seed=0)).cuda()
+        out = torch.empty_like(x)
+
+        def step():
+            dec.amp_stage(1, x, flags=flags, out=out, stream=stream)
+    else:
+        z = torch.from_numpy(synth.make_latents(batch, frames)).cuda()
+        out = torch.empty((batch, 1, 800 * frames), dtype=torch.float32, device="cuda")
+
+        def step():
+            dec.decode(z, flags=flags, out=out, stream=stream)
     for _ in range(args.warmup):
-        dec.decode(z, flags=flags, out=out, stream=stream)
+        step()
     torch.cuda.synchronize()
 
-    # Timed region: K decodes. In the last one the library brackets each AMP
+    # Timed region: K steps. In the last one the library brackets each AMP
     # conv launch (the roofline kernel) with HIP events on the decode stream
     # (events on every step would add their own cost, ~2%, to every step).
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -180,7 +249,7 @@ def main():
     for i in range(args.steps):
         if i == args.steps - 1:
             dec.timing(_lib.MH3A_TIMING_AMP_CONV)
-        dec.decode(z, flags=flags, out=out, stream=stream)
+        step()
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
@@ -190,43 +259,25 @@ def main():
     # bracketed (the events add ~2% when on every launch).
     dec.timing(_lib.MH3A_TIMING_ALL)
     for _ in range(args.steps):
-        dec.decode(z, flags=flags, out=out, stream=stream)
+        step()
     torch.cuda.synchronize()
     kernels = dec.timing_read()
     dec.timing(_lib.MH3A_TIMING_OFF)
 
     ms_step = ms_total / args.steps
-    audio_s = batch * frames / LATENTS_PER_SECOND
-    value = audio_s / (ms_step / 1e3)
     amp = amp_only.get("amp_conv", {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
-    achieved = amp["flops"] / (amp["ms"] / 1e3) / 1e12 if amp["ms"] > 0 else 0.0
-    split = os.environ.get("MH3A_BX6") != "0" and not args.bf16
-    peak = BF16_MFMA_PEAK_TFLOPS / SPLIT_PRODUCTS if split else FP32_MFMA_PEAK_TFLOPS
-    per_step = {
-        name: {
-            "launches_per_step": k["launches"] / args.steps,
-            "ms_per_step": round(k["ms"] / args.steps, 4),
-            "tflops": round(k["flops"] / (k["ms"] / 1e3) / 1e12, 2) if k["ms"] > 0 else None,
-            "gbs_compulsory": round(k["bytes"] / (k["ms"] / 1e3) / 1e9, 1) if k["ms"] > 0 else None,
-        }
-        for name, k in kernels.items()
-    }
     total_flops = sum(k["flops"] for k in kernels.values()) / args.steps
-    line = {
-        "metric": "decoded audio-sec/s (B=2, 30 s clips, fp32)" if args.workload == "c3" else
-                  f"decoded audio-sec/s ({args.workload})",
-        "value": round(value, 2),
-        "unit": "audio-s/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16x3" if args.bf16 else "f32",
-        "data": "synthetic",
-        "config": {
+    if stage_bench:
+        metric, unit = "AMP stage-1 set TFLOP/s (c4, fp32)", "TFLOP/s"
+        value = total_flops / (ms_step / 1e3) / 1e12
+        config = {"workload": f"AMP residual-block set of stage 1 of the MiniMax-H3 audio-VAE decoder, {desc}, "
+                              "seeded random weights", "batch": batch, "channels": channels, "length": length}
+    else:
+        metric = ("decoded audio-sec/s (B=2, 30 s clips, fp32)" if args.workload == "c3" else
+                  f"decoded audio-sec/s ({args.workload})")
+        unit = "audio-s/s"
+        value = batch * frames / LATENTS_PER_SECOND / (ms_step / 1e3)
+        config = {
             "workload": f"BigVGAN decode of the MiniMax-H3 audio VAE, {desc}, default decoder "
                         "(32->2048 proj, conv_pre 2048->1024, 7 upsampling stages 1024->8 ch, AMP k 3/7/11 "
                         "d 1/3/5), seeded random weights, 32 kHz mono output",
@@ -234,28 +285,33 @@ def main():
             "frames": frames,
             "samples_per_item": 800 * frames,
             "flags": flags,
-        },
+        }
+    kernel_desc = ("conv_kernel, AMP dilated convs of the 64-512 channel stages (packed activated input; " +
+                   {"split": "six bf16 piece products per fp32 product on v_mfma_f32_32x32x16_bf16, fp32 "
+                             "accumulation)",
+                    "bf16x3": "three bf16 piece products (two-piece split) on v_mfma_f32_32x32x16_bf16)",
+                    "fp32": "fp32 matrix cores)"}[form])
+    line = {
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"split": "f32", "bf16x3": "bf16x3", "fp32": "f32"}[form],
+        "data": "synthetic",
+        "config": config,
         "algorithmic_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
-        "roofline": {
-            "kernel": "conv_kernel, AMP dilated convs of the 64-512 channel stages (packed activated input; "
-                      + ("six bf16 piece products per fp32 product on v_mfma_f32_32x32x16_bf16, fp32 accumulation)"
-                         if split else "fp32 matrix cores)"),
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": round(peak, 2),
-            "peak_basis": ("dense bf16 matrix peak 2500 TFLOP/s / 6 piece products (fp32-equivalent)" if split
-                           else "dense fp32 matrix peak"),
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(args.workload, flags),
-            "launches_timed": amp["launches"],
-            "avg_launch_us": round(1e3 * amp["ms"] / max(1, amp["launches"]), 2),
-            "flops_per_launch": amp["flops"] / max(1, amp["launches"]),
-        },
-        "kernels": per_step,
+        "roofline": dict(roofline_entry(kernel_desc, amp, form),
+                         traffic=measured_traffic(args.workload, flags, args.fp32_matrix)),
+        "kernels": _per_step(kernels, args.steps),
         "wall_s_timed": round(wall, 4),
     }
-    if args.graph:
+    if args.graph and not stage_bench:
         # one decode captured on a side stream (after a warm-up call there),
         # then K replays between synchronizations: the launch overhead of the
         # ~130 kernels goes away, which matters for the small workloads
@@ -276,7 +332,7 @@ def main():
             g.replay()
         torch.cuda.synchronize()
         line["graph_ms_per_step"] = round((time.perf_counter() - t0) / args.steps * 1e3, 4)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not stage_bench:
         line["cpu_baseline"] = cpu_baseline(params, args.cpu_latents)
     print(json.dumps(line), flush=True)
     dec.close()
@@ -289,11 +345,7 @@ def cpu_baseline_encode(params, n_samples):
     import numpy as np
     import oracle as O
     from neural_audio_vae_amd import synth
-    try:
-        import threadpoolctl
-        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = _blas_threads()
     wave = synth.make_waveform(1, n_samples, seed=0)
     t0 = time.perf_counter()
     h = O.encode_hidden(params, wave)
@@ -304,8 +356,9 @@ def cpu_baseline_encode(params, n_samples):
         "unit": "audio-s/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"oracle encode of a {n_samples}-sample waveform ({n_samples / SAMPLE_RATE:.2f} s of audio) "
-                  f"in {dt:.1f} s",
+        "sample": f"numpy oracle (fp64 inside each op; per-tap matmuls on {threads} BLAS threads, the Snake "
+                  f"steps on one thread): encode of a {n_samples}-sample waveform ({n_samples / SAMPLE_RATE:.2f} s "
+                  f"of audio, a bounded sample) in {dt:.1f} s",
     }
 
 
@@ -325,7 +378,8 @@ def main_encode(args):
         return 2
     batch, samples, desc = ENC_WORKLOADS[args.workload]
     params = synth.make_encoder_params(seed=0)
-    enc = Encoder(params)
+    form = "fp32" if args.fp32_matrix else "split"
+    enc = Encoder(params, {"matrix_form": _lib.MH3A_MATRIX_FP32} if args.fp32_matrix else None)
     x = torch.from_numpy(synth.make_waveform(batch, samples, seed=0)).cuda()
     out = torch.empty((batch, enc.latent_dim, enc.frames(samples)), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -353,9 +407,6 @@ def main_encode(args):
     ms_step = ms_total / args.steps
     value = batch * samples / SAMPLE_RATE / (ms_step / 1e3)
     k7 = unit_only.get("enc_unit_conv", {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
-    achieved = k7["flops"] / (k7["ms"] / 1e3) / 1e12 if k7["ms"] > 0 else 0.0
-    split = os.environ.get("MH3A_BX6") != "0"
-    peak = BF16_MFMA_PEAK_TFLOPS / SPLIT_PRODUCTS if split else FP32_MFMA_PEAK_TFLOPS
     total_flops = sum(k["flops"] for k in kernels.values()) / args.steps
     line = {
         "metric": f"encoded audio-sec/s ({args.workload}, fp32)",
@@ -377,31 +428,11 @@ def main_encode(args):
             "samples_per_item": samples,
         },
         "algorithmic_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
-        "roofline": {
-            "kernel": "conv_kernel, the residual units' k7 dilated convs (split-product packed input; "
-                      + ("six bf16 piece products per fp32 product on v_mfma_f32_32x32x16_bf16)" if split
-                         else "fp32 matrix cores)"),
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": round(peak, 2),
-            "peak_basis": ("dense bf16 matrix peak 2500 TFLOP/s / 6 piece products (fp32-equivalent)" if split
-                           else "dense fp32 matrix peak"),
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(args.workload, 0),
-            "launches_timed": k7["launches"],
-            "avg_launch_us": round(1e3 * k7["ms"] / max(1, k7["launches"]), 2),
-            "flops_per_launch": k7["flops"] / max(1, k7["launches"]),
-        },
-        "kernels": {
-            name: {
-                "launches_per_step": k["launches"] / args.steps,
-                "ms_per_step": round(k["ms"] / args.steps, 4),
-                "tflops": round(k["flops"] / (k["ms"] / 1e3) / 1e12, 2) if k["ms"] > 0 else None,
-                "gbs_compulsory": round(k["bytes"] / (k["ms"] / 1e3) / 1e9, 1) if k["ms"] > 0 else None,
-            }
-            for name, k in kernels.items()
-        },
+        "roofline": dict(roofline_entry(
+            "conv_kernel, the residual units' k7 dilated convs (split-product packed input; "
+            + ("six bf16 piece products per fp32 product on v_mfma_f32_32x32x16_bf16)" if form == "split"
+               else "fp32 matrix cores)"), k7, form), traffic=measured_traffic(args.workload, 0, args.fp32_matrix)),
+        "kernels": _per_step(kernels, args.steps),
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:

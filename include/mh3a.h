@@ -77,6 +77,16 @@ extern "C" {
 #define MH3A_FLAG_BATCH_INVARIANT 0x8u
 #define MH3A_FLAG_ALL 0xFu
 
+/* ---- matrix-core form of the convolutions (mh3a_config.matrix_form,
+ * mh3a_encoder_config.matrix_form), fixed at create ---- */
+/* Every conv with split-product weights runs on the bf16 matrix cores,
+ * each fp32 operand split into three bf16 pieces and the six products of
+ * order <= 2 summed in fp32 (fp32-level accuracy; the default). */
+#define MH3A_MATRIX_SPLIT 0
+/* Every conv runs on the fp32 matrix cores (v_mfma_f32_32x32x2f32 /
+ * 16x16x4f32): slower, kept as a second, independent form of the products. */
+#define MH3A_MATRIX_FP32 1
+
 /* ---- architecture limits ---- */
 #define MH3A_MAX_STAGES 8
 #define MH3A_MAX_RESBLOCKS 4
@@ -112,6 +122,7 @@ typedef struct {
     int filter_taps;                /* only 12 is supported */
     double filter_cutoff;
     double filter_half_width;
+    int matrix_form;                /* MH3A_MATRIX_SPLIT (default) or MH3A_MATRIX_FP32 */
 } mh3a_config;
 
 /* Fill *cfg with the defaults above. */
@@ -299,6 +310,7 @@ typedef struct {
     int num_blocks;                   /* strided blocks (5) */
     int rates[MH3A_MAX_ENC_BLOCKS];   /* their strides (2, 4, 4, 5, 5) */
     int latent_dim;                   /* hidden channels (2048) */
+    int matrix_form;                  /* MH3A_MATRIX_SPLIT (default) or MH3A_MATRIX_FP32 */
 } mh3a_encoder_config;
 void mh3a_encoder_config_default(mh3a_encoder_config* cfg);
 int mh3a_encoder_create(const mh3a_encoder_config* cfg, const mh3a_tensor* params, int n_params, int device,

@@ -27,6 +27,7 @@ MH3A_FLAG_BF16_MFMA = 0x2
 MH3A_FLAG_NO_CLAMP = 0x4
 MH3A_FLAG_BATCH_INVARIANT = 0x8
 MH3A_TIMING_OFF, MH3A_TIMING_ALL, MH3A_TIMING_AMP_CONV = 0, 1, 2
+MH3A_MATRIX_SPLIT, MH3A_MATRIX_FP32 = 0, 1
 
 MH3A_MAX_STAGES = 8
 MH3A_MAX_RESBLOCKS = 4
@@ -79,6 +80,7 @@ class mh3a_config(Structure):
         ("filter_taps", c_int),
         ("filter_cutoff", c_double),
         ("filter_half_width", c_double),
+        ("matrix_form", c_int),
     ]
 
 
@@ -87,7 +89,7 @@ MH3A_MAX_ENC_BLOCKS = 8
 
 class mh3a_encoder_config(Structure):
     _fields_ = [("encoder_dim", c_int), ("num_blocks", c_int), ("rates", c_int * MH3A_MAX_ENC_BLOCKS),
-                ("latent_dim", c_int)]
+                ("latent_dim", c_int), ("matrix_form", c_int)]
 
 
 class mh3a_kernel_stats(Structure):
@@ -193,7 +195,7 @@ def make_config(overrides=None):
     constructor's keyword names (decoder_rates, resblock_kernel_sizes, ...)."""
     cfg = mh3a_config_default()
     o = dict(overrides or {})
-    for key in ("latent_channels", "latent_dim", "decoder_dim", "hop_length", "filter_taps"):
+    for key in ("latent_channels", "latent_dim", "decoder_dim", "hop_length", "filter_taps", "matrix_form"):
         if key in o:
             setattr(cfg, key, int(o[key]))
     for key in ("filter_cutoff", "filter_half_width"):
@@ -348,10 +350,10 @@ def mh3a_encoder_config_default():
 
 def make_encoder_config(overrides=None):
     """An mh3a_encoder_config from the defaults plus encoder_dim,
-    encoder_rates and latent_dim overrides."""
+    encoder_rates, latent_dim and matrix_form overrides."""
     cfg = mh3a_encoder_config_default()
     o = dict(overrides or {})
-    for key in ("encoder_dim", "latent_dim"):
+    for key in ("encoder_dim", "latent_dim", "matrix_form"):
         if key in o:
             setattr(cfg, key, int(o[key]))
     if "encoder_rates" in o:

@@ -264,6 +264,8 @@ int check_config(const mh3a_config* c) {
     if (c->filter_taps != kTaps) return fail(MH3A_E_CONFIG, "only %d-tap resampling filters are supported", kTaps);
     if (!(c->filter_cutoff > 0.0 && c->filter_cutoff < 0.5 && c->filter_half_width > 0.0))
         return fail(MH3A_E_CONFIG, "bad filter cutoff / half width");
+    if (c->matrix_form != MH3A_MATRIX_SPLIT && c->matrix_form != MH3A_MATRIX_FP32)
+        return fail(MH3A_E_CONFIG, "unknown matrix_form %d", c->matrix_form);
     return MH3A_OK;
 }
 
@@ -397,16 +399,9 @@ int64_t plan_partial_floats(const ConvLayer& L, int positions, int groups, const
 }
 
 // Whether packed AMP inputs take the split-product form (bf16 pieces and
-// six-way products on bf16 matrix cores, fp32-level accuracy; see kPieces).
-// MH3A_BX6=0 selects the fp32 matrix-core form (a tuning aid).
-bool bx6_disabled() {
-    static const bool off = [] {
-        const char* e = std::getenv("MH3A_BX6");
-        return e && !std::strcmp(e, "0");
-    }();
-    return off;
-}
-bool use_bx6(const mh3a_decoder* d) { return d->bx6_ok && !bx6_disabled(); }
+// six-way products on bf16 matrix cores, fp32-level accuracy; see kPieces):
+// the default matrix form, when every AMP conv has the weights for it.
+bool use_bx6(const mh3a_decoder* d) { return d->bx6_ok && d->cfg.matrix_form == MH3A_MATRIX_SPLIT; }
 
 // Whether an AMP conv of a (batch, C, L) activation fuses its activation.
 // Fused, the producer waves compute it per tile on the SIMDs whose matrix
@@ -418,17 +413,8 @@ bool use_bx6(const mh3a_decoder* d) { return d->bx6_ok && !bx6_disabled(); }
 // 128 to 512 channels, ties at 64 and loses below, where the pass (~30 us
 // per 15 M samples) costs more than the contention saves. Small launches
 // stay fused (one launch, less latency).
-// MH3A_AMP_ACT=fused|separate overrides (a tuning aid).
 bool amp_act_fused(const mh3a_decoder* d, int64_t batch, int64_t c, int64_t len) {
     if (!d->pk_ok) return true;
-    static const int mode = [] {
-        const char* e = std::getenv("MH3A_AMP_ACT");
-        if (!e) return 0;
-        if (!std::strcmp(e, "fused")) return 1;
-        if (!std::strcmp(e, "separate")) return 2;
-        return 0;
-    }();
-    if (mode) return mode == 1;
     // split-product convs gain enough from matrix-core speed to pay for the
     // separate pass from 64 channels on
     return c < (use_bx6(d) ? 64 : 128) || batch * c * len < kSeparateActMin;
@@ -454,17 +440,15 @@ ConvPlan plan_conv(const mh3a_net* d, const ConvLayer& L, int positions, int bat
     auto it = d->plans.find(key);
     if (it != d->plans.end()) return {(TileId)it->second.first, it->second.second};
     const ConvPlan p = mh3a::plan_conv(shape_of(L, fused, bx6), positions, batch, bf16, invariant, d->num_cus);
-    // MH3A_PLAN_LOG=1 prints each new plan to stderr (a tuning aid)
-    static const bool log = [] {
-        const char* e = std::getenv("MH3A_PLAN_LOG");
-        return e && *e == '1';
-    }();
-    if (log) {
+#ifdef MH3A_PLAN_LOG
+    // (build-time option: -DMH3A_PLAN_LOG prints each new plan to stderr)
+    {
         const TileShape ts = tile_shape(p.tile);
         std::fprintf(stderr, "mh3a plan: %s c_in %d c_out %d taps %d dil %d positions %d batch %d%s%s -> tile %dx%d ksplit %d\n",
                      kKindNames[L.kind], L.c_in, L.c_out, L.taps, L.dil, positions, batch, invariant ? " (invariant)" : "",
                      (L.act >= 0 && !fused) ? " (act separate)" : "", ts.m, ts.n, p.ksplit);
     }
+#endif
     if (d->plans.size() > 4096) d->plans.clear();
     d->plans.emplace(key, std::make_pair((int)p.tile, p.ksplit));
     return p;
@@ -641,13 +625,8 @@ bool amp_unit_split(const mh3a_decoder* d, int stage) {
 
 // Whether stage s runs each residual unit as one launch (unit_kernel): fp32
 // operands, a channel count and every conv's taps and dilation that the
-// kernel has instances for. MH3A_AMP_UNIT=0 turns it off (a tuning aid).
+// kernel has instances for.
 bool amp_unit_path(const mh3a_decoder* d, int stage, bool bf16) {
-    static const bool off = [] {
-        const char* e = std::getenv("MH3A_AMP_UNIT");
-        return e && !std::strcmp(e, "0");
-    }();
-    if (off) return false;
     for (const ConvLayer& L : d->amp[stage])
         if (L.w16_off < 0 || L.b_off < 0 || L.act < 0 || !unit_supported(L.c_out, L.taps, L.dil)) return false;
     // the bf16 operand flag needs the split-product unit kernel (three products)
@@ -1625,6 +1604,8 @@ int enc_check_config(const mh3a_encoder_config* c) {
         dim *= 2;
     }
     if (hop > 65536 || dim > 65536) return fail(MH3A_E_CONFIG, "encoder hop or width too large");
+    if (c->matrix_form != MH3A_MATRIX_SPLIT && c->matrix_form != MH3A_MATRIX_FP32)
+        return fail(MH3A_E_CONFIG, "unknown matrix_form %d", c->matrix_form);
     return MH3A_OK;
 }
 
@@ -1690,15 +1671,17 @@ int enc_snake_layer(Blob& blob, const Table& t, const std::string& name, int c, 
     return MH3A_OK;
 }
 
-bool enc_bx6(const ConvLayer& L) { return L.w6_off >= 0 && !bx6_disabled(); }
+bool enc_bx6(const mh3a_encoder* e, const ConvLayer& L) {
+    return L.w6_off >= 0 && e->cfg.matrix_form == MH3A_MATRIX_SPLIT;
+}
 
 // Per-item lengths: S' = frames * hop samples after the right pad; block i
 // runs at L_i = S' / (r_0 ... r_{i-1}) positions.
 int64_t enc_frames(const mh3a_encoder* e, int64_t samples) { return (samples + e->hop - 1) / e->hop; }
 
 // Floats of one Snake output (per item) feeding conv L over l_out positions.
-int64_t enc_snake_item_floats(const ConvLayer& L, int64_t l_out) {
-    if (enc_bx6(L)) return (int64_t)((L.c_in + kChunk - 1) / kChunk) * kPieces * 4 * pk_lp(l_out);
+int64_t enc_snake_item_floats(const mh3a_encoder* e, const ConvLayer& L, int64_t l_out) {
+    if (enc_bx6(e, L)) return (int64_t)((L.c_in + kChunk - 1) / kChunk) * kPieces * 4 * pk_lp(l_out);
     return (int64_t)L.c_in * l_out;
 }
 
@@ -1710,7 +1693,7 @@ EncWs enc_ws_floats(const mh3a_encoder* e, int64_t batch, int64_t frames, bool i
     EncWs w{0, 0, 0, 0};
     int64_t len = frames * e->hop;
     auto part = [&](const ConvLayer& L, int64_t positions) {
-        const bool bx6 = enc_bx6(L);
+        const bool bx6 = enc_bx6(e, L);
         const ConvPlan pl = plan_conv(e, L, (int)positions, (int)batch, false, inv, true, bx6);
         w.partial = std::max(w.partial, plan_partial_floats(L, (int)positions, (int)batch, pl, true));
     };
@@ -1722,16 +1705,16 @@ EncWs enc_ws_floats(const mh3a_encoder* e, int64_t batch, int64_t frames, bool i
         for (int u = 0; u < 3; ++u) {
             const ConvLayer& k7 = e->unit_conv[(i * 3 + u) * 2];
             const ConvLayer& k1 = e->unit_conv[(i * 3 + u) * 2 + 1];
-            w.p = std::max({w.p, enc_snake_item_floats(k7, len), enc_snake_item_floats(k1, len)});
+            w.p = std::max({w.p, enc_snake_item_floats(e, k7, len), enc_snake_item_floats(e, k1, len)});
             part(k7, len);
             part(k1, len);
         }
-        w.p = std::max(w.p, enc_snake_item_floats(e->down[i], len / s + 1));
+        w.p = std::max(w.p, enc_snake_item_floats(e, e->down[i], len / s + 1));
         part(e->down[i], len / s);
         len /= s;
         w.x = std::max(w.x, (int64_t)2 * C * len);
     }
-    w.p = std::max(w.p, enc_snake_item_floats(e->conv_out, len));
+    w.p = std::max(w.p, enc_snake_item_floats(e, e->conv_out, len));
     part(e->conv_out, len);
     w.r = w.x;
     w.x = round_up(w.x * batch, 64);
@@ -1773,8 +1756,8 @@ hipError_t enc_run_snake(const mh3a_encoder* e, const SnakeLayer& S, const ConvL
     a.shift = shift;
     a.l_out = l_out;
     a.y = y;
-    a.y_bstride = enc_snake_item_floats(L, l_out);
-    a.lp = enc_bx6(L) ? (int)pk_lp(l_out) : 0;
+    a.y_bstride = enc_snake_item_floats(e, L, l_out);
+    a.lp = enc_bx6(e, L) ? (int)pk_lp(l_out) : 0;
     TimedLaunch tl(e, st, KIND_ENC_SNAKE);
     hipError_t err = launch_snake(a, batch, st);
     const double n_in = (double)batch * S.c * l, n_out = (double)batch * S.c * s * l_out;
@@ -1785,8 +1768,8 @@ hipError_t enc_run_snake(const mh3a_encoder* e, const SnakeLayer& S, const ConvL
 // conv L over its Snake input y (as enc_run_snake wrote it, l_in positions)
 hipError_t enc_run_conv(const mh3a_encoder* e, const ConvLayer& L, const float* p, int l_in, int positions,
                         float* out, int batch, const float* res, bool inv, float* partial, hipStream_t st) {
-    const bool bx6 = enc_bx6(L);
-    return run_conv(e, L, p, enc_snake_item_floats(L, l_in), l_in, positions, out, (int64_t)L.c_out * positions,
+    const bool bx6 = enc_bx6(e, L);
+    return run_conv(e, L, p, enc_snake_item_floats(e, L, l_in), l_in, positions, out, (int64_t)L.c_out * positions,
                     batch, res, nullptr, 1.0f, false, inv, true, partial, st, bx6 ? (int)pk_lp(l_in) : 0, bx6);
 }
 

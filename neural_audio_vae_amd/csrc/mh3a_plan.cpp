@@ -65,16 +65,14 @@ double tile_cost(const ConvShape& L, TileId id, int positions, int groups, bool 
     return cost;
 }
 
-// MH3A_CONV_TILE=<index into MH3A_TILE_LIST> forces one tile shape for
-// every conv launch whose LDS it fits (a tuning aid, read once).
-int forced_tile() {
-    static const int v = [] {
-        const char* e = std::getenv("MH3A_CONV_TILE");
-        if (!e || !*e) return -1;
-        const int t = std::atoi(e);
-        return (t >= 0 && t < TILE_COUNT) ? t : -1;
-    }();
-    return v;
+// Build-time option -DMH3A_FORCE_TILE=<index into MH3A_TILE_LIST> forces one
+// tile shape for every conv launch whose LDS it fits (a tuning aid).
+constexpr int forced_tile() {
+#ifdef MH3A_FORCE_TILE
+    return (MH3A_FORCE_TILE >= 0 && MH3A_FORCE_TILE < TILE_COUNT) ? MH3A_FORCE_TILE : -1;
+#else
+    return -1;
+#endif
 }
 
 TileId choose_tile(const ConvShape& L, int positions, int groups, bool bf16, int ksplit, int num_cus) {

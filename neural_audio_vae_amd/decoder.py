@@ -1,7 +1,9 @@
-"""Decoder: torch-tensor convenience over the mh3a C ABI.
+"""Decoder and Encoder: torch-tensor convenience over the mh3a C ABI.
 
 torch supplies device memory and the stream; every step of the decode runs
-in the library's HIP kernels.
+in the library's HIP kernels. The C ABI takes raw device pointers and no
+buffer sizes, so these wrappers check every tensor they hand to it (dtype,
+device, contiguity and exact shape) before the call.
 """
 
 from __future__ import annotations
@@ -21,14 +23,88 @@ def _torch():
     return torch
 
 
+class _Workspaces:
+    """One device workspace per stream (concurrent calls on different
+    streams need distinct workspaces). A workspace is allocated on its own
+    stream, so when a larger call outgrows it, freeing it is ordered after
+    the kernels that used it. A workspace used while that stream was being
+    captured into a HIP graph may still be referenced by the graph: such
+    buffers are kept until close()."""
+
+    def __init__(self, device):
+        self.device = device
+        self.by_stream = {}
+        self.captured = []
+
+    def get(self, nbytes, stream):
+        torch = _torch()
+        key = stream.cuda_stream
+        ws = self.by_stream.get(key)
+        capturing = torch.cuda.is_current_stream_capturing()
+        if ws is None or ws.numel() < nbytes:
+            if capturing:
+                raise RuntimeError("the first call of a shape must run outside graph capture (it sizes the workspace)")
+            with torch.cuda.stream(stream):
+                ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=f"cuda:{self.device}")
+            self.by_stream[key] = ws
+        if capturing and not any(w is ws for w in self.captured):
+            self.captured.append(ws)
+        return ws
+
+    def clear(self):
+        self.by_stream, self.captured = {}, []
+
+
+def _check_tensor(t, name, device, shape=None, ndim=None):
+    """A float32, contiguous CUDA tensor on cuda:<device> (of `shape` if
+    given); raises ValueError otherwise. Only reads the tensor's metadata."""
+    import torch
+
+    if not (getattr(t, "is_cuda", False) and getattr(t, "dtype", None) == torch.float32):
+        raise ValueError(f"{name} must be a float32 CUDA tensor")
+    if t.device.index != device:
+        raise ValueError(f"{name} is on {t.device}, the library object on cuda:{device}")
+    if ndim is not None and len(t.shape) != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _input(t, name, device, ndim, stream):
+    """The input as a contiguous tensor; a temporary copy is marked as used
+    by `stream` so that the allocator keeps it until the kernels are done."""
+    _check_tensor(t, name, device, ndim=ndim)
+    if t.is_contiguous():
+        return t
+    c = t.contiguous()
+    c.record_stream(stream)
+    return c
+
+
+def _output(out, name, device, shape, stream):
+    if out is None:
+        torch = _torch()
+        with torch.cuda.stream(stream):
+            return torch.empty(shape, dtype=torch.float32, device=f"cuda:{device}")
+    _check_tensor(out, name, device, shape=shape)
+    if not out.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return out
+
+
+def _stream(stream, device):
+    torch = _torch()
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
 class Decoder:
     """A decoder built once from host parameters (weight norm folded and
     filters designed at construction).
 
     The decode only enqueues kernels on the given stream (no allocation,
-    memset or synchronization inside), so a call can be captured into a HIP
-    graph (torch.cuda.graph) once a first call of the same shape has sized
-    the workspace; workspaces are kept until close()."""
+    memset or synchronization inside the library), so a call can be
+    captured into a HIP graph (torch.cuda.graph) once a first call of the
+    same shape on that stream has sized its workspace."""
 
     def __init__(self, params, config=None, latents_mean=None, latents_std=None, device=0):
         self.config = dict(config or {})
@@ -38,14 +114,14 @@ class Decoder:
         self.hop = cfg.hop_length
         self.num_ups = cfg.num_ups
         self._h = _lib.mh3a_decoder_create(cfg, params, latents_mean, latents_std, self.device)
-        self._ws = None
-        self._old_ws = []
+        self._ws = _Workspaces(self.device)
 
     def close(self):
         if getattr(self, "_h", None):
             _lib.mh3a_destroy(self._h)
             self._h = None
-        self._ws, self._old_ws = None, []
+        if getattr(self, "_ws", None) is not None:
+            self._ws.clear()
 
     def __del__(self):
         try:
@@ -53,38 +129,23 @@ class Decoder:
         except Exception:
             pass
 
-    def _workspace(self, nbytes):
-        torch = _torch()
-        if self._ws is None or self._ws.numel() < nbytes:
-            # a captured HIP graph may still use the previous buffer: keep it
-            # until close()
-            if self._ws is not None:
-                self._old_ws.append(self._ws)
-            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=f"cuda:{self.device}")
-        return self._ws
-
-    @staticmethod
-    def _check_input(t, ndim, name):
-        torch = _torch()
-        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == torch.float32 and t.dim() == ndim):
-            raise ValueError(f"{name} must be a float32 CUDA tensor with {ndim} dims")
-        return t.contiguous()
-
     def workspace_size(self, batch, frames, flags=0):
         return _lib.mh3a_decode_workspace_size(self._h, batch, frames, flags)
 
+    def _latents(self, latents, st):
+        z = _input(latents, "latents", self.device, 3, st)
+        if z.shape[1] != self.latent_channels:
+            raise ValueError(f"latents must have {self.latent_channels} channels, got {z.shape[1]}")
+        return z
+
     def decode(self, latents, flags=0, out=None, stream=None):
-        torch = _torch()
-        z = self._check_input(latents, 3, "latents")
-        b, c, n = z.shape
-        if c != self.latent_channels:
-            raise ValueError(f"latents must have {self.latent_channels} channels")
-        if out is None:
-            out = torch.empty((b, 1, self.hop * n), dtype=torch.float32, device=z.device)
-        nbytes = self.workspace_size(b, n, flags)
-        ws = self._workspace(nbytes)
-        st = (stream or torch.cuda.current_stream(z.device)).cuda_stream
-        _lib.mh3a_decode(self._h, z.data_ptr(), b, n, out.data_ptr(), ws.data_ptr(), ws.numel(), flags, st)
+        st = _stream(stream, self.device)
+        z = self._latents(latents, st)
+        b, _, n = z.shape
+        out = _output(out, "out", self.device, (b, 1, self.hop * n), st)
+        ws = self._ws.get(self.workspace_size(b, n, flags), st)
+        _lib.mh3a_decode(self._h, z.data_ptr(), b, n, out.data_ptr(), ws.data_ptr(), ws.numel(), flags,
+                         st.cuda_stream)
         return out
 
     def timing(self, enable):
@@ -96,16 +157,15 @@ class Decoder:
     def layer_shape(self, frames, upto):
         return _lib.mh3a_decode_layer_shape(self._h, frames, upto)
 
-    def decode_partial(self, latents, upto, flags=0):
-        torch = _torch()
-        z = self._check_input(latents, 3, "latents")
-        b, c, n = z.shape
+    def decode_partial(self, latents, upto, flags=0, stream=None):
+        st = _stream(stream, self.device)
+        z = self._latents(latents, st)
+        b, _, n = z.shape
         ch, length = self.layer_shape(n, upto)
-        out = torch.empty((b, ch, length), dtype=torch.float32, device=z.device)
-        ws = self._workspace(self.workspace_size(b, n, flags))
-        st = torch.cuda.current_stream(z.device).cuda_stream
+        out = _output(None, "out", self.device, (b, ch, length), st)
+        ws = self._ws.get(self.workspace_size(b, n, flags), st)
         _lib.mh3a_decode_partial(self._h, z.data_ptr(), b, n, upto, out.data_ptr(), ws.data_ptr(), ws.numel(), flags,
-                                 st)
+                                 st.cuda_stream)
         return out
 
     def margin(self):
@@ -116,31 +176,33 @@ class Decoder:
         """decode() in time chunks of chunk_frames latents, each decoded from
         a window widened by margin() latents per side and cropped; the
         workspace depends on chunk_frames, not on the sequence length."""
-        torch = _torch()
-        z = self._check_input(latents, 3, "latents")
-        b, c, n = z.shape
-        if c != self.latent_channels:
-            raise ValueError(f"latents must have {self.latent_channels} channels")
-        if out is None:
-            out = torch.empty((b, 1, self.hop * n), dtype=torch.float32, device=z.device)
+        st = _stream(stream, self.device)
+        z = self._latents(latents, st)
+        b, _, n = z.shape
+        out = _output(out, "out", self.device, (b, 1, self.hop * n), st)
         nbytes = _lib.mh3a_decode_chunked_workspace_size(self._h, b, n, chunk_frames, flags)
-        ws = self._workspace(nbytes)
-        st = (stream or torch.cuda.current_stream(z.device)).cuda_stream
+        ws = self._ws.get(nbytes, st)
         _lib.mh3a_decode_chunked(self._h, z.data_ptr(), b, n, chunk_frames, out.data_ptr(), ws.data_ptr(), ws.numel(),
-                                 flags, st)
+                                 flags, st.cuda_stream)
         return out
 
+    def stage_channels(self, stage):
+        """Channels of upsampling stage `stage` (its AMP set's width)."""
+        if not 0 <= int(stage) < self.num_ups:
+            raise ValueError(f"stage must be in [0, {self.num_ups})")
+        return self.layer_shape(1, 3 + 2 * int(stage))[0]
+
     def amp_stage(self, stage, x, flags=0, out=None, stream=None):
-        torch = _torch()
-        x = self._check_input(x, 3, "x")
+        st = _stream(stream, self.device)
+        x = _input(x, "x", self.device, 3, st)
         b, c, length = x.shape
-        if out is None:
-            out = torch.empty_like(x)
+        if c != self.stage_channels(stage):
+            raise ValueError(f"stage {stage} has {self.stage_channels(stage)} channels, x has {c}")
+        out = _output(out, "out", self.device, (b, c, length), st)
         nbytes = _lib.mh3a_amp_stage_workspace_size(self._h, stage, b, length)
-        ws = self._workspace(nbytes)
-        st = (stream or torch.cuda.current_stream(x.device)).cuda_stream
+        ws = self._ws.get(nbytes, st)
         _lib.mh3a_amp_stage(self._h, stage, x.data_ptr(), b, length, out.data_ptr(), ws.data_ptr(), ws.numel(), flags,
-                            st)
+                            st.cuda_stream)
         return out
 
 
@@ -158,14 +220,14 @@ class Encoder:
         cfg = _lib.make_encoder_config(self.config)
         self.latent_dim = cfg.latent_dim
         self._h = _lib.mh3a_encoder_create(cfg, params, self.device)
-        self._ws = None
-        self._old_ws = []
+        self._ws = _Workspaces(self.device)
 
     def close(self):
         if getattr(self, "_h", None):
             _lib.mh3a_encoder_destroy(self._h)
             self._h = None
-        self._ws, self._old_ws = None, []
+        if getattr(self, "_ws", None) is not None:
+            self._ws.clear()
 
     def __del__(self):
         try:
@@ -180,21 +242,15 @@ class Encoder:
         return _lib.mh3a_encode_workspace_size(self._h, batch, samples, flags)
 
     def encode_hidden(self, wave, flags=0, out=None, stream=None):
-        torch = _torch()
-        x = Decoder._check_input(wave, 3, "wave")
+        st = _stream(stream, self.device)
+        x = _input(wave, "wave", self.device, 3, st)
         b, c, s = x.shape
         if c != 1:
             raise ValueError("wave must be (B, 1, samples)")
-        if out is None:
-            out = torch.empty((b, self.latent_dim, self.frames(s)), dtype=torch.float32, device=x.device)
-        nbytes = self.workspace_size(b, s, flags)
-        if self._ws is None or self._ws.numel() < nbytes:
-            if self._ws is not None:
-                self._old_ws.append(self._ws)  # a captured graph may still use it
-            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=f"cuda:{self.device}")
-        st = (stream or torch.cuda.current_stream(x.device)).cuda_stream
-        _lib.mh3a_encode_hidden(self._h, x.data_ptr(), b, s, out.data_ptr(), self._ws.data_ptr(), self._ws.numel(),
-                                flags, st)
+        out = _output(out, "out", self.device, (b, self.latent_dim, self.frames(s)), st)
+        ws = self._ws.get(self.workspace_size(b, s, flags), st)
+        _lib.mh3a_encode_hidden(self._h, x.data_ptr(), b, s, out.data_ptr(), ws.data_ptr(), ws.numel(), flags,
+                                st.cuda_stream)
         return out
 
     def timing(self, mode):

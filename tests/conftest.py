@@ -11,6 +11,46 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+    config.addinivalue_line("markers", "full_oracle(*jobs): GPU test that compares a full-size workload with "
+                                       "oracle results computed in background workers (tests/full_oracle.py)")
+
+
+_FULL_ORACLE = None
+
+
+def pytest_collection_finish(session):
+    """Start the oracle workers for the selected full-size tests (only when
+    such tests are selected and a GPU is there to run them)."""
+    global _FULL_ORACLE
+    names = []
+    for item in session.items:
+        m = item.get_closest_marker("full_oracle")
+        if m:
+            names += [n for n in m.args if n not in names]
+    if not names:
+        return
+    try:
+        import torch
+        if torch.cuda.device_count() < 1:  # (counting devices does not initialise the GPU)
+            return
+    except Exception:
+        return
+    from tests.full_oracle import Pool
+    _FULL_ORACLE = Pool(names)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    global _FULL_ORACLE
+    if _FULL_ORACLE is not None:
+        _FULL_ORACLE.close()
+        _FULL_ORACLE = None
+
+
+@pytest.fixture(scope="session")
+def full_oracle():
+    if _FULL_ORACLE is None:
+        pytest.skip("full-size oracle workers not started (no GPU)")
+    return _FULL_ORACLE
 
 
 @pytest.fixture(scope="session")

@@ -109,3 +109,48 @@ def test_checkpoint_decoder_and_encoder_match_direct(tmp_path, dec_params):
     torch.cuda.synchronize()
     for o in (dec, enc, ref_dec, ref_enc):
         o.close()
+
+
+@pytest.mark.gpu
+def test_checkpoint_decoder_and_encoder_match_the_oracle(tmp_path, dec_params):
+    # A component directory as the loader reads it (weights, config.json with
+    # the de-normalization vectors, released filter buffers for two
+    # activations): the loaded decoder and encoder against the oracle run on
+    # the arrays that were written, with the config and vectors as written.
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import oracle as O
+    p = dict(dec_params)
+    rng = np.random.default_rng(7)
+    for name in ("decoder.resblocks.4.activations.3", "decoder.activation_post"):
+        f = rng.uniform(-0.2, 0.6, size=12).astype(np.float32)
+        p[name + ".upsample.filter"] = f
+        p[name + ".downsample.lowpass.filter"] = np.ascontiguousarray(f[::-1])
+    enc_params = synth.make_encoder_params(dict(ENC_SMALL), seed=2)
+    mean, std = synth.make_denorm(SMALL_CONFIG["latent_channels"])
+    config = dict(SMALL_CONFIG, latents_mean=[float(v) for v in mean], latents_std=[float(v) for v in std],
+                  **ENC_SMALL)
+    extra = {"mean_proj.weight": np.ones((2, 2, 1), np.float32), "logs_proj.weight": np.ones((2, 2, 1), np.float32),
+             "pre_block.attn.qkv.weight": np.ones((6, 2), np.float32)}
+    d = write_component(tmp_path, dict(p, **enc_params), config=config, extra=extra)
+    print("[case] checkpoint-loaded decoder / encoder vs the oracle", flush=True)
+    dec, enc = checkpoint.load_from_dir(d, include_encoder=True)
+    z = synth.make_latents(2, 9, seed=4, channels=SMALL_CONFIG["latent_channels"])
+    got = dec.decode(torch.from_numpy(z).cuda(), flags=0x1 | 0x4).cpu().numpy().astype(np.float64)
+    ref = O.decode(p, z, SMALL_CONFIG, denormalize=True, latents_mean=mean, latents_std=std,
+                   clamp=False).astype(np.float64)
+    rl = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    tol = 1e-3 * max(1.0, float(np.max(np.abs(ref))) / 10.0)
+    print(f"[parity] checkpoint decode: rel_l2={rl:.3e} max_abs={np.max(np.abs(got - ref)):.3e}", flush=True)
+    assert rl <= 1e-4 and np.max(np.abs(got - ref)) <= tol
+    w = synth.make_waveform(2, 3 * 800 + 211, seed=3)
+    h = enc.encode_hidden(torch.from_numpy(w).cuda()).cpu().numpy().astype(np.float64)
+    href = O.encode_hidden(enc_params, w, ENC_SMALL).astype(np.float64)
+    rl = float(np.linalg.norm(h - href) / np.linalg.norm(href))
+    tol = 1e-3 * max(1.0, float(np.max(np.abs(href))) / 10.0)
+    print(f"[parity] checkpoint encode: rel_l2={rl:.3e} max_abs={np.max(np.abs(h - href)):.3e}", flush=True)
+    assert rl <= 1e-4 and np.max(np.abs(h - href)) <= tol
+    torch.cuda.synchronize()
+    dec.close()
+    enc.close()

@@ -9,16 +9,12 @@ The full-size workload (2 x 960000 samples) is checked on sampled frame
 windows: the oracle encodes only the samples within the stack's reach of
 each window (encoder_margin_frames, pinned in test_oracle_pins.py)."""
 
-import os
-import subprocess
-import sys
-
 import numpy as np
 import pytest
 
 import oracle as O
 from neural_audio_vae_amd import synth
-from tests.conftest import ROOT, encoder_margin_frames
+from tests.conftest import encoder_margin_frames
 
 pytestmark = pytest.mark.gpu
 
@@ -135,31 +131,12 @@ def test_encoder_argument_errors(default_encoder):
     torch.cuda.synchronize()
 
 
-_FP32_CHECK = r"""
-import sys
-sys.path.insert(0, sys.argv[1])
-import numpy as np, torch
-import oracle as O
-from neural_audio_vae_amd import Encoder, synth
-params = synth.make_encoder_params(seed=4)
-wave = synth.make_waveform(1, 5 * 800 - 77, seed=4)
-enc = Encoder(params)
-got = enc.encode_hidden(torch.from_numpy(wave).cuda())
-torch.cuda.synchronize()
-got = got.cpu().numpy().astype(np.float64)
-ref = O.encode_hidden(params, wave).astype(np.float64)
-rl = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-ma = float(np.max(np.abs(got - ref)))
-tol = 1e-3 * max(1.0, float(np.max(np.abs(ref))) / 10.0)
-print(f"fp32 encoder: rel_l2={rl:.3e} max_abs={ma:.3e} tol {tol:.2e}")
-print("ok" if rl <= 1e-4 and ma <= tol else "FAIL")
-"""
-
-
 def test_encoder_fp32_forms(dev):
-    # MH3A_BX6=0 keeps every conv on fp32 matrix cores with plain-row inputs
-    env = dict(os.environ, MH3A_BX6="0")
-    print("[case] fp32 encoder in a subprocess (MH3A_BX6=0)", flush=True)
-    r = subprocess.run([sys.executable, "-c", _FP32_CHECK, ROOT], env=env, capture_output=True, text=True, timeout=240)
-    print(r.stdout, flush=True)
-    assert r.returncode == 0 and "ok" in r.stdout.split(), r.stdout + r.stderr[-2000:]
+    # matrix_form = fp32 keeps every conv on fp32 matrix cores with plain-row inputs
+    from neural_audio_vae_amd import Encoder, _lib
+    print("[case] fp32 encoder (matrix_form = MH3A_MATRIX_FP32)", flush=True)
+    params = synth.make_encoder_params(seed=4)
+    wave = synth.make_waveform(1, 5 * HOP - 77, seed=4)
+    enc = Encoder(params, {"matrix_form": _lib.MH3A_MATRIX_FP32})
+    check("fp32 encoder S=3923", encode(enc, wave), O.encode_hidden(params, wave))
+    enc.close()
