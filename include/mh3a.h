@@ -184,6 +184,27 @@ int mh3a_decode(mh3a_decoder* dec, const float* latents, int64_t batch, int64_t 
                 void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
+ * mh3a_decode with no allocation and no workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving
+ * loops, harnesses that forbid hipMalloc). The intermediates live in a
+ * static device array of MH3A_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds from module load until the process ends; its
+ * address is looked up once per device by mh3a_decoder_create. The call
+ * allocates nothing and enqueues the same kernels as mh3a_decode.
+ *
+ * The scratch is shared by every call on one GPU (every decoder on it) and
+ * keeps the last call's contents; nothing in it needs to start at zero.
+ * Calls that overlap on one GPU (on different streams, or from several
+ * threads without ordering) race on it: order them, or use mh3a_decode.
+ * Errors: MH3A_E_INVALID_ARG (as mh3a_decode), MH3A_E_WORKSPACE when the
+ * decode's workspace (mh3a_decode_workspace_size) exceeds the scratch,
+ * MH3A_E_HIP.
+ */
+#define MH3A_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int mh3a_decode_noalloc(mh3a_decoder* dec, const float* latents, int64_t batch, int64_t frames, float* wave,
+                        uint32_t flags, void* stream);
+
+/*
  * The decode, stopped after layer `upto`, with that layer's output copied
  * to `out` (device). Layer numbering follows the decode order: 0 =
  * dec_in_proj (B, latent_dim, N), 1 = conv_pre (B, decoder_dim, N), then for

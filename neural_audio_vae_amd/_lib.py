@@ -39,6 +39,7 @@ EXPORTED = (
     "mh3a_destroy",
     "mh3a_decode_workspace_size",
     "mh3a_decode",
+    "mh3a_decode_noalloc",
     "mh3a_decode_layer_shape",
     "mh3a_decode_partial",
     "mh3a_decode_margin",
@@ -129,6 +130,8 @@ def load():
     lib.mh3a_decode_workspace_size.restype = c_int
     lib.mh3a_decode.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_uint32, c_void_p]
     lib.mh3a_decode.restype = c_int
+    lib.mh3a_decode_noalloc.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_uint32, c_void_p]
+    lib.mh3a_decode_noalloc.restype = c_int
     lib.mh3a_decode_layer_shape.argtypes = [c_void_p, c_int64, c_int, POINTER(c_int64), POINTER(c_int64)]
     lib.mh3a_decode_layer_shape.restype = c_int
     lib.mh3a_decode_partial.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_int, c_void_p, c_void_p, c_size_t,
@@ -285,6 +288,13 @@ def mh3a_decode_workspace_size(handle, batch, frames, flags=0):
 def mh3a_decode(handle, latents_ptr, batch, frames, wave_ptr, workspace_ptr, workspace_bytes, flags, stream):
     return _check(load().mh3a_decode(handle, latents_ptr, batch, frames, wave_ptr, workspace_ptr, workspace_bytes,
                                      flags, stream))
+
+
+MH3A_NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def mh3a_decode_noalloc(handle, latents_ptr, batch, frames, wave_ptr, flags, stream):
+    return _check(load().mh3a_decode_noalloc(handle, latents_ptr, batch, frames, wave_ptr, flags, stream))
 
 
 def mh3a_decode_layer_shape(handle, frames, upto):

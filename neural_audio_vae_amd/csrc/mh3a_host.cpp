@@ -1396,6 +1396,9 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
     HIP_TRY(hipSetDevice(device));
     HIP_TRY(hipDeviceGetAttribute(&d->num_cus, hipDeviceAttributeMultiprocessorCount, device));
     d->num_cus = std::max(1, d->num_cus);
+    // the device address of this GPU's static scratch (mh3a_decode_noalloc),
+    // looked up once per device
+    HIP_TRY(noalloc_scratch_lookup(device));
     d->blob_floats = (int64_t)blob.h.size();
     HIP_TRY(hipMalloc((void**)&d->blob, sizeof(float) * blob.h.size()));
     HIP_TRY(hipMemcpy(d->blob, blob.h.data(), sizeof(float) * blob.h.size(), hipMemcpyHostToDevice));
@@ -1432,6 +1435,22 @@ int mh3a_decode(mh3a_decoder* d, const float* latents, int64_t batch, int64_t fr
                 size_t workspace_bytes, uint32_t flags, void* stream) {
     if (!wave) return fail(MH3A_E_INVALID_ARG, "wave is null");
     return run_decode(d, latents, batch, frames, wave, -1, nullptr, workspace, workspace_bytes, flags,
+                      static_cast<hipStream_t>(stream));
+}
+
+int mh3a_decode_noalloc(mh3a_decoder* d, const float* latents, int64_t batch, int64_t frames, float* wave,
+                        uint32_t flags, void* stream) {
+    int rc = check_decode_args(d, batch, frames, flags);
+    if (rc) return rc;
+    if (!wave) return fail(MH3A_E_INVALID_ARG, "wave is null");
+    const size_t need = decode_ws_bytes(d, batch, frames, flags);
+    if (need > kNoAllocScratchBytes)
+        return fail(MH3A_E_WORKSPACE, "decode of %lld x %lld latents needs %zu bytes of scratch; the static scratch "
+                    "holds %zu (use mh3a_decode with a workspace)", (long long)batch, (long long)frames, need,
+                    kNoAllocScratchBytes);
+    void* ws = noalloc_scratch(d->device);
+    if (!ws) return fail(MH3A_E_HIP, "no static scratch address for device %d", d->device);
+    return run_decode(d, latents, batch, frames, wave, -1, nullptr, ws, kNoAllocScratchBytes, flags,
                       static_cast<hipStream_t>(stream));
 }
 

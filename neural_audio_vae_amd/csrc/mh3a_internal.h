@@ -259,4 +259,12 @@ struct FinalArgs {
 };
 hipError_t launch_final(const FinalArgs& a, int batch, hipStream_t stream);
 
+// Static device scratch of mh3a_decode_noalloc (mh3a_noalloc.hip): its size,
+// the once-per-device lookup of its device address (hipGetSymbolAddress
+// with the device current; called from the decoder's create) and that
+// address (null before the lookup).
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;  // MH3A_NOALLOC_SCRATCH_BYTES
+hipError_t noalloc_scratch_lookup(int device);
+void* noalloc_scratch(int device);
+
 }  // namespace mh3a
