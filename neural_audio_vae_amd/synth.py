@@ -20,7 +20,8 @@ Distributions (there are no released weights to load):
 Every stream is a numpy PCG64 generator keyed by ``(seed, stream, ...)``:
 stream 0 parameters, 1 latents, 2 mean/std, 3 free-standing stage inputs,
 4 encoder parameters (plain Snake ``alpha ~ U[0.5, 1.5]``), 5 waveforms
-(``N(0, 0.25)``, clipped to [-1, 1]).
+(``N(0, 0.25)``, clipped to [-1, 1]), 6 attention-projection and mean_proj
+parameters.
 The parameters therefore do not depend on the batch or sequence length.
 """
 
@@ -192,3 +193,52 @@ def make_waveform(batch, samples, seed=0):
     """Waveforms (batch, 1, samples) ~ N(0, 0.25) clipped to [-1, 1], float32."""
     rng = np.random.default_rng([seed, 5, batch, samples])
     return np.clip(0.5 * rng.standard_normal((batch, 1, samples)), -1.0, 1.0).astype(np.float32)
+
+
+PRE_DEFAULTS = {"latent_dim": 2048, "latent_channels": 32, "num_attention_heads": 8, "mlp_width": 128}
+# q/k and v weights are N(0, 1) / sqrt(D) times these: the encoder's hidden
+# state has an rms of ~120 under the synthetic encoder weights, so the
+# attention scores then spread over a few units (neither uniform nor
+# one-hot) and the GeGLU sees values of order one.
+QK_SCALE, V_SCALE = 0.01, 0.1
+
+
+def pre_block_param_specs(config=None):
+    """(name, shape, kind) of the attention projection and mean_proj."""
+    c = dict(PRE_DEFAULTS)
+    if config:
+        c.update({k: v for k, v in config.items() if k in PRE_DEFAULTS})
+    d, lc, f = c["latent_dim"], c["latent_channels"], c["mlp_width"]
+    return [
+        ("pre_block.attn.qkv.weight", (3 * d, d), "qkv"),
+        ("pre_block.attn.q_bias", (d,), "bias"),
+        ("pre_block.attn.v_bias", (d,), "bias"),
+        ("pre_block.attn.proj.weight", (lc, lc), "w"),
+        ("pre_block.attn.proj.bias", (lc,), "bias"),
+        ("pre_block.mlp.fc1.weight", (2 * f, lc), "w"),
+        ("pre_block.mlp.fc1.bias", (2 * f,), "bias"),
+        ("pre_block.mlp.fc2.weight", (lc, f), "w"),
+        ("pre_block.mlp.fc2.bias", (lc,), "bias"),
+        ("mean_proj.weight", (lc, lc, 1), "w"),
+        ("mean_proj.bias", (lc,), "bias"),
+    ]
+
+
+def make_pre_block_params(config=None, seed=0):
+    """Attention-projection and mean_proj parameters, name -> float32 array:
+    linear weights N(0, 1) / sqrt(fan_in) (q, k times QK_SCALE, v times
+    V_SCALE), biases N(0, 0.01)."""
+    rng = np.random.default_rng([seed, 6])
+    out = {}
+    for name, shape, kind in pre_block_param_specs(config):
+        if kind == "qkv":
+            arr = rng.standard_normal(shape) / np.sqrt(shape[1])
+            d = shape[0] // 3
+            arr[:2 * d] *= QK_SCALE
+            arr[2 * d:] *= V_SCALE
+        elif kind == "w":
+            arr = rng.standard_normal(shape) / np.sqrt(shape[1])
+        else:
+            arr = rng.normal(0.0, 0.01, size=shape)
+        out[name] = np.ascontiguousarray(arr, dtype=np.float32)
+    return out

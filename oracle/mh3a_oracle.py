@@ -57,6 +57,40 @@ the source of ``encode`` on the FastVideo page, with these readings:
   convolution has kernel 3 (padding 1) and latent_dim output channels.
 * E3 the crop ``x[..., pad:-pad]`` never fires: every unit keeps the
   length ("same" padding), so pad = 0.
+
+The attention projection ``pre_block`` and the posterior mean
+(``encode_item``) follow the Encoder bullet of the FastVideo module
+overview, which describes the block in prose only (causal multi-head
+attention over the latent stream with q/v biases and a forced zero k bias,
+head averaging, average pooling into latent_channels streams, an output
+projection and a GeGLU MLP), the source of ``encode`` (the block runs on the
+hidden state laid out time-major, then ``mean_proj`` is a 1x1 conv with
+bias) and the diffusers page (``is_causal=True`` through the attention
+dispatcher; ``num_attention_heads`` 8; ``latent_channels`` is the width of
+``mean_proj``; the pipeline consumes only the posterior mean, never
+``logs_proj``). Readings:
+
+* P1 tokens are the N hidden frames, each a D = latent_dim vector; one
+  fused projection ``pre_block.attn.qkv.weight`` (3D, D) gives q, k, v (in
+  that order, the page's required tensor name) plus a bias (b_q, 0, b_v):
+  the q and v biases are ``pre_block.attn.q_bias`` / ``v_bias`` (or the q
+  and v thirds of a fused ``qkv.bias``), the k bias is zero whatever is
+  stored.
+* P2 H = num_attention_heads heads of hd = D / H consecutive features;
+  scores q_t . k_u / sqrt(hd) (the scaled-dot-product default), causal:
+  token t attends to u <= t; softmax over u; o_h[t] = sum_u p v_u.
+* P3 head averaging: o[t] = (1 / H) sum_h o_h[t], a vector of hd.
+* P4 average pooling into C = latent_channels streams: stream c is the
+  mean of the g = hd / C consecutive features [c g, (c + 1) g).
+* P5 output projection ``pre_block.attn.proj`` (C -> C, bias).
+* P6 GeGLU MLP: ``pre_block.mlp.fc1`` (C -> 2F, bias) whose first half is
+  the value and second half the gate, value * GELU(gate) with the exact
+  (erf) GELU, then ``pre_block.mlp.fc2`` (F -> C, bias); F from the
+  weights' shapes.
+* P7 the steps compose in the order listed, with no residual connection
+  and no normalization (none is named).
+* P8 mean = ``mean_proj`` (1x1 conv, C -> latent_channels, bias) of the
+  block's output laid out channels-first again.
 """
 
 from __future__ import annotations
@@ -82,6 +116,7 @@ DEFAULT_CONFIG = {
     "hop_length": 800,
     "encoder_dim": 64,
     "encoder_rates": (2, 4, 4, 5, 5),
+    "num_attention_heads": 8,
     # Reading R4: BigVGAN's resampler, ratio 2.
     "filter_taps": 12,
     "filter_cutoff": 0.25,
@@ -464,3 +499,93 @@ def encode_hidden(params, wave, config=None):
     """Waveforms (B, 1, S) -> hidden (B, latent_dim, ceil(S / hop))."""
     wave = np.asarray(wave, dtype=F32)
     return np.stack([encode_hidden_item(params, wave[i].reshape(-1), config) for i in range(wave.shape[0])])
+
+
+# ---------------------------------------------------------------------------
+# Attention projection ``pre_block`` and the posterior mean (FastVideo
+# "minimax_h3_audio_vae", module overview, Encoder bullet, and the source of
+# ``encode``; diffusers "AutoencoderKLMiniMaxH3Audio", introduction and
+# section "encode"; readings P1-P8)
+# ---------------------------------------------------------------------------
+
+def gelu(x):
+    """Exact GELU: x Phi(x) = x (1 + erf(x / sqrt 2)) / 2, in float64."""
+    x = np.asarray(x, dtype=F64)
+    erf = np.frompyfunc(math.erf, 1, 1)
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)).astype(F64))
+
+
+def qkv_bias(params, dim):
+    """(b_q, 0, b_v) of length 3D (reading P1): separate q / v biases, or the
+    q and v thirds of a fused bias; the k third is zero either way."""
+    if "pre_block.attn.q_bias" in params:
+        bq = np.asarray(params["pre_block.attn.q_bias"], dtype=F64).reshape(-1)
+        bv = np.asarray(params["pre_block.attn.v_bias"], dtype=F64).reshape(-1)
+    elif "pre_block.attn.qkv.bias" in params:
+        b = np.asarray(params["pre_block.attn.qkv.bias"], dtype=F64).reshape(-1)
+        bq, bv = b[:dim], b[2 * dim:]
+    else:
+        bq = bv = np.zeros(dim)
+    return np.concatenate([bq, np.zeros(dim), bv])
+
+
+def causal_attention_heads_mean(q, k, v, heads):
+    """q, k, v (N, D) float32 -> (N, D / heads): per head h (features
+    [h hd, (h + 1) hd)), softmax over u <= t of q_t . k_u / sqrt(hd),
+    times v_u, then the mean over the heads (readings P2, P3). float64
+    inside, float32 out."""
+    q, k, v = (np.asarray(a, dtype=F64) for a in (q, k, v))
+    n, dim = q.shape
+    hd = dim // heads
+    future = np.triu(np.ones((n, n), dtype=bool), 1)
+    out = np.zeros((n, hd), dtype=F64)
+    for h in range(heads):
+        sl = slice(h * hd, (h + 1) * hd)
+        s = q[:, sl] @ k[:, sl].T / math.sqrt(hd)
+        s[future] = -np.inf
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out += p @ v[:, sl]
+    return _f32(out / heads)
+
+
+def pre_block_item(params, hidden, config=None):
+    """The attention projection of one item: hidden (D, N) float32 ->
+    (C, N) float32, C = latent_channels (readings P1-P7)."""
+    cfg = dict(DEFAULT_CONFIG, **(config or {}))
+    heads, c = cfg["num_attention_heads"], cfg["latent_channels"]
+    x = np.asarray(hidden, dtype=F32).T  # tokens = frames
+    dim = x.shape[1]
+    hd = dim // heads
+    assert hd * heads == dim and hd % c == 0, (dim, heads, c)
+    w = np.asarray(params["pre_block.attn.qkv.weight"], dtype=F64)
+    qkv = _f32(x.astype(F64) @ w.T + qkv_bias(params, dim))
+    o = causal_attention_heads_mean(qkv[:, :dim], qkv[:, dim:2 * dim], qkv[:, 2 * dim:], heads)
+    a = _f32(o.astype(F64).reshape(o.shape[0], c, hd // c).mean(axis=2))
+
+    def linear(z, name):
+        return z.astype(F64) @ np.asarray(params[name + ".weight"], dtype=F64).T + \
+            np.asarray(params[name + ".bias"], dtype=F64)
+
+    y = _f32(linear(a, "pre_block.attn.proj"))
+    hcat = linear(y, "pre_block.mlp.fc1")
+    f = hcat.shape[1] // 2
+    m = _f32(hcat[:, :f] * gelu(hcat[:, f:]))
+    return _f32(linear(m, "pre_block.mlp.fc2")).T
+
+
+def encode_item(params, wave, config=None):
+    """One waveform (S,) -> the posterior mean (latent_channels, ceil(S / hop)):
+    the convolution stack, the attention projection, then mean_proj (1x1
+    conv with bias)."""
+    hidden = encode_hidden_item(params, wave, config)
+    proj = pre_block_item(params, hidden, config)
+    return conv1d(proj, params["mean_proj.weight"], params["mean_proj.bias"])
+
+
+def encode(params, wave, config=None):
+    """Waveforms (B, 1, S) -> posterior means (B, latent_channels, ceil(S / hop));
+    items are independent."""
+    wave = np.asarray(wave, dtype=F32)
+    return np.stack([encode_item(params, wave[i].reshape(-1), config) for i in range(wave.shape[0])])

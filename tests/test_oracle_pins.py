@@ -631,3 +631,125 @@ def test_encoder_window_interior_equals_full_encode():
     # the right edge: the window ends at the ragged end of the waveform
     win = O.encode_hidden(params, wave[:, :, (n - 1 - m) * 800:], ENC_SMALL)
     np.testing.assert_array_equal(win[:, :, m:], full[:, :, n - 1:])
+
+
+# ---------------------------------------------------------------------------
+# Attention projection pre_block and the posterior mean (FastVideo
+# "minimax_h3_audio_vae", module overview, Encoder bullet; diffusers
+# "AutoencoderKLMiniMaxH3Audio": is_causal=True, mean_proj)
+# ---------------------------------------------------------------------------
+
+PB_SMALL = {"latent_dim": 16, "latent_channels": 4, "num_attention_heads": 2, "mlp_width": 6}
+
+
+def pre_block_torch(params, hidden, heads, c):
+    """The readings written with torch's own routines in float64: F.linear,
+    scaled_dot_product_attention with is_causal=True (the mask the diffusers
+    page names), a mean over heads, avg_pool1d, F.gelu (exact), conv1d."""
+    P = {k: torch.tensor(np.asarray(v, np.float64)) for k, v in params.items()}
+    x = torch.tensor(np.asarray(hidden, np.float64)).T  # (N, D)
+    n, d = x.shape
+    hd = d // heads
+    bias = torch.cat([P["pre_block.attn.q_bias"], torch.zeros(d, dtype=F64), P["pre_block.attn.v_bias"]])
+    q, k, v = F.linear(x, P["pre_block.attn.qkv.weight"], bias).split(d, dim=1)
+    q, k, v = (t.reshape(n, heads, hd).transpose(0, 1) for t in (q, k, v))  # (H, N, hd)
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True).mean(dim=0)  # (N, hd)
+    a = F.avg_pool1d(o.unsqueeze(1), kernel_size=hd // c).squeeze(1)       # (N, C)
+    y = F.linear(a, P["pre_block.attn.proj.weight"], P["pre_block.attn.proj.bias"])
+    val, gate = F.linear(y, P["pre_block.mlp.fc1.weight"], P["pre_block.mlp.fc1.bias"]).chunk(2, dim=1)
+    m = val * F.gelu(gate, approximate="none")
+    y2 = F.linear(m, P["pre_block.mlp.fc2.weight"], P["pre_block.mlp.fc2.bias"])
+    return F.conv1d(y2.T.unsqueeze(0), P["mean_proj.weight"], P["mean_proj.bias"])[0].numpy()
+
+
+@pytest.mark.parametrize("cfg,n", [(PB_SMALL, 13), ({"latent_dim": 64, "latent_channels": 4,
+                                                     "num_attention_heads": 8, "mlp_width": 16}, 40)])
+def test_pre_block_and_mean_proj_match_torch_composition(cfg, n):
+    p = synth.make_pre_block_params(cfg, seed=1)
+    hidden = synth.make_signal((cfg["latent_dim"], n), seed=2, scale=100.0)
+    proj = O.pre_block_item(p, hidden, cfg)
+    got = O.conv1d(proj, p["mean_proj.weight"], p["mean_proj.bias"])
+    ref = pre_block_torch(p, hidden, cfg["num_attention_heads"], cfg["latent_channels"])
+    assert got.shape == (cfg["latent_channels"], n)
+    assert rel_l2(got, ref) < 2e-6  # the oracle rounds six intermediate results to float32
+
+
+def test_first_token_attends_only_to_itself_and_uniform_scores_give_running_means():
+    rng = np.random.default_rng(0)
+    n, d, heads = 9, 12, 3
+    q, k, v = (rng.standard_normal((n, d)).astype(np.float32) for _ in range(3))
+    o = O.causal_attention_heads_mean(q, k, v, heads)
+    hd = d // heads
+    # token 0 sees only itself: the mean over heads of its own v
+    np.testing.assert_allclose(o[0], v[0].reshape(heads, hd).mean(axis=0), rtol=1e-6)
+    # q = 0: every allowed score is 0, the softmax is uniform over u <= t,
+    # so each head's output is the running mean of v
+    o0 = O.causal_attention_heads_mean(np.zeros_like(q), k, v, heads)
+    run = np.cumsum(v.astype(np.float64), axis=0) / np.arange(1, n + 1)[:, None]
+    np.testing.assert_allclose(o0, run.reshape(n, heads, hd).mean(axis=1), rtol=1e-6, atol=1e-7)
+
+
+def test_identical_heads_average_to_one_head():
+    rng = np.random.default_rng(1)
+    n, hd, heads = 7, 4, 3
+    q1, k1, v1 = (rng.standard_normal((n, hd)).astype(np.float32) for _ in range(3))
+    one = O.causal_attention_heads_mean(q1, k1, v1, 1)
+    many = O.causal_attention_heads_mean(np.tile(q1, heads), np.tile(k1, heads), np.tile(v1, heads), heads)
+    np.testing.assert_allclose(many, one, rtol=1e-6)
+
+
+def test_attention_is_causal():
+    # changing the hidden state at frame t changes no output before t
+    p = synth.make_pre_block_params(PB_SMALL, seed=3)
+    h = synth.make_signal((16, 11), seed=4, scale=100.0)
+    a = O.pre_block_item(p, h, PB_SMALL)
+    h2 = h.copy()
+    h2[:, 6] += 50.0
+    b = O.pre_block_item(p, h2, PB_SMALL)
+    np.testing.assert_array_equal(a[:, :6], b[:, :6])
+    assert np.abs(a[:, 6:] - b[:, 6:]).max() > 1e-3
+
+
+def test_k_bias_is_forced_to_zero_and_fused_bias_form():
+    p = synth.make_pre_block_params(PB_SMALL, seed=5)
+    h = synth.make_signal((16, 8), seed=6, scale=100.0)
+    ref = O.pre_block_item(p, h, PB_SMALL)
+    fused = {k: v for k, v in p.items() if k not in ("pre_block.attn.q_bias", "pre_block.attn.v_bias")}
+    kb = np.full(16, 3.0, np.float32)  # a stored k bias is ignored
+    fused["pre_block.attn.qkv.bias"] = np.concatenate([p["pre_block.attn.q_bias"], kb, p["pre_block.attn.v_bias"]])
+    np.testing.assert_array_equal(O.pre_block_item(fused, h, PB_SMALL), ref)
+
+
+def test_gelu_closed_forms_and_geglu_half_order():
+    # GELU(x) = x Phi(x): Phi(1) = 0.841344746068543, Phi(2) = 0.977249868051821
+    np.testing.assert_allclose(O.gelu([0.0, 1.0, -1.0, 2.0]),
+                               [0.0, 0.841344746068543, -0.158655253931457, 1.954499736103642], rtol=1e-13)
+    # fc1 rows: the value half reads 1, the gate half reads stream 0; a block
+    # whose attention output is constant makes the gate known exactly
+    cfg = dict(PB_SMALL, mlp_width=1)
+    p = synth.make_pre_block_params(cfg, seed=7)
+    p["pre_block.attn.qkv.weight"][:] = 0.0
+    p["pre_block.attn.v_bias"][:] = 2.0       # every v is 2 -> every pooled stream is 2
+    p["pre_block.attn.proj.weight"][:] = np.eye(4, dtype=np.float32)
+    p["pre_block.attn.proj.bias"][:] = 0.0
+    p["pre_block.mlp.fc1.weight"][:] = [[0, 0, 0, 0], [0.5, 0, 0, 0]]  # value 0 + 1 (bias), gate 1
+    p["pre_block.mlp.fc1.bias"][:] = [1.0, 0.0]
+    p["pre_block.mlp.fc2.weight"][:] = 1.0
+    p["pre_block.mlp.fc2.bias"][:] = 0.0
+    out = O.pre_block_item(p, np.zeros((16, 3), np.float32), cfg)
+    np.testing.assert_allclose(out, 0.841344746068543, rtol=1e-6)  # value 1 times GELU(gate 1)
+    p["pre_block.mlp.fc1.bias"][:] = [3.0, 0.0]  # value 3, gate 1: 3 GELU(1) = 2.524; swapped halves: GELU(3) = 2.996
+    out = O.pre_block_item(p, np.zeros((16, 3), np.float32), cfg)
+    np.testing.assert_allclose(out, 3 * 0.841344746068543, rtol=1e-6)
+
+
+def test_encode_mean_of_items_is_independent_and_composes():
+    cfg = dict(PB_SMALL, encoder_dim=4)
+    p = dict(synth.make_encoder_params(cfg, seed=8), **synth.make_pre_block_params(cfg, seed=8))
+    w = synth.make_waveform(2, 3 * 800 + 5, seed=8)
+    m = O.encode(p, w, cfg)
+    assert m.shape == (2, 4, 4)
+    np.testing.assert_array_equal(m[1], O.encode(p, w[1:2], cfg)[0])
+    h = O.encode_hidden(p, w[:1], cfg)[0]
+    np.testing.assert_array_equal(m[0], O.conv1d(O.pre_block_item(p, h, cfg), p["mean_proj.weight"],
+                                                 p["mean_proj.bias"]))
