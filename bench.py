@@ -340,15 +340,15 @@ def main():
 
 
 def cpu_baseline_encode(params, n_samples):
-    """The oracle's encoder stack, as it stands, on the first n samples of
-    item 0 of the workload."""
+    """The oracle's encode (stack, attention projection, mean_proj), as it
+    stands, on the first n samples of item 0 of the workload."""
     import numpy as np
     import oracle as O
     from neural_audio_vae_amd import synth
     threads = _blas_threads()
     wave = synth.make_waveform(1, n_samples, seed=0)
     t0 = time.perf_counter()
-    h = O.encode_hidden(params, wave)
+    h = O.encode(params, wave)
     dt = time.perf_counter() - t0
     assert h.shape[-1] == -(-n_samples // 800)
     return {
@@ -363,9 +363,10 @@ def cpu_baseline_encode(params, n_samples):
 
 
 def main_encode(args):
-    """A step is one pass of the encoder's convolution stack (k7 conv, five
-    strided blocks of Snake residual units, final Snake + k3 conv) over a
-    batch of seeded synthetic waveforms resident in HBM."""
+    """A step is one whole encode to the posterior mean: the convolution
+    stack (k7 conv, five strided blocks of Snake residual units, final Snake
+    + k3 conv), the causal attention projection and mean_proj, over a batch
+    of seeded synthetic waveforms resident in HBM."""
     import torch
     from neural_audio_vae_amd import Encoder, _lib, synth
 
@@ -377,14 +378,14 @@ def main_encode(args):
         print(f"--workload {args.workload} is a decoder workload (use --path decode)", file=sys.stderr)
         return 2
     batch, samples, desc = ENC_WORKLOADS[args.workload]
-    params = synth.make_encoder_params(seed=0)
+    params = dict(synth.make_encoder_params(seed=0), **synth.make_pre_block_params(seed=0))
     form = "fp32" if args.fp32_matrix else "split"
     enc = Encoder(params, {"matrix_form": _lib.MH3A_MATRIX_FP32} if args.fp32_matrix else None)
     x = torch.from_numpy(synth.make_waveform(batch, samples, seed=0)).cuda()
-    out = torch.empty((batch, enc.latent_dim, enc.frames(samples)), dtype=torch.float32, device="cuda")
+    out = torch.empty((batch, enc.latent_channels, enc.frames(samples)), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        enc.encode_hidden(x, out=out, stream=stream)
+        enc.encode_mean(x, out=out, stream=stream)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
@@ -392,7 +393,7 @@ def main_encode(args):
     for i in range(args.steps):
         if i == args.steps - 1:
             enc.timing(_lib.MH3A_TIMING_AMP_CONV)  # the residual units' k7 convs only
-        enc.encode_hidden(x, out=out, stream=stream)
+        enc.encode_mean(x, out=out, stream=stream)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
@@ -400,7 +401,7 @@ def main_encode(args):
     unit_only = enc.timing_read()
     enc.timing(_lib.MH3A_TIMING_ALL)
     for _ in range(args.steps):
-        enc.encode_hidden(x, out=out, stream=stream)
+        enc.encode_mean(x, out=out, stream=stream)
     torch.cuda.synchronize()
     kernels = enc.timing_read()
     enc.timing(_lib.MH3A_TIMING_OFF)
@@ -422,8 +423,9 @@ def main_encode(args):
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"encoder convolution stack of the MiniMax-H3 audio VAE, {desc}, encoder_dim 64, "
-                        "rates (2, 4, 4, 5, 5), hidden 2048, seeded random weights",
+            "workload": f"encoder of the MiniMax-H3 audio VAE to the posterior mean, {desc}: convolution stack "
+                        "(encoder_dim 64, rates (2, 4, 4, 5, 5), hidden 2048), causal attention projection (8 heads, "
+                        "32 streams, GeGLU 128) and mean_proj, seeded random weights",
             "batch": batch,
             "samples_per_item": samples,
         },

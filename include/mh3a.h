@@ -332,6 +332,8 @@ typedef struct {
     int rates[MH3A_MAX_ENC_BLOCKS];   /* their strides (2, 4, 4, 5, 5) */
     int latent_dim;                   /* hidden channels (2048) */
     int matrix_form;                  /* MH3A_MATRIX_SPLIT (default) or MH3A_MATRIX_FP32 */
+    int latent_channels;              /* posterior width: mean_proj outputs (32) */
+    int num_attention_heads;          /* heads of the attention projection (8) */
 } mh3a_encoder_config;
 void mh3a_encoder_config_default(mh3a_encoder_config* cfg);
 int mh3a_encoder_create(const mh3a_encoder_config* cfg, const mh3a_tensor* params, int n_params, int device,
@@ -345,6 +347,42 @@ int mh3a_encode_workspace_size(const mh3a_encoder* enc, int64_t batch, int64_t s
 /* wave: device (B, 1, samples); hidden: device (B, latent_dim, F). */
 int mh3a_encode_hidden(mh3a_encoder* enc, const float* wave, int64_t batch, int64_t samples, float* hidden,
                        void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * The whole encode: waveform -> posterior mean (the mode, the only part of
+ * the posterior the MiniMax-H3 pipeline consumes: diffusers
+ * "AutoencoderKLMiniMaxH3Audio", section "encode"; logs_proj is not
+ * evaluated). The convolution stack, then the attention projection
+ * `pre_block` and `mean_proj` (FastVideo "minimax_h3_audio_vae", module
+ * overview, Encoder bullet, and the source of encode; the page gives the
+ * block in prose only -- these are the readings taken):
+ *   tokens are the F hidden frames; q, k, v = x W^T + (b_q, 0, b_v) with
+ *     W = pre_block.attn.qkv.weight (3 latent_dim, latent_dim), b_q / b_v =
+ *     pre_block.attn.q_bias / v_bias (or the q and v thirds of a fused
+ *     pre_block.attn.qkv.bias; absent = 0); the k bias is zero whatever is
+ *     stored;
+ *   H = num_attention_heads heads of hd = latent_dim / H consecutive
+ *     features (hd a power of two in [8, 256]); causal softmax attention
+ *     (token t attends to u <= t), scores scaled by 1 / sqrt(hd);
+ *   the head outputs averaged (a vector of hd per token), then average
+ *     pooled into C = latent_channels streams of hd / C consecutive
+ *     features;
+ *   pre_block.attn.proj.{weight (C, C), bias}; then the GeGLU MLP:
+ *     pre_block.mlp.fc1.{weight (2 F, C), bias} whose first F outputs are
+ *     the value and last F the gate, value * GELU(gate) (exact erf form),
+ *     pre_block.mlp.fc2.{weight (C, F), bias}; no residual, no norm;
+ *   mean = mean_proj.{weight (C, C, 1), bias}, a 1x1 conv.
+ * The encoder has these stages when its parameters hold
+ * pre_block.attn.qkv.weight (then every tensor above but the q/v biases is
+ * required). mean: device (B, latent_channels, F) with F = ceil(samples /
+ * hop). Workspace: mh3a_encode_mean_workspace_size bytes, 256-byte aligned.
+ * Errors as mh3a_encode_hidden, and MH3A_E_MISSING_TENSOR for an encoder
+ * built without the attention projection.
+ */
+int mh3a_encode_mean_workspace_size(const mh3a_encoder* enc, int64_t batch, int64_t samples, uint32_t flags,
+                                    size_t* bytes);
+int mh3a_encode_mean(mh3a_encoder* enc, const float* wave, int64_t batch, int64_t samples, float* mean,
+                     void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
 /* Kernel timing as mh3a_timing_enable / mh3a_timing_read (MH3A_TIMING_AMP_CONV
  * selects the residual units' k7 convs). */
 int mh3a_encoder_timing_enable(mh3a_encoder* enc, int enable);

@@ -56,6 +56,8 @@ EXPORTED = (
     "mh3a_encode_frames",
     "mh3a_encode_workspace_size",
     "mh3a_encode_hidden",
+    "mh3a_encode_mean_workspace_size",
+    "mh3a_encode_mean",
     "mh3a_encoder_timing_enable",
     "mh3a_encoder_timing_read",
 )
@@ -90,7 +92,8 @@ MH3A_MAX_ENC_BLOCKS = 8
 
 class mh3a_encoder_config(Structure):
     _fields_ = [("encoder_dim", c_int), ("num_blocks", c_int), ("rates", c_int * MH3A_MAX_ENC_BLOCKS),
-                ("latent_dim", c_int), ("matrix_form", c_int)]
+                ("latent_dim", c_int), ("matrix_form", c_int), ("latent_channels", c_int),
+                ("num_attention_heads", c_int)]
 
 
 class mh3a_kernel_stats(Structure):
@@ -169,6 +172,11 @@ def load():
     lib.mh3a_encode_hidden.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_uint32,
                                        c_void_p]
     lib.mh3a_encode_hidden.restype = c_int
+    lib.mh3a_encode_mean_workspace_size.argtypes = [c_void_p, c_int64, c_int64, c_uint32, POINTER(c_size_t)]
+    lib.mh3a_encode_mean_workspace_size.restype = c_int
+    lib.mh3a_encode_mean.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_uint32,
+                                     c_void_p]
+    lib.mh3a_encode_mean.restype = c_int
     lib.mh3a_encoder_timing_enable.argtypes = [c_void_p, c_int]
     lib.mh3a_encoder_timing_enable.restype = c_int
     lib.mh3a_encoder_timing_read.argtypes = [c_void_p, POINTER(mh3a_kernel_stats), c_int, POINTER(c_int)]
@@ -360,10 +368,11 @@ def mh3a_encoder_config_default():
 
 def make_encoder_config(overrides=None):
     """An mh3a_encoder_config from the defaults plus encoder_dim,
-    encoder_rates, latent_dim and matrix_form overrides."""
+    encoder_rates, latent_dim, matrix_form, latent_channels and
+    num_attention_heads overrides."""
     cfg = mh3a_encoder_config_default()
     o = dict(overrides or {})
-    for key in ("encoder_dim", "latent_dim", "matrix_form"):
+    for key in ("encoder_dim", "latent_dim", "matrix_form", "latent_channels", "num_attention_heads"):
         if key in o:
             setattr(cfg, key, int(o[key]))
     if "encoder_rates" in o:
@@ -415,3 +424,14 @@ def mh3a_encoder_timing_read(handle):
     _check(load().mh3a_encoder_timing_read(handle, arr, MH3A_MAX_KERNEL_KINDS, byref(n)))
     return {arr[i].name.decode(): {"launches": arr[i].launches, "ms": arr[i].ms, "flops": arr[i].flops,
                                    "bytes": arr[i].bytes} for i in range(n.value)}
+
+
+def mh3a_encode_mean_workspace_size(handle, batch, samples, flags=0):
+    n = c_size_t()
+    _check(load().mh3a_encode_mean_workspace_size(handle, batch, samples, flags, byref(n)))
+    return n.value
+
+
+def mh3a_encode_mean(handle, wave_ptr, batch, samples, mean_ptr, workspace_ptr, workspace_bytes, flags, stream):
+    return _check(load().mh3a_encode_mean(handle, wave_ptr, batch, samples, mean_ptr, workspace_ptr,
+                                          workspace_bytes, flags, stream))

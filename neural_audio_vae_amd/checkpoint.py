@@ -93,7 +93,8 @@ def load_from_file(weights_path, include_encoder=False, config=None, component_d
                   device=device)
     enc = None
     if include_encoder:
-        enc_cfg = {k: config[k] for k in ("encoder_dim", "encoder_rates", "latent_dim") if k in config}
+        enc_cfg = {k: config[k] for k in ("encoder_dim", "encoder_rates", "latent_dim", "latent_channels",
+                                          "num_attention_heads") if k in config}
         enc = Encoder(params, enc_cfg, device=device)
     return dec, enc
 

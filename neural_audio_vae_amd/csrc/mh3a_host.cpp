@@ -163,11 +163,14 @@ enum Kind {
     KIND_ENC_UNIT_CONV,  // encoder: the residual units' dilated k7 convs
     KIND_ENC_CONV,       // encoder: pointwise, strided, first and last convs
     KIND_ENC_SNAKE,      // encoder: Snake (and space-to-depth) passes
+    KIND_ENC_ATTN,       // encoder: causal attention of the attention projection
+    KIND_ENC_TAIL,       // encoder: head sum, projection, GeGLU MLP, mean_proj
     KIND_COUNT
 };
 const char* const kKindNames[KIND_COUNT] = {"dec_in_proj", "conv_pre",   "ups_transposed_conv", "amp_conv",
                                             "amp_act",     "act_post_conv_post", "amp_unit", "input_split",
-                                            "enc_unit_conv", "enc_conv", "enc_snake"};
+                                            "enc_unit_conv", "enc_conv", "enc_snake", "enc_attention",
+                                            "enc_proj_mlp_mean"};
 static_assert(KIND_COUNT <= MH3A_MAX_KERNEL_KINDS, "timing classes fit mh3a_timing_read's table");
 
 struct TimingRec {
@@ -1606,6 +1609,12 @@ struct mh3a_encoder : mh3a_net {
     std::vector<SnakeLayer> snakes;    // [block][unit][0, 1], then [block] before `down`, then the final one
     std::vector<int> block_c;          // input channels of each block
     int hop = 1;
+    // the attention projection and mean_proj (present when the parameters
+    // hold pre_block.attn.qkv.weight)
+    bool has_pre = false;
+    ConvLayer qkv;                     // 1x1, latent_dim -> 3 latent_dim, bias (b_q, 0, b_v)
+    int pre_hd = 0, pre_f = 0;         // head width, GeGLU width
+    int64_t wf_off = -1, bf_off = -1, w1_off = -1, b1_off = -1, w2_off = -1, b2_off = -1, wm_off = -1, bm_off = -1;
 };
 
 namespace {
@@ -1625,6 +1634,8 @@ int enc_check_config(const mh3a_encoder_config* c) {
     if (hop > 65536 || dim > 65536) return fail(MH3A_E_CONFIG, "encoder hop or width too large");
     if (c->matrix_form != MH3A_MATRIX_SPLIT && c->matrix_form != MH3A_MATRIX_FP32)
         return fail(MH3A_E_CONFIG, "unknown matrix_form %d", c->matrix_form);
+    if (c->latent_channels < 1 || c->num_attention_heads < 1)
+        return fail(MH3A_E_CONFIG, "latent_channels and num_attention_heads must be positive");
     return MH3A_OK;
 }
 
@@ -1690,6 +1701,100 @@ int enc_snake_layer(Blob& blob, const Table& t, const std::string& name, int c, 
     return MH3A_OK;
 }
 
+// A linear layer's weight (rows, cols), also accepted as (rows, cols, 1).
+int fetch_matrix(const Table& t, const std::string& name, int64_t rows, int64_t cols, const float** out) {
+    const Param* p = t.get(name);
+    if (!p) return fail(MH3A_E_MISSING_TENSOR, "missing %s", name.c_str());
+    if (!shape_is(p, rows, cols) && !shape_is(p, rows, cols, 1))
+        return fail(MH3A_E_SHAPE, "%s must be (%lld, %lld)", name.c_str(), (long long)rows, (long long)cols);
+    *out = p->data;
+    return MH3A_OK;
+}
+
+// The attention projection and mean_proj (FastVideo "minimax_h3_audio_vae",
+// module overview, Encoder bullet, and the source of encode). Readings:
+// one fused q/k/v projection `pre_block.attn.qkv.weight` (3 D, D) with bias
+// (b_q, 0, b_v) -- `pre_block.attn.q_bias` / `v_bias`, or the q and v thirds
+// of a fused `qkv.bias`, absent meaning zero; the k bias is zero whatever
+// is stored; H heads of hd = D / H features, scores scaled by 1 / sqrt(hd),
+// causal; the heads averaged; average pooling of hd features into C =
+// latent_channels streams of hd / C consecutive features; the output
+// projection `pre_block.attn.proj` (C -> C); the GeGLU MLP
+// `pre_block.mlp.fc1` (C -> 2 F, value half then gate half, exact GELU)
+// and `pre_block.mlp.fc2` (F -> C); `mean_proj` (1x1, C -> C). The head
+// mean and the pooling are linear, so they are folded here into the output
+// projection's weights: wf[o][j] = proj[o][j / g] / (g H), g = hd / C.
+int enc_pre_block(Blob& blob, const Table& t, mh3a_encoder* e) {
+    const mh3a_encoder_config& c = e->cfg;
+    const int D = c.latent_dim, H = c.num_attention_heads, C = c.latent_channels;
+    if (D % H) return fail(MH3A_E_CONFIG, "latent_dim %d is not a multiple of num_attention_heads %d", D, H);
+    const int hd = D / H;
+    if (!attn_head_width_ok(hd)) return fail(MH3A_E_CONFIG, "head width %d must be a power of two in [8, 256]", hd);
+    if (hd % C)
+        return fail(MH3A_E_CONFIG, "head width %d is not a multiple of latent_channels %d (average pooling)", hd, C);
+    int rc;
+    const float* wqkv = nullptr;
+    if ((rc = fetch_matrix(t, "pre_block.attn.qkv.weight", 3 * (int64_t)D, D, &wqkv))) return rc;
+    std::vector<float> bias(3 * (size_t)D, 0.0f);
+    const float* bq = nullptr;
+    const float* bv = nullptr;
+    if (t.get("pre_block.attn.q_bias") || t.get("pre_block.attn.v_bias")) {
+        if ((rc = fetch_vector(t, "pre_block.attn.q_bias", D, &bq))) return rc;
+        if ((rc = fetch_vector(t, "pre_block.attn.v_bias", D, &bv))) return rc;
+    } else if (t.get("pre_block.attn.qkv.bias")) {
+        const float* b3 = nullptr;
+        if ((rc = fetch_vector(t, "pre_block.attn.qkv.bias", 3 * (int64_t)D, &b3))) return rc;
+        bq = b3;
+        bv = b3 + 2 * (size_t)D;  // the k third is not read: forced to zero
+    }
+    for (int i = 0; i < D; ++i) {
+        bias[i] = bq ? bq[i] : 0.0f;
+        bias[2 * (size_t)D + i] = bv ? bv[i] : 0.0f;
+    }
+    std::vector<float> w(wqkv, wqkv + 3 * (size_t)D * D);
+    ConvLayer& Q = e->qkv;
+    add_conv(blob, Q, w, bias.data(), 3 * D, D, 1);
+    Q.dil = 1;
+    Q.alg_taps = 1;
+    Q.kind = KIND_ENC_CONV;
+    if (enc_split_ok(Q)) {
+        Q.w6_off = blob.reserve(packed_weight_floats6(3 * D, D, 1));
+        pack_conv_weights6(w.data(), 3 * D, D, 1, blob.h.data() + Q.w6_off);
+    }
+    const float *wp = nullptr, *bp = nullptr, *w1 = nullptr, *b1 = nullptr, *w2 = nullptr, *b2 = nullptr;
+    const float *wm = nullptr, *bm = nullptr;
+    if ((rc = fetch_matrix(t, "pre_block.attn.proj.weight", C, C, &wp))) return rc;
+    if ((rc = fetch_vector(t, "pre_block.attn.proj.bias", C, &bp))) return rc;
+    const Param* p1 = t.get("pre_block.mlp.fc1.weight");
+    if (!p1) return fail(MH3A_E_MISSING_TENSOR, "missing pre_block.mlp.fc1.weight");
+    const int64_t f2 = p1->shape[0];
+    if (f2 < 2 || f2 % 2) return fail(MH3A_E_SHAPE, "pre_block.mlp.fc1.weight needs an even number of rows");
+    const int F = (int)(f2 / 2);
+    if ((rc = fetch_matrix(t, "pre_block.mlp.fc1.weight", f2, C, &w1))) return rc;
+    if ((rc = fetch_vector(t, "pre_block.mlp.fc1.bias", f2, &b1))) return rc;
+    if ((rc = fetch_matrix(t, "pre_block.mlp.fc2.weight", C, F, &w2))) return rc;
+    if ((rc = fetch_vector(t, "pre_block.mlp.fc2.bias", C, &b2))) return rc;
+    if ((rc = fetch_matrix(t, "mean_proj.weight", C, C, &wm))) return rc;
+    if ((rc = fetch_vector(t, "mean_proj.bias", C, &bm))) return rc;
+    const int g = hd / C;
+    std::vector<float> wf((size_t)C * hd);
+    for (int o = 0; o < C; ++o)
+        for (int j = 0; j < hd; ++j) wf[(size_t)o * hd + j] = (float)((double)wp[(size_t)o * C + j / g] / ((double)g * H));
+    e->wf_off = blob.add(wf.data(), (int64_t)wf.size());
+    e->bf_off = blob.add(bp, C);
+    e->w1_off = blob.add(w1, f2 * C);
+    e->b1_off = blob.add(b1, f2);
+    e->w2_off = blob.add(w2, (int64_t)C * F);
+    e->b2_off = blob.add(b2, C);
+    e->wm_off = blob.add(wm, (int64_t)C * C);
+    e->bm_off = blob.add(bm, C);
+    if (pre_tail_lds_bytes(hd, C, F) > 160 * 1024) return fail(MH3A_E_CONFIG, "attention projection too wide");
+    e->pre_hd = hd;
+    e->pre_f = F;
+    e->has_pre = true;
+    return MH3A_OK;
+}
+
 bool enc_bx6(const mh3a_encoder* e, const ConvLayer& L) {
     return L.w6_off >= 0 && e->cfg.matrix_form == MH3A_MATRIX_SPLIT;
 }
@@ -1708,7 +1813,7 @@ struct EncWs {
     int64_t x, r, p, partial;  // floats of each region (all items)
 };
 
-EncWs enc_ws_floats(const mh3a_encoder* e, int64_t batch, int64_t frames, bool inv) {
+EncWs enc_ws_floats(const mh3a_encoder* e, int64_t batch, int64_t frames, bool inv, bool pre = false) {
     EncWs w{0, 0, 0, 0};
     int64_t len = frames * e->hop;
     auto part = [&](const ConvLayer& L, int64_t positions) {
@@ -1736,6 +1841,14 @@ EncWs enc_ws_floats(const mh3a_encoder* e, int64_t batch, int64_t frames, bool i
     w.p = std::max(w.p, enc_snake_item_floats(e, e->conv_out, len));
     part(e->conv_out, len);
     w.r = w.x;
+    if (pre) {
+        // hidden -> R; its split form -> P; q/k/v -> X; the heads' outputs -> R
+        const int64_t D = e->cfg.latent_dim;
+        w.x = std::max(w.x, 3 * D * frames);
+        w.r = std::max(w.r, D * frames);
+        w.p = std::max(w.p, enc_snake_item_floats(e, e->qkv, frames));
+        part(e->qkv, frames);
+    }
     w.x = round_up(w.x * batch, 64);
     w.r = round_up(w.r * batch, 64);
     w.p = round_up(w.p * batch, 64);
@@ -1756,8 +1869,8 @@ int enc_check_args(const mh3a_encoder* e, int64_t batch, int64_t samples, uint32
     return MH3A_OK;
 }
 
-size_t enc_ws_bytes(const mh3a_encoder* e, int64_t batch, int64_t samples, uint32_t flags) {
-    const EncWs w = enc_ws_floats(e, batch, enc_frames(e, samples), (flags & MH3A_FLAG_BATCH_INVARIANT) != 0);
+size_t enc_ws_bytes(const mh3a_encoder* e, int64_t batch, int64_t samples, uint32_t flags, bool pre = false) {
+    const EncWs w = enc_ws_floats(e, batch, enc_frames(e, samples), (flags & MH3A_FLAG_BATCH_INVARIANT) != 0, pre);
     return (size_t)(w.x + w.r + w.p + w.partial) * sizeof(float);
 }
 
@@ -1792,18 +1905,25 @@ hipError_t enc_run_conv(const mh3a_encoder* e, const ConvLayer& L, const float* 
                     batch, res, nullptr, 1.0f, false, inv, true, partial, st, bx6 ? (int)pk_lp(l_in) : 0, bx6);
 }
 
-int run_encode(mh3a_encoder* e, const float* wave, int64_t batch, int64_t samples, float* hidden, void* ws,
-               size_t ws_bytes, uint32_t flags, hipStream_t st) {
+// hidden != null: the convolution stack into `hidden`; mean != null: the
+// whole encode (stack, attention projection, mean_proj) into `mean`, the
+// hidden state staying in the workspace.
+int run_encode(mh3a_encoder* e, const float* wave, int64_t batch, int64_t samples, float* hidden, float* mean,
+               void* ws, size_t ws_bytes, uint32_t flags, hipStream_t st) {
     int rc = enc_check_args(e, batch, samples, flags);
     if (rc) return rc;
-    if (!wave || !hidden) return fail(MH3A_E_INVALID_ARG, "null wave or hidden pointer");
+    const bool pre = mean != nullptr;
+    if (!wave || !(hidden || mean)) return fail(MH3A_E_INVALID_ARG, "null wave or output pointer");
+    if (pre && !e->has_pre)
+        return fail(MH3A_E_MISSING_TENSOR, "the encoder was built without the attention projection "
+                    "(pre_block.attn.qkv.weight and the tensors that go with it)");
     if (!ws) return fail(MH3A_E_WORKSPACE, "workspace is null");
     if ((uintptr_t)ws % 256) return fail(MH3A_E_WORKSPACE, "workspace must be 256-byte aligned");
     const bool inv = (flags & MH3A_FLAG_BATCH_INVARIANT) != 0;
-    const size_t need = enc_ws_bytes(e, batch, samples, flags);
+    const size_t need = enc_ws_bytes(e, batch, samples, flags, pre);
     if (ws_bytes < need) return fail(MH3A_E_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     const int64_t frames = enc_frames(e, samples);
-    const EncWs w = enc_ws_floats(e, batch, frames, inv);
+    const EncWs w = enc_ws_floats(e, batch, frames, inv, pre);
     float* bufX = static_cast<float*>(ws);
     float* bufR = bufX + w.x;
     float* bufP = bufR + w.r;
@@ -1835,7 +1955,72 @@ int run_encode(mh3a_encoder* e, const float* wave, int64_t batch, int64_t sample
         len = lout;
     }
     HIP_TRY(enc_run_snake(e, e->snakes[si++], e->conv_out, bufX, len, 1, 0, len, bufP, B, st));
-    HIP_TRY(enc_run_conv(e, e->conv_out, bufP, len, len, hidden, B, nullptr, inv, partial, st));
+    float* hid = pre ? bufR : hidden;
+    HIP_TRY(enc_run_conv(e, e->conv_out, bufP, len, len, hid, B, nullptr, inv, partial, st));
+    if (!pre) return ok();
+
+    // attention projection: q/k/v (pointwise conv) -> X, heads -> R, then the tail -> mean
+    const int D = e->cfg.latent_dim, F = (int)frames;
+    const ConvLayer& Q = e->qkv;
+    if (enc_bx6(e, Q)) {
+        ActArgs sa;
+        std::memset(&sa, 0, sizeof sa);
+        sa.x = hid;
+        sa.x_bstride = (int64_t)D * F;
+        sa.y = bufP;
+        sa.y_bstride = enc_snake_item_floats(e, Q, F);
+        sa.c = D;
+        sa.l = F;
+        sa.lp = (int)pk_lp(F);
+        sa.pieces = kPieces;
+        TimedLaunch tl(e, st, KIND_ENC_SNAKE);
+        HIP_TRY(launch_split(sa, B, st));
+        tl.done(KIND_ENC_SNAKE, 0.0, 10.0 * B * (double)D * F);
+        HIP_TRY(enc_run_conv(e, Q, bufP, F, F, bufX, B, nullptr, inv, partial, st));
+    } else {
+        HIP_TRY(run_conv(e, Q, hid, (int64_t)D * F, F, F, bufX, 3 * (int64_t)D * F, B, nullptr, nullptr, 1.0f, false,
+                         inv, true, partial, st));
+    }
+    AttnArgs aa;
+    aa.qkv = bufX;
+    aa.qkv_bstride = 3 * (int64_t)D * F;
+    aa.o = bufR;
+    aa.o_bstride = (int64_t)D * F;
+    aa.n = F;
+    aa.dim = D;
+    aa.heads = e->cfg.num_attention_heads;
+    aa.hd = e->pre_hd;
+    aa.inv_sqrt_hd = (float)(1.0 / std::sqrt((double)e->pre_hd));
+    {
+        TimedLaunch tl(e, st, KIND_ENC_ATTN);
+        HIP_TRY(launch_attention(aa, B, st));
+        // q.k and p.v over the causal triangle
+        tl.done(KIND_ENC_ATTN, 4.0 * B * (double)D * F * (F + 1) / 2.0, 4.0 * B * (double)D * F * 4.0);
+    }
+    const int C = e->cfg.latent_channels;
+    PreTailArgs ta;
+    ta.o = bufR;
+    ta.o_bstride = (int64_t)D * F;
+    ta.n = F;
+    ta.heads = e->cfg.num_attention_heads;
+    ta.hd = e->pre_hd;
+    ta.c = C;
+    ta.f = e->pre_f;
+    ta.lc = C;
+    ta.wf = e->blob + e->wf_off;
+    ta.bf = e->blob + e->bf_off;
+    ta.w1 = e->blob + e->w1_off;
+    ta.b1 = e->blob + e->b1_off;
+    ta.w2 = e->blob + e->w2_off;
+    ta.b2 = e->blob + e->b2_off;
+    ta.wm = e->blob + e->wm_off;
+    ta.bm = e->blob + e->bm_off;
+    ta.y = mean;
+    ta.y_bstride = (int64_t)C * F;
+    TimedLaunch tl(e, st, KIND_ENC_TAIL);
+    HIP_TRY(launch_pre_tail(ta, B, st));
+    tl.done(KIND_ENC_TAIL, 2.0 * B * (double)F * (D + (double)C * e->pre_hd + 3.0 * C * e->pre_f + (double)C * C),
+            4.0 * B * (double)F * (D + C));
     return ok();
 }
 
@@ -1851,6 +2036,8 @@ void mh3a_encoder_config_default(mh3a_encoder_config* c) {
     const int rates[5] = {2, 4, 4, 5, 5};
     for (int i = 0; i < 5; ++i) c->rates[i] = rates[i];
     c->latent_dim = 2048;
+    c->latent_channels = 32;
+    c->num_attention_heads = 8;
 }
 
 int mh3a_encoder_create(const mh3a_encoder_config* cfg, const mh3a_tensor* params, int n_params, int device,
@@ -1919,6 +2106,7 @@ int mh3a_encoder_create(const mh3a_encoder_config* cfg, const mh3a_tensor* param
     if ((rc = enc_conv(blob, t, "encoder.block." + std::to_string(cfg->num_blocks + 2), e->conv_out, cfg->latent_dim,
                        dim, 3, 1, 1, KIND_ENC_CONV)))
         return rc;
+    if (t.get("pre_block.attn.qkv.weight") && (rc = enc_pre_block(blob, t, e))) return rc;
 
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(MH3A_E_HIP, "no HIP device available");
@@ -1962,7 +2150,26 @@ int mh3a_encode_workspace_size(const mh3a_encoder* e, int64_t batch, int64_t sam
 
 int mh3a_encode_hidden(mh3a_encoder* e, const float* wave, int64_t batch, int64_t samples, float* hidden,
                        void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
-    return run_encode(e, wave, batch, samples, hidden, workspace, workspace_bytes, flags,
+    if (!hidden) return fail(MH3A_E_INVALID_ARG, "hidden is null");
+    return run_encode(e, wave, batch, samples, hidden, nullptr, workspace, workspace_bytes, flags,
+                      static_cast<hipStream_t>(stream));
+}
+
+int mh3a_encode_mean_workspace_size(const mh3a_encoder* e, int64_t batch, int64_t samples, uint32_t flags,
+                                    size_t* bytes) {
+    if (!bytes) return fail(MH3A_E_INVALID_ARG, "bytes is null");
+    *bytes = 0;
+    int rc = enc_check_args(e, batch, samples, flags);
+    if (rc) return rc;
+    if (!e->has_pre) return fail(MH3A_E_MISSING_TENSOR, "the encoder was built without the attention projection");
+    *bytes = enc_ws_bytes(e, batch, samples, flags, true);
+    return ok();
+}
+
+int mh3a_encode_mean(mh3a_encoder* e, const float* wave, int64_t batch, int64_t samples, float* mean,
+                     void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+    if (!mean) return fail(MH3A_E_INVALID_ARG, "mean is null");
+    return run_encode(e, wave, batch, samples, nullptr, mean, workspace, workspace_bytes, flags,
                       static_cast<hipStream_t>(stream));
 }
 

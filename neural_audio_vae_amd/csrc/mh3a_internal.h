@@ -267,4 +267,43 @@ constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;  // MH3A_NOALLOC_SCRA
 hipError_t noalloc_scratch_lookup(int device);
 void* noalloc_scratch(int device);
 
+// Causal multi-head attention of the encoder's attention projection:
+// qkv (B, 3 dim, n) channel-major rows (q, k, v thirds, head h at features
+// [h hd, (h + 1) hd) of each), o (B, dim, n) the heads' outputs side by side.
+struct AttnArgs {
+    const float* qkv;
+    int64_t qkv_bstride;
+    float* o;
+    int64_t o_bstride;
+    int n, dim, heads, hd;  // hd = dim / heads, one of attn_head_width_ok's
+    float inv_sqrt_hd;
+};
+// Head widths the attention kernel has instances for: 8, 16, ..., 256.
+bool attn_head_width_ok(int hd);
+size_t attn_lds_bytes(int hd);
+hipError_t launch_attention(const AttnArgs& a, int batch, hipStream_t stream);
+
+// The rest of the attention projection and mean_proj, per token:
+//   y = wf (sum_h o_h) + bf        (wf: the output projection with the head
+//                                   mean and the average pooling folded in)
+//   g = (w1_v y + b1_v) * GELU(w1_g y + b1_g)
+//   z = w2 g + b2;   out = wm z + bm
+struct PreTailArgs {
+    const float* o;
+    int64_t o_bstride;
+    int n, heads, hd, c, f, lc;
+    const float* wf;  // [c][hd]
+    const float* bf;  // [c]
+    const float* w1;  // [2 f][c] (value rows, then gate rows)
+    const float* b1;  // [2 f]
+    const float* w2;  // [c][f]
+    const float* b2;  // [c]
+    const float* wm;  // [lc][c]
+    const float* bm;  // [lc]
+    float* y;         // (B, lc, n)
+    int64_t y_bstride;
+};
+size_t pre_tail_lds_bytes(int hd, int c, int f);
+hipError_t launch_pre_tail(const PreTailArgs& a, int batch, hipStream_t stream);
+
 }  // namespace mh3a

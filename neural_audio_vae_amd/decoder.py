@@ -219,6 +219,7 @@ class Encoder:
         self.device = int(device)
         cfg = _lib.make_encoder_config(self.config)
         self.latent_dim = cfg.latent_dim
+        self.latent_channels = cfg.latent_channels
         self._h = _lib.mh3a_encoder_create(cfg, params, self.device)
         self._ws = _Workspaces(self.device)
 
@@ -251,6 +252,21 @@ class Encoder:
         ws = self._ws.get(self.workspace_size(b, s, flags), st)
         _lib.mh3a_encode_hidden(self._h, x.data_ptr(), b, s, out.data_ptr(), ws.data_ptr(), ws.numel(), flags,
                                 st.cuda_stream)
+        return out
+
+    def encode_mean(self, wave, flags=0, out=None, stream=None):
+        """Waveform (B, 1, S) -> posterior mean (B, latent_channels,
+        ceil(S / hop)): the convolution stack, the attention projection and
+        mean_proj (the encoder must hold the pre_block parameters)."""
+        st = _stream(stream, self.device)
+        x = _input(wave, "wave", self.device, 3, st)
+        b, c, s = x.shape
+        if c != 1:
+            raise ValueError("wave must be (B, 1, samples)")
+        out = _output(out, "out", self.device, (b, self.latent_channels, self.frames(s)), st)
+        ws = self._ws.get(_lib.mh3a_encode_mean_workspace_size(self._h, b, s, flags), st)
+        _lib.mh3a_encode_mean(self._h, x.data_ptr(), b, s, out.data_ptr(), ws.data_ptr(), ws.numel(), flags,
+                              st.cuda_stream)
         return out
 
     def timing(self, mode):

@@ -13,6 +13,9 @@ from neural_audio_vae_amd import checkpoint, synth
 from tests.conftest import SMALL_CONFIG
 
 ENC_SMALL = {"encoder_dim": 4, "latent_dim": 16}
+# the attention projection of that encoder: latent_channels must match the
+# decoder's (4), two heads of 8 features
+PRE_SMALL = {"latent_dim": 16, "latent_channels": 4, "num_attention_heads": 2, "mlp_width": 6}
 
 
 def write_component(tmp_path, params, config=None, extra=None):
@@ -94,18 +97,19 @@ def test_checkpoint_decoder_and_encoder_match_direct(tmp_path, dec_params):
     mean, std = synth.make_denorm(SMALL_CONFIG["latent_channels"])
     config = dict(SMALL_CONFIG, latents_mean=[float(v) for v in mean], latents_std=[float(v) for v in std],
                   **ENC_SMALL)
-    extra = {"mean_proj.weight": np.ones((2, 2, 1), np.float32), "logs_proj.weight": np.ones((2, 2, 1), np.float32),
-             "pre_block.attn.qkv.weight": np.ones((6, 2), np.float32)}
+    extra = dict(synth.make_pre_block_params(PRE_SMALL, seed=2), **{"logs_proj.weight": np.ones((4, 4, 1), np.float32)})
+    config["num_attention_heads"] = 2
     d = write_component(tmp_path, dict(dec_params, **enc_params), config=config, extra=extra)
     print("[case] checkpoint load + decode / encode vs direct", flush=True)
     dec, enc = checkpoint.load_from_dir(d, include_encoder=True)
     ref_dec = Decoder(dec_params, SMALL_CONFIG, latents_mean=mean, latents_std=std)
-    ref_enc = Encoder(enc_params, ENC_SMALL)
+    ref_enc = Encoder(dict(enc_params, **extra), dict(ENC_SMALL, latent_channels=4, num_attention_heads=2))
     z = torch.from_numpy(synth.make_latents(2, 3, seed=1, channels=4)).cuda()
     np.testing.assert_array_equal(dec.decode(z, flags=0x1 | 0x4).cpu().numpy(),
                                   ref_dec.decode(z, flags=0x1 | 0x4).cpu().numpy())
     w = torch.from_numpy(synth.make_waveform(1, 2400, seed=1)).cuda()
     np.testing.assert_array_equal(enc.encode_hidden(w).cpu().numpy(), ref_enc.encode_hidden(w).cpu().numpy())
+    np.testing.assert_array_equal(enc.encode_mean(w).cpu().numpy(), ref_enc.encode_mean(w).cpu().numpy())
     torch.cuda.synchronize()
     for o in (dec, enc, ref_dec, ref_enc):
         o.close()
@@ -131,8 +135,9 @@ def test_checkpoint_decoder_and_encoder_match_the_oracle(tmp_path, dec_params):
     mean, std = synth.make_denorm(SMALL_CONFIG["latent_channels"])
     config = dict(SMALL_CONFIG, latents_mean=[float(v) for v in mean], latents_std=[float(v) for v in std],
                   **ENC_SMALL)
-    extra = {"mean_proj.weight": np.ones((2, 2, 1), np.float32), "logs_proj.weight": np.ones((2, 2, 1), np.float32),
-             "pre_block.attn.qkv.weight": np.ones((6, 2), np.float32)}
+    pre = synth.make_pre_block_params(PRE_SMALL, seed=3)
+    extra = dict(pre, **{"logs_proj.weight": np.ones((4, 4, 1), np.float32)})
+    config["num_attention_heads"] = 2
     d = write_component(tmp_path, dict(p, **enc_params), config=config, extra=extra)
     print("[case] checkpoint-loaded decoder / encoder vs the oracle", flush=True)
     dec, enc = checkpoint.load_from_dir(d, include_encoder=True)
@@ -151,6 +156,13 @@ def test_checkpoint_decoder_and_encoder_match_the_oracle(tmp_path, dec_params):
     tol = 1e-3 * max(1.0, float(np.max(np.abs(href))) / 10.0)
     print(f"[parity] checkpoint encode: rel_l2={rl:.3e} max_abs={np.max(np.abs(h - href)):.3e}", flush=True)
     assert rl <= 1e-4 and np.max(np.abs(h - href)) <= tol
+    # the posterior mean: stack, attention projection, mean_proj
+    ocfg = dict(ENC_SMALL, latent_channels=4, num_attention_heads=2)
+    mu = enc.encode_mean(torch.from_numpy(w).cuda()).cpu().numpy().astype(np.float64)
+    muref = O.encode(dict(enc_params, **pre), w, ocfg).astype(np.float64)
+    rl = float(np.linalg.norm(mu - muref) / np.linalg.norm(muref))
+    print(f"[parity] checkpoint encode mean: rel_l2={rl:.3e} max_abs={np.max(np.abs(mu - muref)):.3e}", flush=True)
+    assert rl <= 1e-4 and np.max(np.abs(mu - muref)) <= 1e-3
     torch.cuda.synchronize()
     dec.close()
     enc.close()

@@ -22,6 +22,9 @@ torch = pytest.importorskip("torch")
 
 REL_TOL, ABS_TOL, REF_SCALE = 1e-4, 1e-3, 10.0
 ENC_SMALL = {"encoder_dim": 4, "latent_dim": 16}
+# its attention projection: two heads of 8 features pooled into 4 streams
+PRE_SMALL = {"latent_dim": 16, "latent_channels": 4, "num_attention_heads": 2, "mlp_width": 6}
+ENC_PRE_SMALL = dict(ENC_SMALL, latent_channels=4, num_attention_heads=2)
 HOP = 800
 
 
@@ -69,6 +72,64 @@ def test_small_encoder_matches_oracle(dev):
         got = encode(enc, wave)
         check(f"small B={batch} S={samples}", got, O.encode_hidden(params, wave, ENC_SMALL))
     enc.close()
+
+
+def encode_mean(enc, wave, flags=0):
+    out = enc.encode_mean(torch.from_numpy(wave).cuda(), flags=flags)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_small_encoder_mean_matches_oracle(dev):
+    # the whole encode: stack, causal attention projection, mean_proj; 71
+    # frames span three 32-token query blocks with a ragged last one
+    from neural_audio_vae_amd import Encoder
+    params = dict(synth.make_encoder_params(ENC_SMALL, seed=3), **synth.make_pre_block_params(PRE_SMALL, seed=3))
+    enc = Encoder(params, ENC_PRE_SMALL)
+    for batch, samples in ((2, 9 * HOP + 37), (1, 1), (1, 70 * HOP + 5), (2, 64 * HOP)):
+        print(f"[case] small encoder mean B={batch} S={samples}", flush=True)
+        wave = synth.make_waveform(batch, samples, seed=samples + 1)
+        got = encode_mean(enc, wave)
+        check(f"small mean B={batch} S={samples}", got, O.encode(params, wave, ENC_PRE_SMALL))
+    enc.close()
+
+
+@pytest.fixture(scope="module")
+def default_encoder_pre(dev):
+    from neural_audio_vae_amd import Encoder
+    params = dict(synth.make_encoder_params(seed=0), **synth.make_pre_block_params(seed=0))
+    e = Encoder(params)
+    yield e, params
+    e.close()
+
+
+def test_default_encoder_mean_matches_oracle(default_encoder_pre):
+    # default widths: 8 heads of 256 features, 32 streams, GeGLU width 128
+    enc, params = default_encoder_pre
+    for batch, samples in ((2, 7 * HOP + 123), (1, 70 * HOP + 5)):
+        print(f"[case] default encoder mean B={batch} S={samples}", flush=True)
+        wave = synth.make_waveform(batch, samples, seed=11)
+        got = encode_mean(enc, wave)
+        assert got.shape == (batch, 32, -(-samples // HOP))
+        check(f"default mean B={batch} S={samples}", got, O.encode(params, wave))
+
+
+def test_encoder_mean_fp32_forms(dev):
+    from neural_audio_vae_amd import Encoder, _lib
+    print("[case] fp32 encoder mean (matrix_form = MH3A_MATRIX_FP32)", flush=True)
+    params = dict(synth.make_encoder_params(seed=4), **synth.make_pre_block_params(seed=4))
+    wave = synth.make_waveform(1, 40 * HOP - 77, seed=4)
+    enc = Encoder(params, {"matrix_form": _lib.MH3A_MATRIX_FP32})
+    check("fp32 encoder mean S=31923", encode_mean(enc, wave), O.encode(params, wave))
+    enc.close()
+
+
+def test_encode_mean_needs_the_attention_projection(default_encoder):
+    from neural_audio_vae_amd import _lib
+    enc, _ = default_encoder  # built from the convolution stack's parameters only
+    with pytest.raises(_lib.MH3AError) as e:
+        enc.encode_mean(torch.zeros((1, 1, HOP), device="cuda"))
+    assert e.value.code == _lib.MH3A_E_MISSING_TENSOR
 
 
 def test_default_encoder_ragged_matches_oracle(default_encoder):

@@ -87,23 +87,37 @@ def test_c3_every_output(c3_out, full_oracle, item):
 
 
 @pytest.fixture(scope="module")
-def e3_out(dev):
+def e3_params():
+    return dict(synth.make_encoder_params(seed=0), **synth.make_pre_block_params(seed=0))
+
+
+@pytest.fixture(scope="module")
+def e3_out(dev, e3_params):
+    """(hidden, posterior mean) of the e3 workload on the GPU."""
     from neural_audio_vae_amd import Encoder
     batch, samples, seed = FO.E3
-    enc = Encoder(synth.make_encoder_params(seed=0))
+    enc = Encoder(e3_params)
     print(f"[case] e3 encode B={batch} S={samples}", flush=True)
-    h = enc.encode_hidden(torch.from_numpy(synth.make_waveform(batch, samples, seed=seed)).to(dev))
+    wave = torch.from_numpy(synth.make_waveform(batch, samples, seed=seed)).to(dev)
+    h = enc.encode_hidden(wave)
+    mu = enc.encode_mean(wave)
     torch.cuda.synchronize()
-    out = h.cpu().numpy()
+    out = h.cpu().numpy(), mu.cpu().numpy()
     enc.close()
     return out
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.full_oracle(*[f"e3/0/{k}" for k in range(len(FO.E3_WINDOWS))])
-def test_e3_item0_every_frame(e3_out, full_oracle):
-    # item 0's 1200 frames from four oracle windows whose interiors tile it
+def test_e3_item0_every_frame(e3_out, e3_params, full_oracle):
+    # item 0's 1200 frames from four oracle windows whose interiors tile it;
+    # then the attention projection (causal over all 1200 frames) and
+    # mean_proj of the oracle on that hidden state
+    import oracle as O
+    hidden, mean = e3_out
     parts = [full_oracle.result(f"e3/0/{k}") for k in range(len(FO.E3_WINDOWS))]
     ref = np.concatenate(parts, axis=1)
-    assert ref.shape == e3_out[0].shape
-    check("e3 item 0 hidden", e3_out[0], ref, abs_tol=ABS_TOL * max(1.0, float(np.max(np.abs(ref))) / 10.0))
+    assert ref.shape == hidden[0].shape
+    check("e3 item 0 hidden", hidden[0], ref, abs_tol=ABS_TOL * max(1.0, float(np.max(np.abs(ref))) / 10.0))
+    mref = O.conv1d(O.pre_block_item(e3_params, ref), e3_params["mean_proj.weight"], e3_params["mean_proj.bias"])
+    check("e3 item 0 posterior mean", mean[0], mref)
