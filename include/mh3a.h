@@ -81,11 +81,21 @@ extern "C" {
  * mh3a_encoder_config.matrix_form), fixed at create ---- */
 /* Every conv with split-product weights runs on the bf16 matrix cores,
  * each fp32 operand split into three bf16 pieces and the six products of
- * order <= 2 summed in fp32 (fp32-level accuracy; the default). */
+ * order <= 2 summed in fp32 (about 2^-27 relative per product; the
+ * encoder's default). */
 #define MH3A_MATRIX_SPLIT 0
 /* Every conv runs on the fp32 matrix cores (v_mfma_f32_32x32x2f32 /
  * 16x16x4f32): slower, kept as a second, independent form of the products. */
 #define MH3A_MATRIX_FP32 1
+/* The decoder's default: the wide convs (AMP convs of 64+ channels,
+ * conv_pre, the transposed convs) split each operand into two fp16 pieces,
+ * v0 = fp16(v), v1 = fp16(v - v0), the weights first scaled by a power of
+ * two per layer, and sum the three products w0 x0, w0 x1, w1 x0 in fp32 on
+ * the fp16 matrix cores (about 2^-22 relative per product). Every value
+ * those convs read must stay below 65504 in magnitude (the fp16 range);
+ * MH3A_MATRIX_SPLIT has no such bound. The narrow stages' fused unit
+ * kernel and the bf16 flag keep bf16 pieces. Decoder only. */
+#define MH3A_MATRIX_SPLIT_F16 2
 
 /* ---- architecture limits ---- */
 #define MH3A_MAX_STAGES 8
@@ -122,7 +132,7 @@ typedef struct {
     int filter_taps;                /* only 12 is supported */
     double filter_cutoff;
     double filter_half_width;
-    int matrix_form;                /* MH3A_MATRIX_SPLIT (default) or MH3A_MATRIX_FP32 */
+    int matrix_form;                /* MH3A_MATRIX_SPLIT_F16 (default), _SPLIT or _FP32 */
 } mh3a_config;
 
 /* Fill *cfg with the defaults above. */

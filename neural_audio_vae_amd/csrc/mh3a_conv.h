@@ -24,7 +24,9 @@ namespace mh3a {
 //
 // PREC selects the products: 0 fp32 matrix cores; 1 the bf16 operand
 // variant (three-term split on fp32 matrix cores); 2 split products on bf16
-// matrix cores (packed input in the split-product form, see kPieces); 3 the
+// matrix cores (packed input in the split-product form, see kPieces); 4 the
+// two-piece fp16 form on fp16 matrix cores (three products w0 x0, w0 x1,
+// w1 x0 with the weights scaled by 2^e, see kPiecesH); 3 the
 // bf16 operand variant on bf16 matrix cores (pieces 0 and 1 only, the three
 // products w0 x0, w0 x1, w1 x0: the numerics of PREC 1).
 //
@@ -35,9 +37,11 @@ template <int MBW, int NBW, int WM, int WN, bool ACT, int PREC, int TAPS, int RB
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((MBW * NBW <= 4 && PREC < 2) ? 4 : 1)))
 conv_kernel(ConvArgs a) {
     constexpr bool BF16 = PREC == 1;
-    constexpr bool BX6 = PREC >= 2;            // bf16 matrix cores on the pieces
-    constexpr int NPROD = PREC == 3 ? 3 : 6;   // piece products per pair
-    constexpr int NPA = PREC == 3 ? 2 : kPieces;  // weight / activation pieces used
+    constexpr bool BX6 = PREC >= 2;            // bf16 / fp16 matrix cores on the pieces
+    constexpr bool H16 = PREC == 4;            // fp16 pieces (two per value)
+    constexpr int NPROD = PREC == 2 ? 6 : 3;   // piece products per pair
+    constexpr int NPA = PREC == 2 ? kPieces : 2;  // weight / activation pieces used
+    constexpr int NPL = H16 ? kPiecesH : kPieces; // planes per chunk of the packed input (and weight pieces)
     static_assert(WM * WN == 4, "four consumer waves");
     static_assert(RB == 32 || (RB == 16 && MBW == 1 && WM == 1 && TAPS > 0 && !BF16), "16-row tiles");
     constexpr int CI = kChunk;
@@ -50,14 +54,14 @@ conv_kernel(ConvArgs a) {
     constexpr int PS6 = bx6_plane(NWG, TAPS > 0 ? TAPS : 1, DMAX);  // split-product plane stride (positions)
     // an item is CPI chunks (split products: two, so that each barrier hands
     // over as much matrix-core work as an fp32 item)
-    constexpr int CPI = BX6 ? bx6_cpi(NWG, TAPS, DMAX) : 1;
+    constexpr int CPI = BX6 ? bx6_cpi(NWG, TAPS, DMAX, NPL) : 1;
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const bool producer = wave >= 4;
     const int W = NWG + (a.taps - 1) * a.dil;
-    // one item's operand window: [CI][W] floats, or kPieces planes of PS6 16-byte groups
-    const int ABUF = BX6 ? CPI * kPieces * PS6 * 4 : CI * W;
+    // one item's operand window: [CI][W] floats, or NPL planes of PS6 16-byte groups per chunk
+    const int ABUF = BX6 ? CPI * NPL * PS6 * 4 : CI * W;
     float* abuf = lds;                       // [2][ABUF]
     float* xs = lds + 2 * CI * W;            // [CI][act_xs_len(W)]   (act only)
     float* ss = xs + CI * act_xs_len(W);     // [CI][act_ss_len(W)]   (act only)
@@ -189,6 +193,11 @@ conv_kernel(ConvArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb)
             bias_frag[mb] = (hi == 0 && c0 == 0) ? a.bias[min((mb_base + mb) * 32 + lo, a.c_out - 1)] : 0.0f;
+        if constexpr (H16) {
+            // the sums carry the weights' scale 2^e until the epilogue
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb) bias_frag[mb] *= a.wscale;
+        }
     };
     auto init_acc = [&]() {
         const float ones = hi == 0 ? 1.0f : 0.0f;
@@ -270,31 +279,39 @@ conv_kernel(ConvArgs a) {
     // is padding. Weights ride a three-slot ring two pairs ahead.
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+    typedef _Float16 v8h __attribute__((ext_vector_type(8)));
     const int G6 = nch * (TAPS > 0 ? TAPS : 1) / 2;  // weight groups (slot pairs) per 32-row block
-    v4u A6a[BX6 ? kPieces : 1][MBW], A6b[BX6 ? kPieces : 1][MBW], A6c[BX6 ? kPieces : 1][MBW];
-    auto load_a6 = [&](v4u (&dst)[BX6 ? kPieces : 1][MBW], int mb_base, int ph, int g) {
-        const v4u* wp = reinterpret_cast<const v4u*>(a.w6 + (int64_t)ph * a.w6_phase_stride) + (int64_t)g * kPieces * 64 + lane;
+    constexpr int NAW = BX6 ? NPL : 1;  // weight pieces per slot pair in the packing
+    v4u A6a[NAW][MBW], A6b[NAW][MBW], A6c[NAW][MBW];
+    auto load_a6 = [&](v4u (&dst)[NAW][MBW], int mb_base, int ph, int g) {
+        const v4u* wp = reinterpret_cast<const v4u*>(a.w6 + (int64_t)ph * a.w6_phase_stride) + (int64_t)g * NAW * 64 + lane;
 #pragma unroll
         for (int p = 0; p < (BX6 ? NPA : 1); ++p)
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb)
-                dst[p][mb] = wp[((int64_t)min(mb_base + mb, mb_tot - 1) * G6 * kPieces + p) * 64];
+                dst[p][mb] = wp[((int64_t)min(mb_base + mb, mb_tot - 1) * G6 * NAW + p) * 64];
     };
     // the six products of order <= 2 (the first three for PREC 3): (A piece, B piece),
     // measured 1-2% faster in this order
-    auto mfma6 = [&](const v4u (&A)[BX6 ? kPieces : 1][MBW], const v4u (&B)[BX6 ? kPieces : 1][NBW]) {
+    auto mfma6 = [&](const v4u (&A)[NAW][MBW], const v4u (&B)[NAW][NBW]) {
         // by activation piece, so that only piece 0's LDS reads gate the first
-        // products (PREC 3: the first three entries are its products too)
+        // products (PREC 3 and 4: the first three entries)
         constexpr int TA[6] = {0, 1, 0, 2, 1, 0}, TB[6] = {0, 0, 1, 0, 1, 2};
 #pragma unroll
         for (int t = 0; t < NPROD; ++t)
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < NBW; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(v8bf, A[BX6 ? TA[t] : 0][mb]), __builtin_bit_cast(v8bf, B[BX6 ? TB[t] : 0][nb]),
-                        acc[mb][nb], 0, 0, 0);
+                for (int nb = 0; nb < NBW; ++nb) {
+                    if constexpr (H16)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(v8h, A[TA[t]][mb]), __builtin_bit_cast(v8h, B[TB[t]][nb]), acc[mb][nb],
+                            0, 0, 0);
+                    else
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(v8bf, A[BX6 ? TA[t] : 0][mb]),
+                            __builtin_bit_cast(v8bf, B[BX6 ? TB[t] : 0][nb]), acc[mb][nb], 0, 0, 0);
+                }
     };
 
     // The pipeline walks items (tile, chunk) with chunk fastest. Producers
@@ -331,17 +348,17 @@ conv_kernel(ConvArgs a) {
             // run of W 16-byte groups, already in the operand layout; the
             // memory unit copies it to LDS 1 KB per wave instruction, so the
             // producers issue no vector ALU work next to the matrix cores.
-            // (split products: kPieces planes per chunk instead of two parities)
-            constexpr int NPL = BX6 ? kPieces : 2;
+            // (split products: the pieces' planes per chunk instead of two parities)
+            constexpr int NPLI = BX6 ? NPL : 2;
             const int DS = BX6 ? PS6 : W;    // LDS plane stride (positions)
             const int pw = wave - 4;
             const int segs = (W + 63) >> 6;  // 64-position segments per plane
             // item c of tile t: chunks t.c0 + CPI c + cc, planes one after another
             auto dma = [&](const Tile& t, int c, float* dst) {
                 const float* src = a.x + (int64_t)t.b * a.x_bstride +
-                                   ((int64_t)(t.c0 + CPI * c) * NPL * a.pk_lp + kPkPadL + t.n_lo) * 4;
-                for (int q = pw; q < CPI * NPL * segs; q += 4) {
-                    const int hp = q / segs;  // plane within the item (chunk cc = hp / NPL)
+                                   ((int64_t)(t.c0 + CPI * c) * NPLI * a.pk_lp + kPkPadL + t.n_lo) * 4;
+                for (int q = pw; q < CPI * NPLI * segs; q += 4) {
+                    const int hp = q / segs;  // plane within the item (chunk cc = hp / NPLI)
                     const int pos0 = (q - hp * segs) * 64;
                     const int pos = pos0 + lane;
                     auto* ldst = (__attribute__((address_space(3))) void*)(dst + (hp * DS + pos0) * 4);
@@ -555,8 +572,8 @@ conv_kernel(ConvArgs a) {
             // item's pair u + 2 - NPI) loads while pair u multiplies
 #pragma unroll
             for (int u = 0; u < NPI; ++u) {
-                v4u(&use)[kPieces][MBW] = (u % 3 == 0) ? A6a : ((u % 3 == 1) ? A6b : A6c);
-                v4u(&fill)[kPieces][MBW] = ((u + 2) % 3 == 0) ? A6a : (((u + 2) % 3 == 1) ? A6b : A6c);
+                v4u(&use)[NAW][MBW] = (u % 3 == 0) ? A6a : ((u % 3 == 1) ? A6b : A6c);
+                v4u(&fill)[NAW][MBW] = ((u + 2) % 3 == 0) ? A6a : (((u + 2) % 3 == 1) ? A6b : A6c);
                 if (u + 2 < NPI) {
                     load_a6(fill, mb_base, cur.ph, q0 + u + 2);
                 } else {
@@ -564,10 +581,10 @@ conv_kernel(ConvArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 const int s0 = 2 * u, s1 = 2 * u + 1;
-                const int off0 = (s0 / TAPS) * kPieces * PS6 + (s0 % TAPS) * a.dil;
-                const int off1 = (s1 / TAPS) * kPieces * PS6 + (s1 % TAPS) * a.dil;
+                const int off0 = (s0 / TAPS) * NPL * PS6 + (s0 % TAPS) * a.dil;
+                const int off1 = (s1 / TAPS) * NPL * PS6 + (s1 % TAPS) * a.dil;
                 const float* bq = bb_0 + (hi ? off1 : off0) * 4;
-                v4u Bv[kPieces][NBW];
+                v4u Bv[NAW][NBW];
 #pragma unroll
                 for (int p = 0; p < NPA; ++p)
 #pragma unroll
@@ -579,7 +596,7 @@ conv_kernel(ConvArgs a) {
             // the next item's pairs 0 and 1 sit in slots NPI % 3, (NPI + 1) % 3
             if constexpr (NPI % 3 == 1) {
 #pragma unroll
-                for (int p = 0; p < kPieces; ++p)
+                for (int p = 0; p < NAW; ++p)
 #pragma unroll
                     for (int mb = 0; mb < MBW; ++mb) {
                         A6a[p][mb] = A6b[p][mb];
@@ -587,7 +604,7 @@ conv_kernel(ConvArgs a) {
                     }
             } else if constexpr (NPI % 3 == 2) {
 #pragma unroll
-                for (int p = 0; p < kPieces; ++p)
+                for (int p = 0; p < NAW; ++p)
 #pragma unroll
                     for (int mb = 0; mb < MBW; ++mb) {
                         const v4u t0 = A6c[p][mb];
@@ -669,6 +686,15 @@ conv_kernel(ConvArgs a) {
             }
         }
         if (cur_c == ipt - 1) {
+            if constexpr (H16) {
+                // the sums carry 2^e (the weights' scale): back to the output's scale (exact)
+#pragma unroll
+                for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[mb][nb][r] *= a.out_scale;
+            }
             if (a.ksplit > 1) {
                 // raw partial sums of this K range in MFMA fragment order:
                 // [wave][mb][nb][r][lane], so each register is one 256-byte
@@ -885,6 +911,22 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
             if (a.bx6) {
                 // split products: bf16 pieces, one phase, planes sized for kBx6MaxDil
                 if (!a.w6 || a.dil < 1) return hipErrorInvalidValue;
+                if (a.h16) {
+                    // two fp16 pieces, three products (AMP convs, conv_pre, transposed convs)
+                    if (a.bf16 || a.dil > kBx6MaxDil ||
+                        (((a.c_in + kChunk - 1) / kChunk) / a.ksplit) % bx6_cpi(NWG, a.taps, kBx6MaxDil, kPiecesH))
+                        return hipErrorInvalidValue;
+#define MH3A_TAPSH(T)                                                                                          \
+    if (a.taps == T)                                                                                          \
+        return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 4, T>, a, tiles,                        \
+                                 sizeof(float) * (size_t)conv_lds_floats6(NWG, T, kBx6MaxDil, kPiecesH), stream);
+                    MH3A_TAPSH(2)
+                    MH3A_TAPSH(3)
+                    MH3A_TAPSH(7)
+                    MH3A_TAPSH(11)
+#undef MH3A_TAPSH
+                    return hipErrorInvalidValue;
+                }
                 // whole items per K range
                 if ((((a.c_in + kChunk - 1) / kChunk) / a.ksplit) % bx6_cpi(NWG, a.taps)) return hipErrorInvalidValue;
                 if (a.dil > kBx6MaxDil) {

@@ -268,6 +268,38 @@ __device__ __forceinline__ void split3_pack8(const float (&v)[8], uint4 (&g)[3])
 #pragma unroll
     for (int p = 0; p < 3; ++p) g[p] = make_uint4(w[p][0], w[p][1], w[p][2], w[p][3]);
 }
+// The two fp16 pieces of 8 values as two 16-byte groups: g[0] = fp16(v),
+// g[1] = fp16(v - fp16(v)) (round to nearest even; the difference is exact
+// in fp32). v0 + v1 equals v to about 2^-22 relative for |v| >= 2^-3 and to
+// 2^-25 absolute below (the second piece is then subnormal); |v| must stay
+// below the fp16 range, 65504.
+__device__ __forceinline__ void split2h_pack8(const float (&v)[8], uint4 (&g)[2]) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    unsigned w[2][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const f2 x = {v[2 * k], v[2 * k + 1]};
+        const h2 p0 = __builtin_convertvector(x, h2);
+        const f2 back = __builtin_convertvector(p0, f2);
+        const f2 r = {x.x - back.x, x.y - back.y};
+        const h2 p1 = __builtin_convertvector(r, h2);
+        w[0][k] = __builtin_bit_cast(unsigned, p0);
+        w[1][k] = __builtin_bit_cast(unsigned, p1);
+    }
+    g[0] = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
+    g[1] = make_uint4(w[1][0], w[1][1], w[1][2], w[1][3]);
+}
+// Pieces of 8 values in form PC (kPieces: bf16 x 3; kPiecesH: fp16 x 2).
+template <int PC>
+__device__ __forceinline__ void split_pack8(const float (&v)[8], uint4 (&g)[PC]) {
+    if constexpr (PC == kPieces) {
+        split3_pack8(v, g);
+    } else {
+        static_assert(PC == kPiecesH, "piece forms: bf16 x 3 or fp16 x 2");
+        split2h_pack8(v, g);
+    }
+}
 // The three bf16 pieces of v (raw bits): v0 = bf16(v), v1 = bf16(v - v0),
 // v2 = bf16(v - v0 - v1); both differences are exact in fp32.
 __device__ __forceinline__ void split3_bf16(float v, unsigned& p0, unsigned& p1, unsigned& p2) {
@@ -289,8 +321,8 @@ __host__ __device__ constexpr int conv_lds_floats(int W, bool act) {
 // each), PS sized for the largest dilation so that plane offsets are
 // compile-time constants.
 __host__ __device__ constexpr int bx6_plane(int nwg, int taps, int dmax = kBx6MaxDil) { return nwg + (taps - 1) * dmax; }
-__host__ __device__ constexpr int conv_lds_floats6(int nwg, int taps, int dmax = kBx6MaxDil) {
-    return 2 * bx6_cpi(nwg, taps, dmax) * kPieces * bx6_plane(nwg, taps, dmax) * 4 + kTouchFloats;  // two item buffers
+__host__ __device__ constexpr int conv_lds_floats6(int nwg, int taps, int dmax = kBx6MaxDil, int planes = kPieces) {
+    return 2 * bx6_cpi(nwg, taps, dmax, planes) * planes * bx6_plane(nwg, taps, dmax) * 4 + kTouchFloats;  // two items
 }
 
 }  // namespace mh3a

@@ -144,6 +144,9 @@ struct ConvLayer {
     int64_t w6_off = -1;   // bf16 pieces for split products, or -1
     int64_t w6u_off = -1;  // bf16 pieces for the split-product unit kernel (<= 32 channels), or -1
     int64_t w6_phase_stride = 0;
+    int64_t wh_off = -1;   // fp16 pieces of the weights scaled by wh_scale (kPiecesH form), or -1
+    int64_t wh_phase_stride = 0;
+    float wh_scale = 1.0f; // 2^e
     int64_t w_phase_stride = 0;
     int64_t b_off = -1;
     int act = -1;       // index into acts, -1 = none
@@ -221,6 +224,7 @@ struct mh3a_decoder : mh3a_net {
     std::vector<int> stage_c;   // output channels per stage
     bool pk_ok = false;         // every AMP conv can read a packed activated input
     bool bx6_ok = false;        // ... and has split-product weights (see kPieces)
+    bool h16_ok = false;        // ... and fp16 weight pieces (see kPiecesH)
 };
 
 namespace {
@@ -267,7 +271,8 @@ int check_config(const mh3a_config* c) {
     if (c->filter_taps != kTaps) return fail(MH3A_E_CONFIG, "only %d-tap resampling filters are supported", kTaps);
     if (!(c->filter_cutoff > 0.0 && c->filter_cutoff < 0.5 && c->filter_half_width > 0.0))
         return fail(MH3A_E_CONFIG, "bad filter cutoff / half width");
-    if (c->matrix_form != MH3A_MATRIX_SPLIT && c->matrix_form != MH3A_MATRIX_FP32)
+    if (c->matrix_form != MH3A_MATRIX_SPLIT && c->matrix_form != MH3A_MATRIX_FP32 &&
+        c->matrix_form != MH3A_MATRIX_SPLIT_F16)
         return fail(MH3A_E_CONFIG, "unknown matrix_form %d", c->matrix_form);
     return MH3A_OK;
 }
@@ -401,10 +406,12 @@ int64_t plan_partial_floats(const ConvLayer& L, int positions, int groups, const
     return mh3a::plan_partial_floats(shape_of(L, fused), positions, groups, p);
 }
 
-// Whether packed AMP inputs take the split-product form (bf16 pieces and
-// six-way products on bf16 matrix cores, fp32-level accuracy; see kPieces):
-// the default matrix form, when every AMP conv has the weights for it.
-bool use_bx6(const mh3a_decoder* d) { return d->bx6_ok && d->cfg.matrix_form == MH3A_MATRIX_SPLIT; }
+// Whether packed AMP inputs take a split-product form (every matrix form but
+// fp32, when every AMP conv has the weights for it): bf16 pieces with six
+// products (kPieces), or, in the default form, fp16 pieces with three
+// (kPiecesH; use_h16).
+bool use_bx6(const mh3a_decoder* d) { return d->bx6_ok && d->cfg.matrix_form != MH3A_MATRIX_FP32; }
+bool use_h16(const mh3a_decoder* d) { return use_bx6(d) && d->h16_ok && d->cfg.matrix_form == MH3A_MATRIX_SPLIT_F16; }
 
 // Whether an AMP conv of a (batch, C, L) activation fuses its activation.
 // Fused, the producer waves compute it per tile on the SIMDs whose matrix
@@ -434,6 +441,8 @@ bool stage_px(const mh3a_decoder* d, int64_t batch, int c, int64_t len, bool bf1
 // Whether conv_pre / a transposed conv reads its input in the split-product
 // form (a split pass, then the packed path): layers packed for it at create.
 bool pre_bx6(const mh3a_decoder* d, const ConvLayer& L) { return use_bx6(d) && L.w6_off >= 0; }
+// ... and in the fp16 form
+bool pre_h16(const mh3a_decoder* d, const ConvLayer& L) { return pre_bx6(d, L) && use_h16(d) && L.wh_off >= 0; }
 
 // Plans are cached per launch shape.
 ConvPlan plan_conv(const mh3a_net* d, const ConvLayer& L, int positions, int batch, bool bf16, bool invariant,
@@ -495,13 +504,23 @@ struct TimedLaunch {
 hipError_t run_conv(const mh3a_net* d, const ConvLayer& L, const float* x, int64_t x_bstride, int l_in,
                     int positions, float* y, int64_t y_bstride, int batch, const float* res, const float* sum_in,
                     float scale, bool bf16, bool invariant, bool fused, float* partial, hipStream_t st,
-                    int pk_lp = 0, bool bx6 = false) {
+                    int pk_lp = 0, bool bx6 = false, bool h16 = false) {
     ConvArgs a;
     std::memset(&a, 0, sizeof a);
     a.pk_lp = pk_lp;
     a.bx6 = bx6 ? 1 : 0;
     a.w6 = L.w6_off >= 0 ? d->blob + L.w6_off : nullptr;
     a.w6_phase_stride = L.w6_phase_stride;
+    a.wscale = 1.0f;
+    a.out_scale = 1.0f;
+    if (h16) {
+        if (!bx6 || L.wh_off < 0) return hipErrorInvalidValue;
+        a.h16 = 1;
+        a.w6 = d->blob + L.wh_off;
+        a.w6_phase_stride = L.wh_phase_stride;
+        a.wscale = L.wh_scale;
+        a.out_scale = 1.0f / L.wh_scale;  // exact: a power of two
+    }
     a.x = x;
     a.x_bstride = x_bstride;
     a.c_in = L.c_in;
@@ -575,7 +594,7 @@ int64_t pk_item_floats(const mh3a_decoder* d, int c, int64_t len) {
 // The standalone activation of AMP layer `act_idx`: y = act(x), x (B, C, L)
 // rows, y packed.
 hipError_t run_act(const mh3a_decoder* d, int act_idx, const float* x, float* y, int batch, int c, int64_t len,
-                   bool pieces, hipStream_t st) {
+                   int pieces, hipStream_t st) {
     ActArgs a;
     a.x = x;
     a.x_bstride = (int64_t)c * len;
@@ -584,7 +603,7 @@ hipError_t run_act(const mh3a_decoder* d, int act_idx, const float* x, float* y,
     a.c = c;
     a.l = (int)len;
     a.lp = (int)pk_lp(len);
-    a.pieces = pieces ? kPieces : 0;
+    a.pieces = pieces;
     a.act = act_params(d, act_idx);
     TimedLaunch tl(d, st, KIND_AMP_ACT);
     hipError_t e = launch_act(a, batch, st);
@@ -596,7 +615,8 @@ hipError_t run_act(const mh3a_decoder* d, int act_idx, const float* x, float* y,
 
 // The split pass of a conv input: x (B, c, len) rows -> y in the packed
 // split-product form.
-hipError_t run_split(const mh3a_decoder* d, const float* x, float* y, int batch, int c, int64_t len, hipStream_t st) {
+hipError_t run_split(const mh3a_decoder* d, const float* x, float* y, int batch, int c, int64_t len, int pieces,
+                     hipStream_t st) {
     ActArgs a;
     std::memset(&a, 0, sizeof a);
     a.x = x;
@@ -606,11 +626,11 @@ hipError_t run_split(const mh3a_decoder* d, const float* x, float* y, int batch,
     a.c = c;
     a.l = (int)len;
     a.lp = (int)pk_lp(len);
-    a.pieces = kPieces;
+    a.pieces = pieces;
     TimedLaunch tl(d, st, KIND_SPLIT);
     hipError_t e = launch_split(a, batch, st);
     const double n = (double)batch * c * len;
-    tl.done(KIND_SPLIT, 0.0, 10.0 * n);  // 4 bytes in, 6 out
+    tl.done(KIND_SPLIT, 0.0, (4.0 + 2.0 * pieces) * n);  // 4 bytes in, 2 per piece out
     return e;
 }
 
@@ -695,7 +715,9 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, floa
     const bool fused = amp_act_fused(d, batch, C, len);
     const int64_t pbs = pk_item_floats(d, C, len);  // packed batch stride
     const int plp = fused ? 0 : (int)pk_lp(len);
-    const bool px = stage_px(d, batch, C, len, bf16);  // packed inputs in the split-product form
+    const bool px = stage_px(d, batch, C, len, bf16);  // packed inputs in a split-product form
+    const bool h16 = px && use_h16(d) && !bf16;         // ... the fp16 one (the bf16 flag keeps bf16 pieces)
+    const int pieces = px ? (h16 ? kPiecesH : kPieces) : 0;
     for (int j = 0; j < nrb; ++j) {
         for (int n = 0; n < nd; ++n) {
             const ConvLayer& c1 = d->amp[stage][(j * nd + n) * 2 + 0];
@@ -703,14 +725,14 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, floa
             const float* xin = (n == 0) ? h : x_buf;
             const float* in1 = xin;
             if (!fused) {
-                HIP_TRY(run_act(d, c1.act, xin, a_buf, batch, C, len, px, st));
+                HIP_TRY(run_act(d, c1.act, xin, a_buf, batch, C, len, pieces, st));
                 in1 = a_buf;
             }
             HIP_TRY(run_conv(d, c1, in1, fused ? bs : pbs, L, L, t_buf, bs, batch, nullptr, nullptr, 1.0f, bf16,
-                             invariant, fused, partial, st, plp, px));
+                             invariant, fused, partial, st, plp, px, h16));
             const float* in2 = t_buf;
             if (!fused) {
-                HIP_TRY(run_act(d, c2.act, t_buf, a_buf, batch, C, len, px, st));
+                HIP_TRY(run_act(d, c2.act, t_buf, a_buf, batch, C, len, pieces, st));
                 in2 = a_buf;
             }
             const bool last = (n == nd - 1);
@@ -718,7 +740,7 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, floa
             const float* sum_in = (last && j > 0) ? s_buf : nullptr;
             const float scale = (last && j == nrb - 1) ? 1.0f / (float)nrb : 1.0f;
             HIP_TRY(run_conv(d, c2, in2, fused ? bs : pbs, L, L, yout, bs, batch, xin, sum_in, scale, bf16, invariant,
-                             fused, partial, st, plp, px));
+                             fused, partial, st, plp, px, h16));
         }
     }
     return MH3A_OK;
@@ -831,10 +853,11 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
                      true, partial, st));
     if (upto == 0) return finish(bufX, (int64_t)B * c.latent_dim * N);
     if (pre_bx6(d, d->conv_pre)) {
-        HIP_TRY(run_split(d, bufX, bufA, B, c.latent_dim, N, st));
+        const bool h16 = pre_h16(d, d->conv_pre);
+        HIP_TRY(run_split(d, bufX, bufA, B, c.latent_dim, N, h16 ? kPiecesH : kPieces, st));
         HIP_TRY(run_conv(d, d->conv_pre, bufA, pk_item_floats(d, c.latent_dim, N), N, N, bufS,
                          (int64_t)c.decoder_dim * N, B, nullptr, nullptr, 1.0f, false, invariant, true, partial, st,
-                         (int)pk_lp(N), true));
+                         (int)pk_lp(N), true, h16));
     } else {
         HIP_TRY(run_conv(d, d->conv_pre, bufX, (int64_t)c.latent_dim * N, N, N, bufS, (int64_t)c.decoder_dim * N, B,
                          nullptr, nullptr, 1.0f, false, invariant, true, partial, st));
@@ -846,10 +869,11 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
         const int C = d->stage_c[s];
         const int64_t lout = len * c.rates[s];
         if (pre_bx6(d, d->ups[s])) {
-            HIP_TRY(run_split(d, bufS, bufA, B, cin, len, st));
+            const bool h16 = pre_h16(d, d->ups[s]);
+            HIP_TRY(run_split(d, bufS, bufA, B, cin, len, h16 ? kPiecesH : kPieces, st));
             HIP_TRY(run_conv(d, d->ups[s], bufA, pk_item_floats(d, cin, len), (int)len, (int)len, bufH,
                              (int64_t)C * lout, B, nullptr, nullptr, 1.0f, false, invariant, true, partial, st,
-                             (int)pk_lp(len), true));
+                             (int)pk_lp(len), true, h16));
         } else {
             HIP_TRY(run_conv(d, d->ups[s], bufS, (int64_t)cin * len, (int)len, (int)len, bufH, (int64_t)C * lout, B,
                              nullptr, nullptr, 1.0f, false, invariant, true, partial, st));
@@ -1128,6 +1152,59 @@ void pack_conv_weights6(const float* w, int c_out, int c_in, int taps, float* ou
             }
 }
 
+// fp16 pieces of a layer's weights for v_mfma_f32_32x32x16_f16 (see
+// kPiecesH): w' = w 2^e with e chosen so that max |w'| lies in [2^14, 2^15),
+// w0 = fp16(w'), w1 = fp16(w' - w0), both rounded to nearest even; the
+// operand order of pack_conv_weights6 with two pieces.
+int weight_exponent_h(const float* w, int64_t n) {
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; ++i) m = std::max(m, std::fabs(w[i]));
+    if (!(m > 0.0f) || !std::isfinite(m)) return 0;
+    int k = 0;
+    std::frexp(m, &k);  // m = f 2^k, f in [0.5, 1)
+    return std::min(100, std::max(-100, 15 - k));
+}
+
+int64_t packed_weight_floats_h(int c_out, int c_in, int taps) {
+    const int64_t nmb = (c_out + 31) / 32, nch = (c_in + kChunk - 1) / kChunk, np = (nch * taps + 1) / 2;
+    return nmb * np * kPiecesH * 64 * 4;
+}
+
+static uint16_t f16_bits(float v) {
+    const _Float16 h = (_Float16)v;
+    uint16_t b;
+    std::memcpy(&b, &h, 2);
+    return b;
+}
+static float f16_value(uint16_t b) {
+    _Float16 h;
+    std::memcpy(&h, &b, 2);
+    return (float)h;
+}
+
+void pack_conv_weights_h(const float* w, int c_out, int c_in, int taps, int e, float* out) {
+    const int nmb = (c_out + 31) / 32, nch = (c_in + kChunk - 1) / kChunk, np = (nch * taps + 1) / 2;
+    uint32_t* o = reinterpret_cast<uint32_t*>(out);
+    for (int mb = 0; mb < nmb; ++mb)
+        for (int q = 0; q < np; ++q)
+            for (int l = 0; l < 64; ++l) {
+                const int slot = 2 * q + (l >> 5), ch = slot / taps, j = slot % taps;
+                uint16_t pc[kPiecesH][kChunk];
+                for (int i = 0; i < kChunk; ++i) {
+                    const int m = mb * 32 + (l & 31), c = ch * kChunk + i;
+                    const float v = (m < c_out && ch < nch && c < c_in)
+                                        ? std::ldexp(w[((int64_t)m * c_in + c) * taps + j], e) : 0.0f;
+                    const uint16_t p0 = f16_bits(v);
+                    pc[0][i] = p0;
+                    pc[1][i] = f16_bits(v - f16_value(p0));
+                }
+                for (int p = 0; p < kPiecesH; ++p) {
+                    uint32_t* g = o + ((((int64_t)mb * np + q) * kPiecesH + p) * 64 + l) * 4;
+                    for (int k = 0; k < 4; ++k) g[k] = (uint32_t)pc[p][2 * k] | ((uint32_t)pc[p][2 * k + 1] << 16);
+                }
+            }
+}
+
 // Split-product weights of the unit kernel (v_mfma_f32_16x16x32_bf16): for
 // 16-row block mb, K-step ks, piece p and lane l, the 8 bf16 values
 // piece_p(W[mb*16 + l%16, cb*8 + i, ks*TG + tsub]), i = 0..7, where the
@@ -1199,6 +1276,7 @@ void mh3a_config_default(mh3a_config* c) {
     c->filter_taps = 12;
     c->filter_cutoff = 0.25;
     c->filter_half_width = 0.3;
+    c->matrix_form = MH3A_MATRIX_SPLIT_F16;
 }
 
 const char* mh3a_last_error(void) { return g_err.c_str(); }
@@ -1278,6 +1356,12 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
     if (split_input_ok(d->conv_pre)) {
         d->conv_pre.w6_off = blob.reserve(packed_weight_floats6(c.decoder_dim, c.latent_dim, 7));
         pack_conv_weights6(w.data(), c.decoder_dim, c.latent_dim, 7, blob.h.data() + d->conv_pre.w6_off);
+        if (c.matrix_form == MH3A_MATRIX_SPLIT_F16) {
+            const int e = weight_exponent_h(w.data(), (int64_t)w.size());
+            d->conv_pre.wh_off = blob.reserve(packed_weight_floats_h(c.decoder_dim, c.latent_dim, 7));
+            d->conv_pre.wh_scale = std::ldexp(1.0f, e);
+            pack_conv_weights_h(w.data(), c.decoder_dim, c.latent_dim, 7, e, blob.h.data() + d->conv_pre.wh_off);
+        }
     }
 
     int cin = c.decoder_dim;
@@ -1316,6 +1400,14 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
             U.w6_off = blob.reserve(per6 * r);
             U.w6_phase_stride = per6;
         }
+        const bool splith = split6 && c.matrix_form == MH3A_MATRIX_SPLIT_F16;
+        const int64_t perh = splith ? packed_weight_floats_h(C, cin, ku) : 0;
+        const int eh = splith ? weight_exponent_h(w.data(), (int64_t)w.size()) : 0;  // one exponent for every phase
+        if (splith) {
+            U.wh_off = blob.reserve(perh * r);
+            U.wh_phase_stride = perh;
+            U.wh_scale = std::ldexp(1.0f, eh);
+        }
         std::vector<float> wph((size_t)C * cin * ku);
         for (int ph = 0; ph < r; ++ph) {
             const int q0 = (ph + pad) % r;
@@ -1327,6 +1419,7 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
                     }
             pack_conv_weights(wph.data(), C, cin, ku, blob.h.data() + U.w_off + ph * per);
             if (split6) pack_conv_weights6(wph.data(), C, cin, ku, blob.h.data() + U.w6_off + ph * per6);
+            if (splith) pack_conv_weights_h(wph.data(), C, cin, ku, eh, blob.h.data() + U.wh_off + ph * perh);
         }
         U.b_off = blob.add(bias, C);
         // AMP blocks
@@ -1344,6 +1437,12 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
                     if (kk == 3 || kk == 7 || kk == 11) {
                         L.w6_off = blob.reserve(packed_weight_floats6(C, C, kk));
                         pack_conv_weights6(w.data(), C, C, kk, blob.h.data() + L.w6_off);
+                        if (c.matrix_form == MH3A_MATRIX_SPLIT_F16) {
+                            const int e = weight_exponent_h(w.data(), (int64_t)w.size());
+                            L.wh_off = blob.reserve(packed_weight_floats_h(C, C, kk));
+                            L.wh_scale = std::ldexp(1.0f, e);
+                            pack_conv_weights_h(w.data(), C, C, kk, e, blob.h.data() + L.wh_off);
+                        }
                     }
                     if (C <= 32 && C % 8 == 0 && (kk == 3 || kk == 7 || kk == 11)) {
                         L.w6u_off = blob.reserve(unit_weight_floats6(C, kk));
@@ -1391,6 +1490,11 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
     for (const auto& stage_layers : d->amp)
         for (const ConvLayer& L : stage_layers)
             if (L.w6_off < 0 || L.dil > kBx6MaxDil) d->bx6_ok = false;
+    // the fp16 form needs the pieces of every AMP conv of the split-product stages
+    d->h16_ok = d->bx6_ok && c.matrix_form == MH3A_MATRIX_SPLIT_F16;
+    for (const auto& stage_layers : d->amp)
+        for (const ConvLayer& L : stage_layers)
+            if (L.w6_off >= 0 && L.wh_off < 0) d->h16_ok = false;
 
     // upload
     int ndev = 0;
@@ -1633,7 +1737,7 @@ int enc_check_config(const mh3a_encoder_config* c) {
     }
     if (hop > 65536 || dim > 65536) return fail(MH3A_E_CONFIG, "encoder hop or width too large");
     if (c->matrix_form != MH3A_MATRIX_SPLIT && c->matrix_form != MH3A_MATRIX_FP32)
-        return fail(MH3A_E_CONFIG, "unknown matrix_form %d", c->matrix_form);
+        return fail(MH3A_E_CONFIG, "matrix_form %d: the encoder has the bf16 split and fp32 forms", c->matrix_form);
     if (c->latent_channels < 1 || c->num_attention_heads < 1)
         return fail(MH3A_E_CONFIG, "latent_channels and num_attention_heads must be positive");
     return MH3A_OK;

@@ -59,6 +59,10 @@ struct ConvArgs {
     float* partial;       // ksplit * tiles * tile_m * tile_n floats of raw sums
     int pk_lp;            // packed input (see below): padded row length; 0 = plain rows
     int bx6;              // packed input holds bf16 pieces; products split six ways (see below)
+    int h16;              // (with bx6) the two-piece fp16 form instead (see kPiecesH); w6 then
+                          // holds the fp16 weight pieces scaled by wscale = 2^e
+    float wscale;         // 2^e (h16), applied to the bias the sums start from
+    float out_scale;      // 2^-e (h16), applied to the sums
 };
 
 // Packed activated input of an AMP conv, written by the standalone
@@ -81,6 +85,15 @@ constexpr int kPkPadR = 288;
 // fp32 accumulation, which keeps fp32-level accuracy (the dropped products
 // are about 2^-27 of w x).
 constexpr int kPieces = 3;
+// Two-piece fp16 form: v0 = fp16(v), v1 = fp16(v - v0), so v0 + v1 equals v
+// to about 2^-22 relative (|v| >= 2^-3; 2^-25 absolute below), |v| < 65504.
+// Per item [chunk][piece][lp][8 fp16], the padding as above. With the
+// weights split the same way after scaling by 2^e (e per layer, so that the
+// largest |w| 2^e lies in [2^14, 2^15): no weight piece overflows and every
+// weight's second piece stays in the normal range), a conv sums the three
+// products w0 x0, w0 x1, w1 x0 on fp16 matrix cores with fp32 accumulation
+// and scales the sums by 2^-e; the dropped w1 x1 is about 2^-22 of w x.
+constexpr int kPiecesH = 2;
 // Largest dilation the split-product conv has LDS planes for.
 constexpr int kBx6MaxDil = 5;
 // Dilation bound of the wider-plane instances (7 taps; the encoder's units).
@@ -90,9 +103,9 @@ constexpr int kBx6WideDil = 9;
 // per barrier), halved until the two item buffers fit 156 KB of LDS
 // (256-wide tiles). Measured against two chunks per item for
 // 3+ taps: about 1% faster. The chunks of a K range must be a multiple of it.
-constexpr int bx6_cpi(int nwg, int taps, int dmax = kBx6MaxDil) {
+constexpr int bx6_cpi(int nwg, int taps, int dmax = kBx6MaxDil, int planes = kPieces) {
     int c = taps <= 7 ? 8 : 4;
-    while (c > 2 && 2 * c * kPieces * (nwg + (taps - 1) * dmax) * 16 > 156 * 1024) c /= 2;
+    while (c > 2 && 2 * c * planes * (nwg + (taps - 1) * dmax) * 16 > 156 * 1024) c /= 2;
     return c;
 }
 // The largest item any tile uses for a tap count (eligibility: whole items).
@@ -190,12 +203,12 @@ struct ActArgs {
     int c;
     int l;
     int lp;
-    int pieces;         // 0: fp32 packed layout; kPieces: bf16 pieces (split-product form)
+    int pieces;         // 0: fp32 packed layout; kPieces: bf16 pieces; kPiecesH: fp16 pieces
     ActParams act;
 };
 hipError_t launch_act(const ActArgs& a, int batch, hipStream_t stream);
 // The same layout without the activation: y = x in the split-product form
-// (a.act unused, a.pieces must be kPieces).
+// (a.act unused, a.pieces kPieces or kPiecesH).
 hipError_t launch_split(const ActArgs& a, int batch, hipStream_t stream);
 
 // One AMP residual unit in one launch, for narrow stages:

@@ -144,7 +144,9 @@ __global__ void __launch_bounds__(256) final_kernel(FinalArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kActT = 256;
 
-template <int W, bool PIECES>
+// PC: 0 writes the fp32 packed layout (two channel-parity planes); kPieces /
+// kPiecesH the split-product forms (bf16 x 3 / fp16 x 2 planes).
+template <int W, int PC>
 __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
     constexpr int CI = kChunk;
     // each channel's result row reuses its x row (dead after the up pass)
@@ -156,7 +158,7 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
     const int chunk = blockIdx.y;
     const int b = blockIdx.z;
     const int ci = threadIdx.x >> 5, lane32 = threadIdx.x & 31;
-    constexpr int NPL = PIECES ? kPieces : 2;  // planes per chunk: pieces, or channel parities
+    constexpr int NPL = PC ? PC : 2;  // planes per chunk: pieces, or channel parities
     float* yc = a.y + (int64_t)b * a.y_bstride + (int64_t)chunk * NPL * a.lp * 4;
     if (t0 >= a.l || t0 + W <= 0) {
         // all padding
@@ -171,7 +173,7 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
     constexpr int XS = act_xs_len(W);
     stage_act<CI, W>(as, xs, ss, a.x + (int64_t)b * a.x_bstride, chunk * CI, a.c, a.l, t0, f, a.act.ab, ci, lane32, XS);
     __syncthreads();
-    if constexpr (PIECES) {
+    if constexpr (PC != 0) {
         // one position per thread: the 8 channels' pieces, 16 bytes per plane
         for (int w = threadIdx.x; w < W; w += 256) {
             const int q = t0 + kPkPadL + w;
@@ -180,10 +182,10 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
             float v8[8];
 #pragma unroll
             for (int c = 0; c < CI; ++c) v8[c] = as[c * XS + w];
-            uint4 g[kPieces];
-            split3_pack8(v8, g);
+            uint4 g[PC];
+            split_pack8<PC>(v8, g);
 #pragma unroll
-            for (int p = 0; p < kPieces; ++p) *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = g[p];
+            for (int p = 0; p < PC; ++p) *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = g[p];
         }
         return;
     }
@@ -200,11 +202,14 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
 hipError_t launch_act(const ActArgs& a, int batch, hipStream_t stream) {
     if (a.c < 1 || a.l < 1 || batch < 1 || !a.act.taps || a.lp != a.l + kPkPadL + kPkPadR) return hipErrorInvalidValue;
     dim3 grid((a.lp + kActT - 1) / kActT, (a.c + kChunk - 1) / kChunk, batch);
-    if (a.pieces != 0 && a.pieces != kPieces) return hipErrorInvalidValue;
-    if (a.pieces)
-        hipLaunchKernelGGL((act_kernel<kActT, true>), grid, dim3(256), 0, stream, a);
+    if (a.pieces == kPieces)
+        hipLaunchKernelGGL((act_kernel<kActT, kPieces>), grid, dim3(256), 0, stream, a);
+    else if (a.pieces == kPiecesH)
+        hipLaunchKernelGGL((act_kernel<kActT, kPiecesH>), grid, dim3(256), 0, stream, a);
+    else if (a.pieces == 0)
+        hipLaunchKernelGGL((act_kernel<kActT, 0>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((act_kernel<kActT, false>), grid, dim3(256), 0, stream, a);
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -689,9 +694,11 @@ hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-// x (B, c, l) rows -> the split-product packed layout (kPieces planes per
-// chunk of 8 channels, zero pads): one padded position per thread, the 8
-// channels' pieces written as three 16-byte groups.
+// x (B, c, l) rows -> a split-product packed layout (PC planes per chunk of
+// 8 channels, zero pads; PC = kPieces bf16 or kPiecesH fp16 pieces): one
+// padded position per thread, the 8 channels' pieces written as PC 16-byte
+// groups.
+template <int PC>
 __global__ void __launch_bounds__(256) split_kernel(ActArgs a) {
     const int q = blockIdx.x * 256 + threadIdx.x;  // index in the padded row
     const int chunk = blockIdx.y, b = blockIdx.z;
@@ -705,18 +712,22 @@ __global__ void __launch_bounds__(256) split_kernel(ActArgs a) {
         const int ch = chunk * kChunk + i;
         v8[i] = (in && ch < a.c) ? xb[(int64_t)ch * a.l + n] : 0.0f;
     }
-    uint4 g[kPieces];
-    split3_pack8(v8, g);
-    float* yc = a.y + (int64_t)b * a.y_bstride + (int64_t)chunk * kPieces * a.lp * 4;
+    uint4 g[PC];
+    split_pack8<PC>(v8, g);
+    float* yc = a.y + (int64_t)b * a.y_bstride + (int64_t)chunk * PC * a.lp * 4;
 #pragma unroll
-    for (int p = 0; p < kPieces; ++p) *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = g[p];
+    for (int p = 0; p < PC; ++p) *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = g[p];
 }
 
 hipError_t launch_split(const ActArgs& a, int batch, hipStream_t stream) {
-    if (a.c < 1 || a.l < 1 || batch < 1 || batch > 65535 || a.pieces != kPieces || a.lp != a.l + kPkPadL + kPkPadR)
-        return hipErrorInvalidValue;
+    if (a.c < 1 || a.l < 1 || batch < 1 || batch > 65535 || a.lp != a.l + kPkPadL + kPkPadR) return hipErrorInvalidValue;
     dim3 grid((a.lp + 255) / 256, (a.c + kChunk - 1) / kChunk, batch);
-    hipLaunchKernelGGL(split_kernel, grid, dim3(256), 0, stream, a);
+    if (a.pieces == kPieces)
+        hipLaunchKernelGGL(split_kernel<kPieces>, grid, dim3(256), 0, stream, a);
+    else if (a.pieces == kPiecesH)
+        hipLaunchKernelGGL(split_kernel<kPiecesH>, grid, dim3(256), 0, stream, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -443,24 +443,33 @@ def test_chunked_decode_argument_errors(default_decoder, dev):
 
 
 # ---------------------------------------------------------------------------
-# fp32 matrix-core forms (matrix_form = MH3A_MATRIX_FP32, fixed at create)
+# The other matrix-core forms (matrix_form fixed at create): fp32 matrix
+# cores throughout, and bf16 pieces with six products; the default (fp16
+# pieces, three products) runs everywhere else in this file.
 # ---------------------------------------------------------------------------
 
-def test_fp32_matrix_core_forms(default_params, dev):
-    # The fp32 forms (packed fp32 input at 512 channels, fused activation at
-    # 256 on this short signal, fp32 unit kernel, plain-row conv_pre and
-    # transposed convs): a decoder created with matrix_form = fp32.
+@pytest.mark.parametrize("form", ["fp32", "bf16x6"])
+def test_other_matrix_core_forms(default_params, dev, form):
+    # fp32: packed fp32 input at 512 channels, fused activation at 256 on
+    # this short signal, fp32 unit kernel, plain-row conv_pre and transposed
+    # convs; bf16x6: the split-product convs on three bf16 pieces
     from neural_audio_vae_amd import Decoder, _lib
-    print("[case] fp32 matrix-core forms (matrix_form = MH3A_MATRIX_FP32)", flush=True)
-    d = Decoder(default_params, {"matrix_form": _lib.MH3A_MATRIX_FP32})
+    mf = {"fp32": _lib.MH3A_MATRIX_FP32, "bf16x6": _lib.MH3A_MATRIX_SPLIT}[form]
+    print(f"[case] matrix form {form} (matrix_form = {mf})", flush=True)
+    d = Decoder(default_params, {"matrix_form": mf})
     z, y, _ = c1_oracle_stages()
     got = host(d.decode(gpu(z, dev), flags=NO_CLAMP))
-    assert_close("fp32 forms c1 decode", got[0], y)
+    assert_close(f"{form} form c1 decode", got[0], y)
     for stage, c in ((0, 512), (1, 256), (4, 32)):
         x = synth.make_signal((1, c, 3000), seed=stage)
         out = host(d.amp_stage(stage, gpu(x, dev)))
         ref = O.stage_amp(x[0][:, 1380:1684], default_params, stage)[:, 120:184]  # 120 samples of margin
-        assert_close(f"fp32 forms stage {stage} [1500,1564)", out[0][:, 1500:1564], ref)
+        assert_close(f"{form} form stage {stage} [1500,1564)", out[0][:, 1500:1564], ref)
+    if form == "bf16x6":
+        z3 = synth.make_latents(2, 1200)
+        windows = [(0, 600, 603), (1, 1198, 1200)]
+        got = host(d.decode(gpu(z3, dev), flags=NO_CLAMP))
+        check_windows("bf16x6 form c3", got, oracle_windows(default_params, z3, windows), windows)
     d.close()
 
 
