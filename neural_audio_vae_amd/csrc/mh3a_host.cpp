@@ -145,6 +145,7 @@ struct ConvLayer {
     int64_t w6u_off = -1;  // bf16 pieces for the split-product unit kernel (<= 32 channels), or -1
     int64_t w6_phase_stride = 0;
     int64_t wh_off = -1;   // fp16 pieces of the weights scaled by wh_scale (kPiecesH form), or -1
+    int64_t whu_off = -1;  // the same in the unit kernel's order (<= 32 channels), or -1
     int64_t wh_phase_stride = 0;
     float wh_scale = 1.0f; // 2^e
     int64_t w_phase_stride = 0;
@@ -668,6 +669,10 @@ int run_amp_units(const mh3a_decoder* d, int stage, const float* h, float* x_buf
     const int C = d->stage_c[stage];
     const int nrb = c.num_resblocks, nd = c.num_dilations;
     const bool split = amp_unit_split(d, stage);
+    // fp16 pieces in the default matrix form (the bf16 flag keeps bf16 pieces)
+    bool h16 = split && !bf16 && d->cfg.matrix_form == MH3A_MATRIX_SPLIT_F16;
+    for (const ConvLayer& L : d->amp[stage])
+        if (L.whu_off < 0) h16 = false;
     for (int j = 0; j < nrb; ++j) {
         const float* xin = h;
         for (int n = 0; n < nd; ++n) {
@@ -684,11 +689,13 @@ int run_amp_units(const mh3a_decoder* d, int stage, const float* h, float* x_buf
             u.l = (int)len;
             u.taps = c1.taps;
             u.dil = c1.dil;
-            u.split = split ? (bf16 ? 3 : 6) : 0;
-            u.w1 = d->blob + (split ? c1.w6u_off : c1.w16_off);
+            u.split = split ? (h16 ? 2 : (bf16 ? 3 : 6)) : 0;
+            u.w1 = d->blob + (h16 ? c1.whu_off : (split ? c1.w6u_off : c1.w16_off));
             u.b1 = d->blob + c1.b_off;
             u.act1 = act_params(d, c1.act);
-            u.w2 = d->blob + (split ? c2.w6u_off : c2.w16_off);
+            u.w2 = d->blob + (h16 ? c2.whu_off : (split ? c2.w6u_off : c2.w16_off));
+            u.wscale1 = h16 ? c1.wh_scale : 1.0f;
+            u.wscale2 = h16 ? c2.wh_scale : 1.0f;
             u.b2 = d->blob + c2.b_off;
             u.act2 = act_params(d, c2.act);
             if (c2.taps != c1.taps || c2.dil != 1) return fail(MH3A_E_INVALID_ARG, "unit convs disagree");
@@ -1242,6 +1249,36 @@ void pack_unit_weights6(const float* w, int c, int taps, float* out) {
             }
 }
 
+// The same operand order with two fp16 pieces of w 2^e (see
+// pack_conv_weights_h).
+int64_t unit_weight_floats_h(int c, int taps) {
+    const int cb = c / 8, tg = 4 / cb, ks = (taps + tg - 1) / tg, nmb = (c + 15) / 16;
+    return (int64_t)nmb * ks * kPiecesH * 64 * 4;
+}
+
+void pack_unit_weights_h(const float* w, int c, int taps, int e, float* out) {
+    const int CB = c / 8, TG = 4 / CB, KS = (taps + TG - 1) / TG, nmb = (c + 15) / 16;
+    uint32_t* o = reinterpret_cast<uint32_t*>(out);
+    for (int mb = 0; mb < nmb; ++mb)
+        for (int ks = 0; ks < KS; ++ks)
+            for (int l = 0; l < 64; ++l) {
+                const int g4 = l >> 4, cb = g4 % CB, tsub = g4 / CB, m = mb * 16 + (l & 15), j = ks * TG + tsub;
+                uint16_t pc[kPiecesH][8];
+                for (int i = 0; i < 8; ++i) {
+                    const int ci = cb * 8 + i;
+                    const float v =
+                        (m < c && ci < c && j < taps) ? std::ldexp(w[((int64_t)m * c + ci) * taps + j], e) : 0.0f;
+                    const uint16_t p0 = f16_bits(v);
+                    pc[0][i] = p0;
+                    pc[1][i] = f16_bits(v - f16_value(p0));
+                }
+                for (int p = 0; p < kPiecesH; ++p) {
+                    uint32_t* g = o + ((((int64_t)mb * KS + ks) * kPiecesH + p) * 64 + l) * 4;
+                    for (int k = 0; k < 4; ++k) g[k] = (uint32_t)pc[p][2 * k] | ((uint32_t)pc[p][2 * k + 1] << 16);
+                }
+            }
+}
+
 }  // namespace mh3a
 
 // ===========================================================================
@@ -1447,6 +1484,12 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
                     if (C <= 32 && C % 8 == 0 && (kk == 3 || kk == 7 || kk == 11)) {
                         L.w6u_off = blob.reserve(unit_weight_floats6(C, kk));
                         pack_unit_weights6(w.data(), C, kk, blob.h.data() + L.w6u_off);
+                        if (c.matrix_form == MH3A_MATRIX_SPLIT_F16) {
+                            const int e = weight_exponent_h(w.data(), (int64_t)w.size());
+                            L.whu_off = blob.reserve(unit_weight_floats_h(C, kk));
+                            L.wh_scale = std::ldexp(1.0f, e);
+                            pack_unit_weights_h(w.data(), C, kk, e, blob.h.data() + L.whu_off);
+                        }
                     }
                     if (C <= 32 && (kk == 3 || kk == 7 || kk == 11)) {
                         L.w16_off = blob.reserve(packed_weight_floats16(C, C, kk));

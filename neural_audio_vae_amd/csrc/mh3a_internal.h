@@ -231,7 +231,9 @@ struct UnitArgs {
     const float* b2;
     ActParams act2;
     int split;            // 0: fp32 matrix cores; 6 / 3: w1, w2 in the split-product unit order
-                          // (pack_unit_weights6), six / three piece products on bf16 matrix cores
+                          // (pack_unit_weights6), six / three piece products on bf16 matrix cores;
+                          // 2: fp16 pieces (pack_unit_weights_h), three products on fp16 matrix cores
+    float wscale1, wscale2;  // (split 2) the 2^e each conv's weights were scaled by
 };
 // Shapes the unit kernel has instances for: c in {8, 16, 32}, taps in
 // {3, 7, 11}, 1 <= dil <= kUnitMaxDil.
@@ -241,6 +243,9 @@ hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream);
 // Unit-kernel weights as bf16 pieces for v_mfma_f32_16x16x32_bf16.
 int64_t unit_weight_floats6(int c, int taps);
 void pack_unit_weights6(const float* w, int c, int taps, float* out);
+// ... and as fp16 pieces of w 2^e for v_mfma_f32_16x16x32_f16 (kPiecesH).
+int64_t unit_weight_floats_h(int c, int taps);
+void pack_unit_weights_h(const float* w, int c, int taps, int e, float* out);
 
 // Encoder Snake: y = snake(x) regrouped space-to-depth by s (s = 1: plain):
 // output channel c * s + r at position t is snake(x[c, t * s + r - shift]),

@@ -457,8 +457,9 @@ struct Unit6Geom {
 };
 
 // fp32 rows (stride rs) of n positions -> pieces (16-byte group per
-// position and channel block, planes of WP positions)
-template <int C, int WP>
+// position and channel block, planes of WP positions; NPC = kPieces bf16 or
+// kPiecesH fp16 pieces)
+template <int C, int WP, int NPC>
 __device__ __forceinline__ void unit_pack6(const float* rows, int rs, int n, uint4* pc) {
     constexpr int CB = C / 8;
     for (int idx = threadIdx.x; idx < n * CB; idx += 256) {
@@ -466,38 +467,47 @@ __device__ __forceinline__ void unit_pack6(const float* rows, int rs, int n, uin
         float v8[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) v8[i] = rows[(cb * 8 + i) * rs + w];
-        uint4 g[kPieces];
-        split3_pack8(v8, g);
+        uint4 g[NPC];
+        split_pack8<NPC>(v8, g);
 #pragma unroll
-        for (int p = 0; p < kPieces; ++p) pc[p * WP * CB + idx] = g[p];
+        for (int p = 0; p < NPC; ++p) pc[p * WP * CB + idx] = g[p];
     }
 }
 
-// out[co][n] = bias[co] + sum W[co][ci][j] A[ci][n + j dil], A as pieces
-template <int C, int K, int WP, int NOUT, int NPROD, typename Pre, typename Epi>
+// out[co][n] = bias[co] + sum W[co][ci][j] A[ci][n + j dil], A as pieces.
+// PF: 6 = bf16 pieces, six products; 3 = bf16 pieces, three; 2 = fp16
+// pieces, three, the weights scaled by wscale (2^e) and the sums by its
+// inverse before epi.
+template <int C, int K, int WP, int NOUT, int PF, typename Pre, typename Epi>
 __device__ __forceinline__ void unit_conv6(const uint4* __restrict__ pc, const float* __restrict__ wp,
-                                           const float* __restrict__ bias, int dil, Pre pre, Epi epi) {
+                                           const float* __restrict__ bias, int dil, float wscale, Pre pre, Epi epi) {
     typedef float v4f __attribute__((ext_vector_type(4)));
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+    typedef _Float16 v8h __attribute__((ext_vector_type(8)));
     using S = UnitConvSplit<C, NOUT>;
-    constexpr int CB = C / 8, TG = 4 / CB, KS = (K + TG - 1) / TG;
+    constexpr bool H16 = PF == 2;
+    constexpr int NPROD = PF == 6 ? 6 : 3;
+    constexpr int NPW = H16 ? kPiecesH : kPieces;  // weight pieces in the packing
     constexpr int NPU = NPROD == 3 ? 2 : kPieces;  // pieces used
+    constexpr int CB = C / 8, TG = 4 / CB, KS = (K + TG - 1) / TG;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int mb = wave / S::WPM, ws = wave % S::WPM;
     const int g4 = lane >> 4, cb = g4 % CB, tsub = g4 / CB, col = lane & 15;
-    v4u wr[KS][kPieces];
-    const v4u* w6 = reinterpret_cast<const v4u*>(wp) + (int64_t)mb * KS * kPieces * 64 + lane;
+    v4u wr[KS][NPW];
+    const v4u* w6 = reinterpret_cast<const v4u*>(wp) + (int64_t)mb * KS * NPW * 64 + lane;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int p = 0; p < NPU; ++p) wr[ks][p] = w6[(ks * kPieces + p) * 64];
+        for (int p = 0; p < NPU; ++p) wr[ks][p] = w6[(ks * NPW + p) * 64];
     float bv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int co = mb * 16 + 4 * g4 + r;
         bv[r] = co < C ? bias[co] : 0.0f;
+        if constexpr (H16) bv[r] *= wscale;  // the sums carry 2^e until epi
     }
+    const float out_scale = 1.0f / wscale;  // exact: a power of two
     const v4u* pcv = reinterpret_cast<const v4u*>(pc);
     constexpr int TA[6] = {0, 0, 1, 0, 1, 2}, TB[6] = {0, 1, 0, 2, 1, 0};
     for (int bt = 0; bt < S::NBAT; ++bt) {
@@ -514,7 +524,7 @@ __device__ __forceinline__ void unit_conv6(const uint4* __restrict__ pc, const f
         for (int ks = 0; ks < KS; ++ks) {
             const int tap = min(ks * TG + tsub, K - 1);  // padded taps re-read the last one (zero weights)
             const int off = (col + tap * dil) * CB + cb;
-            v4u b[S::NBB][kPieces];
+            v4u b[S::NBB][NPW];
 #pragma unroll
             for (int q = 0; q < S::NBB; ++q)
 #pragma unroll
@@ -522,21 +532,29 @@ __device__ __forceinline__ void unit_conv6(const uint4* __restrict__ pc, const f
 #pragma unroll
             for (int t = 0; t < NPROD; ++t)
 #pragma unroll
-                for (int q = 0; q < S::NBB; ++q)
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, wr[ks][TA[t]]),
-                                                                     __builtin_bit_cast(v8bf, b[q][TB[t]]), acc[q], 0,
-                                                                     0, 0);
+                for (int q = 0; q < S::NBB; ++q) {
+                    if constexpr (H16)
+                        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, wr[ks][TA[t]]),
+                                                                        __builtin_bit_cast(v8h, b[q][TB[t]]), acc[q],
+                                                                        0, 0, 0);
+                    else
+                        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, wr[ks][TA[t]]),
+                                                                         __builtin_bit_cast(v8bf, b[q][TB[t]]), acc[q],
+                                                                         0, 0, 0);
+                }
         }
 #pragma unroll
         for (int q = 0; q < S::NBB; ++q) {
             const int nb = ws + S::WPM * (bt * S::NBB + q);
+            if constexpr (H16) acc[q] *= out_scale;
             if (nb < S::NBLK) epi(q, acc[q], mb, nb);
         }
     }
 }
 
-template <int C, int K, int T, int NPROD>
+template <int C, int K, int T, int PF>
 __global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
+    constexpr int NPC = PF == 2 ? kPiecesH : kPieces;  // pieces per value in LDS
     typedef float v4f __attribute__((ext_vector_type(4)));
     using G = UnitGeom<C, K, T>;
     using G6 = Unit6Geom<C, K, T>;
@@ -583,11 +601,11 @@ __global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
         wave_lds_sync();
     }
     __syncthreads();
-    unit_pack6<C, G6::WP>(xr, XS1, W1, pc);
+    unit_pack6<C, G6::WP, NPC>(xr, XS1, W1, pc);
     __syncthreads();
     // conv1 -> Y1 rows
-    unit_conv6<C, K, G6::WP, G::NY1, NPROD>(
-        pc, a.w1, a.b1, dil, [](int, int, int) {},
+    unit_conv6<C, K, G6::WP, G::NY1, PF>(
+        pc, a.w1, a.b1, dil, a.wscale1, [](int, int, int) {},
         [&](int, v4f acc, int mb, int nb) {
             const int n = nb * 16 + (lane & 15);
 #pragma unroll
@@ -616,13 +634,13 @@ __global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
         }
     }
     __syncthreads();
-    unit_pack6<C, G6::WP>(xr, G::XS2, G::W2, pc);
+    unit_pack6<C, G6::WP, NPC>(xr, G::XS2, G::W2, pc);
     __syncthreads();
     float rs[S2::NBB][4];
     const float* sb = a.sum_in ? a.sum_in + (int64_t)b * a.bstride : nullptr;
     float* yb = a.y + (int64_t)b * a.bstride;
-    unit_conv6<C, K, G6::WP, T, NPROD>(
-        pc, a.w2, a.b2, 1,
+    unit_conv6<C, K, G6::WP, T, PF>(
+        pc, a.w2, a.b2, 1, a.wscale2,
         [&](int q, int mb, int nb) {
             const int n = min(p0 + nb * 16 + (lane & 15), L - 1);
 #pragma unroll
@@ -642,17 +660,17 @@ __global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
         });
 }
 
-template <int C, int K, int T, int NPROD>
+template <int C, int K, int T, int PF>
 static hipError_t launch_unit6_t(const UnitArgs& a, int batch, hipStream_t stream) {
     constexpr size_t lds = sizeof(float) * Unit6Geom<C, K, T>::LDS_FLOATS;
     static_assert(2 * lds <= 160 * 1024, "two workgroups per compute unit");
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void*)unit6_kernel<C, K, T, NPROD>,
+        hipError_t e = hipFuncSetAttribute((const void*)unit6_kernel<C, K, T, PF>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     dim3 grid((a.l + T - 1) / T, batch);
-    hipLaunchKernelGGL((unit6_kernel<C, K, T, NPROD>), grid, dim3(256), lds, stream, a);
+    hipLaunchKernelGGL((unit6_kernel<C, K, T, PF>), grid, dim3(256), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -678,7 +696,8 @@ static hipError_t launch_unit_t(const UnitArgs& a, int batch, hipStream_t stream
 // Tile widths: 128 positions at 32 channels, 256 at 16, 512 at 8 (about
 // 60-80 KB of LDS each, two workgroups per compute unit).
 hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream) {
-    if (!unit_supported(a.c, a.taps, a.dil) || (a.split != 0 && a.split != 3 && a.split != 6) || a.l < 1 || batch < 1 ||
+    if (!unit_supported(a.c, a.taps, a.dil) || (a.split != 0 && a.split != 2 && a.split != 3 && a.split != 6) ||
+        a.l < 1 || batch < 1 ||
         batch > 65535 || !a.x || !a.y ||
         a.x == a.y || !a.w1 || !a.w2 || !a.b1 || !a.b2 || !a.act1.taps || !a.act2.taps)
         return hipErrorInvalidValue;
@@ -686,6 +705,7 @@ hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream) {
     if (a.c == C_ && a.taps == K_)                                             \
         return a.split == 6   ? launch_unit6_t<C_, K_, T_, 6>(a, batch, stream)                             \
                : a.split == 3 ? launch_unit6_t<C_, K_, T_, 3>(a, batch, stream)                             \
+               : a.split == 2 ? launch_unit6_t<C_, K_, T_, 2>(a, batch, stream)                             \
                               : launch_unit_t<C_, K_, T_>(a, batch, stream);
     MH3A_UNIT(32, 3, 128) MH3A_UNIT(32, 7, 128) MH3A_UNIT(32, 11, 128)
     MH3A_UNIT(16, 3, 256) MH3A_UNIT(16, 7, 256) MH3A_UNIT(16, 11, 256)
