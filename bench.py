@@ -15,17 +15,17 @@ random weights. `--workload c4` times the stage-1 AMP set alone on
 (2, 256, 30000).
 
 `roofline` covers the dominant kernel, the AMP dilated convolution of the
-wide stages (conv_kernel on the packed activated input; its products run as
-six bf16 piece products on the bf16 matrix cores with fp32 accumulation,
-fp32-accurate), whose kernel durations come from HIP events the library
-records on the decode stream around every AMP conv launch of the last timed
-step (other launches are not bracketed there; a second, untimed pass with
-every launch bracketed gives the per-class breakdown). `achieved` counts
-the method's FLOPs (2 C_out C_in k per output); `peak` is the dense peak of
-the matrix instruction the kernel issues (bf16, 2500 TFLOP/s; fp32 with
---fp32-matrix), so `frac` is at most 1 / products. The named extras give
-the matrix pipe's occupancy counting every piece product, and the ratio to
-the fp32 matrix peak.
+wide stages (conv_kernel on the packed activated input; by default its
+products run as three fp16 piece products per fp32 product on the fp16
+matrix cores with fp32 accumulation, fp32-accurate), whose kernel durations
+come from HIP events the library records on the decode stream around every
+AMP conv launch of the last timed step (other launches are not bracketed
+there; a second, untimed pass with every launch bracketed gives the
+per-class breakdown). `achieved` counts the method's FLOPs (2 C_out C_in k
+per output); `peak` is the dense peak of the matrix instruction the kernel
+issues (fp16 / bf16, 2500 TFLOP/s; fp32 with --fp32-matrix), so `frac` is at
+most 1 / products. The named extras give the matrix pipe's occupancy
+counting every piece product, and the ratio to the fp32 matrix peak.
 `cpu_baseline` times the CPU oracle (numpy, fp64 inside each op) on a
 bounded sample: the first 320 latents of item 0, decoded in full.
 """
@@ -44,7 +44,8 @@ if ROOT not in sys.path:
 
 FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
-SPLIT_PRODUCTS = 6              # bf16 piece products per fp32 product
+SPLIT_PRODUCTS = 6              # bf16 piece products per fp32 product (matrix_form SPLIT)
+F16_PRODUCTS = 3                # fp16 piece products per fp32 product (the default form)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 LATENTS_PER_SECOND = 40         # 32 kHz / hop 800
 SAMPLE_RATE = 32000
@@ -74,6 +75,8 @@ def parse():
     ap.add_argument("--bf16", action="store_true", help="bf16-split matrix-core operands (MH3A_FLAG_BF16_MFMA)")
     ap.add_argument("--fp32-matrix", action="store_true",
                     help="build the decoder with matrix_form = MH3A_MATRIX_FP32 (fp32 matrix cores throughout)")
+    ap.add_argument("--bf16x6", action="store_true",
+                    help="build the decoder with matrix_form = MH3A_MATRIX_SPLIT (six bf16 piece products)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time K replays of one decode captured in a HIP graph (graph_ms_per_step)")
@@ -153,9 +156,10 @@ def cpu_baseline(params, n_latents):
 
 def roofline_entry(kernel, stats, form):
     """The roofline record of the matrix-core kernel from its HIP-event
-    stats: `form` is "split" (six bf16 piece products), "bf16x3" (three) or
-    "fp32" (fp32 matrix cores)."""
-    products = {"split": SPLIT_PRODUCTS, "bf16x3": 3, "fp32": 1}[form]
+    stats: `form` is "f16x3" (three fp16 piece products, the default),
+    "split" (six bf16 piece products), "bf16x3" (three bf16 piece products)
+    or "fp32" (fp32 matrix cores)."""
+    products = {"f16x3": F16_PRODUCTS, "split": SPLIT_PRODUCTS, "bf16x3": 3, "fp32": 1}[form]
     peak = FP32_MFMA_PEAK_TFLOPS if form == "fp32" else BF16_MFMA_PEAK_TFLOPS
     achieved = stats["flops"] / (stats["ms"] / 1e3) / 1e12 if stats["ms"] > 0 else 0.0
     return {
@@ -163,8 +167,9 @@ def roofline_entry(kernel, stats, form):
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": peak,
-        "peak_basis": ("dense fp32 matrix peak (v_mfma_f32_32x32x2f32)" if form == "fp32" else
-                       "dense bf16 matrix peak (v_mfma_f32_32x32x16_bf16, the instruction issued)"),
+        "peak_basis": {"fp32": "dense fp32 matrix peak (v_mfma_f32_32x32x2f32)",
+                       "f16x3": "dense fp16 matrix peak (v_mfma_f32_32x32x16_f16, the instruction issued)"}.get(
+                           form, "dense bf16 matrix peak (v_mfma_f32_32x32x16_bf16, the instruction issued)"),
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
         "achieved_counts": "the method's FLOPs, 2 C_out C_in k per output",
@@ -217,10 +222,11 @@ def main():
         batch, frames, flags, desc = WORKLOADS[args.workload]
     if args.bf16:
         flags |= 0x2
-    form = "fp32" if args.fp32_matrix else ("bf16x3" if args.bf16 else "split")
+    form = "fp32" if args.fp32_matrix else ("bf16x3" if args.bf16 else ("split" if args.bf16x6 else "f16x3"))
     params = synth.make_params()
     mean, std = synth.make_denorm()
-    cfg = {"matrix_form": _lib.MH3A_MATRIX_FP32} if args.fp32_matrix else None
+    cfg = ({"matrix_form": _lib.MH3A_MATRIX_FP32} if args.fp32_matrix else
+           {"matrix_form": _lib.MH3A_MATRIX_SPLIT} if args.bf16x6 else None)
     dec = Decoder(params, cfg, latents_mean=mean, latents_std=std)
     stream = torch.cuda.current_stream()
     if stage_bench:
@@ -287,7 +293,9 @@ def main():
             "flags": flags,
         }
     kernel_desc = ("conv_kernel, AMP dilated convs of the 64-512 channel stages (packed activated input; " +
-                   {"split": "six bf16 piece products per fp32 product on v_mfma_f32_32x32x16_bf16, fp32 "
+                   {"f16x3": "three fp16 piece products per fp32 product (two pieces per operand, weights "
+                             "scaled by 2^e) on v_mfma_f32_32x32x16_f16, fp32 accumulation)",
+                    "split": "six bf16 piece products per fp32 product on v_mfma_f32_32x32x16_bf16, fp32 "
                              "accumulation)",
                     "bf16x3": "three bf16 piece products (two-piece split) on v_mfma_f32_32x32x16_bf16)",
                     "fp32": "fp32 matrix cores)"}[form])
@@ -302,7 +310,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"split": "f32", "bf16x3": "bf16x3", "fp32": "f32"}[form],
+        "dtype": {"f16x3": "f32", "split": "f32", "bf16x3": "bf16x3", "fp32": "f32"}[form],
         "data": "synthetic",
         "config": config,
         "algorithmic_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),

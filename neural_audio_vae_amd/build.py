@@ -36,8 +36,8 @@ def hipcc():
     raise RuntimeError("hipcc not found; the mh3a library needs the ROCm toolchain")
 
 
-def compile_flags():
-    return [
+def compile_flags(defines=()):
+    return [f"-D{d}" for d in defines] + [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # keep the compiler from emitting packed fp32 VALU ops (the host
         # pass warns that it does not know the feature; only the device
@@ -47,24 +47,30 @@ def compile_flags():
     ]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + compile_flags() + ["-c", src, "-o", obj]
+def _compile(src, verbose, defines=(), obj_dir=OBJ):
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + compile_flags(defines) + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     return src, obj, res
 
 
-def build(verbose=False, jobs=None):
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose=False, jobs=None, defines=(), out=LIB, only=None):
+    """Compile every source (or only those named in `only`, taking the other
+    objects from the last full build) with optional -D defines (the
+    documented build-time options) and link `out`."""
+    obj_dir = OBJ if not defines else os.path.join(OBJ, "_".join(d.replace("=", "") for d in defines))
+    os.makedirs(obj_dir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(16, os.cpu_count() or 1)
-    objs, failed = [], []
+    failed = []
     # the largest translation units first
     order = sorted(srcs, key=lambda s: -os.path.getsize(s))
+    todo = [s for s in order if only is None or os.path.basename(s) in only]
+    objs = [os.path.join(OBJ, os.path.basename(s) + ".o") for s in order if s not in todo]
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        for src, obj, res in ex.map(lambda s: _compile(s, verbose), order):
+        for src, obj, res in ex.map(lambda s: _compile(s, verbose, defines, obj_dir), todo):
             if res.returncode != 0:
                 failed.append((src, res))
             objs.append(obj)
@@ -72,7 +78,7 @@ def build(verbose=False, jobs=None):
         for src, res in failed:
             sys.stderr.write(f"--- {os.path.basename(src)}\n" + res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libmh3a.so")
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + sorted(objs)
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -80,8 +86,8 @@ def build(verbose=False, jobs=None):
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("linking libmh3a.so failed")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
