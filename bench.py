@@ -101,25 +101,37 @@ def copy_probe(nbytes):
     return 0
 
 
-def measured_traffic(workload, flags, fp32_matrix=False):
+def sources_digest():
+    """sha256 over the library's sources (csrc/* and include/mh3a.h, sorted
+    by path): a counter record holds for the build it was taken on."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "neural_audio_vae_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "mh3a.h"))
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, form):
     """HBM bytes per launch of the roofline kernel from the committed
     rocprofv3 counter runs (profiles/amp_conv_c3_traffic.json for the
     decode's AMP convs, profiles/enc_unit_conv_e3_traffic.json for the
-    encoder's k7 convs), or None when the kernel sources changed since the
-    counters were taken or the workload differs."""
-    import hashlib
+    encoder's k7 convs), or None when the library's sources changed since
+    the counters were taken, or the workload or matrix form differs."""
     files = {"c3": "amp_conv_c3_traffic.json", "e3": "enc_unit_conv_e3_traffic.json"}
-    if workload not in files or flags & 0x2 or fp32_matrix:
+    if workload not in files:
         return None
     path = os.path.join(ROOT, "profiles", files[workload])
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in rec["sources"]:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
+    if rec.get("form") != form or rec.get("source_sha256") != sources_digest():
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def _blas_threads():
@@ -315,7 +327,7 @@ def main():
         "config": config,
         "algorithmic_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
         "roofline": dict(roofline_entry(kernel_desc, amp, form),
-                         traffic=measured_traffic(args.workload, flags, args.fp32_matrix)),
+                         traffic=measured_traffic(args.workload, form)),
         "kernels": _per_step(kernels, args.steps),
         "wall_s_timed": round(wall, 4),
     }
@@ -441,7 +453,7 @@ def main_encode(args):
         "roofline": dict(roofline_entry(
             "conv_kernel, the residual units' k7 dilated convs (split-product packed input; "
             + ("six bf16 piece products per fp32 product on v_mfma_f32_32x32x16_bf16)" if form == "split"
-               else "fp32 matrix cores)"), k7, form), traffic=measured_traffic(args.workload, 0, args.fp32_matrix)),
+               else "fp32 matrix cores)"), k7, form), traffic=measured_traffic(args.workload, form)),
         "kernels": _per_step(kernels, args.steps),
         "wall_s_timed": round(wall, 4),
     }

@@ -695,7 +695,64 @@ conv_kernel(ConvArgs a) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) acc[mb][nb][r] *= a.out_scale;
             }
-            if (a.ksplit > 1) {
+            // Whole tiles (every row and column inside the output, no K
+            // split) take the buffer-instruction epilogue: one buffer
+            // resource per array over the batch item's slice, the lane's
+            // column in the vector offset and each register's row and block
+            // in the scalar offset, so no output costs an address computation
+            // or an exec-mask branch. Block k + 1's residual and running-sum
+            // loads go out before block k's stores (exact for in-place
+            // updates: they read other outputs than block k writes).
+            const bool whole = a.ksplit == 1 && (mb_base + MBW) * 32 <= a.c_out &&
+                               cur.p0 + NWG <= a.positions && a.y_bstride <= kEpiMaxSlice &&
+                               a.y_bstride >= (int64_t)a.c_out * a.out_mul * a.positions;
+            auto epilogue_whole = [&](auto has_res, auto has_sum) {
+                constexpr bool HR = decltype(has_res)::value, HS = decltype(has_sum)::value;
+                constexpr int NB = MBW * NBW;
+                const int64_t ybase = (int64_t)cur.b * a.y_bstride;
+                const int nbytes = (int)(a.y_bstride * 4);
+                const auto ry = __builtin_amdgcn_make_buffer_rsrc(a.y + ybase, (short)0, nbytes, kBufferWord3);
+                const auto rr = __builtin_amdgcn_make_buffer_rsrc((void*)(HR ? a.res + ybase : a.y + ybase), (short)0,
+                                                                  nbytes, kBufferWord3);
+                const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(HS ? a.sum_in + ybase : a.y + ybase),
+                                                                  (short)0, nbytes, kBufferWord3);
+                const int ost = a.out_mul * a.positions;
+                const int vlane = ((mb_base * 32 + 4 * hi) * ost + a.out_mul * (cur.p0 + colbase) + a.out_add[cur.ph]) * 4;
+                auto soff = [&](int k, int r) {
+                    return ((k / NBW * 32 + 8 * (r >> 2) + (r & 3)) * ost + a.out_mul * (k % NBW) * 32) * 4;
+                };
+                float rv[2][16], sv[2][16];
+                auto load = [&](int k) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        if constexpr (HR)
+                            rv[k & 1][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, vlane, soff(k, r), 0));
+                        if constexpr (HS)
+                            sv[k & 1][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vlane, soff(k, r), 0));
+                    }
+                };
+                if constexpr (HR || HS) load(0);
+#pragma unroll
+                for (int k = 0; k < NB; ++k) {
+                    if constexpr (HR || HS)
+                        if (k + 1 < NB) load(k + 1);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float v = acc[k / NBW][k % NBW][r];
+                        if constexpr (HR) v += rv[k & 1][r];
+                        if constexpr (HS) v += sv[k & 1][r];
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v * a.scale), ry, vlane, soff(k, r), 0);
+                    }
+                }
+            };
+            using T_ = std::true_type;
+            using F_ = std::false_type;
+            if (whole) {
+                if (a.res && a.sum_in) epilogue_whole(T_{}, T_{});
+                else if (a.res) epilogue_whole(T_{}, F_{});
+                else if (a.sum_in) epilogue_whole(F_{}, T_{});
+                else epilogue_whole(F_{}, F_{});
+            } else if (a.ksplit > 1) {
                 // raw partial sums of this K range in MFMA fragment order:
                 // [wave][mb][nb][r][lane], so each register is one 256-byte
                 // row of the wave and the 16 of a block share one address

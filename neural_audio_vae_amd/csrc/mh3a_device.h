@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "mh3a_internal.h"
 
@@ -309,6 +310,12 @@ __device__ __forceinline__ void split3_bf16(float v, unsigned& p0, unsigned& p1,
     const float r2 = r1 - __uint_as_float(p1 << 16);
     p2 = bf16_bits(r2);
 }
+
+// Word 3 of a buffer resource for raw dword access on gfx9-family chips
+// (data format 32, no swizzle), and the largest batch-item slice (floats)
+// whose byte offsets a buffer instruction takes without overflow.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int64_t kEpiMaxSlice = (int64_t)1 << 29;
 
 // LDS floats of the conv kernel for window width W: the double-buffered
 // operand window, the activation staging (act only) and 64 floats per

@@ -47,11 +47,15 @@ int ok() {
 }
 
 // ---------------------------------------------------------------------------
-// Kaiser-windowed sinc low-pass (FastVideo "minimax_h3_audio_vae",
-// kaiser_sinc_filter1d): the attenuation uses (K/2 - 1) and 4 * half_width
-// as released; window = I0(beta sqrt(1 - r^2)) / I0(beta); taps
-// 2 fc w[n] sinc(2 fc t_n) on a half-integer grid for even K, normalized to
-// unit sum. Evaluated in double.
+// Kaiser-windowed sinc low-pass of the anti-aliased activation (FastVideo
+// "minimax_h3_audio_vae", the Activation1d samplers' filter design). Kaiser's
+// design rules (J. F. Kaiser, 1974): a window of N taps and transition width
+// dw (fraction of Nyquist) reaches A = 7.95 + 2.285 (N - 1) pi dw dB, and A dB
+// asks for beta = 0 below 21 dB, 0.5842 (A - 21)^0.4 + 0.07886 (A - 21) up
+// to 50 dB, 0.1102 (A - 8.7) above. The released filter evaluates them at
+// N = K / 2 and dw = 4 * half_width. Window I0(beta sqrt(1 - r^2)) / I0(beta);
+// taps 2 fc w[n] sinc(2 fc t_n) on a half-integer grid for even K, normalized
+// to unit sum. Evaluated in double.
 // ---------------------------------------------------------------------------
 double bessel_i0(double x) {
     const double q = 0.25 * x * x;
@@ -64,16 +68,17 @@ double bessel_i0(double x) {
     return sum;
 }
 
+static double kaiser_attenuation(int taps, double width) { return 7.95 + 2.285 * (taps - 1) * M_PI * width; }
+
+static double kaiser_beta_for(double a) {
+    if (a < 21.0) return 0.0;
+    if (a <= 50.0) return 0.5842 * std::pow(a - 21.0, 0.4) + 0.07886 * (a - 21.0);
+    return 0.1102 * (a - 8.7);
+}
+
 void design_lowpass(double cutoff, double half_width, int k, float* out) {
     const int half = k / 2;
-    const double atten = 2.285 * (half - 1) * M_PI * (4.0 * half_width) + 7.95;
-    double beta;
-    if (atten > 50.0)
-        beta = 0.1102 * (atten - 8.7);
-    else if (atten >= 21.0)
-        beta = 0.5842 * std::pow(atten - 21.0, 0.4) + 0.07886 * (atten - 21.0);
-    else
-        beta = 0.0;
+    const double beta = kaiser_beta_for(kaiser_attenuation(half, 4.0 * half_width));
     std::vector<double> f(k);
     double sum = 0.0;
     const double i0b = bessel_i0(beta);

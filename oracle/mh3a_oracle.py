@@ -129,8 +129,9 @@ def _f32(a):
 
 
 # ---------------------------------------------------------------------------
-# Kaiser-windowed sinc low-pass: FastVideo "minimax_h3_audio_vae",
-# function kaiser_sinc_filter1d.
+# Kaiser-windowed sinc low-pass of the anti-aliased activation: FastVideo
+# "minimax_h3_audio_vae", the filter design of the Activation1d up/down
+# samplers (kaiser_sinc_filter1d), from Kaiser's published design rules.
 # ---------------------------------------------------------------------------
 
 def bessel_i0(x):
@@ -148,17 +149,35 @@ def bessel_i0(x):
     return total
 
 
+def kaiser_attenuation(numtaps, width):
+    """Kaiser's empirical length rule for a Kaiser-window FIR low-pass of
+    numtaps taps and transition width `width` (a fraction of the Nyquist
+    band), solved for the stop-band attenuation in dB:
+    A = 7.95 + 2.285 (numtaps - 1) pi width (J. F. Kaiser, "Nonrecursive
+    digital filter design using the I0-sinh window function", 1974)."""
+    return 7.95 + 2.285 * (numtaps - 1) * math.pi * width
+
+
+def kaiser_beta_for(attenuation):
+    """Kaiser's shape parameter for a stop-band attenuation of A dB (same
+    source; the Kaiser-window design rule in Oppenheim and Schafer,
+    Discrete-Time Signal Processing): 0 below 21 dB, then
+    0.5842 (A - 21)^0.4 + 0.07886 (A - 21) up to 50 dB, then
+    0.1102 (A - 8.7)."""
+    a = attenuation
+    if a < 21.0:
+        return 0.0
+    if a <= 50.0:
+        return 0.5842 * (a - 21.0) ** 0.4 + 0.07886 * (a - 21.0)
+    return 0.1102 * (a - 8.7)
+
+
 def kaiser_beta(cutoff, half_width, kernel_size):
-    """The page's Kaiser shape parameter: attenuation from the half size
-    (kernel_size // 2 minus one, as released) and 4 * half_width, then the
-    three-branch Kaiser formula."""
-    half_size = kernel_size // 2
-    attenuation = 2.285 * (half_size - 1) * math.pi * (4.0 * half_width) + 7.95
-    if attenuation > 50.0:
-        return 0.1102 * (attenuation - 8.7)
-    if attenuation >= 21.0:
-        return 0.5842 * (attenuation - 21.0) ** 0.4 + 0.07886 * (attenuation - 21.0)
-    return 0.0
+    """The beta of the pages' anti-aliasing low-pass: Kaiser's rules above
+    with the released filter's two readings of them, the length taken as
+    kernel_size // 2 (not kernel_size) and the width as 4 * half_width.
+    The cutoff does not enter."""
+    return kaiser_beta_for(kaiser_attenuation(kernel_size // 2, 4.0 * half_width))
 
 
 def kaiser_window(n, beta):

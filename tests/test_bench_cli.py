@@ -21,7 +21,8 @@ def test_traffic_lookup_only_for_profiled_workloads():
     sys.path.insert(0, ROOT)
     import bench
 
-    assert bench.measured_traffic("c1", 0) is None
-    assert bench.measured_traffic("c3", 0x2) is None  # the bf16 operand variant was not profiled
-    v = bench.measured_traffic("c3", 0)
-    assert v is None or v > 1e8  # None once the kernel sources change after the counters were taken
+    assert bench.measured_traffic("c1", "f16x3") is None
+    assert bench.measured_traffic("c3", "bf16x3") is None  # the bf16 operand variant was not profiled
+    v = bench.measured_traffic("c3", "f16x3")
+    assert v is None or v > 1e8  # None once the library's sources change after the counters were taken
+    assert len(bench.sources_digest()) == 64
