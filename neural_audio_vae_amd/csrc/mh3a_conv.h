@@ -282,7 +282,14 @@ conv_kernel(ConvArgs a) {
     typedef _Float16 v8h __attribute__((ext_vector_type(8)));
     const int G6 = nch * (TAPS > 0 ? TAPS : 1) / 2;  // weight groups (slot pairs) per 32-row block
     constexpr int NAW = BX6 ? NPL : 1;  // weight pieces per slot pair in the packing
-    v4u A6a[NAW][MBW], A6b[NAW][MBW], A6c[NAW][MBW];
+    // weight ring: slot u % RING holds pair u, loaded RING - 1 pairs ahead
+    // (at most an item's pairs ahead)
+    constexpr int NPI6 = BX6 ? CPI * (TAPS > 0 ? TAPS : 1) / 2 : 2;
+    // (three slots for the six-product form: its three weight pieces per
+    // slot leave no registers for more)
+    constexpr int RING_W = PREC == 2 ? 3 : kWeightRing;
+    constexpr int RING = RING_W < NPI6 + 1 ? RING_W : NPI6 + 1;
+    v4u A6r[RING][NAW][MBW];
     auto load_a6 = [&](v4u (&dst)[NAW][MBW], int mb_base, int ph, int g) {
         const v4u* wp = reinterpret_cast<const v4u*>(a.w6 + (int64_t)ph * a.w6_phase_stride) + (int64_t)g * NAW * 64 + lane;
 #pragma unroll
@@ -530,8 +537,8 @@ conv_kernel(ConvArgs a) {
     if constexpr (BX6) {
         const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
         const int g0 = cur.c0 * TAPS / 2;
-        load_a6(A6a, mb0, cur.ph, g0);
-        load_a6(A6b, mb0, cur.ph, g0 + 1);
+#pragma unroll
+        for (int i = 0; i < RING - 1; ++i) load_a6(A6r[i], mb0, cur.ph, g0 + i);
     } else if constexpr (TAPS > 0) {
         const int mb0 = __builtin_amdgcn_readfirstlane(cur.mt * (MWG / 32) + wm * MBW);
         load_a_nb(Ar0, mb0, cur.ph, cur.c0 * a.taps);
@@ -562,55 +569,101 @@ conv_kernel(ConvArgs a) {
             const int nmb_base = __builtin_amdgcn_readfirstlane(nxt.mt * (MWG / 32) + wm * MBW);
             // the item's CPI chunks hold CPI * TAPS slots: pair u is weight group q0 + u
             constexpr int NPI = CPI * TAPS / 2;
-            static_assert((CPI * TAPS) % 2 == 0 && NPI >= 2, "whole slot pairs; the ring holds two ahead");
+            static_assert((CPI * TAPS) % 2 == 0 && NPI >= RING - 1, "whole slot pairs; the ring's lead within an item");
             const int q0 = (cur.c0 + CPI * cur_c) * TAPS / 2;
             const int nq0 = has_next ? (nxt.c0 + CPI * nxt_c) * TAPS / 2 : q0;
             const int nmb = has_next ? nmb_base : mb_base;
             const int nph6 = has_next ? nxt.ph : cur.ph;
             const float* bb_0 = cur_buf + colbase * 4;
-            // slots 0 and 1 hold pairs 0 and 1 on entry; pair u + 2 (or the next
-            // item's pair u + 2 - NPI) loads while pair u multiplies
-#pragma unroll
-            for (int u = 0; u < NPI; ++u) {
-                v4u(&use)[NAW][MBW] = (u % 3 == 0) ? A6a : ((u % 3 == 1) ? A6b : A6c);
-                v4u(&fill)[NAW][MBW] = ((u + 2) % 3 == 0) ? A6a : (((u + 2) % 3 == 1) ? A6b : A6c);
-                if (u + 2 < NPI) {
-                    load_a6(fill, mb_base, cur.ph, q0 + u + 2);
-                } else {
-                    load_a6(fill, nmb, nph6, nq0 + (u + 2 - NPI));
-                }
-                __builtin_amdgcn_sched_barrier(0);
+            // B operand of pair u, piece p: one 16-byte LDS read per block
+            auto read_b6 = [&](v4u (&dst)[NBW], int u, int p) {
                 const int s0 = 2 * u, s1 = 2 * u + 1;
                 const int off0 = (s0 / TAPS) * NPL * PS6 + (s0 % TAPS) * a.dil;
                 const int off1 = (s1 / TAPS) * NPL * PS6 + (s1 % TAPS) * a.dil;
-                const float* bq = bb_0 + (hi ? off1 : off0) * 4;
-                v4u Bv[NAW][NBW];
+                const float* bq = bb_0 + (hi ? off1 : off0) * 4 + p * PS6 * 4;
 #pragma unroll
-                for (int p = 0; p < NPA; ++p)
+                for (int nb = 0; nb < NBW; ++nb) dst[nb] = *reinterpret_cast<const v4u*>(bq + nb * 32 * 4);
+            };
+            // the products (A piece ta) x (B piece of Bp) of every block
+            auto mfma_piece = [&](const v4u (&A)[NAW][MBW], int ta, const v4u (&Bp)[NBW]) {
 #pragma unroll
-                    for (int nb = 0; nb < NBW; ++nb)
-                        Bv[p][nb] = *reinterpret_cast<const v4u*>(bq + (p * PS6 + nb * 32) * 4);
-                __builtin_amdgcn_sched_barrier(0);
-                mfma6(use, Bv);
+                for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb) {
+                        if constexpr (H16)
+                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                __builtin_bit_cast(v8h, A[ta][mb]), __builtin_bit_cast(v8h, Bp[nb]), acc[mb][nb], 0, 0, 0);
+                        else
+                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(v8bf, A[ta][mb]), __builtin_bit_cast(v8bf, Bp[nb]), acc[mb][nb], 0, 0, 0);
+                    }
+            };
+            if constexpr (NPROD == 3) {
+                // Three products (w0 x0, w1 x0, w0 x1): the LDS reads of pair
+                // u + 1 go out behind pair u's products, piece 0 once
+                // w0 x0 and w1 x0 have taken it, piece 1 once w0 x1 has, so
+                // that only the item's first pair waits on LDS latency (and
+                // no register is added). Slots 0 and 1 of the weight ring
+                // hold pairs 0 and 1 on entry; pair u + 2 (or the next item's
+                // pair u + 2 - NPI) loads while pair u multiplies.
+                v4u B0[NBW], B1[NBW];
+                read_b6(B0, 0, 0);
+                read_b6(B1, 0, 1);
+#pragma unroll
+                for (int u = 0; u < NPI; ++u) {
+                    v4u(&use)[NAW][MBW] = A6r[u % RING];
+                    constexpr int LEAD = RING - 1;
+                    if (u + LEAD < NPI) {
+                        load_a6(A6r[(u + LEAD) % RING], mb_base, cur.ph, q0 + u + LEAD);
+                    } else {
+                        load_a6(A6r[(u + LEAD) % RING], nmb, nph6, nq0 + (u + LEAD - NPI));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma_piece(use, 0, B0);
+                    mfma_piece(use, 1, B0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (u + 1 < NPI) read_b6(B0, u + 1, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma_piece(use, 0, B1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (u + 1 < NPI) read_b6(B1, u + 1, 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                // six products: pair u's reads go out right before its products
+#pragma unroll
+                for (int u = 0; u < NPI; ++u) {
+                    v4u(&use)[NAW][MBW] = A6r[u % RING];
+                    constexpr int LEAD = RING - 1;
+                    if (u + LEAD < NPI) {
+                        load_a6(A6r[(u + LEAD) % RING], mb_base, cur.ph, q0 + u + LEAD);
+                    } else {
+                        load_a6(A6r[(u + LEAD) % RING], nmb, nph6, nq0 + (u + LEAD - NPI));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    v4u Bv[NAW][NBW];
+#pragma unroll
+                    for (int p = 0; p < NPA; ++p) read_b6(Bv[p], u, p);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma6(use, Bv);
+                }
             }
-            // the next item's pairs 0 and 1 sit in slots NPI % 3, (NPI + 1) % 3
-            if constexpr (NPI % 3 == 1) {
+            // the next item's pairs 0 .. RING - 2 sit in slots (NPI + i) % RING:
+            // rotate them to slots i
+            if constexpr (NPI % RING != 0) {
+                v4u rot[RING][NAW][MBW];
 #pragma unroll
-                for (int p = 0; p < NAW; ++p)
+                for (int i = 0; i < RING; ++i)
 #pragma unroll
-                    for (int mb = 0; mb < MBW; ++mb) {
-                        A6a[p][mb] = A6b[p][mb];
-                        A6b[p][mb] = A6c[p][mb];
-                    }
-            } else if constexpr (NPI % 3 == 2) {
+                    for (int p = 0; p < NAW; ++p)
 #pragma unroll
-                for (int p = 0; p < NAW; ++p)
+                        for (int mb = 0; mb < MBW; ++mb) rot[i][p][mb] = A6r[(i + NPI) % RING][p][mb];
 #pragma unroll
-                    for (int mb = 0; mb < MBW; ++mb) {
-                        const v4u t0 = A6c[p][mb];
-                        A6b[p][mb] = A6a[p][mb];
-                        A6a[p][mb] = t0;
-                    }
+                for (int i = 0; i < RING; ++i)
+#pragma unroll
+                    for (int p = 0; p < NAW; ++p)
+#pragma unroll
+                        for (int mb = 0; mb < MBW; ++mb) A6r[i][p][mb] = rot[i][p][mb];
             }
         } else if constexpr (TAPS > 0) {
             // Compile-time tap count: the tap loop is fully unrolled and

@@ -315,6 +315,12 @@ __device__ __forceinline__ void split3_bf16(float v, unsigned& p0, unsigned& p1,
 // (data format 32, no swizzle), and the largest batch-item slice (floats)
 // whose byte offsets a buffer instruction takes without overflow.
 constexpr int kBufferWord3 = 0x00020000;
+// Slots of the split-product conv's weight register ring (weights load
+// kWeightRing - 1 slot pairs ahead of their products).
+#ifndef MH3A_WEIGHT_RING
+#define MH3A_WEIGHT_RING 4
+#endif
+constexpr int kWeightRing = MH3A_WEIGHT_RING;
 constexpr int64_t kEpiMaxSlice = (int64_t)1 << 29;
 
 // LDS floats of the conv kernel for window width W: the double-buffered
