@@ -175,7 +175,7 @@ conv_kernel(ConvArgs a) {
         if constexpr (ACT) {
             wave_lds_sync();
             act_from_xs<CI, true>(dst, xs, ss, (t.c0 + c) * CI, a.c_in, a.l_in, t.n_lo, W, ftaps, ab_st, pci, plane,
-                                  0);
+                                  0, act_xs_len(W));
         }
     };
 

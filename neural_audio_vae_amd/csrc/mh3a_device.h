@@ -31,6 +31,17 @@ __device__ __forceinline__ float snake_beta(float u, float a_over_pi, float hb) 
     return u + hb * (1.0f - c);
 }
 
+// The same SnakeBeta from U = u + hb (the up-sampling FIR's sum started at
+// hb instead of 0): the argument is U (alpha / pi) - hb (alpha / pi), its
+// fractional part (exact) gives the same cosine, and the result is
+// U - hb cos(2 alpha u). Four instructions: fma, fract, cos, fma. `hba` is
+// hb * (alpha / pi).
+__device__ __forceinline__ float snake_beta_biased(float U, float a_over_pi, float hb, float hba) {
+    const float r = __builtin_fmaf(U, a_over_pi, -hba);
+    const float c = __builtin_amdgcn_cosf(__builtin_amdgcn_fractf(r));
+    return __builtin_fmaf(-hb, c, U);
+}
+
 // Make this wave's earlier LDS writes visible to its later LDS reads (the
 // producer steps exchange data only within a wave: 32 lanes own a channel).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -95,10 +106,11 @@ __device__ __forceinline__ ActTaps load_act_taps(const float* tp) {
 template <int CI, bool PAIRED = false>
 __device__ __forceinline__ void act_from_xs(float* as, float* xs, float* __restrict__ ss, int ch0, int c_in, int l_in,
                                             int n_lo, int W, const ActTaps& f, float2 ab, int ci, int lane32,
-                                            int as_stride) {
+                                            int as_stride, int xs_stride) {
     const int ch = ch0 + ci;
     const bool live = ch < c_in;
-    const int XS = act_xs_len(W), SH = act_ss_half(W);
+    const int XS = xs_stride, SH = act_ss_half(W);
+    const float hba = ab.x * ab.y;
     float* xrow = xs + ci * XS;
     // slot m of the 2x-rate signal, s[2 n_lo - 5 + m]: even m = 2k at ev[k],
     // odd m = 2k + 1 at od[k + 1]
@@ -121,7 +133,8 @@ __device__ __forceinline__ void act_from_xs(float* as, float* xs, float* __restr
             const float2 x45 = *reinterpret_cast<const float2*>(xrow + idx + 4);
             const float2 x67 = *reinterpret_cast<const float2*>(xrow + idx + 6);
             const float X[8] = {x01.x, x01.y, x23.x, x23.y, x45.x, x45.y, x67.x, x67.y};
-            float ue0 = 0.f, uo0 = 0.f, ue1 = 0.f, uo1 = 0.f;
+            // the sums start at hb (see snake_beta_biased)
+            float ue0 = ab.y, uo0 = ab.y, ue1 = ab.y, uo1 = ab.y;
 #pragma unroll
             for (int e = 0; e < 6; ++e) {
                 ue0 = fmaf(fe[e], X[5 - e], ue0);
@@ -130,8 +143,10 @@ __device__ __forceinline__ void act_from_xs(float* as, float* xs, float* __restr
                 uo1 = fmaf(fo[e], X[7 - e], uo1);
             }
             // s[2t'] is slot 2 idx - 1 (od[idx]), s[2t' + 1] slot 2 idx (ev[idx])
-            *reinterpret_cast<float2*>(od + idx) = make_float2(snake_beta(ue0, ab.x, ab.y), snake_beta(ue1, ab.x, ab.y));
-            *reinterpret_cast<float2*>(ev + idx) = make_float2(snake_beta(uo0, ab.x, ab.y), snake_beta(uo1, ab.x, ab.y));
+            *reinterpret_cast<float2*>(od + idx) = make_float2(snake_beta_biased(ue0, ab.x, ab.y, hba),
+                                                               snake_beta_biased(ue1, ab.x, ab.y, hba));
+            *reinterpret_cast<float2*>(ev + idx) = make_float2(snake_beta_biased(uo0, ab.x, ab.y, hba),
+                                                               snake_beta_biased(uo1, ab.x, ab.y, hba));
         }
         wave_lds_sync();
         // outputs w, w + 1: a[w] = sum_q f[q] slot[2w + q], i.e. f[2j] ev[w + j]
@@ -175,14 +190,14 @@ __device__ __forceinline__ void act_from_xs(float* as, float* xs, float* __restr
         const int tq = n_lo - 3 + idx;
         const int tc = clampi(tq, 0, l_in - 1);
         const float* xv = xrow + (tc - n_lo + 3);  // xv[e] = X[tc - 3 + e]
-        float ue = 0.0f, uo = 0.0f;
+        float ue = ab.y, uo = ab.y;
 #pragma unroll
         for (int e = 0; e < 6; ++e) {
             ue = fmaf(fe[e], xv[5 - e], ue);
             uo = fmaf(fo[e], xv[6 - e], uo);
         }
-        float se = snake_beta(ue, ab.x, ab.y);
-        float so = snake_beta(uo, ab.x, ab.y);
+        float se = snake_beta_biased(ue, ab.x, ab.y, hba);
+        float so = snake_beta_biased(uo, ab.x, ab.y, hba);
         if (tq < 0) so = se;
         if (tq >= l_in) se = so;
         od[idx] = se;
@@ -226,7 +241,7 @@ __device__ __forceinline__ void stage_act(float* as, float* xs, float* __restric
         if (w < XL) xrow[w] = live ? v[r] : 0.0f;
     }
     wave_lds_sync();
-    act_from_xs<CI>(as, xs, ss, ch0, c_in, l_in, n_lo, W, f, ab, ci, lane32, as_stride);
+    act_from_xs<CI>(as, xs, ss, ch0, c_in, l_in, n_lo, W, f, ab, ci, lane32, as_stride, XL);
 }
 
 __device__ __forceinline__ float round_bf16(float v) {

@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(256) final_kernel(FinalArgs a) {
 // into LDS rows and stores them packed: each thread writes the 16-byte group
 // of one (hi, position), so every wave stores 1 KB contiguous.
 // ---------------------------------------------------------------------------
-constexpr int kActT = 256;
+constexpr int kActT = 250;  // W + 6 = 256 up-sampling pairs: four full passes of 64 lanes
 
 // PC: 0 writes the fp32 packed layout (two channel-parity planes); kPieces /
 // kPiecesH the split-product forms (bf16 x 3 / fp16 x 2 planes).
@@ -370,7 +370,7 @@ __global__ void __launch_bounds__(256, 2) unit_kernel(UnitArgs a) {
 #pragma unroll
     for (int c0 = 0; c0 < C; c0 += kChunk) {
         act_from_xs<kChunk>(ar + c0 * G::SA, xr + c0 * XS1, ss, c0, C, L, a1_lo, W1, f1, a.act1.ab[c0 + ci], ci,
-                            lane32, G::SA);
+                            lane32, G::SA, XS1);
         wave_lds_sync();  // this wave's 2x-rate rows are reused by its next channels
     }
     __syncthreads();
@@ -402,7 +402,7 @@ __global__ void __launch_bounds__(256, 2) unit_kernel(UnitArgs a) {
 #pragma unroll
         for (int c0 = 0; c0 < C; c0 += kChunk) {
             act_from_xs<kChunk>(ar + c0 * G::SA, xr + c0 * G::XS2, ss, c0, C, L, a2_lo, G::W2, f2, a.act2.ab[c0 + ci],
-                                ci, lane32, G::SA);
+                                ci, lane32, G::SA, G::XS2);
             wave_lds_sync();
         }
     }
@@ -434,43 +434,68 @@ __global__ void __launch_bounds__(256, 2) unit_kernel(UnitArgs a) {
 }
 
 // Split-product form of the unit kernel: the same unit, with both convs on
-// v_mfma_f32_16x16x32_bf16 over three bf16 pieces of the activations and of
-// the weights (the six products of order <= 2, fp32 accumulation; see
-// kPieces). K = 32 per instruction: lane l holds 8 consecutive channels of
-// channel block cb at tap ks * TG + tsub, where (cb, tsub) enumerate the
-// lane's K-group l / 16 (CB = C / 8 channel blocks, TG = 4 / CB taps per
-// instruction; padded taps carry zero weights and re-read the last tap).
+// v_mfma_f32_16x16x32_{bf16,f16} over pieces of the activations and of the
+// weights (fp32 accumulation; see kPieces, kPiecesH). K = 32 per
+// instruction: lane l holds 8 consecutive channels of channel block cb at
+// tap ks * TG + tsub, where (cb, tsub) enumerate the lane's K-group l / 16
+// (CB = C / 8 channel blocks, TG = 4 / CB taps per instruction; padded taps
+// carry zero weights and re-read the last tap).
 // LDS: the fp32 rows (x, then the activation in place, then Y1, then the
 // second activation in place) and one region that is first the
 // activation's 2x-rate scratch, then the pieces of A1, of A2:
-// [piece][position][C bf16], one 16-byte group per (position, channel block).
-template <int C, int K, int T>
+// [piece][position][C / 8][8 channels], one 16-byte group per (piece,
+// position, channel block). Rows are laid out at a stride of 4 mod 16
+// floats, which keeps the pack's reads (8 rows per thread) and conv1's
+// stores of Y1 free of LDS bank conflicts.
+__host__ __device__ constexpr int unit_row_stride(int n) { return ((n + 11) & ~15) + 4; }
+
+template <int C, int K, int T, int NPC>
 struct Unit6Geom {
-    using G = UnitGeom<C, K, T>;
+    static constexpr int R2 = (K - 1) / 2;
+    static constexpr int W2 = T + 2 * R2;                          // act2 outputs (conv2 operand)
+    static constexpr int NX2 = act_xs_len(W2);                     // Y1 positions = act2's input row
+    static constexpr int RS2 = unit_row_stride(NX2);
+    static constexpr int NY1 = (NX2 + 15) / 16 * 16;               // conv1 outputs computed
+    static constexpr int W1MAX = NY1 + 2 * kUnitMaxDil * R2;       // act1 outputs at the widest dilation
+    static constexpr int RS1MAX = unit_row_stride(act_xs_len(W1MAX));
+    static constexpr int XR = RS1MAX > RS2 ? RS1MAX : RS2;
+    static constexpr int LDS_X = C * XR;
     static constexpr int CB = C / 8, TG = 4 / CB, KS = (K + TG - 1) / TG;
-    static constexpr int WP = G::W1MAX;                          // positions per piece plane
-    static constexpr int PC = kPieces * WP * CB * 4;             // floats of the three planes
-    static constexpr int SS = kChunk * act_ss_len(G::W1MAX);     // floats of the 2x-rate scratch
+    static constexpr int WP = W1MAX;                               // positions per piece plane
+    static constexpr int PC = NPC * WP * CB * 4;                   // floats of the piece planes
+    static constexpr int SS = kChunk * act_ss_len(W1MAX);          // floats of the 2x-rate scratch
     static constexpr int LDS_P = PC > SS ? PC : SS;
-    static constexpr int LDS_FLOATS = G::LDS_X + LDS_P;
+    static constexpr int LDS_FLOATS = LDS_X + LDS_P;
     static_assert(C == 8 || C == 16 || C == 32, "8, 16 or 32 channels");
+    static_assert(T % 16 == 0, "whole 16-column blocks");
 };
 
-// fp32 rows (stride rs) of n positions -> pieces (16-byte group per
-// position and channel block, planes of WP positions; NPC = kPieces bf16 or
-// kPiecesH fp16 pieces)
+// fp32 rows (stride rs, 4 mod 16) of n positions -> pieces (16-byte group
+// per position and channel block, planes of WP positions; NPC = kPieces
+// bf16 or kPiecesH fp16 pieces). At 32 channels a wave's 64 items are 16
+// positions of channel blocks 0-1 and 16 other positions of blocks 2-3, so
+// that the 8 row reads and the piece stores meet distinct banks.
 template <int C, int WP, int NPC>
 __device__ __forceinline__ void unit_pack6(const float* rows, int rs, int n, uint4* pc) {
     constexpr int CB = C / 8;
-    for (int idx = threadIdx.x; idx < n * CB; idx += 256) {
-        const int w = idx / CB, cb = idx - w * CB;
+    const int n_items = CB == 4 ? ((n + 31) & ~31) * 4 : n * CB;
+    for (int idx = threadIdx.x; idx < n_items; idx += 256) {
+        int w, cb;
+        if constexpr (CB == 4) {
+            cb = idx & 3;
+            w = 32 * (idx >> 7) + ((idx >> 2) & 15) + 16 * (((idx >> 6) & 1) ^ (cb >> 1));
+            if (w >= n) continue;
+        } else {
+            w = idx / CB;
+            cb = idx - w * CB;
+        }
         float v8[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) v8[i] = rows[(cb * 8 + i) * rs + w];
         uint4 g[NPC];
         split_pack8<NPC>(v8, g);
 #pragma unroll
-        for (int p = 0; p < NPC; ++p) pc[p * WP * CB + idx] = g[p];
+        for (int p = 0; p < NPC; ++p) pc[p * WP * CB + w * CB + cb] = g[p];
     }
 }
 
@@ -552,31 +577,30 @@ __device__ __forceinline__ void unit_conv6(const uint4* __restrict__ pc, const f
     }
 }
 
-template <int C, int K, int T, int PF>
-__global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
+template <int C, int K, int T, int PF, int OCC>
+__global__ void __launch_bounds__(256, OCC) unit6_kernel(UnitArgs a) {
     constexpr int NPC = PF == 2 ? kPiecesH : kPieces;  // pieces per value in LDS
     typedef float v4f __attribute__((ext_vector_type(4)));
-    using G = UnitGeom<C, K, T>;
-    using G6 = Unit6Geom<C, K, T>;
+    using G6 = Unit6Geom<C, K, T, NPC>;
     using S2 = UnitConvSplit<C, T>;
     extern __shared__ __attribute__((aligned(16))) float lds[];
     float* xr = lds;                                             // fp32 rows
-    uint4* pc = reinterpret_cast<uint4*>(lds + G::LDS_X);      // pieces (or the 2x-rate scratch)
-    float* ss = lds + G::LDS_X;
+    uint4* pc = reinterpret_cast<uint4*>(lds + G6::LDS_X);     // pieces (or the 2x-rate scratch)
+    float* ss = lds + G6::LDS_X;
     const int tid = threadIdx.x, lane = tid & 63;
     const int ci = tid >> 5, lane32 = tid & 31;
     const int b = blockIdx.y;
     const int p0 = blockIdx.x * T;
     const int L = a.l, dil = a.dil;
     const float* xb = a.x + (int64_t)b * a.bstride;
-    const int a2_lo = p0 - G::R2, y1_lo = a2_lo - 6;
-    const int W1 = G::NY1 + 2 * dil * G::R2;
-    const int a1_lo = y1_lo - dil * G::R2, x_lo = a1_lo - 6;
-    const int XS1 = act_xs_len(W1);
+    const int a2_lo = p0 - G6::R2, y1_lo = a2_lo - 6;
+    const int W1 = G6::NY1 + 2 * dil * G6::R2;
+    const int a1_lo = y1_lo - dil * G6::R2, x_lo = a1_lo - 6;
+    const int NX1 = act_xs_len(W1), RS1 = unit_row_stride(NX1);
 
     const ActTaps f1 = load_act_taps(a.act1.taps);
     {
-        constexpr int NW = (G::XS1MAX + 255) / 256;
+        constexpr int NW = (act_xs_len(G6::W1MAX) + 255) / 256;
 #pragma unroll
         for (int c0 = 0; c0 < C; c0 += 8) {
             float v[8][NW];
@@ -589,38 +613,38 @@ __global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
             for (int r = 0; r < 8; ++r)
 #pragma unroll
                 for (int u = 0; u < NW; ++u)
-                    if (tid + 256 * u < XS1) xr[(c0 + r) * XS1 + tid + 256 * u] = v[r][u];
+                    if (tid + 256 * u < NX1) xr[(c0 + r) * RS1 + tid + 256 * u] = v[r][u];
         }
     }
     __syncthreads();
     // act1 in place over the x rows (a channel's x row is dead after its up pass)
 #pragma unroll
     for (int c0 = 0; c0 < C; c0 += kChunk) {
-        act_from_xs<kChunk>(xr + c0 * XS1, xr + c0 * XS1, ss, c0, C, L, a1_lo, W1, f1, a.act1.ab[c0 + ci], ci, lane32,
-                            XS1);
+        act_from_xs<kChunk>(xr + c0 * RS1, xr + c0 * RS1, ss, c0, C, L, a1_lo, W1, f1, a.act1.ab[c0 + ci], ci, lane32,
+                            RS1, RS1);
         wave_lds_sync();
     }
     __syncthreads();
-    unit_pack6<C, G6::WP, NPC>(xr, XS1, W1, pc);
+    unit_pack6<C, G6::WP, NPC>(xr, RS1, W1, pc);
     __syncthreads();
     // conv1 -> Y1 rows
-    unit_conv6<C, K, G6::WP, G::NY1, PF>(
+    unit_conv6<C, K, G6::WP, G6::NY1, PF>(
         pc, a.w1, a.b1, dil, a.wscale1, [](int, int, int) {},
         [&](int, v4f acc, int mb, int nb) {
             const int n = nb * 16 + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int co = mb * 16 + 4 * (lane >> 4) + r;
-                if (co < C && n < G::XS2) xr[co * G::XS2 + n] = acc[r];
+                if (co < C && n < G6::NX2) xr[co * G6::RS2 + n] = acc[r];
             }
         });
     __syncthreads();
-    if (y1_lo < 0 || y1_lo + G::XS2 > L) {
+    if (y1_lo < 0 || y1_lo + G6::NX2 > L) {
         const int i0 = -y1_lo, i1 = L - 1 - y1_lo;
-        for (int idx = tid; idx < C * G::XS2; idx += 256) {
-            const int co = idx / G::XS2, w = idx - co * G::XS2;
+        for (int idx = tid; idx < C * G6::NX2; idx += 256) {
+            const int co = idx / G6::NX2, w = idx - co * G6::NX2;
             const int src = w < i0 ? i0 : (w > i1 ? i1 : -1);
-            if (src >= 0) xr[co * G::XS2 + w] = xr[co * G::XS2 + src];
+            if (src >= 0) xr[co * G6::RS2 + w] = xr[co * G6::RS2 + src];
         }
         __syncthreads();
     }
@@ -628,13 +652,13 @@ __global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
         const ActTaps f2 = load_act_taps(a.act2.taps);
 #pragma unroll
         for (int c0 = 0; c0 < C; c0 += kChunk) {
-            act_from_xs<kChunk>(xr + c0 * G::XS2, xr + c0 * G::XS2, ss, c0, C, L, a2_lo, G::W2, f2,
-                                a.act2.ab[c0 + ci], ci, lane32, G::XS2);
+            act_from_xs<kChunk>(xr + c0 * G6::RS2, xr + c0 * G6::RS2, ss, c0, C, L, a2_lo, G6::W2, f2,
+                                a.act2.ab[c0 + ci], ci, lane32, G6::RS2, G6::RS2);
             wave_lds_sync();
         }
     }
     __syncthreads();
-    unit_pack6<C, G6::WP, NPC>(xr, G::XS2, G::W2, pc);
+    unit_pack6<C, G6::WP, NPC>(xr, G6::RS2, G6::W2, pc);
     __syncthreads();
     float rs[S2::NBB][4];
     const float* sb = a.sum_in ? a.sum_in + (int64_t)b * a.bstride : nullptr;
@@ -660,17 +684,18 @@ __global__ void __launch_bounds__(256, 2) unit6_kernel(UnitArgs a) {
         });
 }
 
-template <int C, int K, int T, int PF>
+template <int C, int K, int T, int PF, int OCC>
 static hipError_t launch_unit6_t(const UnitArgs& a, int batch, hipStream_t stream) {
-    constexpr size_t lds = sizeof(float) * Unit6Geom<C, K, T>::LDS_FLOATS;
-    static_assert(2 * lds <= 160 * 1024, "two workgroups per compute unit");
+    constexpr int NPC = PF == 2 ? kPiecesH : kPieces;
+    constexpr size_t lds = sizeof(float) * Unit6Geom<C, K, T, NPC>::LDS_FLOATS;
+    static_assert(OCC * lds <= 160 * 1024, "OCC workgroups per compute unit");
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void*)unit6_kernel<C, K, T, PF>,
+        hipError_t e = hipFuncSetAttribute((const void*)unit6_kernel<C, K, T, PF, OCC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     dim3 grid((a.l + T - 1) / T, batch);
-    hipLaunchKernelGGL((unit6_kernel<C, K, T, PF>), grid, dim3(256), lds, stream, a);
+    hipLaunchKernelGGL((unit6_kernel<C, K, T, PF, OCC>), grid, dim3(256), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -693,23 +718,33 @@ static hipError_t launch_unit_t(const UnitArgs& a, int batch, hipStream_t stream
     return hipGetLastError();
 }
 
-// Tile widths: 128 positions at 32 channels, 256 at 16, 512 at 8 (about
-// 60-80 KB of LDS each, two workgroups per compute unit).
+// Tile widths of the split-product unit kernels (positions T, workgroups per
+// compute unit OCC, from the LDS size): the widest tiles that keep three or
+// four workgroups resident, so that one workgroup's loads and barriers
+// overlap the others' vector and matrix work. The fp32 form keeps 128
+// positions at 32 channels, 256 at 16 and 512 at 8 (two workgroups).
 hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream) {
     if (!unit_supported(a.c, a.taps, a.dil) || (a.split != 0 && a.split != 2 && a.split != 3 && a.split != 6) ||
         a.l < 1 || batch < 1 ||
         batch > 65535 || !a.x || !a.y ||
         a.x == a.y || !a.w1 || !a.w2 || !a.b1 || !a.b2 || !a.act1.taps || !a.act2.taps)
         return hipErrorInvalidValue;
-#define MH3A_UNIT(C_, K_, T_)                                                  \
-    if (a.c == C_ && a.taps == K_)                                             \
-        return a.split == 6   ? launch_unit6_t<C_, K_, T_, 6>(a, batch, stream)                             \
-               : a.split == 3 ? launch_unit6_t<C_, K_, T_, 3>(a, batch, stream)                             \
-               : a.split == 2 ? launch_unit6_t<C_, K_, T_, 2>(a, batch, stream)                             \
-                              : launch_unit_t<C_, K_, T_>(a, batch, stream);
-    MH3A_UNIT(32, 3, 128) MH3A_UNIT(32, 7, 128) MH3A_UNIT(32, 11, 128)
-    MH3A_UNIT(16, 3, 256) MH3A_UNIT(16, 7, 256) MH3A_UNIT(16, 11, 256)
-    MH3A_UNIT(8, 3, 512) MH3A_UNIT(8, 7, 512) MH3A_UNIT(8, 11, 512)
+#define MH3A_UNIT(C_, K_, T0_, T6_, O6_, T2_, O2_)                                                     \
+    if (a.c == C_ && a.taps == K_)                                                                     \
+        return a.split == 6   ? launch_unit6_t<C_, K_, T6_, 6, O6_>(a, batch, stream)                   \
+               : a.split == 3 ? launch_unit6_t<C_, K_, T6_, 3, O6_>(a, batch, stream)                   \
+               : a.split == 2 ? launch_unit6_t<C_, K_, T2_, 2, O2_>(a, batch, stream)                   \
+                              : launch_unit_t<C_, K_, T0_>(a, batch, stream);
+    //        C   K  fp32  bf16 pieces  fp16 pieces
+    MH3A_UNIT(32, 3, 128,  96, 3,       112, 4)
+    MH3A_UNIT(32, 7, 128,  96, 3,       112, 3)
+    MH3A_UNIT(32, 11, 128, 96, 2,       112, 3)
+    MH3A_UNIT(16, 3, 256,  176, 4,      240, 4)
+    MH3A_UNIT(16, 7, 256,  192, 3,      224, 4)
+    MH3A_UNIT(16, 11, 256, 192, 3,      240, 3)
+    MH3A_UNIT(8, 3, 512,   384, 3,      384, 4)
+    MH3A_UNIT(8, 7, 512,   336, 3,      336, 3)
+    MH3A_UNIT(8, 11, 512,  320, 3,      320, 4)
 #undef MH3A_UNIT
     return hipErrorInvalidValue;
 }
