@@ -233,8 +233,15 @@ __device__ __forceinline__ void stage_act(float* as, float* xs, float* __restric
     const float2 ab = live ? abp[ch] : make_float2(0.0f, 0.0f);
     float* xrow = xs + ci * XL;
     float v[NR];
+    if (n_lo - 6 >= 0 && n_lo - 6 + 32 * NR <= l_in) {
+        // every load inside the row: one address, the loads at immediate offsets
+        const float* p = xc + (n_lo - 6 + lane32);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) v[r] = xc[clampi(n_lo - 6 + lane32 + 32 * r, 0, l_in - 1)];
+        for (int r = 0; r < NR; ++r) v[r] = p[32 * r];
+    } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) v[r] = xc[clampi(n_lo - 6 + lane32 + 32 * r, 0, l_in - 1)];
+    }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         const int w = lane32 + 32 * r;

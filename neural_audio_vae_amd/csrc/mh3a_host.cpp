@@ -155,6 +155,7 @@ struct ConvLayer {
     float wh_scale = 1.0f; // 2^e
     int64_t w_phase_stride = 0;
     int64_t b_off = -1;
+    int64_t wv_off = -1;   // transposed convs run on the vector ALU: the folded weight [c_in][c_out][k], or -1
     int act = -1;       // index into acts, -1 = none
     int alg_taps = 1;   // taps per input sample the layer's definition uses
     int kind = 0;       // timing class
@@ -619,6 +620,29 @@ hipError_t run_act(const mh3a_decoder* d, int act_idx, const float* x, float* y,
     return e;
 }
 
+// A narrow stage's transposed conv on the vector ALU: x (B, c_in, len) ->
+// y (B, c_out, r len).
+hipError_t run_ups_vec(const mh3a_decoder* d, const ConvLayer& U, const float* x, float* y, int batch, int len,
+                       int k, hipStream_t st) {
+    UpsVecArgs a;
+    a.x = x;
+    a.y = y;
+    a.w = d->blob + U.wv_off;
+    a.bias = d->blob + U.b_off;
+    a.ci = U.c_in;
+    a.co = U.c_out;
+    a.r = U.phases;
+    a.k = k;
+    a.l = len;
+    TimedLaunch tl(d, st, KIND_UPSAMPLE);
+    hipError_t e = launch_ups_vec(a, batch, st);
+    const double flops = 2.0 * U.c_out * (double)U.c_in * k * len * batch;
+    const double bytes = 4.0 * ((double)batch * U.c_in * len + (double)batch * U.c_out * U.phases * len +
+                                (double)U.c_in * U.c_out * k + U.c_out);
+    tl.done(KIND_UPSAMPLE, flops, bytes);
+    return e;
+}
+
 // The split pass of a conv input: x (B, c, len) rows -> y in the packed
 // split-product form.
 hipError_t run_split(const mh3a_decoder* d, const float* x, float* y, int batch, int c, int64_t len, int pieces,
@@ -880,7 +904,9 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
     for (int s = 0; s < c.num_ups; ++s) {
         const int C = d->stage_c[s];
         const int64_t lout = len * c.rates[s];
-        if (pre_bx6(d, d->ups[s])) {
+        if (d->ups[s].wv_off >= 0) {
+            HIP_TRY(run_ups_vec(d, d->ups[s], bufS, bufH, B, (int)len, c.kernels[s], st));
+        } else if (pre_bx6(d, d->ups[s])) {
             const bool h16 = pre_h16(d, d->ups[s]);
             HIP_TRY(run_split(d, bufS, bufA, B, cin, len, h16 ? kPiecesH : kPieces, st));
             HIP_TRY(run_conv(d, d->ups[s], bufA, pk_item_floats(d, cin, len), (int)len, (int)len, bufH,
@@ -1464,6 +1490,7 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
             if (splith) pack_conv_weights_h(wph.data(), C, cin, ku, eh, blob.h.data() + U.wh_off + ph * perh);
         }
         U.b_off = blob.add(bias, C);
+        if (ups_vec_supported(cin, C, r, k)) U.wv_off = blob.add(w.data(), (int64_t)cin * C * k);
         // AMP blocks
         for (int j = 0; j < c.num_resblocks; ++j) {
             const int kk = c.rb_kernels[j];

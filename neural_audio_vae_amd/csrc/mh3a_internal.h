@@ -179,7 +179,7 @@ struct ConvShape {
 };
 // AMP activations of at least this many (batch x channel x position)
 // elements run as their own pass (see amp_act_fused in mh3a_host.cpp).
-constexpr int64_t kSeparateActMin = (int64_t)1 << 20;
+constexpr int64_t kSeparateActMin = (int64_t)1 << 12;
 // Tile shape and K split of one launch.
 struct ConvPlan {
     TileId tile;
@@ -276,6 +276,20 @@ struct FinalArgs {
     int clamp;
 };
 hipError_t launch_final(const FinalArgs& a, int batch, hipStream_t stream);
+
+// ConvTranspose1d of a narrow stage on the vector ALU (fp32 fused
+// multiply-adds, the polyphase form): y (B, co, r l) = convT(x (B, ci, l)),
+// stride r, kernel k, padding (k - r) / 2, with bias. Supported shapes:
+// ups_vec_supported.
+struct UpsVecArgs {
+    const float* x;     // (B, ci, l)
+    float* y;           // (B, co, r l)
+    const float* w;     // [ci][co][k], the folded transposed-conv weight as stored
+    const float* bias;  // [co]
+    int ci, co, r, k, l;
+};
+bool ups_vec_supported(int ci, int co, int r, int k);
+hipError_t launch_ups_vec(const UpsVecArgs& a, int batch, hipStream_t stream);
 
 // Static device scratch of mh3a_decode_noalloc (mh3a_noalloc.hip): its size,
 // the once-per-device lookup of its device address (hipGetSymbolAddress

@@ -214,6 +214,105 @@ hipError_t launch_act(const ActArgs& a, int batch, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
+// Transposed conv of the narrow stages (8-32 channels) on the vector ALU. In
+// the polyphase form output t = R m + ph is the bias plus, over input
+// channels i and taps q with (ph + P - q) divisible by R (P = (K - R) / 2),
+// W[i][o][q] x[i][m + (ph + P - q) / R], zero outside the sequence. A
+// workgroup owns 256 input positions of one batch item: their window of x
+// (every channel) is staged in LDS, and each thread produces all R phases
+// of its position for every output channel (R CO accumulators). The weights
+// are read at uniform addresses (scalar loads); the outputs of a position
+// are R consecutive floats per channel, stored as one vector per thread.
+// HBM sees x once and y once; these stages have too few channels to fill
+// matrix-core tiles (a 32-row block would be half padding at 16 outputs).
+// ---------------------------------------------------------------------------
+constexpr int ups_off_min(int R, int K) {
+    int v = 1 << 20;
+    for (int ph = 0; ph < R; ++ph)
+        for (int q = 0; q < K; ++q)
+            if ((ph + (K - R) / 2 - q) % R == 0 && (ph + (K - R) / 2 - q) / R < v) v = (ph + (K - R) / 2 - q) / R;
+    return v;
+}
+constexpr int ups_off_max(int R, int K) {
+    int v = -(1 << 20);
+    for (int ph = 0; ph < R; ++ph)
+        for (int q = 0; q < K; ++q)
+            if ((ph + (K - R) / 2 - q) % R == 0 && (ph + (K - R) / 2 - q) / R > v) v = (ph + (K - R) / 2 - q) / R;
+    return v;
+}
+constexpr int kUpsT = 256;
+
+template <int CI, int CO, int R, int K>
+__global__ void __launch_bounds__(256) ups_vec_kernel(UpsVecArgs a) {
+    constexpr int P = (K - R) / 2;
+    constexpr int DLO = ups_off_min(R, K), DHI = ups_off_max(R, K);
+    constexpr int ND = DHI - DLO + 1;
+    constexpr int XW = kUpsT + ND - 1;
+    __shared__ float xs[CI * XW];
+    const int b = blockIdx.y;
+    const int m0 = blockIdx.x * kUpsT;
+    const int L = a.l;
+    const float* xb = a.x + (int64_t)b * CI * L;
+    for (int idx = threadIdx.x; idx < CI * XW; idx += 256) {
+        const int i = idx / XW, w = idx - i * XW;
+        const int m = m0 + DLO + w;
+        xs[idx] = (m >= 0 && m < L) ? xb[(int64_t)i * L + m] : 0.0f;
+    }
+    __syncthreads();
+    const int m = m0 + threadIdx.x;
+    if (m >= L) return;
+    float acc[R][CO];
+#pragma unroll
+    for (int o = 0; o < CO; ++o) {
+        const float bo = a.bias[o];
+#pragma unroll
+        for (int ph = 0; ph < R; ++ph) acc[ph][o] = bo;
+    }
+    const float* __restrict__ w = a.w;
+#pragma unroll 2
+    for (int i = 0; i < CI; ++i) {
+        float xv[ND];
+#pragma unroll
+        for (int e = 0; e < ND; ++e) xv[e] = xs[i * XW + threadIdx.x + e];
+#pragma unroll
+        for (int ph = 0; ph < R; ++ph)
+#pragma unroll
+            for (int q = 0; q < K; ++q) {
+                if ((ph + P - q) % R != 0) continue;
+                const float xq = xv[(ph + P - q) / R - DLO];
+#pragma unroll
+                for (int o = 0; o < CO; ++o) acc[ph][o] = fmaf(w[(i * CO + o) * K + q], xq, acc[ph][o]);
+            }
+    }
+    float* yb = a.y + (int64_t)b * CO * R * L + (int64_t)R * m;
+#pragma unroll
+    for (int o = 0; o < CO; ++o) {
+        if constexpr (R == 2) {
+            *reinterpret_cast<float2*>(yb + (int64_t)o * R * L) = make_float2(acc[0][o], acc[1][o]);
+        } else {
+#pragma unroll
+            for (int ph = 0; ph < R; ++ph) yb[(int64_t)o * R * L + ph] = acc[ph][o];
+        }
+    }
+}
+
+bool ups_vec_supported(int ci, int co, int r, int k) {
+    return r == 2 && k == 4 && ((ci == 32 && co == 16) || (ci == 16 && co == 8));
+}
+
+hipError_t launch_ups_vec(const UpsVecArgs& a, int batch, hipStream_t stream) {
+    if (!ups_vec_supported(a.ci, a.co, a.r, a.k) || a.l < 1 || batch < 1 || batch > 65535 || !a.x || !a.y ||
+        !a.w || !a.bias || a.x == a.y)
+        return hipErrorInvalidValue;
+    dim3 grid((a.l + kUpsT - 1) / kUpsT, batch);
+    if (a.ci == 32)
+        hipLaunchKernelGGL((ups_vec_kernel<32, 16, 2, 4>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((ups_vec_kernel<16, 8, 2, 4>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // One AMP residual unit per launch, for narrow stages (8 to 32 channels):
 //   y = scale * (x + conv2(act2(conv1(act1(x)))) + sum_in)
 // A workgroup of four waves owns T output positions [p0, p0 + T) of one
@@ -443,21 +542,23 @@ __global__ void __launch_bounds__(256, 2) unit_kernel(UnitArgs a) {
 // LDS: the fp32 rows (x, then the activation in place, then Y1, then the
 // second activation in place) and one region that is first the
 // activation's 2x-rate scratch, then the pieces of A1, of A2:
-// [piece][position][C / 8][8 channels], one 16-byte group per (piece,
-// position, channel block). Rows are laid out at a stride of 4 mod 16
-// floats, which keeps the pack's reads (8 rows per thread) and conv1's
-// stores of Y1 free of LDS bank conflicts.
+// [piece][C / 8][position][8 channels], one 16-byte group per (piece,
+// channel block, position). Rows are laid out at a stride of 4 mod 16
+// floats, which keeps conv1's stores of Y1 free of LDS bank conflicts.
+// conv1 runs whole 16-column blocks over the NX2 positions act2 reads; the
+// columns past NX2 read stale pieces beyond A1 (inside the planes) and are
+// never stored, so act1 covers only NX2 + 2 dil R2 positions.
 __host__ __device__ constexpr int unit_row_stride(int n) { return ((n + 11) & ~15) + 4; }
 
 template <int C, int K, int T, int NPC>
 struct Unit6Geom {
     static constexpr int R2 = (K - 1) / 2;
     static constexpr int W2 = T + 2 * R2;                          // act2 outputs (conv2 operand)
-    static constexpr int NX2 = act_xs_len(W2);                     // Y1 positions = act2's input row
+    static constexpr int NX2 = W2 + 12;                            // Y1 positions = act2's input row
     static constexpr int RS2 = unit_row_stride(NX2);
     static constexpr int NY1 = (NX2 + 15) / 16 * 16;               // conv1 outputs computed
-    static constexpr int W1MAX = NY1 + 2 * kUnitMaxDil * R2;       // act1 outputs at the widest dilation
-    static constexpr int RS1MAX = unit_row_stride(act_xs_len(W1MAX));
+    static constexpr int W1MAX = NY1 + 2 * kUnitMaxDil * R2;       // conv1's operand reach at the widest dilation
+    static constexpr int RS1MAX = unit_row_stride(NX2 + 2 * kUnitMaxDil * R2 + 12);
     static constexpr int XR = RS1MAX > RS2 ? RS1MAX : RS2;
     static constexpr int LDS_X = C * XR;
     static constexpr int CB = C / 8, TG = 4 / CB, KS = (K + TG - 1) / TG;
@@ -470,32 +571,24 @@ struct Unit6Geom {
     static_assert(T % 16 == 0, "whole 16-column blocks");
 };
 
-// fp32 rows (stride rs, 4 mod 16) of n positions -> pieces (16-byte group
-// per position and channel block, planes of WP positions; NPC = kPieces
-// bf16 or kPiecesH fp16 pieces). At 32 channels a wave's 64 items are 16
-// positions of channel blocks 0-1 and 16 other positions of blocks 2-3, so
-// that the 8 row reads and the piece stores meet distinct banks.
+// fp32 rows (stride rs) of n positions -> pieces: plane p holds, per channel
+// block cb, WP consecutive 16-byte groups (the 8 channels of the block at
+// one position). A wave's items are consecutive positions of one block, so
+// its 8 row reads and its piece stores are contiguous (no bank conflicts),
+// and so are the conv's operand reads (16 consecutive positions per
+// 16-lane group). NPC = kPieces bf16 or kPiecesH fp16 pieces.
 template <int C, int WP, int NPC>
 __device__ __forceinline__ void unit_pack6(const float* rows, int rs, int n, uint4* pc) {
     constexpr int CB = C / 8;
-    const int n_items = CB == 4 ? ((n + 31) & ~31) * 4 : n * CB;
-    for (int idx = threadIdx.x; idx < n_items; idx += 256) {
-        int w, cb;
-        if constexpr (CB == 4) {
-            cb = idx & 3;
-            w = 32 * (idx >> 7) + ((idx >> 2) & 15) + 16 * (((idx >> 6) & 1) ^ (cb >> 1));
-            if (w >= n) continue;
-        } else {
-            w = idx / CB;
-            cb = idx - w * CB;
-        }
+    for (int idx = threadIdx.x; idx < n * CB; idx += 256) {
+        const int cb = idx / n, w = idx - cb * n;
         float v8[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) v8[i] = rows[(cb * 8 + i) * rs + w];
         uint4 g[NPC];
         split_pack8<NPC>(v8, g);
 #pragma unroll
-        for (int p = 0; p < NPC; ++p) pc[p * WP * CB + w * CB + cb] = g[p];
+        for (int p = 0; p < NPC; ++p) pc[(p * CB + cb) * WP + w] = g[p];
     }
 }
 
@@ -548,12 +641,12 @@ __device__ __forceinline__ void unit_conv6(const uint4* __restrict__ pc, const f
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int tap = min(ks * TG + tsub, K - 1);  // padded taps re-read the last one (zero weights)
-            const int off = (col + tap * dil) * CB + cb;
+            const int off = cb * WP + col + tap * dil;
             v4u b[S::NBB][NPW];
 #pragma unroll
             for (int q = 0; q < S::NBB; ++q)
 #pragma unroll
-                for (int p = 0; p < NPU; ++p) b[q][p] = pcv[p * WP * CB + nbq[q] * 16 * CB + off];
+                for (int p = 0; p < NPU; ++p) b[q][p] = pcv[p * WP * CB + nbq[q] * 16 + off];
 #pragma unroll
             for (int t = 0; t < NPROD; ++t)
 #pragma unroll
@@ -594,21 +687,30 @@ __global__ void __launch_bounds__(256, OCC) unit6_kernel(UnitArgs a) {
     const int L = a.l, dil = a.dil;
     const float* xb = a.x + (int64_t)b * a.bstride;
     const int a2_lo = p0 - G6::R2, y1_lo = a2_lo - 6;
-    const int W1 = G6::NY1 + 2 * dil * G6::R2;
+    const int W1 = G6::NX2 + 2 * dil * G6::R2;
     const int a1_lo = y1_lo - dil * G6::R2, x_lo = a1_lo - 6;
-    const int NX1 = act_xs_len(W1), RS1 = unit_row_stride(NX1);
+    const int NX1 = W1 + 12, RS1 = unit_row_stride(NX1);
 
     const ActTaps f1 = load_act_taps(a.act1.taps);
     {
-        constexpr int NW = (act_xs_len(G6::W1MAX) + 255) / 256;
+        constexpr int NW = (G6::NX2 + 2 * kUnitMaxDil * G6::R2 + 12 + 255) / 256;
+        // inside the sequence: one address per row, the loads at immediate offsets
+        const bool inside = x_lo >= 0 && x_lo + 256 * NW <= L;
+        const int pos0 = inside ? x_lo + tid : 0;
 #pragma unroll
         for (int c0 = 0; c0 < C; c0 += 8) {
             float v[8][NW];
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
+            for (int r = 0; r < 8; ++r) {
+                const float* row = xb + (int64_t)(c0 + r) * L;
+                if (inside) {
 #pragma unroll
-                for (int u = 0; u < NW; ++u)
-                    v[r][u] = xb[(c0 + r) * L + clampi(x_lo + tid + 256 * u, 0, L - 1)];
+                    for (int u = 0; u < NW; ++u) v[r][u] = row[pos0 + 256 * u];
+                } else {
+#pragma unroll
+                    for (int u = 0; u < NW; ++u) v[r][u] = row[clampi(x_lo + tid + 256 * u, 0, L - 1)];
+                }
+            }
 #pragma unroll
             for (int r = 0; r < 8; ++r)
 #pragma unroll
