@@ -232,6 +232,14 @@ struct mh3a_decoder : mh3a_net {
     bool pk_ok = false;         // every AMP conv can read a packed activated input
     bool bx6_ok = false;        // ... and has split-product weights (see kPieces)
     bool h16_ok = false;        // ... and fp16 weight pieces (see kPiecesH)
+    // Concurrent AMP blocks of small decodes (see fork_ways): one side stream
+    // per residual block but the last, the event that releases them at a
+    // stage's start and one per side block marking its last conv; created
+    // at create time (default priority), used under fork_mu.
+    std::vector<hipStream_t> side;
+    hipEvent_t fork_ev = nullptr;
+    std::vector<hipEvent_t> done_ev;
+    std::mutex fork_mu;
 };
 
 namespace {
@@ -692,8 +700,28 @@ bool amp_unit_path(const mh3a_decoder* d, int stage, bool bf16) {
 // writes x_buf / t_buf alternately (a unit reads its input around its own
 // outputs, so it cannot update in place); the block's last unit adds into
 // the running sum s_buf, scaled by 1 / blocks at the last block.
-int run_amp_units(const mh3a_decoder* d, int stage, const float* h, float* x_buf, float* t_buf, float* s_buf,
-                  int batch, int64_t len, bool bf16, hipStream_t st) {
+// Scratch and stream of one residual block of an AMP set. With `fork` the
+// blocks run concurrently: block j < nrb - 1 on side stream j with scratch of
+// its own, the last block on the caller's stream; the stage's start releases
+// the side streams, and block j's last conv (the one that adds the running
+// sum in s_buf) waits for block j - 1's, so the sum accumulates in the
+// sequential order and the results are the same bits.
+struct BlockBufs {
+    float* x;
+    float* t;
+    float* a;
+    float* partial;
+    hipStream_t st;
+};
+
+hipError_t fork_begin(const mh3a_decoder* d, const BlockBufs* bb, int nrb, hipStream_t st) {
+    hipError_t e = hipEventRecord(d->fork_ev, st);
+    for (int j = 0; j + 1 < nrb && e == hipSuccess; ++j) e = hipStreamWaitEvent(bb[j].st, d->fork_ev, 0);
+    return e;
+}
+
+int run_amp_units(const mh3a_decoder* d, int stage, const float* h, const BlockBufs* bb, bool fork, float* s_buf,
+                  int batch, int64_t len, bool bf16) {
     const mh3a_config& c = d->cfg;
     const int C = d->stage_c[stage];
     const int nrb = c.num_resblocks, nd = c.num_dilations;
@@ -702,12 +730,17 @@ int run_amp_units(const mh3a_decoder* d, int stage, const float* h, float* x_buf
     bool h16 = split && !bf16 && d->cfg.matrix_form == MH3A_MATRIX_SPLIT_F16;
     for (const ConvLayer& L : d->amp[stage])
         if (L.whu_off < 0) h16 = false;
+    if (fork) HIP_TRY(fork_begin(d, bb, nrb, bb[nrb - 1].st));
     for (int j = 0; j < nrb; ++j) {
         const float* xin = h;
+        float* const x_buf = bb[j].x;
+        float* const t_buf = bb[j].t;
+        const hipStream_t st = bb[j].st;
         for (int n = 0; n < nd; ++n) {
             const ConvLayer& c1 = d->amp[stage][(j * nd + n) * 2 + 0];
             const ConvLayer& c2 = d->amp[stage][(j * nd + n) * 2 + 1];
             const bool last = (n == nd - 1);
+            if (fork && last && j > 0) HIP_TRY(hipStreamWaitEvent(st, d->done_ev[j - 1], 0));
             UnitArgs u;
             u.x = xin;
             u.y = last ? s_buf : ((n & 1) ? t_buf : x_buf);
@@ -734,27 +767,34 @@ int run_amp_units(const mh3a_decoder* d, int stage, const float* h, float* x_buf
             // two convs of 2 C k multiply-adds per output
             tl.done(KIND_AMP_UNIT, 2.0 * 2.0 * C * (double)c1.alg_taps * n_out,
                     4.0 * (n_out * (2 + (u.sum_in ? 1 : 0)) + 2.0 * C * C * c1.alg_taps + 2.0 * C));
+            if (fork && last && j + 1 < nrb) HIP_TRY(hipEventRecord(d->done_ev[j], st));
             xin = u.y;
         }
     }
     return MH3A_OK;
 }
 
-int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, float* t_buf, float* s_buf, float* a_buf,
-            int batch, int64_t len, bool bf16, bool invariant, float* partial, hipStream_t st) {
+int run_amp(const mh3a_decoder* d, int stage, const float* h, const BlockBufs* bb, bool fork, float* s_buf,
+            int batch, int64_t len, bool bf16, bool invariant) {
     const mh3a_config& c = d->cfg;
     const int C = d->stage_c[stage];
     const int64_t bs = (int64_t)C * len;
     const int nrb = c.num_resblocks, nd = c.num_dilations;
     const int L = (int)len;
-    if (amp_unit_path(d, stage, bf16)) return run_amp_units(d, stage, h, x_buf, t_buf, s_buf, batch, len, bf16, st);
+    if (amp_unit_path(d, stage, bf16)) return run_amp_units(d, stage, h, bb, fork, s_buf, batch, len, bf16);
     const bool fused = amp_act_fused(d, batch, C, len);
     const int64_t pbs = pk_item_floats(d, C, len);  // packed batch stride
     const int plp = fused ? 0 : (int)pk_lp(len);
     const bool px = stage_px(d, batch, C, len, bf16);  // packed inputs in a split-product form
     const bool h16 = px && use_h16(d) && !bf16;         // ... the fp16 one (the bf16 flag keeps bf16 pieces)
     const int pieces = px ? (h16 ? kPiecesH : kPieces) : 0;
+    if (fork) HIP_TRY(fork_begin(d, bb, nrb, bb[nrb - 1].st));
     for (int j = 0; j < nrb; ++j) {
+        float* const x_buf = bb[j].x;
+        float* const t_buf = bb[j].t;
+        float* const a_buf = bb[j].a;
+        float* const partial = bb[j].partial;
+        const hipStream_t st = bb[j].st;
         for (int n = 0; n < nd; ++n) {
             const ConvLayer& c1 = d->amp[stage][(j * nd + n) * 2 + 0];
             const ConvLayer& c2 = d->amp[stage][(j * nd + n) * 2 + 1];
@@ -775,8 +815,10 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, float* x_buf, floa
             float* yout = last ? s_buf : x_buf;
             const float* sum_in = (last && j > 0) ? s_buf : nullptr;
             const float scale = (last && j == nrb - 1) ? 1.0f / (float)nrb : 1.0f;
+            if (fork && last && j > 0) HIP_TRY(hipStreamWaitEvent(st, d->done_ev[j - 1], 0));
             HIP_TRY(run_conv(d, c2, in2, fused ? bs : pbs, L, L, yout, bs, batch, xin, sum_in, scale, bf16, invariant,
                              fused, partial, st, plp, px, h16));
+            if (fork && last && j + 1 < nrb) HIP_TRY(hipEventRecord(d->done_ev[j], st));
         }
     }
     return MH3A_OK;
@@ -844,36 +886,75 @@ int64_t decode_pk_floats(const mh3a_decoder* d, int64_t batch, int64_t frames) {
     return m;
 }
 
+// Decodes of at most this many latents (batch x frames) run the residual
+// blocks of each AMP set concurrently (see BlockBufs): their launches fill a
+// fraction of the GPU each, and the decode is a chain of ~190 of them.
+constexpr int64_t kForkMaxLatents = 800;
+
+// Residual blocks that run at once in a decode (1: one after another).
+int fork_ways(const mh3a_decoder* d, int64_t batch, int64_t frames, bool allow) {
+    const int nrb = d->cfg.num_resblocks;
+    if (!allow || nrb < 2 || (int)d->side.size() < nrb - 1 || batch * frames > kForkMaxLatents) return 1;
+    return nrb;
+}
+
 // Workspace: slots S, H, X, T, then the packed activated input, then the
-// partial sums of split launches.
-size_t decode_ws_bytes(const mh3a_decoder* d, int64_t batch, int64_t frames, uint32_t flags) {
-    const int64_t slots = 4 * round_up(max_cl(d, frames) * batch, 64);
+// partial sums of split launches; with concurrent blocks, then per side
+// block its own X, T, packed input and partial sums.
+struct DecodeLayout {
+    int64_t slot, pk, partial;
+    int ways;
+    int64_t per_block() const { return 2 * slot + pk + partial; }
+    int64_t floats() const { return 4 * slot + pk + partial + (ways - 1) * per_block(); }
+};
+
+DecodeLayout decode_layout(const mh3a_decoder* d, int64_t batch, int64_t frames, uint32_t flags, bool allow_fork) {
     const bool bf16 = (flags & MH3A_FLAG_BF16_MFMA) != 0;
     const bool inv = (flags & MH3A_FLAG_BATCH_INVARIANT) != 0;
-    return (size_t)((slots + decode_pk_floats(d, batch, frames) +
-                     decode_partial_floats(d, (int)batch, (int)frames, bf16, inv)) *
-                    (int64_t)sizeof(float));
+    DecodeLayout l;
+    l.slot = round_up(max_cl(d, frames) * batch, 64);
+    l.pk = decode_pk_floats(d, batch, frames);
+    l.partial = round_up(decode_partial_floats(d, (int)batch, (int)frames, bf16, inv), 64);
+    l.ways = fork_ways(d, batch, frames, allow_fork);
+    return l;
+}
+
+size_t decode_ws_bytes(const mh3a_decoder* d, int64_t batch, int64_t frames, uint32_t flags, bool allow_fork = true) {
+    return (size_t)(decode_layout(d, batch, frames, flags, allow_fork).floats() * (int64_t)sizeof(float));
 }
 
 int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, float* wave, int upto,
-               float* out, void* ws, size_t ws_bytes, uint32_t flags, hipStream_t st) {
+               float* out, void* ws, size_t ws_bytes, uint32_t flags, hipStream_t st, bool allow_fork = true) {
     int rc = check_decode_args(d, batch, frames, flags);
     if (rc) return rc;
     if (!z || (!wave && !out)) return fail(MH3A_E_INVALID_ARG, "null latents or output pointer");
     if (!ws) return fail(MH3A_E_WORKSPACE, "workspace is null");
     if ((uintptr_t)ws % 256) return fail(MH3A_E_WORKSPACE, "workspace must be 256-byte aligned");
-    const size_t need = decode_ws_bytes(d, batch, frames, flags);
+    const DecodeLayout lay = decode_layout(d, batch, frames, flags, allow_fork);
+    const size_t need = (size_t)(lay.floats() * (int64_t)sizeof(float));
     if (ws_bytes < need) return fail(MH3A_E_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     const mh3a_config& c = d->cfg;
     const int B = (int)batch;
     const int N = (int)frames;
-    const int64_t slot = round_up(max_cl(d, frames) * batch, 64);
+    const int64_t slot = lay.slot;
     float* bufS = static_cast<float*>(ws);
     float* bufH = bufS + slot;
     float* bufX = bufH + slot;
     float* bufT = bufX + slot;
     float* bufA = bufT + slot;
-    float* partial = bufA + decode_pk_floats(d, batch, frames);
+    float* partial = bufA + lay.pk;
+    // per residual block: its scratch and stream (the last block, or every
+    // block when they run one after another, on the caller's stream)
+    const int nrb = c.num_resblocks;
+    const bool fork = lay.ways > 1;
+    std::vector<BlockBufs> blocks(nrb, BlockBufs{bufX, bufT, bufA, partial, st});
+    if (fork) {
+        float* p = partial + lay.partial;
+        for (int j = 0; j + 1 < nrb; ++j, p += lay.per_block())
+            blocks[j] = BlockBufs{p, p + slot, p + 2 * slot, p + 2 * slot + lay.pk, d->side[j]};
+    }
+    std::unique_lock<std::mutex> fork_lock(d->fork_mu, std::defer_lock);
+    if (fork) fork_lock.lock();  // one forked decode enqueues at a time (shared side streams and events)
     const bool bf16 = (flags & MH3A_FLAG_BF16_MFMA) != 0;
     const bool invariant = (flags & MH3A_FLAG_BATCH_INVARIANT) != 0;
     HIP_TRY(hipSetDevice(d->device));
@@ -917,7 +998,7 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
                              nullptr, nullptr, 1.0f, false, invariant, true, partial, st));
         }
         if (upto == 2 + 2 * s) return finish(bufH, (int64_t)B * C * lout);
-        rc = run_amp(d, s, bufH, bufX, bufT, bufS, bufA, B, lout, bf16, invariant, partial, st);
+        rc = run_amp(d, s, bufH, blocks.data(), fork, bufS, B, lout, bf16, invariant);
         if (rc) return rc;
         if (upto == 3 + 2 * s) return finish(bufS, (int64_t)B * C * lout);
         len = lout;
@@ -1349,6 +1430,25 @@ void mh3a_config_default(mh3a_config* c) {
 
 const char* mh3a_last_error(void) { return g_err.c_str(); }
 
+namespace {
+// The side streams (default priority, not synchronizing with the null
+// stream) and ordering events of the concurrent AMP blocks, on the current
+// device; false if any creation fails (mh3a_destroy releases what exists).
+bool create_fork(mh3a_decoder* d) {
+    const int nside = d->cfg.num_resblocks - 1;
+    if (nside < 1) return true;
+    if (hipEventCreateWithFlags(&d->fork_ev, hipEventDisableTiming) != hipSuccess) return false;
+    d->done_ev.assign(nside, nullptr);
+    for (int j = 0; j < nside; ++j) {
+        hipStream_t s;
+        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return false;
+        d->side.push_back(s);
+        if (hipEventCreateWithFlags(&d->done_ev[j], hipEventDisableTiming) != hipSuccess) return false;
+    }
+    return true;
+}
+}  // namespace
+
 int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n_params, const float* latents_mean,
                         const float* latents_std, int device, mh3a_decoder** out) {
     if (!out) return fail(MH3A_E_INVALID_ARG, "out is null");
@@ -1583,7 +1683,11 @@ int mh3a_decoder_create(const mh3a_config* cfg, const mh3a_tensor* params, int n
     HIP_TRY(noalloc_scratch_lookup(device));
     d->blob_floats = (int64_t)blob.h.size();
     HIP_TRY(hipMalloc((void**)&d->blob, sizeof(float) * blob.h.size()));
-    HIP_TRY(hipMemcpy(d->blob, blob.h.data(), sizeof(float) * blob.h.size(), hipMemcpyHostToDevice));
+    if (hipMemcpy(d->blob, blob.h.data(), sizeof(float) * blob.h.size(), hipMemcpyHostToDevice) != hipSuccess ||
+        !create_fork(d)) {
+        mh3a_destroy(guard.release());
+        return fail(MH3A_E_HIP, "uploading the parameters or creating the side streams failed");
+    }
     *out = guard.release();
     return ok();
 }
@@ -1595,6 +1699,10 @@ void mh3a_destroy(mh3a_decoder* d) {
         hipDeviceSynchronize();
         hipFree(d->blob);
         for (hipEvent_t e : d->timing.evs) hipEventDestroy(e);
+        for (hipStream_t s : d->side) hipStreamDestroy(s);
+        for (hipEvent_t e : d->done_ev)
+            if (e) hipEventDestroy(e);
+        if (d->fork_ev) hipEventDestroy(d->fork_ev);
     }
     delete d;
 }
@@ -1625,7 +1733,8 @@ int mh3a_decode_noalloc(mh3a_decoder* d, const float* latents, int64_t batch, in
     int rc = check_decode_args(d, batch, frames, flags);
     if (rc) return rc;
     if (!wave) return fail(MH3A_E_INVALID_ARG, "wave is null");
-    const size_t need = decode_ws_bytes(d, batch, frames, flags);
+    // (one block after another: the concurrent form needs more scratch)
+    const size_t need = decode_ws_bytes(d, batch, frames, flags, false);
     if (need > kNoAllocScratchBytes)
         return fail(MH3A_E_WORKSPACE, "decode of %lld x %lld latents needs %zu bytes of scratch; the static scratch "
                     "holds %zu (use mh3a_decode with a workspace)", (long long)batch, (long long)frames, need,
@@ -1633,7 +1742,7 @@ int mh3a_decode_noalloc(mh3a_decoder* d, const float* latents, int64_t batch, in
     void* ws = noalloc_scratch(d->device);
     if (!ws) return fail(MH3A_E_HIP, "no static scratch address for device %d", d->device);
     return run_decode(d, latents, batch, frames, wave, -1, nullptr, ws, kNoAllocScratchBytes, flags,
-                      static_cast<hipStream_t>(stream));
+                      static_cast<hipStream_t>(stream), false);
 }
 
 int mh3a_decode_layer_shape(const mh3a_decoder* d, int64_t frames, int upto, int64_t* channels, int64_t* length) {
@@ -1754,8 +1863,9 @@ int mh3a_amp_stage(mh3a_decoder* d, int stage, const float* x, int64_t batch, in
     float* tb = xb + round_up(batch * d->stage_c[stage] * length, 64);
     float* ab = tb + round_up(batch * d->stage_c[stage] * length, 64);
     float* part = ab + stage_pk_floats(d, stage, batch, length);
-    rc = run_amp(d, stage, x, xb, tb, y, ab, (int)batch, length, (flags & MH3A_FLAG_BF16_MFMA) != 0,
-                 (flags & MH3A_FLAG_BATCH_INVARIANT) != 0, part, static_cast<hipStream_t>(stream));
+    std::vector<BlockBufs> blocks(d->cfg.num_resblocks, BlockBufs{xb, tb, ab, part, static_cast<hipStream_t>(stream)});
+    rc = run_amp(d, stage, x, blocks.data(), false, y, (int)batch, length, (flags & MH3A_FLAG_BF16_MFMA) != 0,
+                 (flags & MH3A_FLAG_BATCH_INVARIANT) != 0);
     if (rc) return rc;
     return ok();
 }
