@@ -460,13 +460,16 @@ bool pre_bx6(const mh3a_decoder* d, const ConvLayer& L) { return use_bx6(d) && L
 bool pre_h16(const mh3a_decoder* d, const ConvLayer& L) { return pre_bx6(d, L) && use_h16(d) && L.wh_off >= 0; }
 
 // Plans are cached per launch shape.
+// `ways`: launches of the same kind that run at once (the concurrent
+// residual blocks), see mh3a::plan_conv.
 ConvPlan plan_conv(const mh3a_net* d, const ConvLayer& L, int positions, int batch, bool bf16, bool invariant,
-                   bool fused, bool bx6 = false) {
-    const PlanKey key{&L, positions, batch, (bf16 ? 1 : 0) | (invariant ? 2 : 0) | (fused ? 4 : 0) | (bx6 ? 8 : 0)};
+                   bool fused, bool bx6 = false, int ways = 1) {
+    const PlanKey key{&L, positions, batch,
+                      (bf16 ? 1 : 0) | (invariant ? 2 : 0) | (fused ? 4 : 0) | (bx6 ? 8 : 0) | (ways << 4)};
     std::lock_guard<std::mutex> lock(d->plan_mu);
     auto it = d->plans.find(key);
     if (it != d->plans.end()) return {(TileId)it->second.first, it->second.second};
-    const ConvPlan p = mh3a::plan_conv(shape_of(L, fused, bx6), positions, batch, bf16, invariant, d->num_cus);
+    const ConvPlan p = mh3a::plan_conv(shape_of(L, fused, bx6), positions, batch, bf16, invariant, d->num_cus, ways);
 #ifdef MH3A_PLAN_LOG
     // (build-time option: -DMH3A_PLAN_LOG prints each new plan to stderr)
     {
@@ -519,7 +522,7 @@ struct TimedLaunch {
 hipError_t run_conv(const mh3a_net* d, const ConvLayer& L, const float* x, int64_t x_bstride, int l_in,
                     int positions, float* y, int64_t y_bstride, int batch, const float* res, const float* sum_in,
                     float scale, bool bf16, bool invariant, bool fused, float* partial, hipStream_t st,
-                    int pk_lp = 0, bool bx6 = false, bool h16 = false) {
+                    int pk_lp = 0, bool bx6 = false, bool h16 = false, int ways = 1) {
     ConvArgs a;
     std::memset(&a, 0, sizeof a);
     a.pk_lp = pk_lp;
@@ -562,7 +565,7 @@ hipError_t run_conv(const mh3a_net* d, const ConvLayer& L, const float* x, int64
     a.scale = scale;
     a.act = fused ? act_params(d, L.act) : ActParams{nullptr, nullptr};
     a.bf16 = bf16 ? 1 : 0;
-    const ConvPlan plan = plan_conv(d, L, positions, batch, bf16, invariant, fused, bx6);
+    const ConvPlan plan = plan_conv(d, L, positions, batch, bf16, invariant, fused, bx6, ways);
     a.ksplit = plan.ksplit;
     a.partial = partial;
     if (plan.ksplit > 1 && !partial) return hipErrorInvalidValue;
@@ -775,7 +778,7 @@ int run_amp_units(const mh3a_decoder* d, int stage, const float* h, const BlockB
 }
 
 int run_amp(const mh3a_decoder* d, int stage, const float* h, const BlockBufs* bb, bool fork, float* s_buf,
-            int batch, int64_t len, bool bf16, bool invariant) {
+            int batch, int64_t len, bool bf16, bool invariant, int ways = 1) {
     const mh3a_config& c = d->cfg;
     const int C = d->stage_c[stage];
     const int64_t bs = (int64_t)C * len;
@@ -805,7 +808,7 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, const BlockBufs* b
                 in1 = a_buf;
             }
             HIP_TRY(run_conv(d, c1, in1, fused ? bs : pbs, L, L, t_buf, bs, batch, nullptr, nullptr, 1.0f, bf16,
-                             invariant, fused, partial, st, plp, px, h16));
+                             invariant, fused, partial, st, plp, px, h16, ways));
             const float* in2 = t_buf;
             if (!fused) {
                 HIP_TRY(run_act(d, c2.act, t_buf, a_buf, batch, C, len, pieces, st));
@@ -817,7 +820,7 @@ int run_amp(const mh3a_decoder* d, int stage, const float* h, const BlockBufs* b
             const float scale = (last && j == nrb - 1) ? 1.0f / (float)nrb : 1.0f;
             if (fork && last && j > 0) HIP_TRY(hipStreamWaitEvent(st, d->done_ev[j - 1], 0));
             HIP_TRY(run_conv(d, c2, in2, fused ? bs : pbs, L, L, yout, bs, batch, xin, sum_in, scale, bf16, invariant,
-                             fused, partial, st, plp, px, h16));
+                             fused, partial, st, plp, px, h16, ways));
             if (fork && last && j + 1 < nrb) HIP_TRY(hipEventRecord(d->done_ev[j], st));
         }
     }
@@ -838,20 +841,22 @@ int check_decode_args(const mh3a_decoder* d, int64_t batch, int64_t frames, uint
 }
 
 // Largest partial-sum region any conv of one AMP stage needs.
-int64_t amp_partial_floats(const mh3a_decoder* d, int stage, int batch, int len, bool bf16, bool inv) {
+int64_t amp_partial_floats(const mh3a_decoder* d, int stage, int batch, int len, bool bf16, bool inv,
+                           int ways = 1) {
     int64_t m = 0;
     if (amp_unit_path(d, stage, bf16)) return 0;  // the unit kernel splits no contraction
     const bool fused = amp_act_fused(d, batch, d->stage_c[stage], len);
     const bool px = stage_px(d, batch, d->stage_c[stage], len, bf16);
     for (const ConvLayer& L : d->amp[stage])
-        m = std::max(m, plan_partial_floats(L, len, batch * L.phases, plan_conv(d, L, len, batch, bf16, inv, fused, px),
-                                            fused));
+        m = std::max(m, plan_partial_floats(L, len, batch * L.phases,
+                                            plan_conv(d, L, len, batch, bf16, inv, fused, px, ways), fused));
     return m;
 }
 
 // Largest partial-sum region any conv of a decode needs.
 // (in_proj, conv_pre and the upsamplers always run full fp32 operands.)
-int64_t decode_partial_floats(const mh3a_decoder* d, int batch, int frames, bool bf16, bool inv) {
+int64_t decode_partial_floats(const mh3a_decoder* d, int batch, int frames, bool bf16, bool inv,
+                              int ways = 1) {
     const mh3a_config& c = d->cfg;
     int64_t m = 0;
     for (const ConvLayer* L : {&d->in_proj, &d->in_proj_dn, &d->conv_pre})
@@ -863,7 +868,7 @@ int64_t decode_partial_floats(const mh3a_decoder* d, int batch, int frames, bool
         m = std::max(m, plan_partial_floats(U, (int)len, batch * U.phases,
                                             plan_conv(d, U, (int)len, batch, false, inv, true, pre_bx6(d, U)), true));
         len *= c.rates[s];
-        m = std::max(m, amp_partial_floats(d, s, batch, (int)len, bf16, inv));
+        m = std::max(m, amp_partial_floats(d, s, batch, (int)len, bf16, inv, ways));
     }
     return m;
 }
@@ -903,7 +908,8 @@ int fork_ways(const mh3a_decoder* d, int64_t batch, int64_t frames, bool allow) 
 // block its own X, T, packed input and partial sums.
 struct DecodeLayout {
     int64_t slot, pk, partial;
-    int ways;
+    int ways;        // residual blocks that run at once in this call
+    int plan_ways;   // ... in a decode of this shape: what the AMP conv plans assume
     int64_t per_block() const { return 2 * slot + pk + partial; }
     int64_t floats() const { return 4 * slot + pk + partial + (ways - 1) * per_block(); }
 };
@@ -914,8 +920,11 @@ DecodeLayout decode_layout(const mh3a_decoder* d, int64_t batch, int64_t frames,
     DecodeLayout l;
     l.slot = round_up(max_cl(d, frames) * batch, 64);
     l.pk = decode_pk_floats(d, batch, frames);
-    l.partial = round_up(decode_partial_floats(d, (int)batch, (int)frames, bf16, inv), 64);
     l.ways = fork_ways(d, batch, frames, allow_fork);
+    // the plans depend on the shape only, so that the no-allocation decode
+    // (blocks one after another) gives the same bits
+    l.plan_ways = fork_ways(d, batch, frames, true);
+    l.partial = round_up(decode_partial_floats(d, (int)batch, (int)frames, bf16, inv, l.plan_ways), 64);
     return l;
 }
 
@@ -998,7 +1007,7 @@ int run_decode(mh3a_decoder* d, const float* z, int64_t batch, int64_t frames, f
                              nullptr, nullptr, 1.0f, false, invariant, true, partial, st));
         }
         if (upto == 2 + 2 * s) return finish(bufH, (int64_t)B * C * lout);
-        rc = run_amp(d, s, bufH, blocks.data(), fork, bufS, B, lout, bf16, invariant);
+        rc = run_amp(d, s, bufH, blocks.data(), fork, bufS, B, lout, bf16, invariant, lay.plan_ways);
         if (rc) return rc;
         if (upto == 3 + 2 * s) return finish(bufS, (int64_t)B * C * lout);
         len = lout;

@@ -188,8 +188,10 @@ struct ConvPlan {
 // Bound on a plan's partial sums (floats), which live in the workspace.
 constexpr int64_t kMaxPartialFloats = (int64_t)32 << 20;
 // Plan one conv launch of `batch` items over `positions` output positions
-// per phase on a device with num_cus compute units.
-ConvPlan plan_conv(const ConvShape& s, int positions, int batch, bool bf16, bool invariant, int num_cus);
+// per phase on a device with num_cus compute units, running next to
+// ways - 1 launches of the same kind (1: alone).
+ConvPlan plan_conv(const ConvShape& s, int positions, int batch, bool bf16, bool invariant, int num_cus,
+                   int ways = 1);
 // Floats of partial sums the plan needs (0 without a K split).
 int64_t plan_partial_floats(const ConvShape& s, int positions, int groups, const ConvPlan& p);
 

@@ -142,12 +142,24 @@ TileId choose_tile(const ConvShape& L, int positions, int groups, bool bf16, int
 
 }  // namespace
 
-ConvPlan plan_conv(const ConvShape& L, int positions, int batch, bool bf16, bool invariant, int num_cus) {
+ConvPlan plan_conv(const ConvShape& L, int positions, int batch, bool bf16, bool invariant, int num_cus,
+                   int ways) {
     // AMP convs of <= 16 output channels: 16-row tiles (a 32-row block would
     // be half or three quarters padding); they never split (1-2 chunks).
     if (L.amp && L.m16 && !bf16 && !L.bx6 && forced_tile() < 0) return {TILE_16x256, 1};
     const int nch = (L.c_in + kChunk - 1) / kChunk;
     const int item_groups = invariant ? L.phases : batch * L.phases;
+    // Launches that run next to ways - 1 others (the concurrent residual
+    // blocks) take no K split once their tiles together cover half the
+    // compute units: the split's partial sums and reduce pass then cost more
+    // than the idle units they would fill (measured on B=2 x N=200).
+    if (ways > 1 && !invariant) {
+        const TileId t1 = choose_tile(L, positions, batch * L.phases, bf16, 1, num_cus);
+        const TileShape s1 = tile_shape(t1);
+        const int64_t tiles = (int64_t)((L.c_out + s1.m - 1) / s1.m) * ((positions + s1.n - 1) / s1.n) * batch *
+                              L.phases;
+        if (tiles * ways >= num_cus / 2) return {t1, 1};
+    }
     int best_s = 1;
     double best = 1e300;
     for (int S = 1; S <= 64 && S <= nch; S *= 2) {
