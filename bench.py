@@ -74,9 +74,9 @@ def parse():
     ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + sorted(ENC_WORKLOADS))
     ap.add_argument("--bf16", action="store_true", help="bf16-split matrix-core operands (MH3A_FLAG_BF16_MFMA)")
     ap.add_argument("--fp32-matrix", action="store_true",
-                    help="build the decoder with matrix_form = MH3A_MATRIX_FP32 (fp32 matrix cores throughout)")
+                    help="build the decoder (or encoder) with matrix_form = MH3A_MATRIX_FP32 (fp32 matrix cores throughout)")
     ap.add_argument("--bf16x6", action="store_true",
-                    help="build the decoder with matrix_form = MH3A_MATRIX_SPLIT (six bf16 piece products)")
+                    help="build the decoder (or encoder) with matrix_form = MH3A_MATRIX_SPLIT (six bf16 piece products)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time K replays of one decode captured in a HIP graph (graph_ms_per_step)")
@@ -399,8 +399,9 @@ def main_encode(args):
         return 2
     batch, samples, desc = ENC_WORKLOADS[args.workload]
     params = dict(synth.make_encoder_params(seed=0), **synth.make_pre_block_params(seed=0))
-    form = "fp32" if args.fp32_matrix else "split"
-    enc = Encoder(params, {"matrix_form": _lib.MH3A_MATRIX_FP32} if args.fp32_matrix else None)
+    form = "fp32" if args.fp32_matrix else ("split" if args.bf16x6 else "f16x3")
+    enc = Encoder(params, {"matrix_form": _lib.MH3A_MATRIX_FP32} if args.fp32_matrix else
+                  {"matrix_form": _lib.MH3A_MATRIX_SPLIT} if args.bf16x6 else None)
     x = torch.from_numpy(synth.make_waveform(batch, samples, seed=0)).cuda()
     out = torch.empty((batch, enc.latent_channels, enc.frames(samples)), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -452,8 +453,10 @@ def main_encode(args):
         "algorithmic_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
         "roofline": dict(roofline_entry(
             "conv_kernel, the residual units' k7 dilated convs (split-product packed input; "
-            + ("six bf16 piece products per fp32 product on v_mfma_f32_32x32x16_bf16)" if form == "split"
-               else "fp32 matrix cores)"), k7, form), traffic=measured_traffic(args.workload, form)),
+            + {"f16x3": "three fp16 piece products per fp32 product (two pieces per operand, weights scaled by "
+                        "2^e) on v_mfma_f32_32x32x16_f16, fp32 accumulation)",
+               "split": "six bf16 piece products per fp32 product on v_mfma_f32_32x32x16_bf16)",
+               "fp32": "fp32 matrix cores)"}[form], k7, form), traffic=measured_traffic(args.workload, form)),
         "kernels": _per_step(kernels, args.steps),
         "wall_s_timed": round(wall, 4),
     }

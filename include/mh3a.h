@@ -341,7 +341,7 @@ typedef struct {
     int num_blocks;                   /* strided blocks (5) */
     int rates[MH3A_MAX_ENC_BLOCKS];   /* their strides (2, 4, 4, 5, 5) */
     int latent_dim;                   /* hidden channels (2048) */
-    int matrix_form;                  /* MH3A_MATRIX_SPLIT (default) or MH3A_MATRIX_FP32 */
+    int matrix_form;                  /* MH3A_MATRIX_SPLIT_F16 (default), _SPLIT or _FP32 */
     int latent_channels;              /* posterior width: mean_proj outputs (32) */
     int num_attention_heads;          /* heads of the attention projection (8) */
 } mh3a_encoder_config;

@@ -1022,7 +1022,17 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
                 // split products: bf16 pieces, one phase, planes sized for kBx6MaxDil
                 if (!a.w6 || a.dil < 1) return hipErrorInvalidValue;
                 if (a.h16) {
-                    // two fp16 pieces, three products (AMP convs, conv_pre, transposed convs)
+                    // two fp16 pieces, three products (AMP convs, conv_pre, transposed convs,
+                    // the encoder's convs)
+                    if (a.dil > kBx6MaxDil) {
+                        // wider planes: 7 taps up to dilation kBx6WideDil (encoder units)
+                        if (a.taps != 7 || a.dil > kBx6WideDil || a.bf16 ||
+                            (((a.c_in + kChunk - 1) / kChunk) / a.ksplit) % bx6_cpi(NWG, 7, kBx6WideDil, kPiecesH))
+                            return hipErrorInvalidValue;
+                        return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 4, 7, 32, kBx6WideDil>, a, tiles,
+                                                 sizeof(float) * (size_t)conv_lds_floats6(NWG, 7, kBx6WideDil, kPiecesH),
+                                                 stream);
+                    }
                     if (a.bf16 || a.dil > kBx6MaxDil ||
                         (((a.c_in + kChunk - 1) / kChunk) / a.ksplit) % bx6_cpi(NWG, a.taps, kBx6MaxDil, kPiecesH))
                         return hipErrorInvalidValue;
@@ -1030,6 +1040,7 @@ static hipError_t launch_tile(const ConvArgs& a, hipStream_t stream) {
     if (a.taps == T)                                                                                          \
         return launch_persistent(conv_kernel<MBW, NBW, WM, WN, false, 4, T>, a, tiles,                        \
                                  sizeof(float) * (size_t)conv_lds_floats6(NWG, T, kBx6MaxDil, kPiecesH), stream);
+                    MH3A_TAPSH(1)
                     MH3A_TAPSH(2)
                     MH3A_TAPSH(3)
                     MH3A_TAPSH(7)

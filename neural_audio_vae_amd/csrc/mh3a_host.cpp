@@ -1930,8 +1930,9 @@ int enc_check_config(const mh3a_encoder_config* c) {
         dim *= 2;
     }
     if (hop > 65536 || dim > 65536) return fail(MH3A_E_CONFIG, "encoder hop or width too large");
-    if (c->matrix_form != MH3A_MATRIX_SPLIT && c->matrix_form != MH3A_MATRIX_FP32)
-        return fail(MH3A_E_CONFIG, "matrix_form %d: the encoder has the bf16 split and fp32 forms", c->matrix_form);
+    if (c->matrix_form != MH3A_MATRIX_SPLIT && c->matrix_form != MH3A_MATRIX_FP32 &&
+        c->matrix_form != MH3A_MATRIX_SPLIT_F16)
+        return fail(MH3A_E_CONFIG, "unknown matrix_form %d", c->matrix_form);
     if (c->latent_channels < 1 || c->num_attention_heads < 1)
         return fail(MH3A_E_CONFIG, "latent_channels and num_attention_heads must be positive");
     return MH3A_OK;
@@ -1962,10 +1963,23 @@ bool enc_split_ok(const ConvLayer& L) {
     return -L.in_off[0] <= kPkPadL && 255 + (L.taps - 1) * L.dil + L.in_off[0] <= kPkPadR;
 }
 
+// The split-product weights of an encoder conv (bf16 pieces; in the fp16
+// form also the fp16 pieces of the weights scaled by 2^e, see kPiecesH).
+void enc_pack_split(Blob& blob, ConvLayer& L, const std::vector<float>& w, int c_out, int c_in, int k, int form) {
+    L.w6_off = blob.reserve(packed_weight_floats6(c_out, c_in, k));
+    pack_conv_weights6(w.data(), c_out, c_in, k, blob.h.data() + L.w6_off);
+    if (form == MH3A_MATRIX_SPLIT_F16) {
+        const int e = weight_exponent_h(w.data(), (int64_t)w.size());
+        L.wh_off = blob.reserve(packed_weight_floats_h(c_out, c_in, k));
+        L.wh_scale = std::ldexp(1.0f, e);
+        pack_conv_weights_h(w.data(), c_out, c_in, k, e, blob.h.data() + L.wh_off);
+    }
+}
+
 // A weight-normalized conv of the encoder: fp32 packing always, split-product
 // pieces where the packed path serves it.
 int enc_conv(Blob& blob, const Table& t, const std::string& prefix, ConvLayer& L, int c_out, int c_in, int k, int dil,
-             int pad, int kind) {
+             int pad, int kind, int form) {
     std::vector<float> w;
     const float* bias = nullptr;
     int rc = fetch_weight(t, prefix, c_out, c_in, k, w);
@@ -1976,10 +1990,7 @@ int enc_conv(Blob& blob, const Table& t, const std::string& prefix, ConvLayer& L
     L.in_off[0] = -pad;
     L.alg_taps = k;
     L.kind = kind;
-    if (enc_split_ok(L)) {
-        L.w6_off = blob.reserve(packed_weight_floats6(c_out, c_in, k));
-        pack_conv_weights6(w.data(), c_out, c_in, k, blob.h.data() + L.w6_off);
-    }
+    if (enc_split_ok(L)) enc_pack_split(blob, L, w, c_out, c_in, k, form);
     return MH3A_OK;
 }
 
@@ -2055,10 +2066,7 @@ int enc_pre_block(Blob& blob, const Table& t, mh3a_encoder* e) {
     Q.dil = 1;
     Q.alg_taps = 1;
     Q.kind = KIND_ENC_CONV;
-    if (enc_split_ok(Q)) {
-        Q.w6_off = blob.reserve(packed_weight_floats6(3 * D, D, 1));
-        pack_conv_weights6(w.data(), 3 * D, D, 1, blob.h.data() + Q.w6_off);
-    }
+    if (enc_split_ok(Q)) enc_pack_split(blob, Q, w, 3 * D, D, 1, e->cfg.matrix_form);
     const float *wp = nullptr, *bp = nullptr, *w1 = nullptr, *b1 = nullptr, *w2 = nullptr, *b2 = nullptr;
     const float *wm = nullptr, *bm = nullptr;
     if ((rc = fetch_matrix(t, "pre_block.attn.proj.weight", C, C, &wp))) return rc;
@@ -2094,7 +2102,11 @@ int enc_pre_block(Blob& blob, const Table& t, mh3a_encoder* e) {
 }
 
 bool enc_bx6(const mh3a_encoder* e, const ConvLayer& L) {
-    return L.w6_off >= 0 && e->cfg.matrix_form == MH3A_MATRIX_SPLIT;
+    return L.w6_off >= 0 && e->cfg.matrix_form != MH3A_MATRIX_FP32;
+}
+// ... in the fp16 form (two pieces, three products)
+bool enc_h16(const mh3a_encoder* e, const ConvLayer& L) {
+    return enc_bx6(e, L) && L.wh_off >= 0 && e->cfg.matrix_form == MH3A_MATRIX_SPLIT_F16;
 }
 
 // Per-item lengths: S' = frames * hop samples after the right pad; block i
@@ -2103,7 +2115,8 @@ int64_t enc_frames(const mh3a_encoder* e, int64_t samples) { return (samples + e
 
 // Floats of one Snake output (per item) feeding conv L over l_out positions.
 int64_t enc_snake_item_floats(const mh3a_encoder* e, const ConvLayer& L, int64_t l_out) {
-    if (enc_bx6(e, L)) return (int64_t)((L.c_in + kChunk - 1) / kChunk) * kPieces * 4 * pk_lp(l_out);
+    if (enc_bx6(e, L))
+        return (int64_t)((L.c_in + kChunk - 1) / kChunk) * (enc_h16(e, L) ? kPiecesH : kPieces) * 4 * pk_lp(l_out);
     return (int64_t)L.c_in * l_out;
 }
 
@@ -2188,10 +2201,11 @@ hipError_t enc_run_snake(const mh3a_encoder* e, const SnakeLayer& S, const ConvL
     a.y = y;
     a.y_bstride = enc_snake_item_floats(e, L, l_out);
     a.lp = enc_bx6(e, L) ? (int)pk_lp(l_out) : 0;
+    a.pieces = enc_h16(e, L) ? kPiecesH : kPieces;
     TimedLaunch tl(e, st, KIND_ENC_SNAKE);
     hipError_t err = launch_snake(a, batch, st);
     const double n_in = (double)batch * S.c * l, n_out = (double)batch * S.c * s * l_out;
-    tl.done(KIND_ENC_SNAKE, 4.0 * n_in, 4.0 * n_in + (a.lp ? 6.0 : 4.0) * n_out);
+    tl.done(KIND_ENC_SNAKE, 4.0 * n_in, 4.0 * n_in + (a.lp ? 2.0 * a.pieces : 4.0) * n_out);
     return err;
 }
 
@@ -2200,7 +2214,8 @@ hipError_t enc_run_conv(const mh3a_encoder* e, const ConvLayer& L, const float* 
                         float* out, int batch, const float* res, bool inv, float* partial, hipStream_t st) {
     const bool bx6 = enc_bx6(e, L);
     return run_conv(e, L, p, enc_snake_item_floats(e, L, l_in), l_in, positions, out, (int64_t)L.c_out * positions,
-                    batch, res, nullptr, 1.0f, false, inv, true, partial, st, bx6 ? (int)pk_lp(l_in) : 0, bx6);
+                    batch, res, nullptr, 1.0f, false, inv, true, partial, st, bx6 ? (int)pk_lp(l_in) : 0, bx6,
+                    enc_h16(e, L));
 }
 
 // hidden != null: the convolution stack into `hidden`; mean != null: the
@@ -2270,10 +2285,10 @@ int run_encode(mh3a_encoder* e, const float* wave, int64_t batch, int64_t sample
         sa.c = D;
         sa.l = F;
         sa.lp = (int)pk_lp(F);
-        sa.pieces = kPieces;
+        sa.pieces = enc_h16(e, Q) ? kPiecesH : kPieces;
         TimedLaunch tl(e, st, KIND_ENC_SNAKE);
         HIP_TRY(launch_split(sa, B, st));
-        tl.done(KIND_ENC_SNAKE, 0.0, 10.0 * B * (double)D * F);
+        tl.done(KIND_ENC_SNAKE, 0.0, (4.0 + 2.0 * sa.pieces) * B * (double)D * F);
         HIP_TRY(enc_run_conv(e, Q, bufP, F, F, bufX, B, nullptr, inv, partial, st));
     } else {
         HIP_TRY(run_conv(e, Q, hid, (int64_t)D * F, F, F, bufX, 3 * (int64_t)D * F, B, nullptr, nullptr, 1.0f, false,
@@ -2336,6 +2351,7 @@ void mh3a_encoder_config_default(mh3a_encoder_config* c) {
     c->latent_dim = 2048;
     c->latent_channels = 32;
     c->num_attention_heads = 8;
+    c->matrix_form = MH3A_MATRIX_SPLIT_F16;
 }
 
 int mh3a_encoder_create(const mh3a_encoder_config* cfg, const mh3a_tensor* params, int n_params, int device,
@@ -2357,7 +2373,8 @@ int mh3a_encoder_create(const mh3a_encoder_config* cfg, const mh3a_tensor* param
     e->device = device;
     Blob blob;
     int dim = cfg->encoder_dim;
-    if ((rc = enc_conv(blob, t, "encoder.block.0", e->conv_in, dim, 1, 7, 1, 3, KIND_ENC_CONV))) return rc;
+    if ((rc = enc_conv(blob, t, "encoder.block.0", e->conv_in, dim, 1, 7, 1, 3, KIND_ENC_CONV, cfg->matrix_form)))
+        return rc;
     e->hop = 1;
     for (int i = 0; i < cfg->num_blocks; ++i) {
         const std::string pre = "encoder.block." + std::to_string(i + 1);
@@ -2369,9 +2386,12 @@ int mh3a_encoder_create(const mh3a_encoder_config* cfg, const mh3a_tensor* param
             ConvLayer k7, k1;
             const int d = kEncDils[u];
             if ((rc = enc_snake_layer(blob, t, q + ".block.0.alpha", dim, e->snakes))) return rc;
-            if ((rc = enc_conv(blob, t, q + ".block.1", k7, dim, dim, 7, d, 3 * d, KIND_ENC_UNIT_CONV))) return rc;
+            if ((rc = enc_conv(blob, t, q + ".block.1", k7, dim, dim, 7, d, 3 * d, KIND_ENC_UNIT_CONV,
+                               cfg->matrix_form)))
+                return rc;
             if ((rc = enc_snake_layer(blob, t, q + ".block.2.alpha", dim, e->snakes))) return rc;
-            if ((rc = enc_conv(blob, t, q + ".block.3", k1, dim, dim, 1, 1, 0, KIND_ENC_CONV))) return rc;
+            if ((rc = enc_conv(blob, t, q + ".block.3", k1, dim, dim, 1, 1, 0, KIND_ENC_CONV, cfg->matrix_form)))
+                return rc;
             e->unit_conv.push_back(k7);
             e->unit_conv.push_back(k1);
         }
@@ -2392,17 +2412,14 @@ int mh3a_encoder_create(const mh3a_encoder_config* cfg, const mh3a_tensor* param
         add_conv(blob, D, w2, bias, 2 * dim, dim * s, 2);
         D.alg_taps = 2;
         D.kind = KIND_ENC_CONV;
-        if (enc_split_ok(D)) {
-            D.w6_off = blob.reserve(packed_weight_floats6(2 * dim, dim * s, 2));
-            pack_conv_weights6(w2.data(), 2 * dim, dim * s, 2, blob.h.data() + D.w6_off);
-        }
+        if (enc_split_ok(D)) enc_pack_split(blob, D, w2, 2 * dim, dim * s, 2, cfg->matrix_form);
         e->down.push_back(D);
         dim *= 2;
     }
     const std::string fin = "encoder.block." + std::to_string(cfg->num_blocks + 1);
     if ((rc = enc_snake_layer(blob, t, fin + ".alpha", dim, e->snakes))) return rc;
     if ((rc = enc_conv(blob, t, "encoder.block." + std::to_string(cfg->num_blocks + 2), e->conv_out, cfg->latent_dim,
-                       dim, 3, 1, 1, KIND_ENC_CONV)))
+                       dim, 3, 1, 1, KIND_ENC_CONV, cfg->matrix_form)))
         return rc;
     if (t.get("pre_block.attn.qkv.weight") && (rc = enc_pre_block(blob, t, e))) return rc;
 

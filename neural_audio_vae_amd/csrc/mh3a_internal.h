@@ -262,6 +262,7 @@ struct SnakeArgs {
     float* y;
     int64_t y_bstride;
     int lp;
+    int pieces;          // (lp > 0) kPieces bf16 or kPiecesH fp16 pieces per value
 };
 hipError_t launch_snake(const SnakeArgs& a, int batch, hipStream_t stream);
 

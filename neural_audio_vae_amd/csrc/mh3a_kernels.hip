@@ -904,6 +904,7 @@ __device__ __forceinline__ float snake_at(const SnakeArgs& a, const float* xb, i
     return snake_beta(xb[(int64_t)c * a.l + n], ab.x, ab.y);
 }
 
+template <int PC>
 __global__ void __launch_bounds__(256) snake_packed_kernel(SnakeArgs a) {
     const int q = blockIdx.x * 256 + threadIdx.x;
     const int chunk = blockIdx.y, b = blockIdx.z;
@@ -912,11 +913,11 @@ __global__ void __launch_bounds__(256) snake_packed_kernel(SnakeArgs a) {
     float v8[kChunk];
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) v8[i] = snake_at(a, xb, chunk * kChunk + i, q - kPkPadL);
-    uint4 g[kPieces];
-    split3_pack8(v8, g);
-    float* yc = a.y + (int64_t)b * a.y_bstride + (int64_t)chunk * kPieces * a.lp * 4;
+    uint4 g[PC];
+    split_pack8<PC>(v8, g);
+    float* yc = a.y + (int64_t)b * a.y_bstride + (int64_t)chunk * PC * a.lp * 4;
 #pragma unroll
-    for (int p = 0; p < kPieces; ++p) *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = g[p];
+    for (int p = 0; p < PC; ++p) *reinterpret_cast<uint4*>(yc + ((int64_t)p * a.lp + q) * 4) = g[p];
 }
 
 __global__ void __launch_bounds__(256) snake_rows_kernel(SnakeArgs a) {
@@ -931,9 +932,13 @@ hipError_t launch_snake(const SnakeArgs& a, int batch, hipStream_t stream) {
     if (a.c < 1 || a.l < 1 || a.s < 1 || a.l_out < 1 || batch < 1 || batch > 65535 || oc > 65535 * (int64_t)kChunk)
         return hipErrorInvalidValue;
     if (a.lp > 0) {
-        if (a.lp != a.l_out + kPkPadL + kPkPadR) return hipErrorInvalidValue;
+        if (a.lp != a.l_out + kPkPadL + kPkPadR || (a.pieces != kPieces && a.pieces != kPiecesH))
+            return hipErrorInvalidValue;
         dim3 grid((a.lp + 255) / 256, (unsigned)((oc + kChunk - 1) / kChunk), batch);
-        hipLaunchKernelGGL(snake_packed_kernel, grid, dim3(256), 0, stream, a);
+        if (a.pieces == kPiecesH)
+            hipLaunchKernelGGL(snake_packed_kernel<kPiecesH>, grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL(snake_packed_kernel<kPieces>, grid, dim3(256), 0, stream, a);
     } else {
         if (oc > 65535) return hipErrorInvalidValue;
         dim3 grid((a.l_out + 255) / 256, (unsigned)oc, batch);

@@ -202,16 +202,15 @@ def test_encoder_null_handle_errors():
 
 
 def test_matrix_form_defaults_and_checks(small):
-    # the decoder defaults to fp16 pieces, the encoder to bf16 pieces; an
-    # unknown form (or the fp16 one for the encoder) is a config error,
-    # raised before any HIP call
+    # the decoder and the encoder default to fp16 pieces; an unknown form is
+    # a config error, raised before any HIP call
     assert _lib.mh3a_config_default().matrix_form == _lib.MH3A_MATRIX_SPLIT_F16
-    assert _lib.mh3a_encoder_config_default().matrix_form == _lib.MH3A_MATRIX_SPLIT
+    assert _lib.mh3a_encoder_config_default().matrix_form == _lib.MH3A_MATRIX_SPLIT_F16
     with pytest.raises(_lib.MH3AError) as e:
         _lib.mh3a_decoder_create(_lib.make_config(dict(SMALL_CONFIG, matrix_form=7)), small)
     assert e.value.code == _lib.MH3A_E_CONFIG
     enc = synth.make_encoder_params({"encoder_dim": 4, "latent_dim": 16}, seed=1)
     with pytest.raises(_lib.MH3AError) as e:
         _lib.mh3a_encoder_create(_lib.make_encoder_config({"encoder_dim": 4, "latent_dim": 16,
-                                                          "matrix_form": _lib.MH3A_MATRIX_SPLIT_F16}), enc)
+                                                          "matrix_form": 7}), enc)
     assert e.value.code == _lib.MH3A_E_CONFIG

@@ -114,13 +114,17 @@ def test_default_encoder_mean_matches_oracle(default_encoder_pre):
         check(f"default mean B={batch} S={samples}", got, O.encode(params, wave))
 
 
-def test_encoder_mean_fp32_forms(dev):
+@pytest.mark.parametrize("form", ["fp32", "bf16x6"])
+def test_encoder_mean_other_forms(dev, form):
+    # the non-default matrix forms: fp32 matrix cores on plain rows, and six
+    # bf16 piece products (the default is three fp16 piece products)
     from neural_audio_vae_amd import Encoder, _lib
-    print("[case] fp32 encoder mean (matrix_form = MH3A_MATRIX_FP32)", flush=True)
+    mf = {"fp32": _lib.MH3A_MATRIX_FP32, "bf16x6": _lib.MH3A_MATRIX_SPLIT}[form]
+    print(f"[case] {form} encoder mean (matrix_form = {mf})", flush=True)
     params = dict(synth.make_encoder_params(seed=4), **synth.make_pre_block_params(seed=4))
     wave = synth.make_waveform(1, 40 * HOP - 77, seed=4)
-    enc = Encoder(params, {"matrix_form": _lib.MH3A_MATRIX_FP32})
-    check("fp32 encoder mean S=31923", encode_mean(enc, wave), O.encode(params, wave))
+    enc = Encoder(params, {"matrix_form": mf})
+    check(f"{form} encoder mean S=31923", encode_mean(enc, wave), O.encode(params, wave))
     enc.close()
 
 
@@ -192,12 +196,15 @@ def test_encoder_argument_errors(default_encoder):
     torch.cuda.synchronize()
 
 
-def test_encoder_fp32_forms(dev):
-    # matrix_form = fp32 keeps every conv on fp32 matrix cores with plain-row inputs
+@pytest.mark.parametrize("form", ["fp32", "bf16x6"])
+def test_encoder_other_forms(dev, form):
+    # matrix_form = fp32 keeps every conv on fp32 matrix cores with plain-row
+    # inputs; _SPLIT runs six bf16 piece products on the packed input
     from neural_audio_vae_amd import Encoder, _lib
-    print("[case] fp32 encoder (matrix_form = MH3A_MATRIX_FP32)", flush=True)
+    mf = {"fp32": _lib.MH3A_MATRIX_FP32, "bf16x6": _lib.MH3A_MATRIX_SPLIT}[form]
+    print(f"[case] {form} encoder (matrix_form = {mf})", flush=True)
     params = synth.make_encoder_params(seed=4)
     wave = synth.make_waveform(1, 5 * HOP - 77, seed=4)
-    enc = Encoder(params, {"matrix_form": _lib.MH3A_MATRIX_FP32})
-    check("fp32 encoder S=3923", encode(enc, wave), O.encode_hidden(params, wave))
+    enc = Encoder(params, {"matrix_form": mf})
+    check(f"{form} encoder S=3923", encode(enc, wave), O.encode_hidden(params, wave))
     enc.close()
