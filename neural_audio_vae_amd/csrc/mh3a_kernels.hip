@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(256) final_kernel(FinalArgs a) {
 // into LDS rows and stores them packed: each thread writes the 16-byte group
 // of one (hi, position), so every wave stores 1 KB contiguous.
 // ---------------------------------------------------------------------------
-constexpr int kActT = 250;  // W + 6 = 256 up-sampling pairs: four full passes of 64 lanes
+constexpr int kActT = 186;  // W + 6 = 192 up-sampling pairs: three full passes of 64 lanes (8 workgroups per CU)
 
 // PC: 0 writes the fp32 packed layout (two channel-parity planes); kPieces /
 // kPiecesH the split-product forms (bf16 x 3 / fp16 x 2 planes).
