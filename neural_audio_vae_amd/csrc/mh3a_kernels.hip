@@ -670,7 +670,11 @@ __device__ __forceinline__ void unit_conv6(const uint4* __restrict__ pc, const f
     }
 }
 
-template <int C, int K, int T, int PF, int OCC>
+// DIL > 0 fixes the dilation at compile time (then row strides, window
+// widths and conv1's tap offsets are constants: the pieces' pack loop needs
+// no runtime division and its row reads take immediate offsets); DIL = 0
+// reads it from the arguments.
+template <int C, int K, int T, int PF, int OCC, int DIL>
 __global__ void __launch_bounds__(256, OCC) unit6_kernel(UnitArgs a) {
     constexpr int NPC = PF == 2 ? kPiecesH : kPieces;  // pieces per value in LDS
     typedef float v4f __attribute__((ext_vector_type(4)));
@@ -684,7 +688,7 @@ __global__ void __launch_bounds__(256, OCC) unit6_kernel(UnitArgs a) {
     const int ci = tid >> 5, lane32 = tid & 31;
     const int b = blockIdx.y;
     const int p0 = blockIdx.x * T;
-    const int L = a.l, dil = a.dil;
+    const int L = a.l, dil = DIL > 0 ? DIL : a.dil;
     const float* xb = a.x + (int64_t)b * a.bstride;
     const int a2_lo = p0 - G6::R2, y1_lo = a2_lo - 6;
     const int W1 = G6::NX2 + 2 * dil * G6::R2;
@@ -693,7 +697,7 @@ __global__ void __launch_bounds__(256, OCC) unit6_kernel(UnitArgs a) {
 
     const ActTaps f1 = load_act_taps(a.act1.taps);
     {
-        constexpr int NW = (G6::NX2 + 2 * kUnitMaxDil * G6::R2 + 12 + 255) / 256;
+        constexpr int NW = (G6::NX2 + 2 * (DIL > 0 ? DIL : kUnitMaxDil) * G6::R2 + 12 + 255) / 256;
         // inside the sequence: one address per row, the loads at immediate offsets
         const bool inside = x_lo >= 0 && x_lo + 256 * NW <= L;
         const int pos0 = inside ? x_lo + tid : 0;
@@ -786,19 +790,31 @@ __global__ void __launch_bounds__(256, OCC) unit6_kernel(UnitArgs a) {
         });
 }
 
-template <int C, int K, int T, int PF, int OCC>
+template <int C, int K, int T, int PF, int OCC, int DIL>
 static hipError_t launch_unit6_t(const UnitArgs& a, int batch, hipStream_t stream) {
     constexpr int NPC = PF == 2 ? kPiecesH : kPieces;
     constexpr size_t lds = sizeof(float) * Unit6Geom<C, K, T, NPC>::LDS_FLOATS;
     static_assert(OCC * lds <= 160 * 1024, "OCC workgroups per compute unit");
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void*)unit6_kernel<C, K, T, PF, OCC>,
+        hipError_t e = hipFuncSetAttribute((const void*)unit6_kernel<C, K, T, PF, OCC, DIL>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     dim3 grid((a.l + T - 1) / T, batch);
-    hipLaunchKernelGGL((unit6_kernel<C, K, T, PF, OCC>), grid, dim3(256), lds, stream, a);
+    hipLaunchKernelGGL((unit6_kernel<C, K, T, PF, OCC, DIL>), grid, dim3(256), lds, stream, a);
     return hipGetLastError();
+}
+
+// The default (fp16 piece) form has instances for the dilations 1, 3 and 5
+// of the residual blocks; other dilations and forms read it at run time.
+template <int C, int K, int T, int PF, int OCC>
+static hipError_t launch_unit6_d(const UnitArgs& a, int batch, hipStream_t stream) {
+    if constexpr (PF == 2) {
+        if (a.dil == 1) return launch_unit6_t<C, K, T, PF, OCC, 1>(a, batch, stream);
+        if (a.dil == 3) return launch_unit6_t<C, K, T, PF, OCC, 3>(a, batch, stream);
+        if (a.dil == 5) return launch_unit6_t<C, K, T, PF, OCC, 5>(a, batch, stream);
+    }
+    return launch_unit6_t<C, K, T, PF, OCC, 0>(a, batch, stream);
 }
 
 bool unit_supported(int c, int taps, int dil) {
@@ -833,9 +849,9 @@ hipError_t launch_unit(const UnitArgs& a, int batch, hipStream_t stream) {
         return hipErrorInvalidValue;
 #define MH3A_UNIT(C_, K_, T0_, T6_, O6_, T2_, O2_)                                                     \
     if (a.c == C_ && a.taps == K_)                                                                     \
-        return a.split == 6   ? launch_unit6_t<C_, K_, T6_, 6, O6_>(a, batch, stream)                   \
-               : a.split == 3 ? launch_unit6_t<C_, K_, T6_, 3, O6_>(a, batch, stream)                   \
-               : a.split == 2 ? launch_unit6_t<C_, K_, T2_, 2, O2_>(a, batch, stream)                   \
+        return a.split == 6   ? launch_unit6_d<C_, K_, T6_, 6, O6_>(a, batch, stream)                   \
+               : a.split == 3 ? launch_unit6_d<C_, K_, T6_, 3, O6_>(a, batch, stream)                   \
+               : a.split == 2 ? launch_unit6_d<C_, K_, T2_, 2, O2_>(a, batch, stream)                   \
                               : launch_unit_t<C_, K_, T0_>(a, batch, stream);
     //        C   K  fp32  bf16 pieces  fp16 pieces
     MH3A_UNIT(32, 3, 128,  96, 3,       112, 4)
