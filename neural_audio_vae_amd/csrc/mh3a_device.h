@@ -215,13 +215,83 @@ __device__ __forceinline__ void act_from_xs(float* as, float* xs, float* __restr
     }
 }
 
+// The interior case of act_from_xs (window inside the sequence, every
+// channel live) with four up-sampling pairs and four outputs per lane
+// instead of two: per sample the lane's LDS traffic drops from about 68 to
+// 48 bytes (each x value and each 2x-rate slot is read by fewer lanes) at
+// the same multiply-add count. W is a compile-time width with W % 4 == 2,
+// so the last pass's extra pairs and outputs stay inside the rows:
+// pairs up to W + 5 from x values up to W + 11 (the 2x-rate planes hold
+// act_ss_half(W) = W + 10 slots, the x rows act_xs_len(W) = W + 14 loaded
+// values), reads of slots up to W + 7, and outputs up to W + 1 (the result
+// row aliases the x row). Outputs at W and W + 1 are garbage that no caller
+// reads.
+template <int W>
+__device__ __forceinline__ void act_interior4(float* arow, const float* xrow, float* __restrict__ ev,
+                                              float* __restrict__ od, const ActTaps& f, float2 ab, int lane32) {
+    static_assert(W % 4 == 2, "W = 2 mod 4");
+    static_assert(act_ss_half(W) >= W + 10 && act_xs_len(W) >= W + 12, "rows hold the last pass");
+    const float hba = ab.x * ab.y;
+    const float(&fe)[6] = f.fe;
+    const float(&fo)[6] = f.fo;
+    const float(&fd)[12] = f.fd;
+    // pairs idx .. idx + 3 (t' = n_lo - 3 + idx): X[t' - 3 ...] = xrow[idx ...]
+    for (int idx = 4 * lane32; idx < W + 6; idx += 128) {
+        const float4 x0 = *reinterpret_cast<const float4*>(xrow + idx);
+        const float4 x1 = *reinterpret_cast<const float4*>(xrow + idx + 4);
+        const float2 x2 = *reinterpret_cast<const float2*>(xrow + idx + 8);
+        const float X[10] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w, x2.x, x2.y};
+        float ue[4], uo[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            ue[k] = ab.y;
+            uo[k] = ab.y;  // the sums start at hb (see snake_beta_biased)
+        }
+#pragma unroll
+        for (int e = 0; e < 6; ++e)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                ue[k] = fmaf(fe[e], X[k + 5 - e], ue[k]);
+                uo[k] = fmaf(fo[e], X[k + 6 - e], uo[k]);
+            }
+        // pair idx + k: s[2t'] at od[idx + k], s[2t' + 1] at ev[idx + k]
+        *reinterpret_cast<float4*>(od + idx) =
+            make_float4(snake_beta_biased(ue[0], ab.x, ab.y, hba), snake_beta_biased(ue[1], ab.x, ab.y, hba),
+                        snake_beta_biased(ue[2], ab.x, ab.y, hba), snake_beta_biased(ue[3], ab.x, ab.y, hba));
+        *reinterpret_cast<float4*>(ev + idx) =
+            make_float4(snake_beta_biased(uo[0], ab.x, ab.y, hba), snake_beta_biased(uo[1], ab.x, ab.y, hba),
+                        snake_beta_biased(uo[2], ab.x, ab.y, hba), snake_beta_biased(uo[3], ab.x, ab.y, hba));
+    }
+    wave_lds_sync();
+    // outputs w .. w + 3: a[w] = sum_j f[2j] ev[w + j] + f[2j + 1] od[w + j + 1]
+    for (int w = 4 * lane32; w < W; w += 128) {
+        const float4 e0 = *reinterpret_cast<const float4*>(ev + w);
+        const float4 e1 = *reinterpret_cast<const float4*>(ev + w + 4);
+        const float e2 = ev[w + 8];
+        const float4 o0 = *reinterpret_cast<const float4*>(od + w);
+        const float4 o1 = *reinterpret_cast<const float4*>(od + w + 4);
+        const float2 o2 = *reinterpret_cast<const float2*>(od + w + 8);
+        const float E[9] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w, e2};
+        const float O[10] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w, o2.x, o2.y};
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 6; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                acc[k] = fmaf(fd[2 * j], E[k + j], acc[k]);
+                acc[k] = fmaf(fd[2 * j + 1], O[k + j + 1], acc[k]);
+            }
+        *reinterpret_cast<float4*>(arow + w) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+}
+
 // Load X[n_lo - 6 ...] (replicate-clamped) for channel ch0 + ci into xs and
 // run act_from_xs into rows of `as` (stride as_stride; `as` may be xs itself
 // with stride act_xs_len(W): a channel's x row is dead once its up pass is
 // done, and each channel's rows belong to one wave).
 // The row is loaded into registers with every load in flight at once (a
 // loop of load-then-store would wait one memory latency per element).
-template <int CI, int W>
+template <int CI, int W, int P = 2>
 __device__ __forceinline__ void stage_act(float* as, float* xs, float* __restrict__ ss, const float* __restrict__ xb,
                                           int ch0, int c_in, int l_in, int n_lo, const ActTaps& f,
                                           const float2* abp, int ci, int lane32, int as_stride) {
@@ -248,6 +318,14 @@ __device__ __forceinline__ void stage_act(float* as, float* xs, float* __restric
         if (w < XL) xrow[w] = live ? v[r] : 0.0f;
     }
     wave_lds_sync();
+    if constexpr (P == 4) {
+        // (the interior test of act_from_xs)
+        if (n_lo - 6 >= 0 && n_lo + W + 8 <= l_in && ch0 + CI <= c_in) {
+            float* ev = ss + ci * 2 * act_ss_half(W);
+            act_interior4<W>(as + ci * as_stride, xrow, ev, ev + act_ss_half(W), f, ab, lane32);
+            return;
+        }
+    }
     act_from_xs<CI>(as, xs, ss, ch0, c_in, l_in, n_lo, W, f, ab, ci, lane32, as_stride, XL);
 }
 

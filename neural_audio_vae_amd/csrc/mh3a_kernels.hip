@@ -142,7 +142,20 @@ __global__ void __launch_bounds__(256) final_kernel(FinalArgs a) {
 // into LDS rows and stores them packed: each thread writes the 16-byte group
 // of one (hi, position), so every wave stores 1 KB contiguous.
 // ---------------------------------------------------------------------------
-constexpr int kActT = 186;  // W + 6 = 192 up-sampling pairs: three full passes of 64 lanes (8 workgroups per CU)
+// Interior tiles take four up-sampling pairs and four outputs per lane
+// (act_interior4): W + 6 = 128 pairs and 122 outputs are one pass of 32
+// lanes per channel, and 8 workgroups fill a CU's 32 wave slots. (Measured
+// 1.7% faster than two per lane on 186-position tiles; the build-time
+// options MH3A_ACT_T / MH3A_ACT_P = 2 select other widths and the two-per-lane path.)
+#ifndef MH3A_ACT_T
+#define MH3A_ACT_T 122
+#endif
+#ifndef MH3A_ACT_P
+#define MH3A_ACT_P 4
+#endif
+constexpr int kActT = MH3A_ACT_T;
+constexpr int kActP = MH3A_ACT_P;
+static_assert(kActP == 2 || (kActP == 4 && kActT % 4 == 2), "four per lane needs W = 2 mod 4");
 
 // PC: 0 writes the fp32 packed layout (two channel-parity planes); kPieces /
 // kPiecesH the split-product forms (bf16 x 3 / fp16 x 2 planes).
@@ -171,7 +184,8 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
     }
     const ActTaps f = load_act_taps(a.act.taps);
     constexpr int XS = act_xs_len(W);
-    stage_act<CI, W>(as, xs, ss, a.x + (int64_t)b * a.x_bstride, chunk * CI, a.c, a.l, t0, f, a.act.ab, ci, lane32, XS);
+    stage_act<CI, W, kActP>(as, xs, ss, a.x + (int64_t)b * a.x_bstride, chunk * CI, a.c, a.l, t0, f, a.act.ab, ci,
+                            lane32, XS);
     __syncthreads();
     if constexpr (PC != 0) {
         // one position per thread: the 8 channels' pieces, 16 bytes per plane
