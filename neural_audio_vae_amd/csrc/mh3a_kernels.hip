@@ -131,7 +131,9 @@ __global__ void __launch_bounds__(256) final_kernel(FinalArgs a) {
     }
     if (t < a.l) {
         float v = acc + a.bias;
-        if (a.clamp) v = fminf(fmaxf(v, -1.0f), 1.0f);
+        // clamp to [-1, 1]; NaN stays NaN (as torch.clamp and mx.clip do):
+        // fmax / fmin alone would map it to -1 and hide a non-finite signal
+        if (a.clamp && !__builtin_isnan(v)) v = fminf(fmaxf(v, -1.0f), 1.0f);
         a.y[(int64_t)b * a.l + t] = v;
     }
 }

@@ -105,6 +105,35 @@ def test_small_decoder_full_decode(small_decoder, small_params, dev, batch, fram
     assert np.all(np.abs(got_c) <= 1.0)
 
 
+def test_small_decoder_nan_latent_propagates_like_the_oracle(small_decoder, small_params, dev):
+    # A NaN latent (a degenerate input) turns the samples within the
+    # decoder's receptive radius into NaN, clamped or not (the clamp keeps
+    # NaN, as the pages' torch.clamp / mx.clip do), and the samples outside
+    # it decode as usual. Every sample the oracle makes NaN is NaN here too.
+    # The transposed convs of rate 5 and kernel 9 run each phase as two taps
+    # and phase 2 has one real tap, so its zero-weight slot multiplies a
+    # neighbouring input: at the edge of a NaN region 0 * NaN widens the NaN
+    # band by a few samples (less than one latent, 800 samples).
+    z = synth.make_latents(1, 80, seed=11, channels=4)
+    z[0, 2, 5] = np.nan
+    ref = O.decode(small_params, z, SMALL_CONFIG, clamp=False)
+    bad = np.isnan(ref)
+    assert bad.any() and not bad.all()
+    idx = np.nonzero(bad[0, 0])[0]
+    lo, hi = int(idx.min()), int(idx.max())
+    assert idx.size == hi - lo + 1  # one contiguous region
+    for flags, r in ((NO_CLAMP, ref), (0, O.decode(small_params, z, SMALL_CONFIG, clamp=True))):
+        got = host(small_decoder.decode(gpu(z, dev), flags=flags))
+        gbad = np.isnan(got)
+        assert gbad[bad].all(), "every oracle NaN is NaN on the GPU"
+        extra = np.nonzero(gbad[0, 0] & ~bad[0, 0])[0]
+        print(f"[parity] NaN latent flags={flags}: oracle NaN [{lo}, {hi}], GPU-only NaN {extra.size}"
+              + (f" in [{extra.min()}, {extra.max()}]" if extra.size else ""), flush=True)
+        assert np.all((extra >= lo - 800) & (extra <= hi + 800)) and extra.size < 800
+        ok = ~gbad
+        assert_close(f"small NaN latent flags={flags} (finite samples)", got[ok], r[ok], abs_=scaled_abs(r[ok]))
+
+
 def test_small_decoder_fold_uses_axis0_of_each_weight(dev):
     # g drawn away from ||v||: the fold changes every weight, per output
     # channel for convs and per input channel for the transposed convs.

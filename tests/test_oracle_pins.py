@@ -339,6 +339,26 @@ def zero_alpha_bias(params):
     return p
 
 
+def test_clamp_keeps_nan_as_torch_clamp(small_params):
+    # The decode's final clamp follows torch.clamp (the pages' module) on
+    # non-finite values: NaN stays NaN, +-inf saturate. A NaN latent spreads
+    # only within the receptive radius (about 31 latents), so late samples
+    # stay finite.
+    v = np.array([np.nan, 2.0, -3.0, np.inf, -np.inf, 0.25], np.float32)
+    want = torch.clamp(torch.from_numpy(v), -1.0, 1.0).numpy()
+    got = np.minimum(np.maximum(v, np.float32(-1.0)), np.float32(1.0))
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    np.testing.assert_array_equal(got[~np.isnan(want)], want[~np.isnan(want)])
+    z = synth.make_latents(1, 80, seed=11, channels=4)
+    z[0, 2, 5] = np.nan
+    y = O.decode(small_params, z, SMALL_CONFIG, clamp=True)[0, 0]
+    u = O.decode(small_params, z, SMALL_CONFIG, clamp=False)[0, 0]
+    np.testing.assert_array_equal(np.isnan(y), np.isnan(u))
+    assert np.isnan(y[800 * 5]) and not np.isnan(y[800 * 60:]).any()
+    fin = ~np.isnan(u)
+    np.testing.assert_array_equal(y[fin], torch.clamp(torch.from_numpy(u[fin]), -1.0, 1.0).numpy())
+
+
 @pytest.mark.parametrize("n", [1, 4])
 def test_decode_length_and_clamp(default_params, n):
     z = synth.make_latents(1, n)
