@@ -134,6 +134,32 @@ def test_small_decoder_nan_latent_propagates_like_the_oracle(small_decoder, smal
         assert_close(f"small NaN latent flags={flags} (finite samples)", got[ok], r[ok], abs_=scaled_abs(r[ok]))
 
 
+def test_fp16_piece_form_out_of_range_gives_nan_and_the_bf16x6_form_matches(small_decoder, small_params, dev):
+    # The default matrix form splits every conv input of the wide stages into
+    # two fp16 pieces, which holds while the inputs stay below fp16's 65504.
+    # Latents scaled by 1e5 drive the layer outputs to ~1e5 (the oracle stays
+    # finite): the default form then returns NaN samples, clamped or not,
+    # never finite wrong ones, while the six-product bf16 form (fp32's range)
+    # matches the oracle.
+    from neural_audio_vae_amd import Decoder, _lib
+    z = (synth.make_latents(1, 6, seed=12, channels=4) * np.float32(1e5)).astype(np.float32)
+    ref, stages = O.decode_item(small_params, z[0], SMALL_CONFIG, clamp=False, return_stages=True)
+    ref = ref[None]
+    assert np.isfinite(ref).all() and max(float(np.abs(s).max()) for s in stages) > 65504
+    for flags in (NO_CLAMP, 0):
+        got = host(small_decoder.decode(gpu(z, dev), flags=flags))
+        nan = np.isnan(got)
+        print(f"[parity] fp16 form, latents x1e5, flags={flags}: NaN samples {int(nan.sum())} of {nan.size}", flush=True)
+        assert nan.any() and np.isfinite(got[~nan]).all()
+        if (~nan).any():
+            r = ref if flags else np.clip(ref, -1, 1)
+            assert_close(f"fp16 form x1e5 flags={flags} (finite samples)", got[~nan], r[~nan], abs_=scaled_abs(r[~nan]))
+    d6 = Decoder(small_params, dict(SMALL_CONFIG, matrix_form=_lib.MH3A_MATRIX_SPLIT))
+    got6 = host(d6.decode(gpu(z, dev), flags=NO_CLAMP))
+    d6.close()
+    assert_close("bf16x6 form, latents x1e5", got6, ref, abs_=scaled_abs(ref))
+
+
 def test_small_decoder_fold_uses_axis0_of_each_weight(dev):
     # g drawn away from ||v||: the fold changes every weight, per output
     # channel for convs and per input channel for the transposed convs.
